@@ -1,0 +1,236 @@
+/*
+ * libbeamlayer — forward pass of one Beam-style sparse MoE decoder layer on
+ * AMD MI355X (gfx950), at batch-1 decode and at chunked prefill.
+ *
+ * What the layer computes is described on the "Reflection Beam 1.0 on vLLM"
+ * page (sections cited per call as [Attn], [MoE], [Opt]):
+ *   [Attn] "Attention: sliding-window layers and NoPE full-attention layers"
+ *   [MoE]  "MoE and residual stream: FP32 router, sandwich norm, depth-scaled residual"
+ *   [Opt]  "Agent-driven optimisation makes batch-1 decode 2.71x faster"
+ *          (its seven numbered changes are cited as [Opt]/1 .. [Opt]/7)
+ *   [Graph] "The fused decode graph runs one MoE layer in 13 kernels"
+ * and, for the second model's variant switches, the "vLLM Day-0 support:
+ * Recursive's Flint" page, section "Flint model architecture" [Flint].
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - Types: bf16 tensors are passed as uint16_t bit patterns, fp8 e4m3fn (OCP)
+ *    cache entries as uint8_t codes, router tensors as float (binary32),
+ *    token positions, sequence slots and expert ids as int32_t.
+ *  - Memory: every tensor argument is a caller-owned DEVICE pointer, row-major,
+ *    contiguous and 16-byte aligned. Structs (beam_dims, beam_kv) live in host
+ *    memory; their pointer fields are device pointers. The library allocates
+ *    nothing: calls that need scratch take a caller-owned device workspace
+ *    (`ws`, `ws_bytes`), sized by beam_workspace_size(). Workspace contents on
+ *    entry are ignored and on exit undefined.
+ *  - Streams: `stream` is a hipStream_t (NULL = the null stream). Every call
+ *    only enqueues kernels on it: no host synchronisation, no allocation, no
+ *    memset, so every call may be captured into a HIP graph. Inputs must not
+ *    be modified until the enqueued work completes.
+ *  - Status: every call returns BEAM_OK (0) or a negative BEAM_E_* code.
+ *    Arguments are validated on the host before any HIP call (NULL pointers,
+ *    shapes, alignment, workspace size); then the device is checked
+ *    (BEAM_E_NODEV when no GPU is present); launch failures give BEAM_E_HIP.
+ *    beam_last_error() returns a thread-local message for the last failure.
+ *  - Data-dependent checks run on the device: a position outside the cache
+ *    or an expert id outside [0, E) skips the offending token or expert and
+ *    raises a device error flag that beam_check() reports.
+ *  - Threading: calls are reentrant; two calls that share output buffers or a
+ *    workspace must be ordered by the caller (same stream).
+ *
+ * KV-cache layout (one cache per layer, caller-owned):
+ *  - K: [S][Hkv][Lmax][d]  (key-major: one key's d values contiguous)
+ *  - V: [S][Hkv][d][Lmax]  (value-transposed: one dim's values over positions
+ *                           contiguous), so that the attention contraction over
+ *                           keys reads contiguous runs for the matrix cores.
+ *  - Element type bf16, or fp8 e4m3fn codes c with value decode(c) * scale
+ *    (one k_scale for the whole K cache, one v_scale for V).
+ *  - Lmax must be a multiple of 64.
+ */
+#ifndef BEAMLAYER_H
+#define BEAMLAYER_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define BEAM_VERSION 100
+
+enum beam_status {
+  BEAM_OK = 0,
+  BEAM_E_NULL = -1,        /* a required pointer is NULL                         */
+  BEAM_E_SHAPE = -2,       /* inconsistent or out-of-range sizes                 */
+  BEAM_E_UNSUPPORTED = -3, /* sizes outside the compiled specialisations, dtype  */
+  BEAM_E_ALIGN = -4,       /* a tensor pointer is not 16-byte aligned            */
+  BEAM_E_WORKSPACE = -5,   /* ws_bytes smaller than beam_workspace_size()        */
+  BEAM_E_HIP = -6,         /* a HIP launch or runtime call failed                */
+  BEAM_E_NODEV = -7,       /* no usable GPU                                      */
+  BEAM_E_DEVICE = -8       /* a device-side check tripped (see beam_check)       */
+};
+
+enum beam_attn_mode { BEAM_SWA_ROPE = 0, BEAM_NOPE_SSMAX = 1 };
+enum beam_kv_dtype { BEAM_KV_BF16 = 0, BEAM_KV_FP8_E4M3 = 1 };
+enum beam_op {
+  BEAM_OP_QKV = 1,       /* beam_qk_norm_rope_ssmax_kvwrite */
+  BEAM_OP_ATTN_SWA = 2,  /* beam_attn_swa                   */
+  BEAM_OP_ATTN_NOPE = 3, /* beam_attn_nope_ssmax            */
+  BEAM_OP_OUT_GATE = 4,  /* beam_out_gate                   */
+  BEAM_OP_ROUTER = 5,    /* beam_router_fp32_grouped_topk   */
+  BEAM_OP_MOE = 6,       /* beam_moe_swiglu_combine         */
+  BEAM_OP_DENSE = 7      /* beam_dense_swiglu (dims->F read as the dense d_ff) */
+};
+
+/* Layer shape. D hidden size; Hq/Hkv query/kv heads (Hq % Hkv == 0, group
+ * Hq/Hkv <= 16); d head dim (32, 64 or 128); G gate width (Hq*d: one gate
+ * value per attention output element, or 0 for no output gate); E experts in
+ * n_group groups, keep topk_group groups then topk experts; F expert d_ff;
+ * window SWA keys including the current token; eps RMSNorm epsilon;
+ * route_scale multiplier of the renormalised routing weights (2.5 on Beam). */
+typedef struct beam_dims {
+  int D, Hq, Hkv, d, G, E, n_group, topk_group, topk, F, window;
+  float eps, route_scale;
+} beam_dims;
+
+/* One layer's KV cache (see the layout above). k, v: device pointers;
+ * dtype: beam_kv_dtype; k_scale/v_scale: fp8 dequantisation scales (> 0,
+ * ignored for bf16); S sequence slots; Lmax positions per slot. */
+typedef struct beam_kv {
+  void* k;
+  void* v;
+  int dtype;
+  float k_scale, v_scale;
+  int S, Lmax;
+} beam_kv;
+
+/* Sublayer boundary [MoE] sandwich norm + depth-scaled residual, fused as in
+ * [Opt]/1:   a = RMSNorm(y; w_post)                (bf16)
+ *            h <- sqrt((n-1)/n) * h + a / sqrt(n)  (bf16, in place)
+ *            x_out = RMSNorm(h; w_pre)             (bf16)
+ * RMSNorm(v; w) = v / sqrt(mean(v^2) + eps) * w, statistics in fp32.
+ * y [T][D], h [T][D] (in/out), x_out [T][D], gains [D], all bf16.
+ * y == NULL: only x_out = RMSNorm(h; w_pre) (the layer-entry pre-norm; h is
+ * read only). w_post == NULL: a = y (no post-norm). n == 0: plain add h + a
+ * (pre-norm models, [Flint]). Errors: T <= 0, D not a multiple of 8 or
+ * above 8192, n < 0. */
+int beam_boundary_norm_residual(const beam_dims* dims, int T, const uint16_t* y,
+                                const uint16_t* w_post, uint16_t* h,
+                                const uint16_t* w_pre, uint16_t* x_out, int n,
+                                void* stream);
+
+/* Packed projection and per-head Q/K processing with the cache write
+ * ([Opt]/5 packed q|k|v|gate GEMM, [Opt]/2 and [Opt]/6 fused norm, RoPE/SSMax
+ * and KV update; [Attn]):
+ *   qkvg = bf16(x . w_qkvg^T), w_qkvg [Hq*d + 2*Hkv*d + G][D] bf16 with row
+ *   blocks q (head-major), k, v, gate.
+ *   q_h <- RMSNorm_d(q_h; w_qnorm), k_j <- RMSNorm_d(k_j; w_knorm) (one [d]
+ *   gain each, shared by all heads), then
+ *     mode BEAM_SWA_ROPE:   rotate q and k at position pos[t] (rotate-half
+ *                           pairs (i, i+d/2); rope_cs[pos][i] = cos, and
+ *                           rope_cs[pos][d/2+i] = sin, of pos*theta^(-2i/d),
+ *                           table [Lmax][d] fp32, see beam_rope_table);
+ *     mode BEAM_NOPE_SSMAX: q <- q * (1 + (pos[t]+1)/2048)^0.1, keys as is.
+ *   q_out [T][Hq][d] = bf16(q); g_out [T][G] = the gate rows (bf16);
+ *   cache slot (seq[t], pos[t]) <- k, v (bf16, or e4m3 of value/scale with
+ *   round-to-nearest-even and saturation at 448).
+ * x [T][D] bf16; pos, seq [T] int32 (device). ws >= beam_workspace_size(QKV).
+ * Errors: invalid mode; RoPE without rope_cs; Hq % Hkv; d unsupported; fp8
+ * with a scale <= 0. Device check: pos outside [0, Lmax) or seq outside
+ * [0, S) skips that token's cache write and raises the device flag. */
+int beam_qk_norm_rope_ssmax_kvwrite(const beam_dims* dims, int T, const uint16_t* x,
+                                    const uint16_t* w_qkvg, const uint16_t* w_qnorm,
+                                    const uint16_t* w_knorm, const int32_t* pos,
+                                    const int32_t* seq, int mode, const float* rope_cs,
+                                    uint16_t* q_out, uint16_t* g_out, const beam_kv* kv,
+                                    void* ws, size_t ws_bytes, void* stream);
+
+/* GQA attention over a sliding window [Attn]: query head h of token t reads
+ * kv head floor(h*Hkv/Hq) of slot seq[t] at positions
+ * [max(0, pos[t]-window+1), pos[t]] (window keys including itself), scores
+ * q.k/sqrt(d), fp32 softmax and accumulation, o [T][Hq][d] bf16.
+ * sink (optional, [Flint]): per-head fp32 logit added to the softmax
+ * denominator only. max_pos >= max(pos) (host value used to size the grid).
+ * ws >= beam_workspace_size(ATTN_SWA, T, max_pos + 1).
+ * Errors: window <= 0, max_pos >= Lmax. */
+int beam_attn_swa(const beam_dims* dims, int T, const uint16_t* q, const int32_t* pos,
+                  const int32_t* seq, const beam_kv* kv, const float* sink, uint16_t* o,
+                  int max_pos, void* ws, size_t ws_bytes, void* stream);
+
+/* Full-context attention of a NoPE layer [Attn]: as beam_attn_swa over all
+ * positions [0, pos[t]]; the SSMax query scale was applied by the q/k call.
+ * ws >= beam_workspace_size(ATTN_NOPE, T, max_pos + 1) (split-K partials). */
+int beam_attn_nope_ssmax(const beam_dims* dims, int T, const uint16_t* q,
+                         const int32_t* pos, const int32_t* seq, const beam_kv* kv,
+                         const float* sink, uint16_t* o, int max_pos, void* ws,
+                         size_t ws_bytes, void* stream);
+
+/* Sigmoid output gate and o_proj ([Attn]; [Opt]/2 gate kernel):
+ *   z = bf16(o * sigmoid(g + b_gate[head]))  elementwise over [T][Hq*d]
+ *   y = bf16(z . w_o^T), w_o [D][Hq*d] bf16, y [T][D] bf16.
+ * g == NULL (with G == 0): z = o (no gate). ws >= beam_workspace_size(OUT_GATE).
+ * Errors: G not in {0, Hq*d}; g/b_gate NULL while G > 0. */
+int beam_out_gate(const beam_dims* dims, int T, const uint16_t* o, const uint16_t* g,
+                  const uint16_t* b_gate, const uint16_t* w_o, uint16_t* y, void* ws,
+                  size_t ws_bytes, void* stream);
+
+/* FP32 router with DeepSeek-V3 grouped selection ([MoE]; [Opt]/4):
+ *   logits = fp32(x) . w_r^T (fp32 weights [E][D], fp32 accumulation)
+ *   s = sigmoid(logits); s' = s + b_corr (b_corr may be NULL = 0)
+ *   group score = sum of the two largest s' in each of n_group groups;
+ *   keep topk_group groups; pick topk experts by s' among them;
+ *   w = route_scale * s / sum(s) over the picked experts.
+ * Ties go to the lower index; idx [T][topk] int32 ordered by s' descending,
+ * w [T][topk] fp32, logits [T][E] fp32 (optional output).
+ * ws >= beam_workspace_size(ROUTER). Errors: E % n_group; topk_group >
+ * n_group; topk > topk_group*E/n_group; topk > 32; E > 1024. */
+int beam_router_fp32_grouped_topk(const beam_dims* dims, int T, const uint16_t* x,
+                                  const float* w_r, const float* b_corr, int32_t* idx,
+                                  float* w, float* logits, void* ws, size_t ws_bytes,
+                                  void* stream);
+
+/* Routed SwiGLU experts and the weighted combine ([MoE]; [Opt]/3 combine):
+ *   for each token t and k < topk, e = idx[t][k]:
+ *     u = bf16(x_t . w13[e]^T)   w13 [E][2F][D] bf16 (rows 0..F-1 gate, F..2F-1 up)
+ *     a = bf16(silu(u[:F]) * u[F:])
+ *     acc += w[t][k] * (a . w2[e]^T)  (fp32)   w2 [E][D][F] bf16
+ *   plus, when shared_w13 != NULL, one always-on expert with weight 1 ([Flint]);
+ *   y [T][D] = bf16(acc).
+ * Only the selected experts' weights are read. ws >= beam_workspace_size(MOE).
+ * Device check: ids outside [0, E) are skipped and raise the device flag. */
+int beam_moe_swiglu_combine(const beam_dims* dims, int T, const uint16_t* x,
+                            const int32_t* idx, const float* w, const uint16_t* w13,
+                            const uint16_t* w2, const uint16_t* shared_w13,
+                            const uint16_t* shared_w2, uint16_t* y, void* ws,
+                            size_t ws_bytes, void* stream);
+
+/* Dense SwiGLU MLP of the first layers ([MoE]; [Opt]/7):
+ *   u = bf16(x . w13^T) (w13 [2*Fd][D], gate rows then up rows),
+ *   a = bf16(silu(u[:Fd]) * u[Fd:]), y = bf16(a . w2^T) (w2 [D][Fd]).
+ * Errors: Fd % 64, D % 8. ws >= beam_workspace_size(DENSE) with dims->F = Fd. */
+int beam_dense_swiglu(int T, int D, int Fd, const uint16_t* x, const uint16_t* w13,
+                      const uint16_t* w2, uint16_t* y, void* ws, size_t ws_bytes,
+                      void* stream);
+
+/* Bytes of workspace `op` needs for T tokens; max_ctx bounds the attended
+ * context (max_pos + 1) for the attention ops and is ignored otherwise.
+ * Returns 0 for ops that need none and (size_t)-1 for invalid arguments. */
+size_t beam_workspace_size(const beam_dims* dims, int op, int T, int max_ctx);
+
+/* Host helper: fill out[Lmax][d] (host memory) with the RoPE table used by
+ * beam_qk_norm_rope_ssmax_kvwrite, computed in double and stored as float. */
+int beam_rope_table(float* out, int Lmax, int d, double theta);
+
+/* Waits for `stream`, then reports BEAM_E_HIP for a failed kernel or
+ * BEAM_E_DEVICE if a device-side check tripped since the last beam_check
+ * (the flag is cleared). */
+int beam_check(void* stream);
+
+const char* beam_last_error(void);
+int beam_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* BEAMLAYER_H */

@@ -1,0 +1,411 @@
+// C ABI of libbeamlayer: argument validation, workspace accounting and shape
+// dispatch to the HIP kernels. See include/beamlayer.h for the contract.
+#include "beamlayer.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <mutex>
+#include <string>
+
+#include "internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int device_ready() {
+  static std::once_flag once;
+  static bool ok = false;
+  std::call_once(once, [] {
+    int n = 0;
+    ok = (hipGetDeviceCount(&n) == hipSuccess && n > 0);
+  });
+  return ok ? BEAM_OK : fail(BEAM_E_NODEV, "no HIP device available");
+}
+
+int launched(int rc, const char* fn) {
+  if (rc == 0) return BEAM_OK;
+  return fail(BEAM_E_HIP, "%s: kernel launch failed: %s", fn,
+              hipGetErrorString(hipGetLastError()));
+}
+
+bool misaligned(const void* p) { return p && (reinterpret_cast<uintptr_t>(p) & 15u); }
+
+size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
+
+#define REQ(p) \
+  if (!(p)) return fail(BEAM_E_NULL, "%s: %s is NULL", __func__, #p)
+#define ALN(p) \
+  if (misaligned(p)) return fail(BEAM_E_ALIGN, "%s: %s is not 16-byte aligned", __func__, #p)
+#define SHAPE(cond, ...) \
+  if (!(cond)) return fail(BEAM_E_SHAPE, __VA_ARGS__)
+#define UNSUP(cond, ...) \
+  if (!(cond)) return fail(BEAM_E_UNSUPPORTED, __VA_ARGS__)
+
+hipStream_t S_(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+// Checks common to every call that reads a beam_dims.
+int check_dims_attn(const beam_dims* d, const char* fn) {
+  if (d->D <= 0 || d->Hq <= 0 || d->Hkv <= 0 || d->d <= 0)
+    return fail(BEAM_E_SHAPE, "%s: non-positive dimension", fn);
+  if (d->Hq % d->Hkv) return fail(BEAM_E_SHAPE, "%s: Hq %% Hkv != 0", fn);
+  if (d->Hq / d->Hkv > 16) return fail(BEAM_E_UNSUPPORTED, "%s: GQA group above 16", fn);
+  if (d->d != 32 && d->d != 64 && d->d != 128)
+    return fail(BEAM_E_UNSUPPORTED, "%s: head dim %d not in {32, 64, 128}", fn, d->d);
+  if (d->D % 8 || d->D > 8192) return fail(BEAM_E_UNSUPPORTED, "%s: D must be a multiple of 8 <= 8192", fn);
+  if (d->G != 0 && d->G != d->Hq * d->d)
+    return fail(BEAM_E_UNSUPPORTED, "%s: gate width must be 0 or Hq*d", fn);
+  return BEAM_OK;
+}
+
+int check_kv(const beam_kv* kv, const char* fn) {
+  if (!kv) return fail(BEAM_E_NULL, "%s: kv is NULL", fn);
+  if (!kv->k || !kv->v) return fail(BEAM_E_NULL, "%s: kv->k or kv->v is NULL", fn);
+  if (misaligned(kv->k) || misaligned(kv->v))
+    return fail(BEAM_E_ALIGN, "%s: cache not 16-byte aligned", fn);
+  if (kv->S <= 0 || kv->Lmax <= 0) return fail(BEAM_E_SHAPE, "%s: cache S/Lmax <= 0", fn);
+  if (kv->Lmax % 64) return fail(BEAM_E_SHAPE, "%s: Lmax must be a multiple of 64", fn);
+  if (kv->dtype != BEAM_KV_BF16 && kv->dtype != BEAM_KV_FP8_E4M3)
+    return fail(BEAM_E_UNSUPPORTED, "%s: unknown kv dtype %d", fn, kv->dtype);
+  if (kv->dtype == BEAM_KV_FP8_E4M3 && !(kv->k_scale > 0.f && kv->v_scale > 0.f))
+    return fail(BEAM_E_SHAPE, "%s: fp8 cache scales must be > 0", fn);
+  return BEAM_OK;
+}
+
+size_t ws_qkv(const beam_dims* d, int T) {
+  return align256((size_t)T * (d->Hq + 2 * d->Hkv) * d->d * 2);
+}
+int attn_span(const beam_dims* d, int swa, int max_ctx) {
+  return swa ? std::min(max_ctx, d->window + 63) : max_ctx;
+}
+size_t ws_attn(const beam_dims* d, int swa, int T, int max_ctx) {
+  const int nch = beam::attn_nch_bound(T, d->Hkv, attn_span(d, swa, max_ctx));
+  return align256((size_t)T * d->Hq * nch * (d->d + 4) * 4);
+}
+size_t ws_out_gate(const beam_dims* d, int T) { return align256((size_t)T * d->Hq * d->d * 2); }
+size_t ws_router(const beam_dims* d, int T) { return align256((size_t)T * d->E * 4); }
+size_t ws_moe(const beam_dims* d, int T) {
+  return align256((size_t)T * (d->topk + 1) * d->F * 2);
+}
+size_t ws_dense(int T, int Fd) { return align256((size_t)T * Fd * 2); }
+
+int attn_impl(const beam_dims* dims, int T, const uint16_t* q, const int32_t* pos,
+              const int32_t* seq, const beam_kv* kv, const float* sink, uint16_t* o,
+              int max_pos, void* ws, size_t ws_bytes, void* stream, int swa, const char* fn) {
+  if (!dims) return fail(BEAM_E_NULL, "%s: dims is NULL", fn);
+  if (!q || !pos || !seq || !o || !ws) return fail(BEAM_E_NULL, "%s: NULL tensor argument", fn);
+  if (misaligned(q) || misaligned(o) || misaligned(ws) || misaligned(sink))
+    return fail(BEAM_E_ALIGN, "%s: tensor not 16-byte aligned", fn);
+  int rc = check_dims_attn(dims, fn);
+  if (rc) return rc;
+  if ((rc = check_kv(kv, fn))) return rc;
+  if (T <= 0) return fail(BEAM_E_SHAPE, "%s: T <= 0", fn);
+  if (swa && dims->window <= 0) return fail(BEAM_E_SHAPE, "%s: window <= 0", fn);
+  if (max_pos < 0 || max_pos >= kv->Lmax)
+    return fail(BEAM_E_SHAPE, "%s: max_pos %d outside [0, Lmax)", fn, max_pos);
+  const int span = attn_span(dims, swa, max_pos + 1);
+  int tpw, nch;
+  beam::attn_plan(T, dims->Hkv, span, &tpw, &nch);
+  const size_t need = (size_t)T * dims->Hq * nch * (dims->d + 4) * 4;
+  if (ws_bytes < need)
+    return fail(BEAM_E_WORKSPACE, "%s: workspace %zu < %zu bytes", fn, ws_bytes, need);
+  if ((rc = device_ready())) return rc;
+  const int fp8 = kv->dtype == BEAM_KV_FP8_E4M3;
+  return launched(beam::launch_attn_decode(T, dims->Hq, dims->Hkv, dims->d, swa, dims->window,
+                                           fp8, q, pos, seq, kv->k, kv->v,
+                                           fp8 ? kv->k_scale : 1.f, fp8 ? kv->v_scale : 1.f,
+                                           kv->S, kv->Lmax, sink, o, span, (float*)ws, S_(stream)),
+                  fn);
+}
+
+}  // namespace
+
+extern "C" {
+
+int beam_version(void) { return BEAM_VERSION; }
+
+const char* beam_last_error(void) { return g_last_error.c_str(); }
+
+int beam_boundary_norm_residual(const beam_dims* dims, int T, const uint16_t* y,
+                                const uint16_t* w_post, uint16_t* h, const uint16_t* w_pre,
+                                uint16_t* x_out, int n, void* stream) {
+  REQ(dims);
+  REQ(h);
+  REQ(w_pre);
+  REQ(x_out);
+  ALN(y);
+  ALN(w_post);
+  ALN(h);
+  ALN(w_pre);
+  ALN(x_out);
+  SHAPE(T > 0, "%s: T <= 0", __func__);
+  SHAPE(n >= 0, "%s: n < 0", __func__);
+  UNSUP(dims->D > 0 && dims->D % 8 == 0 && dims->D <= 8192,
+        "%s: D must be a positive multiple of 8 <= 8192", __func__);
+  int rc = device_ready();
+  if (rc) return rc;
+  return launched(beam::launch_boundary(T, dims->D, y, w_post, h, w_pre, x_out, n, dims->eps,
+                                        S_(stream)),
+                  __func__);
+}
+
+int beam_qk_norm_rope_ssmax_kvwrite(const beam_dims* dims, int T, const uint16_t* x,
+                                    const uint16_t* w_qkvg, const uint16_t* w_qnorm,
+                                    const uint16_t* w_knorm, const int32_t* pos,
+                                    const int32_t* seq, int mode, const float* rope_cs,
+                                    uint16_t* q_out, uint16_t* g_out, const beam_kv* kv,
+                                    void* ws, size_t ws_bytes, void* stream) {
+  REQ(dims);
+  REQ(x);
+  REQ(w_qkvg);
+  REQ(w_qnorm);
+  REQ(w_knorm);
+  REQ(pos);
+  REQ(seq);
+  REQ(q_out);
+  REQ(ws);
+  ALN(x);
+  ALN(w_qkvg);
+  ALN(q_out);
+  ALN(g_out);
+  ALN(ws);
+  int rc = check_dims_attn(dims, __func__);
+  if (rc) return rc;
+  if ((rc = check_kv(kv, __func__))) return rc;
+  SHAPE(T > 0, "%s: T <= 0", __func__);
+  if (mode != BEAM_SWA_ROPE && mode != BEAM_NOPE_SSMAX)
+    return fail(BEAM_E_SHAPE, "%s: invalid mode %d", __func__, mode);
+  if (mode == BEAM_SWA_ROPE && !rope_cs)
+    return fail(BEAM_E_NULL, "%s: RoPE mode needs rope_cs", __func__);
+  if (dims->G > 0 && !g_out) return fail(BEAM_E_NULL, "%s: g_out is NULL", __func__);
+  if (ws_bytes < ws_qkv(dims, T))
+    return fail(BEAM_E_WORKSPACE, "%s: workspace %zu < %zu bytes", __func__, ws_bytes,
+                ws_qkv(dims, T));
+  if ((rc = device_ready())) return rc;
+  const int Nqkv = (dims->Hq + 2 * dims->Hkv) * dims->d;
+  uint16_t* qkv = (uint16_t*)ws;
+  if (beam::launch_gemv_qkvg(T, Nqkv + dims->G, dims->D, Nqkv, w_qkvg, x, qkv, g_out,
+                             S_(stream)))
+    return launched(-1, __func__);
+  const int fp8 = kv->dtype == BEAM_KV_FP8_E4M3;
+  return launched(beam::launch_qk_epilogue(T, dims->Hq, dims->Hkv, dims->d, qkv, w_qnorm,
+                                           w_knorm, pos, seq, mode, rope_cs, q_out, kv->k,
+                                           kv->v, fp8, fp8 ? kv->k_scale : 1.f,
+                                           fp8 ? kv->v_scale : 1.f, kv->S, kv->Lmax,
+                                           dims->eps, S_(stream)),
+                  __func__);
+}
+
+int beam_attn_swa(const beam_dims* dims, int T, const uint16_t* q, const int32_t* pos,
+                  const int32_t* seq, const beam_kv* kv, const float* sink, uint16_t* o,
+                  int max_pos, void* ws, size_t ws_bytes, void* stream) {
+  return attn_impl(dims, T, q, pos, seq, kv, sink, o, max_pos, ws, ws_bytes, stream, 1,
+                   __func__);
+}
+
+int beam_attn_nope_ssmax(const beam_dims* dims, int T, const uint16_t* q,
+                         const int32_t* pos, const int32_t* seq, const beam_kv* kv,
+                         const float* sink, uint16_t* o, int max_pos, void* ws,
+                         size_t ws_bytes, void* stream) {
+  return attn_impl(dims, T, q, pos, seq, kv, sink, o, max_pos, ws, ws_bytes, stream, 0,
+                   __func__);
+}
+
+int beam_out_gate(const beam_dims* dims, int T, const uint16_t* o, const uint16_t* g,
+                  const uint16_t* b_gate, const uint16_t* w_o, uint16_t* y, void* ws,
+                  size_t ws_bytes, void* stream) {
+  REQ(dims);
+  REQ(o);
+  REQ(w_o);
+  REQ(y);
+  ALN(o);
+  ALN(g);
+  ALN(w_o);
+  ALN(y);
+  ALN(ws);
+  int rc = check_dims_attn(dims, __func__);
+  if (rc) return rc;
+  SHAPE(T > 0, "%s: T <= 0", __func__);
+  if (dims->G > 0 && (!g || !b_gate))
+    return fail(BEAM_E_NULL, "%s: gate input or bias is NULL", __func__);
+  (void)ws;
+  (void)ws_bytes;
+  if ((rc = device_ready())) return rc;
+  const int K = dims->Hq * dims->d;
+  return launched(beam::launch_gemv_gate_oproj(T, dims->D, K, dims->d, w_o, o,
+                                               dims->G ? g : nullptr, b_gate, y, S_(stream)),
+                  __func__);
+}
+
+int beam_router_fp32_grouped_topk(const beam_dims* dims, int T, const uint16_t* x,
+                                  const float* w_r, const float* b_corr, int32_t* idx,
+                                  float* w, float* logits, void* ws, size_t ws_bytes,
+                                  void* stream) {
+  REQ(dims);
+  REQ(x);
+  REQ(w_r);
+  REQ(idx);
+  REQ(w);
+  ALN(x);
+  ALN(w_r);
+  ALN(logits);
+  ALN(ws);
+  SHAPE(T > 0, "%s: T <= 0", __func__);
+  const int E = dims->E, ng = dims->n_group, tg = dims->topk_group, K = dims->topk;
+  SHAPE(E > 0 && ng > 0 && tg > 0 && K > 0, "%s: non-positive routing size", __func__);
+  SHAPE(E % ng == 0, "%s: E %% n_group != 0", __func__);
+  SHAPE(tg <= ng, "%s: topk_group > n_group", __func__);
+  SHAPE(K <= tg * (E / ng), "%s: topk > topk_group * E / n_group", __func__);
+  UNSUP(K <= 32, "%s: topk > 32", __func__);
+  UNSUP(E <= 1024 && ng <= 64, "%s: E > 1024 or n_group > 64", __func__);
+  UNSUP(dims->D > 0 && dims->D % 8 == 0, "%s: D must be a positive multiple of 8", __func__);
+  float* lg = logits;
+  if (!lg) {
+    REQ(ws);
+    if (ws_bytes < ws_router(dims, T))
+      return fail(BEAM_E_WORKSPACE, "%s: workspace %zu < %zu bytes", __func__, ws_bytes,
+                  ws_router(dims, T));
+    lg = (float*)ws;
+  }
+  int rc = device_ready();
+  if (rc) return rc;
+  return launched(beam::launch_router(T, E, dims->D, ng, tg, K, dims->route_scale, x, w_r,
+                                      b_corr, lg, idx, w, S_(stream)),
+                  __func__);
+}
+
+int beam_moe_swiglu_combine(const beam_dims* dims, int T, const uint16_t* x,
+                            const int32_t* idx, const float* w, const uint16_t* w13,
+                            const uint16_t* w2, const uint16_t* shared_w13,
+                            const uint16_t* shared_w2, uint16_t* y, void* ws,
+                            size_t ws_bytes, void* stream) {
+  REQ(dims);
+  REQ(x);
+  REQ(idx);
+  REQ(w);
+  REQ(w13);
+  REQ(w2);
+  REQ(y);
+  REQ(ws);
+  ALN(x);
+  ALN(w13);
+  ALN(w2);
+  ALN(shared_w13);
+  ALN(shared_w2);
+  ALN(y);
+  ALN(ws);
+  SHAPE(T > 0, "%s: T <= 0", __func__);
+  SHAPE(dims->E > 0 && dims->topk > 0 && dims->F > 0, "%s: non-positive E/topk/F", __func__);
+  if ((shared_w13 == nullptr) != (shared_w2 == nullptr))
+    return fail(BEAM_E_NULL, "%s: shared_w13 and shared_w2 must both be set or both NULL",
+                __func__);
+  UNSUP(dims->D > 0 && dims->D % 8 == 0 && dims->D <= 8192,
+        "%s: D must be a positive multiple of 8 <= 8192", __func__);
+  UNSUP(dims->F % 8 == 0, "%s: F must be a multiple of 8", __func__);
+  if (ws_bytes < ws_moe(dims, T))
+    return fail(BEAM_E_WORKSPACE, "%s: workspace %zu < %zu bytes", __func__, ws_bytes,
+                ws_moe(dims, T));
+  int rc = device_ready();
+  if (rc) return rc;
+  const int spt = dims->topk + (shared_w13 ? 1 : 0);
+  uint16_t* act = (uint16_t*)ws;
+  if (beam::launch_expert_w13(T, dims->D, dims->F, dims->E, dims->topk, spt, w13, shared_w13,
+                              idx, x, act, S_(stream)))
+    return launched(-1, __func__);
+  return launched(beam::launch_expert_w2(T, dims->D, dims->F, dims->E, dims->topk, spt, w2,
+                                         shared_w2, idx, w, act, y, S_(stream)),
+                  __func__);
+}
+
+int beam_dense_swiglu(int T, int D, int Fd, const uint16_t* x, const uint16_t* w13,
+                      const uint16_t* w2, uint16_t* y, void* ws, size_t ws_bytes,
+                      void* stream) {
+  REQ(x);
+  REQ(w13);
+  REQ(w2);
+  REQ(y);
+  REQ(ws);
+  ALN(x);
+  ALN(w13);
+  ALN(w2);
+  ALN(y);
+  ALN(ws);
+  SHAPE(T > 0, "%s: T <= 0", __func__);
+  SHAPE(Fd > 0 && Fd % 64 == 0, "%s: Fd must be a positive multiple of 64", __func__);
+  UNSUP(D > 0 && D % 8 == 0 && D <= 8192, "%s: D must be a positive multiple of 8 <= 8192",
+        __func__);
+  if (ws_bytes < ws_dense(T, Fd))
+    return fail(BEAM_E_WORKSPACE, "%s: workspace %zu < %zu bytes", __func__, ws_bytes,
+                ws_dense(T, Fd));
+  int rc = device_ready();
+  if (rc) return rc;
+  uint16_t* act = (uint16_t*)ws;
+  if (beam::launch_expert_w13(T, D, Fd, 1, 1, 1, w13, nullptr, nullptr, x, act, S_(stream)))
+    return launched(-1, __func__);
+  return launched(beam::launch_expert_w2(T, D, Fd, 1, 1, 1, w2, nullptr, nullptr, nullptr, act,
+                                         y, S_(stream)),
+                  __func__);
+}
+
+size_t beam_workspace_size(const beam_dims* dims, int op, int T, int max_ctx) {
+  if (!dims || T <= 0) return (size_t)-1;
+  switch (op) {
+    case BEAM_OP_QKV: return ws_qkv(dims, T);
+    case BEAM_OP_ATTN_SWA:
+    case BEAM_OP_ATTN_NOPE:
+      if (max_ctx <= 0 || dims->Hkv <= 0) return (size_t)-1;
+      return ws_attn(dims, op == BEAM_OP_ATTN_SWA, T, max_ctx);
+    case BEAM_OP_OUT_GATE: return ws_out_gate(dims, T);
+    case BEAM_OP_ROUTER: return ws_router(dims, T);
+    case BEAM_OP_MOE: return ws_moe(dims, T);
+    case BEAM_OP_DENSE: return ws_dense(T, dims->F);
+    default: return (size_t)-1;
+  }
+}
+
+int beam_rope_table(float* out, int Lmax, int d, double theta) {
+  if (!out) return fail(BEAM_E_NULL, "%s: out is NULL", __func__);
+  if (Lmax <= 0 || d <= 0 || d % 2 || !(theta > 0))
+    return fail(BEAM_E_SHAPE, "%s: bad Lmax/d/theta", __func__);
+  const int half = d / 2;
+  for (int i = 0; i < half; ++i) {
+    const double inv_freq = std::pow(theta, -2.0 * i / d);
+    for (int p = 0; p < Lmax; ++p) {
+      const double a = (double)p * inv_freq;
+      out[(size_t)p * d + i] = (float)std::cos(a);
+      out[(size_t)p * d + half + i] = (float)std::sin(a);
+    }
+  }
+  return BEAM_OK;
+}
+
+int beam_check(void* stream) {
+  int rc = device_ready();
+  if (rc) return rc;
+  hipError_t e = hipStreamSynchronize(S_(stream));
+  if (e != hipSuccess) return fail(BEAM_E_HIP, "beam_check: %s", hipGetErrorString(e));
+  const int f = beam::gemv_read_clear_err() | beam::qk_read_clear_err() |
+                beam::attn_read_clear_err();
+  if (f < 0) return fail(BEAM_E_HIP, "beam_check: reading the device flags failed");
+  if (f)
+    return fail(BEAM_E_DEVICE, "beam_check: device check tripped:%s%s%s",
+                (f & 1) ? " position outside the cache" : "",
+                (f & 2) ? " sequence slot outside the cache" : "",
+                (f & 4) ? " expert id outside [0, E)" : "");
+  return BEAM_OK;
+}
+
+}  // extern "C"

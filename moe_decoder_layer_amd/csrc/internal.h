@@ -1,0 +1,51 @@
+// Host-side launchers of the libbeamlayer kernels (internal interface between
+// the C ABI in abi.cpp and the kernel translation units). Each launcher only
+// enqueues work on `st` and returns 0, or -1 when a launch fails.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <algorithm>
+
+namespace beam {
+
+int launch_boundary(int T, int D, const uint16_t* y, const uint16_t* w_post, uint16_t* h,
+                    const uint16_t* w_pre, uint16_t* x_out, int n, float eps, hipStream_t st);
+
+int launch_gemv_qkvg(int T, int N, int K, int Nqkv, const uint16_t* W, const uint16_t* X,
+                     uint16_t* qkv, uint16_t* g_out, hipStream_t st);
+int launch_gemv_gate_oproj(int T, int N, int K, int hd, const uint16_t* W, const uint16_t* O,
+                           const uint16_t* G, const uint16_t* bgate, uint16_t* Y,
+                           hipStream_t st);
+int launch_expert_w13(int T, int D, int F, int E, int topk, int spt, const uint16_t* w13,
+                      const uint16_t* shared_w13, const int32_t* idx, const uint16_t* X,
+                      uint16_t* act, hipStream_t st);
+int launch_expert_w2(int T, int D, int F, int E, int topk, int spt, const uint16_t* w2,
+                     const uint16_t* shared_w2, const int32_t* idx, const float* wts,
+                     const uint16_t* act, uint16_t* Y, hipStream_t st);
+
+int launch_qk_epilogue(int T, int Hq, int Hkv, int hd, const uint16_t* qkv, const uint16_t* wq,
+                       const uint16_t* wk, const int32_t* pos, const int32_t* seq, int mode,
+                       const float* rope_cs, uint16_t* q_out, void* kc, void* vc, int fp8,
+                       float k_scale, float v_scale, int S, int Lmax, float eps,
+                       hipStream_t st);
+
+void attn_plan(int T, int Hkv, int span, int* tpw, int* nch);
+int attn_nch_bound(int T, int Hkv, int span);
+int launch_attn_decode(int T, int Hq, int Hkv, int hd, int swa, int window, int fp8,
+                       const uint16_t* q, const int32_t* pos, const int32_t* seq,
+                       const void* kc, const void* vc, float k_scale, float v_scale, int S,
+                       int Lmax, const float* sink, uint16_t* o, int span, float* part,
+                       hipStream_t st);
+
+int launch_router(int T, int E, int D, int ng, int tg, int K, float route_scale,
+                  const uint16_t* X, const float* Wr, const float* bcorr, float* logits,
+                  int32_t* idx, float* w, hipStream_t st);
+
+// device-side check flags (read and cleared by beam_check)
+int gemv_read_clear_err();
+int qk_read_clear_err();
+int attn_read_clear_err();
+
+}  // namespace beam

@@ -1,0 +1,286 @@
+// Decode-shaped GQA attention over the KV cache ("Reflection Beam 1.0 on
+// vLLM", Attention section: 48 query heads share 8 kv heads, head dim 128;
+// SWA layers see the last 512 positions, NoPE layers all of them).
+//
+// Split-K ("flash decoding"): workgroup (chunk c, kv head j, token t) covers
+// 256*tpw keys of the token's visible range, each of its 4 waves a run of tpw
+// tiles of 64 keys. Per tile and wave, on the matrix cores:
+//   S^T[key][head] = K[key][:] . Q[head][:]   16x16x32 bf16 MFMA, the GQA group
+//                                             (<= 16 query heads) is the N axis
+//   O^T[dim][head] += V^T[dim][key] . P^T[key][head]
+// With S^T in the C layout, lane l owns query head l%16 for 16 keys, so the
+// online-softmax state (m, l) of a head is lane-local up to two xor shuffles,
+// and the probabilities a lane holds are exactly the keys it needs as the B
+// operand of the P.V product (no LDS round trip). V is stored transposed in
+// the cache so each lane's 4-key runs of one dim are contiguous.
+// fp8 caches are widened to bf16 exactly with gfx950's packed conversion; the
+// per-tensor scales are applied to the scores (k) and the output (v).
+// Each wave's (m, l, O) is merged in LDS; one fp32 record per (t, head, c) goes
+// to the workspace and attn_merge_kernel combines the chunks.
+#include "common.h"
+#include "internal.h"
+
+namespace beam {
+
+BEAM_ERR_FLAG_DECL(attn)
+BEAM_ERR_FLAG_READER(attn)
+
+template <int HD, bool FP8, bool SWA>
+__global__ __launch_bounds__(256) void attn_decode_partial_kernel(
+    const uint16_t* __restrict__ q, const int32_t* __restrict__ pos,
+    const int32_t* __restrict__ seq, const void* __restrict__ kc, const void* __restrict__ vc,
+    int S, int Lmax, int Hq, int Hkv, int window, int tpw, float score_scale, int nch_stride,
+    float* __restrict__ part) {
+  constexpr int KS = HD / 32;  // k-steps of the score product
+  constexpr int DT = HD / 16;  // 16-dim tiles of the output
+  constexpr int GD = HD / 4;   // dims each lane group covers in the score product
+  __shared__ float sm_m[4][16], sm_l[4][16];
+  __shared__ float sm_o[4][16][HD + 4];
+
+  const int c = blockIdx.x, j = blockIdx.y, t = blockIdx.z;
+  const int grp = Hq / Hkv;
+  const int p = pos[t], s = seq[t];
+  if (p < 0 || p >= Lmax || s < 0 || s >= S) {
+    if (c == 0 && j == 0 && threadIdx.x == 0) BEAM_RAISE(attn, p < 0 || p >= Lmax ? ERR_POS : ERR_SEQ);
+    return;
+  }
+  const int lo = SWA ? max(0, p - window + 1) : 0;
+  const int lo_al = lo & ~63;
+  const int CK = 256 * tpw;
+  const int nch = (p + 1 - lo_al + CK - 1) / CK;
+  if (c >= nch) return;
+
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int g = lane >> 4, col = lane & 15;
+
+  bf16x8 qf[KS];
+  if (col < grp) {
+    const uint16_t* qp = q + ((size_t)t * Hq + j * grp + col) * HD + g * GD;
+#pragma unroll
+    for (int i = 0; i < KS; ++i) qf[i] = as_bf16x8(ld16(qp + i * 8));
+  } else {
+#pragma unroll
+    for (int i = 0; i < KS; ++i) qf[i] = bf16x8{};
+  }
+
+  const size_t krow0 = ((size_t)s * Hkv + j) * (size_t)Lmax;  // K row of position 0
+  const size_t vrow0 = ((size_t)s * Hkv + j) * (size_t)HD;    // V^T row of dim 0
+  float m = -INFINITY, lsum = 0.f;
+  f32x4 o[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int tile0 = (lo_al >> 6) + (c * 4 + wave) * tpw;
+  for (int it = 0; it < tpw; ++it) {
+    const int kb = (tile0 + it) << 6;
+    if (kb > p) break;
+    f32x4 sacc[4];
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      sacc[st] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const size_t kr = (krow0 + kb + st * 16 + col) * HD + g * GD;
+#pragma unroll
+      for (int i = 0; i < KS; ++i) {
+        bf16x8 kf;
+        if constexpr (FP8) {
+          kf = e4m3x8_to_bf16x8(*reinterpret_cast<const uint2*>((const uint8_t*)kc + kr + i * 8));
+        } else {
+          kf = as_bf16x8(ld16((const uint16_t*)kc + kr + i * 8));
+        }
+        sacc[st] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[i], sacc[st], 0, 0, 0);
+      }
+    }
+    // scores (log2 domain), window mask, online softmax
+    float mx = -INFINITY;
+#pragma unroll
+    for (int st = 0; st < 4; ++st)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int key = kb + st * 16 + 4 * g + r;
+        float v = sacc[st][r] * score_scale;
+        v = (key < lo || key > p) ? -INFINITY : v;
+        sacc[st][r] = v;
+        mx = fmaxf(mx, v);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float mn = fmaxf(m, mx);  // finite: each visited tile holds a key in [lo, p]
+    const float alpha = exp2f(m - mn);
+    float rs = 0.f;
+#pragma unroll
+    for (int st = 0; st < 4; ++st)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float pr = exp2f(sacc[st][r] - mn);
+        sacc[st][r] = pr;
+        rs += pr;
+      }
+    rs += __shfl_xor(rs, 16, 64);
+    rs += __shfl_xor(rs, 32, 64);
+    lsum = lsum * alpha + rs;
+    m = mn;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
+
+    const bool edge = (kb < lo) || (kb + 63 > p);
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh) {
+      const bf16x8 pf = {(__bf16)sacc[2 * kh][0],     (__bf16)sacc[2 * kh][1],
+                         (__bf16)sacc[2 * kh][2],     (__bf16)sacc[2 * kh][3],
+                         (__bf16)sacc[2 * kh + 1][0], (__bf16)sacc[2 * kh + 1][1],
+                         (__bf16)sacc[2 * kh + 1][2], (__bf16)sacc[2 * kh + 1][3]};
+      const int key0 = kb + kh * 32 + 4 * g, key1 = key0 + 16;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const size_t vr = (vrow0 + dt * 16 + col) * (size_t)Lmax;
+        bf16x8 vf;
+        if constexpr (FP8) {
+          const uint8_t* vb = (const uint8_t*)vc + vr;
+          const bf16x4 a = e4m3x4_to_bf16x4(*reinterpret_cast<const uint32_t*>(vb + key0));
+          const bf16x4 b = e4m3x4_to_bf16x4(*reinterpret_cast<const uint32_t*>(vb + key1));
+          vf = bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+        } else {
+          const uint16_t* vb = (const uint16_t*)vc + vr;
+          const uint2 a = *reinterpret_cast<const uint2*>(vb + key0);
+          const uint2 b = *reinterpret_cast<const uint2*>(vb + key1);
+          vf = __builtin_bit_cast(bf16x8, uint4{a.x, a.y, b.x, b.y});
+        }
+        if (edge) {  // keys outside [lo, p] may hold anything: zero them
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const int key = (i < 4 ? key0 + i : key1 + i - 4);
+            if (key < lo || key > p) vf[i] = (__bf16)0.0f;
+          }
+        }
+        o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf, o[dt], 0, 0, 0);
+      }
+    }
+  }
+
+  if (g == 0) {
+    sm_m[wave][col] = m;
+    sm_l[wave][col] = lsum;
+  }
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sm_o[wave][col][dt * 16 + 4 * g + r] = o[dt][r];
+  __syncthreads();
+  for (int i = threadIdx.x; i < grp * HD; i += 256) {
+    const int hh = i / HD, dim = i - hh * HD;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, sm_m[w][hh]);
+    float L = 0.f, O = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float e = (sm_m[w][hh] == -INFINITY) ? 0.f : exp2f(sm_m[w][hh] - M);
+      L += e * sm_l[w][hh];
+      O += e * sm_o[w][hh][dim];
+    }
+    float* rec = part + (((size_t)t * Hq + j * grp + hh) * nch_stride + c) * (HD + 4);
+    if (dim == 0) {
+      rec[0] = M;
+      rec[1] = L;
+    }
+    rec[4 + dim] = O;
+  }
+}
+
+// Combine the chunks of one (token, head): o = sum_c 2^(m_c-M) O_c / sum_c 2^(m_c-M) l_c.
+// An attention sink adds 2^(sink*log2e - M) to the denominator only.
+template <int HD>
+__global__ __launch_bounds__(64) void attn_merge_kernel(
+    const float* __restrict__ part, const int32_t* __restrict__ pos,
+    const int32_t* __restrict__ seq, int S, int Lmax, int Hq, int window, int swa, int tpw,
+    int nch_stride, const float* __restrict__ sink, float v_scale, uint16_t* __restrict__ o) {
+  const int h = blockIdx.x, t = blockIdx.y, lane = threadIdx.x;
+  uint16_t* out = o + ((size_t)t * Hq + h) * HD;
+  const int p = pos[t], s = seq[t];
+  if (p < 0 || p >= Lmax || s < 0 || s >= S) {
+    for (int d = lane; d < HD; d += 64) out[d] = 0;
+    return;
+  }
+  const int lo = swa ? max(0, p - window + 1) : 0;
+  const int lo_al = lo & ~63;
+  const int CK = 256 * tpw;
+  const int nch = (p + 1 - lo_al + CK - 1) / CK;
+  const float* rec0 = part + ((size_t)t * Hq + h) * nch_stride * (HD + 4);
+  float M = -INFINITY;
+  for (int c = 0; c < nch; ++c) M = fmaxf(M, rec0[(size_t)c * (HD + 4)]);
+  const float sl2 = sink ? sink[h] * 1.4426950408889634f : -INFINITY;
+  M = fmaxf(M, sl2);
+  float L = sink ? exp2f(sl2 - M) : 0.f;
+  float acc[HD / 64 > 0 ? HD / 64 : 1] = {};
+  for (int c = 0; c < nch; ++c) {
+    const float* rec = rec0 + (size_t)c * (HD + 4);
+    const float e = exp2f(rec[0] - M);
+    L += e * rec[1];
+#pragma unroll
+    for (int k = 0; k < (HD + 63) / 64; ++k) {
+      const int d = lane + 64 * k;
+      if (d < HD) acc[k] += e * rec[4 + d];
+    }
+  }
+  const float inv = v_scale / L;
+#pragma unroll
+  for (int k = 0; k < (HD + 63) / 64; ++k) {
+    const int d = lane + 64 * k;
+    if (d < HD) out[d] = f2bf(acc[k] * inv);
+  }
+}
+
+void attn_plan(int T, int Hkv, int span, int* tpw, int* nch) {
+  const int tiles = (span + 63) / 64;
+  const int target = std::max(1, 2048 / std::max(1, Hkv * T));
+  int w = (tiles + 4 * target - 1) / (4 * target);
+  w = std::min(std::max(w, 1), 64);
+  *tpw = w;
+  *nch = std::max(1, (tiles + 4 * w - 1) / (4 * w));
+}
+
+int attn_nch_bound(int T, int Hkv, int span) {
+  const int tiles = (span + 63) / 64;
+  const int target = std::max(1, 2048 / std::max(1, Hkv * T));
+  return std::max(std::max(1, std::min(target, (tiles + 3) / 4)), (tiles + 255) / 256);
+}
+
+int launch_attn_decode(int T, int Hq, int Hkv, int hd, int swa, int window, int fp8,
+                       const uint16_t* q, const int32_t* pos, const int32_t* seq,
+                       const void* kc, const void* vc, float k_scale, float v_scale, int S,
+                       int Lmax, const float* sink, uint16_t* o, int span, float* part,
+                       hipStream_t st) {
+  int tpw, nch;
+  attn_plan(T, Hkv, span, &tpw, &nch);
+  const float score_scale = k_scale / sqrtf((float)hd) * 1.4426950408889634f;
+  const dim3 grid(nch, Hkv, T);
+#define PART(HD_, F8, SW)                                                                    \
+  hipLaunchKernelGGL((attn_decode_partial_kernel<HD_, F8, SW>), grid, dim3(256), 0, st, q,  \
+                     pos, seq, kc, vc, S, Lmax, Hq, Hkv, window, tpw, score_scale, nch, part)
+#define BY_MODE(HD_)                                    \
+  if (fp8) {                                           \
+    if (swa) PART(HD_, true, true); else PART(HD_, true, false);   \
+  } else {                                             \
+    if (swa) PART(HD_, false, true); else PART(HD_, false, false); \
+  }
+  if (hd == 128) { BY_MODE(128) }
+  else if (hd == 64) { BY_MODE(64) }
+  else { BY_MODE(32) }
+#undef BY_MODE
+#undef PART
+  if (hipGetLastError() != hipSuccess) return -1;
+  const dim3 mg(Hq, T);
+  const float vs = fp8 ? v_scale : 1.0f;
+  if (hd == 128)
+    hipLaunchKernelGGL((attn_merge_kernel<128>), mg, dim3(64), 0, st, part, pos, seq, S, Lmax, Hq,
+                       window, swa, tpw, nch, sink, vs, o);
+  else if (hd == 64)
+    hipLaunchKernelGGL((attn_merge_kernel<64>), mg, dim3(64), 0, st, part, pos, seq, S, Lmax, Hq,
+                       window, swa, tpw, nch, sink, vs, o);
+  else
+    hipLaunchKernelGGL((attn_merge_kernel<32>), mg, dim3(64), 0, st, part, pos, seq, S, Lmax, Hq,
+                       window, swa, tpw, nch, sink, vs, o);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+}  // namespace beam

@@ -194,7 +194,8 @@ def attention(dims, q, pos, seq, cache: KVCache, mode: str, sink=None) -> np.nda
         lo = max(0, p - dims.window + 1) if mode == "swa" else 0
         for h in range(dims.Hq):
             j = h // grp
-            K, V = cache.keys(int(seq[t]), j, lo, p)
+            if h % grp == 0:                      # one fetch per kv head
+                K, V = cache.keys(int(seq[t]), j, lo, p)
             z = K @ q[t, h] / math.sqrt(dims.d)
             m = z.max() if sink is None else max(z.max(), float(sink[h]))
             e = np.exp(z - m)

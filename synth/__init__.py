@@ -132,7 +132,7 @@ def make_dense(dims: Dims, seed: int, layer: int):
 
 
 def make_params(dims: Dims, seed: int, layer: int, experts: bool = True,
-                dense: bool = False) -> dict:
+                dense: bool = False, projections: bool = True) -> dict:
     """All small per-layer tensors, plus every expert when experts=True.
 
     Gains for the layer's four sandwich norms and the next layer's pre-norm,
@@ -145,10 +145,11 @@ def make_params(dims: Dims, seed: int, layer: int, experts: bool = True,
         p[name] = uniform_bf16((D,), 0.5, 1.5, seed, layer, name)
     p["w_qnorm"] = uniform_bf16((d,), 0.5, 1.5, seed, layer, "w_qnorm")
     p["w_knorm"] = uniform_bf16((d,), 0.5, 1.5, seed, layer, "w_knorm")
-    p["w_qkvg"] = normal_bf16((dims.qkvg_rows, D), 0.02, seed, layer, "w_qkvg")
+    if projections:
+        p["w_qkvg"] = normal_bf16((dims.qkvg_rows, D), 0.02, seed, layer, "w_qkvg")
+        p["w_o"] = normal_bf16((D, dims.Hq * d), 0.02, seed, layer, "w_o")
     if dims.G:
         p["b_gate"] = uniform_bf16((dims.Hq,), -1.0, 1.0, seed, layer, "b_gate")
-    p["w_o"] = normal_bf16((D, dims.Hq * d), 0.02, seed, layer, "w_o")
     g = rng(seed, layer, "w_r")
     p["w_r"] = (g.standard_normal((dims.E, D), dtype=np.float32) * np.float32(0.02))
     g = rng(seed, layer, "b_corr")
@@ -199,3 +200,48 @@ def make_kv_prior(dims: Dims, S: int, ctx: int, kv: str, seed: int, layer: int):
 
 def with_dims(cfg: Config, **kw) -> Config:
     return replace(cfg, dims=replace(cfg.dims, **kw))
+
+
+# ---------------------------------------------------------------------------
+# Full-size tensors are drawn on the device with torch's counter-based
+# generator (seeded from the same key scheme); the oracle reads back only the
+# slices it needs.
+def _torch_gen(seed: int, key, device):
+    g = torch.Generator(device=device)
+    g.manual_seed(((seed & 0xFFFFFFFF) << 32) ^ _key(*key))
+    return g
+
+
+def torch_normal_bf16(shape, std, seed, *key, device="cuda", out=None):
+    """N(0, std) drawn in fp32 on `device`, cast to bf16; returned as int16 bits."""
+    g = _torch_gen(seed, key, device)
+    t = (torch.randn(shape, generator=g, device=device, dtype=torch.float32) * std)
+    t = t.to(torch.bfloat16).view(torch.int16)
+    if out is not None:
+        out.copy_(t)
+        return out
+    return t
+
+
+def torch_uniform_bf16(shape, lo, hi, seed, *key, device="cuda"):
+    g = _torch_gen(seed, key, device)
+    t = torch.rand(shape, generator=g, device=device, dtype=torch.float32) * (hi - lo) + lo
+    return t.to(torch.bfloat16).view(torch.int16)
+
+
+def torch_kv_prior(dims: Dims, S: int, ctx: int, kv: str, seed: int, layer: int, device="cuda"):
+    """Device version of make_kv_prior: logical K, V [S][Hkv][ctx][d] as int16 bf16
+    bits or uint8 e4m3fn codes, plus the two scales."""
+    out = []
+    for name in ("k", "v"):
+        g = _torch_gen(seed, (layer, "kv_prior", name), device)
+        a = torch.randn((S, dims.Hkv, ctx, dims.d), generator=g, device=device,
+                        dtype=torch.float32)
+        if kv == "bf16":
+            out += [a.to(torch.bfloat16).view(torch.int16), 1.0]
+        else:
+            scale = float(a.abs().max()) / 448.0
+            q = (a / scale).clamp_(-448.0, 448.0).to(torch.float8_e4m3fn).view(torch.uint8)
+            out += [q, scale]
+        del a
+    return out[0], out[2], out[1], out[3]

@@ -1,0 +1,141 @@
+"""The C-ABI library: loads, exports what the header declares, and rejects bad
+arguments on the host before any HIP call (no GPU needed)."""
+import ctypes
+
+import numpy as np
+import pytest
+import torch
+
+import moe_decoder_layer_amd as B
+import synth
+
+NO_GPU = not torch.cuda.is_available()
+# Fake device addresses are only ever passed to calls that must fail
+# validation (or find no device); never run these where a GPU is present.
+cpu_only = pytest.mark.skipif(not NO_GPU, reason="fake-pointer checks run on GPU-less hosts only")
+
+A = 0x10000          # a 16-byte aligned fake address
+MIS = 0x10002        # misaligned
+
+
+def test_library_exports_every_declared_symbol():
+    names = B.header_functions()
+    assert len(names) == 13
+    L = ctypes.CDLL(B.LIB_PATH)
+    for n in names:
+        assert hasattr(L, n), n
+    assert B.beam_version() == 100
+
+
+def _dims(i=0, **kw):
+    d = synth.with_dims(synth.config(i), **kw).dims
+    return B.dims_from(d)
+
+
+def _rc(name, *args):
+    return getattr(B.lib(), name)(*args)
+
+
+@cpu_only
+def test_boundary_validation_and_nodev():
+    d = _dims()
+    by = ctypes.byref(d)
+    assert _rc("beam_boundary_norm_residual", by, 1, A, A, None, A, A, 5, None) == -1
+    assert _rc("beam_boundary_norm_residual", None, 1, A, A, A, A, A, 5, None) == -1
+    assert _rc("beam_boundary_norm_residual", by, 0, A, A, A, A, A, 5, None) == -2
+    assert _rc("beam_boundary_norm_residual", by, 1, A, A, A, A, A, -1, None) == -2
+    assert _rc("beam_boundary_norm_residual", by, 1, MIS, A, A, A, A, 5, None) == -4
+    bad = _dims(D=250)
+    assert _rc("beam_boundary_norm_residual", ctypes.byref(bad), 1, A, A, A, A, A, 5, None) == -3
+    assert _rc("beam_boundary_norm_residual", by, 1, A, A, A, A, A, 5, None) == -7
+    assert "device" in B.beam_last_error()
+
+
+@cpu_only
+def test_qkv_validation():
+    d = _dims()
+    by = ctypes.byref(d)
+    kv = B.kv_struct(A, A, B.BEAM_KV_BF16, 1.0, 1.0, 1, 128)
+    ws = B.beam_workspace_size(d, B.BEAM_OP_QKV, 1)
+    args = lambda **o: [by, o.get("T", 1), A, A, A, A, A, A, o.get("mode", 0),  # noqa: E731
+                        o.get("rope", A), A, A, ctypes.byref(o.get("kv", kv)), A,
+                        o.get("ws", ws), None]
+    assert _rc("beam_qk_norm_rope_ssmax_kvwrite", *args(mode=7)) == -2
+    assert _rc("beam_qk_norm_rope_ssmax_kvwrite", *args(rope=None)) == -1
+    assert _rc("beam_qk_norm_rope_ssmax_kvwrite", *args(ws=ws - 1)) == -5
+    kv8 = B.kv_struct(A, A, B.BEAM_KV_FP8_E4M3, 0.0, 1.0, 1, 128)
+    assert _rc("beam_qk_norm_rope_ssmax_kvwrite", *args(kv=kv8)) == -2
+    kvL = B.kv_struct(A, A, B.BEAM_KV_BF16, 1.0, 1.0, 1, 100)
+    assert _rc("beam_qk_norm_rope_ssmax_kvwrite", *args(kv=kvL)) == -2
+    d2 = _dims(Hkv=3)
+    a2 = args()
+    a2[0] = ctypes.byref(d2)
+    assert _rc("beam_qk_norm_rope_ssmax_kvwrite", *a2) == -2
+    d3 = _dims(d=48)
+    a3 = args()
+    a3[0] = ctypes.byref(d3)
+    assert _rc("beam_qk_norm_rope_ssmax_kvwrite", *a3) == -3
+    assert _rc("beam_qk_norm_rope_ssmax_kvwrite", *args()) == -7
+
+
+@cpu_only
+def test_attention_router_moe_validation():
+    d = _dims()
+    by = ctypes.byref(d)
+    kv = B.kv_struct(A, A, B.BEAM_KV_BF16, 1.0, 1.0, 1, 128)
+    ws = B.beam_workspace_size(d, B.BEAM_OP_ATTN_NOPE, 1, 65)
+    assert _rc("beam_attn_nope_ssmax", by, 1, A, A, A, ctypes.byref(kv), None, A, 128, A, ws,
+               None) == -2                                     # max_pos >= Lmax
+    assert _rc("beam_attn_nope_ssmax", by, 1, A, A, A, ctypes.byref(kv), None, A, 64, A, 16,
+               None) == -5
+    assert _rc("beam_attn_nope_ssmax", by, 1, A, A, A, ctypes.byref(kv), None, A, 64, A, ws,
+               None) == -7
+    dw = _dims(window=0)
+    assert _rc("beam_attn_swa", ctypes.byref(dw), 1, A, A, A, ctypes.byref(kv), None, A, 64, A,
+               ws, None) == -2
+    # router: topk larger than the kept groups can hold
+    dr = _dims(topk=9)
+    assert _rc("beam_router_fp32_grouped_topk", ctypes.byref(dr), 1, A, A, None, A, A, A, None,
+               0, None) == -2
+    dr = _dims(E=15)
+    assert _rc("beam_router_fp32_grouped_topk", ctypes.byref(dr), 1, A, A, None, A, A, A, None,
+               0, None) == -2
+    assert _rc("beam_router_fp32_grouped_topk", by, 1, A, A, None, A, A, None, A, 16,
+               None) == -5
+    assert _rc("beam_router_fp32_grouped_topk", by, 1, A, A, None, A, A, A, None, 0, None) == -7
+    wsm = B.beam_workspace_size(d, B.BEAM_OP_MOE, 1)
+    assert _rc("beam_moe_swiglu_combine", by, 1, A, A, A, A, A, A, None, A, A, wsm, None) == -1
+    assert _rc("beam_moe_swiglu_combine", by, 1, A, A, A, A, A, None, None, A, A, wsm - 256,
+               None) == -5
+    assert _rc("beam_moe_swiglu_combine", by, 1, A, A, A, A, A, None, None, A, A, wsm,
+               None) == -7
+    assert _rc("beam_dense_swiglu", 1, 256, 100, A, A, A, A, A, 1 << 20, None) == -2
+    assert _rc("beam_dense_swiglu", 1, 256, 512, A, A, A, A, A, 1 << 20, None) == -7
+    assert _rc("beam_out_gate", by, 1, A, None, A, A, A, None, 0, None) == -1
+    assert _rc("beam_out_gate", by, 1, A, A, A, A, A, None, 0, None) == -7
+
+
+def test_workspace_sizes():
+    d = _dims(1)
+    assert B.beam_workspace_size(d, B.BEAM_OP_QKV, 1) >= (48 + 16) * 128 * 2
+    a = B.beam_workspace_size(d, B.BEAM_OP_ATTN_NOPE, 1, 100001)
+    s = B.beam_workspace_size(d, B.BEAM_OP_ATTN_SWA, 1, 100001)
+    assert a > s > 0
+    # monotone in the context bound
+    sizes = [B.beam_workspace_size(d, B.BEAM_OP_ATTN_NOPE, 1, c) for c in range(1000, 200000, 997)]
+    assert all(x <= y for x, y in zip(sizes, sizes[1:]))
+    with pytest.raises(B.BeamError):
+        B.beam_workspace_size(d, 99, 1)
+
+
+def test_rope_table_host_helper():
+    L, dd, theta = 300, 32, 1e4
+    out = np.zeros((L, dd), np.float32)
+    B.beam_rope_table(out, L, dd, theta)
+    p = np.arange(L)[:, None]
+    i = np.arange(dd // 2)[None, :]
+    ang = p * theta ** (-2.0 * i / dd)
+    np.testing.assert_array_equal(out[:, :dd // 2], np.cos(ang).astype(np.float32))
+    np.testing.assert_array_equal(out[:, dd // 2:], np.sin(ang).astype(np.float32))
+    with pytest.raises(B.BeamError):
+        B.beam_rope_table(out, L, 31, theta)

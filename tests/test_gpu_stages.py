@@ -1,0 +1,288 @@
+"""Per-call parity of the HIP path against the oracle, each call fed the same
+seeded inputs (GPU)."""
+import numpy as np
+import pytest
+import torch
+
+import moe_decoder_layer_amd as B
+import synth
+from beamrun import (Cache, Params, assert_rms_close, bits_f64, check_routing, code_pos, dev,
+                     host_bits, rope_table, ws)
+from oracle import layer as L
+from oracle.numerics import e4m3_quantize, round_bf16
+
+pytestmark = pytest.mark.gpu
+
+CFG0 = synth.config(0).dims
+BEAM = synth.config(1).dims
+I16 = dict(dtype=torch.int16, device="cuda")
+
+
+def _dims(base, **kw):
+    return synth.with_dims(synth.Config("", base), **kw).dims
+
+
+# ------------------------------------------------------------------ boundary
+@pytest.mark.parametrize("D,T", [(256, 1), (256, 37), (5120, 1), (5120, 600)])
+@pytest.mark.parametrize("case", ["entry", "n5", "n1", "plain"])
+def test_boundary(D, T, case):
+    dims = _dims(CFG0, D=D)
+    h = synth.make_h((T, D), 1, "bh", D, T)
+    y = synth.make_h((T, D), 1, "by", D, T)
+    wp = synth.uniform_bf16((D,), 0.5, 1.5, 1, "wp", D)
+    wn = synth.uniform_bf16((D,), 0.5, 1.5, 1, "wn", D)
+    hd, x = dev(h), torch.empty((T, D), **I16)
+    if case == "entry":
+        B.beam_boundary_norm_residual(dims, T, None, None, hd, dev(wn), x, 0)
+        h_ref, x_ref = L.boundary(None, h, None, wn, 0, dims.eps)
+    elif case == "plain":
+        B.beam_boundary_norm_residual(dims, T, dev(y), None, hd, dev(wn), x, 0)
+        h_ref, x_ref = L.boundary(y, h, None, wn, 0, dims.eps)
+    else:
+        n = 5 if case == "n5" else 1
+        B.beam_boundary_norm_residual(dims, T, dev(y), dev(wp), hd, dev(wn), x, n)
+        h_ref, x_ref = L.boundary(y, h, wp, wn, n, dims.eps)
+    B.beam_check()
+    hg, xg = bits_f64(host_bits(hd)), bits_f64(host_bits(x))
+    assert_rms_close(hg, h_ref, "h")
+    assert_rms_close(xg, x_ref, "x")
+    assert np.mean(hg == h_ref) > 0.97 and np.mean(xg == x_ref) > 0.97
+
+
+# ------------------------------------------------------------------ q/k + cache write
+@pytest.mark.parametrize("base,T,pos0", [(CFG0, 1, 64), (CFG0, 32, 64), (BEAM, 1, 3000),
+                                         (BEAM, 3, 17)])
+@pytest.mark.parametrize("mode", ["swa", "nope"])
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_qk_norm_kvwrite(base, T, pos0, mode, kv):
+    dims = base
+    Lmax = 4096 if dims.D > 1000 else 128
+    P = Params(dims, 0, 3, moe=False)
+    x = synth.make_h((T, dims.D), 2, "qx", T)
+    pos = np.arange(pos0, pos0 + T, dtype=np.int32)
+    seq = (np.arange(T) % 2).astype(np.int32)
+    cache = Cache(dims, 2, Lmax, kv, 0.013, 0.021)
+    q = torch.empty((T, dims.Hq, dims.d), **I16)
+    g = torch.empty((T, dims.G), **I16)
+    rope = rope_table(Lmax, dims.d, dims.theta) if mode == "swa" else None
+    B.beam_qk_norm_rope_ssmax_kvwrite(
+        dims, T, dev(x), P.t["w_qkvg"], P.t["w_qnorm"], P.t["w_knorm"], dev(pos), dev(seq),
+        B.BEAM_SWA_ROPE if mode == "swa" else B.BEAM_NOPE_SSMAX, rope, q, g, cache.struct(),
+        ws(dims, B.BEAM_OP_QKV, T))
+    B.beam_check()
+    qkvg = L.qkvg_projection(x, P.np("w_qkvg"))
+    qr, kr, vr, gr = L.split_qkvg(dims, qkvg)
+    qn, kn = L.qk_norm_position(dims, qr, kr, pos, mode, P.np("w_qnorm"), P.np("w_knorm"))
+    assert_rms_close(bits_f64(host_bits(q)), round_bf16(qn), "q")
+    assert_rms_close(bits_f64(host_bits(g)), gr, "g")
+    K = cache.K.cpu().numpy()
+    V = cache.V.cpu().numpy()
+    for t in range(T):
+        s, p = seq[t], pos[t]
+        kg, vg = K[s, :, p, :], V[s, :, :, p]
+        if kv == "bf16":
+            assert_rms_close(bits_f64(kg.view(np.uint16)), round_bf16(kn[t]), "k")
+            np.testing.assert_array_equal(vg.view(np.uint16), _bits(vr[t]))
+        else:
+            for got, ref, sc in ((kg, kn[t], 0.013), (vg, vr[t], 0.021)):
+                assert np.max(np.abs(code_pos(got) - code_pos(e4m3_quantize(ref, sc)))) <= 1
+    # nothing outside the written slots changed
+    mask = np.ones(K.shape[:3], bool)
+    for t in range(T):
+        mask[seq[t], :, pos[t]] = False
+    fill = 0x7FC0 if kv == "bf16" else 0x7F
+    assert np.all(K.view(np.uint16 if kv == "bf16" else np.uint8)[mask] == fill)
+
+
+def _bits(v):
+    from oracle.numerics import f64_to_bf16_bits
+    return f64_to_bf16_bits(v)
+
+
+# ------------------------------------------------------------------ attention
+def _needle_cache(dims, Lmax, fill, kv, q, pos, seq, needles, seed):
+    """Random N(0,1) prior over [0, fill) plus keys aligned with the token's
+    first query head of each group at the needle positions (scores far above
+    the rest, so a dropped or misplaced key changes the output)."""
+    S = int(seq.max()) + 1
+    Kp, Vp, ks, vs = synth.torch_kv_prior(dims, S, fill, kv, seed, 7)
+    cache = Cache(dims, S, Lmax, kv, ks, vs)
+    cache.fill_prior(Kp, Vp)
+    grp = dims.Hq // dims.Hkv
+    qf = bits_f64(host_bits(q))
+    for t, p in enumerate(pos):
+        for u in needles(int(p)):
+            for j in range(dims.Hkv):
+                qh = qf[t, j * grp]
+                kvec = qh * (6.0 * np.sqrt(dims.d) / max(np.dot(qh, qh), 1e-6))
+                if kv == "bf16":
+                    cache.K[seq[t], j, u] = dev(_bits(kvec))
+                else:
+                    cache.K[seq[t], j, u] = torch.from_numpy(e4m3_quantize(kvec, ks)).cuda()
+    return cache
+
+
+@pytest.mark.parametrize("case", ["tiny", "beam_multi", "beam_long"])
+@pytest.mark.parametrize("mode", ["swa", "nope"])
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_attention(case, mode, kv):
+    if case == "tiny":
+        dims, Lmax, fill = CFG0, 192, 128
+        pos = np.array([0, 15, 16, 63, 64, 100, 127], np.int32)
+    elif case == "beam_multi":
+        dims, Lmax, fill = BEAM, 4096, 3000
+        pos = np.array([0, 511, 512, 1000, 2047, 2999], np.int32)
+    else:
+        dims, Lmax, fill = BEAM, 100352, 100001
+        pos = np.array([100000], np.int32)
+    T = len(pos)
+    seq = (np.arange(T) % 2).astype(np.int32) if case != "beam_long" else np.zeros(T, np.int32)
+    q = dev(synth.make_h((T, dims.Hq, dims.d), 3, "aq", case))
+    W = dims.window
+
+    def needles(p):
+        c = {0, p, max(0, p - 1), max(0, p - W + 1), max(0, p - W), (p // 256) * 256,
+             max(0, (p // 1024) * 1024 - 1)}
+        return sorted(u for u in c if u <= p)
+
+    cache = _needle_cache(dims, Lmax, fill, kv, q, pos, seq, needles, 4)
+    o = torch.empty((T, dims.Hq, dims.d), **I16)
+    sink = None
+    mp = int(pos.max())
+    fn = B.beam_attn_swa if mode == "swa" else B.beam_attn_nope_ssmax
+    op = B.BEAM_OP_ATTN_SWA if mode == "swa" else B.BEAM_OP_ATTN_NOPE
+    fn(dims, T, q, dev(pos), dev(seq), cache.struct(), sink, o, mp, ws(dims, op, T, mp + 1))
+    B.beam_check()
+    ref = L.attention(dims, bits_f64(host_bits(q)), pos, seq, cache.oracle(mp + 1), mode)
+    assert_rms_close(bits_f64(host_bits(o)), ref, "o")
+
+
+@pytest.mark.parametrize("mode", ["swa", "nope"])
+def test_attention_sink(mode):
+    dims = CFG0
+    pos = np.array([5, 40, 99], np.int32)
+    T = 3
+    seq = np.zeros(T, np.int32)
+    q = dev(synth.make_h((T, dims.Hq, dims.d), 3, "sq"))
+    cache = _needle_cache(dims, 128, 128, "bf16", q, pos, seq, lambda p: [], 5)
+    sink = torch.tensor([0.5, -1.0, 3.0, 8.0], dtype=torch.float32, device="cuda")
+    o = torch.empty((T, dims.Hq, dims.d), **I16)
+    fn = B.beam_attn_swa if mode == "swa" else B.beam_attn_nope_ssmax
+    op = B.BEAM_OP_ATTN_SWA if mode == "swa" else B.BEAM_OP_ATTN_NOPE
+    fn(dims, T, q, dev(pos), dev(seq), cache.struct(), sink, o, 99, ws(dims, op, T, 100))
+    B.beam_check()
+    ref = L.attention(dims, bits_f64(host_bits(q)), pos, seq, cache.oracle(100), mode,
+                      sink=sink.cpu().numpy())
+    assert_rms_close(bits_f64(host_bits(o)), ref, "o")
+
+
+# ------------------------------------------------------------------ gate + o_proj
+@pytest.mark.parametrize("base,T", [(CFG0, 1), (CFG0, 9), (BEAM, 1), (BEAM, 2)])
+def test_out_gate(base, T):
+    dims = base
+    P = Params(dims, 0, 4, moe=False)
+    o = synth.make_h((T, dims.Hq * dims.d), 5, "go", T)
+    g = synth.make_h((T, dims.G), 5, "gg", T)
+    y = torch.empty((T, dims.D), **I16)
+    B.beam_out_gate(dims, T, dev(o), dev(g), P.t["b_gate"], P.t["w_o"], y)
+    B.beam_check()
+    z = L.output_gate(dims, bits_f64(o).reshape(T, dims.Hq, dims.d), bits_f64(g), P.np("b_gate"))
+    assert_rms_close(bits_f64(host_bits(y)), L.o_proj(z, P.np("w_o")), "y")
+
+
+# ------------------------------------------------------------------ router
+@pytest.mark.parametrize("base,T", [(CFG0, 1), (CFG0, 70), (BEAM, 1), (BEAM, 4), (BEAM, 300)])
+def test_router(base, T):
+    dims = base
+    P = Params(dims, 0, 5, moe=False)
+    x = synth.make_h((T, dims.D), 6, "rx", T)
+    idx = torch.empty((T, dims.topk), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, dims.topk), dtype=torch.float32, device="cuda")
+    lg = torch.empty((T, dims.E), dtype=torch.float32, device="cuda")
+    B.beam_router_fp32_grouped_topk(dims, T, dev(x), P.t["w_r"], P.t["b_corr"], idx, w, lg)
+    B.beam_check()
+    check_routing(dims, x, P, idx.cpu().numpy(), w.cpu().numpy(), lg.cpu().numpy(), "router")
+    # without logits output (workspace path) the selection is identical
+    idx2 = torch.empty_like(idx)
+    w2 = torch.empty_like(w)
+    B.beam_router_fp32_grouped_topk(dims, T, dev(x), P.t["w_r"], P.t["b_corr"], idx2, w2, None,
+                                    ws(dims, B.BEAM_OP_ROUTER, T))
+    assert torch.equal(idx, idx2) and torch.equal(w, w2)
+
+
+# ------------------------------------------------------------------ experts
+_BEAM_P = {}
+
+
+def _beam_params():
+    if "p" not in _BEAM_P:
+        _BEAM_P["p"] = Params(BEAM, 0, 10, moe=True, device_draw=True)
+    return _BEAM_P["p"]
+
+
+@pytest.mark.parametrize("base,T", [(CFG0, 1), (CFG0, 5), (BEAM, 1), (BEAM, 2)])
+def test_moe(base, T):
+    dims = base
+    P = Params(dims, 0, 6) if dims is CFG0 else _beam_params()
+    x = synth.make_h((T, dims.D), 7, "mx", T)
+    g = np.random.default_rng(8)
+    idx = np.stack([g.choice(dims.E, dims.topk, replace=False) for _ in range(T)]).astype(np.int32)
+    w = g.uniform(0.05, 0.6, (T, dims.topk)).astype(np.float32)
+    y = torch.empty((T, dims.D), **I16)
+    B.beam_moe_swiglu_combine(dims, T, dev(x), dev(idx), dev(w), P.t["w13"], P.t["w2"], None, None,
+                              y, ws(dims, B.BEAM_OP_MOE, T))
+    B.beam_check()
+    ref = L.moe(dims, x, idx, w, P.expert)
+    assert_rms_close(bits_f64(host_bits(y)), ref, "y2")
+
+
+def test_moe_shared_expert():
+    dims = _dims(CFG0, shared=True, topk=3, n_group=1, topk_group=1)
+    P = Params(dims, 0, 6)
+    T = 3
+    x = synth.make_h((T, dims.D), 7, "msx")
+    idx = np.array([[1, 5, 9], [0, 15, 7], [3, 4, 2]], np.int32)
+    w = np.full((T, 3), 0.3, np.float32)
+    y = torch.empty((T, dims.D), **I16)
+    B.beam_moe_swiglu_combine(dims, T, dev(x), dev(idx), dev(w), P.t["w13"], P.t["w2"],
+                              P.t["shared_w13"], P.t["shared_w2"], y, ws(dims, B.BEAM_OP_MOE, T))
+    B.beam_check()
+    ref = L.moe(dims, x, idx, w, P.expert, shared=(P.np("shared_w13"), P.np("shared_w2")))
+    assert_rms_close(bits_f64(host_bits(y)), ref, "y2")
+
+
+def test_moe_bad_expert_id_is_flagged():
+    """An id outside [0, E) is skipped by the kernels' own check and reported."""
+    dims = CFG0
+    P = Params(dims, 0, 6)
+    x = synth.make_h((1, dims.D), 7, "bad")
+    idx = np.array([[1, 2, dims.E, 3]], np.int32)
+    w = np.full((1, 4), 0.5, np.float32)
+    y = torch.empty((1, dims.D), **I16)
+    B.beam_moe_swiglu_combine(dims, 1, dev(x), dev(idx), dev(w), P.t["w13"], P.t["w2"], None, None,
+                              y, ws(dims, B.BEAM_OP_MOE, 1))
+    with pytest.raises(B.BeamError) as e:
+        B.beam_check()
+    assert e.value.code == -8
+    B.beam_check()                      # flag cleared
+    ref = L.moe(dims, x, np.array([[1, 2, 3]]), w[:, :3], P.expert)
+    assert_rms_close(bits_f64(host_bits(y)), ref, "y2 without the bad slot")
+
+
+@pytest.mark.parametrize("base,T", [(CFG0, 1), (CFG0, 6), (BEAM, 1)])
+def test_dense(base, T):
+    dims = base
+    layer = 0
+    if dims is CFG0:
+        w13, w2 = synth.make_dense(dims, 0, layer)
+        w13d, w2d = dev(w13), dev(w2)
+    else:
+        w13d = synth.torch_normal_bf16((2 * dims.Fd, dims.D), 0.02, 0, layer, "dense_w13")
+        w2d = synth.torch_normal_bf16((dims.D, dims.Fd), 0.02, 0, layer, "dense_w2")
+        w13, w2 = host_bits(w13d), host_bits(w2d)
+    x = synth.make_h((T, dims.D), 9, "dx", T)
+    y = torch.empty((T, dims.D), **I16)
+    dd = _dims(dims, F=dims.Fd)
+    B.beam_dense_swiglu(T, dims.D, dims.Fd, dev(x), w13d, w2d, y, ws(dd, B.BEAM_OP_DENSE, T))
+    B.beam_check()
+    assert_rms_close(bits_f64(host_bits(y)), L.dense_ffn(x, w13, w2, dims.Fd), "y2")

@@ -205,6 +205,20 @@ int beam_moe_swiglu_combine(const beam_dims* dims, int T, const uint16_t* x,
                             const uint16_t* shared_w2, uint16_t* y, void* ws,
                             size_t ws_bytes, void* stream);
 
+/* The two phases of beam_moe_swiglu_combine, for callers that schedule them
+ * separately (beam_moe_swiglu_combine == up, then down, with act in ws):
+ *   up:   act[t][k][:] = bf16(silu(u[:F]) * u[F:]) for every routed slot k
+ *         (and slot topk for the shared expert when shared_w13 != NULL);
+ *         act [T][topk (+1)][F] bf16, caller-owned.
+ *   down: y = bf16(sum_k w[t][k] * (act[t][k] . w2[e]^T) (+ shared, weight 1)).
+ * Both read only the selected experts' rows. Device check as above. */
+int beam_moe_experts_up(const beam_dims* dims, int T, const uint16_t* x, const int32_t* idx,
+                        const uint16_t* w13, const uint16_t* shared_w13, uint16_t* act,
+                        void* stream);
+int beam_moe_experts_down(const beam_dims* dims, int T, const int32_t* idx, const float* w,
+                          const uint16_t* w2, const uint16_t* shared_w2, const uint16_t* act,
+                          uint16_t* y, void* stream);
+
 /* Dense SwiGLU MLP of the first layers ([MoE]; [Opt]/7):
  *   u = bf16(x . w13^T) (w13 [2*Fd][D], gate rows then up rows),
  *   a = bf16(silu(u[:Fd]) * u[Fd:]), y = bf16(a . w2^T) (w2 [D][Fd]).

@@ -21,7 +21,8 @@ __all__ = [
     "BeamError", "beam_dims", "beam_kv", "lib", "dims_from", "kv_struct",
     "beam_boundary_norm_residual", "beam_qk_norm_rope_ssmax_kvwrite", "beam_attn_swa",
     "beam_attn_nope_ssmax", "beam_out_gate", "beam_router_fp32_grouped_topk",
-    "beam_moe_swiglu_combine", "beam_dense_swiglu", "beam_workspace_size", "beam_rope_table",
+    "beam_moe_swiglu_combine", "beam_moe_experts_up", "beam_moe_experts_down",
+    "beam_dense_swiglu", "beam_workspace_size", "beam_rope_table",
     "beam_check", "beam_last_error", "beam_version",
     "BEAM_SWA_ROPE", "BEAM_NOPE_SSMAX", "BEAM_KV_BF16", "BEAM_KV_FP8_E4M3",
     "BEAM_OP_QKV", "BEAM_OP_ATTN_SWA", "BEAM_OP_ATTN_NOPE", "BEAM_OP_OUT_GATE",
@@ -80,6 +81,8 @@ def lib():
                                               c_size_t, P],
             "beam_moe_swiglu_combine": [POINTER(beam_dims), c_int, P, P, P, P, P, P, P, P, P,
                                         c_size_t, P],
+            "beam_moe_experts_up": [POINTER(beam_dims), c_int, P, P, P, P, P, P],
+            "beam_moe_experts_down": [POINTER(beam_dims), c_int, P, P, P, P, P, P, P],
             "beam_dense_swiglu": [c_int, c_int, c_int, P, P, P, P, P, c_size_t, P],
             "beam_rope_table": [P, c_int, c_int, c_double],
             "beam_check": [P],
@@ -202,6 +205,18 @@ def beam_moe_swiglu_combine(dims, T, x, idx, w, w13, w2, shared_w13, shared_w2, 
     wp, wb = _ws(ws)
     _call("beam_moe_swiglu_combine", ctypes.byref(d), T, _p(x), _p(idx), _p(w), _p(w13),
           _p(w2), _p(shared_w13), _p(shared_w2), _p(y), wp, wb, _s(stream))
+
+
+def beam_moe_experts_up(dims, T, x, idx, w13, shared_w13, act, stream=None):
+    d = _d(dims)
+    _call("beam_moe_experts_up", ctypes.byref(d), T, _p(x), _p(idx), _p(w13), _p(shared_w13),
+          _p(act), _s(stream))
+
+
+def beam_moe_experts_down(dims, T, idx, w, w2, shared_w2, act, y, stream=None):
+    d = _d(dims)
+    _call("beam_moe_experts_down", ctypes.byref(d), T, _p(idx), _p(w), _p(w2), _p(shared_w2),
+          _p(act), _p(y), _s(stream))
 
 
 def beam_dense_swiglu(T, D, Fd, x, w13, w2, y, ws, stream=None):

@@ -330,6 +330,57 @@ int beam_moe_swiglu_combine(const beam_dims* dims, int T, const uint16_t* x,
                   __func__);
 }
 
+int beam_moe_experts_up(const beam_dims* dims, int T, const uint16_t* x, const int32_t* idx,
+                        const uint16_t* w13, const uint16_t* shared_w13, uint16_t* act,
+                        void* stream) {
+  REQ(dims);
+  REQ(x);
+  REQ(idx);
+  REQ(w13);
+  REQ(act);
+  ALN(x);
+  ALN(w13);
+  ALN(shared_w13);
+  ALN(act);
+  SHAPE(T > 0, "%s: T <= 0", __func__);
+  SHAPE(dims->E > 0 && dims->topk > 0 && dims->F > 0, "%s: non-positive E/topk/F", __func__);
+  UNSUP(dims->D > 0 && dims->D % 8 == 0 && dims->D <= 8192,
+        "%s: D must be a positive multiple of 8 <= 8192", __func__);
+  UNSUP(dims->F % 8 == 0, "%s: F must be a multiple of 8", __func__);
+  int rc = device_ready();
+  if (rc) return rc;
+  const int spt = dims->topk + (shared_w13 ? 1 : 0);
+  return launched(beam::launch_expert_w13(T, dims->D, dims->F, dims->E, dims->topk, spt, w13,
+                                          shared_w13, idx, x, act, S_(stream)),
+                  __func__);
+}
+
+int beam_moe_experts_down(const beam_dims* dims, int T, const int32_t* idx, const float* w,
+                          const uint16_t* w2, const uint16_t* shared_w2, const uint16_t* act,
+                          uint16_t* y, void* stream) {
+  REQ(dims);
+  REQ(idx);
+  REQ(w);
+  REQ(w2);
+  REQ(act);
+  REQ(y);
+  ALN(w2);
+  ALN(shared_w2);
+  ALN(act);
+  ALN(y);
+  SHAPE(T > 0, "%s: T <= 0", __func__);
+  SHAPE(dims->E > 0 && dims->topk > 0 && dims->F > 0, "%s: non-positive E/topk/F", __func__);
+  UNSUP(dims->D > 0 && dims->D % 8 == 0 && dims->D <= 8192,
+        "%s: D must be a positive multiple of 8 <= 8192", __func__);
+  UNSUP(dims->F % 8 == 0, "%s: F must be a multiple of 8", __func__);
+  int rc = device_ready();
+  if (rc) return rc;
+  const int spt = dims->topk + (shared_w2 ? 1 : 0);
+  return launched(beam::launch_expert_w2(T, dims->D, dims->F, dims->E, dims->topk, spt, w2,
+                                         shared_w2, idx, w, act, y, S_(stream)),
+                  __func__);
+}
+
 int beam_dense_swiglu(int T, int D, int Fd, const uint16_t* x, const uint16_t* w13,
                       const uint16_t* w2, uint16_t* y, void* ws, size_t ws_bytes,
                       void* stream) {

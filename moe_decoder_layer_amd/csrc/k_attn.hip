@@ -15,6 +15,8 @@
 // the cache so each lane's 4-key runs of one dim are contiguous.
 // fp8 caches are widened to bf16 exactly with gfx950's packed conversion; the
 // per-tensor scales are applied to the scores (k) and the output (v).
+// Probabilities enter the P.V product as hi + lo bf16 pairs (two MFMAs), so
+// the only bf16 rounding of the attention path is its output.
 // Each wave's (m, l, O) is merged in LDS; one fp32 record per (t, head, c) goes
 // to the workspace and attn_merge_kernel combines the chunks.
 #include "common.h"
@@ -125,10 +127,15 @@ __global__ __launch_bounds__(256) void attn_decode_partial_kernel(
     const bool edge = (kb < lo) || (kb + 63 > p);
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh) {
-      const bf16x8 pf = {(__bf16)sacc[2 * kh][0],     (__bf16)sacc[2 * kh][1],
-                         (__bf16)sacc[2 * kh][2],     (__bf16)sacc[2 * kh][3],
-                         (__bf16)sacc[2 * kh + 1][0], (__bf16)sacc[2 * kh + 1][1],
-                         (__bf16)sacc[2 * kh + 1][2], (__bf16)sacc[2 * kh + 1][3]};
+      // P as a sum of two bf16 parts (hi + lo): the product keeps ~16 bits of
+      // each probability instead of 8, at the cost of a second MFMA per tile
+      bf16x8 pf, pl;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float pv = sacc[2 * kh + (i >> 2)][i & 3];
+        pf[i] = (__bf16)pv;
+        pl[i] = (__bf16)(pv - (float)pf[i]);
+      }
       const int key0 = kb + kh * 32 + 4 * g, key1 = key0 + 16;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
@@ -153,6 +160,7 @@ __global__ __launch_bounds__(256) void attn_decode_partial_kernel(
           }
         }
         o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf, o[dt], 0, 0, 0);
+        o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pl, o[dt], 0, 0, 0);
       }
     }
   }

@@ -47,16 +47,40 @@ def rms(a) -> float:
     return float(np.sqrt(np.mean(a * a))) if a.size else 0.0
 
 
-def assert_rms_close(got, ref, name="", frac=1e-2):
-    """max|got - ref| <= frac * rms(ref), element by element."""
+def bf16_ulp(ref) -> np.ndarray:
+    """Spacing of bf16 values at |ref| (8 significant bits)."""
+    a = np.abs(np.asarray(ref, np.float64))
+    e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    return np.where(a > 0, np.exp2(np.maximum(e, -126) - 7), 0.0)
+
+
+def assert_rms_close(got, ref, name="", frac=1e-2, ulps=1):
+    """Parity bar for bf16 tensors: every element within
+    max(frac * rms(ref), ulps bf16 ulps of the reference element), and the RMS
+    of the error within frac * rms(ref).
+
+    The ulp allowance exists because the tensors are bf16: where the GPU's fp32
+    value and the oracle's float64 value straddle a rounding boundary the two
+    roundings differ by one ulp, and above 2.56 * rms one bf16 ulp is larger
+    than 1e-2 * rms. Stage comparisons feed the oracle the GPU's stored
+    upstream tensors, so one rounding point separates them (ulps=1); whole-layer
+    comparisons chain two (h_mid then h_out, ulps=2).
+    Returns max|got - ref| / rms(ref)."""
     got = np.asarray(got, np.float64)
     ref = np.asarray(ref, np.float64)
     assert got.shape == ref.shape, (name, got.shape, ref.shape)
     assert np.all(np.isfinite(got)), f"{name}: non-finite GPU values"
-    err = float(np.max(np.abs(got - ref))) if got.size else 0.0
-    tol = frac * rms(ref)
-    assert err <= tol, f"{name}: max|err| {err:.3e} > {frac} * rms {rms(ref):.3e}"
-    return err / max(rms(ref), 1e-30)
+    if got.size == 0:
+        return 0.0
+    err = np.abs(got - ref)
+    r = rms(ref)
+    tol = frac * r
+    bad = err > np.maximum(tol, ulps * bf16_ulp(ref) * 1.0000001)
+    assert not np.any(bad), (f"{name}: {int(bad.sum())} of {err.size} elements beyond "
+                             f"max({frac}*rms, {ulps} ulp); worst |err| {err.max():.3e}, "
+                             f"rms {r:.3e}")
+    assert rms(err) <= tol, f"{name}: rms(err) {rms(err):.3e} > {frac} * rms {r:.3e}"
+    return float(err.max() / max(r, 1e-30))
 
 
 def code_pos(c):

@@ -40,6 +40,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--chain", type=int, default=8, help="layer-steps per captured graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--prefill-reps", type=int, default=3)
     ap.add_argument("--cpu-steps", type=int, default=3)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB copy kernel (HBM counter calibration)")
@@ -235,9 +237,138 @@ def main():
                           "achieved": round(step_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                           "frac": round(step_gbs / HBM_PEAK_GBS, 4)},
     }
+    if not a.no_prefill:
+        del sets
+        torch.cuda.empty_cache()
+        out["prefill"] = prefill_leg(a)
     if not a.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(sets[0], dims, ex, a.cpu_steps)
+        if a.no_prefill:
+            cpu_set = sets[0]
+        else:
+            cpu_set = LayerSet(dims, 0, ex["layer"], pos0, Lmax)
+        out["cpu_baseline"] = cpu_baseline(cpu_set, dims, ex, a.cpu_steps)
     print(json.dumps(out))
+
+
+MFMA_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak (published)
+
+
+def prefill_leg(a):
+    """Chunked prefill: 8 sequences x 2048 new tokens, each after 100,000 prior
+    tokens (bf16 cache), through one NoPE MoE layer, one SWA MoE layer and the
+    dense layer 0. Returns per-layer ms, tok/s and MFMA-roofline fraction."""
+    import numpy as np
+    import torch
+
+    import moe_decoder_layer_amd as B
+    import synth
+    cfg = synth.config(3)
+    ex = cfg.extra
+    S, C, prior, Lmax = ex["S"], ex["chunk"], ex["prior"], ex["Lmax"]
+    T = S * C
+    base = synth.config(1).dims
+    I16 = dict(dtype=torch.int16, device="cuda")
+    pos = torch.tensor(np.concatenate([np.arange(prior, prior + C)] * S), dtype=torch.int32,
+                       device="cuda")
+    seq = torch.tensor(np.repeat(np.arange(S), C), dtype=torch.int32, device="cuda")
+    rope_h = np.zeros((Lmax, base.d), np.float32)
+    B.beam_rope_table(rope_h, Lmax, base.d, base.theta)
+    rope = torch.from_numpy(rope_h).cuda()
+    res = {}
+    for name, layer in (("nope_moe", ex["layers"]["nope_moe"]), ("swa_moe", ex["layers"]["swa_moe"]),
+                        ("dense", ex["layers"]["dense"])):
+        dims = base
+        mode = "swa" if name != "nope_moe" else "nope"
+        ffn = "dense" if name == "dense" else "moe"
+        n = 2 * layer + 1
+        t0 = time.time()
+        p = synth.make_params(dims, 0, layer, experts=False, projections=False)
+        t = {k: torch.from_numpy(np.ascontiguousarray(v.view(np.int16) if v.dtype == np.uint16
+                                                      else v)).cuda() for k, v in p.items()}
+        t["w_qkvg"] = synth.torch_normal_bf16((dims.qkvg_rows, dims.D), 0.02, 0, layer, "w_qkvg")
+        t["w_o"] = synth.torch_normal_bf16((dims.D, dims.Hq * dims.d), 0.02, 0, layer, "w_o")
+        if ffn == "moe":
+            w13 = torch.empty((dims.E, 2 * dims.F, dims.D), **I16)
+            w2 = torch.empty((dims.E, dims.D, dims.F), **I16)
+            for e in range(dims.E):
+                synth.torch_normal_bf16((2 * dims.F, dims.D), 0.02, 0, layer, "w13", e, out=w13[e])
+                synth.torch_normal_bf16((dims.D, dims.F), 0.02, 0, layer, "w2", e, out=w2[e])
+        else:
+            w13 = synth.torch_normal_bf16((2 * dims.Fd, dims.D), 0.02, 0, layer, "dense_w13")
+            w2 = synth.torch_normal_bf16((dims.D, dims.Fd), 0.02, 0, layer, "dense_w2")
+        K = torch.empty((S, dims.Hkv, Lmax, dims.d), **I16)
+        V = torch.empty((S, dims.Hkv, dims.d, Lmax), **I16)
+        Kp, Vp, _, _ = synth.torch_kv_prior(dims, S, prior, "bf16", 0, layer)
+        K[:, :, :prior] = Kp
+        V[:, :, :, :prior] = Vp.transpose(2, 3)
+        del Kp, Vp
+        kv = B.kv_struct(K, V, B.BEAM_KV_BF16, 1.0, 1.0, S, Lmax)
+        h0 = synth.torch_normal_bf16((T, dims.D), 1.0, 0, "prefill_h", name)
+        h = torch.empty_like(h0)
+        x = torch.empty((T, dims.D), **I16)
+        q = torch.empty((T, dims.Hq, dims.d), **I16)
+        g = torch.empty((T, dims.G), **I16)
+        o = torch.empty((T, dims.Hq, dims.d), **I16)
+        y = torch.empty((T, dims.D), **I16)
+        x2 = torch.empty((T, dims.D), **I16)
+        y2 = torch.empty((T, dims.D), **I16)
+        idx = torch.empty((T, dims.topk), dtype=torch.int32, device="cuda")
+        w = torch.empty((T, dims.topk), dtype=torch.float32, device="cuda")
+        wsz = lambda op, dd=dims: torch.empty(  # noqa: E731
+            max(256, B.beam_workspace_size(dd, op, T, prior + C)), dtype=torch.uint8, device="cuda")
+        ws_q, ws_a, ws_o, ws_r = (wsz(B.BEAM_OP_QKV), wsz(B.BEAM_OP_ATTN_NOPE),
+                                  wsz(B.BEAM_OP_OUT_GATE), wsz(B.BEAM_OP_ROUTER))
+        if ffn == "moe":
+            ws_f = wsz(B.BEAM_OP_MOE)
+        else:
+            ws_f = wsz(B.BEAM_OP_DENSE, synth.with_dims(synth.Config("", dims), F=dims.Fd).dims)
+        attn = B.beam_attn_nope_ssmax if mode == "nope" else B.beam_attn_swa
+        m = B.BEAM_NOPE_SSMAX if mode == "nope" else B.BEAM_SWA_ROPE
+        log(f"[bench] prefill {name}: set up in {time.time() - t0:.1f}s")
+
+        def layer_fwd():
+            h.copy_(h0)
+            B.beam_boundary_norm_residual(dims, T, None, None, h, t["w_attn_pre"], x, 0)
+            B.beam_qk_norm_rope_ssmax_kvwrite(dims, T, x, t["w_qkvg"], t["w_qnorm"], t["w_knorm"],
+                                              pos, seq, m, rope if mode == "swa" else None, q, g,
+                                              kv, ws_q)
+            attn(dims, T, q, pos, seq, kv, None, o, prior + C - 1, ws_a)
+            B.beam_out_gate(dims, T, o, g, t["b_gate"], t["w_o"], y, ws_o)
+            B.beam_boundary_norm_residual(dims, T, y, t["w_attn_post"], h, t["w_ffn_pre"], x2, n)
+            if ffn == "moe":
+                B.beam_router_fp32_grouped_topk(dims, T, x2, t["w_r"], t["b_corr"], idx, w, None,
+                                                ws_r)
+                B.beam_moe_swiglu_combine(dims, T, x2, idx, w, w13, w2, None, None, y2, ws_f)
+            else:
+                B.beam_dense_swiglu(T, dims.D, dims.Fd, x2, w13, w2, y2, ws_f)
+            B.beam_boundary_norm_residual(dims, T, y2, t["w_ffn_post"], h, t["w_next_pre"], x,
+                                          n + 1)
+
+        layer_fwd()
+        torch.cuda.synchronize()
+        B.beam_check()
+        reps = a.prefill_reps
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            layer_fwd()
+        e1.record()
+        torch.cuda.synchronize()
+        B.beam_check()
+        ms = e0.elapsed_time(e1) / reps
+        keys = (S * (C * prior + C * (C + 1) // 2)) if mode == "nope" else T * dims.window
+        proj = 2 * dims.D * dims.qkvg_rows + 2 * dims.Hq * dims.d * dims.D
+        ffn_fl = (dims.topk * 3 * 2 * dims.D * dims.F) if ffn == "moe" else 3 * 2 * dims.D * dims.Fd
+        flops = T * (proj + ffn_fl) + keys * 4 * dims.d * dims.Hq
+        tf = flops / (ms * 1e-3) / 1e12
+        res[name] = {"ms": round(ms, 3), "tok_s": round(T / (ms * 1e-3), 1),
+                     "algorithmic_flop": flops, "tflops": round(tf, 1),
+                     "mfma_frac": round(tf / MFMA_PEAK_TFLOPS, 4)}
+        log(f"[bench] prefill {name}: {ms:.2f} ms/layer, {T / ms * 1e3:.0f} tok/s, {tf:.0f} TFLOP/s")
+        del t, w13, w2, K, V, ws_f, ws_q, ws_a
+        torch.cuda.empty_cache()
+    res["workload"] = "8 sequences x 2048 new tokens after 100,000 prior tokens each, bf16 cache"
+    return res
 
 
 def cpu_baseline(L: "LayerSet", dims, ex, nsteps):

@@ -92,12 +92,40 @@ int attn_span(const beam_dims* d, int swa, int max_ctx) {
   return swa ? std::min(max_ctx, d->window + 63) : max_ctx;
 }
 size_t ws_attn(const beam_dims* d, int swa, int T, int max_ctx) {
+  if (T > beam::kGemvMaxT && d->Hkv > 0 && d->Hq / d->Hkv <= 8) return 0;  // no partials
   const int nch = beam::attn_nch_bound(T, d->Hkv, attn_span(d, swa, max_ctx));
   return align256((size_t)T * d->Hq * nch * (d->d + 4) * 4);
 }
 size_t ws_out_gate(const beam_dims* d, int T) { return align256((size_t)T * d->Hq * d->d * 2); }
 size_t ws_router(const beam_dims* d, int T) { return align256((size_t)T * d->E * 4); }
+
+// Many-token MoE workspace, in order: counts[E], seg_off[E+1], tile_off[E+1],
+// perm[P], inv[P] (int32); act[P][F] bf16; out[P][D] fp32; shared expert
+// act_s[T][F] bf16 and out_s[T][D] fp32.
+struct MoeWs {
+  size_t counts, seg_off, tile_off, perm, inv, act, out, act_s, out_s, total;
+};
+MoeWs moe_ws_layout(const beam_dims* d, int T) {
+  const size_t P = (size_t)T * d->topk, E = d->E;
+  MoeWs w{};
+  size_t o = 0;
+  w.counts = o; o += align256(E * 4);
+  w.seg_off = o; o += align256((E + 1) * 4);
+  w.tile_off = o; o += align256((E + 1) * 4);
+  w.perm = o; o += align256(P * 4);
+  w.inv = o; o += align256(P * 4);
+  w.act = o; o += align256(P * d->F * 2);
+  w.out = o; o += align256(P * d->D * 4);
+  w.act_s = o; o += align256((size_t)T * d->F * 2);
+  w.out_s = o; o += align256((size_t)T * d->D * 4);
+  w.total = o;
+  return w;
+}
+bool moe_many(const beam_dims* d, int T) {
+  return T > beam::kGemvMaxT && d->D % 64 == 0 && d->F % 64 == 0;
+}
 size_t ws_moe(const beam_dims* d, int T) {
+  if (moe_many(d, T)) return moe_ws_layout(d, T).total;
   return align256((size_t)T * (d->topk + 1) * d->F * 2);
 }
 size_t ws_dense(int T, int Fd) { return align256((size_t)T * Fd * 2); }
@@ -116,6 +144,15 @@ int attn_impl(const beam_dims* dims, int T, const uint16_t* q, const int32_t* po
   if (swa && dims->window <= 0) return fail(BEAM_E_SHAPE, "%s: window <= 0", fn);
   if (max_pos < 0 || max_pos >= kv->Lmax)
     return fail(BEAM_E_SHAPE, "%s: max_pos %d outside [0, Lmax)", fn, max_pos);
+  const int fp8 = kv->dtype == BEAM_KV_FP8_E4M3;
+  if (T > beam::kGemvMaxT && dims->Hq / dims->Hkv <= 8) {
+    if ((rc = device_ready())) return rc;
+    return launched(beam::launch_attn_prefill(T, dims->Hq, dims->Hkv, dims->d, swa, dims->window,
+                                              fp8, q, pos, seq, kv->k, kv->v,
+                                              fp8 ? kv->k_scale : 1.f, fp8 ? kv->v_scale : 1.f,
+                                              kv->S, kv->Lmax, sink, o, S_(stream)),
+                    fn);
+  }
   const int span = attn_span(dims, swa, max_pos + 1);
   int tpw, nch;
   beam::attn_plan(T, dims->Hkv, span, &tpw, &nch);
@@ -123,7 +160,6 @@ int attn_impl(const beam_dims* dims, int T, const uint16_t* q, const int32_t* po
   if (ws_bytes < need)
     return fail(BEAM_E_WORKSPACE, "%s: workspace %zu < %zu bytes", fn, ws_bytes, need);
   if ((rc = device_ready())) return rc;
-  const int fp8 = kv->dtype == BEAM_KV_FP8_E4M3;
   return launched(beam::launch_attn_decode(T, dims->Hq, dims->Hkv, dims->d, swa, dims->window,
                                            fp8, q, pos, seq, kv->k, kv->v,
                                            fp8 ? kv->k_scale : 1.f, fp8 ? kv->v_scale : 1.f,
@@ -197,9 +233,13 @@ int beam_qk_norm_rope_ssmax_kvwrite(const beam_dims* dims, int T, const uint16_t
   if ((rc = device_ready())) return rc;
   const int Nqkv = (dims->Hq + 2 * dims->Hkv) * dims->d;
   uint16_t* qkv = (uint16_t*)ws;
-  if (beam::launch_gemv_qkvg(T, Nqkv + dims->G, dims->D, Nqkv, w_qkvg, x, qkv, g_out,
-                             S_(stream)))
-    return launched(-1, __func__);
+  const int rcg = (T > beam::kGemvMaxT && dims->D % 64 == 0)
+                      ? beam::launch_gemm_bf16(T, Nqkv + dims->G, dims->D, x, dims->D, w_qkvg,
+                                               dims->D, qkv, Nqkv, g_out, dims->G, Nqkv,
+                                               S_(stream))
+                      : beam::launch_gemv_qkvg(T, Nqkv + dims->G, dims->D, Nqkv, w_qkvg, x, qkv,
+                                               g_out, S_(stream));
+  if (rcg) return launched(-1, __func__);
   const int fp8 = kv->dtype == BEAM_KV_FP8_E4M3;
   return launched(beam::launch_qk_epilogue(T, dims->Hq, dims->Hkv, dims->d, qkv, w_qnorm,
                                            w_knorm, pos, seq, mode, rope_cs, q_out, kv->k,
@@ -241,10 +281,26 @@ int beam_out_gate(const beam_dims* dims, int T, const uint16_t* o, const uint16_
   SHAPE(T > 0, "%s: T <= 0", __func__);
   if (dims->G > 0 && (!g || !b_gate))
     return fail(BEAM_E_NULL, "%s: gate input or bias is NULL", __func__);
-  (void)ws;
-  (void)ws_bytes;
-  if ((rc = device_ready())) return rc;
   const int K = dims->Hq * dims->d;
+  if (T > beam::kGemvMaxT && K % 64 == 0) {
+    const uint16_t* a = o;
+    if (dims->G) {
+      REQ(ws);
+      if (ws_bytes < ws_out_gate(dims, T))
+        return fail(BEAM_E_WORKSPACE, "%s: workspace %zu < %zu bytes", __func__, ws_bytes,
+                    ws_out_gate(dims, T));
+    }
+    if ((rc = device_ready())) return rc;
+    if (dims->G) {
+      if (beam::launch_gate(T, dims->Hq, dims->d, o, g, b_gate, (uint16_t*)ws, S_(stream)))
+        return launched(-1, __func__);
+      a = (const uint16_t*)ws;
+    }
+    return launched(beam::launch_gemm_bf16(T, dims->D, K, a, K, w_o, K, y, dims->D, nullptr, 0,
+                                           dims->D, S_(stream)),
+                    __func__);
+  }
+  if ((rc = device_ready())) return rc;
   return launched(beam::launch_gemv_gate_oproj(T, dims->D, K, dims->d, w_o, o,
                                                dims->G ? g : nullptr, b_gate, y, S_(stream)),
                   __func__);
@@ -320,6 +376,39 @@ int beam_moe_swiglu_combine(const beam_dims* dims, int T, const uint16_t* x,
                 ws_moe(dims, T));
   int rc = device_ready();
   if (rc) return rc;
+  if (moe_many(dims, T)) {
+    const MoeWs L = moe_ws_layout(dims, T);
+    char* b = (char*)ws;
+    int32_t* counts = (int32_t*)(b + L.counts);
+    int32_t* seg_off = (int32_t*)(b + L.seg_off);
+    int32_t* tile_off = (int32_t*)(b + L.tile_off);
+    int32_t* perm = (int32_t*)(b + L.perm);
+    int32_t* inv = (int32_t*)(b + L.inv);
+    uint16_t* act = (uint16_t*)(b + L.act);
+    float* out = (float*)(b + L.out);
+    const int E = dims->E, K = dims->topk, D = dims->D, F = dims->F;
+    const int BMr = beam::gemm_tile_rows();
+    const int max_tiles = (T * K + BMr - 1) / BMr + E;
+    const hipStream_t st = S_(stream);
+    if (beam::launch_moe_route(T, K, E, idx, BMr, counts, seg_off, tile_off, perm, inv, st) ||
+        beam::launch_gemm_swiglu(T * K, F, D, x, D, perm, w13, seg_off, tile_off, E,
+                                 (long long)2 * F * D, max_tiles, act, st) ||
+        beam::launch_gemm_f32(T * K, D, F, act, F, w2, seg_off, tile_off, E, (long long)D * F,
+                              max_tiles, out, D, st))
+      return launched(-1, __func__);
+    float* out_s = nullptr;
+    if (shared_w13) {
+      uint16_t* act_s = (uint16_t*)(b + L.act_s);
+      out_s = (float*)(b + L.out_s);
+      if (beam::launch_gemm_swiglu(T, F, D, x, D, nullptr, shared_w13, nullptr, nullptr, 1, 0, 0,
+                                   act_s, st) ||
+          beam::launch_gemm_f32(T, D, F, act_s, F, shared_w2, nullptr, nullptr, 1, 0, 0, out_s,
+                                D, st))
+        return launched(-1, __func__);
+    }
+    return launched(beam::launch_moe_combine(T, K, E, D, out, inv, w, idx, out_s, y, st),
+                    __func__);
+  }
   const int spt = dims->topk + (shared_w13 ? 1 : 0);
   uint16_t* act = (uint16_t*)ws;
   if (beam::launch_expert_w13(T, dims->D, dims->F, dims->E, dims->topk, spt, w13, shared_w13,
@@ -404,6 +493,14 @@ int beam_dense_swiglu(int T, int D, int Fd, const uint16_t* x, const uint16_t* w
   int rc = device_ready();
   if (rc) return rc;
   uint16_t* act = (uint16_t*)ws;
+  if (T > beam::kGemvMaxT && D % 64 == 0) {
+    if (beam::launch_gemm_swiglu(T, Fd, D, x, D, nullptr, w13, nullptr, nullptr, 1, 0, 0, act,
+                                 S_(stream)))
+      return launched(-1, __func__);
+    return launched(beam::launch_gemm_bf16(T, D, Fd, act, Fd, w2, Fd, y, D, nullptr, 0, D,
+                                           S_(stream)),
+                    __func__);
+  }
   if (beam::launch_expert_w13(T, D, Fd, 1, 1, 1, w13, nullptr, nullptr, x, act, S_(stream)))
     return launched(-1, __func__);
   return launched(beam::launch_expert_w2(T, D, Fd, 1, 1, 1, w2, nullptr, nullptr, nullptr, act,
@@ -449,7 +546,7 @@ int beam_check(void* stream) {
   hipError_t e = hipStreamSynchronize(S_(stream));
   if (e != hipSuccess) return fail(BEAM_E_HIP, "beam_check: %s", hipGetErrorString(e));
   const int f = beam::gemv_read_clear_err() | beam::qk_read_clear_err() |
-                beam::attn_read_clear_err();
+                beam::attn_read_clear_err() | beam::moe_read_clear_err();
   if (f < 0) return fail(BEAM_E_HIP, "beam_check: reading the device flags failed");
   if (f)
     return fail(BEAM_E_DEVICE, "beam_check: device check tripped:%s%s%s",

@@ -43,9 +43,34 @@ int launch_router(int T, int E, int D, int ng, int tg, int K, float route_scale,
                   const uint16_t* X, const float* Wr, const float* bcorr, float* logits,
                   int32_t* idx, float* w, hipStream_t st);
 
+// many-token (prefill) path
+constexpr int kGemvMaxT = 4;  // T above this runs on the matrix-core kernels
+int gemm_tile_rows();
+int launch_gemm_bf16(int M, int N, int K, const uint16_t* A, int lda, const uint16_t* B, int ldb,
+                     uint16_t* out, int ldo, uint16_t* out2, int ldo2, int n1, hipStream_t st);
+int launch_gemm_swiglu(int M, int F, int K, const uint16_t* A, int lda, const int32_t* gather,
+                       const uint16_t* B, const int32_t* seg_off, const int32_t* tile_off, int E,
+                       long long b_stride, int max_mtiles, uint16_t* act, hipStream_t st);
+int launch_gemm_f32(int M, int N, int K, const uint16_t* A, int lda, const uint16_t* B,
+                    const int32_t* seg_off, const int32_t* tile_off, int E, long long b_stride,
+                    int max_mtiles, float* out, int ldo, hipStream_t st);
+int launch_moe_route(int T, int K, int E, const int32_t* idx, int tile_rows, int32_t* counts,
+                     int32_t* seg_off, int32_t* tile_off, int32_t* perm, int32_t* inv,
+                     hipStream_t st);
+int launch_moe_combine(int T, int K, int E, int D, const float* out, const int32_t* inv,
+                       const float* w, const int32_t* idx, const float* shared_out, uint16_t* y,
+                       hipStream_t st);
+int launch_gate(int T, int Hq, int hd, const uint16_t* o, const uint16_t* g, const uint16_t* b,
+                uint16_t* z, hipStream_t st);
+int launch_attn_prefill(int T, int Hq, int Hkv, int hd, int swa, int window, int fp8,
+                        const uint16_t* q, const int32_t* pos, const int32_t* seq,
+                        const void* kc, const void* vc, float k_scale, float v_scale, int S,
+                        int Lmax, const float* sink, uint16_t* o, hipStream_t st);
+
 // device-side check flags (read and cleared by beam_check)
 int gemv_read_clear_err();
 int qk_read_clear_err();
 int attn_read_clear_err();
+int moe_read_clear_err();
 
 }  // namespace beam

@@ -1,0 +1,250 @@
+// bf16 matrix-core GEMMs for many-token (prefill) steps:
+//   C[m][n] = sum_k A[m][k] * B[n][k]      A: activations [M][K], B: weight rows [N][K]
+// fp32 accumulation on gfx950's v_mfma_f32_32x32x16_bf16.
+//
+// Tiling: a 256-thread workgroup owns a 256 x 256 tile of C; its 4 waves sit
+// in a 2 x 2 grid and each owns 128 x 128 (4 x 4 MFMA blocks of 32 x 32,
+// 256 fp32 accumulators per lane). K advances in slabs of 64: the next slab
+// is fetched from global memory into registers while the current one is
+// multiplied out of LDS, then stored into the other half of a double buffer.
+// LDS rows are 128 bytes (64 bf16); the eight 16-byte chunks of row r are
+// stored at chunk ^ (r & 7) so the 16-byte fragment reads of 8 consecutive
+// rows land on distinct banks.
+//
+// Variants (template Epi) cover the projections of the Beam layer ("Reflection
+// Beam 1.0 on vLLM": packed q|k|v|gate GEMM of optimisation change 5, o_proj,
+// the dense SwiGLU MLP of the MoE section, and the routed experts):
+//   EPI_BF16   bf16 store, optionally split in two destinations at column n1
+//   EPI_SWIGLU B rows are gate/up pairs; act = bf16(silu(bf16(g)) * bf16(u))
+//   EPI_F32    fp32 store (per-(token, expert) rows for the weighted combine)
+// Grouped mode: the M axis is a list of per-expert row segments; tile i maps to
+// (expert, first row) through a prefix sum of per-expert tile counts, A rows
+// may be gathered through an index list, and B is that expert's weight block.
+#include "common.h"
+#include "internal.h"
+
+namespace beam {
+
+constexpr int BM = 256, BN = 256, BK = 64;
+constexpr int GEMM_THREADS = 256;
+
+enum : int { EPI_BF16 = 0, EPI_SWIGLU = 1, EPI_F32 = 2 };
+
+struct GemmArgs {
+  const uint16_t* A;      // [M][lda] (or gathered rows)
+  const uint16_t* B;      // [N][ldb] (per-expert base + e * b_expert_stride in grouped mode)
+  int M, N, K;
+  int lda, ldb;
+  const int32_t* a_gather;    // row -> A row index (nullptr: identity)
+  // grouped mode
+  const int32_t* seg_off;     // [E+1] row offsets of the expert segments (nullptr: plain)
+  const int32_t* tile_off;    // [E+1] prefix sums of per-expert M-tile counts
+  int E;
+  long long b_expert_stride;  // elements between experts' weight blocks
+  // epilogue
+  void* out;
+  int ldo;
+  void* out2;                 // EPI_BF16 split destination (columns >= n1)
+  int ldo2, n1;
+  int F;                      // EPI_SWIGLU: up rows start at F (B row index)
+};
+
+__device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ (row & 7); }
+
+template <int EPI>
+__global__ __launch_bounds__(GEMM_THREADS) void gemm_bf16_kernel(GemmArgs g) {
+  extern __shared__ __align__(16) uint16_t lds[];
+  // double buffer: A0 | A1 | B0 | B1
+  auto As = [&](int buf) { return lds + buf * (BM * BK); };
+  auto Bs = [&](int buf) { return lds + 2 * BM * BK + buf * (BN * BK); };
+
+  // ---- tile -> (rows, expert) ------------------------------------------------
+  int m0, mrows, e = 0;
+  if (g.seg_off) {
+    const int ti = blockIdx.y;
+    if (ti >= g.tile_off[g.E]) return;
+    int lo = 0, hi = g.E;  // largest e with tile_off[e] <= ti
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (g.tile_off[mid] <= ti) lo = mid; else hi = mid;
+    }
+    e = lo;
+    const int seg0 = g.seg_off[e], seg1 = g.seg_off[e + 1];
+    m0 = seg0 + (ti - g.tile_off[e]) * BM;
+    mrows = min(BM, seg1 - m0);
+  } else {
+    m0 = blockIdx.y * BM;
+    mrows = min(BM, g.M - m0);
+  }
+  const int n0 = blockIdx.x * BN;  // tile column origin (EPI_SWIGLU: in act columns x 2)
+  const uint16_t* Bbase = g.B + (long long)e * g.b_expert_stride;
+
+  // ---- global load assignment: thread -> (row, 16 B chunk) ---------------------
+  const int tid = threadIdx.x;
+  const int lrow = tid >> 3, lchunk = tid & 7;  // rows lrow + 32 i, i < 8
+  const uint16_t* a_src[8];
+  const uint16_t* b_src[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int r = lrow + 32 * i;
+    const int rr = min(r, mrows - 1);
+    const int arow = g.a_gather ? g.a_gather[m0 + rr] : m0 + rr;
+    a_src[i] = g.A + (long long)arow * g.lda + lchunk * 8;
+    int brow;
+    if constexpr (EPI == EPI_SWIGLU) {
+      // local column c = r: wave column wc = c / 128; within it 64 gate then 64 up
+      const int wc = r >> 7, cc = r & 127;
+      const int f = (n0 >> 1) + wc * 64 + (cc & 63);
+      brow = (cc < 64) ? f : g.F + f;
+      brow = min(brow, (cc < 64 ? g.F : 2 * g.F) - 1);
+    } else {
+      brow = min(n0 + r, g.N - 1);
+    }
+    b_src[i] = Bbase + (long long)brow * g.ldb + lchunk * 8;
+  }
+
+  uint4 ra[8], rb[8];
+  auto gload = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      ra[i] = ld16(a_src[i] + k0);
+      rb[i] = ld16_nt(b_src[i] + k0);
+    }
+  };
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int r = lrow + 32 * i;
+      *reinterpret_cast<uint4*>(As(buf) + r * BK + swz(r, lchunk) * 8) = ra[i];
+      *reinterpret_cast<uint4*>(Bs(buf) + r * BK + swz(r, lchunk) * 8) = rb[i];
+    }
+  };
+
+  const int wave = tid >> 6, lane = tid & 63;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int lr = lane & 31, lk = lane >> 5;  // fragment row / k half
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
+
+  const int KT = g.K / BK;
+  gload(0);
+  lstore(0);
+  __syncthreads();
+  for (int kt = 0; kt < KT; ++kt) {
+    const int cur = kt & 1;
+    if (kt + 1 < KT) gload((kt + 1) * BK);
+    const uint16_t* Ab = As(cur) + (wm * 128) * BK;
+    const uint16_t* Bb = Bs(cur) + (wn * 128) * BK;
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ++ks) {
+      const int chunk = ks * 2 + lk;  // 8 bf16 = one 16 B chunk
+      bf16x8 af[4], bfr[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = i * 32 + lr;
+        af[i] = *reinterpret_cast<const bf16x8*>(Ab + r * BK + swz(r, chunk) * 8);
+        bfr[i] = *reinterpret_cast<const bf16x8*>(Bb + r * BK + swz(r, chunk) * 8);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    }
+    if (kt + 1 < KT) lstore(cur ^ 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue -------------------------------------------------------------------
+  // acc[i][j][4*ii + jj] = C[row 32 i + 8 ii + 4 lk + jj][col 32 j + lr] of the wave tile
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) {
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int rloc = wm * 128 + 32 * i + 8 * ii + 4 * lk + jj;
+        if (rloc >= mrows) continue;
+        const long long m = m0 + rloc;
+        if constexpr (EPI == EPI_SWIGLU) {
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            const int f = (n0 >> 1) + wn * 64 + 32 * j + lr;
+            if (f < g.F) {
+              const float gt = round_bf(acc[i][j][4 * ii + jj]);
+              const float up = round_bf(acc[i][j + 2][4 * ii + jj]);
+              reinterpret_cast<uint16_t*>(g.out)[m * g.ldo + f] = f2bf(siluf(gt) * up);
+            }
+          }
+        } else {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int n = n0 + wn * 128 + 32 * j + lr;
+            if (n >= g.N) continue;
+            const float v = acc[i][j][4 * ii + jj];
+            if constexpr (EPI == EPI_F32) {
+              reinterpret_cast<float*>(g.out)[m * g.ldo + n] = v;
+            } else {
+              if (n < g.n1)
+                reinterpret_cast<uint16_t*>(g.out)[m * g.ldo + n] = f2bf(v);
+              else
+                reinterpret_cast<uint16_t*>(g.out2)[m * g.ldo2 + (n - g.n1)] = f2bf(v);
+            }
+          }
+        }
+      }
+    }
+  }
+}
+
+static size_t gemm_lds_bytes() { return (size_t)2 * (BM + BN) * BK * 2; }
+
+template <int EPI>
+static int launch(const GemmArgs& a, int grid_n, int grid_m, hipStream_t st) {
+  static bool attr_set = false;
+  if (!attr_set) {
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_bf16_kernel<EPI>),
+                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)gemm_lds_bytes());
+    attr_set = true;
+  }
+  hipLaunchKernelGGL(gemm_bf16_kernel<EPI>, dim3(grid_n, grid_m), dim3(GEMM_THREADS),
+                     gemm_lds_bytes(), st, a);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+int launch_gemm_bf16(int M, int N, int K, const uint16_t* A, int lda, const uint16_t* B, int ldb,
+                     uint16_t* out, int ldo, uint16_t* out2, int ldo2, int n1, hipStream_t st) {
+  GemmArgs a{};
+  a.A = A; a.B = B; a.M = M; a.N = N; a.K = K; a.lda = lda; a.ldb = ldb;
+  a.out = out; a.ldo = ldo; a.out2 = out2; a.ldo2 = ldo2; a.n1 = out2 ? n1 : N;
+  return launch<EPI_BF16>(a, (N + BN - 1) / BN, (M + BM - 1) / BM, st);
+}
+
+int launch_gemm_swiglu(int M, int F, int K, const uint16_t* A, int lda, const int32_t* gather,
+                       const uint16_t* B, const int32_t* seg_off, const int32_t* tile_off, int E,
+                       long long b_stride, int max_mtiles, uint16_t* act, hipStream_t st) {
+  GemmArgs a{};
+  a.A = A; a.B = B; a.M = M; a.N = 2 * F; a.K = K; a.lda = lda; a.ldb = K;
+  a.a_gather = gather; a.seg_off = seg_off; a.tile_off = tile_off; a.E = E;
+  a.b_expert_stride = b_stride; a.out = act; a.ldo = F; a.F = F; a.n1 = 2 * F;
+  const int gm = seg_off ? max_mtiles : (M + BM - 1) / BM;
+  return launch<EPI_SWIGLU>(a, (2 * F + BN - 1) / BN, gm, st);
+}
+
+int launch_gemm_f32(int M, int N, int K, const uint16_t* A, int lda, const uint16_t* B,
+                    const int32_t* seg_off, const int32_t* tile_off, int E, long long b_stride,
+                    int max_mtiles, float* out, int ldo, hipStream_t st) {
+  GemmArgs a{};
+  a.A = A; a.B = B; a.M = M; a.N = N; a.K = K; a.lda = lda; a.ldb = K;
+  a.seg_off = seg_off; a.tile_off = tile_off; a.E = E; a.b_expert_stride = b_stride;
+  a.out = out; a.ldo = ldo; a.n1 = N;
+  const int gm = seg_off ? max_mtiles : (M + BM - 1) / BM;
+  return launch<EPI_F32>(a, (N + BN - 1) / BN, gm, st);
+}
+
+int gemm_tile_rows() { return BM; }
+
+}  // namespace beam

@@ -297,15 +297,19 @@ def moe(dims, x, idx, w, get_expert, shared=None) -> np.ndarray:
     shared: optional (w13, w2) of an always-on expert with weight 1 ([Flint])."""
     x = as_f64(x)
     T = x.shape[0]
+    idx = np.asarray(idx)
     acc = np.zeros((T, dims.D), F64)
-    for t in range(T):
-        for k in range(idx.shape[1]):
-            w13, w2 = get_expert(int(idx[t, k]))
-            _, y = swiglu_ffn(x[t], w13, w2, dims.F)
-            acc[t] += float(w[t, k]) * y
-        if shared is not None:
-            _, y = swiglu_ffn(x[t], shared[0], shared[1], dims.F)
-            acc[t] += y
+    # each term w[t][k] * FFN_e(x_t) of the sum, visited expert by expert so
+    # every expert's weights are read once
+    for e in np.unique(idx):
+        w13, w2 = get_expert(int(e))
+        tt, kk = np.nonzero(idx == e)
+        _, y = swiglu_ffn(x[tt], w13, w2, dims.F)
+        for r, (t, k) in enumerate(zip(tt, kk)):
+            acc[t] += float(w[t, k]) * y[r]
+    if shared is not None:
+        _, y = swiglu_ffn(x, shared[0], shared[1], dims.F)
+        acc += y
     return bf(acc)
 
 

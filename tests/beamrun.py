@@ -231,9 +231,12 @@ def run_layer(dims, P: Params, cache: Cache, h_bits, pos, seq, mode: str, n: int
     m = B.BEAM_SWA_ROPE if mode == "swa" else B.BEAM_NOPE_SSMAX
     if rope is None and mode == "swa":
         rope = rope_table(cache.Lmax, dims.d, dims.theta)
+    wsq = ws(dims, B.BEAM_OP_QKV, T)
     B.beam_qk_norm_rope_ssmax_kvwrite(dims, T, x, t["w_qkvg"], t["w_qnorm"], t["w_knorm"],
                                       pos_t, seq_t, m, rope if mode == "swa" else None, q,
-                                      g if dims.G else None, kvs, ws(dims, B.BEAM_OP_QKV, T))
+                                      g if dims.G else None, kvs, wsq)
+    nqkv = (dims.Hq + 2 * dims.Hkv) * dims.d
+    out["qkv"] = host_bits(wsq[:T * nqkv * 2].view(torch.int16).view(T, nqkv))
     o = torch.empty((T, dims.Hq, dims.d), **I16)
     max_pos = int(np.max(pos))
     attn = B.beam_attn_swa if mode == "swa" else B.beam_attn_nope_ssmax

@@ -20,7 +20,11 @@ def check_stages(dims, P: Params, cache: Cache, g, pos, seq, mode, n, ffn, sink=
     _, x_ref = L.boundary(None, g["h_in"], None, P.np("w_attn_pre"), 0, eps)
     assert_rms_close(bits_f64(g["x"]), x_ref, "x")
     qkvg = L.qkvg_projection(g["x"], P.np("w_qkvg"))
-    q, k, v, gg = L.split_qkvg(dims, qkvg)
+    nqkv = (dims.Hq + 2 * dims.Hkv) * dims.d
+    assert_rms_close(bits_f64(g["qkv"]), qkvg[:, :nqkv], "qkv projection")
+    # the per-head stage is fed the GPU's stored projection
+    q, k, v, _ = L.split_qkvg(dims, np.concatenate([bits_f64(g["qkv"]), qkvg[:, nqkv:]], 1))
+    gg = qkvg[:, nqkv:nqkv + dims.G]
     qn, kn = L.qk_norm_position(dims, q, k, pos, mode, P.np("w_qnorm"), P.np("w_knorm"))
     assert_rms_close(bits_f64(g["q"]), round_bf16(qn), "q")
     if dims.G:

@@ -67,13 +67,20 @@ def test_qk_norm_kvwrite(base, T, pos0, mode, kv):
     q = torch.empty((T, dims.Hq, dims.d), **I16)
     g = torch.empty((T, dims.G), **I16)
     rope = rope_table(Lmax, dims.d, dims.theta) if mode == "swa" else None
+    wsq = ws(dims, B.BEAM_OP_QKV, T)
     B.beam_qk_norm_rope_ssmax_kvwrite(
         dims, T, dev(x), P.t["w_qkvg"], P.t["w_qnorm"], P.t["w_knorm"], dev(pos), dev(seq),
-        B.BEAM_SWA_ROPE if mode == "swa" else B.BEAM_NOPE_SSMAX, rope, q, g, cache.struct(),
-        ws(dims, B.BEAM_OP_QKV, T))
+        B.BEAM_SWA_ROPE if mode == "swa" else B.BEAM_NOPE_SSMAX, rope, q, g, cache.struct(), wsq)
     B.beam_check()
     qkvg = L.qkvg_projection(x, P.np("w_qkvg"))
-    qr, kr, vr, gr = L.split_qkvg(dims, qkvg)
+    nqkv = (dims.Hq + 2 * dims.Hkv) * dims.d
+    # the projection (first rounding point) against the oracle; the per-head
+    # stage against the oracle fed the GPU's stored projection
+    gq = wsq[:T * nqkv * 2].view(torch.int16).view(T, nqkv)
+    assert_rms_close(bits_f64(host_bits(gq)), qkvg[:, :nqkv], "qkv projection")
+    qkv_gpu = np.concatenate([bits_f64(host_bits(gq)), qkvg[:, nqkv:]], axis=1)
+    qr, kr, vr, gr = L.split_qkvg(dims, qkv_gpu)
+    _, _, _, gr = L.split_qkvg(dims, qkvg)
     qn, kn = L.qk_norm_position(dims, qr, kr, pos, mode, P.np("w_qnorm"), P.np("w_knorm"))
     assert_rms_close(bits_f64(host_bits(q)), round_bf16(qn), "q")
     assert_rms_close(bits_f64(host_bits(g)), gr, "g")
@@ -124,13 +131,24 @@ def _needle_cache(dims, Lmax, fill, kv, q, pos, seq, needles, seed):
     return cache
 
 
-@pytest.mark.parametrize("case", ["tiny", "beam_multi", "beam_long"])
+@pytest.mark.parametrize("case", ["tiny", "tiny_few", "beam_multi", "beam_few", "beam_long",
+                                  "beam_chunk"])
 @pytest.mark.parametrize("mode", ["swa", "nope"])
 @pytest.mark.parametrize("kv", ["bf16", "fp8"])
 def test_attention(case, mode, kv):
+    """Few tokens (<= 4) take the split-K kernel, more take the flash kernel."""
     if case == "tiny":
         dims, Lmax, fill = CFG0, 192, 128
         pos = np.array([0, 15, 16, 63, 64, 100, 127], np.int32)
+    elif case == "tiny_few":
+        dims, Lmax, fill = CFG0, 192, 128
+        pos = np.array([3, 64, 127], np.int32)
+    elif case == "beam_few":
+        dims, Lmax, fill = BEAM, 4096, 3000
+        pos = np.array([700, 2999], np.int32)
+    elif case == "beam_chunk":  # a prefill chunk: 70 consecutive tokens after 2900 prior
+        dims, Lmax, fill = BEAM, 4096, 2970
+        pos = np.arange(2900, 2970, dtype=np.int32)
     elif case == "beam_multi":
         dims, Lmax, fill = BEAM, 4096, 3000
         pos = np.array([0, 511, 512, 1000, 2047, 2999], np.int32)
@@ -138,7 +156,8 @@ def test_attention(case, mode, kv):
         dims, Lmax, fill = BEAM, 100352, 100001
         pos = np.array([100000], np.int32)
     T = len(pos)
-    seq = (np.arange(T) % 2).astype(np.int32) if case != "beam_long" else np.zeros(T, np.int32)
+    seq = (np.arange(T) % 2).astype(np.int32) if case not in ("beam_long", "beam_chunk") \
+        else np.zeros(T, np.int32)
     q = dev(synth.make_h((T, dims.Hq, dims.d), 3, "aq", case))
     W = dims.window
 
@@ -186,7 +205,8 @@ def test_out_gate(base, T):
     o = synth.make_h((T, dims.Hq * dims.d), 5, "go", T)
     g = synth.make_h((T, dims.G), 5, "gg", T)
     y = torch.empty((T, dims.D), **I16)
-    B.beam_out_gate(dims, T, dev(o), dev(g), P.t["b_gate"], P.t["w_o"], y)
+    B.beam_out_gate(dims, T, dev(o), dev(g), P.t["b_gate"], P.t["w_o"], y,
+                    ws(dims, B.BEAM_OP_OUT_GATE, T))
     B.beam_check()
     z = L.output_gate(dims, bits_f64(o).reshape(T, dims.Hq, dims.d), bits_f64(g), P.np("b_gate"))
     assert_rms_close(bits_f64(host_bits(y)), L.o_proj(z, P.np("w_o")), "y")
@@ -288,3 +308,37 @@ def test_dense(base, T):
     B.beam_dense_swiglu(T, dims.D, dims.Fd, dev(x), w13d, w2d, y, ws(dd, B.BEAM_OP_DENSE, T))
     B.beam_check()
     assert_rms_close(bits_f64(host_bits(y)), L.dense_ffn(x, w13, w2, dims.Fd), "y2")
+
+
+# ------------------------------------------------------------------ matrix-core paths at Beam shapes
+@pytest.mark.parametrize("T", [300])
+def test_qkv_gemm_beam(T):
+    """Packed projection on the MFMA GEMM (ragged 256-row tiles) + epilogue."""
+    test_qk_norm_kvwrite(BEAM, T, 17, "nope", "bf16")
+
+
+def test_out_gate_gemm_beam():
+    test_out_gate(BEAM, 300)
+
+
+def test_dense_gemm_beam():
+    test_dense(BEAM, 300)
+
+
+def test_moe_grouped_gemm_beam():
+    """Grouped expert GEMMs: 300 tokens all routed to the same 8 experts, so each
+    expert segment has 300 rows (one full and one ragged 256-row tile), plus
+    a second run spread over 24 experts (single ragged tiles)."""
+    dims = BEAM
+    P = _beam_params()
+    T = 300
+    x = synth.make_h((T, dims.D), 7, "mgx")
+    g = np.random.default_rng(9)
+    for pool in (np.array([3, 17, 40, 99, 128, 200, 201, 255]), g.choice(256, 24, replace=False)):
+        idx = np.stack([g.choice(pool, dims.topk, replace=False) for _ in range(T)]).astype(np.int32)
+        w = g.uniform(0.05, 0.6, (T, dims.topk)).astype(np.float32)
+        y = torch.empty((T, dims.D), **I16)
+        B.beam_moe_swiglu_combine(dims, T, dev(x), dev(idx), dev(w), P.t["w13"], P.t["w2"], None,
+                                  None, y, ws(dims, B.BEAM_OP_MOE, T))
+        B.beam_check()
+        assert_rms_close(bits_f64(host_bits(y)), L.moe(dims, x, idx, w, P.expert), "y2")

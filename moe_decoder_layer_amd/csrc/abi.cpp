@@ -92,7 +92,8 @@ int attn_span(const beam_dims* d, int swa, int max_ctx) {
   return swa ? std::min(max_ctx, d->window + 63) : max_ctx;
 }
 size_t ws_attn(const beam_dims* d, int swa, int T, int max_ctx) {
-  if (T > beam::kGemvMaxT && d->Hkv > 0 && d->Hq / d->Hkv <= 8) return 0;  // no partials
+  if (T > beam::kGemvMaxT && d->Hkv > 0 && beam::attn_prefill_ok(d->Hq / d->Hkv, d->d))
+    return 0;  // the many-token kernel needs no partials
   const int nch = beam::attn_nch_bound(T, d->Hkv, attn_span(d, swa, max_ctx));
   return align256((size_t)T * d->Hq * nch * (d->d + 4) * 4);
 }
@@ -145,7 +146,7 @@ int attn_impl(const beam_dims* dims, int T, const uint16_t* q, const int32_t* po
   if (max_pos < 0 || max_pos >= kv->Lmax)
     return fail(BEAM_E_SHAPE, "%s: max_pos %d outside [0, Lmax)", fn, max_pos);
   const int fp8 = kv->dtype == BEAM_KV_FP8_E4M3;
-  if (T > beam::kGemvMaxT && dims->Hq / dims->Hkv <= 8) {
+  if (T > beam::kGemvMaxT && beam::attn_prefill_ok(dims->Hq / dims->Hkv, dims->d)) {
     if ((rc = device_ready())) return rc;
     return launched(beam::launch_attn_prefill(T, dims->Hq, dims->Hkv, dims->d, swa, dims->window,
                                               fp8, q, pos, seq, kv->k, kv->v,

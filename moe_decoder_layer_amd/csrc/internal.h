@@ -62,6 +62,12 @@ int launch_moe_combine(int T, int K, int E, int D, const float* out, const int32
                        hipStream_t st);
 int launch_gate(int T, int Hq, int hd, const uint16_t* o, const uint16_t* g, const uint16_t* b,
                 uint16_t* z, hipStream_t st);
+// the many-token attention kernel covers these GQA group / head-dim shapes
+inline bool attn_prefill_ok(int grp, int hd) {
+  int ntb = (grp <= 6) ? 2 : 1;
+  while (256 * grp * ntb < 16 * hd) ++ntb;
+  return grp >= 1 && grp * ntb <= 12;
+}
 int launch_attn_prefill(int T, int Hq, int Hkv, int hd, int swa, int window, int fp8,
                         const uint16_t* q, const int32_t* pos, const int32_t* seq,
                         const void* kc, const void* vc, float k_scale, float v_scale, int S,

@@ -1,19 +1,25 @@
 // Many-token GQA attention over the KV cache (chunked prefill): causal inside
 // the chunk, sliding window on SWA layers, full context on NoPE layers
 // ("Reflection Beam 1.0 on vLLM", Attention section). The chunk's own keys
-// were written to the cache first, so every token reads keys
-// [lo_t, p_t] of its sequence from the cache alone.
+// were written to the cache first, so every token reads keys [lo_t, p_t] of
+// its sequence from the cache alone.
 //
-// Workgroup = (block of 32 consecutive tokens, kv head j); wave w is query
-// head j * grp + w, so the group's waves read the same K/V lines (shared
-// through the CU's L1). Per 32-key block and wave, on 32x32x16 bf16 MFMA:
-//   S^T[key][token] = K[key][:] . Q[token][:]
-//   O^T[dim][token] += V^T[dim][key] . P^T[key][token]   (P as hi + lo bf16)
-// In the S^T layout lane l owns token l % 32, so the online softmax state is
+// Workgroup = (block of 32*ntb consecutive tokens, kv head j): one wave per
+// (query head of the group, 32-token sub-block), so every wave of the
+// workgroup consumes the same keys. Keys advance in tiles of 64, staged
+// cooperatively into a double-buffered LDS ring: the next tile's global loads
+// are in flight while the current tile is multiplied out of LDS. K and V are
+// held as bf16 (fp8 caches are widened exactly while staged); probabilities
+// enter the P.V product as a hi + lo pair of bf16 values (two MFMAs), so the
+// attention output's only bf16 rounding is its store:
+//   S^T[key][token] = K[key][:] . Q[token][:]            32x32x16 bf16 MFMA
+//   O^T[dim][token] += V^T[dim][key] . (P_hi + P_lo)^T    2 x 32x32x16 bf16 MFMA
+// In the S^T layout lane l owns token l % 32: the online softmax state is
 // lane-local up to one xor-32 shuffle, and a lane's probabilities are the B
-// operand it needs for P.V. Keys are visited in the union of the 32 tokens'
-// ranges; per-token masks cut each token's own range, and value rows outside
-// the union are zeroed before they can meet a zero probability.
+// operand it needs for P.V. LDS rows are padded (K rows by 16 bytes, V^T rows
+// by 8) so the fragment reads of consecutive rows hit distinct banks while
+// every per-step offset stays an immediate. Value entries outside the tile's
+// valid key range are zeroed while staged (they may hold anything).
 // Tokens of several sequences in one block are handled in one pass per
 // sequence.
 #include "common.h"
@@ -21,25 +27,40 @@
 
 namespace beam {
 
+constexpr int KT = 64;  // keys per LDS tile
+
 template <int HD, bool FP8, bool SWA>
-__global__ __launch_bounds__(512) void attn_prefill_kernel(
+__global__ __launch_bounds__(768) void attn_prefill_kernel(
     const uint16_t* __restrict__ q, const int32_t* __restrict__ pos,
     const int32_t* __restrict__ seq, const void* __restrict__ kc, const void* __restrict__ vc,
-    int S, int Lmax, int Hq, int Hkv, int window, float score_scale, int T,
+    int S, int Lmax, int Hq, int Hkv, int window, float score_scale, int T, int ntb,
     const float* __restrict__ sink, float v_scale, uint16_t* __restrict__ o) {
-  constexpr int KS = HD / 16;  // k-steps of the score product (16 dims each)
-  constexpr int DB = HD / 32;  // 32-dim blocks of the output
-  constexpr int LD = HD / 2;   // dims per lane half in the score product
+  constexpr int KS = HD / 16;    // k-steps of the score product
+  constexpr int DB = HD / 32;    // 32-dim blocks of the output
+  constexpr int LD = HD / 2;     // dims per lane half in the score product
+  constexpr int KSTR = HD + 8;   // LDS row stride of K (bf16 elements)
+  constexpr int VSTR = KT + 4;   // LDS row stride of V^T (bf16 elements)
+  constexpr int NKU = KT * HD / 8;  // 8-element load units of a K tile
+  constexpr int NU = NKU + HD * (KT / 8);
+  extern __shared__ __align__(16) uint16_t lds[];
+  // [K0 | K1 | V0 | V1]
+  auto sK = [&](int b) { return lds + b * (KT * KSTR); };
+  auto sV = [&](int b) { return lds + 2 * KT * KSTR + b * (HD * VSTR); };
+  __shared__ int sinfo[3];
+
+  const int nthr = blockDim.x, tid = threadIdx.x;
   const int j = blockIdx.y;
   const int grp = Hq / Hkv;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int h = j * grp + wave;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int hh = wave % grp, tb = wave / grp;
+  const int h = j * grp + hh;
   const int tc = lane & 31, g = lane >> 5;
-  const int t = blockIdx.x * 32 + tc;
+  const int tblk = 32 * ntb;
+  const int t0 = blockIdx.x * tblk;
+  const int t = t0 + 32 * tb + tc;
   const bool tok = t < T;
-  int p = tok ? pos[t] : -1;
-  int s = tok ? seq[t] : -1;
-  if (p < 0 || p >= Lmax || s < 0 || s >= S) {  // invalid tokens attend nothing
+  int p = tok ? pos[t] : -1, s = tok ? seq[t] : -1;
+  if (p < 0 || p >= Lmax || s < 0 || s >= S) {
     p = -1;
     s = -1;
   }
@@ -54,107 +75,180 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(
 #pragma unroll
     for (int i = 0; i < KS; ++i) qf[i] = bf16x8{};
   }
-
   float m = -INFINITY, lsum = 0.f;
   f32x16 oacc[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) oacc[db] = f32x16{};
 
+  constexpr int UPT = 4;  // load units per thread per tile (NU <= UPT * 512)
+  uint4 reg[UPT];
+
   int s_prev = -1;
   for (;;) {
-    // next sequence present in the block (ascending), and its key range
-    int s_cur = (s > s_prev) ? s : 0x7fffffff;
-    for (int o2 = 32; o2 > 0; o2 >>= 1) s_cur = min(s_cur, __shfl_xor(s_cur, o2, 64));
+    // ---- next sequence present in the block, and its key range ------------
+    if (wave == 0) {
+      int sc = 0x7fffffff;
+      int tt = t0 + lane, pp = -1, ss = -1;
+      if (lane < tblk && tt < T) {
+        pp = pos[tt];
+        ss = seq[tt];
+        if (pp < 0 || pp >= Lmax || ss < 0 || ss >= S) ss = -1;
+      }
+      sc = (ss > s_prev) ? ss : 0x7fffffff;
+      for (int o2 = 32; o2 > 0; o2 >>= 1) sc = min(sc, __shfl_xor(sc, o2, 64));
+      const bool in = (ss == sc);
+      int kmn = in ? (SWA ? max(0, pp - window + 1) : 0) : 0x7fffffff;
+      int kmx = in ? pp : -1;
+      for (int o2 = 32; o2 > 0; o2 >>= 1) {
+        kmn = min(kmn, __shfl_xor(kmn, o2, 64));
+        kmx = max(kmx, __shfl_xor(kmx, o2, 64));
+      }
+      if (lane == 0) {
+        sinfo[0] = sc;
+        sinfo[1] = kmn;
+        sinfo[2] = kmx;
+      }
+    }
+    __syncthreads();
+    const int s_cur = sinfo[0], kmin = sinfo[1], kmax = sinfo[2];
+    __syncthreads();
     if (s_cur == 0x7fffffff) break;
     s_prev = s_cur;
     const bool mine = (s == s_cur);
-    int kmin = mine ? lo : 0x7fffffff, kmax = mine ? p : -1;
-    for (int o2 = 32; o2 > 0; o2 >>= 1) {
-      kmin = min(kmin, __shfl_xor(kmin, o2, 64));
-      kmax = max(kmax, __shfl_xor(kmax, o2, 64));
-    }
     const size_t krow0 = ((size_t)s_cur * Hkv + j) * (size_t)Lmax;
     const size_t vrow0 = ((size_t)s_cur * Hkv + j) * (size_t)HD;
-    for (int kb = kmin & ~31; kb <= kmax; kb += 32) {
-      f32x16 sacc = f32x16{};
-      const size_t kr = (krow0 + kb + tc) * HD + g * LD;
+    const int kb0 = kmin & ~(KT - 1);
+    const int ntiles = (kmax - kb0) / KT + 1;
+
+    auto gload = [&](int kb) {
 #pragma unroll
-      for (int i = 0; i < KS; ++i) {
-        bf16x8 kf;
-        if constexpr (FP8) {
-          kf = e4m3x8_to_bf16x8(*reinterpret_cast<const uint2*>((const uint8_t*)kc + kr + i * 8));
-        } else {
-          kf = as_bf16x8(ld16((const uint16_t*)kc + kr + i * 8));
-        }
-        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[i], sacc, 0, 0, 0);
-      }
-      // sacc[4 i + jj] = S[key kb + 8 i + 4 g + jj][token tc]
-      float mx = -INFINITY;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          const int key = kb + 8 * i + 4 * g + jj;
-          float v = sacc[4 * i + jj] * score_scale;
-          v = (!mine || key < lo || key > p) ? -INFINITY : v;
-          sacc[4 * i + jj] = v;
-          mx = fmaxf(mx, v);
-        }
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float mn = fmaxf(m, mx);
-      const float alpha = (mn == -INFINITY) ? 1.f : exp2f(m - mn);
-      float rs = 0.f;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float pr = (mn == -INFINITY) ? 0.f : exp2f(sacc[i] - mn);
-        sacc[i] = pr;
-        rs += pr;
-      }
-      rs += __shfl_xor(rs, 32, 64);
-      lsum = lsum * alpha + rs;
-      m = mn;
-#pragma unroll
-      for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
-      const bool edge = (kb < kmin) || (kb + 31 > kmax);
-#pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        bf16x8 ph, pl;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const float pv = sacc[4 * (2 * st + (i >> 2)) + (i & 3)];
-          ph[i] = (__bf16)pv;
-          pl[i] = (__bf16)(pv - (float)ph[i]);
-        }
-        const int key0 = kb + 16 * st + 4 * g, key1 = key0 + 8;
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const size_t vr = (vrow0 + db * 32 + tc) * (size_t)Lmax;
-          bf16x8 vf;
+      for (int n = 0; n < UPT; ++n) {
+        const int u = tid + n * nthr;
+        if (u >= NU) break;
+        if (u < NKU) {
+          const int row = u / (HD / 8), c = u % (HD / 8);
+          const size_t off = (krow0 + kb + row) * HD + c * 8;
           if constexpr (FP8) {
-            const uint8_t* vb = (const uint8_t*)vc + vr;
-            const bf16x4 a = e4m3x4_to_bf16x4(*reinterpret_cast<const uint32_t*>(vb + key0));
-            const bf16x4 b = e4m3x4_to_bf16x4(*reinterpret_cast<const uint32_t*>(vb + key1));
-            vf = bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+            const uint2 w = *reinterpret_cast<const uint2*>((const uint8_t*)kc + off);
+            reg[n] = uint4{w.x, w.y, 0u, 0u};
           } else {
-            const uint16_t* vb = (const uint16_t*)vc + vr;
-            const uint2 a = *reinterpret_cast<const uint2*>(vb + key0);
-            const uint2 b = *reinterpret_cast<const uint2*>(vb + key1);
-            vf = __builtin_bit_cast(bf16x8, uint4{a.x, a.y, b.x, b.y});
+            reg[n] = ld16((const uint16_t*)kc + off);
           }
-          if (edge) {
+        } else {
+          const int u2 = u - NKU, dim = u2 >> 3, c = u2 & 7;
+          const size_t off = (vrow0 + dim) * (size_t)Lmax + kb + c * 8;
+          if constexpr (FP8) {
+            const uint2 w = *reinterpret_cast<const uint2*>((const uint8_t*)vc + off);
+            reg[n] = uint4{w.x, w.y, 0u, 0u};
+          } else {
+            reg[n] = ld16((const uint16_t*)vc + off);
+          }
+        }
+      }
+    };
+    auto lstore = [&](int buf, int kb) {
+#pragma unroll
+      for (int n = 0; n < UPT; ++n) {
+        const int u = tid + n * nthr;
+        if (u >= NU) break;
+        if (u < NKU) {
+          const int row = u / (HD / 8), c = u % (HD / 8);
+          uint4 v = reg[n];
+          if constexpr (FP8) v = __builtin_bit_cast(uint4, e4m3x8_to_bf16x8(uint2{v.x, v.y}));
+          *reinterpret_cast<uint4*>(sK(buf) + row * KSTR + c * 8) = v;
+        } else {
+          const int u2 = u - NKU, dim = u2 >> 3, c = u2 & 7;
+          bf16x8 hv;
+          if constexpr (FP8) hv = e4m3x8_to_bf16x8(uint2{reg[n].x, reg[n].y});
+          else hv = as_bf16x8(reg[n]);
+          const int key = kb + c * 8;
+          if (key < kmin || key + 7 > kmax) {  // edge tile: zero keys outside the range
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+              if (key + e < kmin || key + e > kmax) hv[e] = (__bf16)0.0f;
+          }
+          uint16_t* vrow = sV(buf) + dim * VSTR + c * 8;
+          const uint4 hb = __builtin_bit_cast(uint4, hv);
+          *reinterpret_cast<uint2*>(vrow) = uint2{hb.x, hb.y};
+          *reinterpret_cast<uint2*>(vrow + 4) = uint2{hb.z, hb.w};
+        }
+      }
+    };
+
+    gload(kb0);
+    lstore(0, kb0);
+    __syncthreads();
+    for (int it = 0; it < ntiles; ++it) {
+      const int cur = it & 1;
+      const int kb = kb0 + it * KT;
+      if (it + 1 < ntiles) gload(kb + KT);
+      if (__any(mine)) {  // waves with no token of this sequence only stage
+#pragma unroll 1
+        for (int kh = 0; kh < 2; ++kh) {
+          const int kbase = kb + kh * 32;
+          f32x16 sacc = f32x16{};
+          const uint16_t* krow = sK(cur) + (kh * 32 + tc) * KSTR + g * LD;
+#pragma unroll
+          for (int i = 0; i < KS; ++i) {
+            const bf16x8 kf = *reinterpret_cast<const bf16x8*>(krow + i * 8);
+            sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[i], sacc, 0, 0, 0);
+          }
+          // sacc[4 i + jj] = S[key kbase + 8 i + 4 g + jj][token tc]
+          float mx = -INFINITY;
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+              const int key = kbase + 8 * i + 4 * g + jj;
+              float v = sacc[4 * i + jj] * score_scale;
+              v = (!mine || key < lo || key > p) ? -INFINITY : v;
+              sacc[4 * i + jj] = v;
+              mx = fmaxf(mx, v);
+            }
+          mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+          const float mn = fmaxf(m, mx);
+          const float alpha = (mn == -INFINITY) ? 1.f : exp2f(m - mn);
+          float rs = 0.f;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const float pr = (mn == -INFINITY) ? 0.f : exp2f(sacc[i] - mn);
+            sacc[i] = pr;
+            rs += pr;
+          }
+          rs += __shfl_xor(rs, 32, 64);
+          lsum = lsum * alpha + rs;
+          m = mn;
+          if (__any(alpha != 1.f)) {  // rescale only when some running max moved
+#pragma unroll
+            for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
+          }
+#pragma unroll
+          for (int st = 0; st < 2; ++st) {
+            bf16x8 ph, pl;
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
-              const int key = (i < 4 ? key0 + i : key1 + i - 4);
-              if (key < kmin || key > kmax) vf[i] = (__bf16)0.0f;
+              const float pv = sacc[4 * (2 * st + (i >> 2)) + (i & 3)];
+              ph[i] = (__bf16)pv;
+              pl[i] = (__bf16)(pv - (float)ph[i]);
+            }
+            // this lane's keys: kh*32 + 16*st + 4*g + [0, 4) and the same + 8
+            const uint16_t* vcol = sV(cur) + tc * VSTR + kh * 32 + 16 * st + 4 * g;
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+              const uint2 a = *reinterpret_cast<const uint2*>(vcol + db * 32 * VSTR);
+              const uint2 b = *reinterpret_cast<const uint2*>(vcol + db * 32 * VSTR + 8);
+              const bf16x8 vf = __builtin_bit_cast(bf16x8, uint4{a.x, a.y, b.x, b.y});
+              oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, ph, oacc[db], 0, 0, 0);
+              oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pl, oacc[db], 0, 0, 0);
             }
           }
-          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, ph, oacc[db], 0, 0, 0);
-          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pl, oacc[db], 0, 0, 0);
         }
       }
+      if (it + 1 < ntiles) lstore(cur ^ 1, kb + KT);
+      __syncthreads();
     }
   }
-  if (!tok) return;
+  if (!tok || tb >= ntb) return;
   if (sink) {
     const float sl2 = sink[h] * 1.4426950408889634f;
     const float mn = fmaxf(m, sl2);
@@ -178,17 +272,35 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(
     }
 }
 
+static size_t attn_prefill_lds(int hd) {
+  return 2 * (size_t)KT * (hd + 8) * 2 + 2 * (size_t)hd * (KT + 4) * 2;
+}
+
 int launch_attn_prefill(int T, int Hq, int Hkv, int hd, int swa, int window, int fp8,
                         const uint16_t* q, const int32_t* pos, const int32_t* seq,
                         const void* kc, const void* vc, float k_scale, float v_scale, int S,
                         int Lmax, const float* sink, uint16_t* o, hipStream_t st) {
   const float score_scale = k_scale / sqrtf((float)hd) * 1.4426950408889634f;
   const int grp = Hq / Hkv;
-  const dim3 grid((T + 31) / 32, Hkv), block(64 * grp);
+  // waves per workgroup = grp * ntb <= 12; every thread stages at most 4 units
+  // of 8 elements, so 256 * grp * ntb >= 16 * hd
+  int ntb = (grp <= 6) ? 2 : 1;
+  while (256 * grp * ntb < 16 * hd) ++ntb;
+  if (grp * ntb > 12) return -1;
+  const dim3 grid((T + 32 * ntb - 1) / (32 * ntb), Hkv), block(64 * grp * ntb);
   const float vs = fp8 ? v_scale : 1.0f;
-#define PF(HD_, F8, SW)                                                                      \
-  hipLaunchKernelGGL((attn_prefill_kernel<HD_, F8, SW>), grid, block, 0, st, q, pos, seq, kc, \
-                     vc, S, Lmax, Hq, Hkv, window, score_scale, T, sink, vs, o)
+#define PF(HD_, F8, SW)                                                                       \
+  do {                                                                                         \
+    const size_t sh = attn_prefill_lds(HD_);                                                   \
+    static bool attr = false;                                                                  \
+    if (!attr) {                                                                               \
+      (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_prefill_kernel<HD_, F8, SW>), \
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)sh);          \
+      attr = true;                                                                             \
+    }                                                                                          \
+    hipLaunchKernelGGL((attn_prefill_kernel<HD_, F8, SW>), grid, block, sh, st, q, pos, seq,  \
+                       kc, vc, S, Lmax, Hq, Hkv, window, score_scale, T, ntb, sink, vs, o);    \
+  } while (0)
 #define BY_MODE(HD_)                                                  \
   if (fp8) {                                                         \
     if (swa) PF(HD_, true, true); else PF(HD_, true, false);         \

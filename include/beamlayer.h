@@ -152,7 +152,8 @@ int beam_qk_norm_rope_ssmax_kvwrite(const beam_dims* dims, int T, const uint16_t
  * q.k/sqrt(d), fp32 softmax and accumulation, o [T][Hq][d] bf16.
  * sink (optional, [Flint]): per-head fp32 logit added to the softmax
  * denominator only. max_pos >= max(pos) (host value used to size the grid).
- * ws >= beam_workspace_size(ATTN_SWA, T, max_pos + 1).
+ * ws >= beam_workspace_size(ATTN_SWA, T, max_pos + 1); ws may be NULL when that
+ * size is 0 (a span short enough for one pass, or the many-token kernel).
  * Errors: window <= 0, max_pos >= Lmax. */
 int beam_attn_swa(const beam_dims* dims, int T, const uint16_t* q, const int32_t* pos,
                   const int32_t* seq, const beam_kv* kv, const float* sink, uint16_t* o,

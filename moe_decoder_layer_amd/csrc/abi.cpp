@@ -94,6 +94,7 @@ int attn_span(const beam_dims* d, int swa, int max_ctx) {
 size_t ws_attn(const beam_dims* d, int swa, int T, int max_ctx) {
   if (T > beam::kGemvMaxT && d->Hkv > 0 && beam::attn_prefill_ok(d->Hq / d->Hkv, d->d))
     return 0;  // the many-token kernel needs no partials
+  if (attn_span(d, swa, max_ctx) <= beam::attn_direct_span()) return 0;
   const int nch = beam::attn_nch_bound(T, d->Hkv, attn_span(d, swa, max_ctx));
   return align256((size_t)T * d->Hq * nch * (d->d + 4) * 4);
 }
@@ -135,7 +136,7 @@ int attn_impl(const beam_dims* dims, int T, const uint16_t* q, const int32_t* po
               const int32_t* seq, const beam_kv* kv, const float* sink, uint16_t* o,
               int max_pos, void* ws, size_t ws_bytes, void* stream, int swa, const char* fn) {
   if (!dims) return fail(BEAM_E_NULL, "%s: dims is NULL", fn);
-  if (!q || !pos || !seq || !o || !ws) return fail(BEAM_E_NULL, "%s: NULL tensor argument", fn);
+  if (!q || !pos || !seq || !o) return fail(BEAM_E_NULL, "%s: NULL tensor argument", fn);
   if (misaligned(q) || misaligned(o) || misaligned(ws) || misaligned(sink))
     return fail(BEAM_E_ALIGN, "%s: tensor not 16-byte aligned", fn);
   int rc = check_dims_attn(dims, fn);
@@ -157,9 +158,10 @@ int attn_impl(const beam_dims* dims, int T, const uint16_t* q, const int32_t* po
   const int span = attn_span(dims, swa, max_pos + 1);
   int tpw, nch;
   beam::attn_plan(T, dims->Hkv, span, &tpw, &nch);
-  const size_t need = (size_t)T * dims->Hq * nch * (dims->d + 4) * 4;
-  if (ws_bytes < need)
-    return fail(BEAM_E_WORKSPACE, "%s: workspace %zu < %zu bytes", fn, ws_bytes, need);
+  const size_t need = (nch == 1) ? 0 : (size_t)T * dims->Hq * nch * (dims->d + 4) * 4;
+  if (need && (!ws || ws_bytes < need))
+    return fail(ws ? BEAM_E_WORKSPACE : BEAM_E_NULL, "%s: workspace %zu < %zu bytes", fn,
+                ws ? ws_bytes : 0, need);
   if ((rc = device_ready())) return rc;
   return launched(beam::launch_attn_decode(T, dims->Hq, dims->Hkv, dims->d, swa, dims->window,
                                            fp8, q, pos, seq, kv->k, kv->v,

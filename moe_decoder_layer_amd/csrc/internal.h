@@ -32,6 +32,7 @@ int launch_qk_epilogue(int T, int Hq, int Hkv, int hd, const uint16_t* qkv, cons
                        hipStream_t st);
 
 void attn_plan(int T, int Hkv, int span, int* tpw, int* nch);
+int attn_direct_span();  // spans up to this are taken in one pass (no partials)
 int attn_nch_bound(int T, int Hkv, int span);
 int launch_attn_decode(int T, int Hq, int Hkv, int hd, int swa, int window, int fp8,
                        const uint16_t* q, const int32_t* pos, const int32_t* seq,

@@ -27,28 +27,36 @@ namespace beam {
 BEAM_ERR_FLAG_DECL(attn)
 BEAM_ERR_FLAG_READER(attn)
 
-template <int HD, bool FP8, bool SWA>
-__global__ __launch_bounds__(256) void attn_decode_partial_kernel(
+// NW waves per workgroup; GS query-head slots kept for the LDS merge (>= group).
+// Split-K workgroups take contiguous runs of tpw tiles per wave; a one-pass
+// workgroup (o_direct != nullptr) deals the span's tiles round-robin to its
+// waves so no wave walks more than ceil(tiles / NW) of them.
+template <int HD, bool FP8, bool SWA, int NW, int GS>
+__global__ __launch_bounds__(NW * 64) void attn_decode_partial_kernel(
     const uint16_t* __restrict__ q, const int32_t* __restrict__ pos,
     const int32_t* __restrict__ seq, const void* __restrict__ kc, const void* __restrict__ vc,
     int S, int Lmax, int Hq, int Hkv, int window, int tpw, float score_scale, int nch_stride,
-    float* __restrict__ part) {
+    float* __restrict__ part, uint16_t* __restrict__ o_direct, const float* __restrict__ sink,
+    float v_scale) {
   constexpr int KS = HD / 32;  // k-steps of the score product
   constexpr int DT = HD / 16;  // 16-dim tiles of the output
   constexpr int GD = HD / 4;   // dims each lane group covers in the score product
-  __shared__ float sm_m[4][16], sm_l[4][16];
-  __shared__ float sm_o[4][16][HD + 4];
+  __shared__ float sm_m[NW][16], sm_l[NW][16];
+  __shared__ float sm_o[NW][GS][HD + 4];
 
   const int c = blockIdx.x, j = blockIdx.y, t = blockIdx.z;
   const int grp = Hq / Hkv;
   const int p = pos[t], s = seq[t];
   if (p < 0 || p >= Lmax || s < 0 || s >= S) {
     if (c == 0 && j == 0 && threadIdx.x == 0) BEAM_RAISE(attn, p < 0 || p >= Lmax ? ERR_POS : ERR_SEQ);
+    if (o_direct && c == 0)
+      for (int i = threadIdx.x; i < grp * HD; i += NW * 64)
+        o_direct[((size_t)t * Hq + j * grp) * HD + i] = 0;
     return;
   }
   const int lo = SWA ? max(0, p - window + 1) : 0;
   const int lo_al = lo & ~63;
-  const int CK = 256 * tpw;
+  const int CK = NW * 64 * tpw;
   const int nch = (p + 1 - lo_al + CK - 1) / CK;
   if (c >= nch) return;
 
@@ -72,25 +80,53 @@ __global__ __launch_bounds__(256) void attn_decode_partial_kernel(
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int tile0 = (lo_al >> 6) + (c * 4 + wave) * tpw;
+  const bool rr = (o_direct != nullptr);
+  const int tile0 = (lo_al >> 6) + (rr ? wave : (c * NW + wave) * tpw);
   for (int it = 0; it < tpw; ++it) {
-    const int kb = (tile0 + it) << 6;
+    const int kb = (tile0 + (rr ? it * NW : it)) << 6;
     if (kb > p) break;
+    // the tile's K and V fragments are all requested before any is used
+    bf16x8 kf[4][KS];
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      const size_t kr = (krow0 + kb + st * 16 + col) * HD + g * GD;
+#pragma unroll
+      for (int i = 0; i < KS; ++i) {
+        if constexpr (FP8) {
+          kf[st][i] =
+              e4m3x8_to_bf16x8(*reinterpret_cast<const uint2*>((const uint8_t*)kc + kr + i * 8));
+        } else {
+          kf[st][i] = as_bf16x8(ld16((const uint16_t*)kc + kr + i * 8));
+        }
+      }
+    }
+    bf16x8 vfr[2][DT];
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh) {
+      const int key0 = kb + kh * 32 + 4 * g, key1 = key0 + 16;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const size_t vr = (vrow0 + dt * 16 + col) * (size_t)Lmax;
+        if constexpr (FP8) {
+          const uint8_t* vb = (const uint8_t*)vc + vr;
+          const bf16x4 a = e4m3x4_to_bf16x4(*reinterpret_cast<const uint32_t*>(vb + key0));
+          const bf16x4 b = e4m3x4_to_bf16x4(*reinterpret_cast<const uint32_t*>(vb + key1));
+          vfr[kh][dt] = bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+        } else {
+          const uint16_t* vb = (const uint16_t*)vc + vr;
+          const uint2 a = *reinterpret_cast<const uint2*>(vb + key0);
+          const uint2 b = *reinterpret_cast<const uint2*>(vb + key1);
+          vfr[kh][dt] = __builtin_bit_cast(bf16x8, uint4{a.x, a.y, b.x, b.y});
+        }
+      }
+    }
     f32x4 sacc[4];
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
       sacc[st] = f32x4{0.f, 0.f, 0.f, 0.f};
-      const size_t kr = (krow0 + kb + st * 16 + col) * HD + g * GD;
 #pragma unroll
-      for (int i = 0; i < KS; ++i) {
-        bf16x8 kf;
-        if constexpr (FP8) {
-          kf = e4m3x8_to_bf16x8(*reinterpret_cast<const uint2*>((const uint8_t*)kc + kr + i * 8));
-        } else {
-          kf = as_bf16x8(ld16((const uint16_t*)kc + kr + i * 8));
-        }
-        sacc[st] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[i], sacc[st], 0, 0, 0);
-      }
+      for (int i = 0; i < KS; ++i)
+        sacc[st] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[st][i], qf[i], sacc[st], 0, 0, 0);
     }
     // scores (log2 domain), window mask, online softmax
     float mx = -INFINITY;
@@ -139,19 +175,7 @@ __global__ __launch_bounds__(256) void attn_decode_partial_kernel(
       const int key0 = kb + kh * 32 + 4 * g, key1 = key0 + 16;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
-        const size_t vr = (vrow0 + dt * 16 + col) * (size_t)Lmax;
-        bf16x8 vf;
-        if constexpr (FP8) {
-          const uint8_t* vb = (const uint8_t*)vc + vr;
-          const bf16x4 a = e4m3x4_to_bf16x4(*reinterpret_cast<const uint32_t*>(vb + key0));
-          const bf16x4 b = e4m3x4_to_bf16x4(*reinterpret_cast<const uint32_t*>(vb + key1));
-          vf = bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-        } else {
-          const uint16_t* vb = (const uint16_t*)vc + vr;
-          const uint2 a = *reinterpret_cast<const uint2*>(vb + key0);
-          const uint2 b = *reinterpret_cast<const uint2*>(vb + key1);
-          vf = __builtin_bit_cast(bf16x8, uint4{a.x, a.y, b.x, b.y});
-        }
+        bf16x8 vf = vfr[kh][dt];
         if (edge) {  // keys outside [lo, p] may hold anything: zero them
 #pragma unroll
           for (int i = 0; i < 8; ++i) {
@@ -172,19 +196,31 @@ __global__ __launch_bounds__(256) void attn_decode_partial_kernel(
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) sm_o[wave][col][dt * 16 + 4 * g + r] = o[dt][r];
+    for (int r = 0; r < 4; ++r)
+      if (col < GS) sm_o[wave][col][dt * 16 + 4 * g + r] = o[dt][r];
   __syncthreads();
-  for (int i = threadIdx.x; i < grp * HD; i += 256) {
+  for (int i = threadIdx.x; i < grp * HD; i += NW * 64) {
     const int hh = i / HD, dim = i - hh * HD;
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) M = fmaxf(M, sm_m[w][hh]);
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, sm_m[w][hh]);
     float L = 0.f, O = 0.f;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
+    for (int w = 0; w < NW; ++w) {
       const float e = (sm_m[w][hh] == -INFINITY) ? 0.f : exp2f(sm_m[w][hh] - M);
       L += e * sm_l[w][hh];
       O += e * sm_o[w][hh][dim];
+    }
+    if (o_direct) {  // the whole span was this workgroup's: normalise and store
+      if (sink) {
+        const float sl2 = sink[j * grp + hh] * 1.4426950408889634f;
+        const float Mn = fmaxf(M, sl2);
+        const float a = exp2f(M - Mn);
+        L = L * a + exp2f(sl2 - Mn);
+        O *= a;
+      }
+      o_direct[((size_t)t * Hq + j * grp + hh) * HD + dim] = f2bf(O * (v_scale / L));
+      continue;
     }
     float* rec = part + (((size_t)t * Hq + j * grp + hh) * nch_stride + c) * (HD + 4);
     if (dim == 0) {
@@ -238,8 +274,18 @@ __global__ __launch_bounds__(64) void attn_merge_kernel(
   }
 }
 
+// Keys per workgroup at or below which a token's span is taken in one pass
+// (outputs written directly, no merge).
+constexpr int kDirectSpan = 1024;
+int attn_direct_span() { return kDirectSpan + 63; }
+
 void attn_plan(int T, int Hkv, int span, int* tpw, int* nch) {
   const int tiles = (span + 63) / 64;
+  if (span <= kDirectSpan + 63) {  // one pass: 8 waves, tiles dealt round-robin
+    *tpw = std::max(1, (tiles + 7) / 8);
+    *nch = 1;
+    return;
+  }
   const int target = std::max(1, 2048 / std::max(1, Hkv * T));
   int w = (tiles + 4 * target - 1) / (4 * target);
   w = std::min(std::max(w, 1), 64);
@@ -262,9 +308,19 @@ int launch_attn_decode(int T, int Hq, int Hkv, int hd, int swa, int window, int 
   attn_plan(T, Hkv, span, &tpw, &nch);
   const float score_scale = k_scale / sqrtf((float)hd) * 1.4426950408889634f;
   const dim3 grid(nch, Hkv, T);
+  const bool direct = (nch == 1);
+  uint16_t* od = direct ? o : nullptr;
+  const float vsc = fp8 ? v_scale : 1.0f;
 #define PART(HD_, F8, SW)                                                                    \
-  hipLaunchKernelGGL((attn_decode_partial_kernel<HD_, F8, SW>), grid, dim3(256), 0, st, q,  \
-                     pos, seq, kc, vc, S, Lmax, Hq, Hkv, window, tpw, score_scale, nch, part)
+  if (direct && Hq / Hkv <= 8)                                                               \
+    hipLaunchKernelGGL((attn_decode_partial_kernel<HD_, F8, SW, 8, 8>), grid, dim3(512), 0,  \
+                       st, q, pos, seq, kc, vc, S, Lmax, Hq, Hkv, window, tpw, score_scale,  \
+                       nch, part, od, sink, vsc);                                            \
+  else                                                                                       \
+    hipLaunchKernelGGL((attn_decode_partial_kernel<HD_, F8, SW, 4, 16>), grid, dim3(256), 0, \
+                       st, q, pos, seq, kc, vc, S, Lmax, Hq, Hkv, window,                    \
+                       direct ? std::max(1, (tpw * 8 + 3) / 4) : tpw, score_scale, nch,      \
+                       part, od, sink, vsc)
 #define BY_MODE(HD_)                                    \
   if (fp8) {                                           \
     if (swa) PART(HD_, true, true); else PART(HD_, true, false);   \
@@ -277,6 +333,7 @@ int launch_attn_decode(int T, int Hq, int Hkv, int hd, int swa, int window, int 
 #undef BY_MODE
 #undef PART
   if (hipGetLastError() != hipSuccess) return -1;
+  if (direct) return 0;
   const dim3 mg(Hq, T);
   const float vs = fp8 ? v_scale : 1.0f;
   if (hd == 128)

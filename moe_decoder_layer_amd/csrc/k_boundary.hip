@@ -31,7 +31,8 @@ __device__ __forceinline__ uint4 pack8(const float* f) {
                pack_bf2(f[6], f[7])};
 }
 
-// mode: 0 = entry (pre-norm of h only), 1 = post-norm + add, 2 = add without post-norm
+// mode: 0 = entry (pre-norm of h only), 1 = post-norm + add, 2 = add without post-norm.
+// Every input row is requested up front so the kernel pays one memory latency.
 __global__ __launch_bounds__(BT) void boundary_kernel(
     int D, const uint16_t* __restrict__ y, const uint16_t* __restrict__ w_post,
     uint16_t* __restrict__ h, const uint16_t* __restrict__ w_pre,
@@ -39,50 +40,52 @@ __global__ __launch_bounds__(BT) void boundary_kernel(
   __shared__ float red[4];
   const int nc = D >> 3;
   const size_t row = (size_t)blockIdx.x * D;
+  uint4 yr[CPT], hr[CPT], wpr[CPT], wnr[CPT];
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) {
+    const int c = threadIdx.x + i * BT;
+    const bool in = c < nc;
+    const uint4 z = {0u, 0u, 0u, 0u};
+    hr[i] = in ? ld16(h + row + c * 8) : z;
+    wnr[i] = in ? ld16(w_pre + c * 8) : z;
+    yr[i] = (in && mode != 0) ? ld16(y + row + c * 8) : z;
+    wpr[i] = (in && mode == 1) ? ld16(w_post + c * 8) : z;
+  }
   float hv[CPT][8];
-  float ss = 0.f;
   if (mode == 1) {
     float yv[CPT][8];
+    float ss = 0.f;
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
-      const int c = threadIdx.x + i * BT;
-      if (c < nc) {
-        unpack8(ld16(y + row + c * 8), yv[i]);
+      unpack8(yr[i], yv[i]);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) ss += yv[i][e] * yv[i][e];
-      }
+      for (int e = 0; e < 8; ++e) ss += yv[i][e] * yv[i][e];
     }
     const float r = rsqrtf(block_sum(ss, red) / D + eps);
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
-      const int c = threadIdx.x + i * BT;
-      if (c < nc) {
-        float wv[8], hh[8];
-        unpack8(ld16(w_post + c * 8), wv);
-        unpack8(ld16(h + row + c * 8), hh);
+      float wv[8], hh[8];
+      unpack8(wpr[i], wv);
+      unpack8(hr[i], hh);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float a = round_bf(yv[i][e] * r * wv[e]);
-          hv[i][e] = round_bf(c_h * hh[e] + c_a * a);
-        }
+      for (int e = 0; e < 8; ++e) {
+        const float a = round_bf(yv[i][e] * r * wv[e]);
+        hv[i][e] = round_bf(c_h * hh[e] + c_a * a);
       }
     }
   } else {
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
-      const int c = threadIdx.x + i * BT;
-      if (c < nc) {
-        unpack8(ld16(h + row + c * 8), hv[i]);
-        if (mode == 2) {
-          float yv[8];
-          unpack8(ld16(y + row + c * 8), yv);
+      unpack8(hr[i], hv[i]);
+      if (mode == 2) {
+        float yv[8];
+        unpack8(yr[i], yv);
 #pragma unroll
-          for (int e = 0; e < 8; ++e) hv[i][e] = round_bf(c_h * hv[i][e] + c_a * yv[e]);
-        }
+        for (int e = 0; e < 8; ++e) hv[i][e] = round_bf(c_h * hv[i][e] + c_a * yv[e]);
       }
     }
   }
-  ss = 0.f;
+  float ss = 0.f;
 #pragma unroll
   for (int i = 0; i < CPT; ++i) {
     const int c = threadIdx.x + i * BT;
@@ -97,7 +100,7 @@ __global__ __launch_bounds__(BT) void boundary_kernel(
     const int c = threadIdx.x + i * BT;
     if (c < nc) {
       float wv[8], xo[8];
-      unpack8(ld16(w_pre + c * 8), wv);
+      unpack8(wnr[i], wv);
 #pragma unroll
       for (int e = 0; e < 8; ++e) xo[e] = hv[i][e] * r * wv[e];
       if (mode != 0) *reinterpret_cast<uint4*>(h + row + c * 8) = pack8(hv[i]);

@@ -52,15 +52,18 @@ __global__ __launch_bounds__(256) void qk_norm_pos_kvwrite_kernel(
     return;
   }
   const bool is_q = head < Hq;
-  const float r = rsqrtf(wave_sum(a * a + b * b) / hd + eps);
+  // gains and the RoPE row are requested before the reduction needs `a`, `b`
   const uint16_t* w = is_q ? wq : wk;
+  const float wa = act ? bf2f(w[lane]) : 0.f, wb = act ? bf2f(w[lane + half]) : 0.f;
+  const bool rot = (mode == 0) && slot_ok && act;
+  const float c = rot ? rope_cs[(size_t)p * hd + lane] : 1.f;
+  const float sn = rot ? rope_cs[(size_t)p * hd + half + lane] : 0.f;
+  const float r = rsqrtf(wave_sum(a * a + b * b) / hd + eps);
   if (act) {
-    a = a * r * bf2f(w[lane]);
-    b = b * r * bf2f(w[lane + half]);
+    a = a * r * wa;
+    b = b * r * wb;
     if (mode == 0) {  // RoPE at position p (table row p: cos then sin)
       if (slot_ok) {
-        const float c = rope_cs[(size_t)p * hd + lane];
-        const float sn = rope_cs[(size_t)p * hd + half + lane];
         const float a2 = a * c - b * sn;
         const float b2 = b * c + a * sn;
         a = a2;

@@ -7,9 +7,10 @@
 //  router_logits_gemv   few tokens: one workgroup per expert row, the fp32 row
 //                       streamed once, K split over 4 waves, fixed-order sum
 //  router_logits_gemm   many tokens: 64x64 fp32 tiles staged through LDS
-//  router_topk          one wave per token: group scores (sum of the two best
-//                       biased scores), top groups, top experts by wave-wide
-//                       arg-max with ties to the lower index
+//  router_topk          one workgroup per token, one thread per expert: group
+//                       scores (sum of the two best biased scores), top groups
+//                       by rank, top experts by block-wide arg-max rounds
+//                       (ties to the lower index)
 #include "common.h"
 #include "internal.h"
 
@@ -96,100 +97,91 @@ __global__ __launch_bounds__(RT) void router_logits_gemm_kernel(
     }
 }
 
-// Wave-wide arg-max: larger value wins, equal values go to the lower index.
-__device__ __forceinline__ void wave_argmax(float& v, int& i) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const float v2 = __shfl_xor(v, o, 64);
-    const int i2 = __shfl_xor(i, o, 64);
-    if (v2 > v || (v2 == v && i2 < i)) {
-      v = v2;
-      i = i2;
-    }
-  }
-}
-
 constexpr int EMAX = 1024;
 
-__global__ __launch_bounds__(RT) void router_topk_kernel(
+// One workgroup per token, one thread per expert. Groups are chosen by rank
+// (the number of groups that beat a group: larger score, or equal score and
+// lower index); experts by topk rounds of a block-wide arg-max. Both break
+// ties towards the lower index, and experts come out in selection order.
+__global__ __launch_bounds__(EMAX) void router_topk_kernel(
     const float* __restrict__ logits, const float* __restrict__ bcorr, int T, int E, int ng,
     int tg, int K, float route_scale, int32_t* __restrict__ idx, float* __restrict__ wout) {
-  __shared__ float s_raw[4][EMAX];
-  __shared__ float s_b[4][EMAX];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + wave;
-  if (t < T) {
-    for (int e = lane; e < E; e += 64) {
-      const float lg = logits[(size_t)t * E + e];
-      const float sv = 1.0f / (1.0f + expf(-lg));
-      s_raw[wave][e] = sv;
-      s_b[wave][e] = sv + (bcorr ? bcorr[e] : 0.f);
-    }
+  __shared__ float s_b[EMAX];
+  __shared__ float g1[64], g2[64], gsc[64], ssel[32];
+  __shared__ float wv_best[EMAX / 64];
+  __shared__ int wi_best[EMAX / 64];
+  const int t = blockIdx.x, e = threadIdx.x;
+  const bool act = e < E;
+  const int gs = E / ng;
+  const int grp = act ? e / gs : 0;
+  float sv = 0.f, sb = -INFINITY;
+  if (act) {
+    const float lg = logits[(size_t)t * E + e];
+    sv = 1.0f / (1.0f + expf(-lg));
+    sb = sv + (bcorr ? bcorr[e] : 0.f);
+    s_b[e] = sb;
   }
   __syncthreads();
-  if (t >= T) return;
-  const int gs = E / ng;
-  // group score: the two largest biased scores of the group, summed
-  float gsc = -INFINITY;
-  if (lane < ng) {
-    float b1 = -INFINITY, b2 = -INFINITY;
-    for (int e = lane * gs; e < (lane + 1) * gs; ++e) {
-      const float v = s_b[wave][e];
-      if (v > b1) {
-        b2 = b1;
-        b1 = v;
-      } else if (v > b2) {
-        b2 = v;
+  // rank inside the group -> the group's two best biased scores
+  if (act) {
+    int r = 0;
+    const int g0 = grp * gs;
+    for (int m = g0; m < g0 + gs; ++m) {
+      const float v = s_b[m];
+      r += (v > sb) || (v == sb && m < e);
+    }
+    if (r == 0) g1[grp] = sb;
+    if (r == 1) g2[grp] = sb;
+  }
+  __syncthreads();
+  if (e < ng) gsc[e] = (gs >= 2) ? g1[e] + g2[e] : g1[e];
+  __syncthreads();
+  // group rank -> kept groups; candidates are the kept groups' experts
+  bool kept = false;
+  if (act) {
+    const float my = gsc[grp];
+    int r = 0;
+    for (int h = 0; h < ng; ++h) r += (gsc[h] > my) || (gsc[h] == my && h < grp);
+    kept = r < tg;
+  }
+  // topk rounds of a block-wide arg-max over the kept experts' biased scores
+  float v = kept ? sb : -INFINITY;
+  const int lane = e & 63, wave = e >> 6, nw = blockDim.x >> 6;
+  for (int k = 0; k < K; ++k) {
+    float bv = v;
+    int bi = act ? e : 0x7fffffff;
+#pragma unroll
+    for (int o2 = 32; o2 > 0; o2 >>= 1) {
+      const float v2 = __shfl_xor(bv, o2, 64);
+      const int i2 = __shfl_xor(bi, o2, 64);
+      if (v2 > bv || (v2 == bv && i2 < bi)) {
+        bv = v2;
+        bi = i2;
       }
     }
-    gsc = (gs >= 2) ? b1 + b2 : b1;
-  }
-  uint64_t kept = 0;
-  for (int r = 0; r < tg; ++r) {
-    float v = gsc;
-    int i = (lane < ng) ? lane : 1 << 30;
-    wave_argmax(v, i);
-    kept |= 1ull << i;
-    if (lane == i) gsc = -INFINITY;
-  }
-  // candidates: experts of the kept groups; lane holds e = lane + 64*k
-  constexpr int PER = EMAX / 64;
-  float cand[PER];
-#pragma unroll
-  for (int k = 0; k < PER; ++k) {
-    const int e = lane + 64 * k;
-    cand[k] = (e < E && ((kept >> (e / gs)) & 1ull)) ? s_b[wave][e] : -INFINITY;
-  }
-  int myidx = 0;
-  float mys = 0.f;
-  float ssum = 0.f;
-  for (int r = 0; r < K; ++r) {
-    float v = -INFINITY;
-    int i = 1 << 30;
-#pragma unroll
-    for (int k = 0; k < PER; ++k) {
-      const int e = lane + 64 * k;
-      if (cand[k] > v || (cand[k] == v && e < i)) {
-        v = cand[k];
-        i = e;
+    if (lane == 0) {
+      wv_best[wave] = bv;
+      wi_best[wave] = bi;
+    }
+    __syncthreads();
+    float gv = wv_best[0];
+    int gi = wi_best[0];
+    for (int w2 = 1; w2 < nw; ++w2)
+      if (wv_best[w2] > gv || (wv_best[w2] == gv && wi_best[w2] < gi)) {
+        gv = wv_best[w2];
+        gi = wi_best[w2];
       }
+    if (e == gi) {
+      v = -INFINITY;
+      idx[(size_t)t * K + k] = e;
+      ssel[k] = sv;
     }
-    wave_argmax(v, i);
-    if ((i & 63) == lane) {
-#pragma unroll
-      for (int k = 0; k < PER; ++k)
-        if (lane + 64 * k == i) cand[k] = -INFINITY;
-    }
-    const float si = s_raw[wave][i];
-    ssum += si;
-    if (lane == r) {
-      myidx = i;
-      mys = si;
-    }
+    __syncthreads();
   }
-  if (lane < K) {
-    idx[(size_t)t * K + lane] = myidx;
-    wout[(size_t)t * K + lane] = route_scale * mys / ssum;
+  if (e < K) {
+    float sum = 0.f;
+    for (int k = 0; k < K; ++k) sum += ssel[k];
+    wout[(size_t)t * K + e] = route_scale * ssel[e] / sum;
   }
 }
 
@@ -204,8 +196,9 @@ int launch_router(int T, int E, int D, int ng, int tg, int K, float route_scale,
                        0, st, X, Wr, T, E, D, logits);
   }
   if (hipGetLastError() != hipSuccess) return -1;
-  hipLaunchKernelGGL(router_topk_kernel, dim3((T + 3) / 4), dim3(RT), 0, st, logits, bcorr, T, E,
-                     ng, tg, K, route_scale, idx, w);
+  const int threads = ((E + 63) / 64) * 64;
+  hipLaunchKernelGGL(router_topk_kernel, dim3(T), dim3(threads), 0, st, logits, bcorr, T, E, ng,
+                     tg, K, route_scale, idx, w);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

@@ -82,13 +82,19 @@ def test_qkv_validation():
 def test_attention_router_moe_validation():
     d = _dims()
     by = ctypes.byref(d)
-    kv = B.kv_struct(A, A, B.BEAM_KV_BF16, 1.0, 1.0, 1, 128)
-    ws = B.beam_workspace_size(d, B.BEAM_OP_ATTN_NOPE, 1, 65)
-    assert _rc("beam_attn_nope_ssmax", by, 1, A, A, A, ctypes.byref(kv), None, A, 128, A, ws,
+    kv = B.kv_struct(A, A, B.BEAM_KV_BF16, 1.0, 1.0, 1, 8192)
+    ws = B.beam_workspace_size(d, B.BEAM_OP_ATTN_NOPE, 1, 8000)
+    assert _rc("beam_attn_nope_ssmax", by, 1, A, A, A, ctypes.byref(kv), None, A, 8192, A, ws,
                None) == -2                                     # max_pos >= Lmax
-    assert _rc("beam_attn_nope_ssmax", by, 1, A, A, A, ctypes.byref(kv), None, A, 64, A, 16,
+    # a long context is split over workgroups and needs the partials workspace
+    assert _rc("beam_attn_nope_ssmax", by, 1, A, A, A, ctypes.byref(kv), None, A, 7999, A, 16,
                None) == -5
-    assert _rc("beam_attn_nope_ssmax", by, 1, A, A, A, ctypes.byref(kv), None, A, 64, A, ws,
+    assert _rc("beam_attn_nope_ssmax", by, 1, A, A, A, ctypes.byref(kv), None, A, 7999, None, 0,
+               None) == -1
+    assert _rc("beam_attn_nope_ssmax", by, 1, A, A, A, ctypes.byref(kv), None, A, 7999, A, ws,
+               None) == -7
+    # a short one is taken in one pass and needs none
+    assert _rc("beam_attn_nope_ssmax", by, 1, A, A, A, ctypes.byref(kv), None, A, 64, None, 0,
                None) == -7
     dw = _dims(window=0)
     assert _rc("beam_attn_swa", ctypes.byref(dw), 1, A, A, A, ctypes.byref(kv), None, A, 64, A,
@@ -120,7 +126,7 @@ def test_workspace_sizes():
     assert B.beam_workspace_size(d, B.BEAM_OP_QKV, 1) >= (48 + 16) * 128 * 2
     a = B.beam_workspace_size(d, B.BEAM_OP_ATTN_NOPE, 1, 100001)
     s = B.beam_workspace_size(d, B.BEAM_OP_ATTN_SWA, 1, 100001)
-    assert a > s > 0
+    assert a > 0 and s == 0     # a 512-key window is taken in one pass: no partials
     # monotone in the context bound
     sizes = [B.beam_workspace_size(d, B.BEAM_OP_ATTN_NOPE, 1, c) for c in range(1000, 200000, 997)]
     assert all(x <= y for x, y in zip(sizes, sizes[1:]))

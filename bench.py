@@ -131,7 +131,7 @@ def main():
     rope_h = np.zeros((Lmax, dims.d), np.float32)
     B.beam_rope_table(rope_h, Lmax, dims.d, dims.theta)
     rope = torch.from_numpy(rope_h).cuda()
-    wsz = lambda op, ctx=0: torch.empty(max(256, B.beam_workspace_size(dims, op, 1, ctx)),  # noqa
+    wsz = lambda op, ctx=0: torch.zeros(max(256, B.beam_workspace_size(dims, op, 1, ctx)),  # noqa
                                         dtype=torch.uint8, device="cuda")
     ws_qkv, ws_attn = wsz(B.BEAM_OP_QKV), wsz(B.BEAM_OP_ATTN_SWA, pos0 + 1)
     ws_r, ws_moe = wsz(B.BEAM_OP_ROUTER), wsz(B.BEAM_OP_MOE)
@@ -314,7 +314,7 @@ def prefill_leg(a):
         y2 = torch.empty((T, dims.D), **I16)
         idx = torch.empty((T, dims.topk), dtype=torch.int32, device="cuda")
         w = torch.empty((T, dims.topk), dtype=torch.float32, device="cuda")
-        wsz = lambda op, dd=dims: torch.empty(  # noqa: E731
+        wsz = lambda op, dd=dims: torch.zeros(  # noqa: E731
             max(256, B.beam_workspace_size(dd, op, T, prior + C)), dtype=torch.uint8, device="cuda")
         ws_q, ws_a, ws_o, ws_r = (wsz(B.BEAM_OP_QKV), wsz(B.BEAM_OP_ATTN_NOPE),
                                   wsz(B.BEAM_OP_OUT_GATE), wsz(B.BEAM_OP_ROUTER))

@@ -21,8 +21,13 @@
  *    contiguous and 16-byte aligned. Structs (beam_dims, beam_kv) live in host
  *    memory; their pointer fields are device pointers. The library allocates
  *    nothing: calls that need scratch take a caller-owned device workspace
- *    (`ws`, `ws_bytes`), sized by beam_workspace_size(). Workspace contents on
- *    entry are ignored and on exit undefined.
+ *    (`ws`, `ws_bytes`), sized by beam_workspace_size(). A workspace starts
+ *    with a 1024-byte block of counters (used where the last workgroup to
+ *    finish combines the others' partial results) that must hold zeros when a
+ *    call starts; every call that completes leaves it zeroed, so zero-fill a
+ *    workspace once when it is allocated (and again after a device fault).
+ *    The rest of its contents is ignored on entry and undefined on exit. One
+ *    workspace may serve every call that is ordered on one stream.
  *  - Streams: `stream` is a hipStream_t (NULL = the null stream). Every call
  *    only enqueues kernels on it: no host synchronisation, no allocation, no
  *    memset, so every call may be captured into a HIP graph. Inputs must not
@@ -152,8 +157,8 @@ int beam_qk_norm_rope_ssmax_kvwrite(const beam_dims* dims, int T, const uint16_t
  * q.k/sqrt(d), fp32 softmax and accumulation, o [T][Hq][d] bf16.
  * sink (optional, [Flint]): per-head fp32 logit added to the softmax
  * denominator only. max_pos >= max(pos) (host value used to size the grid).
- * ws >= beam_workspace_size(ATTN_SWA, T, max_pos + 1); ws may be NULL when that
- * size is 0 (a span short enough for one pass, or the many-token kernel).
+ * ws >= beam_workspace_size(ATTN_SWA, T, max_pos + 1) (counter block and
+ * split-K partials).
  * Errors: window <= 0, max_pos >= Lmax. */
 int beam_attn_swa(const beam_dims* dims, int T, const uint16_t* q, const int32_t* pos,
                   const int32_t* seq, const beam_kv* kv, const float* sink, uint16_t* o,
@@ -184,7 +189,8 @@ int beam_out_gate(const beam_dims* dims, int T, const uint16_t* o, const uint16_
  *   w = route_scale * s / sum(s) over the picked experts.
  * Ties go to the lower index; idx [T][topk] int32 ordered by s' descending,
  * w [T][topk] fp32, logits [T][E] fp32 (optional output).
- * ws >= beam_workspace_size(ROUTER). Errors: E % n_group; topk_group >
+ * ws >= beam_workspace_size(ROUTER) (1024 bytes, the counter block, suffice
+ * when logits is given). Errors: E % n_group; topk_group >
  * n_group; topk > topk_group*E/n_group; topk > 32; E > 1024. */
 int beam_router_fp32_grouped_topk(const beam_dims* dims, int T, const uint16_t* x,
                                   const float* w_r, const float* b_corr, int32_t* idx,

@@ -85,21 +85,28 @@ int check_kv(const beam_kv* kv, const char* fn) {
   return BEAM_OK;
 }
 
+// Every workspace is [kCtlBytes of counters][the call's data].
+constexpr size_t kCtl = beam::kCtlBytes;
+char* ws_data(void* ws) { return (char*)ws + kCtl; }
+unsigned* ws_ctl(void* ws) { return (unsigned*)ws; }
+
 size_t ws_qkv(const beam_dims* d, int T) {
-  return align256((size_t)T * (d->Hq + 2 * d->Hkv) * d->d * 2);
+  return kCtl + align256((size_t)T * (d->Hq + 2 * d->Hkv) * d->d * 2);
 }
 int attn_span(const beam_dims* d, int swa, int max_ctx) {
   return swa ? std::min(max_ctx, d->window + 63) : max_ctx;
 }
 size_t ws_attn(const beam_dims* d, int swa, int T, int max_ctx) {
   if (T > beam::kGemvMaxT && d->Hkv > 0 && beam::attn_prefill_ok(d->Hq / d->Hkv, d->d))
-    return 0;  // the many-token kernel needs no partials
-  if (attn_span(d, swa, max_ctx) <= beam::attn_direct_span()) return 0;
+    return kCtl;  // the many-token kernel needs no partials
   const int nch = beam::attn_nch_bound(T, d->Hkv, attn_span(d, swa, max_ctx));
-  return align256((size_t)T * d->Hq * nch * (d->d + 4) * 4);
+  if (nch == 1) return kCtl;
+  return kCtl + align256((size_t)T * d->Hq * nch * (d->d + 4) * 4);
 }
-size_t ws_out_gate(const beam_dims* d, int T) { return align256((size_t)T * d->Hq * d->d * 2); }
-size_t ws_router(const beam_dims* d, int T) { return align256((size_t)T * d->E * 4); }
+size_t ws_out_gate(const beam_dims* d, int T) {
+  return kCtl + align256((size_t)T * d->Hq * d->d * 2);
+}
+size_t ws_router(const beam_dims* d, int T) { return kCtl + align256((size_t)T * d->E * 4); }
 
 // Many-token MoE workspace, in order: counts[E], seg_off[E+1], tile_off[E+1],
 // perm[P], inv[P] (int32); act[P][F] bf16; out[P][D] fp32; shared expert
@@ -127,10 +134,10 @@ bool moe_many(const beam_dims* d, int T) {
   return T > beam::kGemvMaxT && d->D % 64 == 0 && d->F % 64 == 0;
 }
 size_t ws_moe(const beam_dims* d, int T) {
-  if (moe_many(d, T)) return moe_ws_layout(d, T).total;
-  return align256((size_t)T * (d->topk + 1) * d->F * 2);
+  if (moe_many(d, T)) return kCtl + moe_ws_layout(d, T).total;
+  return kCtl + align256((size_t)T * (d->topk + 1) * d->F * 2);
 }
-size_t ws_dense(int T, int Fd) { return align256((size_t)T * Fd * 2); }
+size_t ws_dense(int T, int Fd) { return kCtl + align256((size_t)T * Fd * 2); }
 
 int attn_impl(const beam_dims* dims, int T, const uint16_t* q, const int32_t* pos,
               const int32_t* seq, const beam_kv* kv, const float* sink, uint16_t* o,
@@ -148,6 +155,9 @@ int attn_impl(const beam_dims* dims, int T, const uint16_t* q, const int32_t* po
     return fail(BEAM_E_SHAPE, "%s: max_pos %d outside [0, Lmax)", fn, max_pos);
   const int fp8 = kv->dtype == BEAM_KV_FP8_E4M3;
   if (T > beam::kGemvMaxT && beam::attn_prefill_ok(dims->Hq / dims->Hkv, dims->d)) {
+    if (!ws || ws_bytes < kCtl)
+      return fail(ws ? BEAM_E_WORKSPACE : BEAM_E_NULL, "%s: workspace %zu < %zu bytes", fn,
+                  ws ? ws_bytes : 0, kCtl);
     if ((rc = device_ready())) return rc;
     return launched(beam::launch_attn_prefill(T, dims->Hq, dims->Hkv, dims->d, swa, dims->window,
                                               fp8, q, pos, seq, kv->k, kv->v,
@@ -156,17 +166,16 @@ int attn_impl(const beam_dims* dims, int T, const uint16_t* q, const int32_t* po
                     fn);
   }
   const int span = attn_span(dims, swa, max_pos + 1);
-  int tpw, nch;
-  beam::attn_plan(T, dims->Hkv, span, &tpw, &nch);
-  const size_t need = (nch == 1) ? 0 : (size_t)T * dims->Hq * nch * (dims->d + 4) * 4;
-  if (need && (!ws || ws_bytes < need))
+  const size_t need = ws_attn(dims, swa, T, max_pos + 1);
+  if (!ws || ws_bytes < need)
     return fail(ws ? BEAM_E_WORKSPACE : BEAM_E_NULL, "%s: workspace %zu < %zu bytes", fn,
                 ws ? ws_bytes : 0, need);
   if ((rc = device_ready())) return rc;
   return launched(beam::launch_attn_decode(T, dims->Hq, dims->Hkv, dims->d, swa, dims->window,
                                            fp8, q, pos, seq, kv->k, kv->v,
                                            fp8 ? kv->k_scale : 1.f, fp8 ? kv->v_scale : 1.f,
-                                           kv->S, kv->Lmax, sink, o, span, (float*)ws, S_(stream)),
+                                           kv->S, kv->Lmax, sink, o, span, (float*)ws_data(ws),
+                                           ws_ctl(ws), S_(stream)),
                   fn);
 }
 
@@ -235,7 +244,7 @@ int beam_qk_norm_rope_ssmax_kvwrite(const beam_dims* dims, int T, const uint16_t
                 ws_qkv(dims, T));
   if ((rc = device_ready())) return rc;
   const int Nqkv = (dims->Hq + 2 * dims->Hkv) * dims->d;
-  uint16_t* qkv = (uint16_t*)ws;
+  uint16_t* qkv = (uint16_t*)ws_data(ws);
   const int rcg = (T > beam::kGemvMaxT && dims->D % 64 == 0)
                       ? beam::launch_gemm_bf16(T, Nqkv + dims->G, dims->D, x, dims->D, w_qkvg,
                                                dims->D, qkv, Nqkv, g_out, dims->G, Nqkv,
@@ -295,9 +304,10 @@ int beam_out_gate(const beam_dims* dims, int T, const uint16_t* o, const uint16_
     }
     if ((rc = device_ready())) return rc;
     if (dims->G) {
-      if (beam::launch_gate(T, dims->Hq, dims->d, o, g, b_gate, (uint16_t*)ws, S_(stream)))
+      if (beam::launch_gate(T, dims->Hq, dims->d, o, g, b_gate, (uint16_t*)ws_data(ws),
+                            S_(stream)))
         return launched(-1, __func__);
-      a = (const uint16_t*)ws;
+      a = (const uint16_t*)ws_data(ws);
     }
     return launched(beam::launch_gemm_bf16(T, dims->D, K, a, K, w_o, K, y, dims->D, nullptr, 0,
                                            dims->D, S_(stream)),
@@ -331,18 +341,15 @@ int beam_router_fp32_grouped_topk(const beam_dims* dims, int T, const uint16_t* 
   UNSUP(K <= 32, "%s: topk > 32", __func__);
   UNSUP(E <= 1024 && ng <= 64, "%s: E > 1024 or n_group > 64", __func__);
   UNSUP(dims->D > 0 && dims->D % 8 == 0, "%s: D must be a positive multiple of 8", __func__);
-  float* lg = logits;
-  if (!lg) {
-    REQ(ws);
-    if (ws_bytes < ws_router(dims, T))
-      return fail(BEAM_E_WORKSPACE, "%s: workspace %zu < %zu bytes", __func__, ws_bytes,
-                  ws_router(dims, T));
-    lg = (float*)ws;
-  }
+  REQ(ws);
+  const size_t need = logits ? kCtl : ws_router(dims, T);
+  if (ws_bytes < need)
+    return fail(BEAM_E_WORKSPACE, "%s: workspace %zu < %zu bytes", __func__, ws_bytes, need);
+  float* lg = logits ? logits : (float*)ws_data(ws);
   int rc = device_ready();
   if (rc) return rc;
   return launched(beam::launch_router(T, E, dims->D, ng, tg, K, dims->route_scale, x, w_r,
-                                      b_corr, lg, idx, w, S_(stream)),
+                                      b_corr, lg, idx, w, ws_ctl(ws), S_(stream)),
                   __func__);
 }
 
@@ -381,7 +388,7 @@ int beam_moe_swiglu_combine(const beam_dims* dims, int T, const uint16_t* x,
   if (rc) return rc;
   if (moe_many(dims, T)) {
     const MoeWs L = moe_ws_layout(dims, T);
-    char* b = (char*)ws;
+    char* b = ws_data(ws);
     int32_t* counts = (int32_t*)(b + L.counts);
     int32_t* seg_off = (int32_t*)(b + L.seg_off);
     int32_t* tile_off = (int32_t*)(b + L.tile_off);
@@ -413,7 +420,7 @@ int beam_moe_swiglu_combine(const beam_dims* dims, int T, const uint16_t* x,
                     __func__);
   }
   const int spt = dims->topk + (shared_w13 ? 1 : 0);
-  uint16_t* act = (uint16_t*)ws;
+  uint16_t* act = (uint16_t*)ws_data(ws);
   if (beam::launch_expert_w13(T, dims->D, dims->F, dims->E, dims->topk, spt, w13, shared_w13,
                               idx, x, act, S_(stream)))
     return launched(-1, __func__);
@@ -495,7 +502,7 @@ int beam_dense_swiglu(int T, int D, int Fd, const uint16_t* x, const uint16_t* w
                 ws_dense(T, Fd));
   int rc = device_ready();
   if (rc) return rc;
-  uint16_t* act = (uint16_t*)ws;
+  uint16_t* act = (uint16_t*)ws_data(ws);
   if (T > beam::kGemvMaxT && D % 64 == 0) {
     if (beam::launch_gemm_swiglu(T, Fd, D, x, D, nullptr, w13, nullptr, nullptr, 1, 0, 0, act,
                                  S_(stream)))

@@ -94,11 +94,47 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
-// ---- math ------------------------------------------------------------------
-__device__ __forceinline__ float sigmoidf_fast(float x) {
-  return __frcp_rn(1.0f + __expf(-x));
+// ---- last-arriver election ---------------------------------------------------
+// Workgroups that each publish partial results and then need one of them to
+// combine everything. Published values are written with st_dev: a relaxed
+// device-scope store, which goes through to the device's coherence point
+// instead of staying in this XCD's L2, so no L2 write-back is needed. Each wave
+// waits for its own stores to complete, the workgroup meets at a barrier, and
+// one relaxed device-scope atomic per workgroup counts arrivals. Returns true
+// (uniformly) in the workgroup that arrives last; it resets the counter for
+// the next launch and, after an acquire fence, reads what the others
+// published. No workgroup ever waits on another, so nothing can hang.
+// *ctr must be zero when the launch starts.
+__device__ __forceinline__ void st_dev(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ float siluf(float x) { return x / (1.0f + __expf(-x)); }
+
+__device__ __forceinline__ bool last_arrival(unsigned* ctr, unsigned nblocks, int* sflag) {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's stores are complete
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const unsigned old =
+        __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int last = (old == nblocks - 1u);
+    if (last) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *sflag = last;
+  }
+  __syncthreads();
+  const bool last = *sflag != 0;
+  if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  return last;
+}
+
+// ---- math ------------------------------------------------------------------
+// exp and reciprocal on the transcendental unit (about 1 ulp each in fp32),
+// instead of an IEEE division sequence: these run once per activation element
+// in the gate and SwiGLU epilogues, where a division would cost ~10 VALU ops.
+__device__ __forceinline__ float sigmoidf_fast(float x) {
+  return __builtin_amdgcn_rcpf(1.0f + __expf(-x));
+}
+__device__ __forceinline__ float siluf(float x) {
+  return x * __builtin_amdgcn_rcpf(1.0f + __expf(-x));
+}
 
 // ---- device-side argument checks ---------------------------------------------
 // Each translation unit that checks data-dependent indices owns one flag.

@@ -31,18 +31,24 @@ int launch_qk_epilogue(int T, int Hq, int Hkv, int hd, const uint16_t* qkv, cons
                        float k_scale, float v_scale, int S, int Lmax, float eps,
                        hipStream_t st);
 
+// Every workspace starts with a block of kCtlBytes of zeroed uint32 counters
+// (last-arriver elections); kernels that use them leave them at zero.
+constexpr size_t kCtlBytes = 1024;
+constexpr int kAttnCounters = 256;      // (token, kv head) pairs with a fused merge
+constexpr int kAttnFusedMergeMax = 8;   // chunks the last workgroup still merges
+
 void attn_plan(int T, int Hkv, int span, int* tpw, int* nch);
-int attn_direct_span();  // spans up to this are taken in one pass (no partials)
 int attn_nch_bound(int T, int Hkv, int span);
+bool attn_fused_merge(int T, int Hkv, int nch);
 int launch_attn_decode(int T, int Hq, int Hkv, int hd, int swa, int window, int fp8,
                        const uint16_t* q, const int32_t* pos, const int32_t* seq,
                        const void* kc, const void* vc, float k_scale, float v_scale, int S,
                        int Lmax, const float* sink, uint16_t* o, int span, float* part,
-                       hipStream_t st);
+                       unsigned* ctr, hipStream_t st);
 
 int launch_router(int T, int E, int D, int ng, int tg, int K, float route_scale,
                   const uint16_t* X, const float* Wr, const float* bcorr, float* logits,
-                  int32_t* idx, float* w, hipStream_t st);
+                  int32_t* idx, float* w, unsigned* ctr, hipStream_t st);
 
 // many-token (prefill) path
 constexpr int kGemvMaxT = 4;  // T above this runs on the matrix-core kernels

@@ -18,7 +18,9 @@
 // Probabilities enter the P.V product as hi + lo bf16 pairs (two MFMAs), so
 // the only bf16 rounding of the attention path is its output.
 // Each wave's (m, l, O) is merged in LDS; one fp32 record per (t, head, c) goes
-// to the workspace and attn_merge_kernel combines the chunks.
+// to the workspace. The chunks of a (token, kv head) are combined by the last
+// of its workgroups to finish when there are few of them, else by
+// attn_merge_kernel; a span that fits one workgroup is normalised in place.
 #include "common.h"
 #include "internal.h"
 
@@ -30,22 +32,39 @@ BEAM_ERR_FLAG_READER(attn)
 // NW waves per workgroup; GS query-head slots kept for the LDS merge (>= group).
 // Split-K workgroups take contiguous runs of tpw tiles per wave; a one-pass
 // workgroup (o_direct != nullptr) deals the span's tiles round-robin to its
-// waves so no wave walks more than ceil(tiles / NW) of them.
+// waves so no wave walks more than ceil(tiles / NW) of them. With ctr set, the
+// last workgroup of each (token, kv head) to finish merges its chunks and
+// writes o_direct (ctr[t * Hkv + j] counts arrivals and is left at zero).
 template <int HD, bool FP8, bool SWA, int NW, int GS>
 __global__ __launch_bounds__(NW * 64) void attn_decode_partial_kernel(
     const uint16_t* __restrict__ q, const int32_t* __restrict__ pos,
     const int32_t* __restrict__ seq, const void* __restrict__ kc, const void* __restrict__ vc,
     int S, int Lmax, int Hq, int Hkv, int window, int tpw, float score_scale, int nch_stride,
-    float* __restrict__ part, uint16_t* __restrict__ o_direct, const float* __restrict__ sink,
-    float v_scale) {
+    float* part, uint16_t* __restrict__ o_direct, const float* __restrict__ sink,
+    float v_scale, unsigned* ctr) {
   constexpr int KS = HD / 32;  // k-steps of the score product
   constexpr int DT = HD / 16;  // 16-dim tiles of the output
   constexpr int GD = HD / 4;   // dims each lane group covers in the score product
   __shared__ float sm_m[NW][16], sm_l[NW][16];
   __shared__ float sm_o[NW][GS][HD + 4];
+  __shared__ int s_last;
 
   const int c = blockIdx.x, j = blockIdx.y, t = blockIdx.z;
   const int grp = Hq / Hkv;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int g = lane >> 4, col = lane & 15;
+
+  // the query fragments do not depend on the position: request them first
+  bf16x8 qf[KS];
+  if (col < grp) {
+    const uint16_t* qp = q + ((size_t)t * Hq + j * grp + col) * HD + g * GD;
+#pragma unroll
+    for (int i = 0; i < KS; ++i) qf[i] = as_bf16x8(ld16(qp + i * 8));
+  } else {
+#pragma unroll
+    for (int i = 0; i < KS; ++i) qf[i] = bf16x8{};
+  }
+
   const int p = pos[t], s = seq[t];
   if (p < 0 || p >= Lmax || s < 0 || s >= S) {
     if (c == 0 && j == 0 && threadIdx.x == 0) BEAM_RAISE(attn, p < 0 || p >= Lmax ? ERR_POS : ERR_SEQ);
@@ -60,19 +79,6 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_partial_kernel(
   const int nch = (p + 1 - lo_al + CK - 1) / CK;
   if (c >= nch) return;
 
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int g = lane >> 4, col = lane & 15;
-
-  bf16x8 qf[KS];
-  if (col < grp) {
-    const uint16_t* qp = q + ((size_t)t * Hq + j * grp + col) * HD + g * GD;
-#pragma unroll
-    for (int i = 0; i < KS; ++i) qf[i] = as_bf16x8(ld16(qp + i * 8));
-  } else {
-#pragma unroll
-    for (int i = 0; i < KS; ++i) qf[i] = bf16x8{};
-  }
-
   const size_t krow0 = ((size_t)s * Hkv + j) * (size_t)Lmax;  // K row of position 0
   const size_t vrow0 = ((size_t)s * Hkv + j) * (size_t)HD;    // V^T row of dim 0
   float m = -INFINITY, lsum = 0.f;
@@ -80,7 +86,7 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_partial_kernel(
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const bool rr = (o_direct != nullptr);
+  const bool rr = (o_direct != nullptr) && (ctr == nullptr);
   const int tile0 = (lo_al >> 6) + (rr ? wave : (c * NW + wave) * tpw);
   for (int it = 0; it < tpw; ++it) {
     const int kb = (tile0 + (rr ? it * NW : it)) << 6;
@@ -211,7 +217,7 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_partial_kernel(
       L += e * sm_l[w][hh];
       O += e * sm_o[w][hh][dim];
     }
-    if (o_direct) {  // the whole span was this workgroup's: normalise and store
+    if (rr) {  // the whole span was this workgroup's: normalise and store
       if (sink) {
         const float sl2 = sink[j * grp + hh] * 1.4426950408889634f;
         const float Mn = fmaxf(M, sl2);
@@ -224,25 +230,75 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_partial_kernel(
     }
     float* rec = part + (((size_t)t * Hq + j * grp + hh) * nch_stride + c) * (HD + 4);
     if (dim == 0) {
-      rec[0] = M;
-      rec[1] = L;
+      st_dev(rec, M);
+      st_dev(rec + 1, L);
     }
-    rec[4 + dim] = O;
+    st_dev(rec + 4 + dim, O);
+  }
+  if (ctr == nullptr || !last_arrival(ctr + (size_t)t * Hkv + j, nch, &s_last)) return;
+  // Last of the token's nch (<= kAttnFusedMergeMax) workgroups for this kv
+  // head: wave w combines heads w, w + NW, ... in chunk order, with every
+  // chunk's record requested before any is used.
+  constexpr int MX = kAttnFusedMergeMax;
+  constexpr int DPL = (HD + 63) / 64;  // dims per lane
+  for (int hh = wave; hh < grp; hh += NW) {
+    const float* rec0 = part + ((size_t)t * Hq + j * grp + hh) * nch_stride * (HD + 4);
+    float mc[MX], lc[MX], oc[MX][DPL];
+#pragma unroll
+    for (int cc = 0; cc < MX; ++cc) {
+      const float* rec = rec0 + (size_t)min(cc, nch - 1) * (HD + 4);
+      mc[cc] = rec[0];
+      lc[cc] = rec[1];
+#pragma unroll
+      for (int k = 0; k < DPL; ++k) {
+        const int d = lane + 64 * k;
+        oc[cc][k] = d < HD ? rec[4 + d] : 0.f;
+      }
+    }
+    float M = -INFINITY;
+#pragma unroll
+    for (int cc = 0; cc < MX; ++cc)
+      if (cc < nch) M = fmaxf(M, mc[cc]);
+    const float sl2 = sink ? sink[j * grp + hh] * 1.4426950408889634f : -INFINITY;
+    M = fmaxf(M, sl2);
+    float L = sink ? exp2f(sl2 - M) : 0.f;
+    float O[DPL] = {};
+#pragma unroll
+    for (int cc = 0; cc < MX; ++cc) {
+      if (cc < nch) {
+        const float e = exp2f(mc[cc] - M);
+        L += e * lc[cc];
+#pragma unroll
+        for (int k = 0; k < DPL; ++k) O[k] += e * oc[cc][k];
+      }
+    }
+    const float inv = v_scale / L;
+#pragma unroll
+    for (int k = 0; k < DPL; ++k) {
+      const int d = lane + 64 * k;
+      if (d < HD) o_direct[((size_t)t * Hq + j * grp + hh) * HD + d] = f2bf(O[k] * inv);
+    }
   }
 }
 
 // Combine the chunks of one (token, head): o = sum_c 2^(m_c-M) O_c / sum_c 2^(m_c-M) l_c.
-// An attention sink adds 2^(sink*log2e - M) to the denominator only.
+// An attention sink adds 2^(sink*log2e - M) to the denominator only. Wave w
+// takes chunks w, w + 4, ... in batches of 8 whose records are all requested
+// before use, keeping a running (M, L, O); the 4 waves combine through LDS.
 template <int HD>
-__global__ __launch_bounds__(64) void attn_merge_kernel(
+__global__ __launch_bounds__(256) void attn_merge_kernel(
     const float* __restrict__ part, const int32_t* __restrict__ pos,
     const int32_t* __restrict__ seq, int S, int Lmax, int Hq, int window, int swa, int tpw,
     int nch_stride, const float* __restrict__ sink, float v_scale, uint16_t* __restrict__ o) {
-  const int h = blockIdx.x, t = blockIdx.y, lane = threadIdx.x;
+  constexpr int DPL = (HD + 63) / 64;
+  constexpr int B = 8;
+  __shared__ float sm_m[4], sm_l[4], sm_o[4][HD];
+  const int h = blockIdx.x, t = blockIdx.y;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   uint16_t* out = o + ((size_t)t * Hq + h) * HD;
   const int p = pos[t], s = seq[t];
   if (p < 0 || p >= Lmax || s < 0 || s >= S) {
-    for (int d = lane; d < HD; d += 64) out[d] = 0;
+    for (int d = threadIdx.x; d < HD; d += 256) out[d] = 0;
     return;
   }
   const int lo = swa ? max(0, p - window + 1) : 0;
@@ -250,42 +306,74 @@ __global__ __launch_bounds__(64) void attn_merge_kernel(
   const int CK = 256 * tpw;
   const int nch = (p + 1 - lo_al + CK - 1) / CK;
   const float* rec0 = part + ((size_t)t * Hq + h) * nch_stride * (HD + 4);
-  float M = -INFINITY;
-  for (int c = 0; c < nch; ++c) M = fmaxf(M, rec0[(size_t)c * (HD + 4)]);
-  const float sl2 = sink ? sink[h] * 1.4426950408889634f : -INFINITY;
-  M = fmaxf(M, sl2);
-  float L = sink ? exp2f(sl2 - M) : 0.f;
-  float acc[HD / 64 > 0 ? HD / 64 : 1] = {};
-  for (int c = 0; c < nch; ++c) {
-    const float* rec = rec0 + (size_t)c * (HD + 4);
-    const float e = exp2f(rec[0] - M);
-    L += e * rec[1];
+  float M = -INFINITY, L = 0.f, O[DPL] = {};
+  for (int c0 = wave; c0 < nch; c0 += 4 * B) {
+    float mc[B], lc[B], oc[B][DPL];
 #pragma unroll
-    for (int k = 0; k < (HD + 63) / 64; ++k) {
+    for (int b = 0; b < B; ++b) {
+      const float* rec = rec0 + (size_t)min(c0 + 4 * b, nch - 1) * (HD + 4);
+      mc[b] = rec[0];
+      lc[b] = rec[1];
+#pragma unroll
+      for (int k = 0; k < DPL; ++k) {
+        const int d = lane + 64 * k;
+        oc[b][k] = d < HD ? rec[4 + d] : 0.f;
+      }
+    }
+    float Mn = M;
+#pragma unroll
+    for (int b = 0; b < B; ++b)
+      if (c0 + 4 * b < nch) Mn = fmaxf(Mn, mc[b]);
+    const float a = exp2f(M - Mn);  // M = -inf on the first batch: a = 0
+    L *= a;
+#pragma unroll
+    for (int k = 0; k < DPL; ++k) O[k] *= a;
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+      if (c0 + 4 * b < nch) {
+        const float e = exp2f(mc[b] - Mn);
+        L += e * lc[b];
+#pragma unroll
+        for (int k = 0; k < DPL; ++k) O[k] += e * oc[b][k];
+      }
+    }
+    M = Mn;
+  }
+  if (lane == 0) {
+    sm_m[wave] = M;
+    sm_l[wave] = L;
+  }
+#pragma unroll
+  for (int k = 0; k < DPL; ++k) {
+    const int d = lane + 64 * k;
+    if (d < HD) sm_o[wave][d] = O[k];
+  }
+  __syncthreads();
+  if (wave != 0) return;
+  float Mt = fmaxf(fmaxf(sm_m[0], sm_m[1]), fmaxf(sm_m[2], sm_m[3]));
+  const float sl2 = sink ? sink[h] * 1.4426950408889634f : -INFINITY;
+  Mt = fmaxf(Mt, sl2);
+  float Lt = sink ? exp2f(sl2 - Mt) : 0.f, Ot[DPL] = {};
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const float e = (sm_m[w] == -INFINITY) ? 0.f : exp2f(sm_m[w] - Mt);
+    Lt += e * sm_l[w];
+#pragma unroll
+    for (int k = 0; k < DPL; ++k) {
       const int d = lane + 64 * k;
-      if (d < HD) acc[k] += e * rec[4 + d];
+      if (d < HD) Ot[k] += e * sm_o[w][d];
     }
   }
-  const float inv = v_scale / L;
+  const float inv = v_scale / Lt;
 #pragma unroll
-  for (int k = 0; k < (HD + 63) / 64; ++k) {
+  for (int k = 0; k < DPL; ++k) {
     const int d = lane + 64 * k;
-    if (d < HD) out[d] = f2bf(acc[k] * inv);
+    if (d < HD) out[d] = f2bf(Ot[k] * inv);
   }
 }
 
-// Keys per workgroup at or below which a token's span is taken in one pass
-// (outputs written directly, no merge).
-constexpr int kDirectSpan = 1024;
-int attn_direct_span() { return kDirectSpan + 63; }
-
 void attn_plan(int T, int Hkv, int span, int* tpw, int* nch) {
   const int tiles = (span + 63) / 64;
-  if (span <= kDirectSpan + 63) {  // one pass: 8 waves, tiles dealt round-robin
-    *tpw = std::max(1, (tiles + 7) / 8);
-    *nch = 1;
-    return;
-  }
   const int target = std::max(1, 2048 / std::max(1, Hkv * T));
   int w = (tiles + 4 * target - 1) / (4 * target);
   w = std::min(std::max(w, 1), 64);
@@ -293,34 +381,35 @@ void attn_plan(int T, int Hkv, int span, int* tpw, int* nch) {
   *nch = std::max(1, (tiles + 4 * w - 1) / (4 * w));
 }
 
+// An upper bound of attn_plan's nch over every span up to `span`, monotone in
+// span, so a workspace sized for a context bound serves any shorter one.
 int attn_nch_bound(int T, int Hkv, int span) {
   const int tiles = (span + 63) / 64;
   const int target = std::max(1, 2048 / std::max(1, Hkv * T));
   return std::max(std::max(1, std::min(target, (tiles + 3) / 4)), (tiles + 255) / 256);
 }
 
+bool attn_fused_merge(int T, int Hkv, int nch) {
+  return nch > 1 && nch <= kAttnFusedMergeMax && T * Hkv <= kAttnCounters;
+}
+
 int launch_attn_decode(int T, int Hq, int Hkv, int hd, int swa, int window, int fp8,
                        const uint16_t* q, const int32_t* pos, const int32_t* seq,
                        const void* kc, const void* vc, float k_scale, float v_scale, int S,
                        int Lmax, const float* sink, uint16_t* o, int span, float* part,
-                       hipStream_t st) {
+                       unsigned* ctr, hipStream_t st) {
   int tpw, nch;
   attn_plan(T, Hkv, span, &tpw, &nch);
   const float score_scale = k_scale / sqrtf((float)hd) * 1.4426950408889634f;
   const dim3 grid(nch, Hkv, T);
-  const bool direct = (nch == 1);
-  uint16_t* od = direct ? o : nullptr;
+  const bool fused = attn_fused_merge(T, Hkv, nch);
+  uint16_t* od = (nch == 1 || fused) ? o : nullptr;
+  unsigned* cp = fused ? ctr : nullptr;
   const float vsc = fp8 ? v_scale : 1.0f;
-#define PART(HD_, F8, SW)                                                                    \
-  if (direct && Hq / Hkv <= 8)                                                               \
-    hipLaunchKernelGGL((attn_decode_partial_kernel<HD_, F8, SW, 8, 8>), grid, dim3(512), 0,  \
-                       st, q, pos, seq, kc, vc, S, Lmax, Hq, Hkv, window, tpw, score_scale,  \
-                       nch, part, od, sink, vsc);                                            \
-  else                                                                                       \
-    hipLaunchKernelGGL((attn_decode_partial_kernel<HD_, F8, SW, 4, 16>), grid, dim3(256), 0, \
-                       st, q, pos, seq, kc, vc, S, Lmax, Hq, Hkv, window,                    \
-                       direct ? std::max(1, (tpw * 8 + 3) / 4) : tpw, score_scale, nch,      \
-                       part, od, sink, vsc)
+#define PART(HD_, F8, SW)                                                                   \
+  hipLaunchKernelGGL((attn_decode_partial_kernel<HD_, F8, SW, 4, 16>), grid, dim3(256), 0, \
+                     st, q, pos, seq, kc, vc, S, Lmax, Hq, Hkv, window, tpw, score_scale,   \
+                     nch, part, od, sink, vsc, cp)
 #define BY_MODE(HD_)                                    \
   if (fp8) {                                           \
     if (swa) PART(HD_, true, true); else PART(HD_, true, false);   \
@@ -333,17 +422,17 @@ int launch_attn_decode(int T, int Hq, int Hkv, int hd, int swa, int window, int 
 #undef BY_MODE
 #undef PART
   if (hipGetLastError() != hipSuccess) return -1;
-  if (direct) return 0;
+  if (od) return 0;
   const dim3 mg(Hq, T);
   const float vs = fp8 ? v_scale : 1.0f;
   if (hd == 128)
-    hipLaunchKernelGGL((attn_merge_kernel<128>), mg, dim3(64), 0, st, part, pos, seq, S, Lmax, Hq,
+    hipLaunchKernelGGL((attn_merge_kernel<128>), mg, dim3(256), 0, st, part, pos, seq, S, Lmax, Hq,
                        window, swa, tpw, nch, sink, vs, o);
   else if (hd == 64)
-    hipLaunchKernelGGL((attn_merge_kernel<64>), mg, dim3(64), 0, st, part, pos, seq, S, Lmax, Hq,
+    hipLaunchKernelGGL((attn_merge_kernel<64>), mg, dim3(256), 0, st, part, pos, seq, S, Lmax, Hq,
                        window, swa, tpw, nch, sink, vs, o);
   else
-    hipLaunchKernelGGL((attn_merge_kernel<32>), mg, dim3(64), 0, st, part, pos, seq, S, Lmax, Hq,
+    hipLaunchKernelGGL((attn_merge_kernel<32>), mg, dim3(256), 0, st, part, pos, seq, S, Lmax, Hq,
                        window, swa, tpw, nch, sink, vs, o);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }

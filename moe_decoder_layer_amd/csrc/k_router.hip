@@ -4,56 +4,22 @@
 // times 2.5; weights, accumulation and logits all FP32; optimisation change 4
 // gives the router its own small-batch FP32 GEMM).
 //
-//  router_logits_gemv   few tokens: one workgroup per expert row, the fp32 row
-//                       streamed once, K split over 4 waves, fixed-order sum
+//  router_decode        few tokens: one wave per expert row, the fp32 row
+//                       streamed once; the workgroup that finishes last runs
+//                       the selection for every token (no second launch)
 //  router_logits_gemm   many tokens: 64x64 fp32 tiles staged through LDS
-//  router_topk          one workgroup per token, one thread per expert: group
-//                       scores (sum of the two best biased scores), top groups
-//                       by rank, top experts by block-wide arg-max rounds
-//                       (ties to the lower index)
+//  router_topk          many tokens: one workgroup per token
+// Selection (route_token), one thread per expert: group scores (sum of the two
+// best biased scores), the top groups by rank, then the top experts by rank
+// among the kept groups' best experts. A rank counts the candidates that beat
+// a candidate (larger value, or equal value and lower index), so ties go to
+// the lower index and the experts come out in descending biased-score order.
 #include "common.h"
 #include "internal.h"
 
 namespace beam {
 
 constexpr int RT = 256;
-
-template <int TT>
-__global__ __launch_bounds__(RT) void router_logits_gemv_kernel(
-    const uint16_t* __restrict__ X, const float* __restrict__ Wr, int T, int E, int D,
-    float* __restrict__ logits) {
-  __shared__ float red[4][TT];
-  const int e = blockIdx.x, t0 = blockIdx.y * TT;
-  const float* w = Wr + (size_t)e * D;
-  float acc[TT] = {};
-  const int nc = D >> 2;  // float4 chunks
-  for (int c = threadIdx.x; c < nc; c += RT) {
-    const f32x4 wv = ld16f_nt(w + (size_t)c * 4);
-#pragma unroll
-    for (int t = 0; t < TT; ++t) {
-      if (t0 + t < T) {
-        const uint2 xv = *reinterpret_cast<const uint2*>(X + (size_t)(t0 + t) * D + c * 4);
-        float a = acc[t];
-        a = __builtin_fmaf(bf_lo(xv.x), wv[0], a);
-        a = __builtin_fmaf(bf_hi(xv.x), wv[1], a);
-        a = __builtin_fmaf(bf_lo(xv.y), wv[2], a);
-        a = __builtin_fmaf(bf_hi(xv.y), wv[3], a);
-        acc[t] = a;
-      }
-    }
-  }
-  const int wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int t = 0; t < TT; ++t) {
-    const float v = wave_sum(acc[t]);
-    if ((threadIdx.x & 63) == 0) red[wave][t] = v;
-  }
-  __syncthreads();
-  if (threadIdx.x < TT && t0 + (int)threadIdx.x < T) {
-    const int t = threadIdx.x;
-    logits[(size_t)(t0 + t) * E + e] = ((red[0][t] + red[1][t]) + red[2][t]) + red[3][t];
-  }
-}
 
 // 64 tokens x 64 experts per workgroup, k-steps of 16; each thread 4x4 outputs.
 __global__ __launch_bounds__(RT) void router_logits_gemm_kernel(
@@ -99,102 +65,168 @@ __global__ __launch_bounds__(RT) void router_logits_gemm_kernel(
 
 constexpr int EMAX = 1024;
 
-// One workgroup per token, one thread per expert. Groups are chosen by rank
-// (the number of groups that beat a group: larger score, or equal score and
-// lower index); experts by topk rounds of a block-wide arg-max. Both break
-// ties towards the lower index, and experts come out in selection order.
-__global__ __launch_bounds__(EMAX) void router_topk_kernel(
-    const float* __restrict__ logits, const float* __restrict__ bcorr, int T, int E, int ng,
-    int tg, int K, float route_scale, int32_t* __restrict__ idx, float* __restrict__ wout) {
-  __shared__ float s_b[EMAX];
-  __shared__ float g1[64], g2[64], gsc[64], ssel[32];
-  __shared__ float wv_best[EMAX / 64];
-  __shared__ int wi_best[EMAX / 64];
-  const int t = blockIdx.x, e = threadIdx.x;
+// Grouped top-k of one token, one thread per expert (E <= blockDim.x).
+// lg: the token's logits; bias: this thread's correction bias (0 when none).
+// LDS scratch: s_b, cand_v, cand_i >= E entries, g1, g2 >= ng, ssel >= K.
+// An expert among the overall top K is among the top K of its own group, so
+// the final ranking only runs over each kept group's best min(K, group size).
+__device__ void route_token(const float* lg, float bias, int E, int ng, int tg, int K,
+                            float route_scale, int32_t* idx_t, float* w_t, float* s_b,
+                            float* cand_v, int* cand_i, float* g1, float* g2, float* ssel) {
+  const int e = threadIdx.x;
   const bool act = e < E;
   const int gs = E / ng;
+  const int kc = min(K, gs);  // candidates per kept group
+  const int nc = tg * kc;     // <= E
   const int grp = act ? e / gs : 0;
   float sv = 0.f, sb = -INFINITY;
   if (act) {
-    const float lg = logits[(size_t)t * E + e];
-    sv = 1.0f / (1.0f + expf(-lg));
-    sb = sv + (bcorr ? bcorr[e] : 0.f);
+    sv = 1.0f / (1.0f + expf(-lg[e]));
+    sb = sv + bias;
     s_b[e] = sb;
   }
+  if (e < nc) cand_v[e] = -INFINITY;  // slots a group cannot fill stay empty
   __syncthreads();
-  // rank inside the group -> the group's two best biased scores
+  // rank inside the group; the two best give the group's score
+  int rin = 0;
   if (act) {
-    int r = 0;
     const int g0 = grp * gs;
+#pragma unroll 8
     for (int m = g0; m < g0 + gs; ++m) {
       const float v = s_b[m];
-      r += (v > sb) || (v == sb && m < e);
+      rin += (v > sb) || (v == sb && m < e);
     }
-    if (r == 0) g1[grp] = sb;
-    if (r == 1) g2[grp] = sb;
+    if (rin == 0) g1[grp] = sb;
+    if (rin == 1) g2[grp] = sb;
   }
   __syncthreads();
-  if (e < ng) gsc[e] = (gs >= 2) ? g1[e] + g2[e] : g1[e];
+  bool cand = false;  // in a kept group and among its best kc
+  if (act && rin < kc) {
+    const float my = (gs >= 2) ? g1[grp] + g2[grp] : g1[grp];
+    int rg = 0;
+    for (int h = 0; h < ng; ++h) {
+      const float sc = (gs >= 2) ? g1[h] + g2[h] : g1[h];
+      rg += (sc > my) || (sc == my && h < grp);
+    }
+    cand = rg < tg;
+    if (cand) {
+      cand_v[rg * kc + rin] = sb;
+      cand_i[rg * kc + rin] = e;
+    }
+  }
   __syncthreads();
-  // group rank -> kept groups; candidates are the kept groups' experts
-  bool kept = false;
-  if (act) {
-    const float my = gsc[grp];
-    int r = 0;
-    for (int h = 0; h < ng; ++h) r += (gsc[h] > my) || (gsc[h] == my && h < grp);
-    kept = r < tg;
+  // final rank among the candidates (same order: value, then lower index);
+  // empty slots hold -inf and never beat a candidate
+  int r = 0;
+  if (cand) {
+#pragma unroll 8
+    for (int c = 0; c < nc; ++c) {
+      const float v = cand_v[c];
+      r += (v > sb) || (v == sb && cand_i[c] < e);
+    }
   }
-  // topk rounds of a block-wide arg-max over the kept experts' biased scores
-  float v = kept ? sb : -INFINITY;
-  const int lane = e & 63, wave = e >> 6, nw = blockDim.x >> 6;
-  for (int k = 0; k < K; ++k) {
-    float bv = v;
-    int bi = act ? e : 0x7fffffff;
-#pragma unroll
-    for (int o2 = 32; o2 > 0; o2 >>= 1) {
-      const float v2 = __shfl_xor(bv, o2, 64);
-      const int i2 = __shfl_xor(bi, o2, 64);
-      if (v2 > bv || (v2 == bv && i2 < bi)) {
-        bv = v2;
-        bi = i2;
-      }
-    }
-    if (lane == 0) {
-      wv_best[wave] = bv;
-      wi_best[wave] = bi;
-    }
-    __syncthreads();
-    float gv = wv_best[0];
-    int gi = wi_best[0];
-    for (int w2 = 1; w2 < nw; ++w2)
-      if (wv_best[w2] > gv || (wv_best[w2] == gv && wi_best[w2] < gi)) {
-        gv = wv_best[w2];
-        gi = wi_best[w2];
-      }
-    if (e == gi) {
-      v = -INFINITY;
-      idx[(size_t)t * K + k] = e;
-      ssel[k] = sv;
-    }
-    __syncthreads();
+  if (cand && r < K) {
+    idx_t[r] = e;
+    ssel[r] = sv;
   }
+  __syncthreads();
   if (e < K) {
     float sum = 0.f;
     for (int k = 0; k < K; ++k) sum += ssel[k];
-    wout[(size_t)t * K + e] = route_scale * ssel[e] / sum;
+    w_t[e] = route_scale * ssel[e] / sum;
   }
+  __syncthreads();  // the LDS arrays are reused for the next token
+}
+
+__global__ __launch_bounds__(EMAX) void router_topk_kernel(
+    const float* __restrict__ logits, const float* __restrict__ bcorr, int T, int E, int ng,
+    int tg, int K, float route_scale, int32_t* __restrict__ idx, float* __restrict__ wout) {
+  __shared__ float s_b[EMAX], cand_v[EMAX];
+  __shared__ int cand_i[EMAX];
+  __shared__ float g1[64], g2[64], ssel[32];
+  const int t = blockIdx.x;
+  const float bias = (bcorr && (int)threadIdx.x < E) ? bcorr[threadIdx.x] : 0.f;
+  route_token(logits + (size_t)t * E, bias, E, ng, tg, K, route_scale, idx + (size_t)t * K,
+              wout + (size_t)t * K, s_b, cand_v, cand_i, g1, g2, ssel);
+}
+
+// Few tokens: wave w of workgroup b computes the logits of expert 4b + w for
+// up to TT tokens, each lane requesting its MAXC float4 chunks of the row per
+// pass before using any (addresses past the row are clamped and their values
+// zeroed, so the loads carry no branches). The workgroup that finishes last
+// runs the selection for every token (E <= RT).
+template <int TT, int MAXC>
+__global__ __launch_bounds__(RT) void router_decode_kernel(
+    const uint16_t* __restrict__ X, const float* __restrict__ Wr, int T, int E, int D,
+    float* logits, const float* __restrict__ bcorr, int ng, int tg, int K, float route_scale,
+    int32_t* __restrict__ idx, float* __restrict__ wout, unsigned* ctr) {
+  __shared__ float s_b[RT], cand_v[RT];
+  __shared__ int cand_i[RT];
+  __shared__ float g1[64], g2[64], ssel[32];
+  __shared__ int s_last;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  // the selection needs the bias in whichever workgroup ends up last
+  const float bias = (bcorr && (int)threadIdx.x < E) ? bcorr[threadIdx.x] : 0.f;
+  const int e = blockIdx.x * 4 + wave;
+  const float* w = Wr + (size_t)min(e, E - 1) * D;
+  const int nc = D >> 2;  // float4 chunks of a row
+  float acc[TT] = {};
+  for (int c0 = 0; c0 < nc; c0 += MAXC * 64) {
+    f32x4 wv[MAXC];
+#pragma unroll
+    for (int i = 0; i < MAXC; ++i) {
+      const int c = c0 + lane + 64 * i;
+      wv[i] = ld16f_nt(w + (size_t)min(c, nc - 1) * 4);
+    }
+#pragma unroll
+    for (int t = 0; t < TT; ++t) {
+      if (t < T) {
+        uint2 xv[MAXC];
+#pragma unroll
+        for (int i = 0; i < MAXC; ++i) {
+          const int c = c0 + lane + 64 * i;
+          xv[i] = *reinterpret_cast<const uint2*>(X + (size_t)t * D + min(c, nc - 1) * 4);
+        }
+        float a = acc[t];
+#pragma unroll
+        for (int i = 0; i < MAXC; ++i) {
+          if (c0 + lane + 64 * i < nc) {
+            a = __builtin_fmaf(bf_lo(xv[i].x), wv[i][0], a);
+            a = __builtin_fmaf(bf_hi(xv[i].x), wv[i][1], a);
+            a = __builtin_fmaf(bf_lo(xv[i].y), wv[i][2], a);
+            a = __builtin_fmaf(bf_hi(xv[i].y), wv[i][3], a);
+          }
+        }
+        acc[t] = a;
+      }
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < TT; ++t) {
+    const float v = wave_sum(acc[t]);
+    if (lane == 0 && t < T && e < E) st_dev(logits + (size_t)t * E + e, v);
+  }
+  if (!last_arrival(ctr, gridDim.x, &s_last)) return;
+  for (int t = 0; t < T; ++t)
+    route_token(logits + (size_t)t * E, bias, E, ng, tg, K, route_scale, idx + (size_t)t * K,
+                wout + (size_t)t * K, s_b, cand_v, cand_i, g1, g2, ssel);
 }
 
 int launch_router(int T, int E, int D, int ng, int tg, int K, float route_scale,
                   const uint16_t* X, const float* Wr, const float* bcorr, float* logits,
-                  int32_t* idx, float* w, hipStream_t st) {
-  if (T <= 4) {
-    hipLaunchKernelGGL((router_logits_gemv_kernel<4>), dim3(E, 1), dim3(RT), 0, st, X, Wr, T, E,
-                       D, logits);
-  } else {
-    hipLaunchKernelGGL(router_logits_gemm_kernel, dim3((T + 63) / 64, (E + 63) / 64), dim3(RT),
-                       0, st, X, Wr, T, E, D, logits);
+                  int32_t* idx, float* w, unsigned* ctr, hipStream_t st) {
+  if (T <= 4 && E <= RT) {
+    const dim3 grid((E + 3) / 4);
+    if (D <= 8 * 64 * 4)
+      hipLaunchKernelGGL((router_decode_kernel<4, 8>), grid, dim3(RT), 0, st, X, Wr, T, E, D,
+                         logits, bcorr, ng, tg, K, route_scale, idx, w, ctr);
+    else
+      hipLaunchKernelGGL((router_decode_kernel<4, 20>), grid, dim3(RT), 0, st, X, Wr, T, E, D,
+                         logits, bcorr, ng, tg, K, route_scale, idx, w, ctr);
+    return hipGetLastError() == hipSuccess ? 0 : -1;
   }
+  hipLaunchKernelGGL(router_logits_gemm_kernel, dim3((T + 63) / 64, (E + 63) / 64), dim3(RT), 0,
+                     st, X, Wr, T, E, D, logits);
   if (hipGetLastError() != hipSuccess) return -1;
   const int threads = ((E + 63) / 64) * 64;
   hipLaunchKernelGGL(router_topk_kernel, dim3(T), dim3(threads), 0, st, logits, bcorr, T, E, ng,

@@ -207,9 +207,17 @@ class Params:
 
 
 # ----------------------------------------------------------------- GPU layer
+CTL_BYTES = 1024  # counter block at the head of every workspace
+
+
+def ws_payload(w, nbytes):
+    """The first nbytes of a workspace's data area (after the counter block)."""
+    return w[CTL_BYTES:CTL_BYTES + nbytes]
+
+
 def ws(dims, op, T, ctx=0):
     n = B.beam_workspace_size(dims, op, T, ctx)
-    return torch.empty(max(n, 256), dtype=torch.uint8, device="cuda")
+    return torch.zeros(max(n, 256), dtype=torch.uint8, device="cuda")  # counter block zeroed
 
 
 def run_layer(dims, P: Params, cache: Cache, h_bits, pos, seq, mode: str, n: int,
@@ -236,7 +244,7 @@ def run_layer(dims, P: Params, cache: Cache, h_bits, pos, seq, mode: str, n: int
                                       pos_t, seq_t, m, rope if mode == "swa" else None, q,
                                       g if dims.G else None, kvs, wsq)
     nqkv = (dims.Hq + 2 * dims.Hkv) * dims.d
-    out["qkv"] = host_bits(wsq[:T * nqkv * 2].view(torch.int16).view(T, nqkv))
+    out["qkv"] = host_bits(ws_payload(wsq, T * nqkv * 2).view(torch.int16).view(T, nqkv))
     o = torch.empty((T, dims.Hq, dims.d), **I16)
     max_pos = int(np.max(pos))
     attn = B.beam_attn_swa if mode == "swa" else B.beam_attn_nope_ssmax
@@ -254,7 +262,8 @@ def run_layer(dims, P: Params, cache: Cache, h_bits, pos, seq, mode: str, n: int
         idx = torch.empty((T, dims.topk), dtype=torch.int32, device="cuda")
         w = torch.empty((T, dims.topk), dtype=torch.float32, device="cuda")
         logits = torch.empty((T, dims.E), dtype=torch.float32, device="cuda")
-        B.beam_router_fp32_grouped_topk(dims, T, x2, t["w_r"], t["b_corr"], idx, w, logits)
+        B.beam_router_fp32_grouped_topk(dims, T, x2, t["w_r"], t["b_corr"], idx, w, logits,
+                                        ws(dims, B.BEAM_OP_ROUTER, T))
         B.beam_moe_swiglu_combine(dims, T, x2, idx, w, t["w13"], t["w2"], t.get("shared_w13"),
                                   t.get("shared_w2"), y2, ws(dims, B.BEAM_OP_MOE, T))
         out.update(idx=idx.cpu().numpy(), w=w.cpu().numpy(), logits=logits.cpu().numpy())

@@ -93,8 +93,10 @@ def test_attention_router_moe_validation():
                None) == -1
     assert _rc("beam_attn_nope_ssmax", by, 1, A, A, A, ctypes.byref(kv), None, A, 7999, A, ws,
                None) == -7
-    # a short one is taken in one pass and needs none
+    # a short one is taken in one pass and needs only the counter block
     assert _rc("beam_attn_nope_ssmax", by, 1, A, A, A, ctypes.byref(kv), None, A, 64, None, 0,
+               None) == -1
+    assert _rc("beam_attn_nope_ssmax", by, 1, A, A, A, ctypes.byref(kv), None, A, 64, A, 1024,
                None) == -7
     dw = _dims(window=0)
     assert _rc("beam_attn_swa", ctypes.byref(dw), 1, A, A, A, ctypes.byref(kv), None, A, 64, A,
@@ -108,7 +110,12 @@ def test_attention_router_moe_validation():
                0, None) == -2
     assert _rc("beam_router_fp32_grouped_topk", by, 1, A, A, None, A, A, None, A, 16,
                None) == -5
-    assert _rc("beam_router_fp32_grouped_topk", by, 1, A, A, None, A, A, A, None, 0, None) == -7
+    # the counter block is needed even when the logits are an output
+    assert _rc("beam_router_fp32_grouped_topk", by, 1, A, A, None, A, A, A, None, 0, None) == -1
+    assert _rc("beam_router_fp32_grouped_topk", by, 1, A, A, None, A, A, A, A, 1023,
+               None) == -5
+    assert _rc("beam_router_fp32_grouped_topk", by, 1, A, A, None, A, A, A, A, 1024,
+               None) == -7
     wsm = B.beam_workspace_size(d, B.BEAM_OP_MOE, 1)
     assert _rc("beam_moe_swiglu_combine", by, 1, A, A, A, A, A, A, None, A, A, wsm, None) == -1
     assert _rc("beam_moe_swiglu_combine", by, 1, A, A, A, A, A, None, None, A, A, wsm - 256,
@@ -123,10 +130,15 @@ def test_attention_router_moe_validation():
 
 def test_workspace_sizes():
     d = _dims(1)
-    assert B.beam_workspace_size(d, B.BEAM_OP_QKV, 1) >= (48 + 16) * 128 * 2
+    ctl = 1024  # every workspace starts with the zeroed counter block
+    assert B.beam_workspace_size(d, B.BEAM_OP_QKV, 1) >= ctl + (48 + 16) * 128 * 2
+    for op in (B.BEAM_OP_OUT_GATE, B.BEAM_OP_ROUTER, B.BEAM_OP_MOE, B.BEAM_OP_DENSE):
+        assert B.beam_workspace_size(d, op, 1) >= ctl
     a = B.beam_workspace_size(d, B.BEAM_OP_ATTN_NOPE, 1, 100001)
     s = B.beam_workspace_size(d, B.BEAM_OP_ATTN_SWA, 1, 100001)
-    assert a > 0 and s == 0     # a 512-key window is taken in one pass: no partials
+    # a 512-key window is split over 3 workgroups per kv head (48 heads x 3 partial
+    # records of d + 4 floats); the full context over many more
+    assert s == ctl + 48 * 3 * (128 + 4) * 4 and a > s
     # monotone in the context bound
     sizes = [B.beam_workspace_size(d, B.BEAM_OP_ATTN_NOPE, 1, c) for c in range(1000, 200000, 997)]
     assert all(x <= y for x, y in zip(sizes, sizes[1:]))

@@ -7,7 +7,7 @@ import torch
 import moe_decoder_layer_amd as B
 import synth
 from beamrun import (Cache, Params, assert_rms_close, bits_f64, check_routing, code_pos, dev,
-                     host_bits, rope_table, ws)
+                     host_bits, rope_table, ws, ws_payload)
 from oracle import layer as L
 from oracle.numerics import e4m3_quantize, round_bf16
 
@@ -76,7 +76,7 @@ def test_qk_norm_kvwrite(base, T, pos0, mode, kv):
     nqkv = (dims.Hq + 2 * dims.Hkv) * dims.d
     # the projection (first rounding point) against the oracle; the per-head
     # stage against the oracle fed the GPU's stored projection
-    gq = wsq[:T * nqkv * 2].view(torch.int16).view(T, nqkv)
+    gq = ws_payload(wsq, T * nqkv * 2).view(torch.int16).view(T, nqkv)
     assert_rms_close(bits_f64(host_bits(gq)), qkvg[:, :nqkv], "qkv projection")
     qkv_gpu = np.concatenate([bits_f64(host_bits(gq)), qkvg[:, nqkv:]], axis=1)
     qr, kr, vr, gr = L.split_qkvg(dims, qkv_gpu)
@@ -197,6 +197,43 @@ def test_attention_sink(mode):
     assert_rms_close(bits_f64(host_bits(o)), ref, "o")
 
 
+@pytest.mark.parametrize("mode", ["swa", "nope"])
+def test_workspace_counters_reused(mode):
+    """Split-K attention and the decode router elect a last workgroup with
+    counters at the head of the workspace: repeated calls on one workspace
+    give identical results and leave the counter block zeroed."""
+    dims = BEAM
+    pos = np.array([2999], np.int32)
+    seq = np.zeros(1, np.int32)
+    q = dev(synth.make_h((1, dims.Hq, dims.d), 7, "cq"))
+    cache = _needle_cache(dims, 4096, 3000, "bf16", q, pos, seq, lambda p: [], 5)
+    fn = B.beam_attn_swa if mode == "swa" else B.beam_attn_nope_ssmax
+    op = B.BEAM_OP_ATTN_SWA if mode == "swa" else B.BEAM_OP_ATTN_NOPE
+    w = ws(dims, op, 1, 3000)
+    outs = []
+    for _ in range(3):
+        o = torch.empty((1, dims.Hq, dims.d), **I16)
+        fn(dims, 1, q, dev(pos), dev(seq), cache.struct(), None, o, 2999, w)
+        B.beam_check()
+        assert int(w[:1024].count_nonzero()) == 0
+        outs.append(o)
+    assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])
+    ref = L.attention(dims, bits_f64(host_bits(q)), pos, seq, cache.oracle(3000), mode)
+    assert_rms_close(bits_f64(host_bits(outs[0])), ref, "o")
+    # the router shares the workspace (same stream): same counters, same result
+    P = Params(dims, 0, 5, moe=False)
+    x = dev(synth.make_h((1, dims.D), 6, "rx", 1))
+    res = []
+    for _ in range(3):
+        idx = torch.empty((1, dims.topk), dtype=torch.int32, device="cuda")
+        wt = torch.empty((1, dims.topk), dtype=torch.float32, device="cuda")
+        B.beam_router_fp32_grouped_topk(dims, 1, x, P.t["w_r"], P.t["b_corr"], idx, wt, None, w)
+        B.beam_check()
+        assert int(w[:1024].count_nonzero()) == 0
+        res.append((idx, wt))
+    assert all(torch.equal(res[0][0], r[0]) and torch.equal(res[0][1], r[1]) for r in res)
+
+
 # ------------------------------------------------------------------ gate + o_proj
 @pytest.mark.parametrize("base,T", [(CFG0, 1), (CFG0, 9), (BEAM, 1), (BEAM, 2)])
 def test_out_gate(base, T):
@@ -221,7 +258,8 @@ def test_router(base, T):
     idx = torch.empty((T, dims.topk), dtype=torch.int32, device="cuda")
     w = torch.empty((T, dims.topk), dtype=torch.float32, device="cuda")
     lg = torch.empty((T, dims.E), dtype=torch.float32, device="cuda")
-    B.beam_router_fp32_grouped_topk(dims, T, dev(x), P.t["w_r"], P.t["b_corr"], idx, w, lg)
+    B.beam_router_fp32_grouped_topk(dims, T, dev(x), P.t["w_r"], P.t["b_corr"], idx, w, lg,
+                                    ws(dims, B.BEAM_OP_ROUTER, T))
     B.beam_check()
     check_routing(dims, x, P, idx.cpu().numpy(), w.cpu().numpy(), lg.cpu().numpy(), "router")
     # without logits output (workspace path) the selection is identical

@@ -94,6 +94,16 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
+// 16 bytes per lane from global memory straight into LDS (gfx950): a wave
+// writes 64 x 16 B contiguously from the wave-uniform LDS address `lds`. The
+// builtin exists only in the device pass; the host pass compiles an empty body
+// so that it still emits the kernels' launch stubs.
+__device__ __forceinline__ void load_lds16(const void* g, void* lds) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_global_load_lds(g, lds, 16, 0, 0);
+#endif
+}
+
 // ---- last-arriver election ---------------------------------------------------
 // Workgroups that each publish partial results and then need one of them to
 // combine everything. Published values are written with st_dev: a relaxed

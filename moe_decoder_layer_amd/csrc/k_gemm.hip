@@ -5,11 +5,12 @@
 // Tiling: a 256-thread workgroup owns a 256 x 256 tile of C; its 4 waves sit
 // in a 2 x 2 grid and each owns 128 x 128 (4 x 4 MFMA blocks of 32 x 32,
 // 256 fp32 accumulators per lane). K advances in slabs of 64: the next slab
-// is fetched from global memory into registers while the current one is
-// multiplied out of LDS, then stored into the other half of a double buffer.
-// LDS rows are 128 bytes (64 bf16); the eight 16-byte chunks of row r are
-// stored at chunk ^ (r & 7) so the 16-byte fragment reads of 8 consecutive
-// rows land on distinct banks.
+// is loaded from global memory straight into the other half of a double
+// buffer in LDS (no register staging) while the current one is multiplied
+// out; inside a slab the operand fragments of k-step ks + 1 are read from LDS
+// while the MFMAs of k-step ks run. LDS rows are 128 bytes (64 bf16); the
+// eight 16-byte chunks of row r are stored at chunk ^ (r & 7) so the 16-byte
+// fragment reads of 8 consecutive rows land on distinct banks.
 //
 // Variants (template Epi) cover the projections of the Beam layer ("Reflection
 // Beam 1.0 on vLLM": packed q|k|v|gate GEMM of optimisation change 5, o_proj,
@@ -20,17 +21,25 @@
 // Grouped mode: the M axis is a list of per-expert row segments; tile i maps to
 // (expert, first row) through a prefix sum of per-expert tile counts, A rows
 // may be gathered through an index list, and B is that expert's weight block.
+//
+// Tile order: workgroup b of the 1-D grid runs on XCD b % 8, and each XCD has
+// its own L2. Each XCD therefore gets a contiguous eighth of the tile list,
+// walked in column-major groups of kGroupM tile rows, so the ~32 tiles an XCD
+// holds at once share a few A row panels and B column panels in its L2.
 #include "common.h"
 #include "internal.h"
 
 namespace beam {
 
 constexpr int BM = 256, BN = 256, BK = 64;
-constexpr int GEMM_THREADS = 256;
+constexpr int kGemmWaves = 8;  // waves per workgroup (4 or 8)
+constexpr int kXcds = 8;
+constexpr int kGroupM = 8;
 
 enum : int { EPI_BF16 = 0, EPI_SWIGLU = 1, EPI_F32 = 2 };
 
 struct GemmArgs {
+  int tiles_m, tiles_n;       // tile grid (tiles_m counts grouped-mode tile slots)
   const uint16_t* A;      // [M][lda] (or gathered rows)
   const uint16_t* B;      // [N][ldb] (per-expert base + e * b_expert_stride in grouped mode)
   int M, N, K;
@@ -51,17 +60,37 @@ struct GemmArgs {
 
 __device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ (row & 7); }
 
-template <int EPI>
-__global__ __launch_bounds__(GEMM_THREADS) void gemm_bf16_kernel(GemmArgs g) {
+// WAVES = 4: waves in a 2 x 2 grid, 128 x 128 each (1 wave per SIMD);
+// WAVES = 8: waves in a 2 x 4 grid, 128 x 64 each (2 waves per SIMD, so one
+// issues MFMAs while the other waits on LDS).
+template <int EPI, int WAVES>
+__global__ __launch_bounds__(WAVES * 64) void gemm_bf16_kernel(GemmArgs g) {
+  constexpr int WCOLS = WAVES / 2;     // wave grid columns
+  constexpr int WN = BN / WCOLS;       // wave tile width (128 or 64)
+  constexpr int TJ = WN / 32;          // 32-wide MFMA blocks per wave row
+  constexpr int RPW = BM / WAVES;      // tile rows each wave loads (A and B)
   extern __shared__ __align__(16) uint16_t lds[];
   // double buffer: A0 | A1 | B0 | B1
   auto As = [&](int buf) { return lds + buf * (BM * BK); };
   auto Bs = [&](int buf) { return lds + 2 * BM * BK + buf * (BN * BK); };
 
+  // ---- workgroup -> tile (XCD-contiguous, grouped column-major) ---------------
+  int tm, tn;
+  {
+    const int nt = g.tiles_m * g.tiles_n;
+    const int b = blockIdx.x, x = b % kXcds, li = b / kXcds;
+    const int q = nt / kXcds, r = nt % kXcds;
+    const int t = x * q + min(x, r) + li;  // this XCD's li-th tile
+    const int span = kGroupM * g.tiles_n;  // tiles per group of kGroupM tile rows
+    const int grp = t / span, w = t - grp * span;
+    const int rows = min(kGroupM, g.tiles_m - grp * kGroupM);
+    tm = grp * kGroupM + w % rows;
+    tn = w / rows;
+  }
   // ---- tile -> (rows, expert) ------------------------------------------------
   int m0, mrows, e = 0;
   if (g.seg_off) {
-    const int ti = blockIdx.y;
+    const int ti = tm;
     if (ti >= g.tile_off[g.E]) return;
     int lo = 0, hi = g.E;  // largest e with tile_off[e] <= ti
     while (hi - lo > 1) {
@@ -73,88 +102,96 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_bf16_kernel(GemmArgs g) {
     m0 = seg0 + (ti - g.tile_off[e]) * BM;
     mrows = min(BM, seg1 - m0);
   } else {
-    m0 = blockIdx.y * BM;
+    m0 = tm * BM;
     mrows = min(BM, g.M - m0);
   }
-  const int n0 = blockIdx.x * BN;  // tile column origin (EPI_SWIGLU: in act columns x 2)
+  const int n0 = tn * BN;  // tile column origin (EPI_SWIGLU: in act columns x 2)
   const uint16_t* Bbase = g.B + (long long)e * g.b_expert_stride;
 
-  // ---- global load assignment: thread -> (row, 16 B chunk) ---------------------
+  // ---- global -> LDS loads ------------------------------------------------------
+  // gfx950 loads 16 bytes per lane straight into LDS: one wave instruction
+  // fills 1 KiB = 8 consecutive tile rows at a wave-uniform LDS address, lane l
+  // landing at row l / 8, chunk slot l % 8. With the XOR swizzle, slot p of
+  // row r holds k-chunk p ^ (r & 7), so that is the chunk lane l fetches.
+  // Wave w fills rows [RPW w, RPW (w + 1)) of the A and of the B tile.
   const int tid = threadIdx.x;
-  const int lrow = tid >> 3, lchunk = tid & 7;  // rows lrow + 32 i, i < 8
-  const uint16_t* a_src[8];
-  const uint16_t* b_src[8];
+  const int wave = tid >> 6, lane = tid & 63;
+  constexpr int NL = RPW / 8;  // load instructions per wave and matrix
+  const uint16_t* a_src[NL];
+  const uint16_t* b_src[NL];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int r = lrow + 32 * i;
+  for (int i = 0; i < NL; ++i) {
+    const int r = wave * RPW + i * 8 + (lane >> 3);
+    const int c = (lane & 7) ^ (r & 7);
     const int rr = min(r, mrows - 1);
     const int arow = g.a_gather ? g.a_gather[m0 + rr] : m0 + rr;
-    a_src[i] = g.A + (long long)arow * g.lda + lchunk * 8;
+    a_src[i] = g.A + (long long)arow * g.lda + c * 8;
     int brow;
     if constexpr (EPI == EPI_SWIGLU) {
-      // local column c = r: wave column wc = c / 128; within it 64 gate then 64 up
-      const int wc = r >> 7, cc = r & 127;
-      const int f = (n0 >> 1) + wc * 64 + (cc & 63);
-      brow = (cc < 64) ? f : g.F + f;
-      brow = min(brow, (cc < 64 ? g.F : 2 * g.F) - 1);
+      // local column r: wave column wc = r / WN; within it WN/2 gate then WN/2 up
+      const int wc = r / WN, cc = r % WN;
+      const int f = (n0 >> 1) + wc * (WN / 2) + (cc % (WN / 2));
+      brow = (cc < WN / 2) ? f : g.F + f;
+      brow = min(brow, (cc < WN / 2 ? g.F : 2 * g.F) - 1);
     } else {
       brow = min(n0 + r, g.N - 1);
     }
-    b_src[i] = Bbase + (long long)brow * g.ldb + lchunk * 8;
+    b_src[i] = Bbase + (long long)brow * g.ldb + c * 8;
   }
-
-  uint4 ra[8], rb[8];
-  auto gload = [&](int k0) {
+  auto gload = [&](int k0, int buf) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      ra[i] = ld16(a_src[i] + k0);
-      rb[i] = ld16_nt(b_src[i] + k0);
-    }
-  };
-  auto lstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int r = lrow + 32 * i;
-      *reinterpret_cast<uint4*>(As(buf) + r * BK + swz(r, lchunk) * 8) = ra[i];
-      *reinterpret_cast<uint4*>(Bs(buf) + r * BK + swz(r, lchunk) * 8) = rb[i];
+    for (int i = 0; i < NL; ++i) {
+      load_lds16(a_src[i] + k0, As(buf) + (wave * RPW + i * 8) * BK);
+      load_lds16(b_src[i] + k0, Bs(buf) + (wave * RPW + i * 8) * BK);
     }
   };
 
-  const int wave = tid >> 6, lane = tid & 63;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WCOLS, wn = wave % WCOLS;
   const int lr = lane & 31, lk = lane >> 5;  // fragment row / k half
-  f32x16 acc[4][4];
+  f32x16 acc[4][TJ];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
+    for (int j = 0; j < TJ; ++j) acc[i][j] = f32x16{};
+
+  // fragments of k-step ks (16 deep) of buffer buf
+  auto frags = [&](int buf, int ks, bf16x8 (&af)[4], bf16x8 (&bfr)[TJ]) {
+    const uint16_t* Ab = As(buf) + (wm * 128) * BK;
+    const uint16_t* Bb = Bs(buf) + (wn * WN) * BK;
+    const int chunk = ks * 2 + lk;  // 8 bf16 = one 16 B chunk
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = i * 32 + lr;
+      af[i] = *reinterpret_cast<const bf16x8*>(Ab + r * BK + swz(r, chunk) * 8);
+    }
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) {
+      const int r = j * 32 + lr;
+      bfr[j] = *reinterpret_cast<const bf16x8*>(Bb + r * BK + swz(r, chunk) * 8);
+    }
+  };
 
   const int KT = g.K / BK;
-  gload(0);
-  lstore(0);
+  gload(0, 0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   for (int kt = 0; kt < KT; ++kt) {
     const int cur = kt & 1;
-    if (kt + 1 < KT) gload((kt + 1) * BK);
-    const uint16_t* Ab = As(cur) + (wm * 128) * BK;
-    const uint16_t* Bb = Bs(cur) + (wn * 128) * BK;
+    // the other buffer was last read in step kt - 1, which every wave has left
+    if (kt + 1 < KT) gload((kt + 1) * BK, cur ^ 1);
+    bf16x8 af[2][4], bfr[2][TJ];
+    frags(cur, 0, af[0], bfr[0]);
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks) {
-      const int chunk = ks * 2 + lk;  // 8 bf16 = one 16 B chunk
-      bf16x8 af[4], bfr[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = i * 32 + lr;
-        af[i] = *reinterpret_cast<const bf16x8*>(Ab + r * BK + swz(r, chunk) * 8);
-        bfr[i] = *reinterpret_cast<const bf16x8*>(Bb + r * BK + swz(r, chunk) * 8);
-      }
+      if (ks + 1 < BK / 16) frags(cur, ks + 1, af[(ks + 1) & 1], bfr[(ks + 1) & 1]);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < TJ; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks & 1][i], bfr[ks & 1][j],
+                                                             acc[i][j], 0, 0, 0);
     }
-    if (kt + 1 < KT) lstore(cur ^ 1);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's loads of step kt + 1
     __syncthreads();
   }
 
@@ -171,18 +208,18 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_bf16_kernel(GemmArgs g) {
         const long long m = m0 + rloc;
         if constexpr (EPI == EPI_SWIGLU) {
 #pragma unroll
-          for (int j = 0; j < 2; ++j) {
-            const int f = (n0 >> 1) + wn * 64 + 32 * j + lr;
+          for (int j = 0; j < TJ / 2; ++j) {
+            const int f = (n0 >> 1) + wn * (WN / 2) + 32 * j + lr;
             if (f < g.F) {
               const float gt = round_bf(acc[i][j][4 * ii + jj]);
-              const float up = round_bf(acc[i][j + 2][4 * ii + jj]);
+              const float up = round_bf(acc[i][j + TJ / 2][4 * ii + jj]);
               reinterpret_cast<uint16_t*>(g.out)[m * g.ldo + f] = f2bf(siluf(gt) * up);
             }
           }
         } else {
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int n = n0 + wn * 128 + 32 * j + lr;
+          for (int j = 0; j < TJ; ++j) {
+            const int n = n0 + wn * WN + 32 * j + lr;
             if (n >= g.N) continue;
             const float v = acc[i][j][4 * ii + jj];
             if constexpr (EPI == EPI_F32) {
@@ -202,16 +239,19 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_bf16_kernel(GemmArgs g) {
 
 static size_t gemm_lds_bytes() { return (size_t)2 * (BM + BN) * BK * 2; }
 
-template <int EPI>
+template <int EPI, int WAVES = kGemmWaves>
 static int launch(const GemmArgs& a, int grid_n, int grid_m, hipStream_t st) {
   static bool attr_set = false;
   if (!attr_set) {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_bf16_kernel<EPI>),
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_bf16_kernel<EPI, WAVES>),
                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)gemm_lds_bytes());
     attr_set = true;
   }
-  hipLaunchKernelGGL(gemm_bf16_kernel<EPI>, dim3(grid_n, grid_m), dim3(GEMM_THREADS),
-                     gemm_lds_bytes(), st, a);
+  GemmArgs g = a;
+  g.tiles_m = grid_m;
+  g.tiles_n = grid_n;
+  hipLaunchKernelGGL((gemm_bf16_kernel<EPI, WAVES>), dim3(grid_m * grid_n), dim3(WAVES * 64),
+                     gemm_lds_bytes(), st, g);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

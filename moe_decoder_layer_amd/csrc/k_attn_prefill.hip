@@ -272,6 +272,264 @@ __global__ __launch_bounds__(768) void attn_prefill_kernel(
     }
 }
 
+// ---------------------------------------------------------------------------
+// bf16 cache, head dim 128: K and V^T tiles go from global memory straight into
+// LDS (16 bytes per lane; one wave instruction fills 1 KiB), double-buffered,
+// so no registers hold staged data and no padding is possible: bank conflicts
+// are avoided with XOR swizzles instead.
+//   K tile  [64 keys][128 dims]: row r = 16 chunks of 16 B; chunk c of row r
+//           sits at slot c ^ fk(r), fk(r) = (r & 3) | ((r >> 1) & 4).
+//   V^T tile [128 dims][64 keys]: row = 8 chunks (8 keys each); chunk c of
+//           dim row d sits at slot c ^ (d & 7).
+// The score MFMA takes key slot s of a 32-key half from K row perm(s), perm
+// swapping bits 2 and 3, so that after the product lane (tc, g) holds the
+// probabilities of keys 16 st + 8 g + [0, 8) for st = 0, 1: exactly one
+// contiguous 16-byte V^T chunk per P.V step (fk is chosen so the 8 rows read
+// by each group of 8 lanes, perm(0..7) or perm(8..15), hit distinct banks).
+// Keys outside the sequence's [kmin, kmax] may hold anything: scores are
+// replaced by -inf, and on edge tiles the V fragment entries are zeroed.
+constexpr int DMA_HD = 128;
+
+__device__ __forceinline__ int fk_swz(int r) { return (r & 3) | ((r >> 1) & 4); }
+__device__ __forceinline__ int perm23(int s) {
+  return (s & ~12) | ((s & 4) << 1) | ((s & 8) >> 1);
+}
+
+template <bool SWA>
+__global__ __launch_bounds__(768) void attn_prefill_dma_kernel(
+    const uint16_t* __restrict__ q, const int32_t* __restrict__ pos,
+    const int32_t* __restrict__ seq, const uint16_t* __restrict__ kc,
+    const uint16_t* __restrict__ vc, int S, int Lmax, int Hq, int Hkv, int window,
+    float score_scale, int T, int ntb, const float* __restrict__ sink,
+    uint16_t* __restrict__ o) {
+  constexpr int HD = DMA_HD;
+  constexpr int KS = HD / 16;  // k-steps of the score product
+  constexpr int DB = HD / 32;  // 32-dim blocks of the output
+  constexpr int LD = HD / 2;   // dims per lane half in the score product
+  constexpr int TILE = KT * HD;              // elements of one K (or V^T) tile
+  constexpr int NI = 2 * TILE * 2 / 1024;    // 1 KiB load instructions per tile pair (32)
+  extern __shared__ __align__(16) uint16_t lds[];
+  // [K0 | K1 | V0 | V1]
+  auto sK = [&](int b) { return lds + b * TILE; };
+  auto sV = [&](int b) { return lds + 2 * TILE + b * TILE; };
+  __shared__ int sinfo[3];
+
+  const int nw = blockDim.x >> 6, tid = threadIdx.x;
+  const int j = blockIdx.y;
+  const int grp = Hq / Hkv;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int hh = wave % grp, tb = wave / grp;
+  const int h = j * grp + hh;
+  const int tc = lane & 31, g = lane >> 5;
+  const int tblk = 32 * ntb;
+  const int t0 = blockIdx.x * tblk;
+  const int t = t0 + 32 * tb + tc;
+  const bool tok = t < T;
+  int p = tok ? pos[t] : -1, s = tok ? seq[t] : -1;
+  if (p < 0 || p >= Lmax || s < 0 || s >= S) {
+    p = -1;
+    s = -1;
+  }
+  const int lo = SWA ? max(0, p - window + 1) : 0;
+
+  bf16x8 qf[KS];
+  if (p >= 0) {
+    const uint16_t* qp = q + ((size_t)t * Hq + h) * HD + g * LD;
+#pragma unroll
+    for (int i = 0; i < KS; ++i) qf[i] = as_bf16x8(ld16(qp + i * 8));
+  } else {
+#pragma unroll
+    for (int i = 0; i < KS; ++i) qf[i] = bf16x8{};
+  }
+  float m = -INFINITY, lsum = 0.f;
+  f32x16 oacc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) oacc[db] = f32x16{};
+
+  int s_prev = -1;
+  for (;;) {
+    // ---- next sequence present in the block, and its key range ------------
+    if (wave == 0) {
+      int tt = t0 + lane, pp = -1, ss = -1;
+      if (lane < tblk && tt < T) {
+        pp = pos[tt];
+        ss = seq[tt];
+        if (pp < 0 || pp >= Lmax || ss < 0 || ss >= S) ss = -1;
+      }
+      int sc = (ss > s_prev) ? ss : 0x7fffffff;
+      for (int o2 = 32; o2 > 0; o2 >>= 1) sc = min(sc, __shfl_xor(sc, o2, 64));
+      const bool in = (ss == sc);
+      int kmn = in ? (SWA ? max(0, pp - window + 1) : 0) : 0x7fffffff;
+      int kmx = in ? pp : -1;
+      for (int o2 = 32; o2 > 0; o2 >>= 1) {
+        kmn = min(kmn, __shfl_xor(kmn, o2, 64));
+        kmx = max(kmx, __shfl_xor(kmx, o2, 64));
+      }
+      if (lane == 0) {
+        sinfo[0] = sc;
+        sinfo[1] = kmn;
+        sinfo[2] = kmx;
+      }
+    }
+    __syncthreads();
+    const int s_cur = sinfo[0], kmin = sinfo[1], kmax = sinfo[2];
+    __syncthreads();
+    if (s_cur == 0x7fffffff) break;
+    s_prev = s_cur;
+    const bool mine = (s == s_cur);
+    // a tile is interior for this wave when every token of the wave belongs to
+    // this sequence and sees all 64 of its keys: no masking needed
+    int p_min = mine ? p : 0x7fffffff, lo_max = mine ? lo : 0;
+    for (int o2 = 32; o2 > 0; o2 >>= 1) {
+      p_min = min(p_min, __shfl_xor(p_min, o2, 64));
+      lo_max = max(lo_max, __shfl_xor(lo_max, o2, 64));
+    }
+    const bool all_mine = __all(mine);
+    const uint16_t* kbase_p = kc + ((size_t)s_cur * Hkv + j) * (size_t)Lmax * HD;
+    const uint16_t* vbase_p = vc + ((size_t)s_cur * Hkv + j) * (size_t)HD * Lmax;
+    const int kb0 = kmin & ~(KT - 1);
+    const int ntiles = (kmax - kb0) / KT + 1;
+
+    // instruction u < 16: K rows 4u..4u+3; u >= 16: V^T dim rows 8(u-16)..+7.
+    // kb + 63 <= Lmax - 1 (kb is 64-aligned, kb <= kmax < Lmax, Lmax % 64 == 0).
+    auto gload = [&](int kb, int buf) {
+      for (int u = wave; u < NI; u += nw) {
+        if (u < NI / 2) {
+          const int r = 4 * u + (lane >> 4);
+          const int c = (lane & 15) ^ fk_swz(r);
+          load_lds16(kbase_p + (size_t)(kb + r) * HD + c * 8, sK(buf) + 4 * u * HD);
+        } else {
+          const int u2 = u - NI / 2;
+          const int d = 8 * u2 + (lane >> 3);
+          const int c = (lane & 7) ^ (d & 7);
+          load_lds16(vbase_p + (size_t)d * Lmax + kb + c * 8, sV(buf) + 8 * u2 * KT);
+        }
+      }
+    };
+
+    gload(kb0, 0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    for (int it = 0; it < ntiles; ++it) {
+      const int cur = it & 1;
+      const int kb = kb0 + it * KT;
+      // the other buffer was last read in tile it - 1, which every wave has left
+      if (it + 1 < ntiles) gload(kb + KT, cur ^ 1);
+      const bool edge = (kb < kmin) || (kb + KT - 1 > kmax);
+      const bool interior = all_mine && kb >= lo_max && kb + KT - 1 <= p_min;
+      if (__any(mine)) {  // waves with no token of this sequence only load
+#pragma unroll 1
+        for (int kh = 0; kh < 2; ++kh) {
+          const int kbase = kb + kh * 32;
+          f32x16 sacc = f32x16{};
+          const int kr = kh * 32 + perm23(tc);
+          const uint16_t* krow = sK(cur) + kr * HD;
+#pragma unroll
+          for (int i = 0; i < KS; ++i) {
+            const int c = g * (LD / 8) + i;
+            const bf16x8 kf = *reinterpret_cast<const bf16x8*>(krow + (c ^ fk_swz(kr)) * 8);
+            sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[i], sacc, 0, 0, 0);
+          }
+          // sacc[4 i + jj] = S[key kbase + 16 (i >> 1) + 8 g + 4 (i & 1) + jj][token tc],
+          // raw (unscaled) scores; m is the running max of raw scores and the
+          // scale (> 0) enters once, inside exp2(s * c - m * c)
+          if (!interior) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+              for (int jj = 0; jj < 4; ++jj) {
+                const int key = kbase + 16 * (i >> 1) + 8 * g + 4 * (i & 1) + jj;
+                if (!mine || key < lo || key > p) sacc[4 * i + jj] = -INFINITY;
+              }
+          }
+          float mx = -INFINITY;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[i]);
+          mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+          const float mn = fmaxf(m, mx);
+          const float alpha =
+              (mn == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f((m - mn) * score_scale);
+          const float moff = (mn == -INFINITY) ? 0.f : -mn * score_scale;
+          float rs = 0.f;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            // masked scores are -inf: exp2(-inf) = 0
+            const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[i], score_scale, moff));
+            sacc[i] = pr;
+            rs += pr;
+          }
+          rs += __shfl_xor(rs, 32, 64);
+          lsum = lsum * alpha + rs;
+          m = mn;
+          if (__any(alpha != 1.f)) {  // rescale only when some running max moved
+#pragma unroll
+            for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
+          }
+#pragma unroll
+          for (int st = 0; st < 2; ++st) {
+            // hi = p truncated to bf16 (exact, one AND), lo = bf16(p - hi):
+            // p is carried to ~16 bits as in a round-to-nearest split
+            uint32_t phw[4];
+            bf16x8 pl;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+              const float p0 = sacc[4 * (2 * st + (k >> 1)) + 2 * (k & 1)];
+              const float p1 = sacc[4 * (2 * st + (k >> 1)) + 2 * (k & 1) + 1];
+              const uint32_t h0 = __float_as_uint(p0) & 0xffff0000u;
+              const uint32_t h1 = __float_as_uint(p1) & 0xffff0000u;
+              phw[k] = __builtin_amdgcn_perm(h1, h0, 0x07060302u);  // (h0 >> 16) | h1
+              pl[2 * k] = (__bf16)(p0 - __uint_as_float(h0));
+              pl[2 * k + 1] = (__bf16)(p1 - __uint_as_float(h1));
+            }
+            const bf16x8 ph = __builtin_bit_cast(bf16x8, uint4{phw[0], phw[1], phw[2], phw[3]});
+            // this lane's keys: kbase + 16 st + 8 g + [0, 8), one V^T chunk
+            const int vchunk = kh * 4 + 2 * st + g;
+            const int key0 = kbase + 16 * st + 8 * g;
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+              const int d = db * 32 + tc;
+              bf16x8 vf = *reinterpret_cast<const bf16x8*>(sV(cur) + d * KT +
+                                                           (vchunk ^ (d & 7)) * 8);
+              if (edge) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                  if (key0 + e < kmin || key0 + e > kmax) vf[e] = (__bf16)0.0f;
+              }
+              oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, ph, oacc[db], 0, 0, 0);
+              oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pl, oacc[db], 0, 0, 0);
+            }
+          }
+        }
+      }
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's loads of tile it + 1
+      __syncthreads();
+    }
+  }
+  if (!tok || tb >= ntb) return;
+  if (sink) {
+    const float sl2 = sink[h] * 1.4426950408889634f;
+    const float ms = (m == -INFINITY) ? -INFINITY : m * score_scale;  // log2 domain
+    const float mn = fmaxf(ms, sl2);
+    const float a = (m == -INFINITY) ? 0.f : exp2f(ms - mn);
+    lsum = lsum * a + exp2f(sl2 - mn);
+#pragma unroll
+    for (int db = 0; db < DB; ++db) oacc[db] *= a;
+  }
+  const float inv = (lsum > 0.f) ? 1.f / lsum : 0.f;
+  uint16_t* op = o + ((size_t)t * Hq + h) * HD;
+  // oacc[db][4 i + jj] = O[token tc][dim 32 db + 8 i + 4 g + jj]
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int d0 = 32 * db + 8 * i + 4 * g;
+      uint2 w;
+      w.x = pack_bf2(oacc[db][4 * i] * inv, oacc[db][4 * i + 1] * inv);
+      w.y = pack_bf2(oacc[db][4 * i + 2] * inv, oacc[db][4 * i + 3] * inv);
+      *reinterpret_cast<uint2*>(op + d0) = w;
+    }
+}
+
 static size_t attn_prefill_lds(int hd) {
   return 2 * (size_t)KT * (hd + 8) * 2 + 2 * (size_t)hd * (KT + 4) * 2;
 }
@@ -289,6 +547,23 @@ int launch_attn_prefill(int T, int Hq, int Hkv, int hd, int swa, int window, int
   if (grp * ntb > 12) return -1;
   const dim3 grid((T + 32 * ntb - 1) / (32 * ntb), Hkv), block(64 * grp * ntb);
   const float vs = fp8 ? v_scale : 1.0f;
+  if (!fp8 && hd == DMA_HD) {
+    const size_t sh = (size_t)4 * KT * DMA_HD * 2;
+    auto go = [&](auto kern) {
+      static bool attr = false;
+      if (!attr) {
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)sh);
+        attr = true;
+      }
+      hipLaunchKernelGGL(kern, grid, block, sh, st, q, pos, seq, (const uint16_t*)kc,
+                         (const uint16_t*)vc, S, Lmax, Hq, Hkv, window, score_scale, T, ntb,
+                         sink, o);
+    };
+    if (swa) go(attn_prefill_dma_kernel<true>);
+    else go(attn_prefill_dma_kernel<false>);
+    return hipGetLastError() == hipSuccess ? 0 : -1;
+  }
 #define PF(HD_, F8, SW)                                                                       \
   do {                                                                                         \
     const size_t sh = attn_prefill_lds(HD_);                                                   \

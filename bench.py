@@ -45,6 +45,9 @@ def parse():
     ap.add_argument("--cpu-steps", type=int, default=3)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB copy kernel (HBM counter calibration)")
+    ap.add_argument("--counters", action="store_true",
+                    help="only launch the expert gate/up kernel, eagerly, 20 times "
+                         "(a short program for rocprofv3 --pmc passes)")
     return ap.parse_args()
 
 
@@ -150,6 +153,17 @@ def main():
 
     # layer entry pre-norm once; then validate one eager chain
     B.beam_boundary_norm_residual(dims, 1, None, None, h, sets[0].t["w_attn_pre"], x, 0)
+    if a.counters:
+        step(sets[0])           # a routed token: x2 and idx as in a layer step
+        act = torch.empty((1, dims.topk + 1, dims.F), **I16)
+        torch.cuda.synchronize()
+        for i in range(20):
+            B.beam_moe_experts_up(dims, 1, x2, idx, sets[i % 2].t["w13"], None, act)
+        torch.cuda.synchronize()
+        B.beam_check()
+        print(json.dumps({"counters_run": "expert_w13_swiglu_kernel", "launches": 20,
+                          "algorithmic_bytes_per_launch": up_bytes_of(dims)}))
+        return
     for i in range(a.chain):
         step(sets[i % 2])
     B.beam_check()
@@ -202,7 +216,7 @@ def main():
     e1.record(s)
     torch.cuda.synchronize()
     up_us = e0.elapsed_time(e1) * 1000.0 / (5 * up_reps)
-    up_bytes = dims.topk * 2 * dims.F * dims.D * 2 + D * 2 + dims.topk * dims.F * 2
+    up_bytes = up_bytes_of(dims)
     up_gbs = up_bytes / (up_us * 1e-6) / 1e9
     step_bytes = (dims.qkvg_rows * D * 2 + D * dims.Hq * dims.d * 2 + dims.E * D * 4
                   + dims.topk * 3 * dims.F * D * 2 + dims.window * dims.Hkv * dims.d * 2 * 2
@@ -231,7 +245,7 @@ def main():
                    "graph_chain": a.chain},
         "roofline": {"bound": "hbm", "kernel": "expert_w13_swiglu_kernel",
                      "achieved": round(up_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(up_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(up_gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
                      "bytes_per_launch": up_bytes, "us_per_launch": round(up_us, 3)},
         "step_roofline": {"bound": "hbm", "bytes_per_step": step_bytes,
                           "achieved": round(step_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -251,6 +265,52 @@ def main():
 
 
 MFMA_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak (published)
+
+
+def up_bytes_of(dims):
+    """Algorithmic HBM bytes of one expert gate/up launch at batch 1: the 8
+    selected experts' gate and up rows, the activation row in, act out."""
+    return dims.topk * 2 * dims.F * dims.D * 2 + dims.D * 2 + dims.topk * dims.F * 2
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "expert_w13_swiglu_b1_traffic.md")
+KERNEL_SRCS = [os.path.join(ROOT, "moe_decoder_layer_amd", "csrc", f)
+               for f in ("k_gemv.hip", "common.h")]
+
+
+def kernel_source_hash():
+    """sha256 over the sources the expert gate/up kernel is built from."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SRCS:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per launch of the expert gate/up kernel from the committed
+    rocprofv3 counter summary, or None when that summary is missing or was
+    taken on a different version of the kernel source."""
+    try:
+        txt = open(TRAFFIC_FILE).read()
+    except OSError:
+        return None
+    fields = {}
+    for line in txt.splitlines():
+        if line.startswith("- ") and ": " in line:
+            k, v = line[2:].split(": ", 1)
+            fields[k.strip()] = v.strip().strip("`")
+    try:
+        src_hash = kernel_source_hash()
+    except OSError:
+        return None
+    if fields.get("kernel_source_sha256") != src_hash:
+        return None
+    try:
+        return int(fields["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def prefill_leg(a):

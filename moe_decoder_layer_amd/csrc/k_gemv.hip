@@ -170,6 +170,37 @@ __global__ __launch_bounds__(GT) void gemv_gate_oproj_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// Single-token packed projection, a grid resident all at once: each wave
+// requests its whole weight row (NB chunks per lane, K = 64 * NB * 8) before
+// the workgroup stages the activation, so the HBM stream starts at once
+// instead of after the staging round trip.
+template <int NB>
+__global__ __launch_bounds__(GT) void gemv_qkvg_wf_kernel(const uint16_t* __restrict__ W, int N,
+                                                          int K, const uint16_t* __restrict__ X,
+                                                          int Nqkv, uint16_t* __restrict__ qkv,
+                                                          uint16_t* __restrict__ g_out) {
+  extern __shared__ __align__(16) uint16_t xs[];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int n = blockIdx.x * 4 + wave;
+  const uint16_t* wr = W + (size_t)min(n, N - 1) * K;
+  uint4 wv[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) wv[b] = ld16_nt(wr + (size_t)(lane + 64 * b) * 8);
+  stage_rows(xs, X, K, K, 1, 1);
+  __syncthreads();
+  float acc = 0.f;
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+    acc = dot8_bf16(wv[b], *reinterpret_cast<const uint4*>(xs + (lane + 64 * b) * 8), acc);
+  acc = wave_sum(acc);
+  if (lane == 0 && n < N) {
+    const uint16_t v = f2bf(acc);
+    if (n < Nqkv) qkv[n] = v;
+    else g_out[n - Nqkv] = v;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Expert gate/up rows with SwiGLU. Slot s = t * spt + k (spt = topk, plus one
 // for a shared expert): expert e = idx[t*topk + k] (k < topk) or the shared
 // expert (k == topk). act[s][f] = bf16(silu(bf16(gate_f . x)) * bf16(up_f . x)).
@@ -329,6 +360,11 @@ int launch_gemv_qkvg(int T, int N, int K, int Nqkv, const uint16_t* W, const uin
   constexpr int R = 2;
   const dim3 grid((N + 4 * R - 1) / (4 * R), 1);
   const int nb = nb_for(K >> 3);
+  if (T == 1 && (K >> 3) == 640) {
+    hipLaunchKernelGGL((gemv_qkvg_wf_kernel<10>), dim3((N + 3) / 4), dim3(GT), (size_t)K * 2, st,
+                       W, N, K, X, Nqkv, qkv, g_out);
+    return LAUNCH_OK();
+  }
   if (T == 1) {
     const size_t sh = (size_t)K * 2;
 #define Q1(NB) hipLaunchKernelGGL((gemv_qkvg_kernel<R, NB, 1>), grid, dim3(GT), sh, st, W, N, K, X, T, Nqkv, qkv, g_out)

@@ -41,6 +41,7 @@ def parse():
     ap.add_argument("--chain", type=int, default=8, help="layer-steps per captured graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-nope", action="store_true", help="skip the NoPE fp8 decode leg")
     ap.add_argument("--prefill-reps", type=int, default=3)
     ap.add_argument("--cpu-steps", type=int, default=3)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -55,7 +56,7 @@ def parse():
 class LayerSet:
     """One layer's weights and KV cache on the device (random-init, seeded)."""
 
-    def __init__(self, dims, seed, layer, ctx, Lmax):
+    def __init__(self, dims, seed, layer, ctx, Lmax, kv="bf16"):
         import numpy as np
         import torch
 
@@ -76,13 +77,16 @@ class LayerSet:
             synth.torch_normal_bf16((2 * dims.F, dims.D), 0.02, seed, layer, "w13", e, out=w13[e])
             synth.torch_normal_bf16((dims.D, dims.F), 0.02, seed, layer, "w2", e, out=w2[e])
         self.t["w13"], self.t["w2"] = w13, w2
-        K, V, _, _ = synth.torch_kv_prior(dims, 1, ctx, "bf16", seed, layer)
-        self.K = torch.empty((1, dims.Hkv, Lmax, dims.d), dtype=torch.int16, device="cuda")
-        self.V = torch.empty((1, dims.Hkv, dims.d, Lmax), dtype=torch.int16, device="cuda")
+        K, V, ks, vs = synth.torch_kv_prior(dims, 1, ctx, kv, seed, layer)
+        ct = torch.int16 if kv == "bf16" else torch.uint8
+        self.K = torch.empty((1, dims.Hkv, Lmax, dims.d), dtype=ct, device="cuda")
+        self.V = torch.empty((1, dims.Hkv, dims.d, Lmax), dtype=ct, device="cuda")
         self.K[:, :, :ctx] = K
         self.V[:, :, :, :ctx] = V.transpose(2, 3)
         del K, V
-        self.kv = B.kv_struct(self.K, self.V, B.BEAM_KV_BF16, 1.0, 1.0, 1, Lmax)
+        self.kv = B.kv_struct(self.K, self.V,
+                              B.BEAM_KV_BF16 if kv == "bf16" else B.BEAM_KV_FP8_E4M3,
+                              ks, vs, 1, Lmax)
 
 
 def main():
@@ -109,14 +113,109 @@ def main():
                           "launches": 5}))
         return
 
-    cfg = synth.config(1)
-    dims, ex = cfg.dims, cfg.extra
-    pos0, Lmax, n = ex["pos"], ex["Lmax"], ex["n"]
-    t0 = time.time()
-    sets = [LayerSet(dims, seed, ex["layer"], pos0, Lmax) for seed in (0, 1)]
-    log(f"[bench] weights + caches drawn in {time.time() - t0:.1f}s "
-        f"({torch.cuda.memory_allocated() / 2**30:.1f} GiB)")
+    swa = decode_leg(a, 1)
+    if a.counters:
+        return
+    sets, dims, ex = swa.pop("_sets"), swa.pop("_dims"), swa.pop("_ex")
+    us_step = swa["us_mean"]
+    D = dims.D
+    s = torch.cuda.current_stream()
 
+    # --- dominant kernel: the selected-expert gate/up GEMV with SwiGLU ---------
+    I16 = dict(dtype=torch.int16, device="cuda")
+    x2, idx = swa.pop("_x2"), swa.pop("_idx")
+    act = torch.empty((1, dims.topk + 1, dims.F), **I16)
+    up_reps = 40
+    stream = torch.cuda.Stream()
+    g2 = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(g2, stream=stream):
+            for i in range(up_reps):
+                B.beam_moe_experts_up(dims, 1, x2, idx, sets[i % 2].t["w13"], None, act)
+    torch.cuda.synchronize()
+    g2.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(s)
+    for _ in range(5):
+        g2.replay()
+    e1.record(s)
+    torch.cuda.synchronize()
+    up_us = e0.elapsed_time(e1) * 1000.0 / (5 * up_reps)
+    up_bytes = up_bytes_of(dims)
+    up_gbs = up_bytes / (up_us * 1e-6) / 1e9
+    step_bytes = swa["bytes_per_step"]
+    step_gbs = step_bytes / (us_step * 1e-6) / 1e9
+    log(f"[bench] expert gate/up GEMV: {up_us:.2f} us/launch, {up_gbs:.0f} GB/s; "
+        f"step {step_gbs:.0f} GB/s over {step_bytes} B")
+    del g2
+    ceiling = hbm_read_ceiling()
+    log(f"[bench] streaming-read ceiling (torch reduction over 4 GiB): {ceiling:.0f} GB/s")
+
+    out = {
+        "metric": "Beam layer decode µs/step (b=1, 100K ctx) + prefill tok/s; % HBM/MFMA roofline",
+        "value": round(us_step, 3),
+        "unit": "µs/step",
+        "n_gpus": 1,
+        "steps": swa["steps"],
+        "warmup": swa["warmup"],
+        "ms_per_step": round(us_step / 1000.0, 6),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "beam_swa_moe_layer_decode", "batch": 1, "context": ex["pos"],
+                   "kv_cache": "bf16", "hidden": D, "q_heads": dims.Hq, "kv_heads": dims.Hkv,
+                   "head_dim": dims.d, "window": dims.window, "experts": dims.E,
+                   "topk": dims.topk, "expert_dff": dims.F, "weight_sets": 2,
+                   "graph_chain": a.chain},
+        "us_per_step_median": swa["us_median"],
+        "us_per_step_p90": swa["us_p90"],
+        "roofline": {"bound": "hbm", "kernel": "expert_w13_swiglu_kernel",
+                     "achieved": round(up_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(up_gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
+                     "bytes_per_launch": up_bytes, "us_per_launch": round(up_us, 3)},
+        "step_roofline": {"bound": "hbm", "bytes_per_step": step_bytes,
+                          "achieved": round(step_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                          "frac": round(step_gbs / HBM_PEAK_GBS, 4),
+                          "measured_read_ceiling_gbs": round(ceiling, 1)},
+    }
+    cpu_set = sets[0] if (a.no_prefill and a.no_nope) else None
+    del sets
+    torch.cuda.empty_cache()
+    if not a.no_nope:
+        nope = decode_leg(a, 2)
+        for k in ("_sets", "_dims", "_ex", "_x2", "_idx"):
+            nope.pop(k)
+        out["decode_nope"] = nope
+        torch.cuda.empty_cache()
+    if not a.no_prefill:
+        out["prefill"] = prefill_leg(a)
+    if not a.no_cpu_baseline:
+        if cpu_set is None:
+            cpu_set = LayerSet(dims, 0, ex["layer"], ex["pos"], ex["Lmax"])
+        out["cpu_baseline"] = cpu_baseline(cpu_set, dims, ex, a.cpu_steps)
+    print(json.dumps(out))
+
+
+def decode_leg(a, ci):
+    """Batch-1 decode layer-steps of config ci (1: SWA layer 10 on a 100K bf16
+    cache; 2: NoPE layer 11 on a 100K fp8 cache), chained 8 per HIP graph over
+    two alternating full weight sets. Each graph replay is timed on its own
+    (HIP events between replays) for the mean, median and p90 per step."""
+    import numpy as np
+    import torch
+
+    import moe_decoder_layer_amd as B
+    import synth
+    cfg = synth.config(ci)
+    dims, ex = cfg.dims, cfg.extra
+    pos0, Lmax, n, mode, kvt = ex["pos"], ex["Lmax"], ex["n"], ex["mode"], ex["kv"]
+    t0 = time.time()
+    sets = [LayerSet(dims, seed, ex["layer"], pos0, Lmax, kvt) for seed in (0, 1)]
+    log(f"[bench] {mode} decode: weights + caches drawn in {time.time() - t0:.1f}s "
+        f"({torch.cuda.memory_allocated() / 2**30:.1f} GiB)")
     I16 = dict(dtype=torch.int16, device="cuda")
     D = dims.D
     h = synth.torch_normal_bf16((1, D), 1.0, 0, "bench_h")
@@ -131,19 +230,24 @@ def main():
     w = torch.empty((1, dims.topk), dtype=torch.float32, device="cuda")
     pos = torch.tensor([pos0], dtype=torch.int32, device="cuda")
     seq = torch.zeros(1, dtype=torch.int32, device="cuda")
-    rope_h = np.zeros((Lmax, dims.d), np.float32)
-    B.beam_rope_table(rope_h, Lmax, dims.d, dims.theta)
-    rope = torch.from_numpy(rope_h).cuda()
+    rope = None
+    if mode == "swa":
+        rope_h = np.zeros((Lmax, dims.d), np.float32)
+        B.beam_rope_table(rope_h, Lmax, dims.d, dims.theta)
+        rope = torch.from_numpy(rope_h).cuda()
+    attn_op = B.BEAM_OP_ATTN_SWA if mode == "swa" else B.BEAM_OP_ATTN_NOPE
+    attn = B.beam_attn_swa if mode == "swa" else B.beam_attn_nope_ssmax
+    m = B.BEAM_SWA_ROPE if mode == "swa" else B.BEAM_NOPE_SSMAX
     wsz = lambda op, ctx=0: torch.zeros(max(256, B.beam_workspace_size(dims, op, 1, ctx)),  # noqa
                                         dtype=torch.uint8, device="cuda")
-    ws_qkv, ws_attn = wsz(B.BEAM_OP_QKV), wsz(B.BEAM_OP_ATTN_SWA, pos0 + 1)
+    ws_qkv, ws_attn = wsz(B.BEAM_OP_QKV), wsz(attn_op, pos0 + 1)
     ws_r, ws_moe = wsz(B.BEAM_OP_ROUTER), wsz(B.BEAM_OP_MOE)
 
     def step(L: LayerSet):
         t = L.t
         B.beam_qk_norm_rope_ssmax_kvwrite(dims, 1, x, t["w_qkvg"], t["w_qnorm"], t["w_knorm"],
-                                          pos, seq, B.BEAM_SWA_ROPE, rope, q, g, L.kv, ws_qkv)
-        B.beam_attn_swa(dims, 1, q, pos, seq, L.kv, None, o, pos0, ws_attn)
+                                          pos, seq, m, rope, q, g, L.kv, ws_qkv)
+        attn(dims, 1, q, pos, seq, L.kv, None, o, pos0, ws_attn)
         B.beam_out_gate(dims, 1, o, g, t["b_gate"], t["w_o"], y)
         B.beam_boundary_norm_residual(dims, 1, y, t["w_attn_post"], h, t["w_ffn_pre"], x2, n)
         B.beam_router_fp32_grouped_topk(dims, 1, x2, t["w_r"], t["b_corr"], idx, w, None, ws_r)
@@ -163,7 +267,7 @@ def main():
         B.beam_check()
         print(json.dumps({"counters_run": "expert_w13_swiglu_kernel", "launches": 20,
                           "algorithmic_bytes_per_launch": up_bytes_of(dims)}))
-        return
+        return {}
     for i in range(a.chain):
         step(sets[i % 2])
     B.beam_check()
@@ -185,83 +289,52 @@ def main():
         graph.replay()
     torch.cuda.synchronize()
     B.beam_check()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     s = torch.cuda.current_stream()
-    ev0.record(s)
-    for _ in range(reps):
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    evs[0].record(s)
+    for r in range(reps):
         graph.replay()
-    ev1.record(s)
+        evs[r + 1].record(s)
     torch.cuda.synchronize()
     steps = reps * a.chain
-    ms_total = ev0.elapsed_time(ev1)
+    per = np.array([evs[r].elapsed_time(evs[r + 1]) for r in range(reps)]) * 1000.0 / a.chain
+    ms_total = evs[0].elapsed_time(evs[-1])
     us_step = ms_total * 1000.0 / steps
     B.beam_check()
-    log(f"[bench] {steps} layer-steps in {ms_total:.2f} ms: {us_step:.2f} us/step")
+    log(f"[bench] {mode} decode: {steps} layer-steps in {ms_total:.2f} ms: {us_step:.2f} us/step "
+        f"(median {np.median(per):.2f}, p90 {np.percentile(per, 90):.2f})")
+    kv_read = dims.window if mode == "swa" else pos0 + 1
+    kv_bytes = kv_read * dims.Hkv * dims.d * 2 * (2 if kvt == "bf16" else 1)
+    kv_write = dims.Hkv * dims.d * 2 * (2 if kvt == "bf16" else 1)
+    step_bytes = (dims.qkvg_rows * D * 2 + D * dims.Hq * dims.d * 2 + dims.E * D * 4
+                  + dims.topk * 3 * dims.F * D * 2 + kv_bytes + kv_write)
+    del graph
+    res = {"workload": f"beam_{mode}_moe_layer_decode", "kv_cache": kvt, "context": pos0,
+           "steps": steps, "warmup": wreps * a.chain + a.chain,
+           "us_mean": round(us_step, 3), "us_median": round(float(np.median(per)), 3),
+           "us_p90": round(float(np.percentile(per, 90)), 3), "bytes_per_step": step_bytes,
+           "hbm_frac": round(step_bytes / (us_step * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+           "_sets": sets, "_dims": dims, "_ex": ex, "_x2": x2, "_idx": idx}
+    return res
 
-    # --- dominant kernel: the selected-expert gate/up GEMV with SwiGLU ---------
-    act = torch.empty((1, dims.topk + 1, dims.F), **I16)
-    up_reps = 40
-    g2 = torch.cuda.CUDAGraph()
-    with torch.cuda.stream(stream):
-        with torch.cuda.graph(g2, stream=stream):
-            for i in range(up_reps):
-                B.beam_moe_experts_up(dims, 1, x2, idx, sets[i % 2].t["w13"], None, act)
-    torch.cuda.synchronize()
-    g2.replay()
+
+def hbm_read_ceiling():
+    """Read bandwidth of a plain reduction over a 4 GiB buffer (torch's own
+    kernel): a measured streaming ceiling to set beside the nominal 8 TB/s."""
+    import torch
+    x = torch.ones(1 << 30, dtype=torch.float32, device="cuda")
+    for _ in range(2):
+        x.sum()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(s)
+    e0.record()
     for _ in range(5):
-        g2.replay()
-    e1.record(s)
+        x.sum()
+    e1.record()
     torch.cuda.synchronize()
-    up_us = e0.elapsed_time(e1) * 1000.0 / (5 * up_reps)
-    up_bytes = up_bytes_of(dims)
-    up_gbs = up_bytes / (up_us * 1e-6) / 1e9
-    step_bytes = (dims.qkvg_rows * D * 2 + D * dims.Hq * dims.d * 2 + dims.E * D * 4
-                  + dims.topk * 3 * dims.F * D * 2 + dims.window * dims.Hkv * dims.d * 2 * 2
-                  + dims.Hkv * dims.d * 2 * 2)
-    step_gbs = step_bytes / (us_step * 1e-6) / 1e9
-    log(f"[bench] expert gate/up GEMV: {up_us:.2f} us/launch, {up_gbs:.0f} GB/s; "
-        f"step {step_gbs:.0f} GB/s over {step_bytes} B")
-
-    out = {
-        "metric": "Beam layer decode µs/step (b=1, 100K ctx) + prefill tok/s; % HBM/MFMA roofline",
-        "value": round(us_step, 3),
-        "unit": "µs/step",
-        "n_gpus": 1,
-        "steps": steps,
-        "warmup": wreps * a.chain + a.chain,
-        "ms_per_step": round(us_step / 1000.0, 6),
-        "higher_is_better": False,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic",
-        "config": {"workload": "beam_swa_moe_layer_decode", "batch": 1, "context": pos0,
-                   "kv_cache": "bf16", "hidden": D, "q_heads": dims.Hq, "kv_heads": dims.Hkv,
-                   "head_dim": dims.d, "window": dims.window, "experts": dims.E,
-                   "topk": dims.topk, "expert_dff": dims.F, "weight_sets": 2,
-                   "graph_chain": a.chain},
-        "roofline": {"bound": "hbm", "kernel": "expert_w13_swiglu_kernel",
-                     "achieved": round(up_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(up_gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
-                     "bytes_per_launch": up_bytes, "us_per_launch": round(up_us, 3)},
-        "step_roofline": {"bound": "hbm", "bytes_per_step": step_bytes,
-                          "achieved": round(step_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                          "frac": round(step_gbs / HBM_PEAK_GBS, 4)},
-    }
-    if not a.no_prefill:
-        del sets
-        torch.cuda.empty_cache()
-        out["prefill"] = prefill_leg(a)
-    if not a.no_cpu_baseline:
-        if a.no_prefill:
-            cpu_set = sets[0]
-        else:
-            cpu_set = LayerSet(dims, 0, ex["layer"], pos0, Lmax)
-        out["cpu_baseline"] = cpu_baseline(cpu_set, dims, ex, a.cpu_steps)
-    print(json.dumps(out))
+    gbs = 5 * x.numel() * 4 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del x
+    return gbs
 
 
 MFMA_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak (published)

@@ -11,8 +11,10 @@
 // With S^T in the C layout, lane l owns query head l%16 for 16 keys, so the
 // online-softmax state (m, l) of a head is lane-local up to two xor shuffles,
 // and the probabilities a lane holds are exactly the keys it needs as the B
-// operand of the P.V product (no LDS round trip). V is stored transposed in
-// the cache so each lane's 4-key runs of one dim are contiguous.
+// operand of the P.V product (no LDS round trip). The score product takes its
+// keys in a permuted slot order that makes those 8 keys consecutive, and V is
+// stored transposed in the cache, so each lane's V operand is one contiguous
+// load.
 // fp8 caches are widened to bf16 exactly with gfx950's packed conversion; the
 // per-tensor scales are applied to the scores (k) and the output (v).
 // Probabilities enter the P.V product as hi + lo bf16 pairs (two MFMAs), so
@@ -91,39 +93,42 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_partial_kernel(
   for (int it = 0; it < tpw; ++it) {
     const int kb = (tile0 + (rr ? it * NW : it)) << 6;
     if (kb > p) break;
-    // the tile's K and V fragments are all requested before any is used
+    // The tile's K and V fragments are all requested before any is used.
+    // Score block st = 2 kh + b takes, in key slot s, the key
+    // 16 (s / 4) + 8 kh + 4 b + s % 4 of the tile, so that lane (col, g) ends
+    // up holding the probabilities of keys 16 g + [0, 16) (those of half kh at
+    // 16 g + 8 kh + [0, 8)): one contiguous run of V^T per lane and output tile
+    // (32 bytes bf16, 16 bytes fp8).
     bf16x8 kf[4][KS];
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
-      const size_t kr = (krow0 + kb + st * 16 + col) * HD + g * GD;
+      const int key = kb + 16 * (col >> 2) + 8 * (st >> 1) + 4 * (st & 1) + (col & 3);
+      const size_t kr = (krow0 + key) * HD + g * GD;
+      if constexpr (FP8 && KS >= 2) {  // GD = HD / 4 bytes of the row, in 16-byte loads
 #pragma unroll
-      for (int i = 0; i < KS; ++i) {
-        if constexpr (FP8) {
-          kf[st][i] =
-              e4m3x8_to_bf16x8(*reinterpret_cast<const uint2*>((const uint8_t*)kc + kr + i * 8));
-        } else {
-          kf[st][i] = as_bf16x8(ld16((const uint16_t*)kc + kr + i * 8));
+        for (int i = 0; i < KS; i += 2) {
+          const uint4 w = ld16((const uint8_t*)kc + kr + i * 8);
+          kf[st][i] = e4m3x8_to_bf16x8(uint2{w.x, w.y});
+          kf[st][i + 1] = e4m3x8_to_bf16x8(uint2{w.z, w.w});
         }
+      } else if constexpr (FP8) {
+        kf[st][0] = e4m3x8_to_bf16x8(*reinterpret_cast<const uint2*>((const uint8_t*)kc + kr));
+      } else {
+#pragma unroll
+        for (int i = 0; i < KS; ++i) kf[st][i] = as_bf16x8(ld16((const uint16_t*)kc + kr + i * 8));
       }
     }
     bf16x8 vfr[2][DT];
 #pragma unroll
-    for (int kh = 0; kh < 2; ++kh) {
-      const int key0 = kb + kh * 32 + 4 * g, key1 = key0 + 16;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const size_t vr = (vrow0 + dt * 16 + col) * (size_t)Lmax;
-        if constexpr (FP8) {
-          const uint8_t* vb = (const uint8_t*)vc + vr;
-          const bf16x4 a = e4m3x4_to_bf16x4(*reinterpret_cast<const uint32_t*>(vb + key0));
-          const bf16x4 b = e4m3x4_to_bf16x4(*reinterpret_cast<const uint32_t*>(vb + key1));
-          vfr[kh][dt] = bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-        } else {
-          const uint16_t* vb = (const uint16_t*)vc + vr;
-          const uint2 a = *reinterpret_cast<const uint2*>(vb + key0);
-          const uint2 b = *reinterpret_cast<const uint2*>(vb + key1);
-          vfr[kh][dt] = __builtin_bit_cast(bf16x8, uint4{a.x, a.y, b.x, b.y});
-        }
+    for (int dt = 0; dt < DT; ++dt) {
+      const size_t vr = (vrow0 + dt * 16 + col) * (size_t)Lmax + kb + 16 * g;
+      if constexpr (FP8) {
+        const uint4 w = ld16((const uint8_t*)vc + vr);
+        vfr[0][dt] = e4m3x8_to_bf16x8(uint2{w.x, w.y});
+        vfr[1][dt] = e4m3x8_to_bf16x8(uint2{w.z, w.w});
+      } else {
+        vfr[0][dt] = as_bf16x8(ld16((const uint16_t*)vc + vr));
+        vfr[1][dt] = as_bf16x8(ld16((const uint16_t*)vc + vr + 8));
       }
     }
     f32x4 sacc[4];
@@ -140,7 +145,7 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_partial_kernel(
     for (int st = 0; st < 4; ++st)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int key = kb + st * 16 + 4 * g + r;
+        const int key = kb + 16 * g + 8 * (st >> 1) + 4 * (st & 1) + r;
         float v = sacc[st][r] * score_scale;
         v = (key < lo || key > p) ? -INFINITY : v;
         sacc[st][r] = v;
@@ -178,16 +183,14 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_partial_kernel(
         pf[i] = (__bf16)pv;
         pl[i] = (__bf16)(pv - (float)pf[i]);
       }
-      const int key0 = kb + kh * 32 + 4 * g, key1 = key0 + 16;
+      const int key0 = kb + 16 * g + 8 * kh;  // this lane's keys key0 + [0, 8)
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
         bf16x8 vf = vfr[kh][dt];
         if (edge) {  // keys outside [lo, p] may hold anything: zero them
 #pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            const int key = (i < 4 ? key0 + i : key1 + i - 4);
-            if (key < lo || key > p) vf[i] = (__bf16)0.0f;
-          }
+          for (int i = 0; i < 8; ++i)
+            if (key0 + i < lo || key0 + i > p) vf[i] = (__bf16)0.0f;
         }
         o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf, o[dt], 0, 0, 0);
         o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pl, o[dt], 0, 0, 0);
@@ -283,22 +286,23 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_partial_kernel(
 
 // Combine the chunks of one (token, head): o = sum_c 2^(m_c-M) O_c / sum_c 2^(m_c-M) l_c.
 // An attention sink adds 2^(sink*log2e - M) to the denominator only. Wave w
-// takes chunks w, w + 4, ... in batches of 8 whose records are all requested
-// before use, keeping a running (M, L, O); the 4 waves combine through LDS.
+// takes chunks w, w + MW, ... in batches of 8 whose records are all requested
+// before use, keeping a running (M, L, O); the MW waves combine through LDS.
 template <int HD>
-__global__ __launch_bounds__(256) void attn_merge_kernel(
+__global__ __launch_bounds__(1024) void attn_merge_kernel(
     const float* __restrict__ part, const int32_t* __restrict__ pos,
     const int32_t* __restrict__ seq, int S, int Lmax, int Hq, int window, int swa, int tpw,
     int nch_stride, const float* __restrict__ sink, float v_scale, uint16_t* __restrict__ o) {
   constexpr int DPL = (HD + 63) / 64;
   constexpr int B = 8;
-  __shared__ float sm_m[4], sm_l[4], sm_o[4][HD];
+  constexpr int MW = 16;  // waves
+  __shared__ float sm_m[MW], sm_l[MW], sm_o[MW][HD];
   const int h = blockIdx.x, t = blockIdx.y;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   uint16_t* out = o + ((size_t)t * Hq + h) * HD;
   const int p = pos[t], s = seq[t];
   if (p < 0 || p >= Lmax || s < 0 || s >= S) {
-    for (int d = threadIdx.x; d < HD; d += 256) out[d] = 0;
+    for (int d = threadIdx.x; d < HD; d += MW * 64) out[d] = 0;
     return;
   }
   const int lo = swa ? max(0, p - window + 1) : 0;
@@ -307,11 +311,11 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(
   const int nch = (p + 1 - lo_al + CK - 1) / CK;
   const float* rec0 = part + ((size_t)t * Hq + h) * nch_stride * (HD + 4);
   float M = -INFINITY, L = 0.f, O[DPL] = {};
-  for (int c0 = wave; c0 < nch; c0 += 4 * B) {
+  for (int c0 = wave; c0 < nch; c0 += MW * B) {
     float mc[B], lc[B], oc[B][DPL];
 #pragma unroll
     for (int b = 0; b < B; ++b) {
-      const float* rec = rec0 + (size_t)min(c0 + 4 * b, nch - 1) * (HD + 4);
+      const float* rec = rec0 + (size_t)min(c0 + MW * b, nch - 1) * (HD + 4);
       mc[b] = rec[0];
       lc[b] = rec[1];
 #pragma unroll
@@ -323,14 +327,14 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(
     float Mn = M;
 #pragma unroll
     for (int b = 0; b < B; ++b)
-      if (c0 + 4 * b < nch) Mn = fmaxf(Mn, mc[b]);
+      if (c0 + MW * b < nch) Mn = fmaxf(Mn, mc[b]);
     const float a = exp2f(M - Mn);  // M = -inf on the first batch: a = 0
     L *= a;
 #pragma unroll
     for (int k = 0; k < DPL; ++k) O[k] *= a;
 #pragma unroll
     for (int b = 0; b < B; ++b) {
-      if (c0 + 4 * b < nch) {
+      if (c0 + MW * b < nch) {
         const float e = exp2f(mc[b] - Mn);
         L += e * lc[b];
 #pragma unroll
@@ -350,12 +354,14 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(
   }
   __syncthreads();
   if (wave != 0) return;
-  float Mt = fmaxf(fmaxf(sm_m[0], sm_m[1]), fmaxf(sm_m[2], sm_m[3]));
+  float Mt = sm_m[0];
+#pragma unroll
+  for (int w = 1; w < MW; ++w) Mt = fmaxf(Mt, sm_m[w]);
   const float sl2 = sink ? sink[h] * 1.4426950408889634f : -INFINITY;
   Mt = fmaxf(Mt, sl2);
   float Lt = sink ? exp2f(sl2 - Mt) : 0.f, Ot[DPL] = {};
 #pragma unroll
-  for (int w = 0; w < 4; ++w) {
+  for (int w = 0; w < MW; ++w) {
     const float e = (sm_m[w] == -INFINITY) ? 0.f : exp2f(sm_m[w] - Mt);
     Lt += e * sm_l[w];
 #pragma unroll
@@ -372,9 +378,13 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(
   }
 }
 
+// Split-K workgroups per launch aimed for (each wave one 64-key tile until
+// the context needs more than kAttnChunkTarget * 4 tiles).
+constexpr int kAttnChunkTarget = 4096;
+
 void attn_plan(int T, int Hkv, int span, int* tpw, int* nch) {
   const int tiles = (span + 63) / 64;
-  const int target = std::max(1, 2048 / std::max(1, Hkv * T));
+  const int target = std::max(1, kAttnChunkTarget / std::max(1, Hkv * T));
   int w = (tiles + 4 * target - 1) / (4 * target);
   w = std::min(std::max(w, 1), 64);
   *tpw = w;
@@ -385,7 +395,7 @@ void attn_plan(int T, int Hkv, int span, int* tpw, int* nch) {
 // span, so a workspace sized for a context bound serves any shorter one.
 int attn_nch_bound(int T, int Hkv, int span) {
   const int tiles = (span + 63) / 64;
-  const int target = std::max(1, 2048 / std::max(1, Hkv * T));
+  const int target = std::max(1, kAttnChunkTarget / std::max(1, Hkv * T));
   return std::max(std::max(1, std::min(target, (tiles + 3) / 4)), (tiles + 255) / 256);
 }
 
@@ -426,13 +436,13 @@ int launch_attn_decode(int T, int Hq, int Hkv, int hd, int swa, int window, int 
   const dim3 mg(Hq, T);
   const float vs = fp8 ? v_scale : 1.0f;
   if (hd == 128)
-    hipLaunchKernelGGL((attn_merge_kernel<128>), mg, dim3(256), 0, st, part, pos, seq, S, Lmax, Hq,
+    hipLaunchKernelGGL((attn_merge_kernel<128>), mg, dim3(1024), 0, st, part, pos, seq, S, Lmax, Hq,
                        window, swa, tpw, nch, sink, vs, o);
   else if (hd == 64)
-    hipLaunchKernelGGL((attn_merge_kernel<64>), mg, dim3(256), 0, st, part, pos, seq, S, Lmax, Hq,
+    hipLaunchKernelGGL((attn_merge_kernel<64>), mg, dim3(1024), 0, st, part, pos, seq, S, Lmax, Hq,
                        window, swa, tpw, nch, sink, vs, o);
   else
-    hipLaunchKernelGGL((attn_merge_kernel<32>), mg, dim3(256), 0, st, part, pos, seq, S, Lmax, Hq,
+    hipLaunchKernelGGL((attn_merge_kernel<32>), mg, dim3(1024), 0, st, part, pos, seq, S, Lmax, Hq,
                        window, swa, tpw, nch, sink, vs, o);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }

@@ -75,15 +75,20 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_bf16_kernel(GemmArgs g) {
   auto Bs = [&](int buf) { return lds + 2 * BM * BK + buf * (BN * BK); };
 
   // ---- workgroup -> tile (XCD-contiguous, grouped column-major) ---------------
+  // Grouped mode launches the worst-case number of tile rows; only the first
+  // tile_off[E] of them hold rows, so those are what gets split over the XCDs
+  // (the rest of the grid exits at once instead of idling whole XCDs).
   int tm, tn;
   {
-    const int nt = g.tiles_m * g.tiles_n;
+    const int rows_m = g.seg_off ? g.tile_off[g.E] : g.tiles_m;
+    const int nt = rows_m * g.tiles_n;
     const int b = blockIdx.x, x = b % kXcds, li = b / kXcds;
     const int q = nt / kXcds, r = nt % kXcds;
+    if (li >= q + (x < r ? 1 : 0)) return;
     const int t = x * q + min(x, r) + li;  // this XCD's li-th tile
     const int span = kGroupM * g.tiles_n;  // tiles per group of kGroupM tile rows
     const int grp = t / span, w = t - grp * span;
-    const int rows = min(kGroupM, g.tiles_m - grp * kGroupM);
+    const int rows = min(kGroupM, rows_m - grp * kGroupM);
     tm = grp * kGroupM + w % rows;
     tn = w / rows;
   }

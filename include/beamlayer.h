@@ -243,6 +243,13 @@ size_t beam_workspace_size(const beam_dims* dims, int op, int T, int max_ctx);
  * beam_qk_norm_rope_ssmax_kvwrite, computed in double and stored as float. */
 int beam_rope_table(float* out, int Lmax, int d, double theta);
 
+/* Measurement utility (not part of the layer): reads `bytes` of device memory
+ * at p once, with 16-byte non-temporal loads spread over the whole GPU, and
+ * writes nothing but (at most) one word to the device word *sink. Timing it
+ * gives a measured HBM streaming-read ceiling. bytes % 16 == 0, p 16-byte
+ * aligned. */
+int beam_hbm_read(const void* p, size_t bytes, unsigned* sink, void* stream);
+
 /* Waits for `stream`, then reports BEAM_E_HIP for a failed kernel or
  * BEAM_E_DEVICE if a device-side check tripped since the last beam_check
  * (the flag is cleared). */

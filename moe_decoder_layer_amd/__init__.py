@@ -22,7 +22,7 @@ __all__ = [
     "beam_boundary_norm_residual", "beam_qk_norm_rope_ssmax_kvwrite", "beam_attn_swa",
     "beam_attn_nope_ssmax", "beam_out_gate", "beam_router_fp32_grouped_topk",
     "beam_moe_swiglu_combine", "beam_moe_experts_up", "beam_moe_experts_down",
-    "beam_dense_swiglu", "beam_workspace_size", "beam_rope_table",
+    "beam_dense_swiglu", "beam_workspace_size", "beam_rope_table", "beam_hbm_read",
     "beam_check", "beam_last_error", "beam_version",
     "BEAM_SWA_ROPE", "BEAM_NOPE_SSMAX", "BEAM_KV_BF16", "BEAM_KV_FP8_E4M3",
     "BEAM_OP_QKV", "BEAM_OP_ATTN_SWA", "BEAM_OP_ATTN_NOPE", "BEAM_OP_OUT_GATE",
@@ -85,6 +85,7 @@ def lib():
             "beam_moe_experts_down": [POINTER(beam_dims), c_int, P, P, P, P, P, P, P],
             "beam_dense_swiglu": [c_int, c_int, c_int, P, P, P, P, P, c_size_t, P],
             "beam_rope_table": [P, c_int, c_int, c_double],
+            "beam_hbm_read": [P, c_size_t, P, P],
             "beam_check": [P],
             "beam_version": [],
             "beam_last_error": [],
@@ -222,6 +223,11 @@ def beam_moe_experts_down(dims, T, idx, w, w2, shared_w2, act, y, stream=None):
 def beam_dense_swiglu(T, D, Fd, x, w13, w2, y, ws, stream=None):
     wp, wb = _ws(ws)
     _call("beam_dense_swiglu", T, D, Fd, _p(x), _p(w13), _p(w2), _p(y), wp, wb, _s(stream))
+
+
+def beam_hbm_read(buf, sink, stream=None):
+    """Read a device buffer once (HBM streaming-read measurement)."""
+    _call("beam_hbm_read", _p(buf), buf.numel() * buf.element_size(), _p(sink), _s(stream))
 
 
 def beam_workspace_size(dims, op, T, max_ctx=0) -> int:

@@ -534,6 +534,16 @@ size_t beam_workspace_size(const beam_dims* dims, int op, int T, int max_ctx) {
   }
 }
 
+int beam_hbm_read(const void* p, size_t bytes, unsigned* sink, void* stream) {
+  REQ(p);
+  REQ(sink);
+  ALN(p);
+  SHAPE(bytes % 16 == 0, "%s: bytes must be a multiple of 16", __func__);
+  int rc = device_ready();
+  if (rc) return rc;
+  return launched(beam::launch_hbm_read(p, bytes, sink, S_(stream)), __func__);
+}
+
 int beam_rope_table(float* out, int Lmax, int d, double theta) {
   if (!out) return fail(BEAM_E_NULL, "%s: out is NULL", __func__);
   if (Lmax <= 0 || d <= 0 || d % 2 || !(theta > 0))

@@ -80,6 +80,8 @@ int launch_attn_prefill(int T, int Hq, int Hkv, int hd, int swa, int window, int
                         const void* kc, const void* vc, float k_scale, float v_scale, int S,
                         int Lmax, const float* sink, uint16_t* o, hipStream_t st);
 
+int launch_hbm_read(const void* p, size_t bytes, unsigned* sink, hipStream_t st);
+
 // device-side check flags (read and cleared by beam_check)
 int gemv_read_clear_err();
 int qk_read_clear_err();

@@ -20,7 +20,7 @@ MIS = 0x10002        # misaligned
 
 def test_library_exports_every_declared_symbol():
     names = B.header_functions()
-    assert len(names) == 15
+    assert len(names) == 16
     L = ctypes.CDLL(B.LIB_PATH)
     for n in names:
         assert hasattr(L, n), n
@@ -126,6 +126,15 @@ def test_attention_router_moe_validation():
     assert _rc("beam_dense_swiglu", 1, 256, 512, A, A, A, A, A, 1 << 20, None) == -7
     assert _rc("beam_out_gate", by, 1, A, None, A, A, A, None, 0, None) == -1
     assert _rc("beam_out_gate", by, 1, A, A, A, A, A, None, 0, None) == -7
+
+
+@cpu_only
+def test_hbm_read_validation_and_nodev():
+    assert _rc("beam_hbm_read", None, 1024, A, None) == -1
+    assert _rc("beam_hbm_read", A, 1024, None, None) == -1
+    assert _rc("beam_hbm_read", MIS, 1024, A, None) == -4
+    assert _rc("beam_hbm_read", A, 1000, A, None) == -2
+    assert _rc("beam_hbm_read", A, 1024, A, None) == -7
 
 
 def test_workspace_sizes():

@@ -249,8 +249,10 @@ def decode_leg(a, ci):
                                           pos, seq, m, rope, q, g, L.kv, ws_qkv)
         attn(dims, 1, q, pos, seq, L.kv, None, o, pos0, ws_attn)
         B.beam_out_gate(dims, 1, o, g, t["b_gate"], t["w_o"], y)
-        B.beam_boundary_norm_residual(dims, 1, y, t["w_attn_post"], h, t["w_ffn_pre"], x2, n)
-        B.beam_router_fp32_grouped_topk(dims, 1, x2, t["w_r"], t["b_corr"], idx, w, None, ws_r)
+        # attention-side boundary + router in one call (the two calls fused)
+        B.beam_boundary_router_fp32_grouped_topk(dims, 1, y, t["w_attn_post"], h, t["w_ffn_pre"],
+                                                 x2, n, t["w_r"], t["b_corr"], idx, w, None,
+                                                 ws_r)
         B.beam_moe_swiglu_combine(dims, 1, x2, idx, w, t["w13"], t["w2"], None, None, y2,
                                   ws_moe)
         B.beam_boundary_norm_residual(dims, 1, y2, t["w_ffn_post"], h, t["w_next_pre"], x, n + 1)

@@ -197,6 +197,21 @@ int beam_router_fp32_grouped_topk(const beam_dims* dims, int T, const uint16_t* 
                                   float* w, float* logits, void* ws, size_t ws_bytes,
                                   void* stream);
 
+/* The attention-side boundary followed by the router, as one call:
+ * exactly beam_boundary_norm_residual(dims, T, y, w_post, h, w_pre, x_out, n)
+ * then beam_router_fp32_grouped_topk(dims, T, x_out, w_r, b_corr, idx, w,
+ * logits, ws, ws_bytes) ([MoE]; [Opt]/1 and /4), same results bit for bit.
+ * At T = 1 it runs as one kernel: every router workgroup computes the
+ * boundary row while its expert rows load and uses it as the GEMV input, and
+ * the last workgroup stores h and x_out. Arguments and errors are those of the
+ * two calls; ws as for the router. */
+int beam_boundary_router_fp32_grouped_topk(const beam_dims* dims, int T, const uint16_t* y,
+                                           const uint16_t* w_post, uint16_t* h,
+                                           const uint16_t* w_pre, uint16_t* x_out, int n,
+                                           const float* w_r, const float* b_corr,
+                                           int32_t* idx, float* w, float* logits, void* ws,
+                                           size_t ws_bytes, void* stream);
+
 /* Routed SwiGLU experts and the weighted combine ([MoE]; [Opt]/3 combine):
  *   for each token t and k < topk, e = idx[t][k]:
  *     u = bf16(x_t . w13[e]^T)   w13 [E][2F][D] bf16 (rows 0..F-1 gate, F..2F-1 up)

@@ -21,6 +21,7 @@ __all__ = [
     "BeamError", "beam_dims", "beam_kv", "lib", "dims_from", "kv_struct",
     "beam_boundary_norm_residual", "beam_qk_norm_rope_ssmax_kvwrite", "beam_attn_swa",
     "beam_attn_nope_ssmax", "beam_out_gate", "beam_router_fp32_grouped_topk",
+    "beam_boundary_router_fp32_grouped_topk",
     "beam_moe_swiglu_combine", "beam_moe_experts_up", "beam_moe_experts_down",
     "beam_dense_swiglu", "beam_workspace_size", "beam_rope_table", "beam_hbm_read",
     "beam_check", "beam_last_error", "beam_version",
@@ -79,6 +80,8 @@ def lib():
             "beam_out_gate": [POINTER(beam_dims), c_int, P, P, P, P, P, P, c_size_t, P],
             "beam_router_fp32_grouped_topk": [POINTER(beam_dims), c_int, P, P, P, P, P, P, P,
                                               c_size_t, P],
+            "beam_boundary_router_fp32_grouped_topk": [POINTER(beam_dims), c_int, P, P, P, P, P,
+                                                       c_int, P, P, P, P, P, P, c_size_t, P],
             "beam_moe_swiglu_combine": [POINTER(beam_dims), c_int, P, P, P, P, P, P, P, P, P,
                                         c_size_t, P],
             "beam_moe_experts_up": [POINTER(beam_dims), c_int, P, P, P, P, P, P],
@@ -198,6 +201,15 @@ def beam_router_fp32_grouped_topk(dims, T, x, w_r, b_corr, idx, w, logits=None, 
     wp, wb = _ws(ws)
     _call("beam_router_fp32_grouped_topk", ctypes.byref(d), T, _p(x), _p(w_r), _p(b_corr),
           _p(idx), _p(w), _p(logits), wp, wb, _s(stream))
+
+
+def beam_boundary_router_fp32_grouped_topk(dims, T, y, w_post, h, w_pre, x_out, n, w_r, b_corr,
+                                           idx, w, logits=None, ws=None, stream=None):
+    d = _d(dims)
+    wp, wb = _ws(ws)
+    _call("beam_boundary_router_fp32_grouped_topk", ctypes.byref(d), T, _p(y), _p(w_post), _p(h),
+          _p(w_pre), _p(x_out), n, _p(w_r), _p(b_corr), _p(idx), _p(w), _p(logits), wp, wb,
+          _s(stream))
 
 
 def beam_moe_swiglu_combine(dims, T, x, idx, w, w13, w2, shared_w13, shared_w2, y, ws,

@@ -179,6 +179,30 @@ int attn_impl(const beam_dims* dims, int T, const uint16_t* q, const int32_t* po
                   fn);
 }
 
+// Argument checks of the router (shared by the fused boundary + router call).
+int check_router(const beam_dims* dims, int T, const uint16_t* x, const float* w_r, int32_t* idx,
+                 float* w, float* logits, void* ws, size_t ws_bytes, const char* fn) {
+  if (!dims || !x || !w_r || !idx || !w) return fail(BEAM_E_NULL, "%s: NULL argument", fn);
+  if (misaligned(x) || misaligned(w_r) || misaligned(logits) || misaligned(ws))
+    return fail(BEAM_E_ALIGN, "%s: tensor not 16-byte aligned", fn);
+  if (T <= 0) return fail(BEAM_E_SHAPE, "%s: T <= 0", fn);
+  const int E = dims->E, ng = dims->n_group, tg = dims->topk_group, K = dims->topk;
+  if (!(E > 0 && ng > 0 && tg > 0 && K > 0))
+    return fail(BEAM_E_SHAPE, "%s: non-positive routing size", fn);
+  if (E % ng) return fail(BEAM_E_SHAPE, "%s: E %% n_group != 0", fn);
+  if (tg > ng) return fail(BEAM_E_SHAPE, "%s: topk_group > n_group", fn);
+  if (K > tg * (E / ng)) return fail(BEAM_E_SHAPE, "%s: topk > topk_group * E / n_group", fn);
+  if (K > 32) return fail(BEAM_E_UNSUPPORTED, "%s: topk > 32", fn);
+  if (E > 1024 || ng > 64) return fail(BEAM_E_UNSUPPORTED, "%s: E > 1024 or n_group > 64", fn);
+  if (!(dims->D > 0 && dims->D % 8 == 0))
+    return fail(BEAM_E_UNSUPPORTED, "%s: D must be a positive multiple of 8", fn);
+  if (!ws) return fail(BEAM_E_NULL, "%s: ws is NULL", fn);
+  const size_t need = logits ? kCtl : ws_router(dims, T);
+  if (ws_bytes < need)
+    return fail(BEAM_E_WORKSPACE, "%s: workspace %zu < %zu bytes", fn, ws_bytes, need);
+  return BEAM_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -319,37 +343,45 @@ int beam_out_gate(const beam_dims* dims, int T, const uint16_t* o, const uint16_
                   __func__);
 }
 
+
 int beam_router_fp32_grouped_topk(const beam_dims* dims, int T, const uint16_t* x,
                                   const float* w_r, const float* b_corr, int32_t* idx,
                                   float* w, float* logits, void* ws, size_t ws_bytes,
                                   void* stream) {
-  REQ(dims);
-  REQ(x);
-  REQ(w_r);
-  REQ(idx);
-  REQ(w);
-  ALN(x);
-  ALN(w_r);
-  ALN(logits);
-  ALN(ws);
-  SHAPE(T > 0, "%s: T <= 0", __func__);
-  const int E = dims->E, ng = dims->n_group, tg = dims->topk_group, K = dims->topk;
-  SHAPE(E > 0 && ng > 0 && tg > 0 && K > 0, "%s: non-positive routing size", __func__);
-  SHAPE(E % ng == 0, "%s: E %% n_group != 0", __func__);
-  SHAPE(tg <= ng, "%s: topk_group > n_group", __func__);
-  SHAPE(K <= tg * (E / ng), "%s: topk > topk_group * E / n_group", __func__);
-  UNSUP(K <= 32, "%s: topk > 32", __func__);
-  UNSUP(E <= 1024 && ng <= 64, "%s: E > 1024 or n_group > 64", __func__);
-  UNSUP(dims->D > 0 && dims->D % 8 == 0, "%s: D must be a positive multiple of 8", __func__);
-  REQ(ws);
-  const size_t need = logits ? kCtl : ws_router(dims, T);
-  if (ws_bytes < need)
-    return fail(BEAM_E_WORKSPACE, "%s: workspace %zu < %zu bytes", __func__, ws_bytes, need);
-  float* lg = logits ? logits : (float*)ws_data(ws);
-  int rc = device_ready();
+  int rc = check_router(dims, T, x, w_r, idx, w, logits, ws, ws_bytes, __func__);
   if (rc) return rc;
-  return launched(beam::launch_router(T, E, dims->D, ng, tg, K, dims->route_scale, x, w_r,
-                                      b_corr, lg, idx, w, ws_ctl(ws), S_(stream)),
+  float* lg = logits ? logits : (float*)ws_data(ws);
+  if ((rc = device_ready())) return rc;
+  return launched(beam::launch_router(T, dims->E, dims->D, dims->n_group, dims->topk_group,
+                                      dims->topk, dims->route_scale, x, w_r, b_corr, lg, idx, w,
+                                      ws_ctl(ws), S_(stream)),
+                  __func__);
+}
+
+int beam_boundary_router_fp32_grouped_topk(const beam_dims* dims, int T, const uint16_t* y,
+                                           const uint16_t* w_post, uint16_t* h,
+                                           const uint16_t* w_pre, uint16_t* x_out, int n,
+                                           const float* w_r, const float* b_corr,
+                                           int32_t* idx, float* w, float* logits, void* ws,
+                                           size_t ws_bytes, void* stream) {
+  REQ(dims);
+  REQ(h);
+  REQ(w_pre);
+  ALN(y);
+  ALN(w_post);
+  ALN(h);
+  ALN(w_pre);
+  SHAPE(n >= 0, "%s: n < 0", __func__);
+  UNSUP(dims->D > 0 && dims->D % 8 == 0 && dims->D <= 8192,
+        "%s: D must be a positive multiple of 8 <= 8192", __func__);
+  int rc = check_router(dims, T, x_out, w_r, idx, w, logits, ws, ws_bytes, __func__);
+  if (rc) return rc;
+  float* lg = logits ? logits : (float*)ws_data(ws);
+  if ((rc = device_ready())) return rc;
+  return launched(beam::launch_boundary_router(T, dims->D, y, w_post, h, w_pre, x_out, n,
+                                               dims->eps, dims->E, dims->n_group,
+                                               dims->topk_group, dims->topk, dims->route_scale,
+                                               w_r, b_corr, lg, idx, w, ws_ctl(ws), S_(stream)),
                   __func__);
 }
 

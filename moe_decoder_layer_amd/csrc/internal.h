@@ -49,6 +49,12 @@ int launch_attn_decode(int T, int Hq, int Hkv, int hd, int swa, int window, int 
 int launch_router(int T, int E, int D, int ng, int tg, int K, float route_scale,
                   const uint16_t* X, const float* Wr, const float* bcorr, float* logits,
                   int32_t* idx, float* w, unsigned* ctr, hipStream_t st);
+bool boundary_router_fused(int T, int E, int D);
+int launch_boundary_router(int T, int D, const uint16_t* y, const uint16_t* w_post, uint16_t* h,
+                           const uint16_t* w_pre, uint16_t* x_out, int n, float eps, int E,
+                           int ng, int tg, int K, float route_scale, const float* Wr,
+                           const float* bcorr, float* logits, int32_t* idx, float* w,
+                           unsigned* ctr, hipStream_t st);
 
 // many-token (prefill) path
 constexpr int kGemvMaxT = 4;  // T above this runs on the matrix-core kernels

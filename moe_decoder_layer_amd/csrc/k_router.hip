@@ -14,6 +14,7 @@
 // among the kept groups' best experts. A rank counts the candidates that beat
 // a candidate (larger value, or equal value and lower index), so ties go to
 // the lower index and the experts come out in descending biased-score order.
+#include "boundary_row.h"
 #include "common.h"
 #include "internal.h"
 
@@ -210,6 +211,103 @@ __global__ __launch_bounds__(RT) void router_decode_kernel(
   for (int t = 0; t < T; ++t)
     route_token(logits + (size_t)t * E, bias, E, ng, tg, K, route_scale, idx + (size_t)t * K,
                 wout + (size_t)t * K, s_b, cand_v, cand_i, g1, g2, ssel);
+}
+
+// One token: the attention-side sublayer boundary as the router's prologue.
+// Each workgroup requests its expert rows first, computes the boundary row
+// (new residual h and its pre-norm x) while they arrive, keeps x in LDS as the
+// GEMV input, and the last workgroup to finish (after every workgroup has read
+// the old h) stores h and x and runs the selection. Products and sums follow
+// router_decode_kernel's order, so both paths give identical logits.
+template <int MAXC>
+__global__ __launch_bounds__(RT) void boundary_router_kernel(
+    int D, const uint16_t* __restrict__ y, const uint16_t* __restrict__ w_post, uint16_t* h,
+    const uint16_t* __restrict__ w_pre, uint16_t* __restrict__ x_out, int mode, float c_h,
+    float c_a, float eps, const float* __restrict__ Wr, int E, float* logits,
+    const float* __restrict__ bcorr, int ng, int tg, int K, float route_scale,
+    int32_t* __restrict__ idx, float* __restrict__ wout, unsigned* ctr) {
+  constexpr int CPT = 4;  // D <= RT * CPT * 8
+  extern __shared__ __align__(16) uint16_t xs[];  // the token's pre-normed row
+  __shared__ float red[RT / 64];
+  __shared__ float s_b[RT], cand_v[RT];
+  __shared__ int cand_i[RT];
+  __shared__ float g1[64], g2[64], ssel[32];
+  __shared__ int s_last;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int e = blockIdx.x * 4 + wave;
+  const float* w = Wr + (size_t)min(e, E - 1) * D;
+  const int nc = D >> 2;  // float4 chunks of a row (nc <= 64 * MAXC)
+  f32x4 wv[MAXC];
+#pragma unroll
+  for (int i = 0; i < MAXC; ++i) wv[i] = ld16f_nt(w + (size_t)min(lane + 64 * i, nc - 1) * 4);
+  const float bias = (bcorr && (int)threadIdx.x < E) ? bcorr[threadIdx.x] : 0.f;
+
+  BoundaryRow<RT, CPT> br;
+  br.load(D, y, w_post, h, w_pre, mode);
+  uint4 hn[CPT], xo[CPT];
+  br.compute(D, mode, c_h, c_a, eps, red, hn, xo);
+  const int nc8 = D >> 3;
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) {
+    const int c = threadIdx.x + i * RT;
+    if (c < nc8) *reinterpret_cast<uint4*>(xs + c * 8) = xo[i];
+  }
+  __syncthreads();
+  float a = 0.f;
+#pragma unroll
+  for (int i = 0; i < MAXC; ++i) {
+    const int c = lane + 64 * i;
+    if (c < nc) {
+      const uint2 xv = *reinterpret_cast<const uint2*>(xs + c * 4);
+      a = __builtin_fmaf(bf_lo(xv.x), wv[i][0], a);
+      a = __builtin_fmaf(bf_hi(xv.x), wv[i][1], a);
+      a = __builtin_fmaf(bf_lo(xv.y), wv[i][2], a);
+      a = __builtin_fmaf(bf_hi(xv.y), wv[i][3], a);
+    }
+  }
+  const float v = wave_sum(a);
+  if (lane == 0 && e < E) st_dev(logits + e, v);
+  if (!last_arrival(ctr, gridDim.x, &s_last)) return;
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) {
+    const int c = threadIdx.x + i * RT;
+    if (c < nc8) {
+      if (mode != 0) *reinterpret_cast<uint4*>(h + c * 8) = hn[i];
+      *reinterpret_cast<uint4*>(x_out + c * 8) = xo[i];
+    }
+  }
+  route_token(logits, bias, E, ng, tg, K, route_scale, idx, wout, s_b, cand_v, cand_i, g1, g2,
+              ssel);
+}
+
+bool boundary_router_fused(int T, int E, int D) {
+  return T == 1 && E <= RT && D % 8 == 0 && D <= 20 * 64 * 4 && D <= RT * 4 * 8;
+}
+
+int launch_boundary_router(int T, int D, const uint16_t* y, const uint16_t* w_post, uint16_t* h,
+                           const uint16_t* w_pre, uint16_t* x_out, int n, float eps, int E,
+                           int ng, int tg, int K, float route_scale, const float* Wr,
+                           const float* bcorr, float* logits, int32_t* idx, float* w,
+                           unsigned* ctr, hipStream_t st) {
+  if (!boundary_router_fused(T, E, D)) {
+    if (launch_boundary(T, D, y, w_post, h, w_pre, x_out, n, eps, st)) return -1;
+    return launch_router(T, E, D, ng, tg, K, route_scale, x_out, Wr, bcorr, logits, idx, w, ctr,
+                         st);
+  }
+  const int mode = (y == nullptr) ? 0 : (w_post != nullptr ? 1 : 2);
+  float c_h, c_a;
+  boundary_coefs(mode == 0 ? 0 : n, &c_h, &c_a);
+  const dim3 grid((E + 3) / 4);
+  const size_t sh = (size_t)D * 2;
+  if (D <= 8 * 64 * 4)
+    hipLaunchKernelGGL((boundary_router_kernel<8>), grid, dim3(RT), sh, st, D, y, w_post, h,
+                       w_pre, x_out, mode, c_h, c_a, eps, Wr, E, logits, bcorr, ng, tg, K,
+                       route_scale, idx, w, ctr);
+  else
+    hipLaunchKernelGGL((boundary_router_kernel<20>), grid, dim3(RT), sh, st, D, y, w_post, h,
+                       w_pre, x_out, mode, c_h, c_a, eps, Wr, E, logits, bcorr, ng, tg, K,
+                       route_scale, idx, w, ctr);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
 int launch_router(int T, int E, int D, int ng, int tg, int K, float route_scale,

@@ -270,6 +270,40 @@ def test_router(base, T):
     assert torch.equal(idx, idx2) and torch.equal(w, w2)
 
 
+@pytest.mark.parametrize("base,T", [(CFG0, 1), (BEAM, 1), (BEAM, 3)])
+def test_boundary_router_fused_equals_calls(base, T):
+    """The fused boundary + router call gives the two calls' results bit for
+    bit (T = 1 runs as one kernel), also when repeated on one workspace."""
+    dims = base
+    P = Params(dims, 0, 5, moe=False)
+    y = dev(synth.make_h((T, dims.D), 8, "fy", T))
+    h0 = synth.make_h((T, dims.D), 9, "fh", T)
+    n = 21
+
+    def outs():
+        return (torch.empty((T, dims.topk), dtype=torch.int32, device="cuda"),
+                torch.empty((T, dims.topk), dtype=torch.float32, device="cuda"),
+                torch.empty((T, dims.E), dtype=torch.float32, device="cuda"),
+                torch.empty((T, dims.D), **I16))
+    h1 = dev(h0)
+    i1, w1, l1, x1 = outs()
+    B.beam_boundary_norm_residual(dims, T, y, P.t["w_attn_post"], h1, P.t["w_ffn_pre"], x1, n)
+    B.beam_router_fp32_grouped_topk(dims, T, x1, P.t["w_r"], P.t["b_corr"], i1, w1, l1,
+                                    ws(dims, B.BEAM_OP_ROUTER, T))
+    wsf = ws(dims, B.BEAM_OP_ROUTER, T)
+    for _ in range(2):
+        h2 = dev(h0)
+        i2, w2, l2, x2 = outs()
+        B.beam_boundary_router_fp32_grouped_topk(dims, T, y, P.t["w_attn_post"], h2,
+                                                 P.t["w_ffn_pre"], x2, n, P.t["w_r"],
+                                                 P.t["b_corr"], i2, w2, l2, wsf)
+        B.beam_check()
+        for a, b, name in ((h1, h2, "h"), (x1, x2, "x"), (i1, i2, "idx"), (w1, w2, "w"),
+                           (l1, l2, "logits")):
+            assert torch.equal(a, b), name
+        assert int(wsf[:1024].count_nonzero()) == 0
+
+
 # ------------------------------------------------------------------ experts
 _BEAM_P = {}
 

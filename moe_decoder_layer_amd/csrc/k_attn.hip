@@ -37,8 +37,33 @@ BEAM_ERR_FLAG_READER(attn)
 // waves so no wave walks more than ceil(tiles / NW) of them. With ctr set, the
 // last workgroup of each (token, kv head) to finish merges its chunks and
 // writes o_direct (ctr[t * Hkv + j] counts arrivals and is left at zero).
+// Lane group g holds, in k-step i of the score product, the 8 dims from
+// qk_dim(i, g) on (the same for the query and the key operand). With these
+// runs, one 16-byte load per lane covers 64 contiguous bytes of each of 16 key
+// rows across the four lane groups.
+template <int HD, bool FP8>
+__device__ __forceinline__ constexpr int qk_dim(int i, int g) {
+  if constexpr (FP8) return HD >= 64 ? (i >> 1) * 64 + g * 16 + (i & 1) * 8 : g * 8;
+  return i * 32 + g * 8;
+}
+
+// Key, within a 64-key tile, of score slot 4 q4 + r of block st. Lane group g
+// then holds the probabilities of keys half_key(kh, g) + [0, 8) for kh = 0, 1,
+// i.e. exactly its B operand of the two P.V steps, and the matching V^T runs
+// are contiguous across the lane groups (16 keys per lane for fp8: one
+// 16-byte load; 8 keys per half for bf16).
+template <bool FP8>
+__device__ __forceinline__ constexpr int slot_key(int st, int q4, int r) {
+  return FP8 ? 16 * q4 + 8 * (st >> 1) + 4 * (st & 1) + r
+             : 32 * (st >> 1) + 8 * q4 + 4 * (st & 1) + r;
+}
+template <bool FP8>
+__device__ __forceinline__ constexpr int half_key(int kh, int g) {
+  return FP8 ? 16 * g + 8 * kh : 32 * kh + 8 * g;
+}
+
 template <int HD, bool FP8, bool SWA, int NW, int GS>
-__global__ __launch_bounds__(NW * 64) void attn_decode_partial_kernel(
+__device__ __forceinline__ void attn_decode_body(
     const uint16_t* __restrict__ q, const int32_t* __restrict__ pos,
     const int32_t* __restrict__ seq, const void* __restrict__ kc, const void* __restrict__ vc,
     int S, int Lmax, int Hq, int Hkv, int window, int tpw, float score_scale, int nch_stride,
@@ -46,7 +71,6 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_partial_kernel(
     float v_scale, unsigned* ctr) {
   constexpr int KS = HD / 32;  // k-steps of the score product
   constexpr int DT = HD / 16;  // 16-dim tiles of the output
-  constexpr int GD = HD / 4;   // dims each lane group covers in the score product
   __shared__ float sm_m[NW][16], sm_l[NW][16];
   __shared__ float sm_o[NW][GS][HD + 4];
   __shared__ int s_last;
@@ -59,9 +83,9 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_partial_kernel(
   // the query fragments do not depend on the position: request them first
   bf16x8 qf[KS];
   if (col < grp) {
-    const uint16_t* qp = q + ((size_t)t * Hq + j * grp + col) * HD + g * GD;
+    const uint16_t* qp = q + ((size_t)t * Hq + j * grp + col) * HD;
 #pragma unroll
-    for (int i = 0; i < KS; ++i) qf[i] = as_bf16x8(ld16(qp + i * 8));
+    for (int i = 0; i < KS; ++i) qf[i] = as_bf16x8(ld16(qp + qk_dim<HD, FP8>(i, g)));
   } else {
 #pragma unroll
     for (int i = 0; i < KS; ++i) qf[i] = bf16x8{};
@@ -93,42 +117,40 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_partial_kernel(
   for (int it = 0; it < tpw; ++it) {
     const int kb = (tile0 + (rr ? it * NW : it)) << 6;
     if (kb > p) break;
-    // The tile's K and V fragments are all requested before any is used.
-    // Score block st = 2 kh + b takes, in key slot s, the key
-    // 16 (s / 4) + 8 kh + 4 b + s % 4 of the tile, so that lane (col, g) ends
-    // up holding the probabilities of keys 16 g + [0, 16) (those of half kh at
-    // 16 g + 8 kh + [0, 8)): one contiguous run of V^T per lane and output tile
-    // (32 bytes bf16, 16 bytes fp8).
-    bf16x8 kf[4][KS];
+    // The tile's K and V fragments are all requested before any is used (key
+    // slots permuted by slot_key, dims by qk_dim). Fragments stay in their
+    // stored form (fp8 codes: half the registers) until the product that uses
+    // them.
+    constexpr int KR = FP8 ? (KS + 1) / 2 : KS;  // 16-byte K loads per slot
+    uint4 kraw[4][KR];
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
-      const int key = kb + 16 * (col >> 2) + 8 * (st >> 1) + 4 * (st & 1) + (col & 3);
-      const size_t kr = (krow0 + key) * HD + g * GD;
-      if constexpr (FP8 && KS >= 2) {  // GD = HD / 4 bytes of the row, in 16-byte loads
+      const int key = kb + slot_key<FP8>(st, col >> 2, col & 3);
+      const size_t kr = (krow0 + key) * HD;
+      if constexpr (FP8 && KS >= 2) {  // steps 2h, 2h+1 share one 16-byte load
 #pragma unroll
-        for (int i = 0; i < KS; i += 2) {
-          const uint4 w = ld16((const uint8_t*)kc + kr + i * 8);
-          kf[st][i] = e4m3x8_to_bf16x8(uint2{w.x, w.y});
-          kf[st][i + 1] = e4m3x8_to_bf16x8(uint2{w.z, w.w});
-        }
+        for (int i = 0; i < KR; ++i)
+          kraw[st][i] = ld16((const uint8_t*)kc + kr + qk_dim<HD, FP8>(2 * i, g));
       } else if constexpr (FP8) {
-        kf[st][0] = e4m3x8_to_bf16x8(*reinterpret_cast<const uint2*>((const uint8_t*)kc + kr));
+        const uint2 w =
+            *reinterpret_cast<const uint2*>((const uint8_t*)kc + kr + qk_dim<HD, FP8>(0, g));
+        kraw[st][0] = uint4{w.x, w.y, 0u, 0u};
       } else {
 #pragma unroll
-        for (int i = 0; i < KS; ++i) kf[st][i] = as_bf16x8(ld16((const uint16_t*)kc + kr + i * 8));
+        for (int i = 0; i < KS; ++i)
+          kraw[st][i] = ld16((const uint16_t*)kc + kr + qk_dim<HD, FP8>(i, g));
       }
     }
-    bf16x8 vfr[2][DT];
+    constexpr int VR = FP8 ? 1 : 2;  // 16-byte V loads per output tile
+    uint4 vraw[DT][VR];
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
-      const size_t vr = (vrow0 + dt * 16 + col) * (size_t)Lmax + kb + 16 * g;
+      const size_t vr = (vrow0 + dt * 16 + col) * (size_t)Lmax + kb;
       if constexpr (FP8) {
-        const uint4 w = ld16((const uint8_t*)vc + vr);
-        vfr[0][dt] = e4m3x8_to_bf16x8(uint2{w.x, w.y});
-        vfr[1][dt] = e4m3x8_to_bf16x8(uint2{w.z, w.w});
+        vraw[dt][0] = ld16((const uint8_t*)vc + vr + half_key<FP8>(0, g));
       } else {
-        vfr[0][dt] = as_bf16x8(ld16((const uint16_t*)vc + vr));
-        vfr[1][dt] = as_bf16x8(ld16((const uint16_t*)vc + vr + 8));
+        vraw[dt][0] = ld16((const uint16_t*)vc + vr + half_key<FP8>(0, g));
+        vraw[dt][1] = ld16((const uint16_t*)vc + vr + half_key<FP8>(1, g));
       }
     }
     f32x4 sacc[4];
@@ -136,8 +158,16 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_partial_kernel(
     for (int st = 0; st < 4; ++st) {
       sacc[st] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int i = 0; i < KS; ++i)
-        sacc[st] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[st][i], qf[i], sacc[st], 0, 0, 0);
+      for (int i = 0; i < KS; ++i) {
+        bf16x8 kf;
+        if constexpr (FP8) {
+          const uint4 w = kraw[st][i >> 1];
+          kf = e4m3x8_to_bf16x8((i & 1) ? uint2{w.z, w.w} : uint2{w.x, w.y});
+        } else {
+          kf = as_bf16x8(kraw[st][i]);
+        }
+        sacc[st] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[i], sacc[st], 0, 0, 0);
+      }
     }
     // scores (log2 domain), window mask, online softmax
     float mx = -INFINITY;
@@ -145,7 +175,7 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_partial_kernel(
     for (int st = 0; st < 4; ++st)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int key = kb + 16 * g + 8 * (st >> 1) + 4 * (st & 1) + r;
+        const int key = kb + slot_key<FP8>(st, g, r);
         float v = sacc[st][r] * score_scale;
         v = (key < lo || key > p) ? -INFINITY : v;
         sacc[st][r] = v;
@@ -183,10 +213,16 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_partial_kernel(
         pf[i] = (__bf16)pv;
         pl[i] = (__bf16)(pv - (float)pf[i]);
       }
-      const int key0 = kb + 16 * g + 8 * kh;  // this lane's keys key0 + [0, 8)
+      const int key0 = kb + half_key<FP8>(kh, g);  // this lane's keys key0 + [0, 8)
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
-        bf16x8 vf = vfr[kh][dt];
+        bf16x8 vf;
+        if constexpr (FP8) {
+          const uint4 w = vraw[dt][0];
+          vf = e4m3x8_to_bf16x8(kh ? uint2{w.z, w.w} : uint2{w.x, w.y});
+        } else {
+          vf = as_bf16x8(vraw[dt][kh]);
+        }
         if (edge) {  // keys outside [lo, p] may hold anything: zero them
 #pragma unroll
           for (int i = 0; i < 8; ++i)
@@ -282,6 +318,29 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_partial_kernel(
       if (d < HD) o_direct[((size_t)t * Hq + j * grp + hh) * HD + d] = f2bf(O[k] * inv);
     }
   }
+}
+
+#define ATTN_DECODE_PARAMS                                                                    \
+  const uint16_t *__restrict__ q, const int32_t *__restrict__ pos,                          \
+      const int32_t *__restrict__ seq, const void *__restrict__ kc,                         \
+      const void *__restrict__ vc, int S, int Lmax, int Hq, int Hkv, int window, int tpw,   \
+      float score_scale, int nch_stride, float *part, uint16_t *__restrict__ o_direct,      \
+      const float *__restrict__ sink, float v_scale, unsigned *ctr
+#define ATTN_DECODE_ARGS                                                                 \
+  q, pos, seq, kc, vc, S, Lmax, Hq, Hkv, window, tpw, score_scale, nch_stride, part, o_direct, \
+      sink, v_scale, ctr
+
+template <int HD, bool FP8, bool SWA, int NW, int GS>
+__global__ __launch_bounds__(NW * 64) void attn_decode_partial_kernel(ATTN_DECODE_PARAMS) {
+  attn_decode_body<HD, FP8, SWA, NW, GS>(ATTN_DECODE_ARGS);
+}
+
+// Long split-K spans over an fp8 cache: the register budget is held to three
+// waves per SIMD (from two), which keeps more of the cache stream in flight.
+template <int HD, bool SWA>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void
+attn_decode_fp8_stream_kernel(ATTN_DECODE_PARAMS) {
+  attn_decode_body<HD, true, SWA, 4, 16>(ATTN_DECODE_ARGS);
 }
 
 // Combine the chunks of one (token, head): o = sum_c 2^(m_c-M) O_c / sum_c 2^(m_c-M) l_c.
@@ -408,29 +467,35 @@ int launch_attn_decode(int T, int Hq, int Hkv, int hd, int swa, int window, int 
                        const void* kc, const void* vc, float k_scale, float v_scale, int S,
                        int Lmax, const float* sink, uint16_t* o, int span, float* part,
                        unsigned* ctr, hipStream_t st) {
+  const float score_scale = k_scale / sqrtf((float)hd) * 1.4426950408889634f;
+  const float vsc = fp8 ? v_scale : 1.0f;
   int tpw, nch;
   attn_plan(T, Hkv, span, &tpw, &nch);
-  const float score_scale = k_scale / sqrtf((float)hd) * 1.4426950408889634f;
   const dim3 grid(nch, Hkv, T);
   const bool fused = attn_fused_merge(T, Hkv, nch);
   uint16_t* od = (nch == 1 || fused) ? o : nullptr;
   unsigned* cp = fused ? ctr : nullptr;
-  const float vsc = fp8 ? v_scale : 1.0f;
+#define ARGS q, pos, seq, kc, vc, S, Lmax, Hq, Hkv, window, tpw, score_scale, nch, part, od, sink, vsc, cp
 #define PART(HD_, F8, SW)                                                                   \
   hipLaunchKernelGGL((attn_decode_partial_kernel<HD_, F8, SW, 4, 16>), grid, dim3(256), 0, \
-                     st, q, pos, seq, kc, vc, S, Lmax, Hq, Hkv, window, tpw, score_scale,   \
-                     nch, part, od, sink, vsc, cp)
-#define BY_MODE(HD_)                                    \
-  if (fp8) {                                           \
-    if (swa) PART(HD_, true, true); else PART(HD_, true, false);   \
-  } else {                                             \
-    if (swa) PART(HD_, false, true); else PART(HD_, false, false); \
+                     st, ARGS)
+#define STREAM(HD_, SW) \
+  hipLaunchKernelGGL((attn_decode_fp8_stream_kernel<HD_, SW>), grid, dim3(256), 0, st, ARGS)
+#define BY_MODE(HD_)                                                   \
+  if (fp8 && !od) {                                                   \
+    if (swa) STREAM(HD_, true); else STREAM(HD_, false);              \
+  } else if (fp8) {                                                   \
+    if (swa) PART(HD_, true, true); else PART(HD_, true, false);      \
+  } else {                                                            \
+    if (swa) PART(HD_, false, true); else PART(HD_, false, false);    \
   }
   if (hd == 128) { BY_MODE(128) }
   else if (hd == 64) { BY_MODE(64) }
   else { BY_MODE(32) }
 #undef BY_MODE
+#undef STREAM
 #undef PART
+#undef ARGS
   if (hipGetLastError() != hipSuccess) return -1;
   if (od) return 0;
   const dim3 mg(Hq, T);

@@ -3,11 +3,10 @@
 // Beam 1.0 on vLLM": Attention section for the maths; optimisation changes 2
 // and 6 for the fusion).
 //
-// One wave per head: lane i < d/2 holds elements i and i + d/2, which are
-// exactly one rotate-half pair, so RoPE needs no lane exchange. The head's
-// RMS statistic is one wave reduction. Input is the bf16 q|k|v projection.
+// One wave per head (qk_head). Input is the bf16 q|k|v projection.
 #include "common.h"
 #include "internal.h"
+#include "qk_head.h"
 
 namespace beam {
 
@@ -31,76 +30,12 @@ __global__ __launch_bounds__(256) void qk_norm_pos_kvwrite_kernel(
   for (int k = 0; k < tpt; ++k) {
   const int t = blockIdx.y + k * tstride;
   if (t >= T) return;
-  const int half = hd >> 1;
-  const bool act = lane < half;
   const int p = pos[t], s = seq[t];
   const bool slot_ok = (p >= 0 && p < Lmax && s >= 0 && s < S);
   if (!slot_ok && head == 0 && lane == 0)
     BEAM_RAISE(qk, (p < 0 || p >= Lmax) ? ERR_POS : ERR_SEQ);
-
-  const uint16_t* src = qkv + (size_t)t * nheads * hd + (size_t)head * hd;
-  float a = act ? bf2f(src[lane]) : 0.f;
-  float b = act ? bf2f(src[lane + half]) : 0.f;
-
-  if (head >= Hq + Hkv) {  // value head: stored as produced (bf16), or quantised
-    if (!slot_ok || !act) continue;
-    const int j = head - Hq - Hkv;
-    const size_t col = (((size_t)s * Hkv + j) * hd) * (size_t)Lmax + p;  // V^T[s][j][dim][p]
-    if (fp8) {
-      uint8_t* v = (uint8_t*)vc;
-      v[col + (size_t)lane * Lmax] = f2e4m3(__fdiv_rn(a, vs));
-      v[col + (size_t)(lane + half) * Lmax] = f2e4m3(__fdiv_rn(b, vs));
-    } else {
-      uint16_t* v = (uint16_t*)vc;
-      v[col + (size_t)lane * Lmax] = src[lane];
-      v[col + (size_t)(lane + half) * Lmax] = src[lane + half];
-    }
-    continue;
-  }
-  const bool is_q = head < Hq;
-  // gains and the RoPE row are requested before the reduction needs `a`, `b`
-  const uint16_t* w = is_q ? wq : wk;
-  const float wa = act ? bf2f(w[lane]) : 0.f, wb = act ? bf2f(w[lane + half]) : 0.f;
-  const bool rot = (mode == 0) && slot_ok && act;
-  const float c = rot ? rope_cs[(size_t)p * hd + lane] : 1.f;
-  const float sn = rot ? rope_cs[(size_t)p * hd + half + lane] : 0.f;
-  const float r = rsqrtf(wave_sum(a * a + b * b) / hd + eps);
-  if (act) {
-    a = a * r * wa;
-    b = b * r * wb;
-    if (mode == 0) {  // RoPE at position p (table row p: cos then sin)
-      if (slot_ok) {
-        const float a2 = a * c - b * sn;
-        const float b2 = b * c + a * sn;
-        a = a2;
-        b = b2;
-      }
-    } else if (is_q) {  // SSMax: (1 + p/2048)^0.1 with the 1-based position p+1
-      const float sc = __powf(1.0f + (float)(p + 1) * (1.0f / 2048.0f), 0.1f);
-      a *= sc;
-      b *= sc;
-    }
-  }
-  if (is_q) {
-    if (act) {
-      uint16_t* qo = q_out + ((size_t)t * Hq + head) * hd;
-      qo[lane] = f2bf(a);
-      qo[lane + half] = f2bf(b);
-    }
-    continue;
-  }
-  if (!slot_ok || !act) continue;
-  const int j = head - Hq;
-  const size_t row = (((size_t)s * Hkv + j) * Lmax + p) * hd;  // K[s][j][p][:]
-  if (fp8) {
-    uint8_t* k = (uint8_t*)kc;
-    k[row + lane] = f2e4m3(__fdiv_rn(a, ks));
-    k[row + lane + half] = f2e4m3(__fdiv_rn(b, ks));
-  } else {
-    uint16_t* k = (uint16_t*)kc;
-    k[row + lane] = f2bf(a);
-    k[row + lane + half] = f2bf(b);
-  }
+  qk_head(qkv + (size_t)t * nheads * hd + (size_t)head * hd, head, Hq, Hkv, hd, wq, wk, p, s,
+          slot_ok, mode, rope_cs, q_out + (size_t)t * Hq * hd, kc, vc, fp8, ks, vs, Lmax, eps);
   }
 }
 

@@ -103,6 +103,31 @@ def test_qk_norm_kvwrite(base, T, pos0, mode, kv):
     assert np.all(K.view(np.uint16 if kv == "bf16" else np.uint8)[mask] == fill)
 
 
+@pytest.mark.parametrize("base,T", [(BEAM, 1), (CFG0, 3)])
+def test_qk_slot_outside_cache_is_flagged(base, T):
+    """A position at Lmax (or a slot index at S) skips that token's cache write
+    and raises the device flag; the other tokens are written as usual."""
+    dims = base
+    Lmax = 128
+    P = Params(dims, 0, 3, moe=False)
+    x = synth.make_h((T, dims.D), 2, "qbad", T)
+    cache = Cache(dims, 2, Lmax, "bf16", 1.0, 1.0)
+    rope = rope_table(Lmax, dims.d, dims.theta)
+    for pos, seq, msg in ((np.full(T, Lmax, np.int32), np.zeros(T, np.int32), "position"),
+                          (np.arange(T, dtype=np.int32), np.full(T, 2, np.int32), "sequence")):
+        q = torch.empty((T, dims.Hq, dims.d), **I16)
+        g = torch.empty((T, dims.G), **I16)
+        B.beam_qk_norm_rope_ssmax_kvwrite(
+            dims, T, dev(x), P.t["w_qkvg"], P.t["w_qnorm"], P.t["w_knorm"], dev(pos), dev(seq),
+            B.BEAM_SWA_ROPE, rope, q, g, cache.struct(), ws(dims, B.BEAM_OP_QKV, T))
+        with pytest.raises(B.BeamError) as e:
+            B.beam_check()
+        assert e.value.code == -8 and msg in str(e.value)
+        B.beam_check()                  # flag cleared
+    assert np.all(cache.K.cpu().numpy().view(np.uint16) == 0x7FC0)
+    assert np.all(cache.V.cpu().numpy().view(np.uint16) == 0x7FC0)
+
+
 def _bits(v):
     from oracle.numerics import f64_to_bf16_bits
     return f64_to_bf16_bits(v)
@@ -132,12 +157,28 @@ def _needle_cache(dims, Lmax, fill, kv, q, pos, seq, needles, seed):
 
 
 @pytest.mark.parametrize("case", ["tiny", "tiny_few", "beam_multi", "beam_few", "beam_long",
-                                  "beam_chunk"])
+                                  "beam_chunk", "beam_mid", "beam_mid2", "group16_short",
+                                  "group16"])
 @pytest.mark.parametrize("mode", ["swa", "nope"])
 @pytest.mark.parametrize("kv", ["bf16", "fp8"])
 def test_attention(case, mode, kv):
-    """Few tokens (<= 4) take the split-K kernel, more take the flash kernel."""
-    if case == "tiny":
+    """Few tokens (<= 4) take the split-K decode kernel: one chunk normalises
+    in place (tiny_few, group16_short), up to 8 chunks merge in their last
+    workgroup (SWA windows, beam_mid*), more in the merge kernel (beam_long,
+    NoPE beam_few and group16); more tokens take the flash kernel."""
+    if case == "beam_mid":
+        dims, Lmax, fill = BEAM, 4096, 3000
+        pos = np.array([1500], np.int32)
+    elif case == "beam_mid2":
+        dims, Lmax, fill = BEAM, 4096, 3000
+        pos = np.array([1200, 1900], np.int32)
+    elif case == "group16_short":  # GQA group of 16, one chunk
+        dims, Lmax, fill = _dims(BEAM, Hq=32, Hkv=2, G=0), 1024, 256
+        pos = np.array([5, 200], np.int32)
+    elif case == "group16":
+        dims, Lmax, fill = _dims(BEAM, Hq=32, Hkv=2, G=0), 4096, 3000
+        pos = np.array([64, 700, 2999], np.int32)
+    elif case == "tiny":
         dims, Lmax, fill = CFG0, 192, 128
         pos = np.array([0, 15, 16, 63, 64, 100, 127], np.int32)
     elif case == "tiny_few":
@@ -203,7 +244,7 @@ def test_workspace_counters_reused(mode):
     counters at the head of the workspace: repeated calls on one workspace
     give identical results and leave the counter block zeroed."""
     dims = BEAM
-    pos = np.array([2999], np.int32)
+    pos = np.array([1499], np.int32)  # NoPE: 6 chunks merged by the last
     seq = np.zeros(1, np.int32)
     q = dev(synth.make_h((1, dims.Hq, dims.d), 7, "cq"))
     cache = _needle_cache(dims, 4096, 3000, "bf16", q, pos, seq, lambda p: [], 5)
@@ -213,12 +254,12 @@ def test_workspace_counters_reused(mode):
     outs = []
     for _ in range(3):
         o = torch.empty((1, dims.Hq, dims.d), **I16)
-        fn(dims, 1, q, dev(pos), dev(seq), cache.struct(), None, o, 2999, w)
+        fn(dims, 1, q, dev(pos), dev(seq), cache.struct(), None, o, 1499, w)
         B.beam_check()
         assert int(w[:1024].count_nonzero()) == 0
         outs.append(o)
     assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])
-    ref = L.attention(dims, bits_f64(host_bits(q)), pos, seq, cache.oracle(3000), mode)
+    ref = L.attention(dims, bits_f64(host_bits(q)), pos, seq, cache.oracle(1500), mode)
     assert_rms_close(bits_f64(host_bits(outs[0])), ref, "o")
     # the router shares the workspace (same stream): same counters, same result
     P = Params(dims, 0, 5, moe=False)

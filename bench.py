@@ -42,6 +42,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-nope", action="store_true", help="skip the NoPE fp8 decode leg")
+    ap.add_argument("--no-flint", action="store_true",
+                    help="skip the second model's batch-128 decode legs")
     ap.add_argument("--prefill-reps", type=int, default=3)
     ap.add_argument("--cpu-steps", type=int, default=3)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -190,6 +192,9 @@ def main():
             nope.pop(k)
         out["decode_nope"] = nope
         torch.cuda.empty_cache()
+    if not a.no_flint:
+        out["decode_flint_b128"] = {m: flint_leg(a, m) for m in ("swa", "nope")}
+        torch.cuda.empty_cache()
     if not a.no_prefill:
         out["prefill"] = prefill_leg(a)
     if not a.no_cpu_baseline:
@@ -318,6 +323,147 @@ def decode_leg(a, ci):
            "hbm_frac": round(step_bytes / (us_step * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
            "_sets": sets, "_dims": dims, "_ex": ex, "_x2": x2, "_idx": idx}
     return res
+
+
+class FlintSet:
+    """The second model's layer (pre-norm, sinks, no gate, top-6 + shared
+    expert) with a batch of S sequences' bf16 caches, random-init, seeded."""
+
+    def __init__(self, dims, seed, layer, S, ctx, Lmax):
+        import numpy as np
+        import torch
+
+        import moe_decoder_layer_amd as B
+        import synth
+        dev = lambda a: torch.from_numpy(np.ascontiguousarray(  # noqa: E731
+            a.view(np.int16) if a.dtype == np.uint16 else a)).cuda()
+        p = synth.make_params(dims, seed, layer, experts=False, projections=False)
+        self.t = {k: dev(v) for k, v in p.items()}
+        nb = lambda shape, *key: synth.torch_normal_bf16(shape, 0.02, seed, layer, *key)  # noqa
+        self.t["w_qkvg"] = nb((dims.qkvg_rows, dims.D), "w_qkvg")
+        self.t["w_o"] = nb((dims.D, dims.Hq * dims.d), "w_o")
+        w13 = torch.empty((dims.E, 2 * dims.F, dims.D), dtype=torch.int16, device="cuda")
+        w2 = torch.empty((dims.E, dims.D, dims.F), dtype=torch.int16, device="cuda")
+        for e in range(dims.E):
+            synth.torch_normal_bf16((2 * dims.F, dims.D), 0.02, seed, layer, "w13", e, out=w13[e])
+            synth.torch_normal_bf16((dims.D, dims.F), 0.02, seed, layer, "w2", e, out=w2[e])
+        self.t["w13"], self.t["w2"] = w13, w2
+        self.t["shared_w13"] = nb((2 * dims.F, dims.D), "w13", "shared")
+        self.t["shared_w2"] = nb((dims.D, dims.F), "w2", "shared")
+        K, V, ks, vs = synth.torch_kv_prior(dims, S, ctx, "bf16", seed, layer)
+        self.K = torch.empty((S, dims.Hkv, Lmax, dims.d), dtype=torch.int16, device="cuda")
+        self.V = torch.empty((S, dims.Hkv, dims.d, Lmax), dtype=torch.int16, device="cuda")
+        self.K[:, :, :ctx] = K
+        self.V[:, :, :, :ctx] = V.transpose(2, 3)
+        del K, V
+        self.kv = B.kv_struct(self.K, self.V, B.BEAM_KV_BF16, ks, vs, S, Lmax)
+
+
+def flint_leg(a, mode):
+    """The second model's layer shape as a batch of decode steps: 128
+    sequences, one new token each at position 8,192 of a bf16 cache (SWA: the
+    last 513 keys; NoPE: all 8,193), pre-norm layer with per-head sinks, no
+    output gate, sigmoid top-6 of 256 experts plus a shared expert. Steps are
+    chained over two alternating weight sets in one HIP graph, as the Beam
+    legs. Bytes per step count each distinct routed expert once (the
+    selected experts of a step are read once whatever number of tokens
+    chose them)."""
+    import numpy as np
+    import torch
+
+    import moe_decoder_layer_amd as B
+    import synth
+    cfg = synth.config(4)
+    dims, ex = cfg.dims, cfg.extra
+    S, ctx, Lmax = ex["B"], ex["ctx"], ex["Lmax"]
+    T, D = S, dims.D
+    layer = 3
+    t0 = time.time()
+    sets = [FlintSet(dims, seed, layer, S, ctx, Lmax) for seed in (0, 1)]
+    log(f"[bench] flint {mode} b{S} decode: weights + caches drawn in {time.time() - t0:.1f}s "
+        f"({torch.cuda.memory_allocated() / 2**30:.1f} GiB)")
+    I16 = dict(dtype=torch.int16, device="cuda")
+    h = synth.torch_normal_bf16((T, D), 1.0, 0, "bench_flint_h")
+    x = torch.empty((T, D), **I16)
+    q = torch.empty((T, dims.Hq, dims.d), **I16)
+    o = torch.empty((T, dims.Hq, dims.d), **I16)
+    y = torch.empty((T, D), **I16)
+    x2 = torch.empty((T, D), **I16)
+    y2 = torch.empty((T, D), **I16)
+    idx = torch.empty((T, dims.topk), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, dims.topk), dtype=torch.float32, device="cuda")
+    pos = torch.full((T,), ctx, dtype=torch.int32, device="cuda")
+    seq = torch.arange(T, dtype=torch.int32, device="cuda")
+    rope = None
+    if mode == "swa":
+        rope_h = np.zeros((Lmax, dims.d), np.float32)
+        B.beam_rope_table(rope_h, Lmax, dims.d, dims.theta)
+        rope = torch.from_numpy(rope_h).cuda()
+    attn_op = B.BEAM_OP_ATTN_SWA if mode == "swa" else B.BEAM_OP_ATTN_NOPE
+    attn = B.beam_attn_swa if mode == "swa" else B.beam_attn_nope_ssmax
+    m = B.BEAM_SWA_ROPE if mode == "swa" else B.BEAM_NOPE_SSMAX
+    wsz = lambda op, ctx_=0: torch.zeros(max(256, B.beam_workspace_size(dims, op, T, ctx_)),  # noqa
+                                         dtype=torch.uint8, device="cuda")
+    ws_qkv, ws_attn, ws_og = wsz(B.BEAM_OP_QKV), wsz(attn_op, ctx + 1), wsz(B.BEAM_OP_OUT_GATE)
+    ws_r, ws_moe = wsz(B.BEAM_OP_ROUTER), wsz(B.BEAM_OP_MOE)
+
+    def step(L: FlintSet):
+        t = L.t
+        B.beam_qk_norm_rope_ssmax_kvwrite(dims, T, x, t["w_qkvg"], t["w_qnorm"], t["w_knorm"],
+                                          pos, seq, m, rope, q, None, L.kv, ws_qkv)
+        attn(dims, T, q, pos, seq, L.kv, t["sink"], o, ctx, ws_attn)
+        B.beam_out_gate(dims, T, o, None, None, t["w_o"], y, ws_og)
+        B.beam_boundary_norm_residual(dims, T, y, None, h, t["w_ffn_pre"], x2, 0)
+        B.beam_router_fp32_grouped_topk(dims, T, x2, t["w_r"], t["b_corr"], idx, w, None, ws_r)
+        B.beam_moe_swiglu_combine(dims, T, x2, idx, w, t["w13"], t["w2"], t["shared_w13"],
+                                  t["shared_w2"], y2, ws_moe)
+        B.beam_boundary_norm_residual(dims, T, y2, None, h, t["w_next_pre"], x, 0)
+
+    B.beam_boundary_norm_residual(dims, T, None, None, h, sets[0].t["w_attn_pre"], x, 0)
+    distinct = []
+    for i in range(a.chain):
+        step(sets[i % 2])
+        distinct.append(len(np.unique(idx.cpu().numpy())))
+    B.beam_check()
+    assert torch.isfinite(h.view(torch.bfloat16).float()).all(), "non-finite residual stream"
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(graph, stream=stream):
+            for i in range(a.chain):
+                step(sets[i % 2])
+    torch.cuda.current_stream().wait_stream(stream)
+    torch.cuda.synchronize()
+    reps = max(1, min(a.steps, 80) // a.chain)
+    for _ in range(2):
+        graph.replay()
+    torch.cuda.synchronize()
+    s = torch.cuda.current_stream()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    evs[0].record(s)
+    for r in range(reps):
+        graph.replay()
+        evs[r + 1].record(s)
+    torch.cuda.synchronize()
+    B.beam_check()
+    steps = reps * a.chain
+    per = np.array([evs[r].elapsed_time(evs[r + 1]) for r in range(reps)]) * 1000.0 / a.chain
+    us_step = evs[0].elapsed_time(evs[-1]) * 1000.0 / steps
+    ne = float(np.mean(distinct))
+    keys = (dims.window if mode == "swa" else ctx + 1)
+    kv_bytes = T * keys * dims.Hkv * dims.d * 2 * 2
+    step_bytes = int(dims.qkvg_rows * D * 2 + D * dims.Hq * dims.d * 2 + dims.E * D * 4
+                     + (ne + 1) * 3 * dims.F * D * 2 + kv_bytes + T * dims.Hkv * dims.d * 4)
+    log(f"[bench] flint {mode} b{S} decode: {us_step:.2f} us/step (median {np.median(per):.2f}), "
+        f"{ne:.1f} distinct experts/step, {step_bytes / (us_step * 1e-6) / 1e9:.0f} GB/s")
+    del graph, sets
+    return {"workload": f"flint_{mode}_moe_layer_decode_b{S}", "batch": S, "context": ctx,
+            "kv_cache": "bf16", "steps": steps, "us_mean": round(us_step, 3),
+            "us_median": round(float(np.median(per)), 3),
+            "tokens_per_s": round(T / (us_step * 1e-6), 1),
+            "distinct_experts_per_step": round(ne, 1), "bytes_per_step": step_bytes,
+            "hbm_frac": round(step_bytes / (us_step * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
 
 
 def hbm_read_ceiling():

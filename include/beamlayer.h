@@ -159,6 +159,10 @@ int beam_qk_norm_rope_ssmax_kvwrite(const beam_dims* dims, int T, const uint16_t
  * denominator only. max_pos >= max(pos) (host value used to size the grid).
  * ws >= beam_workspace_size(ATTN_SWA, T, max_pos + 1) (counter block and
  * split-K partials).
+ * Kernels: calls of T <= 4 tokens, and of T <= 256 tokens with T <= 4 * kv->S
+ * (a batch of decode steps over many sequences), run split-K per token; other
+ * calls (prefill chunks) run a flash kernel that shares each key tile among
+ * the tokens of a sequence. Both compute the same function.
  * Errors: window <= 0, max_pos >= Lmax. */
 int beam_attn_swa(const beam_dims* dims, int T, const uint16_t* q, const int32_t* pos,
                   const int32_t* seq, const beam_kv* kv, const float* sink, uint16_t* o,
@@ -189,9 +193,12 @@ int beam_out_gate(const beam_dims* dims, int T, const uint16_t* o, const uint16_
  *   w = route_scale * s / sum(s) over the picked experts.
  * Ties go to the lower index; idx [T][topk] int32 ordered by s' descending,
  * w [T][topk] fp32, logits [T][E] fp32 (optional output).
- * ws >= beam_workspace_size(ROUTER) (1024 bytes, the counter block, suffice
- * when logits is given). Errors: E % n_group; topk_group >
- * n_group; topk > topk_group*E/n_group; topk > 32; E > 1024. */
+ * ws >= beam_workspace_size(ROUTER): the counter block, the logits when the
+ * caller passes none, and for T > 4 the partial logits of the K-split GEMM
+ * (when few token tiles split D; T * E * 4 bytes per split, at most D/128
+ * splits). With T <= 4 and logits given, 1024 bytes suffice.
+ * Errors: E % n_group; topk_group > n_group; topk > topk_group*E/n_group;
+ * topk > 32; E > 1024. */
 int beam_router_fp32_grouped_topk(const beam_dims* dims, int T, const uint16_t* x,
                                   const float* w_r, const float* b_corr, int32_t* idx,
                                   float* w, float* logits, void* ws, size_t ws_bytes,

@@ -90,29 +90,58 @@ constexpr size_t kCtl = beam::kCtlBytes;
 char* ws_data(void* ws) { return (char*)ws + kCtl; }
 unsigned* ws_ctl(void* ws) { return (unsigned*)ws; }
 
+size_t ws_qkv_payload(const beam_dims* d, int T) {
+  return align256((size_t)T * (d->Hq + 2 * d->Hkv) * d->d * 2);
+}
 size_t ws_qkv(const beam_dims* d, int T) {
-  return kCtl + align256((size_t)T * (d->Hq + 2 * d->Hkv) * d->d * 2);
+  return kCtl + ws_qkv_payload(d, T) +
+         beam::gemm_split_bytes(T, (d->Hq + 2 * d->Hkv) * d->d + d->G, d->D);
 }
 int attn_span(const beam_dims* d, int swa, int max_ctx) {
   return swa ? std::min(max_ctx, d->window + 63) : max_ctx;
 }
+// Whether an attention call runs the flash kernel (else split-K per token).
+// The workspace bound cannot see the cache's slot count, so it covers the
+// split-K partials for every call of up to kDecodeBatchMaxT tokens.
+bool attn_flash(const beam_dims* d, int T, int S) {
+  if (T <= beam::kGemvMaxT || !beam::attn_prefill_ok(d->Hq / d->Hkv, d->d)) return false;
+  return T > beam::kDecodeBatchMaxT || T > 4 * S;
+}
 size_t ws_attn(const beam_dims* d, int swa, int T, int max_ctx) {
-  if (T > beam::kGemvMaxT && d->Hkv > 0 && beam::attn_prefill_ok(d->Hq / d->Hkv, d->d))
+  if (T > beam::kDecodeBatchMaxT && d->Hkv > 0 && beam::attn_prefill_ok(d->Hq / d->Hkv, d->d))
     return kCtl;  // the many-token kernel needs no partials
   const int nch = beam::attn_nch_bound(T, d->Hkv, attn_span(d, swa, max_ctx));
   if (nch == 1) return kCtl;
   return kCtl + align256((size_t)T * d->Hq * nch * (d->d + 4) * 4);
 }
-size_t ws_out_gate(const beam_dims* d, int T) {
-  return kCtl + align256((size_t)T * d->Hq * d->d * 2);
+size_t ws_out_gate_payload(const beam_dims* d, int T) {
+  return align256((size_t)T * d->Hq * d->d * 2);
 }
-size_t ws_router(const beam_dims* d, int T) { return kCtl + align256((size_t)T * d->E * 4); }
+size_t ws_out_gate(const beam_dims* d, int T) {
+  return kCtl + ws_out_gate_payload(d, T) + beam::gemm_split_bytes(T, d->D, d->Hq * d->d);
+}
+// Router workspace: [counters][logits, when the caller passes none][K-split
+// partial logits of the many-token GEMM, when it splits].
+size_t ws_router_logits(const beam_dims* d, int T, bool own_logits) {
+  return own_logits ? align256((size_t)T * d->E * 4) : 0;
+}
+size_t ws_router(const beam_dims* d, int T, bool own_logits = true) {
+  size_t n = kCtl + ws_router_logits(d, T, own_logits);
+  if (T > 4 && d->E > 0 && d->D > 0) {
+    const int ns = beam::router_splits(T, d->E, d->D);
+    if (ns > 1) n += align256((size_t)ns * T * d->E * 4);
+  }
+  return n;
+}
+float* ws_router_part(const beam_dims* d, int T, bool own_logits, void* ws) {
+  return (float*)(ws_data(ws) + ws_router_logits(d, T, own_logits));
+}
 
 // Many-token MoE workspace, in order: counts[E], seg_off[E+1], tile_off[E+1],
 // perm[P], inv[P] (int32); act[P][F] bf16; out[P][D] fp32; shared expert
 // act_s[T][F] bf16 and out_s[T][D] fp32.
 struct MoeWs {
-  size_t counts, seg_off, tile_off, perm, inv, act, out, act_s, out_s, total;
+  size_t counts, seg_off, tile_off, perm, inv, act, out, act_s, out_s, part, total;
 };
 MoeWs moe_ws_layout(const beam_dims* d, int T) {
   const size_t P = (size_t)T * d->topk, E = d->E;
@@ -127,6 +156,7 @@ MoeWs moe_ws_layout(const beam_dims* d, int T) {
   w.out = o; o += align256(P * d->D * 4);
   w.act_s = o; o += align256((size_t)T * d->F * 2);
   w.out_s = o; o += align256((size_t)T * d->D * 4);
+  w.part = o; o += beam::gemm_split_bytes(T, 2 * d->F, d->D);
   w.total = o;
   return w;
 }
@@ -137,7 +167,10 @@ size_t ws_moe(const beam_dims* d, int T) {
   if (moe_many(d, T)) return kCtl + moe_ws_layout(d, T).total;
   return kCtl + align256((size_t)T * (d->topk + 1) * d->F * 2);
 }
-size_t ws_dense(int T, int Fd) { return kCtl + align256((size_t)T * Fd * 2); }
+size_t ws_dense(int T, int Fd, int D) {
+  return kCtl + align256((size_t)T * Fd * 2) +
+         std::max(beam::gemm_split_bytes(T, 2 * Fd, D), beam::gemm_split_bytes(T, D, Fd));
+}
 
 int attn_impl(const beam_dims* dims, int T, const uint16_t* q, const int32_t* pos,
               const int32_t* seq, const beam_kv* kv, const float* sink, uint16_t* o,
@@ -154,7 +187,7 @@ int attn_impl(const beam_dims* dims, int T, const uint16_t* q, const int32_t* po
   if (max_pos < 0 || max_pos >= kv->Lmax)
     return fail(BEAM_E_SHAPE, "%s: max_pos %d outside [0, Lmax)", fn, max_pos);
   const int fp8 = kv->dtype == BEAM_KV_FP8_E4M3;
-  if (T > beam::kGemvMaxT && beam::attn_prefill_ok(dims->Hq / dims->Hkv, dims->d)) {
+  if (attn_flash(dims, T, kv->S)) {
     if (!ws || ws_bytes < kCtl)
       return fail(ws ? BEAM_E_WORKSPACE : BEAM_E_NULL, "%s: workspace %zu < %zu bytes", fn,
                   ws ? ws_bytes : 0, kCtl);
@@ -197,7 +230,7 @@ int check_router(const beam_dims* dims, int T, const uint16_t* x, const float* w
   if (!(dims->D > 0 && dims->D % 8 == 0))
     return fail(BEAM_E_UNSUPPORTED, "%s: D must be a positive multiple of 8", fn);
   if (!ws) return fail(BEAM_E_NULL, "%s: ws is NULL", fn);
-  const size_t need = logits ? kCtl : ws_router(dims, T);
+  const size_t need = ws_router(dims, T, logits == nullptr);
   if (ws_bytes < need)
     return fail(BEAM_E_WORKSPACE, "%s: workspace %zu < %zu bytes", fn, ws_bytes, need);
   return BEAM_OK;
@@ -272,6 +305,7 @@ int beam_qk_norm_rope_ssmax_kvwrite(const beam_dims* dims, int T, const uint16_t
   const int rcg = (T > beam::kGemvMaxT && dims->D % 64 == 0)
                       ? beam::launch_gemm_bf16(T, Nqkv + dims->G, dims->D, x, dims->D, w_qkvg,
                                                dims->D, qkv, Nqkv, g_out, dims->G, Nqkv,
+                                               (float*)(ws_data(ws) + ws_qkv_payload(dims, T)),
                                                S_(stream))
                       : beam::launch_gemv_qkvg(T, Nqkv + dims->G, dims->D, Nqkv, w_qkvg, x, qkv,
                                                g_out, S_(stream));
@@ -326,6 +360,10 @@ int beam_out_gate(const beam_dims* dims, int T, const uint16_t* o, const uint16_
         return fail(BEAM_E_WORKSPACE, "%s: workspace %zu < %zu bytes", __func__, ws_bytes,
                     ws_out_gate(dims, T));
     }
+    // split-K partials when the workspace holds them (a batch of decode steps)
+    float* part = (ws && ws_bytes >= ws_out_gate(dims, T))
+                      ? (float*)(ws_data(ws) + ws_out_gate_payload(dims, T))
+                      : nullptr;
     if ((rc = device_ready())) return rc;
     if (dims->G) {
       if (beam::launch_gate(T, dims->Hq, dims->d, o, g, b_gate, (uint16_t*)ws_data(ws),
@@ -334,7 +372,7 @@ int beam_out_gate(const beam_dims* dims, int T, const uint16_t* o, const uint16_
       a = (const uint16_t*)ws_data(ws);
     }
     return launched(beam::launch_gemm_bf16(T, dims->D, K, a, K, w_o, K, y, dims->D, nullptr, 0,
-                                           dims->D, S_(stream)),
+                                           dims->D, part, S_(stream)),
                     __func__);
   }
   if ((rc = device_ready())) return rc;
@@ -354,7 +392,8 @@ int beam_router_fp32_grouped_topk(const beam_dims* dims, int T, const uint16_t* 
   if ((rc = device_ready())) return rc;
   return launched(beam::launch_router(T, dims->E, dims->D, dims->n_group, dims->topk_group,
                                       dims->topk, dims->route_scale, x, w_r, b_corr, lg, idx, w,
-                                      ws_ctl(ws), S_(stream)),
+                                      ws_router_part(dims, T, logits == nullptr, ws), ws_ctl(ws),
+                                      S_(stream)),
                   __func__);
 }
 
@@ -381,7 +420,9 @@ int beam_boundary_router_fp32_grouped_topk(const beam_dims* dims, int T, const u
   return launched(beam::launch_boundary_router(T, dims->D, y, w_post, h, w_pre, x_out, n,
                                                dims->eps, dims->E, dims->n_group,
                                                dims->topk_group, dims->topk, dims->route_scale,
-                                               w_r, b_corr, lg, idx, w, ws_ctl(ws), S_(stream)),
+                                               w_r, b_corr, lg, idx, w,
+                                               ws_router_part(dims, T, logits == nullptr, ws),
+                                               ws_ctl(ws), S_(stream)),
                   __func__);
 }
 
@@ -434,7 +475,7 @@ int beam_moe_swiglu_combine(const beam_dims* dims, int T, const uint16_t* x,
     const hipStream_t st = S_(stream);
     if (beam::launch_moe_route(T, K, E, idx, BMr, counts, seg_off, tile_off, perm, inv, st) ||
         beam::launch_gemm_swiglu(T * K, F, D, x, D, perm, w13, seg_off, tile_off, E,
-                                 (long long)2 * F * D, max_tiles, act, st) ||
+                                 (long long)2 * F * D, max_tiles, act, nullptr, st) ||
         beam::launch_gemm_f32(T * K, D, F, act, F, w2, seg_off, tile_off, E, (long long)D * F,
                               max_tiles, out, D, st))
       return launched(-1, __func__);
@@ -443,7 +484,7 @@ int beam_moe_swiglu_combine(const beam_dims* dims, int T, const uint16_t* x,
       uint16_t* act_s = (uint16_t*)(b + L.act_s);
       out_s = (float*)(b + L.out_s);
       if (beam::launch_gemm_swiglu(T, F, D, x, D, nullptr, shared_w13, nullptr, nullptr, 1, 0, 0,
-                                   act_s, st) ||
+                                   act_s, (float*)(b + L.part), st) ||
           beam::launch_gemm_f32(T, D, F, act_s, F, shared_w2, nullptr, nullptr, 1, 0, 0, out_s,
                                 D, st))
         return launched(-1, __func__);
@@ -529,17 +570,18 @@ int beam_dense_swiglu(int T, int D, int Fd, const uint16_t* x, const uint16_t* w
   SHAPE(Fd > 0 && Fd % 64 == 0, "%s: Fd must be a positive multiple of 64", __func__);
   UNSUP(D > 0 && D % 8 == 0 && D <= 8192, "%s: D must be a positive multiple of 8 <= 8192",
         __func__);
-  if (ws_bytes < ws_dense(T, Fd))
+  if (ws_bytes < ws_dense(T, Fd, D))
     return fail(BEAM_E_WORKSPACE, "%s: workspace %zu < %zu bytes", __func__, ws_bytes,
-                ws_dense(T, Fd));
+                ws_dense(T, Fd, D));
   int rc = device_ready();
   if (rc) return rc;
   uint16_t* act = (uint16_t*)ws_data(ws);
   if (T > beam::kGemvMaxT && D % 64 == 0) {
+    float* part = (float*)(ws_data(ws) + align256((size_t)T * Fd * 2));
     if (beam::launch_gemm_swiglu(T, Fd, D, x, D, nullptr, w13, nullptr, nullptr, 1, 0, 0, act,
-                                 S_(stream)))
+                                 part, S_(stream)))
       return launched(-1, __func__);
-    return launched(beam::launch_gemm_bf16(T, D, Fd, act, Fd, w2, Fd, y, D, nullptr, 0, D,
+    return launched(beam::launch_gemm_bf16(T, D, Fd, act, Fd, w2, Fd, y, D, nullptr, 0, D, part,
                                            S_(stream)),
                     __func__);
   }
@@ -561,7 +603,7 @@ size_t beam_workspace_size(const beam_dims* dims, int op, int T, int max_ctx) {
     case BEAM_OP_OUT_GATE: return ws_out_gate(dims, T);
     case BEAM_OP_ROUTER: return ws_router(dims, T);
     case BEAM_OP_MOE: return ws_moe(dims, T);
-    case BEAM_OP_DENSE: return ws_dense(T, dims->F);
+    case BEAM_OP_DENSE: return ws_dense(T, dims->F, dims->D);
     default: return (size_t)-1;
   }
 }

@@ -46,24 +46,36 @@ int launch_attn_decode(int T, int Hq, int Hkv, int hd, int swa, int window, int 
                        int Lmax, const float* sink, uint16_t* o, int span, float* part,
                        unsigned* ctr, hipStream_t st);
 
+// part: K-split partial logits, router_splits(T, E, D) x T x E fp32 (unused
+// and may be null when that is 1).
+int router_splits(int T, int E, int D);
 int launch_router(int T, int E, int D, int ng, int tg, int K, float route_scale,
                   const uint16_t* X, const float* Wr, const float* bcorr, float* logits,
-                  int32_t* idx, float* w, unsigned* ctr, hipStream_t st);
+                  int32_t* idx, float* w, float* part, unsigned* ctr, hipStream_t st);
 bool boundary_router_fused(int T, int E, int D);
 int launch_boundary_router(int T, int D, const uint16_t* y, const uint16_t* w_post, uint16_t* h,
                            const uint16_t* w_pre, uint16_t* x_out, int n, float eps, int E,
                            int ng, int tg, int K, float route_scale, const float* Wr,
                            const float* bcorr, float* logits, int32_t* idx, float* w,
-                           unsigned* ctr, hipStream_t st);
+                           float* part, unsigned* ctr, hipStream_t st);
 
 // many-token (prefill) path
 constexpr int kGemvMaxT = 4;  // T above this runs on the matrix-core kernels
+// Attention calls of at most this many tokens, averaging at most 4 per cache
+// slot (a batch of decode steps), run split-K per token like single-token
+// decode; longer calls (prefill chunks) run the flash kernel.
+constexpr int kDecodeBatchMaxT = 256;
 int gemm_tile_rows();
+// part: fp32 split-K partials of gemm_split_bytes(M, N, K) bytes for short,
+// wide products (nullptr: no split)
+size_t gemm_split_bytes(int M, int N, int K);
 int launch_gemm_bf16(int M, int N, int K, const uint16_t* A, int lda, const uint16_t* B, int ldb,
-                     uint16_t* out, int ldo, uint16_t* out2, int ldo2, int n1, hipStream_t st);
+                     uint16_t* out, int ldo, uint16_t* out2, int ldo2, int n1, float* part,
+                     hipStream_t st);
 int launch_gemm_swiglu(int M, int F, int K, const uint16_t* A, int lda, const int32_t* gather,
                        const uint16_t* B, const int32_t* seg_off, const int32_t* tile_off, int E,
-                       long long b_stride, int max_mtiles, uint16_t* act, hipStream_t st);
+                       long long b_stride, int max_mtiles, uint16_t* act, float* part,
+                       hipStream_t st);
 int launch_gemm_f32(int M, int N, int K, const uint16_t* A, int lda, const uint16_t* B,
                     const int32_t* seg_off, const int32_t* tile_off, int E, long long b_stride,
                     int max_mtiles, float* out, int ldo, hipStream_t st);

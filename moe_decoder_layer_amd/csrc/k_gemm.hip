@@ -56,6 +56,10 @@ struct GemmArgs {
   void* out2;                 // EPI_BF16 split destination (columns >= n1)
   int ldo2, n1;
   int F;                      // EPI_SWIGLU: up rows start at F (B row index)
+  // split-K (EPI_F32 only): blockIdx.y = split z covers k-steps
+  // [z * kt_split, (z + 1) * kt_split) and writes out + z * split_stride
+  int kt_split;               // 0: the whole K range, no split
+  long long split_stride;
 };
 
 __device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ (row & 7); }
@@ -63,7 +67,10 @@ __device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ (row & 7
 // WAVES = 4: waves in a 2 x 2 grid, 128 x 128 each (1 wave per SIMD);
 // WAVES = 8: waves in a 2 x 4 grid, 128 x 64 each (2 waves per SIMD, so one
 // issues MFMAs while the other waits on LDS).
-template <int EPI, int WAVES>
+// SKIP: MFMAs of 32-row blocks past the tile's last row are skipped (wave-
+// uniform branches): for tiles expected to be mostly empty (grouped experts
+// with few tokens each, or M well below the tile height).
+template <int EPI, int WAVES, bool SKIP>
 __global__ __launch_bounds__(WAVES * 64) void gemm_bf16_kernel(GemmArgs g) {
   constexpr int WCOLS = WAVES / 2;     // wave grid columns
   constexpr int WN = BN / WCOLS;       // wave tile width (128 or 64)
@@ -152,6 +159,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_bf16_kernel(GemmArgs g) {
   };
 
   const int wm = wave / WCOLS, wn = wave % WCOLS;
+  const int band = mrows - wm * 128;  // rows of this wave's 128-row band that exist
   const int lr = lane & 31, lk = lane >> 5;  // fragment row / k half
   f32x16 acc[4][TJ];
 #pragma unroll
@@ -176,12 +184,13 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_bf16_kernel(GemmArgs g) {
     }
   };
 
-  const int KT = g.K / BK;
-  gload(0, 0);
+  const int kt0 = g.kt_split ? blockIdx.y * g.kt_split : 0;
+  const int KT = g.kt_split ? kt0 + g.kt_split : g.K / BK;
+  gload(kt0 * BK, 0);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-  for (int kt = 0; kt < KT; ++kt) {
-    const int cur = kt & 1;
+  for (int kt = kt0; kt < KT; ++kt) {
+    const int cur = (kt - kt0) & 1;  // buffer 0 holds the first k-step of this split
     // the other buffer was last read in step kt - 1, which every wave has left
     if (kt + 1 < KT) gload((kt + 1) * BK, cur ^ 1);
     bf16x8 af[2][4], bfr[2][TJ];
@@ -190,11 +199,13 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_bf16_kernel(GemmArgs g) {
     for (int ks = 0; ks < BK / 16; ++ks) {
       if (ks + 1 < BK / 16) frags(cur, ks + 1, af[(ks + 1) & 1], bfr[(ks + 1) & 1]);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 4; ++i) {
+        if (SKIP && 32 * i >= band) continue;
 #pragma unroll
         for (int j = 0; j < TJ; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks & 1][i], bfr[ks & 1][j],
                                                              acc[i][j], 0, 0, 0);
+      }
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's loads of step kt + 1
     __syncthreads();
@@ -228,7 +239,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_bf16_kernel(GemmArgs g) {
             if (n >= g.N) continue;
             const float v = acc[i][j][4 * ii + jj];
             if constexpr (EPI == EPI_F32) {
-              reinterpret_cast<float*>(g.out)[m * g.ldo + n] = v;
+              reinterpret_cast<float*>(g.out)[blockIdx.y * g.split_stride + m * g.ldo + n] = v;
             } else {
               if (n < g.n1)
                 reinterpret_cast<uint16_t*>(g.out)[m * g.ldo + n] = f2bf(v);
@@ -244,38 +255,114 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_bf16_kernel(GemmArgs g) {
 
 static size_t gemm_lds_bytes() { return (size_t)2 * (BM + BN) * BK * 2; }
 
-template <int EPI, int WAVES = kGemmWaves>
-static int launch(const GemmArgs& a, int grid_n, int grid_m, hipStream_t st) {
+template <int EPI, bool SKIP = false, int WAVES = kGemmWaves>
+static int launch(const GemmArgs& a, int grid_n, int grid_m, hipStream_t st, int splits = 1) {
   static bool attr_set = false;
   if (!attr_set) {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_bf16_kernel<EPI, WAVES>),
-                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)gemm_lds_bytes());
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_bf16_kernel<EPI, WAVES, SKIP>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)gemm_lds_bytes());
     attr_set = true;
   }
   GemmArgs g = a;
   g.tiles_m = grid_m;
   g.tiles_n = grid_n;
-  hipLaunchKernelGGL((gemm_bf16_kernel<EPI, WAVES>), dim3(grid_m * grid_n), dim3(WAVES * 64),
-                     gemm_lds_bytes(), st, g);
+  hipLaunchKernelGGL((gemm_bf16_kernel<EPI, WAVES, SKIP>), dim3(grid_m * grid_n, splits),
+                     dim3(WAVES * 64), gemm_lds_bytes(), st, g);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+// ---------------------------------------------------------------------------
+// Split-K for short, wide products (a batch of decode steps: M <= 256 tokens
+// against a weight whose N / 256 column tiles alone would leave most of the
+// chip idle). Each split multiplies a slice of K into an fp32 partial
+// [split][M][N]; gemm_split_reduce adds the partials in split order and
+// applies the epilogue (bf16 store with optional column split, or SwiGLU of
+// the gate / up column halves).
+int gemm_splits(int M, int N, int K) {
+  if (M > BM || K % BK) return 1;
+  const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+  const int ks = K / BK;
+  int s = 1;
+  while (tiles * s * 2 <= 256 && ks % (s * 2) == 0) s *= 2;
+  return s;
+}
+
+size_t gemm_split_bytes(int M, int N, int K) {
+  const int s = gemm_splits(M, N, K);
+  return s > 1 ? (size_t)s * M * N * 4 : 0;
+}
+
+// EPI_BF16: out[m][n] (n < n1) or out2[m][n - n1]; EPI_SWIGLU: out[m][f] =
+// bf16(silu(bf16(g)) * bf16(u)) with g, u the partial sums of columns f, F + f.
+template <int EPI>
+__global__ __launch_bounds__(256) void gemm_split_reduce_kernel(
+    const float* __restrict__ part, int splits, int M, int N, uint16_t* __restrict__ out,
+    int ldo, uint16_t* __restrict__ out2, int ldo2, int n1, int F) {
+  const int ncols = EPI == EPI_SWIGLU ? F : N;
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (long long)M * ncols) return;
+  const int m = (int)(i / ncols), n = (int)(i - (long long)m * ncols);
+  const size_t ss = (size_t)M * N;
+  if constexpr (EPI == EPI_SWIGLU) {
+    float gt = 0.f, up = 0.f;
+    for (int z = 0; z < splits; ++z) {
+      gt += part[z * ss + (size_t)m * N + n];
+      up += part[z * ss + (size_t)m * N + F + n];
+    }
+    out[(size_t)m * ldo + n] = f2bf(siluf(round_bf(gt)) * round_bf(up));
+  } else {
+    float v = 0.f;
+    for (int z = 0; z < splits; ++z) v += part[z * ss + (size_t)m * N + n];
+    if (n < n1) out[(size_t)m * ldo + n] = f2bf(v);
+    else out2[(size_t)m * ldo2 + (n - n1)] = f2bf(v);
+  }
+}
+
+template <int EPI>
+static int launch_split(const GemmArgs& a0, int splits, float* part, hipStream_t st) {
+  GemmArgs a = a0;
+  a.out = part;
+  a.ldo = a.N;
+  a.kt_split = a.K / BK / splits;
+  a.split_stride = (long long)a.M * a.N;
+  const int tn = (a.N + BN - 1) / BN, tm = (a.M + BM - 1) / BM;
+  if (launch<EPI_F32, true>(a, tn, tm, st, splits)) return -1;
+  const long long n = (long long)a.M * (EPI == EPI_SWIGLU ? a0.F : a.N);
+  hipLaunchKernelGGL((gemm_split_reduce_kernel<EPI>), dim3((unsigned)((n + 255) / 256)),
+                     dim3(256), 0, st, part, splits, a.M, a.N,
+                     reinterpret_cast<uint16_t*>(a0.out), a0.ldo,
+                     reinterpret_cast<uint16_t*>(a0.out2), a0.ldo2, a0.n1, a0.F);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
 int launch_gemm_bf16(int M, int N, int K, const uint16_t* A, int lda, const uint16_t* B, int ldb,
-                     uint16_t* out, int ldo, uint16_t* out2, int ldo2, int n1, hipStream_t st) {
+                     uint16_t* out, int ldo, uint16_t* out2, int ldo2, int n1, float* part,
+                     hipStream_t st) {
   GemmArgs a{};
   a.A = A; a.B = B; a.M = M; a.N = N; a.K = K; a.lda = lda; a.ldb = ldb;
   a.out = out; a.ldo = ldo; a.out2 = out2; a.ldo2 = ldo2; a.n1 = out2 ? n1 : N;
+  const int s = gemm_splits(M, N, K);
+  if (s > 1 && part) return launch_split<EPI_BF16>(a, s, part, st);
+  if (M <= BM / 2) return launch<EPI_BF16, true>(a, (N + BN - 1) / BN, (M + BM - 1) / BM, st);
   return launch<EPI_BF16>(a, (N + BN - 1) / BN, (M + BM - 1) / BM, st);
 }
 
 int launch_gemm_swiglu(int M, int F, int K, const uint16_t* A, int lda, const int32_t* gather,
                        const uint16_t* B, const int32_t* seg_off, const int32_t* tile_off, int E,
-                       long long b_stride, int max_mtiles, uint16_t* act, hipStream_t st) {
+                       long long b_stride, int max_mtiles, uint16_t* act, float* part,
+                       hipStream_t st) {
   GemmArgs a{};
   a.A = A; a.B = B; a.M = M; a.N = 2 * F; a.K = K; a.lda = lda; a.ldb = K;
   a.a_gather = gather; a.seg_off = seg_off; a.tile_off = tile_off; a.E = E;
   a.b_expert_stride = b_stride; a.out = act; a.ldo = F; a.F = F; a.n1 = 2 * F;
+  if (!seg_off) {
+    const int s = gemm_splits(M, 2 * F, K);
+    if (s > 1 && part) return launch_split<EPI_SWIGLU>(a, s, part, st);
+  }
   const int gm = seg_off ? max_mtiles : (M + BM - 1) / BM;
+  // grouped segments averaging under half a tile of rows: mostly empty tiles
+  const bool sparse = seg_off ? (long long)M < (long long)E * (BM / 2) : M <= BM / 2;
+  if (sparse) return launch<EPI_SWIGLU, true>(a, (2 * F + BN - 1) / BN, gm, st);
   return launch<EPI_SWIGLU>(a, (2 * F + BN - 1) / BN, gm, st);
 }
 
@@ -287,6 +374,8 @@ int launch_gemm_f32(int M, int N, int K, const uint16_t* A, int lda, const uint1
   a.seg_off = seg_off; a.tile_off = tile_off; a.E = E; a.b_expert_stride = b_stride;
   a.out = out; a.ldo = ldo; a.n1 = N;
   const int gm = seg_off ? max_mtiles : (M + BM - 1) / BM;
+  const bool sparse = seg_off ? (long long)M < (long long)E * (BM / 2) : M <= BM / 2;
+  if (sparse) return launch<EPI_F32, true>(a, (N + BN - 1) / BN, gm, st);
   return launch<EPI_F32>(a, (N + BN - 1) / BN, gm, st);
 }
 

@@ -76,7 +76,9 @@ int launch_qk_epilogue(int T, int Hq, int Hkv, int hd, const uint16_t* qkv, cons
                        const float* rope_cs, uint16_t* q_out, void* kc, void* vc, int fp8,
                        float k_scale, float v_scale, int S, int Lmax, float eps,
                        hipStream_t st) {
-  if (T <= kGemvMaxT) {
+  if (T <= kGemvMaxT || (T <= kDecodeBatchMaxT && T <= 4 * S)) {
+    // few tokens, or a batch of decode steps spread over many sequences: one
+    // wave per (token, head), the value columns written by that wave
     const dim3 grid((Hq + 2 * Hkv + 3) / 4, T);
     hipLaunchKernelGGL(qk_norm_pos_kvwrite_kernel, grid, dim3(256), 0, st, qkv, Hq, Hkv, hd, wq,
                        wk, pos, seq, mode, rope_cs, q_out, kc, vc, fp8, k_scale, v_scale, S,

@@ -22,26 +22,57 @@ namespace beam {
 
 constexpr int RT = 256;
 
-// 64 tokens x 64 experts per workgroup, k-steps of 16; each thread 4x4 outputs.
+// 64 tokens x 64 experts per workgroup, each thread 4 x 4 outputs; K in
+// blocks of 32 staged through LDS as fp32, the next block's 16-byte loads in
+// flight while the current one is multiplied out. blockIdx.z = split of the
+// K range (kc values each): split z writes its partial sums to
+// logits + z * T * E (summed in split order by the selection kernel).
 __global__ __launch_bounds__(RT) void router_logits_gemm_kernel(
-    const uint16_t* __restrict__ X, const float* __restrict__ Wr, int T, int E, int D,
+    const uint16_t* __restrict__ X, const float* __restrict__ Wr, int T, int E, int D, int kc,
     float* __restrict__ logits) {
-  __shared__ float As[16][64 + 4];
-  __shared__ float Bs[16][64 + 4];
+  constexpr int KB = 32;
+  __shared__ float As[KB][64 + 4];
+  __shared__ float Bs[KB][64 + 4];
   const int tm = blockIdx.x * 64, en = blockIdx.y * 64;
+  const int kbeg = blockIdx.z * kc, kend = min(D, kbeg + kc);
   const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
-  float acc[4][4] = {};
-  for (int k0 = 0; k0 < D; k0 += 16) {
-    for (int i = threadIdx.x; i < 64 * 16; i += RT) {
-      const int r = i >> 4, k = i & 15;
-      const int tt = tm + r, ee = en + r;
-      const bool kin = k0 + k < D;
-      As[k][r] = (tt < T && kin) ? bf2f(X[(size_t)tt * D + k0 + k]) : 0.f;
-      Bs[k][r] = (ee < E && kin) ? Wr[(size_t)ee * D + k0 + k] : 0.f;
+  // loader roles: A row ra (token), 8 k from ka; B row rb (expert), 2 x 4 k from kb
+  const int ra = threadIdx.x >> 2, ka = (threadIdx.x & 3) * 8;
+  const int rb = threadIdx.x >> 2, kb = (threadIdx.x & 3) * 8;
+  const bool aok = tm + ra < T, bok = en + rb < E;
+  const uint16_t* ap = X + (size_t)min(tm + ra, T - 1) * D;
+  const float* bp = Wr + (size_t)min(en + rb, E - 1) * D;
+  // D % 8 == 0; a block past kend reads zeros (k beyond D is clamped, masked)
+  auto load = [&](int k0, uint4& av, float4& b0, float4& b1) {
+    const int k = k0 + ka, kk = k0 + kb;
+    av = (aok && k < kend) ? ld16(ap + k) : uint4{0u, 0u, 0u, 0u};
+    if (bok && kk < kend) {
+      b0 = *reinterpret_cast<const float4*>(bp + kk);
+      b1 = *reinterpret_cast<const float4*>(bp + kk + 4);
+    } else {
+      b0 = b1 = float4{0.f, 0.f, 0.f, 0.f};
     }
-    __syncthreads();
+  };
+  auto store = [&](const uint4& av, const float4& b0, const float4& b1) {
+    const uint32_t w[4] = {av.x, av.y, av.z, av.w};
 #pragma unroll
-    for (int k = 0; k < 16; ++k) {
+    for (int i = 0; i < 4; ++i) {
+      As[ka + 2 * i][ra] = __uint_as_float(w[i] << 16);
+      As[ka + 2 * i + 1][ra] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+    Bs[kb + 0][rb] = b0.x; Bs[kb + 1][rb] = b0.y; Bs[kb + 2][rb] = b0.z; Bs[kb + 3][rb] = b0.w;
+    Bs[kb + 4][rb] = b1.x; Bs[kb + 5][rb] = b1.y; Bs[kb + 6][rb] = b1.z; Bs[kb + 7][rb] = b1.w;
+  };
+  float acc[4][4] = {};
+  uint4 av;
+  float4 b0, b1;
+  load(kbeg, av, b0, b1);
+  for (int k0 = kbeg; k0 < kend; k0 += KB) {
+    store(av, b0, b1);
+    __syncthreads();
+    if (k0 + KB < kend) load(k0 + KB, av, b0, b1);
+#pragma unroll 8
+    for (int k = 0; k < KB; ++k) {
       float a[4], b[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -55,13 +86,23 @@ __global__ __launch_bounds__(RT) void router_logits_gemm_kernel(
     }
     __syncthreads();
   }
+  float* out = logits + (size_t)blockIdx.z * T * E;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
       const int tt = tm + ty * 4 + i, ee = en + tx * 4 + jj;
-      if (tt < T && ee < E) logits[(size_t)tt * E + ee] = acc[i][jj];
+      if (tt < T && ee < E) out[(size_t)tt * E + ee] = acc[i][jj];
     }
+}
+
+// Splits of the K range for the many-token logits GEMM: enough workgroups to
+// cover the chip when there are few token tiles, each split a multiple of 32.
+int router_splits(int T, int E, int D) {
+  const int tiles = ((T + 63) / 64) * ((E + 63) / 64);
+  int s = 1;
+  while (s * 2 * tiles <= 256 && D % (s * 2 * 32) == 0 && D / (s * 2) >= 128) s *= 2;
+  return s;
 }
 
 constexpr int EMAX = 1024;
@@ -139,13 +180,21 @@ __device__ void route_token(const float* lg, float bias, int E, int ng, int tg, 
   __syncthreads();  // the LDS arrays are reused for the next token
 }
 
+// part != nullptr: the logits are the sum over nsplit partial arrays, added in
+// split order and written to logits first.
 __global__ __launch_bounds__(EMAX) void router_topk_kernel(
-    const float* __restrict__ logits, const float* __restrict__ bcorr, int T, int E, int ng,
-    int tg, int K, float route_scale, int32_t* __restrict__ idx, float* __restrict__ wout) {
+    float* __restrict__ logits, const float* __restrict__ part, int nsplit,
+    const float* __restrict__ bcorr, int T, int E, int ng, int tg, int K, float route_scale,
+    int32_t* __restrict__ idx, float* __restrict__ wout) {
   __shared__ float s_b[EMAX], cand_v[EMAX];
   __shared__ int cand_i[EMAX];
   __shared__ float g1[64], g2[64], ssel[32];
   const int t = blockIdx.x;
+  if (part != nullptr && (int)threadIdx.x < E) {
+    float v = 0.f;
+    for (int z = 0; z < nsplit; ++z) v += part[((size_t)z * T + t) * E + threadIdx.x];
+    logits[(size_t)t * E + threadIdx.x] = v;
+  }
   const float bias = (bcorr && (int)threadIdx.x < E) ? bcorr[threadIdx.x] : 0.f;
   route_token(logits + (size_t)t * E, bias, E, ng, tg, K, route_scale, idx + (size_t)t * K,
               wout + (size_t)t * K, s_b, cand_v, cand_i, g1, g2, ssel);
@@ -288,11 +337,11 @@ int launch_boundary_router(int T, int D, const uint16_t* y, const uint16_t* w_po
                            const uint16_t* w_pre, uint16_t* x_out, int n, float eps, int E,
                            int ng, int tg, int K, float route_scale, const float* Wr,
                            const float* bcorr, float* logits, int32_t* idx, float* w,
-                           unsigned* ctr, hipStream_t st) {
+                           float* part, unsigned* ctr, hipStream_t st) {
   if (!boundary_router_fused(T, E, D)) {
     if (launch_boundary(T, D, y, w_post, h, w_pre, x_out, n, eps, st)) return -1;
-    return launch_router(T, E, D, ng, tg, K, route_scale, x_out, Wr, bcorr, logits, idx, w, ctr,
-                         st);
+    return launch_router(T, E, D, ng, tg, K, route_scale, x_out, Wr, bcorr, logits, idx, w, part,
+                         ctr, st);
   }
   const int mode = (y == nullptr) ? 0 : (w_post != nullptr ? 1 : 2);
   float c_h, c_a;
@@ -312,7 +361,7 @@ int launch_boundary_router(int T, int D, const uint16_t* y, const uint16_t* w_po
 
 int launch_router(int T, int E, int D, int ng, int tg, int K, float route_scale,
                   const uint16_t* X, const float* Wr, const float* bcorr, float* logits,
-                  int32_t* idx, float* w, unsigned* ctr, hipStream_t st) {
+                  int32_t* idx, float* w, float* part, unsigned* ctr, hipStream_t st) {
   if (T <= 4 && E <= RT) {
     const dim3 grid((E + 3) / 4);
     if (D <= 8 * 64 * 4)
@@ -323,12 +372,15 @@ int launch_router(int T, int E, int D, int ng, int tg, int K, float route_scale,
                          logits, bcorr, ng, tg, K, route_scale, idx, w, ctr);
     return hipGetLastError() == hipSuccess ? 0 : -1;
   }
-  hipLaunchKernelGGL(router_logits_gemm_kernel, dim3((T + 63) / 64, (E + 63) / 64), dim3(RT), 0,
-                     st, X, Wr, T, E, D, logits);
+  const int ns = router_splits(T, E, D);
+  if (ns > 1 && part == nullptr) return -1;
+  const int kc = D / ns;
+  hipLaunchKernelGGL(router_logits_gemm_kernel, dim3((T + 63) / 64, (E + 63) / 64, ns), dim3(RT),
+                     0, st, X, Wr, T, E, D, kc, ns > 1 ? part : logits);
   if (hipGetLastError() != hipSuccess) return -1;
   const int threads = ((E + 63) / 64) * 64;
-  hipLaunchKernelGGL(router_topk_kernel, dim3(T), dim3(threads), 0, st, logits, bcorr, T, E, ng,
-                     tg, K, route_scale, idx, w);
+  hipLaunchKernelGGL(router_topk_kernel, dim3(T), dim3(threads), 0, st, logits,
+                     ns > 1 ? part : nullptr, ns, bcorr, T, E, ng, tg, K, route_scale, idx, w);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

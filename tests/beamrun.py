@@ -56,8 +56,8 @@ def bf16_ulp(ref) -> np.ndarray:
 
 def assert_rms_close(got, ref, name="", frac=1e-2, ulps=1):
     """Parity bar for bf16 tensors: every element within
-    max(frac * rms(ref), ulps bf16 ulps of the reference element), and the RMS
-    of the error within frac * rms(ref).
+    max(frac * rms(ref), ulps bf16 ulps at the larger of the two elements'
+    magnitudes), and the RMS of the error within frac * rms(ref).
 
     The ulp allowance exists because the tensors are bf16: where the GPU's fp32
     value and the oracle's float64 value straddle a rounding boundary the two
@@ -75,7 +75,10 @@ def assert_rms_close(got, ref, name="", frac=1e-2, ulps=1):
     err = np.abs(got - ref)
     r = rms(ref)
     tol = frac * r
-    bad = err > np.maximum(tol, ulps * bf16_ulp(ref) * 1.0000001)
+    # bf16 spacing at the larger of the two magnitudes: across a binade edge
+    # (ref just below a power of two, got just above) the spacing doubles
+    ulp = bf16_ulp(np.maximum(np.abs(ref), np.abs(got)))
+    bad = err > np.maximum(tol, ulps * ulp * 1.0000001)
     assert not np.any(bad), (f"{name}: {int(bad.sum())} of {err.size} elements beyond "
                              f"max({frac}*rms, {ulps} ulp); worst |err| {err.max():.3e}, "
                              f"rms {r:.3e}")
@@ -149,7 +152,8 @@ def rope_table(Lmax, d, theta):
 
 # ----------------------------------------------------------------- params
 SMALL = ("w_attn_pre", "w_attn_post", "w_ffn_pre", "w_ffn_post", "w_next_pre", "w_qnorm",
-         "w_knorm", "w_qkvg", "b_gate", "w_o", "w_r", "b_corr", "sink")
+         "w_knorm", "w_qkvg", "b_gate", "w_o", "w_r", "b_corr", "sink", "shared_w13",
+         "shared_w2")
 
 
 class Params:
@@ -182,6 +186,11 @@ class Params:
                                         out=w13[e])
                 synth.torch_normal_bf16((dims.D, dims.F), 0.02, seed, layer, "w2", e, out=w2[e])
             self.t["w13"], self.t["w2"] = w13, w2
+            if dims.shared:
+                self.t["shared_w13"] = synth.torch_normal_bf16((2 * dims.F, dims.D), 0.02, seed,
+                                                               layer, "w13", "shared")
+                self.t["shared_w2"] = synth.torch_normal_bf16((dims.D, dims.F), 0.02, seed,
+                                                              layer, "w2", "shared")
         if dense:
             self.t["dense_w13"] = synth.torch_normal_bf16((2 * dims.Fd, dims.D), 0.02, seed,
                                                           layer, "dense_w13")
@@ -221,8 +230,9 @@ def ws(dims, op, T, ctx=0):
 
 
 def run_layer(dims, P: Params, cache: Cache, h_bits, pos, seq, mode: str, n: int,
-              ffn="moe", rope=None, keep=True) -> dict:
-    """One layer through the C ABI. Returns host copies of every intermediate."""
+              ffn="moe", rope=None, keep=True, sandwich=True) -> dict:
+    """One layer through the C ABI. Returns host copies of every intermediate.
+    sandwich False: the pre-norm, plain-residual layer form (no post-norms)."""
     T = len(pos)
     D = dims.D
     t = P.t
@@ -255,7 +265,10 @@ def run_layer(dims, P: Params, cache: Cache, h_bits, pos, seq, mode: str, n: int
                     ws(dims, B.BEAM_OP_OUT_GATE, T))
     h_in = h.clone()
     x2 = torch.empty((T, D), **I16)
-    B.beam_boundary_norm_residual(dims, T, y, t["w_attn_post"], h, t["w_ffn_pre"], x2, n)
+    if sandwich:
+        B.beam_boundary_norm_residual(dims, T, y, t["w_attn_post"], h, t["w_ffn_pre"], x2, n)
+    else:
+        B.beam_boundary_norm_residual(dims, T, y, None, h, t["w_ffn_pre"], x2, 0)
     h_mid = h.clone()
     y2 = torch.empty((T, D), **I16)
     if ffn == "moe":
@@ -272,7 +285,10 @@ def run_layer(dims, P: Params, cache: Cache, h_bits, pos, seq, mode: str, n: int
         B.beam_dense_swiglu(T, D, dims.Fd, x2, t["dense_w13"], t["dense_w2"], y2,
                             ws(dd, B.BEAM_OP_DENSE, T))
     xn = torch.empty((T, D), **I16)
-    B.beam_boundary_norm_residual(dims, T, y2, t["w_ffn_post"], h, t["w_next_pre"], xn, n + 1)
+    if sandwich:
+        B.beam_boundary_norm_residual(dims, T, y2, t["w_ffn_post"], h, t["w_next_pre"], xn, n + 1)
+    else:
+        B.beam_boundary_norm_residual(dims, T, y2, None, h, t["w_next_pre"], xn, 0)
     B.beam_check()
     out.update(x=host_bits(x), q=host_bits(q), g=host_bits(g), o=host_bits(o), y=host_bits(y),
                h_in=host_bits(h_in), h_mid=host_bits(h_mid), x2=host_bits(x2), y2=host_bits(y2),

@@ -343,6 +343,67 @@ attn_decode_fp8_stream_kernel(ATTN_DECODE_PARAMS) {
   attn_decode_body<HD, true, SWA, 4, 16>(ATTN_DECODE_ARGS);
 }
 
+// The same combine for spans of at most kAttnFusedMergeMax chunks, one wave
+// per (token, head), four per workgroup: every record requested before use.
+template <int HD>
+__global__ __launch_bounds__(256) void attn_merge_small_kernel(
+    const float* __restrict__ part, const int32_t* __restrict__ pos,
+    const int32_t* __restrict__ seq, int S, int Lmax, int T, int Hq, int window, int swa,
+    int tpw, int nch_stride, const float* __restrict__ sink, float v_scale,
+    uint16_t* __restrict__ o) {
+  constexpr int MX = kAttnFusedMergeMax;
+  constexpr int DPL = (HD + 63) / 64;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int u = blockIdx.x * 4 + wave;
+  if (u >= T * Hq) return;
+  const int t = u / Hq, h = u - t * Hq;
+  uint16_t* out = o + (size_t)u * HD;
+  const int p = pos[t], s = seq[t];
+  if (p < 0 || p >= Lmax || s < 0 || s >= S) {
+    for (int d = lane; d < HD; d += 64) out[d] = 0;
+    return;
+  }
+  const int lo = swa ? max(0, p - window + 1) : 0;
+  const int CK = 256 * tpw;
+  const int nch = (p + 1 - (lo & ~63) + CK - 1) / CK;
+  const float* rec0 = part + (size_t)u * nch_stride * (HD + 4);
+  float mc[MX], lc[MX], oc[MX][DPL];
+#pragma unroll
+  for (int c = 0; c < MX; ++c) {
+    const float* rec = rec0 + (size_t)min(c, nch - 1) * (HD + 4);
+    mc[c] = rec[0];
+    lc[c] = rec[1];
+#pragma unroll
+    for (int k = 0; k < DPL; ++k) {
+      const int d = lane + 64 * k;
+      oc[c][k] = d < HD ? rec[4 + d] : 0.f;
+    }
+  }
+  float M = -INFINITY;
+#pragma unroll
+  for (int c = 0; c < MX; ++c)
+    if (c < nch) M = fmaxf(M, mc[c]);
+  const float sl2 = sink ? sink[h] * 1.4426950408889634f : -INFINITY;
+  M = fmaxf(M, sl2);
+  float L = sink ? exp2f(sl2 - M) : 0.f;
+  float O[DPL] = {};
+#pragma unroll
+  for (int c = 0; c < MX; ++c) {
+    if (c < nch) {
+      const float e = exp2f(mc[c] - M);
+      L += e * lc[c];
+#pragma unroll
+      for (int k = 0; k < DPL; ++k) O[k] += e * oc[c][k];
+    }
+  }
+  const float inv = v_scale / L;
+#pragma unroll
+  for (int k = 0; k < DPL; ++k) {
+    const int d = lane + 64 * k;
+    if (d < HD) out[d] = f2bf(O[k] * inv);
+  }
+}
+
 // Combine the chunks of one (token, head): o = sum_c 2^(m_c-M) O_c / sum_c 2^(m_c-M) l_c.
 // An attention sink adds 2^(sink*log2e - M) to the denominator only. Wave w
 // takes chunks w, w + MW, ... in batches of 8 whose records are all requested
@@ -498,8 +559,19 @@ int launch_attn_decode(int T, int Hq, int Hkv, int hd, int swa, int window, int 
 #undef ARGS
   if (hipGetLastError() != hipSuccess) return -1;
   if (od) return 0;
-  const dim3 mg(Hq, T);
   const float vs = fp8 ? v_scale : 1.0f;
+  if (nch <= kAttnFusedMergeMax) {
+    const dim3 sg((T * Hq + 3) / 4);
+#define SMALL(HD_)                                                                              \
+  hipLaunchKernelGGL((attn_merge_small_kernel<HD_>), sg, dim3(256), 0, st, part, pos, seq, S,   \
+                     Lmax, T, Hq, window, swa, tpw, nch, sink, vs, o)
+    if (hd == 128) SMALL(128);
+    else if (hd == 64) SMALL(64);
+    else SMALL(32);
+#undef SMALL
+    return hipGetLastError() == hipSuccess ? 0 : -1;
+  }
+  const dim3 mg(Hq, T);
   if (hd == 128)
     hipLaunchKernelGGL((attn_merge_kernel<128>), mg, dim3(1024), 0, st, part, pos, seq, S, Lmax, Hq,
                        window, swa, tpw, nch, sink, vs, o);

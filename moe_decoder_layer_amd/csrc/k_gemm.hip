@@ -153,7 +153,10 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_bf16_kernel(GemmArgs g) {
   auto gload = [&](int k0, int buf) {
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
-      load_lds16(a_src[i] + k0, As(buf) + (wave * RPW + i * 8) * BK);
+      // SKIP: A rows past the tile's last row are not fetched (their LDS rows
+      // only feed outputs that are never stored)
+      if (!SKIP || wave * RPW + i * 8 < mrows)
+        load_lds16(a_src[i] + k0, As(buf) + (wave * RPW + i * 8) * BK);
       load_lds16(b_src[i] + k0, Bs(buf) + (wave * RPW + i * 8) * BK);
     }
   };
@@ -283,7 +286,8 @@ int gemm_splits(int M, int N, int K) {
   const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
   const int ks = K / BK;
   int s = 1;
-  while (tiles * s * 2 <= 256 && ks % (s * 2) == 0) s *= 2;
+  // the partials (written, then read back) stay within half the weight bytes
+  while (tiles * s * 2 <= 256 && ks % (s * 2) == 0 && (long long)s * 2 * 4 * M <= K) s *= 2;
   return s;
 }
 

@@ -42,19 +42,44 @@ __global__ __launch_bounds__(256) void moe_count_kernel(const int32_t* __restric
   if (threadIdx.x == 0) counts[e] = c;
 }
 
-__global__ __launch_bounds__(256) void moe_scan_kernel(const int32_t* __restrict__ counts, int E,
-                                                       int tile_rows, int32_t* __restrict__ seg_off,
-                                                       int32_t* __restrict__ tile_off) {
-  if (threadIdx.x != 0) return;
-  int s = 0, ts = 0;
-  for (int e = 0; e < E; ++e) {
-    seg_off[e] = s;
-    tile_off[e] = ts;
-    s += counts[e];
-    ts += (counts[e] + tile_rows - 1) / tile_rows;
+// One workgroup of 1024 threads, thread e holding expert e (E <= 1024): an
+// inclusive scan of (rows, tiles) within each wave, then across the waves.
+__global__ __launch_bounds__(1024) void moe_scan_kernel(const int32_t* __restrict__ counts, int E,
+                                                        int tile_rows, int32_t* __restrict__ seg_off,
+                                                        int32_t* __restrict__ tile_off) {
+  __shared__ int wr[16], wt[16];
+  const int e = threadIdx.x, wave = e >> 6, lane = e & 63;
+  const int c = e < E ? counts[e] : 0;
+  const int tc = (c + tile_rows - 1) / tile_rows;
+  int r = c, t = tc;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int ro = __shfl_up(r, o, 64), to = __shfl_up(t, o, 64);
+    if (lane >= o) {
+      r += ro;
+      t += to;
+    }
   }
-  seg_off[E] = s;
-  tile_off[E] = ts;
+  if (lane == 63) {
+    wr[wave] = r;
+    wt[wave] = t;
+  }
+  __syncthreads();
+  int rb = 0, tb = 0;
+  for (int w = 0; w < wave; ++w) {
+    rb += wr[w];
+    tb += wt[w];
+  }
+  r += rb;
+  t += tb;
+  if (e < E) {
+    seg_off[e] = r - c;  // exclusive prefix
+    tile_off[e] = t - tc;
+  }
+  if (e == E - 1) {
+    seg_off[E] = r;
+    tile_off[E] = t;
+  }
 }
 
 __global__ __launch_bounds__(256) void moe_scatter_kernel(const int32_t* __restrict__ idx, int P,
@@ -143,7 +168,8 @@ int launch_moe_route(int T, int K, int E, const int32_t* idx, int tile_rows, int
                      hipStream_t st) {
   const int P = T * K;
   hipLaunchKernelGGL(moe_count_kernel, dim3(E), dim3(256), 0, st, idx, P, E, counts);
-  hipLaunchKernelGGL(moe_scan_kernel, dim3(1), dim3(256), 0, st, counts, E, tile_rows, seg_off,
+  if (E > 1024) return -1;
+  hipLaunchKernelGGL(moe_scan_kernel, dim3(1), dim3(1024), 0, st, counts, E, tile_rows, seg_off,
                      tile_off);
   hipLaunchKernelGGL(moe_scatter_kernel, dim3(E), dim3(256), 0, st, idx, P, K, seg_off, perm, inv);
   return hipGetLastError() == hipSuccess ? 0 : -1;

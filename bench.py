@@ -45,7 +45,7 @@ def parse():
     ap.add_argument("--no-flint", action="store_true",
                     help="skip the second model's batch-128 decode legs")
     ap.add_argument("--prefill-reps", type=int, default=3)
-    ap.add_argument("--cpu-steps", type=int, default=3)
+    ap.add_argument("--cpu-steps", type=int, default=16)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB copy kernel (HBM counter calibration)")
     ap.add_argument("--counters", action="store_true",

@@ -137,7 +137,7 @@ float* ws_router_part(const beam_dims* d, int T, bool own_logits, void* ws) {
   return (float*)(ws_data(ws) + ws_router_logits(d, T, own_logits));
 }
 
-// Many-token MoE workspace, in order: counts[E], seg_off[E+1], tile_off[E+1],
+// Many-token MoE workspace, in order: counts[chunks][E], seg_off[E+1], tile_off[E+1],
 // perm[P], inv[P] (int32); act[P][F] bf16; out[P][D] fp32; shared expert
 // act_s[T][F] bf16 and out_s[T][D] fp32.
 struct MoeWs {
@@ -147,7 +147,7 @@ MoeWs moe_ws_layout(const beam_dims* d, int T) {
   const size_t P = (size_t)T * d->topk, E = d->E;
   MoeWs w{};
   size_t o = 0;
-  w.counts = o; o += align256(E * 4);
+  w.counts = o; o += align256((size_t)beam::moe_route_chunks((int)P) * E * 4);
   w.seg_off = o; o += align256((E + 1) * 4);
   w.tile_off = o; o += align256((E + 1) * 4);
   w.perm = o; o += align256(P * 4);

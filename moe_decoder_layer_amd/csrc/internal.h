@@ -79,6 +79,8 @@ int launch_gemm_swiglu(int M, int F, int K, const uint16_t* A, int lda, const in
 int launch_gemm_f32(int M, int N, int K, const uint16_t* A, int lda, const uint16_t* B,
                     const int32_t* seg_off, const int32_t* tile_off, int E, long long b_stride,
                     int max_mtiles, float* out, int ldo, hipStream_t st);
+// counts: moe_route_chunks(T * K) x E int32 of scratch
+int moe_route_chunks(int P);
 int launch_moe_route(int T, int K, int E, const int32_t* idx, int tile_rows, int32_t* counts,
                      int32_t* seg_off, int32_t* tile_off, int32_t* perm, int32_t* inv,
                      hipStream_t st);

@@ -2,10 +2,10 @@
 // 1.0 on vLLM", MoE section: every token goes to its 8 selected experts; the
 // page's decode graph uses two routing kernels and two grouped GEMMs).
 //
-//   moe_count_kernel    one workgroup per expert counts its (token, slot) pairs
-//   moe_scan_kernel     row offsets of the expert segments and prefix sums of
-//                       their GEMM tile counts
-//   moe_scatter_kernel  one workgroup per expert writes its pairs in (token,
+//   moe_count_kernel    per chunk of pairs, the count of each expert
+//   moe_scan_kernel     row offsets of the expert segments, prefix sums of
+//                       their GEMM tile counts, each chunk's base per expert
+//   moe_scatter_kernel  one workgroup per chunk writes its pairs in (token,
 //                       slot) order: perm[row] = token, inv[token * K + slot] = row
 //   moe_combine_kernel  y[t] = bf16(sum_k w[t][k] * out[inv[t][k]] (+ shared))
 // All integer work is deterministic (no atomics, stable order), so the grouped
@@ -28,28 +28,38 @@ __device__ __forceinline__ int block_sum_int(int v, int* red) {
   return red[0] + red[1] + red[2] + red[3];
 }
 
+// The (token, slot) pairs are cut into chunks of kRouteChunk; chunk c's
+// per-expert counts go to counts[c][E].
+constexpr int kRouteChunk = 2048;
+
 __global__ __launch_bounds__(256) void moe_count_kernel(const int32_t* __restrict__ idx, int P,
                                                         int E, int32_t* __restrict__ counts) {
-  __shared__ int red[4];
-  const int e = blockIdx.x;
-  int c = 0;
-  for (int i = threadIdx.x; i < P; i += 256) {
+  __shared__ int hist[1024];
+  const int c = blockIdx.x, i0 = c * kRouteChunk, i1 = min(P, i0 + kRouteChunk);
+  for (int e = threadIdx.x; e < E; e += 256) hist[e] = 0;
+  __syncthreads();
+  for (int i = i0 + threadIdx.x; i < i1; i += 256) {
     const int v = idx[i];
-    c += (v == e);
-    if (e == 0 && (v < 0 || v >= E)) BEAM_RAISE(moe, ERR_EXPERT);
+    if (v >= 0 && v < E) atomicAdd(&hist[v], 1);  // an integer count: order-independent
+    else BEAM_RAISE(moe, ERR_EXPERT);
   }
-  c = block_sum_int(c, red);
-  if (threadIdx.x == 0) counts[e] = c;
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += 256) counts[(size_t)c * E + e] = hist[e];
 }
 
-// One workgroup of 1024 threads, thread e holding expert e (E <= 1024): an
-// inclusive scan of (rows, tiles) within each wave, then across the waves.
-__global__ __launch_bounds__(1024) void moe_scan_kernel(const int32_t* __restrict__ counts, int E,
-                                                        int tile_rows, int32_t* __restrict__ seg_off,
+// One workgroup of 1024 threads, thread e holding expert e (E <= 1024): its
+// total over the chunks, an inclusive scan of (rows, tiles) over the experts
+// (within each wave, then across the waves), and then counts[c][e] replaced
+// by the row where chunk c's first pair of expert e goes.
+__global__ __launch_bounds__(1024) void moe_scan_kernel(int32_t* __restrict__ counts, int nch,
+                                                        int E, int tile_rows,
+                                                        int32_t* __restrict__ seg_off,
                                                         int32_t* __restrict__ tile_off) {
   __shared__ int wr[16], wt[16];
   const int e = threadIdx.x, wave = e >> 6, lane = e & 63;
-  const int c = e < E ? counts[e] : 0;
+  int c = 0;
+  if (e < E)
+    for (int ch = 0; ch < nch; ++ch) c += counts[(size_t)ch * E + e];
   const int tc = (c + tile_rows - 1) / tile_rows;
   int r = c, t = tc;
 #pragma unroll
@@ -75,6 +85,12 @@ __global__ __launch_bounds__(1024) void moe_scan_kernel(const int32_t* __restric
   if (e < E) {
     seg_off[e] = r - c;  // exclusive prefix
     tile_off[e] = t - tc;
+    int run = r - c;
+    for (int ch = 0; ch < nch; ++ch) {
+      const int n = counts[(size_t)ch * E + e];
+      counts[(size_t)ch * E + e] = run;
+      run += n;
+    }
   }
   if (e == E - 1) {
     seg_off[E] = r;
@@ -82,30 +98,36 @@ __global__ __launch_bounds__(1024) void moe_scan_kernel(const int32_t* __restric
   }
 }
 
+// One workgroup per chunk, its pairs in order, 256 at a time: a pair's row is
+// its expert's running base for the chunk plus the number of earlier pairs of
+// the same expert in the batch of 256 (pairs keep (token, slot) order within
+// every expert). perm[row] = token, inv[pair] = row.
 __global__ __launch_bounds__(256) void moe_scatter_kernel(const int32_t* __restrict__ idx, int P,
-                                                          int K, const int32_t* __restrict__ seg_off,
+                                                          int K, int E,
+                                                          const int32_t* __restrict__ base,
                                                           int32_t* __restrict__ perm,
                                                           int32_t* __restrict__ inv) {
-  __shared__ int wcount[4];
-  const int e = blockIdx.x;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  int base = seg_off[e];
-  for (int i0 = 0; i0 < P; i0 += 256) {
-    const int i = i0 + threadIdx.x;
-    const bool hit = (i < P) && idx[i] == e;
-    const uint64_t bal = __ballot(hit);
-    const int before = __popcll(bal & ((1ull << lane) - 1ull));
+  __shared__ int run[1024];
+  __shared__ int ex[256];
+  const int c = blockIdx.x, i0 = c * kRouteChunk, i1 = min(P, i0 + kRouteChunk);
+  for (int e = threadIdx.x; e < E; e += 256) run[e] = base[(size_t)c * E + e];
+  for (int b0 = i0; b0 < i1; b0 += 256) {
+    const int i = b0 + threadIdx.x;
+    const int v = i < i1 ? idx[i] : -1;
+    const bool ok = v >= 0 && v < E;
+    __syncthreads();  // run[] updated by the previous batch
+    ex[threadIdx.x] = ok ? v : -1;
     __syncthreads();
-    if (lane == 0) wcount[wave] = __popcll(bal);
-    __syncthreads();
-    int off = base;
-    for (int w = 0; w < wave; ++w) off += wcount[w];
-    if (hit) {
-      const int row = off + before;
+    int before = 0;
+    if (ok)
+      for (int j = 0; j < (int)threadIdx.x; ++j) before += (ex[j] == v);
+    const int row = ok ? run[v] + before : 0;
+    __syncthreads();  // every lane has read run[] for this batch
+    if (ok) {
       perm[row] = i / K;
       inv[i] = row;
+      atomicAdd(&run[v], 1);  // an integer count: order-independent
     }
-    base += wcount[0] + wcount[1] + wcount[2] + wcount[3];
   }
 }
 
@@ -163,15 +185,19 @@ __global__ __launch_bounds__(256) void gate_kernel(const uint16_t* __restrict__ 
   *reinterpret_cast<uint4*>(z + i * 8) = uint4{r[0], r[1], r[2], r[3]};
 }
 
+int moe_route_chunks(int P) { return (P + kRouteChunk - 1) / kRouteChunk; }
+
 int launch_moe_route(int T, int K, int E, const int32_t* idx, int tile_rows, int32_t* counts,
                      int32_t* seg_off, int32_t* tile_off, int32_t* perm, int32_t* inv,
                      hipStream_t st) {
   const int P = T * K;
-  hipLaunchKernelGGL(moe_count_kernel, dim3(E), dim3(256), 0, st, idx, P, E, counts);
   if (E > 1024) return -1;
-  hipLaunchKernelGGL(moe_scan_kernel, dim3(1), dim3(1024), 0, st, counts, E, tile_rows, seg_off,
-                     tile_off);
-  hipLaunchKernelGGL(moe_scatter_kernel, dim3(E), dim3(256), 0, st, idx, P, K, seg_off, perm, inv);
+  const int nch = moe_route_chunks(P);
+  hipLaunchKernelGGL(moe_count_kernel, dim3(nch), dim3(256), 0, st, idx, P, E, counts);
+  hipLaunchKernelGGL(moe_scan_kernel, dim3(1), dim3(1024), 0, st, counts, nch, E, tile_rows,
+                     seg_off, tile_off);
+  hipLaunchKernelGGL(moe_scatter_kernel, dim3(nch), dim3(256), 0, st, idx, P, K, E, counts, perm,
+                     inv);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

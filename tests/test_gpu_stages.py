@@ -53,7 +53,7 @@ def test_boundary(D, T, case):
 
 # ------------------------------------------------------------------ q/k + cache write
 @pytest.mark.parametrize("base,T,pos0", [(CFG0, 1, 64), (CFG0, 32, 64), (BEAM, 1, 3000),
-                                         (BEAM, 3, 17)])
+                                         (BEAM, 3, 17), (BEAM, 40, 1000)])
 @pytest.mark.parametrize("mode", ["swa", "nope"])
 @pytest.mark.parametrize("kv", ["bf16", "fp8"])
 def test_qk_norm_kvwrite(base, T, pos0, mode, kv):
@@ -103,7 +103,7 @@ def test_qk_norm_kvwrite(base, T, pos0, mode, kv):
     assert np.all(K.view(np.uint16 if kv == "bf16" else np.uint8)[mask] == fill)
 
 
-@pytest.mark.parametrize("base,T", [(BEAM, 1), (CFG0, 3)])
+@pytest.mark.parametrize("base,T", [(BEAM, 1), (CFG0, 3), (BEAM, 40)])
 def test_qk_slot_outside_cache_is_flagged(base, T):
     """A position at Lmax (or a slot index at S) skips that token's cache write
     and raises the device flag; the other tokens are written as usual."""

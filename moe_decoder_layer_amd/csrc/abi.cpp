@@ -470,7 +470,7 @@ int beam_moe_swiglu_combine(const beam_dims* dims, int T, const uint16_t* x,
     uint16_t* act = (uint16_t*)(b + L.act);
     float* out = (float*)(b + L.out);
     const int E = dims->E, K = dims->topk, D = dims->D, F = dims->F;
-    const int BMr = beam::gemm_tile_rows();
+    const int BMr = beam::gemm_grouped_rows(T * K, dims->E);
     const int max_tiles = (T * K + BMr - 1) / BMr + E;
     const hipStream_t st = S_(stream);
     if (beam::launch_moe_route(T, K, E, idx, BMr, counts, seg_off, tile_off, perm, inv, st) ||

@@ -65,7 +65,7 @@ constexpr int kGemvMaxT = 4;  // T above this runs on the matrix-core kernels
 // slot (a batch of decode steps), run split-K per token like single-token
 // decode; longer calls (prefill chunks) run the flash kernel.
 constexpr int kDecodeBatchMaxT = 256;
-int gemm_tile_rows();
+int gemm_grouped_rows(int M, int E);  // tile rows of the grouped expert GEMMs
 // part: fp32 split-K partials of gemm_split_bytes(M, N, K) bytes for short,
 // wide products (nullptr: no split)
 size_t gemm_split_bytes(int M, int N, int K);

@@ -70,16 +70,20 @@ __device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ (row & 7
 // SKIP: MFMAs of 32-row blocks past the tile's last row are skipped (wave-
 // uniform branches): for tiles expected to be mostly empty (grouped experts
 // with few tokens each, or M well below the tile height).
-template <int EPI, int WAVES, bool SKIP>
+// TR: tile rows (256, or 32 for grouped segments of a few rows each, which
+// need only a 32-row A tile in LDS: 72 KiB instead of 128, two workgroups per
+// CU, twice the weight streams in flight).
+template <int EPI, int WAVES, bool SKIP, int TR = BM>
 __global__ __launch_bounds__(WAVES * 64) void gemm_bf16_kernel(GemmArgs g) {
+  static_assert(TR == BM || (SKIP && TR == 32), "short tiles need the row skip");
   constexpr int WCOLS = WAVES / 2;     // wave grid columns
   constexpr int WN = BN / WCOLS;       // wave tile width (128 or 64)
   constexpr int TJ = WN / 32;          // 32-wide MFMA blocks per wave row
   constexpr int RPW = BM / WAVES;      // tile rows each wave loads (A and B)
   extern __shared__ __align__(16) uint16_t lds[];
   // double buffer: A0 | A1 | B0 | B1
-  auto As = [&](int buf) { return lds + buf * (BM * BK); };
-  auto Bs = [&](int buf) { return lds + 2 * BM * BK + buf * (BN * BK); };
+  auto As = [&](int buf) { return lds + buf * (TR * BK); };
+  auto Bs = [&](int buf) { return lds + 2 * TR * BK + buf * (BN * BK); };
 
   // ---- workgroup -> tile (XCD-contiguous, grouped column-major) ---------------
   // Grouped mode launches the worst-case number of tile rows; only the first
@@ -111,11 +115,11 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_bf16_kernel(GemmArgs g) {
     }
     e = lo;
     const int seg0 = g.seg_off[e], seg1 = g.seg_off[e + 1];
-    m0 = seg0 + (ti - g.tile_off[e]) * BM;
-    mrows = min(BM, seg1 - m0);
+    m0 = seg0 + (ti - g.tile_off[e]) * TR;
+    mrows = min(TR, seg1 - m0);
   } else {
-    m0 = tm * BM;
-    mrows = min(BM, g.M - m0);
+    m0 = tm * TR;
+    mrows = min(TR, g.M - m0);
   }
   const int n0 = tn * BN;  // tile column origin (EPI_SWIGLU: in act columns x 2)
   const uint16_t* Bbase = g.B + (long long)e * g.b_expert_stride;
@@ -155,7 +159,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_bf16_kernel(GemmArgs g) {
     for (int i = 0; i < NL; ++i) {
       // SKIP: A rows past the tile's last row are not fetched (their LDS rows
       // only feed outputs that are never stored)
-      if (!SKIP || wave * RPW + i * 8 < mrows)
+      if (!SKIP || wave * RPW + i * 8 < mrows)  // (mrows <= TR)
         load_lds16(a_src[i] + k0, As(buf) + (wave * RPW + i * 8) * BK);
       load_lds16(b_src[i] + k0, Bs(buf) + (wave * RPW + i * 8) * BK);
     }
@@ -164,19 +168,23 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_bf16_kernel(GemmArgs g) {
   const int wm = wave / WCOLS, wn = wave % WCOLS;
   const int band = mrows - wm * 128;  // rows of this wave's 128-row band that exist
   const int lr = lane & 31, lk = lane >> 5;  // fragment row / k half
-  f32x16 acc[4][TJ];
+  // 32-row blocks a wave can own: 4, or 1 with 32-row tiles (then only the
+  // first wave row holds rows at all; the accumulators shrink to fit two
+  // workgroups per CU)
+  constexpr int MI = TR >= 128 ? 4 : 1;
+  f32x16 acc[MI][TJ];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < MI; ++i)
 #pragma unroll
     for (int j = 0; j < TJ; ++j) acc[i][j] = f32x16{};
 
   // fragments of k-step ks (16 deep) of buffer buf
-  auto frags = [&](int buf, int ks, bf16x8 (&af)[4], bf16x8 (&bfr)[TJ]) {
+  auto frags = [&](int buf, int ks, bf16x8 (&af)[MI], bf16x8 (&bfr)[TJ]) {
     const uint16_t* Ab = As(buf) + (wm * 128) * BK;
     const uint16_t* Bb = Bs(buf) + (wn * WN) * BK;
     const int chunk = ks * 2 + lk;  // 8 bf16 = one 16 B chunk
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < MI; ++i) {
       const int r = i * 32 + lr;
       af[i] = *reinterpret_cast<const bf16x8*>(Ab + r * BK + swz(r, chunk) * 8);
     }
@@ -196,13 +204,13 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_bf16_kernel(GemmArgs g) {
     const int cur = (kt - kt0) & 1;  // buffer 0 holds the first k-step of this split
     // the other buffer was last read in step kt - 1, which every wave has left
     if (kt + 1 < KT) gload((kt + 1) * BK, cur ^ 1);
-    bf16x8 af[2][4], bfr[2][TJ];
+    bf16x8 af[2][MI], bfr[2][TJ];
     frags(cur, 0, af[0], bfr[0]);
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks) {
       if (ks + 1 < BK / 16) frags(cur, ks + 1, af[(ks + 1) & 1], bfr[(ks + 1) & 1]);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < MI; ++i) {
         if (SKIP && 32 * i >= band) continue;
 #pragma unroll
         for (int j = 0; j < TJ; ++j)
@@ -217,7 +225,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_bf16_kernel(GemmArgs g) {
   // ---- epilogue -------------------------------------------------------------------
   // acc[i][j][4*ii + jj] = C[row 32 i + 8 ii + 4 lk + jj][col 32 j + lr] of the wave tile
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < MI; ++i) {
 #pragma unroll
     for (int ii = 0; ii < 4; ++ii) {
 #pragma unroll
@@ -256,21 +264,22 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_bf16_kernel(GemmArgs g) {
   }
 }
 
-static size_t gemm_lds_bytes() { return (size_t)2 * (BM + BN) * BK * 2; }
+static size_t gemm_lds_bytes(int tr = BM) { return (size_t)2 * (tr + BN) * BK * 2; }
 
-template <int EPI, bool SKIP = false, int WAVES = kGemmWaves>
+template <int EPI, bool SKIP = false, int TR = BM, int WAVES = kGemmWaves>
 static int launch(const GemmArgs& a, int grid_n, int grid_m, hipStream_t st, int splits = 1) {
   static bool attr_set = false;
   if (!attr_set) {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_bf16_kernel<EPI, WAVES, SKIP>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)gemm_lds_bytes());
+    (void)hipFuncSetAttribute(
+        reinterpret_cast<const void*>(&gemm_bf16_kernel<EPI, WAVES, SKIP, TR>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, (int)gemm_lds_bytes(TR));
     attr_set = true;
   }
   GemmArgs g = a;
   g.tiles_m = grid_m;
   g.tiles_n = grid_n;
-  hipLaunchKernelGGL((gemm_bf16_kernel<EPI, WAVES, SKIP>), dim3(grid_m * grid_n, splits),
-                     dim3(WAVES * 64), gemm_lds_bytes(), st, g);
+  hipLaunchKernelGGL((gemm_bf16_kernel<EPI, WAVES, SKIP, TR>), dim3(grid_m * grid_n, splits),
+                     dim3(WAVES * 64), gemm_lds_bytes(TR), st, g);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
@@ -363,11 +372,12 @@ int launch_gemm_swiglu(int M, int F, int K, const uint16_t* A, int lda, const in
     const int s = gemm_splits(M, 2 * F, K);
     if (s > 1 && part) return launch_split<EPI_SWIGLU>(a, s, part, st);
   }
+  const int gn = (2 * F + BN - 1) / BN;
+  if (seg_off && gemm_grouped_rows(M, E) == 32)
+    return launch<EPI_SWIGLU, true, 32>(a, gn, max_mtiles, st);
   const int gm = seg_off ? max_mtiles : (M + BM - 1) / BM;
-  // grouped segments averaging under half a tile of rows: mostly empty tiles
-  const bool sparse = seg_off ? (long long)M < (long long)E * (BM / 2) : M <= BM / 2;
-  if (sparse) return launch<EPI_SWIGLU, true>(a, (2 * F + BN - 1) / BN, gm, st);
-  return launch<EPI_SWIGLU>(a, (2 * F + BN - 1) / BN, gm, st);
+  if (!seg_off && M <= BM / 2) return launch<EPI_SWIGLU, true>(a, gn, gm, st);
+  return launch<EPI_SWIGLU>(a, gn, gm, st);
 }
 
 int launch_gemm_f32(int M, int N, int K, const uint16_t* A, int lda, const uint16_t* B,
@@ -377,12 +387,17 @@ int launch_gemm_f32(int M, int N, int K, const uint16_t* A, int lda, const uint1
   a.A = A; a.B = B; a.M = M; a.N = N; a.K = K; a.lda = lda; a.ldb = K;
   a.seg_off = seg_off; a.tile_off = tile_off; a.E = E; a.b_expert_stride = b_stride;
   a.out = out; a.ldo = ldo; a.n1 = N;
+  const int gn = (N + BN - 1) / BN;
+  if (seg_off && gemm_grouped_rows(M, E) == 32)
+    return launch<EPI_F32, true, 32>(a, gn, max_mtiles, st);
   const int gm = seg_off ? max_mtiles : (M + BM - 1) / BM;
-  const bool sparse = seg_off ? (long long)M < (long long)E * (BM / 2) : M <= BM / 2;
-  if (sparse) return launch<EPI_F32, true>(a, (N + BN - 1) / BN, gm, st);
-  return launch<EPI_F32>(a, (N + BN - 1) / BN, gm, st);
+  if (!seg_off && M <= BM / 2) return launch<EPI_F32, true>(a, gn, gm, st);
+  return launch<EPI_F32>(a, gn, gm, st);
 }
 
-int gemm_tile_rows() { return BM; }
+// Tile rows of the grouped expert GEMMs for M (token, slot) rows over E
+// experts: 32 when the segments average at most 16 rows (a batch of decode
+// steps), else 256. The routing permutation is built with the same value.
+int gemm_grouped_rows(int M, int E) { return (long long)M <= 16LL * E ? 32 : BM; }
 
 }  // namespace beam

@@ -15,7 +15,7 @@ float64 brute force on tiny shapes. The composition of the whole layer has no
 worked example on the pages: parity unpinned beyond its stages, which are
 each pinned, and the invariants (chunking, MoE <-> dense identity) tested.
 """
-from . import accounting, layer, numerics  # noqa: F401
+from . import accounting, layer, mx, numerics  # noqa: F401
 from .layer import (KVCache, attention, boundary, dense_ffn, kv_write,  # noqa: F401
                     layer_forward, moe, o_proj, output_gate, qk_norm_position,
                     qkvg_projection, rms_norm, rope, router, scaled_residual,

@@ -44,6 +44,8 @@ def parse():
     ap.add_argument("--no-nope", action="store_true", help="skip the NoPE fp8 decode leg")
     ap.add_argument("--no-flint", action="store_true",
                     help="skip the second model's batch-128 decode legs")
+    ap.add_argument("--no-mx", action="store_true",
+                    help="skip the SWA decode leg with block-scaled FP8 experts")
     ap.add_argument("--prefill-reps", type=int, default=3)
     ap.add_argument("--cpu-steps", type=int, default=16)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -58,7 +60,7 @@ def parse():
 class LayerSet:
     """One layer's weights and KV cache on the device (random-init, seeded)."""
 
-    def __init__(self, dims, seed, layer, ctx, Lmax, kv="bf16"):
+    def __init__(self, dims, seed, layer, ctx, Lmax, kv="bf16", experts="bf16"):
         import numpy as np
         import torch
 
@@ -79,6 +81,16 @@ class LayerSet:
             synth.torch_normal_bf16((2 * dims.F, dims.D), 0.02, seed, layer, "w13", e, out=w13[e])
             synth.torch_normal_bf16((dims.D, dims.F), 0.02, seed, layer, "w2", e, out=w2[e])
         self.t["w13"], self.t["w2"] = w13, w2
+        if experts == "mxfp8":          # block-scaled copies replace the bf16 experts
+            E, F, D = dims.E, dims.F, dims.D
+            U8 = dict(dtype=torch.uint8, device="cuda")
+            self.mx = (torch.empty((E, 2 * F, D), **U8), torch.empty((E, 2 * F, D // 32), **U8),
+                       torch.empty((E, D, F), **U8), torch.empty((E, D, F // 32), **U8))
+            B.beam_mxfp8_quantize(w13, E * 2 * F, D, self.mx[0], self.mx[1])
+            B.beam_mxfp8_quantize(w2, E * D, F, self.mx[2], self.mx[3])
+            torch.cuda.synchronize()
+            B.beam_check()
+            del self.t["w13"], self.t["w2"], w13, w2
         K, V, ks, vs = synth.torch_kv_prior(dims, 1, ctx, kv, seed, layer)
         ct = torch.int16 if kv == "bf16" else torch.uint8
         self.K = torch.empty((1, dims.Hkv, Lmax, dims.d), dtype=ct, device="cuda")
@@ -192,6 +204,27 @@ def main():
             nope.pop(k)
         out["decode_nope"] = nope
         torch.cuda.empty_cache()
+    if not a.no_mx:
+        mxr = decode_leg(a, 1, "mxfp8")
+        msets, x2m, idxm = mxr.pop("_sets"), mxr.pop("_x2"), mxr.pop("_idx")
+        for k in ("_dims", "_ex"):
+            mxr.pop(k)
+        # the two block-scaled expert kernels alone, alternating weight sets
+        wm = torch.full((1, dims.topk), 0.125, dtype=torch.float32, device="cuda")
+        ym = torch.empty((1, D), **I16)
+        wsm = torch.zeros(B.beam_workspace_size(dims, B.BEAM_OP_MOE, 1), dtype=torch.uint8,
+                          device="cuda")
+        moe_us = graph_us(lambda i: B.beam_moe_swiglu_combine_mxfp8(
+            dims, 1, x2m, idxm, wm, *msets[i % 2].mx, ym, wsm), 40)
+        moe_bytes = dims.topk * 3 * dims.F * D * 33 // 32
+        moe_gbs = moe_bytes / (moe_us * 1e-6) / 1e9
+        log(f"[bench] block-scaled expert kernels: {moe_us:.2f} us per call, {moe_gbs:.0f} GB/s")
+        mxr["experts_call"] = {"us": round(moe_us, 3), "bytes": moe_bytes,
+                               "achieved_gbs": round(moe_gbs, 1),
+                               "frac": round(moe_gbs / HBM_PEAK_GBS, 4)}
+        out["decode_swa_mxfp8_experts"] = mxr
+        del msets
+        torch.cuda.empty_cache()
     if not a.no_flint:
         out["decode_flint_b128"] = {m: flint_leg(a, m) for m in ("swa", "nope")}
         torch.cuda.empty_cache()
@@ -204,11 +237,37 @@ def main():
     print(json.dumps(out))
 
 
-def decode_leg(a, ci):
+def graph_us(fn, reps):
+    """Mean µs of one fn(i) call: reps calls captured in one HIP graph, the
+    graph replayed five times between two events on the current stream."""
+    import torch
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(g, stream=stream):
+            for i in range(reps):
+                fn(i)
+    torch.cuda.current_stream().wait_stream(stream)
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    s = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(s)
+    for _ in range(5):
+        g.replay()
+    e1.record(s)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1000.0 / (5 * reps)
+
+
+def decode_leg(a, ci, experts="bf16"):
     """Batch-1 decode layer-steps of config ci (1: SWA layer 10 on a 100K bf16
     cache; 2: NoPE layer 11 on a 100K fp8 cache), chained 8 per HIP graph over
     two alternating full weight sets. Each graph replay is timed on its own
-    (HIP events between replays) for the mean, median and p90 per step."""
+    (HIP events between replays) for the mean, median and p90 per step.
+    experts "mxfp8": the routed experts run from block-scaled FP8 copies."""
     import numpy as np
     import torch
 
@@ -218,8 +277,8 @@ def decode_leg(a, ci):
     dims, ex = cfg.dims, cfg.extra
     pos0, Lmax, n, mode, kvt = ex["pos"], ex["Lmax"], ex["n"], ex["mode"], ex["kv"]
     t0 = time.time()
-    sets = [LayerSet(dims, seed, ex["layer"], pos0, Lmax, kvt) for seed in (0, 1)]
-    log(f"[bench] {mode} decode: weights + caches drawn in {time.time() - t0:.1f}s "
+    sets = [LayerSet(dims, seed, ex["layer"], pos0, Lmax, kvt, experts) for seed in (0, 1)]
+    log(f"[bench] {mode} decode ({experts} experts): weights + caches drawn in {time.time() - t0:.1f}s "
         f"({torch.cuda.memory_allocated() / 2**30:.1f} GiB)")
     I16 = dict(dtype=torch.int16, device="cuda")
     D = dims.D
@@ -258,8 +317,11 @@ def decode_leg(a, ci):
         B.beam_boundary_router_fp32_grouped_topk(dims, 1, y, t["w_attn_post"], h, t["w_ffn_pre"],
                                                  x2, n, t["w_r"], t["b_corr"], idx, w, None,
                                                  ws_r)
-        B.beam_moe_swiglu_combine(dims, 1, x2, idx, w, t["w13"], t["w2"], None, None, y2,
-                                  ws_moe)
+        if experts == "mxfp8":
+            B.beam_moe_swiglu_combine_mxfp8(dims, 1, x2, idx, w, *L.mx, y2, ws_moe)
+        else:
+            B.beam_moe_swiglu_combine(dims, 1, x2, idx, w, t["w13"], t["w2"], None, None, y2,
+                                      ws_moe)
         B.beam_boundary_norm_residual(dims, 1, y2, t["w_ffn_post"], h, t["w_next_pre"], x, n + 1)
 
     # layer entry pre-norm once; then validate one eager chain
@@ -313,10 +375,14 @@ def decode_leg(a, ci):
     kv_read = dims.window if mode == "swa" else pos0 + 1
     kv_bytes = kv_read * dims.Hkv * dims.d * 2 * (2 if kvt == "bf16" else 1)
     kv_write = dims.Hkv * dims.d * 2 * (2 if kvt == "bf16" else 1)
+    # selected experts: 2 bytes per bf16 weight; 1 + 1/32 per block-scaled one
+    expert_bytes = (dims.topk * 3 * dims.F * D * 2 if experts == "bf16"
+                    else dims.topk * 3 * dims.F * D * 33 // 32)
     step_bytes = (dims.qkvg_rows * D * 2 + D * dims.Hq * dims.d * 2 + dims.E * D * 4
-                  + dims.topk * 3 * dims.F * D * 2 + kv_bytes + kv_write)
+                  + expert_bytes + kv_bytes + kv_write)
     del graph
-    res = {"workload": f"beam_{mode}_moe_layer_decode", "kv_cache": kvt, "context": pos0,
+    res = {"workload": f"beam_{mode}_moe_layer_decode", "kv_cache": kvt, "experts": experts,
+           "context": pos0,
            "steps": steps, "warmup": wreps * a.chain + a.chain,
            "us_mean": round(us_step, 3), "us_median": round(float(np.median(per)), 3),
            "us_p90": round(float(np.percentile(per, 90)), 3), "bytes_per_step": step_bytes,

@@ -248,6 +248,35 @@ int beam_moe_experts_down(const beam_dims* dims, int T, const int32_t* idx, cons
                           const uint16_t* w2, const uint16_t* shared_w2, const uint16_t* act,
                           uint16_t* y, void* stream);
 
+/* Block-scaled FP8 experts (MXFP8). The pages run the routed experts in a
+ * 4-bit block format ([MoE]: d_ff 2,560 "NVFP4"); this is the 8-bit member of
+ * the OCP microscaling family: a weight row [K] is stored as K e4m3fn codes
+ * (uint8) and K/32 E8M0 scale bytes, block b = elements [32b, 32b + 32) of
+ * the row, value(code) * 2^(scale - 127). The shared exponent of a block is
+ * floor(log2(max |w|)) - 8 (so max |w| / 2^exp lies in [256, 512)), each code
+ * is w / 2^exp rounded to nearest even and saturated at +-448; an all-zero
+ * block has scale byte 0.
+ *
+ * beam_mxfp8_quantize: w [rows][K] bf16 (device) -> codes [rows][K] and
+ * scales [rows][K/32] (device). Errors: K not a positive multiple of 32. */
+int beam_mxfp8_quantize(const uint16_t* w, size_t rows, int K, uint8_t* codes, uint8_t* scales,
+                        void* stream);
+
+/* beam_moe_swiglu_combine with MXFP8 expert weights, decode steps (T <= 4):
+ * w13_codes [E][2F][D] (gate rows, then up rows) with w13_scales
+ * [E][2F][D/32]; w2_codes [E][D][F] with w2_scales [E][D][F/32]. Maths as
+ * beam_moe_swiglu_combine with every weight replaced by its dequantised value
+ * (dot products in fp32; act and y rounded to bf16 at the same points); no
+ * shared expert. Only the selected experts' codes and scales are read.
+ * ws >= 1024 + T * topk * F * 2 bytes (beam_workspace_size(MOE) suffices).
+ * Errors: T > 4 (UNSUPPORTED); D or F not a multiple of 32, D > 5120,
+ * F > 2560. Expert ids outside [0, E) are skipped and flagged on the device. */
+int beam_moe_swiglu_combine_mxfp8(const beam_dims* dims, int T, const uint16_t* x,
+                                  const int32_t* idx, const float* w, const uint8_t* w13_codes,
+                                  const uint8_t* w13_scales, const uint8_t* w2_codes,
+                                  const uint8_t* w2_scales, uint16_t* y, void* ws,
+                                  size_t ws_bytes, void* stream);
+
 /* Dense SwiGLU MLP of the first layers ([MoE]; [Opt]/7):
  *   u = bf16(x . w13^T) (w13 [2*Fd][D], gate rows then up rows),
  *   a = bf16(silu(u[:Fd]) * u[Fd:]), y = bf16(a . w2^T) (w2 [D][Fd]).

@@ -426,6 +426,61 @@ int beam_boundary_router_fp32_grouped_topk(const beam_dims* dims, int T, const u
                   __func__);
 }
 
+int beam_mxfp8_quantize(const uint16_t* w, size_t rows, int K, uint8_t* codes, uint8_t* scales,
+                        void* stream) {
+  REQ(w);
+  REQ(codes);
+  REQ(scales);
+  ALN(w);
+  ALN(codes);
+  SHAPE(K > 0 && K % 32 == 0, "%s: K must be a positive multiple of 32", __func__);
+  if (rows == 0) return BEAM_OK;
+  const int rc = device_ready();
+  if (rc) return rc;
+  return launched(beam::launch_mxfp8_quantize(w, (long long)rows * (K / 32), codes, scales,
+                                              S_(stream)),
+                  __func__);
+}
+
+int beam_moe_swiglu_combine_mxfp8(const beam_dims* dims, int T, const uint16_t* x,
+                                  const int32_t* idx, const float* w, const uint8_t* w13_codes,
+                                  const uint8_t* w13_scales, const uint8_t* w2_codes,
+                                  const uint8_t* w2_scales, uint16_t* y, void* ws,
+                                  size_t ws_bytes, void* stream) {
+  REQ(dims);
+  REQ(x);
+  REQ(idx);
+  REQ(w);
+  REQ(w13_codes);
+  REQ(w13_scales);
+  REQ(w2_codes);
+  REQ(w2_scales);
+  REQ(y);
+  REQ(ws);
+  ALN(x);
+  ALN(w13_codes);
+  ALN(w2_codes);
+  ALN(y);
+  ALN(ws);
+  SHAPE(T > 0, "%s: T <= 0", __func__);
+  SHAPE(dims->E > 0 && dims->topk > 0 && dims->F > 0, "%s: non-positive E/topk/F", __func__);
+  UNSUP(T <= beam::kGemvMaxT, "%s: block-scaled experts are decode-only (T <= %d)", __func__,
+        beam::kGemvMaxT);
+  UNSUP(dims->D > 0 && dims->D % 32 == 0 && dims->D <= 5120,
+        "%s: D must be a positive multiple of 32 <= 5120", __func__);
+  UNSUP(dims->F % 32 == 0 && dims->F <= 2560, "%s: F must be a multiple of 32 <= 2560",
+        __func__);
+  const size_t need = kCtl + align256((size_t)T * dims->topk * dims->F * 2);
+  if (ws_bytes < need)
+    return fail(BEAM_E_WORKSPACE, "%s: workspace %zu < %zu bytes", __func__, ws_bytes, need);
+  const int rc = device_ready();
+  if (rc) return rc;
+  return launched(beam::launch_moe_mxfp8(T, dims->D, dims->F, dims->E, dims->topk, w13_codes,
+                                         w13_scales, w2_codes, w2_scales, idx, w, x,
+                                         (uint16_t*)ws_data(ws), y, S_(stream)),
+                  __func__);
+}
+
 int beam_moe_swiglu_combine(const beam_dims* dims, int T, const uint16_t* x,
                             const int32_t* idx, const float* w, const uint16_t* w13,
                             const uint16_t* w2, const uint16_t* shared_w13,
@@ -640,7 +695,8 @@ int beam_check(void* stream) {
   hipError_t e = hipStreamSynchronize(S_(stream));
   if (e != hipSuccess) return fail(BEAM_E_HIP, "beam_check: %s", hipGetErrorString(e));
   const int f = beam::gemv_read_clear_err() | beam::qk_read_clear_err() |
-                beam::attn_read_clear_err() | beam::moe_read_clear_err();
+                beam::attn_read_clear_err() | beam::moe_read_clear_err() |
+                beam::mx_read_clear_err();
   if (f < 0) return fail(BEAM_E_HIP, "beam_check: reading the device flags failed");
   if (f)
     return fail(BEAM_E_DEVICE, "beam_check: device check tripped:%s%s%s",

@@ -21,6 +21,13 @@ int launch_gemv_gate_oproj(int T, int N, int K, int hd, const uint16_t* W, const
 int launch_expert_w13(int T, int D, int F, int E, int topk, int spt, const uint16_t* w13,
                       const uint16_t* shared_w13, const int32_t* idx, const uint16_t* X,
                       uint16_t* act, hipStream_t st);
+// block-scaled fp8 (MXFP8) experts, decode steps
+int launch_mxfp8_quantize(const uint16_t* w, long long nblocks, uint8_t* codes, uint8_t* scales,
+                          hipStream_t st);
+int launch_moe_mxfp8(int T, int D, int F, int E, int topk, const uint8_t* w13c,
+                     const uint8_t* w13s, const uint8_t* w2c, const uint8_t* w2s,
+                     const int32_t* idx, const float* wts, const uint16_t* X, uint16_t* act,
+                     uint16_t* Y, hipStream_t st);
 int launch_expert_w2(int T, int D, int F, int E, int topk, int spt, const uint16_t* w2,
                      const uint16_t* shared_w2, const int32_t* idx, const float* wts,
                      const uint16_t* act, uint16_t* Y, hipStream_t st);
@@ -107,5 +114,6 @@ int gemv_read_clear_err();
 int qk_read_clear_err();
 int attn_read_clear_err();
 int moe_read_clear_err();
+int mx_read_clear_err();
 
 }  // namespace beam

@@ -1,0 +1,248 @@
+// Block-scaled FP8 (MXFP8) expert weights for decode steps.
+//
+// The pages run the routed experts in a 4-bit block format ("Reflection Beam
+// 1.0 on vLLM", MoE section; the library MoE path of the optimisation
+// section quantises for it). Here the experts may instead be stored in the OCP
+// microscaling layout with 8-bit elements: every 32 consecutive weights along
+// a row's reduction axis share one E8M0 scale byte s (the value 2^(s - 127)),
+// each weight is an e4m3fn code. The shared exponent of a block is
+// floor(log2(amax)) - 8 (8: the exponent of the largest normal e4m3 value),
+// so amax / 2^exp lies in [256, 512) and magnitudes above 448 clamp.
+//
+//  mxfp8_quantize_kernel        bf16 rows -> codes + scales, one thread per block
+//  expert_w13_swiglu_mx_kernel  gate/up rows of the selected experts with SwiGLU
+//  expert_w2_combine_mx_kernel  down projection of every selected expert and the
+//                               weighted combine in fp32
+// Both GEMVs read half the bytes of their bf16 counterparts (plus 1/32 for the
+// scales); a 16- or 8-code chunk is widened to bf16 exactly with gfx950's
+// packed conversion, its dot product with the activation is taken in fp32 and
+// multiplied by the block's power-of-two scale.
+#include "common.h"
+#include "internal.h"
+
+namespace beam {
+
+BEAM_ERR_FLAG_DECL(mx)
+BEAM_ERR_FLAG_READER(mx)
+
+constexpr int MT = 256;  // threads per workgroup (4 waves)
+
+// 2^(s - 127) for an E8M0 byte s (s = 0 is the binary32 subnormal 2^-127)
+__device__ __forceinline__ float e8m0_value(uint32_t s) {
+  return s ? __uint_as_float(s << 23) : __uint_as_float(0x400000u);
+}
+
+__device__ __forceinline__ uint4 e4m3x8_bits(uint32_t lo, uint32_t hi) {
+  return __builtin_bit_cast(uint4, e4m3x8_to_bf16x8(uint2{lo, hi}));
+}
+
+__global__ __launch_bounds__(MT) void mxfp8_quantize_kernel(const uint16_t* __restrict__ w,
+                                                            long long nblocks,
+                                                            uint8_t* __restrict__ codes,
+                                                            uint8_t* __restrict__ scales) {
+  const long long i = (long long)blockIdx.x * MT + threadIdx.x;
+  if (i >= nblocks) return;
+  const uint16_t* src = w + i * 32;
+  uint32_t v[16];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const uint4 u = ld16(src + q * 8);
+    v[4 * q] = u.x;
+    v[4 * q + 1] = u.y;
+    v[4 * q + 2] = u.z;
+    v[4 * q + 3] = u.w;
+  }
+  // bf16 magnitudes order like their bit patterns; the exponent field of the
+  // largest is floor(log2(amax)) + 127 for normal values
+  uint32_t amax = 0;
+#pragma unroll
+  for (int k = 0; k < 16; ++k) amax = max(amax, max(v[k] & 0x7fffu, (v[k] >> 16) & 0x7fffu));
+  const int eb = (int)(amax >> 7);
+  const int s = eb == 0 ? -127 : max(-127, eb - 127 - 8);
+  const float inv = __uint_as_float((uint32_t)(127 - s) << 23);  // 2^-s, exact scaling
+  uint32_t out[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    uint32_t word = 0;
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      const int el = 4 * k + h;  // element el: half (el & 1) of v[el >> 1]
+      const uint32_t b = (el & 1) ? (v[el >> 1] & 0xffff0000u) : (v[el >> 1] << 16);
+      word |= (uint32_t)f2e4m3(__uint_as_float(b) * inv) << (8 * h);
+    }
+    out[k] = word;
+  }
+  *reinterpret_cast<uint4*>(codes + i * 32) = uint4{out[0], out[1], out[2], out[3]};
+  *reinterpret_cast<uint4*>(codes + i * 32 + 16) = uint4{out[4], out[5], out[6], out[7]};
+  scales[i] = (uint8_t)(s + 127);
+}
+
+// Gate/up rows: workgroup (f block, slot t * topk + k); wave w takes row
+// f = 4 * blockIdx.x + w of expert idx[t][k], gate row f and up row F + f,
+// in 16-code chunks (lane l: chunks l, l + 64, ...). Weights and their scales
+// are requested before the activation row is staged in LDS.
+template <int NB>
+__global__ __launch_bounds__(MT) void expert_w13_swiglu_mx_kernel(
+    const uint8_t* __restrict__ w13c, const uint8_t* __restrict__ w13s,
+    const int32_t* __restrict__ idx, int E, int topk, int F, int D,
+    const uint16_t* __restrict__ X, uint16_t* __restrict__ act) {
+  extern __shared__ __align__(16) uint16_t xs[];
+  const int s = blockIdx.y;
+  const int t = s / topk;
+  const int e = idx[s];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int f = blockIdx.x * 4 + wave;
+  if (e < 0 || e >= E) {
+    if (threadIdx.x == 0 && blockIdx.x == 0) BEAM_RAISE(mx, ERR_EXPERT);
+    if (lane == 0 && f < F) act[(size_t)s * F + f] = 0;
+    return;
+  }
+  const int nc = D >> 4, nb = D >> 5;  // 16-code chunks and 32-code blocks of a row
+  const size_t grow = (size_t)e * 2 * F + min(f, F - 1);
+  const uint8_t* gc = w13c + grow * D;
+  const uint8_t* uc = gc + (size_t)F * D;
+  const uint8_t* gs = w13s + grow * nb;
+  const uint8_t* us = gs + (size_t)F * nb;
+  uint4 gw[NB], uw[NB];
+  uint32_t gsc[NB], usc[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    const int c = lane + 64 * b;
+    const bool ok = c < nc;
+    gw[b] = ok ? ld16_nt(gc + (size_t)c * 16) : uint4{0u, 0u, 0u, 0u};
+    uw[b] = ok ? ld16_nt(uc + (size_t)c * 16) : uint4{0u, 0u, 0u, 0u};
+    gsc[b] = ok ? gs[c >> 1] : 0u;
+    usc[b] = ok ? us[c >> 1] : 0u;
+  }
+  for (int i = threadIdx.x; i < (D >> 3); i += MT)
+    *reinterpret_cast<uint4*>(xs + i * 8) = ld16(X + (size_t)t * D + i * 8);
+  __syncthreads();
+  if (f >= F) return;
+  float ag = 0.f, au = 0.f;
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    const int c = lane + 64 * b;
+    if (c < nc) {
+      const uint4 x0 = *reinterpret_cast<const uint4*>(xs + c * 16);
+      const uint4 x1 = *reinterpret_cast<const uint4*>(xs + c * 16 + 8);
+      const float pg = dot8_bf16(e4m3x8_bits(gw[b].z, gw[b].w), x1,
+                                 dot8_bf16(e4m3x8_bits(gw[b].x, gw[b].y), x0, 0.f));
+      const float pu = dot8_bf16(e4m3x8_bits(uw[b].z, uw[b].w), x1,
+                                 dot8_bf16(e4m3x8_bits(uw[b].x, uw[b].y), x0, 0.f));
+      ag = __builtin_fmaf(pg, e8m0_value(gsc[b]), ag);
+      au = __builtin_fmaf(pu, e8m0_value(usc[b]), au);
+    }
+  }
+  ag = wave_sum(ag);
+  au = wave_sum(au);
+  if (lane == 0) act[(size_t)s * F + f] = f2bf(siluf(round_bf(ag)) * round_bf(au));
+}
+
+// Down projection + weighted combine: workgroup (ROWS output rows, token t);
+// wave w takes slots w, w + 4, ... and accumulates coef * (W2_e[row] . act)
+// in 8-code chunks; the four waves' partials are added in a fixed order and
+// rounded once.
+template <int ROWS, int NA>
+__global__ __launch_bounds__(MT) void expert_w2_combine_mx_kernel(
+    const uint8_t* __restrict__ w2c, const uint8_t* __restrict__ w2s,
+    const int32_t* __restrict__ idx, const float* __restrict__ wts, int E, int topk, int F,
+    int D, const uint16_t* __restrict__ act, uint16_t* __restrict__ Y) {
+  __shared__ float part[4][ROWS];
+  const int t = blockIdx.y;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int d0 = blockIdx.x * ROWS;
+  const int nc = F >> 3, nb = F >> 5;
+  float accr[ROWS] = {};
+  for (int k = wave; k < topk; k += 4) {
+    const int e = idx[t * topk + k];
+    if (e < 0 || e >= E) {
+      if (lane == 0 && blockIdx.x == 0) BEAM_RAISE(mx, ERR_EXPERT);
+      continue;
+    }
+    const uint8_t* wb = w2c + (size_t)e * D * F;
+    const uint8_t* sb = w2s + (size_t)e * D * nb;
+    const uint16_t* ab = act + ((size_t)t * topk + k) * F;
+    const float coef = wts[t * topk + k];
+    uint2 wv[ROWS][NA];
+    uint32_t sc[ROWS][NA];
+#pragma unroll
+    for (int i = 0; i < NA; ++i) {
+      const int c = lane + 64 * i;
+#pragma unroll
+      for (int r = 0; r < ROWS; ++r) {
+        const bool ok = c < nc && d0 + r < D;
+        wv[r][i] = ok ? *reinterpret_cast<const uint2*>(wb + (size_t)(d0 + r) * F + (size_t)c * 8)
+                      : uint2{0u, 0u};
+        sc[r][i] = ok ? sb[(size_t)(d0 + r) * nb + (c >> 2)] : 0u;
+      }
+    }
+    uint4 av[NA];
+#pragma unroll
+    for (int i = 0; i < NA; ++i) {
+      const int c = lane + 64 * i;
+      av[i] = c < nc ? ld16(ab + (size_t)c * 8) : uint4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int r = 0; r < ROWS; ++r) {
+      float a = 0.f;
+#pragma unroll
+      for (int i = 0; i < NA; ++i)
+        a = __builtin_fmaf(dot8_bf16(e4m3x8_bits(wv[r][i].x, wv[r][i].y), av[i], 0.f),
+                           e8m0_value(sc[r][i]), a);
+      accr[r] = __builtin_fmaf(coef, a, accr[r]);
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < ROWS; ++r) accr[r] = wave_sum(accr[r]);
+  if (lane == 0) {
+#pragma unroll
+    for (int r = 0; r < ROWS; ++r) part[wave][r] = accr[r];
+  }
+  __syncthreads();
+  if (threadIdx.x < ROWS && d0 + (int)threadIdx.x < D) {
+    const int r = threadIdx.x;
+    const float v = ((part[0][r] + part[1][r]) + part[2][r]) + part[3][r];
+    Y[(size_t)t * D + d0 + r] = f2bf(v);
+  }
+}
+
+#define LAUNCH_OK() (hipGetLastError() == hipSuccess ? 0 : -1)
+
+int launch_mxfp8_quantize(const uint16_t* w, long long nblocks, uint8_t* codes, uint8_t* scales,
+                          hipStream_t st) {
+  hipLaunchKernelGGL(mxfp8_quantize_kernel, dim3((unsigned)((nblocks + MT - 1) / MT)), dim3(MT),
+                     0, st, w, nblocks, codes, scales);
+  return LAUNCH_OK();
+}
+
+// act: [T * topk][F] bf16 scratch.
+int launch_moe_mxfp8(int T, int D, int F, int E, int topk, const uint8_t* w13c,
+                     const uint8_t* w13s, const uint8_t* w2c, const uint8_t* w2s,
+                     const int32_t* idx, const float* wts, const uint16_t* X, uint16_t* act,
+                     uint16_t* Y, hipStream_t st) {
+  const int nc13 = D / 16, nc2 = F / 8;
+  const dim3 g13((F + 3) / 4, T * topk);
+  const size_t sh = (size_t)D * 2;
+  if (nc13 <= 64)
+    hipLaunchKernelGGL((expert_w13_swiglu_mx_kernel<1>), g13, dim3(MT), sh, st, w13c, w13s, idx,
+                       E, topk, F, D, X, act);
+  else if (nc13 <= 64 * 5)
+    hipLaunchKernelGGL((expert_w13_swiglu_mx_kernel<5>), g13, dim3(MT), sh, st, w13c, w13s, idx,
+                       E, topk, F, D, X, act);
+  else
+    return -2;
+  if (hipGetLastError() != hipSuccess) return -1;
+  constexpr int ROWS = 2;
+  const dim3 g2((D + ROWS - 1) / ROWS, T);
+  if (nc2 <= 64)
+    hipLaunchKernelGGL((expert_w2_combine_mx_kernel<ROWS, 1>), g2, dim3(MT), 0, st, w2c, w2s, idx,
+                       wts, E, topk, F, D, act, Y);
+  else if (nc2 <= 64 * 5)
+    hipLaunchKernelGGL((expert_w2_combine_mx_kernel<ROWS, 5>), g2, dim3(MT), 0, st, w2c, w2s, idx,
+                       wts, E, topk, F, D, act, Y);
+  else
+    return -2;
+  return LAUNCH_OK();
+}
+
+}  // namespace beam

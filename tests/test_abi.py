@@ -20,7 +20,7 @@ MIS = 0x10002        # misaligned
 
 def test_library_exports_every_declared_symbol():
     names = B.header_functions()
-    assert len(names) == 17
+    assert len(names) == 19
     L = ctypes.CDLL(B.LIB_PATH)
     for n in names:
         assert hasattr(L, n), n
@@ -166,3 +166,24 @@ def test_rope_table_host_helper():
     np.testing.assert_array_equal(out[:, dd // 2:], np.sin(ang).astype(np.float32))
     with pytest.raises(B.BeamError):
         B.beam_rope_table(out, L, 31, theta)
+
+@cpu_only
+def test_mxfp8_validation_and_nodev():
+    assert _rc("beam_mxfp8_quantize", None, 4, 64, A, A, None) == -1
+    assert _rc("beam_mxfp8_quantize", A, 4, 48, A, A, None) == -2
+    assert _rc("beam_mxfp8_quantize", MIS, 4, 64, A, A, None) == -4
+    assert _rc("beam_mxfp8_quantize", A, 0, 64, A, A, None) == 0      # nothing to do
+    assert _rc("beam_mxfp8_quantize", A, 4, 64, A, A, None) == -7
+    d = _dims()
+    by = ctypes.byref(d)
+    need = 1024 + 4 * 64 * 2   # counter block + act [1 * topk][F] bf16
+    args = lambda T=1, ws=need, dims=by: [dims, T, A, A, A, A, A, A, A, A, A, ws, None]  # noqa
+    assert _rc("beam_moe_swiglu_combine_mxfp8", *args(dims=None)) == -1
+    assert _rc("beam_moe_swiglu_combine_mxfp8", *args(T=0)) == -2
+    assert _rc("beam_moe_swiglu_combine_mxfp8", *args(T=5)) == -3
+    d2 = _dims(D=272)
+    assert _rc("beam_moe_swiglu_combine_mxfp8", *args(dims=ctypes.byref(d2))) == -3
+    d3 = _dims(F=80)
+    assert _rc("beam_moe_swiglu_combine_mxfp8", *args(dims=ctypes.byref(d3))) == -3
+    assert _rc("beam_moe_swiglu_combine_mxfp8", *args(ws=need - 1)) == -5
+    assert _rc("beam_moe_swiglu_combine_mxfp8", *args()) == -7

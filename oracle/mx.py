@@ -1,5 +1,5 @@
-"""MXFP8 block quantisation of expert weights, written from the OCP
-Microscaling (MX) format definition (test infrastructure only; see
+"""MXFP8 and MXFP4 block quantisation of expert weights, written from the
+OCP Microscaling (MX) format definition (test infrastructure only; see
 oracle/__init__.py).
 
 The pages run the routed experts in a 4-bit block format ("Reflection Beam
@@ -17,6 +17,12 @@ counterpart used here keeps 8-bit elements:
   saturated at +-448 (magnitudes in (448, 512) clamp);
 * the weight a kernel uses is decode(code) * X.
 
+MXFP4 follows the same scheme with E2M1 elements (1 sign, 2 exponent bits with
+bias 1, 1 mantissa bit: magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6): s =
+floor(log2(amax)) - 2 (2 = the exponent of the largest E2M1 value), so amax / X
+lies in [4, 8) and magnitudes above 6 clamp; two codes share a byte, element 2i
+in the low nibble and 2i + 1 in the high one.
+
 w / X is exact (X is a power of two inside the float64 range), so the only
 rounding is the E4M3 encoding, the same in any precision that holds w.
 """
@@ -29,15 +35,17 @@ from .numerics import e4m3_decode, e4m3_encode
 F64 = np.float64
 BLOCK = 32
 E4M3_EMAX = 8
+E2M1_EMAX = 2
 
 
-def shared_exponents(w) -> np.ndarray:
-    """Scale exponent s of every 32-element block along the last axis."""
+def shared_exponents(w, emax: int = E4M3_EMAX) -> np.ndarray:
+    """Scale exponent s of every 32-element block along the last axis, for an
+    element format whose largest value has exponent emax."""
     w = np.asarray(w, dtype=F64)
     assert w.shape[-1] % BLOCK == 0, "K must be a multiple of 32"
     amax = np.abs(w.reshape(*w.shape[:-1], w.shape[-1] // BLOCK, BLOCK)).max(axis=-1)
     _, e = np.frexp(np.where(amax > 0, amax, 1.0))   # 2**(e-1) <= amax < 2**e
-    s = (e - 1) - E4M3_EMAX
+    s = (e - 1) - emax
     s = np.where(amax > 0, s, -127)
     return np.clip(s, -127, 127).astype(np.int64)
 
@@ -56,4 +64,64 @@ def mxfp8_dequantize(codes, scales) -> np.ndarray:
     c = np.asarray(codes, dtype=np.uint8)
     s = np.asarray(scales, dtype=np.int64) - 127
     v = e4m3_decode(c).reshape(*c.shape[:-1], -1, BLOCK)
+    return np.ldexp(v, s[..., None]).reshape(c.shape)
+
+
+# ---------------------------------------------------------------------------
+# E2M1 elements (MXFP4)
+# ---------------------------------------------------------------------------
+
+def e2m1_magnitudes() -> np.ndarray:
+    """Value of the magnitude codes 0..7 from the field layout: exponent field
+    e (bias 1) and mantissa bit m give m / 2 for e = 0 (subnormal) and
+    (1 + m / 2) * 2^(e - 1) otherwise."""
+    v = []
+    for code in range(8):
+        e, m = code >> 1, code & 1
+        v.append(m / 2.0 if e == 0 else (1.0 + m / 2.0) * 2.0 ** (e - 1))
+    return np.array(v, F64)
+
+
+def e2m1_decode(codes) -> np.ndarray:
+    c = np.asarray(codes, dtype=np.int64)
+    v = e2m1_magnitudes()[c & 7]
+    return np.where(c & 8, -v, v)
+
+
+def e2m1_encode(x) -> np.ndarray:
+    """Nearest E2M1 value, ties to the even code, magnitudes above 6 saturate."""
+    x = np.asarray(x, dtype=F64)
+    a = np.minimum(np.abs(x), 6.0)
+    mags = e2m1_magnitudes()
+    d = np.abs(a[..., None] - mags)
+    c = np.argmin(d, axis=-1)                       # lowest code among equals
+    nxt = np.minimum(c + 1, 7)
+    tie = (c < 7) & (np.take_along_axis(d, nxt[..., None], -1)[..., 0] ==
+                     np.take_along_axis(d, c[..., None], -1)[..., 0])
+    c = np.where(tie & (c & 1 == 1), c + 1, c)
+    return (c | np.where(np.signbit(x), 8, 0)).astype(np.uint8)
+
+
+def mxfp4_quantize(w):
+    """(packed codes uint8 [..., K/2], scales uint8 [..., K/32]) of w [..., K]."""
+    w = np.asarray(w, dtype=F64)
+    s = shared_exponents(w, E2M1_EMAX)
+    x = np.ldexp(w.reshape(*w.shape[:-1], -1, BLOCK), -s[..., None])
+    c = e2m1_encode(x).reshape(w.shape).astype(np.uint8)
+    packed = c[..., 0::2] | (c[..., 1::2] << 4)
+    return packed.astype(np.uint8), (s + 127).astype(np.uint8)
+
+
+def mxfp4_unpack(packed) -> np.ndarray:
+    p = np.asarray(packed, dtype=np.uint8)
+    c = np.empty((*p.shape[:-1], 2 * p.shape[-1]), np.uint8)
+    c[..., 0::2] = p & 0xF
+    c[..., 1::2] = p >> 4
+    return c
+
+
+def mxfp4_dequantize(packed, scales) -> np.ndarray:
+    c = mxfp4_unpack(packed)
+    s = np.asarray(scales, dtype=np.int64) - 127
+    v = e2m1_decode(c).reshape(*c.shape[:-1], -1, BLOCK)
     return np.ldexp(v, s[..., None]).reshape(c.shape)

@@ -1,6 +1,7 @@
-"""Pins of the MXFP8 block codec (oracle/mx.py) against its definition: closed
-forms of the shared exponent, exact round trips of representable blocks,
-brute-force nearest-value search, the error bound, saturation and zero blocks."""
+"""Pins of the MXFP8 and MXFP4 block codecs (oracle/mx.py) against their
+definition: closed forms of the shared exponent, the E2M1 value set, exact
+round trips of representable blocks, nearest-value search by brute force and by
+midpoints, the error bound, saturation, zero blocks and the nibble order."""
 import numpy as np
 
 from oracle import mx
@@ -75,3 +76,81 @@ def test_error_bound_and_saturation():
     c, s = mx.mxfp8_quantize(block)
     assert int(s[0]) - 127 == -8 and c[0] == 0x7E
     assert mx.mxfp8_dequantize(c, s)[0] == 448.0 / 256.0
+
+
+# ------------------------------------------------------------------ MXFP4 (E2M1)
+def test_e2m1_value_set():
+    # OCP MX: E2M1 has max normal 6.0, min normal 1.0, min subnormal 0.5
+    v = mx.e2m1_decode(np.arange(16))
+    assert list(v[:8]) == [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+    assert list(v[8:]) == [-0.0, -0.5, -1.0, -1.5, -2.0, -3.0, -4.0, -6.0]
+    assert np.signbit(v[8])
+    for c in range(16):                                         # exact round trip
+        assert mx.e2m1_encode(v[c]) == c
+
+
+def test_e2m1_nearest_by_midpoints():
+    """Independent of the encoder's search: a magnitude's code is the number of
+    midpoints between consecutive values that lie below it; on a midpoint the
+    even code (zero mantissa bit) wins; above 6 the code saturates."""
+    mids = [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0]
+    g = np.random.default_rng(3)
+    a = np.concatenate([g.uniform(0, 9, 4000), mids, [0.0, 6.0, 7.999, 1e9]])
+    for x in a:
+        if x in mids:                                            # between codes i and i+1
+            i = mids.index(x)
+            c = i if i % 2 == 0 else i + 1
+        else:
+            c = sum(x > m for m in mids)
+        assert mx.e2m1_encode(x) == c, x
+        assert mx.e2m1_encode(-x) == c | 8, x
+
+
+def test_mxfp4_shared_exponent_and_zero_block():
+    # s = floor(log2(amax)) - 2
+    for amax, s in {1.0: -2, 6.0: 0, 7.9: 0, 8.0: 1, 0.02: -8, 2.0 ** -126: -127}.items():
+        block = np.zeros(32)
+        block[11] = -amax
+        assert mx.shared_exponents(block, mx.E2M1_EMAX)[0] == s, (amax, s)
+    p, sc = mx.mxfp4_quantize(np.zeros((3, 64)))
+    assert p.shape == (3, 32) and sc.shape == (3, 2)
+    assert np.all(p == 0) and np.all(sc == 0)
+    assert np.all(mx.mxfp4_dequantize(p, sc) == 0)
+
+
+def test_mxfp4_nibble_order_and_round_trip():
+    g = np.random.default_rng(4)
+    for s in (-12, -3, 0, 7):
+        c = g.integers(0, 16, size=(5, 96))
+        c[:, 0] = 7                                              # 6: the block max sets X
+        c[:, 32] = 15
+        c[:, 64] = 7
+        w = np.ldexp(mx.e2m1_decode(c), s)
+        p, sc = mx.mxfp4_quantize(w)
+        assert np.all(sc.astype(int) - 127 == s)
+        assert np.all(p == ((c[:, 0::2] & 15) | ((c[:, 1::2] & 15) << 4)))
+        np.testing.assert_array_equal(mx.mxfp4_dequantize(p, sc), w)
+    w = np.zeros(32)
+    w[0], w[1] = 6.0, -0.5                                       # X = 1
+    p, _ = mx.mxfp4_quantize(w)
+    assert p[0] == 0x7 | (0x9 << 4)
+
+
+def test_mxfp4_error_bound_and_saturation():
+    g = np.random.default_rng(5)
+    w = g.standard_normal((16, 256)) * 0.02
+    p, sc = mx.mxfp4_quantize(w)
+    d = mx.mxfp4_dequantize(p, sc)
+    X = np.repeat(2.0 ** (sc.astype(int) - 127), 32, axis=1)
+    x = np.abs(w) / X
+    err = np.abs(d - w) / X
+    assert np.all(x < 8)
+    half_step = np.where(x < 2, 0.25, np.where(x < 4, 0.5, 1.0))
+    ok = x <= 6
+    assert np.all(err[ok] <= half_step[ok])
+    assert np.all(err[~ok] == x[~ok] - 6)                         # saturated to 6
+    block = np.full(32, 0.5)
+    block[0] = 7.5                                               # X = 1, 7.5 -> 6
+    p, s = mx.mxfp4_quantize(block)
+    assert int(s[0]) == 127 and (p[0] & 15) == 7
+    assert mx.mxfp4_dequantize(p, s)[0] == 6.0

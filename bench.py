@@ -45,7 +45,7 @@ def parse():
     ap.add_argument("--no-flint", action="store_true",
                     help="skip the second model's batch-128 decode legs")
     ap.add_argument("--no-mx", action="store_true",
-                    help="skip the SWA decode leg with block-scaled FP8 experts")
+                    help="skip the SWA decode legs with block-scaled (MXFP8, MXFP4) experts")
     ap.add_argument("--prefill-reps", type=int, default=3)
     ap.add_argument("--cpu-steps", type=int, default=16)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -81,13 +81,16 @@ class LayerSet:
             synth.torch_normal_bf16((2 * dims.F, dims.D), 0.02, seed, layer, "w13", e, out=w13[e])
             synth.torch_normal_bf16((dims.D, dims.F), 0.02, seed, layer, "w2", e, out=w2[e])
         self.t["w13"], self.t["w2"] = w13, w2
-        if experts == "mxfp8":          # block-scaled copies replace the bf16 experts
+        if experts != "bf16":           # block-scaled copies replace the bf16 experts
             E, F, D = dims.E, dims.F, dims.D
             U8 = dict(dtype=torch.uint8, device="cuda")
-            self.mx = (torch.empty((E, 2 * F, D), **U8), torch.empty((E, 2 * F, D // 32), **U8),
-                       torch.empty((E, D, F), **U8), torch.empty((E, D, F // 32), **U8))
-            B.beam_mxfp8_quantize(w13, E * 2 * F, D, self.mx[0], self.mx[1])
-            B.beam_mxfp8_quantize(w2, E * D, F, self.mx[2], self.mx[3])
+            cpb = 1 if experts == "mxfp8" else 2          # codes per byte
+            self.mx = (torch.empty((E, 2 * F, D // cpb), **U8),
+                       torch.empty((E, 2 * F, D // 32), **U8),
+                       torch.empty((E, D, F // cpb), **U8), torch.empty((E, D, F // 32), **U8))
+            quant = getattr(B, f"beam_{experts}_quantize")
+            quant(w13, E * 2 * F, D, self.mx[0], self.mx[1])
+            quant(w2, E * D, F, self.mx[2], self.mx[3])
             torch.cuda.synchronize()
             B.beam_check()
             del self.t["w13"], self.t["w2"], w13, w2
@@ -204,8 +207,8 @@ def main():
             nope.pop(k)
         out["decode_nope"] = nope
         torch.cuda.empty_cache()
-    if not a.no_mx:
-        mxr = decode_leg(a, 1, "mxfp8")
+    for fmt in ([] if a.no_mx else ["mxfp8", "mxfp4"]):
+        mxr = decode_leg(a, 1, fmt)
         msets, x2m, idxm = mxr.pop("_sets"), mxr.pop("_x2"), mxr.pop("_idx")
         for k in ("_dims", "_ex"):
             mxr.pop(k)
@@ -214,15 +217,15 @@ def main():
         ym = torch.empty((1, D), **I16)
         wsm = torch.zeros(B.beam_workspace_size(dims, B.BEAM_OP_MOE, 1), dtype=torch.uint8,
                           device="cuda")
-        moe_us = graph_us(lambda i: B.beam_moe_swiglu_combine_mxfp8(
-            dims, 1, x2m, idxm, wm, *msets[i % 2].mx, ym, wsm), 40)
-        moe_bytes = dims.topk * 3 * dims.F * D * 33 // 32
+        call = getattr(B, f"beam_moe_swiglu_combine_{fmt}")
+        moe_us = graph_us(lambda i: call(dims, 1, x2m, idxm, wm, *msets[i % 2].mx, ym, wsm), 40)
+        moe_bytes = dims.topk * 3 * dims.F * D * EXPERT_BYTES_PER_32[fmt] // 32
         moe_gbs = moe_bytes / (moe_us * 1e-6) / 1e9
-        log(f"[bench] block-scaled expert kernels: {moe_us:.2f} us per call, {moe_gbs:.0f} GB/s")
+        log(f"[bench] {fmt} expert kernels: {moe_us:.2f} us per call, {moe_gbs:.0f} GB/s")
         mxr["experts_call"] = {"us": round(moe_us, 3), "bytes": moe_bytes,
                                "achieved_gbs": round(moe_gbs, 1),
                                "frac": round(moe_gbs / HBM_PEAK_GBS, 4)}
-        out["decode_swa_mxfp8_experts"] = mxr
+        out[f"decode_swa_{fmt}_experts"] = mxr
         del msets
         torch.cuda.empty_cache()
     if not a.no_flint:
@@ -235,6 +238,10 @@ def main():
             cpu_set = LayerSet(dims, 0, ex["layer"], ex["pos"], ex["Lmax"])
         out["cpu_baseline"] = cpu_baseline(cpu_set, dims, ex, a.cpu_steps)
     print(json.dumps(out))
+
+
+# bytes per 32 expert weights: bf16; e4m3 codes + one scale; e2m1 codes + one scale
+EXPERT_BYTES_PER_32 = {"bf16": 64, "mxfp8": 33, "mxfp4": 17}
 
 
 def graph_us(fn, reps):
@@ -267,7 +274,7 @@ def decode_leg(a, ci, experts="bf16"):
     cache; 2: NoPE layer 11 on a 100K fp8 cache), chained 8 per HIP graph over
     two alternating full weight sets. Each graph replay is timed on its own
     (HIP events between replays) for the mean, median and p90 per step.
-    experts "mxfp8": the routed experts run from block-scaled FP8 copies."""
+    experts "mxfp8" / "mxfp4": the routed experts run from block-scaled copies."""
     import numpy as np
     import torch
 
@@ -306,6 +313,7 @@ def decode_leg(a, ci, experts="bf16"):
                                         dtype=torch.uint8, device="cuda")
     ws_qkv, ws_attn = wsz(B.BEAM_OP_QKV), wsz(attn_op, pos0 + 1)
     ws_r, ws_moe = wsz(B.BEAM_OP_ROUTER), wsz(B.BEAM_OP_MOE)
+    moe_mx = getattr(B, f"beam_moe_swiglu_combine_{experts}", None)
 
     def step(L: LayerSet):
         t = L.t
@@ -317,8 +325,8 @@ def decode_leg(a, ci, experts="bf16"):
         B.beam_boundary_router_fp32_grouped_topk(dims, 1, y, t["w_attn_post"], h, t["w_ffn_pre"],
                                                  x2, n, t["w_r"], t["b_corr"], idx, w, None,
                                                  ws_r)
-        if experts == "mxfp8":
-            B.beam_moe_swiglu_combine_mxfp8(dims, 1, x2, idx, w, *L.mx, y2, ws_moe)
+        if experts != "bf16":
+            moe_mx(dims, 1, x2, idx, w, *L.mx, y2, ws_moe)
         else:
             B.beam_moe_swiglu_combine(dims, 1, x2, idx, w, t["w13"], t["w2"], None, None, y2,
                                       ws_moe)
@@ -375,9 +383,7 @@ def decode_leg(a, ci, experts="bf16"):
     kv_read = dims.window if mode == "swa" else pos0 + 1
     kv_bytes = kv_read * dims.Hkv * dims.d * 2 * (2 if kvt == "bf16" else 1)
     kv_write = dims.Hkv * dims.d * 2 * (2 if kvt == "bf16" else 1)
-    # selected experts: 2 bytes per bf16 weight; 1 + 1/32 per block-scaled one
-    expert_bytes = (dims.topk * 3 * dims.F * D * 2 if experts == "bf16"
-                    else dims.topk * 3 * dims.F * D * 33 // 32)
+    expert_bytes = dims.topk * 3 * dims.F * D * EXPERT_BYTES_PER_32[experts] // 32
     step_bytes = (dims.qkvg_rows * D * 2 + D * dims.Hq * dims.d * 2 + dims.E * D * 4
                   + expert_bytes + kv_bytes + kv_write)
     del graph

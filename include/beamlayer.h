@@ -277,6 +277,26 @@ int beam_moe_swiglu_combine_mxfp8(const beam_dims* dims, int T, const uint16_t* 
                                   const uint8_t* w2_scales, uint16_t* y, void* ws,
                                   size_t ws_bytes, void* stream);
 
+/* MXFP4: the same scheme with e2m1 elements (1 sign bit, 2 exponent bits with
+ * bias 1, 1 mantissa bit: magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6), the format
+ * family of the pages' 4-bit experts ([MoE]). Shared exponent of a block =
+ * floor(log2(max |w|)) - 2 (max |w| / 2^exp in [4, 8)); codes round to nearest
+ * even and saturate at +-6; two codes per byte, element 2i in the low nibble.
+ *
+ * beam_mxfp4_quantize: w [rows][K] bf16 (device) -> codes [rows][K/2] and
+ * scales [rows][K/32] (device). Errors: K not a positive multiple of 32. */
+int beam_mxfp4_quantize(const uint16_t* w, size_t rows, int K, uint8_t* codes, uint8_t* scales,
+                        void* stream);
+
+/* beam_moe_swiglu_combine_mxfp8 with MXFP4 expert weights: w13_codes
+ * [E][2F][D/2], w13_scales [E][2F][D/32], w2_codes [E][D][F/2], w2_scales
+ * [E][D][F/32]. Same maths, sizes, workspace and errors. */
+int beam_moe_swiglu_combine_mxfp4(const beam_dims* dims, int T, const uint16_t* x,
+                                  const int32_t* idx, const float* w, const uint8_t* w13_codes,
+                                  const uint8_t* w13_scales, const uint8_t* w2_codes,
+                                  const uint8_t* w2_scales, uint16_t* y, void* ws,
+                                  size_t ws_bytes, void* stream);
+
 /* Dense SwiGLU MLP of the first layers ([MoE]; [Opt]/7):
  *   u = bf16(x . w13^T) (w13 [2*Fd][D], gate rows then up rows),
  *   a = bf16(silu(u[:Fd]) * u[Fd:]), y = bf16(a . w2^T) (w2 [D][Fd]).

@@ -25,6 +25,7 @@ __all__ = [
     "beam_moe_swiglu_combine", "beam_moe_experts_up", "beam_moe_experts_down",
     "beam_dense_swiglu", "beam_workspace_size", "beam_rope_table", "beam_hbm_read",
     "beam_mxfp8_quantize", "beam_moe_swiglu_combine_mxfp8",
+    "beam_mxfp4_quantize", "beam_moe_swiglu_combine_mxfp4",
     "beam_check", "beam_last_error", "beam_version",
     "BEAM_SWA_ROPE", "BEAM_NOPE_SSMAX", "BEAM_KV_BF16", "BEAM_KV_FP8_E4M3",
     "BEAM_OP_QKV", "BEAM_OP_ATTN_SWA", "BEAM_OP_ATTN_NOPE", "BEAM_OP_OUT_GATE",
@@ -92,6 +93,9 @@ def lib():
             "beam_hbm_read": [P, c_size_t, P, P],
             "beam_mxfp8_quantize": [P, c_size_t, c_int, P, P, P],
             "beam_moe_swiglu_combine_mxfp8": [POINTER(beam_dims), c_int, P, P, P, P, P, P, P, P,
+                                              P, c_size_t, P],
+            "beam_mxfp4_quantize": [P, c_size_t, c_int, P, P, P],
+            "beam_moe_swiglu_combine_mxfp4": [POINTER(beam_dims), c_int, P, P, P, P, P, P, P, P,
                                               P, c_size_t, P],
             "beam_check": [P],
             "beam_version": [],
@@ -250,6 +254,18 @@ def beam_moe_swiglu_combine_mxfp8(dims, T, x, idx, w, w13_codes, w13_scales, w2_
     d = _d(dims)
     wp, wb = _ws(ws)
     _call("beam_moe_swiglu_combine_mxfp8", ctypes.byref(d), T, _p(x), _p(idx), _p(w),
+          _p(w13_codes), _p(w13_scales), _p(w2_codes), _p(w2_scales), _p(y), wp, wb, _s(stream))
+
+
+def beam_mxfp4_quantize(w, rows, K, codes, scales, stream=None):
+    _call("beam_mxfp4_quantize", _p(w), rows, K, _p(codes), _p(scales), _s(stream))
+
+
+def beam_moe_swiglu_combine_mxfp4(dims, T, x, idx, w, w13_codes, w13_scales, w2_codes,
+                                  w2_scales, y, ws, stream=None):
+    d = _d(dims)
+    wp, wb = _ws(ws)
+    _call("beam_moe_swiglu_combine_mxfp4", ctypes.byref(d), T, _p(x), _p(idx), _p(w),
           _p(w13_codes), _p(w13_scales), _p(w2_codes), _p(w2_scales), _p(y), wp, wb, _s(stream))
 
 

@@ -426,20 +426,67 @@ int beam_boundary_router_fp32_grouped_topk(const beam_dims* dims, int T, const u
                   __func__);
 }
 
-int beam_mxfp8_quantize(const uint16_t* w, size_t rows, int K, uint8_t* codes, uint8_t* scales,
-                        void* stream) {
-  REQ(w);
-  REQ(codes);
-  REQ(scales);
-  ALN(w);
-  ALN(codes);
-  SHAPE(K > 0 && K % 32 == 0, "%s: K must be a positive multiple of 32", __func__);
+namespace {
+// shared by the MXFP8 and MXFP4 entry points (bits = 8 or 4 per weight)
+int mx_quantize(int bits, const uint16_t* w, size_t rows, int K, uint8_t* codes,
+                uint8_t* scales, void* stream, const char* fn) {
+  if (!w || !codes || !scales) return fail(BEAM_E_NULL, "%s: NULL tensor argument", fn);
+  if (misaligned(w) || misaligned(codes))
+    return fail(BEAM_E_ALIGN, "%s: tensor not 16-byte aligned", fn);
+  if (K <= 0 || K % 32) return fail(BEAM_E_SHAPE, "%s: K must be a positive multiple of 32", fn);
   if (rows == 0) return BEAM_OK;
   const int rc = device_ready();
   if (rc) return rc;
-  return launched(beam::launch_mxfp8_quantize(w, (long long)rows * (K / 32), codes, scales,
-                                              S_(stream)),
-                  __func__);
+  const long long nb = (long long)rows * (K / 32);
+  return launched(bits == 8 ? beam::launch_mxfp8_quantize(w, nb, codes, scales, S_(stream))
+                            : beam::launch_mxfp4_quantize(w, nb, codes, scales, S_(stream)),
+                  fn);
+}
+
+int moe_mx(int bits, const beam_dims* dims, int T, const uint16_t* x, const int32_t* idx,
+           const float* w, const uint8_t* w13_codes, const uint8_t* w13_scales,
+           const uint8_t* w2_codes, const uint8_t* w2_scales, uint16_t* y, void* ws,
+           size_t ws_bytes, void* stream, const char* fn) {
+  if (!dims) return fail(BEAM_E_NULL, "%s: dims is NULL", fn);
+  if (!x || !idx || !w || !w13_codes || !w13_scales || !w2_codes || !w2_scales || !y || !ws)
+    return fail(BEAM_E_NULL, "%s: NULL tensor argument", fn);
+  if (misaligned(x) || misaligned(w13_codes) || misaligned(w2_codes) || misaligned(y) ||
+      misaligned(ws))
+    return fail(BEAM_E_ALIGN, "%s: tensor not 16-byte aligned", fn);
+  if (T <= 0) return fail(BEAM_E_SHAPE, "%s: T <= 0", fn);
+  if (dims->E <= 0 || dims->topk <= 0 || dims->F <= 0)
+    return fail(BEAM_E_SHAPE, "%s: non-positive E/topk/F", fn);
+  if (T > beam::kGemvMaxT)
+    return fail(BEAM_E_UNSUPPORTED, "%s: block-scaled experts are decode-only (T <= %d)", fn,
+                beam::kGemvMaxT);
+  if (!(dims->D > 0 && dims->D % 32 == 0 && dims->D <= 5120))
+    return fail(BEAM_E_UNSUPPORTED, "%s: D must be a positive multiple of 32 <= 5120", fn);
+  if (!(dims->F % 32 == 0 && dims->F <= 2560))
+    return fail(BEAM_E_UNSUPPORTED, "%s: F must be a multiple of 32 <= 2560", fn);
+  const size_t need = kCtl + align256((size_t)T * dims->topk * dims->F * 2);
+  if (ws_bytes < need)
+    return fail(BEAM_E_WORKSPACE, "%s: workspace %zu < %zu bytes", fn, ws_bytes, need);
+  const int rc = device_ready();
+  if (rc) return rc;
+  uint16_t* act = (uint16_t*)ws_data(ws);
+  const hipStream_t st = S_(stream);
+  const int D = dims->D, F = dims->F, E = dims->E, K = dims->topk;
+  return launched(bits == 8 ? beam::launch_moe_mxfp8(T, D, F, E, K, w13_codes, w13_scales,
+                                                     w2_codes, w2_scales, idx, w, x, act, y, st)
+                            : beam::launch_moe_mxfp4(T, D, F, E, K, w13_codes, w13_scales,
+                                                     w2_codes, w2_scales, idx, w, x, act, y, st),
+                  fn);
+}
+}  // namespace
+
+int beam_mxfp8_quantize(const uint16_t* w, size_t rows, int K, uint8_t* codes, uint8_t* scales,
+                        void* stream) {
+  return mx_quantize(8, w, rows, K, codes, scales, stream, __func__);
+}
+
+int beam_mxfp4_quantize(const uint16_t* w, size_t rows, int K, uint8_t* codes, uint8_t* scales,
+                        void* stream) {
+  return mx_quantize(4, w, rows, K, codes, scales, stream, __func__);
 }
 
 int beam_moe_swiglu_combine_mxfp8(const beam_dims* dims, int T, const uint16_t* x,
@@ -447,38 +494,17 @@ int beam_moe_swiglu_combine_mxfp8(const beam_dims* dims, int T, const uint16_t* 
                                   const uint8_t* w13_scales, const uint8_t* w2_codes,
                                   const uint8_t* w2_scales, uint16_t* y, void* ws,
                                   size_t ws_bytes, void* stream) {
-  REQ(dims);
-  REQ(x);
-  REQ(idx);
-  REQ(w);
-  REQ(w13_codes);
-  REQ(w13_scales);
-  REQ(w2_codes);
-  REQ(w2_scales);
-  REQ(y);
-  REQ(ws);
-  ALN(x);
-  ALN(w13_codes);
-  ALN(w2_codes);
-  ALN(y);
-  ALN(ws);
-  SHAPE(T > 0, "%s: T <= 0", __func__);
-  SHAPE(dims->E > 0 && dims->topk > 0 && dims->F > 0, "%s: non-positive E/topk/F", __func__);
-  UNSUP(T <= beam::kGemvMaxT, "%s: block-scaled experts are decode-only (T <= %d)", __func__,
-        beam::kGemvMaxT);
-  UNSUP(dims->D > 0 && dims->D % 32 == 0 && dims->D <= 5120,
-        "%s: D must be a positive multiple of 32 <= 5120", __func__);
-  UNSUP(dims->F % 32 == 0 && dims->F <= 2560, "%s: F must be a multiple of 32 <= 2560",
-        __func__);
-  const size_t need = kCtl + align256((size_t)T * dims->topk * dims->F * 2);
-  if (ws_bytes < need)
-    return fail(BEAM_E_WORKSPACE, "%s: workspace %zu < %zu bytes", __func__, ws_bytes, need);
-  const int rc = device_ready();
-  if (rc) return rc;
-  return launched(beam::launch_moe_mxfp8(T, dims->D, dims->F, dims->E, dims->topk, w13_codes,
-                                         w13_scales, w2_codes, w2_scales, idx, w, x,
-                                         (uint16_t*)ws_data(ws), y, S_(stream)),
-                  __func__);
+  return moe_mx(8, dims, T, x, idx, w, w13_codes, w13_scales, w2_codes, w2_scales, y, ws,
+                ws_bytes, stream, __func__);
+}
+
+int beam_moe_swiglu_combine_mxfp4(const beam_dims* dims, int T, const uint16_t* x,
+                                  const int32_t* idx, const float* w, const uint8_t* w13_codes,
+                                  const uint8_t* w13_scales, const uint8_t* w2_codes,
+                                  const uint8_t* w2_scales, uint16_t* y, void* ws,
+                                  size_t ws_bytes, void* stream) {
+  return moe_mx(4, dims, T, x, idx, w, w13_codes, w13_scales, w2_codes, w2_scales, y, ws,
+                ws_bytes, stream, __func__);
 }
 
 int beam_moe_swiglu_combine(const beam_dims* dims, int T, const uint16_t* x,

@@ -82,6 +82,22 @@ __device__ __forceinline__ float dot8_bf16(uint4 a, uint4 b, float acc) {
   return acc;
 }
 
+// The same sum with gfx950's packed bf16 dot product (two products and the
+// accumulator per instruction, fp32 result): no unpacking of either operand.
+// bf16 x bf16 products are exact in fp32; only the summation order differs
+// from dot8_bf16.
+__device__ __forceinline__ float dot8_bf16_d2(uint4 a, uint4 b, float acc) {
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a.x),
+                                        __builtin_bit_cast(bf16x2, b.x), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a.y),
+                                        __builtin_bit_cast(bf16x2, b.y), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a.z),
+                                        __builtin_bit_cast(bf16x2, b.z), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a.w),
+                                        __builtin_bit_cast(bf16x2, b.w), acc, false);
+  return acc;
+}
+
 // ---- wave reductions (wave64) ------------------------------------------------
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll

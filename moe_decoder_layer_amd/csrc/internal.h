@@ -28,6 +28,13 @@ int launch_moe_mxfp8(int T, int D, int F, int E, int topk, const uint8_t* w13c,
                      const uint8_t* w13s, const uint8_t* w2c, const uint8_t* w2s,
                      const int32_t* idx, const float* wts, const uint16_t* X, uint16_t* act,
                      uint16_t* Y, hipStream_t st);
+// block-scaled fp4 (MXFP4) experts, decode steps
+int launch_mxfp4_quantize(const uint16_t* w, long long nblocks, uint8_t* codes, uint8_t* scales,
+                          hipStream_t st);
+int launch_moe_mxfp4(int T, int D, int F, int E, int topk, const uint8_t* w13c,
+                     const uint8_t* w13s, const uint8_t* w2c, const uint8_t* w2s,
+                     const int32_t* idx, const float* wts, const uint16_t* X, uint16_t* act,
+                     uint16_t* Y, hipStream_t st);
 int launch_expert_w2(int T, int D, int F, int E, int topk, int spt, const uint16_t* w2,
                      const uint16_t* shared_w2, const int32_t* idx, const float* wts,
                      const uint16_t* act, uint16_t* Y, hipStream_t st);

@@ -1,22 +1,28 @@
-// Block-scaled FP8 (MXFP8) expert weights for decode steps.
+// Block-scaled (MX) expert weights for decode steps: MXFP8 and MXFP4.
 //
 // The pages run the routed experts in a 4-bit block format ("Reflection Beam
 // 1.0 on vLLM", MoE section; the library MoE path of the optimisation
 // section quantises for it). Here the experts may instead be stored in the OCP
-// microscaling layout with 8-bit elements: every 32 consecutive weights along
-// a row's reduction axis share one E8M0 scale byte s (the value 2^(s - 127)),
-// each weight is an e4m3fn code. The shared exponent of a block is
-// floor(log2(amax)) - 8 (8: the exponent of the largest normal e4m3 value),
-// so amax / 2^exp lies in [256, 512) and magnitudes above 448 clamp.
+// microscaling layouts: every 32 consecutive weights along a row's reduction
+// axis share one E8M0 scale byte s (the value 2^(s - 127)).
+// MXFP8: each weight is an e4m3fn code; the shared exponent of a block is
+// floor(log2(amax)) - 8 (8: the exponent of the largest normal e4m3 value), so
+// amax / 2^exp lies in [256, 512) and magnitudes above 448 clamp.
+// MXFP4: each weight is an e2m1 code (1 sign, 2 exponent bits with bias 1, 1
+// mantissa bit: magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6), two per byte (element
+// 2i in the low nibble); the shared exponent is floor(log2(amax)) - 2.
 //
-//  mxfp8_quantize_kernel        bf16 rows -> codes + scales, one thread per block
-//  expert_w13_swiglu_mx_kernel  gate/up rows of the selected experts with SwiGLU
-//  expert_w2_combine_mx_kernel  down projection of every selected expert and the
-//                               weighted combine in fp32
-// Both GEMVs read half the bytes of their bf16 counterparts (plus 1/32 for the
-// scales); a 16- or 8-code chunk is widened to bf16 exactly with gfx950's
-// packed conversion, its dot product with the activation is taken in fp32 and
-// multiplied by the block's power-of-two scale.
+//  mxfp8_quantize_kernel / mxfp4_quantize_kernel
+//                          bf16 rows -> codes + scales, one thread per block
+//  expert_w13_swiglu_mx{,4}_kernel
+//                          gate/up rows of the selected experts with SwiGLU
+//  expert_w2_combine_mx{,4}_kernel
+//                          down projection of every selected expert and the
+//                          weighted combine in fp32
+// The GEMVs read 1/2 (MXFP8) or 1/4 (MXFP4) of the bytes of their bf16
+// counterparts, plus 1/32 or 1/64 for the scales; codes are widened to bf16
+// exactly with gfx950's packed conversions, each chunk's dot product with the
+// activation is taken in fp32 and multiplied by the block's power-of-two scale.
 #include "common.h"
 #include "internal.h"
 
@@ -125,10 +131,10 @@ __global__ __launch_bounds__(MT) void expert_w13_swiglu_mx_kernel(
     if (c < nc) {
       const uint4 x0 = *reinterpret_cast<const uint4*>(xs + c * 16);
       const uint4 x1 = *reinterpret_cast<const uint4*>(xs + c * 16 + 8);
-      const float pg = dot8_bf16(e4m3x8_bits(gw[b].z, gw[b].w), x1,
-                                 dot8_bf16(e4m3x8_bits(gw[b].x, gw[b].y), x0, 0.f));
-      const float pu = dot8_bf16(e4m3x8_bits(uw[b].z, uw[b].w), x1,
-                                 dot8_bf16(e4m3x8_bits(uw[b].x, uw[b].y), x0, 0.f));
+      const float pg = dot8_bf16_d2(e4m3x8_bits(gw[b].z, gw[b].w), x1,
+                                 dot8_bf16_d2(e4m3x8_bits(gw[b].x, gw[b].y), x0, 0.f));
+      const float pu = dot8_bf16_d2(e4m3x8_bits(uw[b].z, uw[b].w), x1,
+                                 dot8_bf16_d2(e4m3x8_bits(uw[b].x, uw[b].y), x0, 0.f));
       ag = __builtin_fmaf(pg, e8m0_value(gsc[b]), ag);
       au = __builtin_fmaf(pu, e8m0_value(usc[b]), au);
     }
@@ -187,7 +193,7 @@ __global__ __launch_bounds__(MT) void expert_w2_combine_mx_kernel(
       float a = 0.f;
 #pragma unroll
       for (int i = 0; i < NA; ++i)
-        a = __builtin_fmaf(dot8_bf16(e4m3x8_bits(wv[r][i].x, wv[r][i].y), av[i], 0.f),
+        a = __builtin_fmaf(dot8_bf16_d2(e4m3x8_bits(wv[r][i].x, wv[r][i].y), av[i], 0.f),
                            e8m0_value(sc[r][i]), a);
       accr[r] = __builtin_fmaf(coef, a, accr[r]);
     }
@@ -202,6 +208,209 @@ __global__ __launch_bounds__(MT) void expert_w2_combine_mx_kernel(
   if (threadIdx.x < ROWS && d0 + (int)threadIdx.x < D) {
     const int r = threadIdx.x;
     const float v = ((part[0][r] + part[1][r]) + part[2][r]) + part[3][r];
+    Y[(size_t)t * D + d0 + r] = f2bf(v);
+  }
+}
+
+// ---- MXFP4 -------------------------------------------------------------------
+// e2m1 code of a scaled weight: the magnitude code counts the midpoints between
+// consecutive e2m1 values that lie below |x| (on a midpoint the even code wins:
+// strict comparisons at midpoints below an even code, non-strict below an odd
+// one), saturating at 6; the sign bit is copied (so -0 keeps it).
+__device__ __forceinline__ uint32_t f2e2m1(float x) {
+  const float a = fabsf(x);
+  const uint32_t c = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
+                     (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) +
+                     (uint32_t)(a > 5.0f);
+  return c | ((__float_as_uint(x) >> 28) & 8u);
+}
+
+// Eight e2m1 codes of a word -> eight bf16 (exact, unit scale); byte b holds
+// elements 2b (low nibble) and 2b + 1.
+__device__ __forceinline__ uint4 e2m1x8_bits(uint32_t w) {
+  return uint4{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 0)),
+               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 1)),
+               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 2)),
+               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 3))};
+}
+
+__global__ __launch_bounds__(MT) void mxfp4_quantize_kernel(const uint16_t* __restrict__ w,
+                                                            long long nblocks,
+                                                            uint8_t* __restrict__ codes,
+                                                            uint8_t* __restrict__ scales) {
+  const long long i = (long long)blockIdx.x * MT + threadIdx.x;
+  if (i >= nblocks) return;
+  const uint16_t* src = w + i * 32;
+  uint32_t v[16];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const uint4 u = ld16(src + q * 8);
+    v[4 * q] = u.x;
+    v[4 * q + 1] = u.y;
+    v[4 * q + 2] = u.z;
+    v[4 * q + 3] = u.w;
+  }
+  uint32_t amax = 0;
+#pragma unroll
+  for (int k = 0; k < 16; ++k) amax = max(amax, max(v[k] & 0x7fffu, (v[k] >> 16) & 0x7fffu));
+  const int eb = (int)(amax >> 7);
+  const int s = eb == 0 ? -127 : max(-127, eb - 127 - 2);
+  const float inv = __uint_as_float((uint32_t)(127 - s) << 23);  // 2^-s, exact scaling
+  uint32_t out[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {  // word k: elements 8k .. 8k + 7, nibble n = element 8k + n
+    uint32_t word = 0;
+#pragma unroll
+    for (int n = 0; n < 8; ++n) {
+      const int el = 8 * k + n;
+      const uint32_t b = (el & 1) ? (v[el >> 1] & 0xffff0000u) : (v[el >> 1] << 16);
+      word |= f2e2m1(__uint_as_float(b) * inv) << (4 * n);
+    }
+    out[k] = word;
+  }
+  *reinterpret_cast<uint4*>(codes + i * 16) = uint4{out[0], out[1], out[2], out[3]};
+  scales[i] = (uint8_t)(s + 127);
+}
+
+// Gate/up rows, MXFP4: as expert_w13_swiglu_mx_kernel with 8-byte chunks of
+// 16 codes (half a scaled block: chunk c of a row has scale byte c / 2); wave
+// w takes rows f0 = NR * (4 * blockIdx.x + w) .. + NR - 1.
+template <int NB, int NR>
+__global__ __launch_bounds__(MT) void expert_w13_swiglu_mx4_kernel(
+    const uint8_t* __restrict__ w13c, const uint8_t* __restrict__ w13s,
+    const int32_t* __restrict__ idx, int E, int topk, int F, int D,
+    const uint16_t* __restrict__ X, uint16_t* __restrict__ act) {
+  extern __shared__ __align__(16) uint16_t xs[];
+  const int s = blockIdx.y;
+  const int t = s / topk;
+  const int e = idx[s];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int f0 = (blockIdx.x * 4 + wave) * NR;
+  if (e < 0 || e >= E) {  // uniform over the workgroup
+    if (threadIdx.x == 0 && blockIdx.x == 0) BEAM_RAISE(mx, ERR_EXPERT);
+    if (lane < NR && f0 + lane < F) act[(size_t)s * F + f0 + lane] = 0;
+    return;
+  }
+  const int nc = D >> 4, nb = D >> 5;  // 16-code chunks and 32-code blocks of a row
+  const size_t rb = (size_t)D >> 1;    // bytes of a row
+  uint2 gw[NR][NB], uw[NR][NB];
+  uint32_t gsc[NR][NB], usc[NR][NB];
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    const size_t grow = (size_t)e * 2 * F + min(f0 + r, F - 1);
+    const uint8_t* gc = w13c + grow * rb;
+    const uint8_t* uc = gc + (size_t)F * rb;
+    const uint8_t* gs = w13s + grow * nb;
+    const uint8_t* us = gs + (size_t)F * nb;
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const int c = lane + 64 * b;
+      const bool ok = c < nc;
+      gw[r][b] = ok ? *reinterpret_cast<const uint2*>(gc + (size_t)c * 8) : uint2{0u, 0u};
+      uw[r][b] = ok ? *reinterpret_cast<const uint2*>(uc + (size_t)c * 8) : uint2{0u, 0u};
+      gsc[r][b] = ok ? gs[c >> 1] : 0u;
+      usc[r][b] = ok ? us[c >> 1] : 0u;
+    }
+  }
+  for (int i = threadIdx.x; i < (D >> 3); i += MT)
+    *reinterpret_cast<uint4*>(xs + i * 8) = ld16(X + (size_t)t * D + i * 8);
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    if (f0 + r >= F) break;  // uniform over the wave
+    float ag = 0.f, au = 0.f;
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const int c = lane + 64 * b;
+      if (c < nc) {
+        const uint4 x0 = *reinterpret_cast<const uint4*>(xs + c * 16);
+        const uint4 x1 = *reinterpret_cast<const uint4*>(xs + c * 16 + 8);
+        const float pg = dot8_bf16_d2(e2m1x8_bits(gw[r][b].y), x1,
+                                      dot8_bf16_d2(e2m1x8_bits(gw[r][b].x), x0, 0.f));
+        const float pu = dot8_bf16_d2(e2m1x8_bits(uw[r][b].y), x1,
+                                      dot8_bf16_d2(e2m1x8_bits(uw[r][b].x), x0, 0.f));
+        ag = __builtin_fmaf(pg, e8m0_value(gsc[r][b]), ag);
+        au = __builtin_fmaf(pu, e8m0_value(usc[r][b]), au);
+      }
+    }
+    ag = wave_sum(ag);
+    au = wave_sum(au);
+    if (lane == 0) act[(size_t)s * F + f0 + r] = f2bf(siluf(round_bf(ag)) * round_bf(au));
+  }
+}
+
+// Down projection + weighted combine, MXFP4: as expert_w2_combine_mx_kernel
+// with 8-byte chunks of 16 codes (scale byte c / 2), ROWS output rows per
+// workgroup and NW waves, wave w taking slots w, w + NW, ... (one each when
+// topk <= NW, so every weight load of the workgroup is in flight at once);
+// each act chunk is read once per slot for all ROWS rows.
+template <int ROWS, int NA, int NW>
+__global__ __launch_bounds__(NW * 64) void expert_w2_combine_mx4_kernel(
+    const uint8_t* __restrict__ w2c, const uint8_t* __restrict__ w2s,
+    const int32_t* __restrict__ idx, const float* __restrict__ wts, int E, int topk, int F,
+    int D, const uint16_t* __restrict__ act, uint16_t* __restrict__ Y) {
+  __shared__ float part[NW][ROWS];
+  const int t = blockIdx.y;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int d0 = blockIdx.x * ROWS;
+  const int nc = F >> 4, nb = F >> 5;
+  const size_t rb = (size_t)F >> 1;
+  float accr[ROWS] = {};
+  for (int k = wave; k < topk; k += NW) {
+    const int e = idx[t * topk + k];
+    if (e < 0 || e >= E) {
+      if (lane == 0 && blockIdx.x == 0) BEAM_RAISE(mx, ERR_EXPERT);
+      continue;
+    }
+    const uint8_t* wb = w2c + (size_t)e * D * rb;
+    const uint8_t* sb = w2s + (size_t)e * D * nb;
+    const uint16_t* ab = act + ((size_t)t * topk + k) * F;
+    const float coef = wts[t * topk + k];
+    uint2 wv[ROWS][NA];
+    uint32_t sc[ROWS][NA];
+#pragma unroll
+    for (int r = 0; r < ROWS; ++r) {
+      const int row = min(d0 + r, D - 1);
+#pragma unroll
+      for (int i = 0; i < NA; ++i) {
+        const int c = lane + 64 * i;
+        const bool ok = c < nc;
+        wv[r][i] = ok ? *reinterpret_cast<const uint2*>(wb + (size_t)row * rb + (size_t)c * 8)
+                      : uint2{0u, 0u};
+        sc[r][i] = ok ? sb[(size_t)row * nb + (c >> 1)] : 0u;
+      }
+    }
+    uint4 av[NA][2];
+#pragma unroll
+    for (int i = 0; i < NA; ++i) {
+      const int c = lane + 64 * i;
+      av[i][0] = c < nc ? ld16(ab + (size_t)c * 16) : uint4{0u, 0u, 0u, 0u};
+      av[i][1] = c < nc ? ld16(ab + (size_t)c * 16 + 8) : uint4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int r = 0; r < ROWS; ++r) {
+      float a = 0.f;
+#pragma unroll
+      for (int i = 0; i < NA; ++i) {
+        const float p = dot8_bf16_d2(e2m1x8_bits(wv[r][i].y), av[i][1],
+                                     dot8_bf16_d2(e2m1x8_bits(wv[r][i].x), av[i][0], 0.f));
+        a = __builtin_fmaf(p, e8m0_value(sc[r][i]), a);
+      }
+      accr[r] = __builtin_fmaf(coef, a, accr[r]);
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < ROWS; ++r) accr[r] = wave_sum(accr[r]);
+  if (lane == 0) {
+#pragma unroll
+    for (int r = 0; r < ROWS; ++r) part[wave][r] = accr[r];
+  }
+  __syncthreads();
+  if (threadIdx.x < ROWS && d0 + (int)threadIdx.x < D) {
+    const int r = threadIdx.x;
+    float v = part[0][r];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) v += part[w][r];
     Y[(size_t)t * D + d0 + r] = f2bf(v);
   }
 }
@@ -242,6 +451,40 @@ int launch_moe_mxfp8(int T, int D, int F, int E, int topk, const uint8_t* w13c,
                        wts, E, topk, F, D, act, Y);
   else
     return -2;
+  return LAUNCH_OK();
+}
+
+int launch_mxfp4_quantize(const uint16_t* w, long long nblocks, uint8_t* codes, uint8_t* scales,
+                          hipStream_t st) {
+  hipLaunchKernelGGL(mxfp4_quantize_kernel, dim3((unsigned)((nblocks + MT - 1) / MT)), dim3(MT),
+                     0, st, w, nblocks, codes, scales);
+  return LAUNCH_OK();
+}
+
+// act: [T * topk][F] bf16 scratch.
+int launch_moe_mxfp4(int T, int D, int F, int E, int topk, const uint8_t* w13c,
+                     const uint8_t* w13s, const uint8_t* w2c, const uint8_t* w2s,
+                     const int32_t* idx, const float* wts, const uint16_t* X, uint16_t* act,
+                     uint16_t* Y, hipStream_t st) {
+  constexpr int NR = 2, ROWS = 4, NW = 4;  // NW: waves of the down-projection workgroup
+  const int nc13 = D / 16, nc2 = F / 16;   // 16-code chunks
+  if (nc13 > 64 * 5 || nc2 > 64 * 3) return -2;
+  const dim3 g13((F + 4 * NR - 1) / (4 * NR), T * topk);
+  const size_t sh = (size_t)D * 2;
+  if (nc13 <= 64)
+    hipLaunchKernelGGL((expert_w13_swiglu_mx4_kernel<1, NR>), g13, dim3(MT), sh, st, w13c, w13s,
+                       idx, E, topk, F, D, X, act);
+  else
+    hipLaunchKernelGGL((expert_w13_swiglu_mx4_kernel<5, NR>), g13, dim3(MT), sh, st, w13c, w13s,
+                       idx, E, topk, F, D, X, act);
+  if (hipGetLastError() != hipSuccess) return -1;
+  const dim3 g2((D + ROWS - 1) / ROWS, T);
+  if (nc2 <= 64)
+    hipLaunchKernelGGL((expert_w2_combine_mx4_kernel<ROWS, 1, NW>), g2, dim3(NW * 64), 0, st,
+                       w2c, w2s, idx, wts, E, topk, F, D, act, Y);
+  else
+    hipLaunchKernelGGL((expert_w2_combine_mx4_kernel<ROWS, 3, NW>), g2, dim3(NW * 64), 0, st,
+                       w2c, w2s, idx, wts, E, topk, F, D, act, Y);
   return LAUNCH_OK();
 }
 

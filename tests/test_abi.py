@@ -20,7 +20,7 @@ MIS = 0x10002        # misaligned
 
 def test_library_exports_every_declared_symbol():
     names = B.header_functions()
-    assert len(names) == 19
+    assert len(names) == 21
     L = ctypes.CDLL(B.LIB_PATH)
     for n in names:
         assert hasattr(L, n), n
@@ -168,22 +168,24 @@ def test_rope_table_host_helper():
         B.beam_rope_table(out, L, 31, theta)
 
 @cpu_only
-def test_mxfp8_validation_and_nodev():
-    assert _rc("beam_mxfp8_quantize", None, 4, 64, A, A, None) == -1
-    assert _rc("beam_mxfp8_quantize", A, 4, 48, A, A, None) == -2
-    assert _rc("beam_mxfp8_quantize", MIS, 4, 64, A, A, None) == -4
-    assert _rc("beam_mxfp8_quantize", A, 0, 64, A, A, None) == 0      # nothing to do
-    assert _rc("beam_mxfp8_quantize", A, 4, 64, A, A, None) == -7
+@pytest.mark.parametrize("fmt", ["mxfp8", "mxfp4"])
+def test_mx_validation_and_nodev(fmt):
+    q, moe = f"beam_{fmt}_quantize", f"beam_moe_swiglu_combine_{fmt}"
+    assert _rc(q, None, 4, 64, A, A, None) == -1
+    assert _rc(q, A, 4, 48, A, A, None) == -2
+    assert _rc(q, MIS, 4, 64, A, A, None) == -4
+    assert _rc(q, A, 0, 64, A, A, None) == 0      # nothing to do
+    assert _rc(q, A, 4, 64, A, A, None) == -7
     d = _dims()
     by = ctypes.byref(d)
     need = 1024 + 4 * 64 * 2   # counter block + act [1 * topk][F] bf16
     args = lambda T=1, ws=need, dims=by: [dims, T, A, A, A, A, A, A, A, A, A, ws, None]  # noqa
-    assert _rc("beam_moe_swiglu_combine_mxfp8", *args(dims=None)) == -1
-    assert _rc("beam_moe_swiglu_combine_mxfp8", *args(T=0)) == -2
-    assert _rc("beam_moe_swiglu_combine_mxfp8", *args(T=5)) == -3
+    assert _rc(moe, *args(dims=None)) == -1
+    assert _rc(moe, *args(T=0)) == -2
+    assert _rc(moe, *args(T=5)) == -3
     d2 = _dims(D=272)
-    assert _rc("beam_moe_swiglu_combine_mxfp8", *args(dims=ctypes.byref(d2))) == -3
+    assert _rc(moe, *args(dims=ctypes.byref(d2))) == -3
     d3 = _dims(F=80)
-    assert _rc("beam_moe_swiglu_combine_mxfp8", *args(dims=ctypes.byref(d3))) == -3
-    assert _rc("beam_moe_swiglu_combine_mxfp8", *args(ws=need - 1)) == -5
-    assert _rc("beam_moe_swiglu_combine_mxfp8", *args()) == -7
+    assert _rc(moe, *args(dims=ctypes.byref(d3))) == -3
+    assert _rc(moe, *args(ws=need - 1)) == -5
+    assert _rc(moe, *args()) == -7

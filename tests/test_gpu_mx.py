@@ -1,10 +1,11 @@
-"""Block-scaled FP8 (MXFP8) expert weights at decode steps.
+"""Block-scaled (MXFP8 and MXFP4) expert weights at decode steps.
 
-The quantiser must agree bit for bit with the oracle's codec (shared exponent
-floor(log2 amax) - 8 per 32 weights along K, e4m3fn codes rounded to nearest
-even and saturated). The expert call is compared, to the same bar as the bf16
-expert call, with the oracle's MoE run on the weights the oracle's own codec
-reconstructs from the bf16 draws."""
+The quantisers must agree bit for bit with the oracle's codecs (per 32 weights
+along K a shared exponent floor(log2 amax) - 8 with e4m3fn codes, or
+floor(log2 amax) - 2 with nibble-packed e2m1 codes; codes rounded to nearest
+even and saturated). The expert calls are compared, to the same bar as the
+bf16 expert call, with the oracle's MoE run on the weights the oracle's own
+codec reconstructs from the bf16 draws."""
 import numpy as np
 import pytest
 import torch
@@ -27,10 +28,15 @@ def _dims(base, **kw):
     return synth.with_dims(synth.Config("", base), **kw).dims
 
 
-def _quantize(w, rows, K):
-    codes = torch.empty((rows, K), **U8)
+FMTS = ["mxfp8", "mxfp4"]
+ORACLE = {"mxfp8": (mx.mxfp8_quantize, mx.mxfp8_dequantize),
+          "mxfp4": (mx.mxfp4_quantize, mx.mxfp4_dequantize)}
+
+
+def _quantize(fmt, w, rows, K):
+    codes = torch.empty((rows, K if fmt == "mxfp8" else K // 2), **U8)
     scales = torch.empty((rows, K // 32), **U8)
-    B.beam_mxfp8_quantize(w, rows, K, codes, scales)
+    getattr(B, f"beam_{fmt}_quantize")(w, rows, K, codes, scales)
     return codes, scales
 
 
@@ -62,20 +68,23 @@ def _special_rows(K, seed):
 
 
 @pytest.mark.parametrize("rows,K", [(1, 32), (37, 96), (300, 5120), (2 * 512 + 3, 2048)])
-def test_quantize_bit_exact(rows, K):
+@pytest.mark.parametrize("fmt", FMTS)
+def test_quantize_bit_exact(fmt, rows, K):
     w = synth.normal_bf16((rows, K), 0.02, 0, "mx_q", rows, K)
     sp = _special_rows(K, rows)
     w[-min(rows, len(sp)):] = sp[:min(rows, len(sp))]
-    codes, scales = _quantize(dev(w), rows, K)
+    codes, scales = _quantize(fmt, dev(w), rows, K)
     B.beam_check()
-    c_ref, s_ref = mx.mxfp8_quantize(bits_f64(w))
+    c_ref, s_ref = ORACLE[fmt][0](bits_f64(w))
     np.testing.assert_array_equal(scales.cpu().numpy(), s_ref)
     np.testing.assert_array_equal(codes.cpu().numpy(), c_ref)
 
 
-def test_quantize_rows_zero_is_a_no_op():
+@pytest.mark.parametrize("fmt", FMTS)
+def test_quantize_rows_zero_is_a_no_op(fmt):
     codes = torch.full((1, 32), 7, **U8)
-    B.beam_mxfp8_quantize(torch.zeros((1, 32), **I16), 0, 32, codes, torch.empty((1, 1), **U8))
+    getattr(B, f"beam_{fmt}_quantize")(torch.zeros((1, 32), **I16), 0, 32, codes,
+                                       torch.empty((1, 1), **U8))
     B.beam_check()
     assert int(codes.sum()) == 7 * 32
 
@@ -84,7 +93,8 @@ class MxExperts:
     """Expert weights drawn as bf16, quantised on the device by the library;
     the oracle side quantises the same bf16 draws with its own codec."""
 
-    def __init__(self, dims, tag, device_draw=False):
+    def __init__(self, fmt, dims, tag, device_draw=False):
+        self.fmt = fmt
         E, F, D = dims.E, dims.F, dims.D
         if device_draw:
             self.w13 = synth.torch_normal_bf16((E, 2 * F, D), 0.02, 0, "mx_w13", tag)
@@ -92,22 +102,24 @@ class MxExperts:
         else:
             self.w13 = dev(synth.normal_bf16((E, 2 * F, D), 0.02, 0, "mx_w13", tag))
             self.w2 = dev(synth.normal_bf16((E, D, F), 0.02, 0, "mx_w2", tag))
-        self.c13, self.s13 = _quantize(self.w13, E * 2 * F, D)
-        self.c2, self.s2 = _quantize(self.w2, E * D, F)
+        self.c13, self.s13 = _quantize(fmt, self.w13, E * 2 * F, D)
+        self.c2, self.s2 = _quantize(fmt, self.w2, E * D, F)
         self._ref = {}
 
     def expert(self, e):
         """Oracle weights of expert e: the codec's reconstruction of the draws."""
         if e not in self._ref:
-            w13 = mx.mxfp8_dequantize(*mx.mxfp8_quantize(bits_f64(host_bits(self.w13[e]))))
-            w2 = mx.mxfp8_dequantize(*mx.mxfp8_quantize(bits_f64(host_bits(self.w2[e]))))
+            q, dq = ORACLE[self.fmt]
+            w13 = dq(*q(bits_f64(host_bits(self.w13[e]))))
+            w2 = dq(*q(bits_f64(host_bits(self.w2[e]))))
             self._ref[e] = (w13, w2)
         return self._ref[e]
 
     def run(self, dims, T, x, idx, w):
         y = torch.empty((T, dims.D), **I16)
-        B.beam_moe_swiglu_combine_mxfp8(dims, T, dev(x), dev(idx), dev(w), self.c13, self.s13,
-                                        self.c2, self.s2, y, ws(dims, B.BEAM_OP_MOE, T))
+        call = getattr(B, f"beam_moe_swiglu_combine_{self.fmt}")
+        call(dims, T, dev(x), dev(idx), dev(w), self.c13, self.s13, self.c2, self.s2, y,
+             ws(dims, B.BEAM_OP_MOE, T))
         return y
 
 
@@ -118,20 +130,24 @@ def _route(dims, T, seed):
     return idx, w
 
 
-# D and F chosen so that both GEMVs take their one-chunk and five-chunk forms,
-# with full and with partly masked lanes (16-code chunks of D, 8-code chunks of F)
+# D and F chosen so that both GEMVs take their one-chunk and many-chunk forms,
+# with full and with partly masked lanes (16-code chunks), and with the scales
+# read as words (K a multiple of 128) or byte by byte
 SMALL = [
     ("cfg0", {}),
     ("ragged", dict(D=1056, F=96, E=6, topk=3)),
     ("wide_f", dict(D=288, F=2080, E=5, topk=2)),
+    ("words", dict(D=512, F=256, E=4, topk=2)),
+    ("wide_d", dict(D=2080, F=64, E=4, topk=2)),
 ]
 
 
 @pytest.mark.parametrize("T", [1, 3, 4])
 @pytest.mark.parametrize("name,kw", SMALL, ids=[s[0] for s in SMALL])
-def test_moe_mxfp8(name, kw, T):
+@pytest.mark.parametrize("fmt", FMTS)
+def test_moe_mx(fmt, name, kw, T):
     dims = _dims(CFG0, n_group=1, topk_group=1, **kw) if kw else CFG0
-    X = MxExperts(dims, name)
+    X = MxExperts(fmt, dims, name)
     x = synth.make_h((T, dims.D), 7, "mxx", name, T)
     idx, w = _route(dims, T, 11 + T)
     y = X.run(dims, T, x, idx, w)
@@ -139,11 +155,12 @@ def test_moe_mxfp8(name, kw, T):
     assert_rms_close(bits_f64(host_bits(y)), L.moe(dims, x, idx, w, X.expert), "y2")
 
 
-def test_moe_mxfp8_beam_shape():
+@pytest.mark.parametrize("fmt", FMTS)
+def test_moe_mx_beam_shape(fmt):
     """Beam's expert shape (D 5,120, F 2,560): two experts, two tokens routed
     to both in opposite order with different weights."""
     dims = _dims(BEAM, E=2, topk=2, n_group=1, topk_group=1)
-    X = MxExperts(dims, "beam", device_draw=True)
+    X = MxExperts(fmt, dims, "beam", device_draw=True)
     T = 2
     x = synth.make_h((T, dims.D), 7, "mxbx")
     idx = np.array([[1, 0], [0, 1]], np.int32)
@@ -153,9 +170,10 @@ def test_moe_mxfp8_beam_shape():
     assert_rms_close(bits_f64(host_bits(y)), L.moe(dims, x, idx, w, X.expert), "y2")
 
 
-def test_moe_mxfp8_bad_expert_id_is_flagged():
+@pytest.mark.parametrize("fmt", FMTS)
+def test_moe_mx_bad_expert_id_is_flagged(fmt):
     dims = CFG0
-    X = MxExperts(dims, "bad")
+    X = MxExperts(fmt, dims, "bad")
     x = synth.make_h((1, dims.D), 7, "mxbad")
     idx = np.array([[1, 2, dims.E, 3]], np.int32)
     w = np.full((1, 4), 0.5, np.float32)
@@ -168,15 +186,16 @@ def test_moe_mxfp8_bad_expert_id_is_flagged():
     assert_rms_close(bits_f64(host_bits(y)), ref, "y2 without the bad slot")
 
 
-def test_moe_mxfp8_rejects_prefill_sizes():
+@pytest.mark.parametrize("fmt", FMTS)
+def test_moe_mx_rejects_prefill_sizes(fmt):
     dims = CFG0
-    X = MxExperts(dims, "big")
+    X = MxExperts(fmt, dims, "big")
     T = 5
     x = torch.zeros((T, dims.D), **I16)
     idx = torch.zeros((T, dims.topk), dtype=torch.int32, device="cuda")
     w = torch.zeros((T, dims.topk), dtype=torch.float32, device="cuda")
     y = torch.empty((T, dims.D), **I16)
     with pytest.raises(B.BeamError) as e:
-        B.beam_moe_swiglu_combine_mxfp8(dims, T, x, idx, w, X.c13, X.s13, X.c2, X.s2, y,
-                                        ws(dims, B.BEAM_OP_MOE, T))
+        getattr(B, f"beam_moe_swiglu_combine_{fmt}")(dims, T, x, idx, w, X.c13, X.s13, X.c2,
+                                                     X.s2, y, ws(dims, B.BEAM_OP_MOE, T))
     assert e.value.code == -3

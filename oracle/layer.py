@@ -320,6 +320,27 @@ def dense_ffn(x, w13, w2, Fd: int) -> np.ndarray:
 
 
 # ----------------------------------------------------------------------------
+# Output head (after the layer stack)
+# ----------------------------------------------------------------------------
+
+def softcap(z, cap: float) -> np.ndarray:
+    """cap * tanh(z / cap): the logit soft cap of Beam's output (cap 30; the
+    architecture notes of the Chinese digest, "Beam model architecture"
+    section). cap = 0 leaves z unchanged."""
+    z = np.asarray(z, dtype=F64)
+    if cap == 0:
+        return z
+    return cap * np.tanh(z / cap)
+
+
+def lm_head_softcap(x, w_head, cap: float) -> np.ndarray:
+    """Logits of T final hidden rows: z[t][v] = x[t] . W[v] (W [V][D], the
+    LM head's rows), then the soft cap; float64, no rounding (the call
+    returns fp32 logits)."""
+    return softcap(as_f64(x) @ as_f64(w_head).T, cap)
+
+
+# ----------------------------------------------------------------------------
 # Whole layer
 # ----------------------------------------------------------------------------
 

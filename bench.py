@@ -46,6 +46,10 @@ def parse():
                     help="skip the second model's batch-128 decode legs")
     ap.add_argument("--no-mx", action="store_true",
                     help="skip the SWA decode legs with block-scaled (MXFP8, MXFP4) experts")
+    ap.add_argument("--no-1m", action="store_true",
+                    help="skip the NoPE fp8 decode leg at a 2^20-token context")
+    ap.add_argument("--no-head", action="store_true",
+                    help="skip the output head (logit soft cap) leg")
     ap.add_argument("--prefill-reps", type=int, default=3)
     ap.add_argument("--cpu-steps", type=int, default=16)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -228,6 +232,16 @@ def main():
         out[f"decode_swa_{fmt}_experts"] = mxr
         del msets
         torch.cuda.empty_cache()
+    if not a.no_1m:
+        # the NoPE fp8 layer at a 2^20-token context: 2 GiB of fp8 KV per layer
+        r1m = decode_leg(a, 2, ctx=1 << 20)
+        for k in ("_sets", "_dims", "_ex", "_x2", "_idx"):
+            r1m.pop(k)
+        out["decode_nope_fp8_1m"] = r1m
+        torch.cuda.empty_cache()
+    if not a.no_head:
+        out["lm_head_softcap_b1"] = head_leg()
+        torch.cuda.empty_cache()
     if not a.no_flint:
         out["decode_flint_b128"] = {m: flint_leg(a, m) for m in ("swa", "nope")}
         torch.cuda.empty_cache()
@@ -242,6 +256,30 @@ def main():
 
 # bytes per 32 expert weights: bf16; e4m3 codes + one scale; e2m1 codes + one scale
 EXPERT_BYTES_PER_32 = {"bf16": 64, "mxfp8": 33, "mxfp4": 17}
+
+
+def head_leg():
+    """The output head with the logit soft cap at one decode token: Beam's
+    hidden size, a synthetic 131,072-entry vocabulary (the pages give none),
+    two weight copies alternated so every call streams its 1.34 GB from HBM."""
+    import torch
+
+    import moe_decoder_layer_amd as B
+    import synth
+    D, V = 5120, 131072
+    ws = [synth.torch_normal_bf16((V, D), 0.02, s, "head_w") for s in (0, 1)]
+    x = synth.torch_normal_bf16((1, D), 1.0, 0, "head_x")
+    logits = torch.empty((1, V), dtype=torch.float32, device="cuda")
+    B.beam_lm_head_softcap(1, D, V, x, ws[0], 30.0, logits)
+    torch.cuda.synchronize()
+    B.beam_check()
+    us = graph_us(lambda i: B.beam_lm_head_softcap(1, D, V, x, ws[i % 2], 30.0, logits), 20)
+    nbytes = V * D * 2 + D * 2 + V * 4
+    gbs = nbytes / (us * 1e-6) / 1e9
+    log(f"[bench] lm head + softcap (D {D}, V {V}, b 1): {us:.2f} us, {gbs:.0f} GB/s")
+    return {"workload": "lm_head_softcap_decode", "hidden": D, "vocab": V, "cap": 30.0,
+            "us": round(us, 3), "bytes": nbytes, "achieved_gbs": round(gbs, 1),
+            "frac": round(gbs / HBM_PEAK_GBS, 4)}
 
 
 def graph_us(fn, reps):
@@ -269,12 +307,13 @@ def graph_us(fn, reps):
     return e0.elapsed_time(e1) * 1000.0 / (5 * reps)
 
 
-def decode_leg(a, ci, experts="bf16"):
+def decode_leg(a, ci, experts="bf16", ctx=None):
     """Batch-1 decode layer-steps of config ci (1: SWA layer 10 on a 100K bf16
     cache; 2: NoPE layer 11 on a 100K fp8 cache), chained 8 per HIP graph over
     two alternating full weight sets. Each graph replay is timed on its own
     (HIP events between replays) for the mean, median and p90 per step.
-    experts "mxfp8" / "mxfp4": the routed experts run from block-scaled copies."""
+    experts "mxfp8" / "mxfp4": the routed experts run from block-scaled copies.
+    ctx: prior tokens in place of the config's (the cache grows to fit)."""
     import numpy as np
     import torch
 
@@ -283,6 +322,8 @@ def decode_leg(a, ci, experts="bf16"):
     cfg = synth.config(ci)
     dims, ex = cfg.dims, cfg.extra
     pos0, Lmax, n, mode, kvt = ex["pos"], ex["Lmax"], ex["n"], ex["mode"], ex["kv"]
+    if ctx is not None:
+        pos0, Lmax = ctx, (ctx + 64) // 64 * 64
     t0 = time.time()
     sets = [LayerSet(dims, seed, ex["layer"], pos0, Lmax, kvt, experts) for seed in (0, 1)]
     log(f"[bench] {mode} decode ({experts} experts): weights + caches drawn in {time.time() - t0:.1f}s "

@@ -297,6 +297,18 @@ int beam_moe_swiglu_combine_mxfp4(const beam_dims* dims, int T, const uint16_t* 
                                   const uint8_t* w2_scales, uint16_t* y, void* ws,
                                   size_t ws_bytes, void* stream);
 
+/* Output head with the logit soft cap (after the layer stack; Beam's
+ * architecture notes give logits = 30 * tanh(z / 30)): x [T][D] bf16 (the
+ * final normed hidden rows), w [V][D] bf16 (the head's rows), logits [T][V]
+ * fp32 (device) = cap * tanh((x[t] . w[v]) / cap), or the plain dot product
+ * when cap is 0. Dot products in fp32. T <= 4: weight-streaming GEMV with the
+ * cap in its epilogue; larger T (D a multiple of 64): the matrix-core GEMM
+ * into logits, then the cap in place. No workspace.
+ * Errors: T or V <= 0 or cap negative / not finite (SHAPE); D not a positive
+ * multiple of 8 <= 8,192 (UNSUPPORTED). */
+int beam_lm_head_softcap(int T, int D, int V, const uint16_t* x, const uint16_t* w, float cap,
+                         float* logits, void* stream);
+
 /* Dense SwiGLU MLP of the first layers ([MoE]; [Opt]/7):
  *   u = bf16(x . w13^T) (w13 [2*Fd][D], gate rows then up rows),
  *   a = bf16(silu(u[:Fd]) * u[Fd:]), y = bf16(a . w2^T) (w2 [D][Fd]).

@@ -25,7 +25,7 @@ __all__ = [
     "beam_moe_swiglu_combine", "beam_moe_experts_up", "beam_moe_experts_down",
     "beam_dense_swiglu", "beam_workspace_size", "beam_rope_table", "beam_hbm_read",
     "beam_mxfp8_quantize", "beam_moe_swiglu_combine_mxfp8",
-    "beam_mxfp4_quantize", "beam_moe_swiglu_combine_mxfp4",
+    "beam_mxfp4_quantize", "beam_moe_swiglu_combine_mxfp4", "beam_lm_head_softcap",
     "beam_check", "beam_last_error", "beam_version",
     "BEAM_SWA_ROPE", "BEAM_NOPE_SSMAX", "BEAM_KV_BF16", "BEAM_KV_FP8_E4M3",
     "BEAM_OP_QKV", "BEAM_OP_ATTN_SWA", "BEAM_OP_ATTN_NOPE", "BEAM_OP_OUT_GATE",
@@ -95,6 +95,7 @@ def lib():
             "beam_moe_swiglu_combine_mxfp8": [POINTER(beam_dims), c_int, P, P, P, P, P, P, P, P,
                                               P, c_size_t, P],
             "beam_mxfp4_quantize": [P, c_size_t, c_int, P, P, P],
+            "beam_lm_head_softcap": [c_int, c_int, c_int, P, P, c_float, P, P],
             "beam_moe_swiglu_combine_mxfp4": [POINTER(beam_dims), c_int, P, P, P, P, P, P, P, P,
                                               P, c_size_t, P],
             "beam_check": [P],
@@ -267,6 +268,10 @@ def beam_moe_swiglu_combine_mxfp4(dims, T, x, idx, w, w13_codes, w13_scales, w2_
     wp, wb = _ws(ws)
     _call("beam_moe_swiglu_combine_mxfp4", ctypes.byref(d), T, _p(x), _p(idx), _p(w),
           _p(w13_codes), _p(w13_scales), _p(w2_codes), _p(w2_scales), _p(y), wp, wb, _s(stream))
+
+
+def beam_lm_head_softcap(T, D, V, x, w, cap, logits, stream=None):
+    _call("beam_lm_head_softcap", T, D, V, _p(x), _p(w), cap, _p(logits), _s(stream))
 
 
 def beam_hbm_read(buf, sink, stream=None):

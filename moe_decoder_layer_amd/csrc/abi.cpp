@@ -673,6 +673,30 @@ int beam_dense_swiglu(int T, int D, int Fd, const uint16_t* x, const uint16_t* w
                   __func__);
 }
 
+int beam_lm_head_softcap(int T, int D, int V, const uint16_t* x, const uint16_t* w, float cap,
+                         float* logits, void* stream) {
+  REQ(x);
+  REQ(w);
+  REQ(logits);
+  ALN(x);
+  ALN(w);
+  ALN(logits);
+  SHAPE(T > 0 && V > 0, "%s: T or V <= 0", __func__);
+  SHAPE(cap >= 0.f && cap <= 3.0e38f, "%s: cap must be finite and >= 0", __func__);
+  UNSUP(D > 0 && D % 8 == 0 && D <= 8192, "%s: D must be a positive multiple of 8 <= 8192",
+        __func__);
+  const int rc = device_ready();
+  if (rc) return rc;
+  const hipStream_t st = S_(stream);
+  if (T > beam::kGemvMaxT && D % 64 == 0) {
+    if (beam::launch_gemm_f32(T, V, D, x, D, w, nullptr, nullptr, 1, 0, 0, logits, V, st))
+      return launched(-1, __func__);
+    if (cap == 0.f) return BEAM_OK;
+    return launched(beam::launch_softcap(logits, (long long)T * V, cap, st), __func__);
+  }
+  return launched(beam::launch_gemv_lm_head(T, V, D, w, x, cap, logits, st), __func__);
+}
+
 size_t beam_workspace_size(const beam_dims* dims, int op, int T, int max_ctx) {
   if (!dims || T <= 0) return (size_t)-1;
   switch (op) {

@@ -18,6 +18,10 @@ int launch_gemv_qkvg(int T, int N, int K, int Nqkv, const uint16_t* W, const uin
 int launch_gemv_gate_oproj(int T, int N, int K, int hd, const uint16_t* W, const uint16_t* O,
                            const uint16_t* G, const uint16_t* bgate, uint16_t* Y,
                            hipStream_t st);
+// output head with the logit soft cap (cap 0: plain logits)
+int launch_gemv_lm_head(int T, int V, int K, const uint16_t* W, const uint16_t* X, float cap,
+                        float* logits, hipStream_t st);
+int launch_softcap(float* z, long long n, float cap, hipStream_t st);
 int launch_expert_w13(int T, int D, int F, int E, int topk, int spt, const uint16_t* w13,
                       const uint16_t* shared_w13, const int32_t* idx, const uint16_t* X,
                       uint16_t* act, hipStream_t st);

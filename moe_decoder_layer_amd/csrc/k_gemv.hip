@@ -345,6 +345,56 @@ __global__ __launch_bounds__(GT) void expert_w2_combine_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// ---------------------------------------------------------------------------
+// Output head with the logit soft cap (Beam's architecture notes): logits
+// [T][V] fp32 = cap * tanh((x . W[v]) / cap), or x . W[v] when cap is 0.
+__device__ __forceinline__ float softcap_f(float z, float cap) {
+  return cap > 0.f ? cap * tanhf(z / cap) : z;
+}
+
+template <int R, int NB, int TT>
+__global__ __launch_bounds__(GT) void gemv_lm_head_kernel(const uint16_t* __restrict__ W, int V,
+                                                          int K, const uint16_t* __restrict__ X,
+                                                          int T, float cap,
+                                                          float* __restrict__ logits) {
+  extern __shared__ __align__(16) uint16_t xs[];
+  const int t0 = blockIdx.y * TT;
+  stage_rows(xs, X + (size_t)t0 * K, K, K, TT, min(TT, T - t0));
+  __syncthreads();
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int n0 = (blockIdx.x * 4 + wave) * R;
+  if (n0 >= V) return;
+  const uint16_t* wr[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) wr[r] = (n0 + r < V) ? W + (size_t)(n0 + r) * K : nullptr;
+  float acc[R][TT] = {};
+  rows_dot<R, NB, TT>(wr, K, xs, lane, acc);
+  if (lane == 0) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      if (n0 + r >= V) break;
+#pragma unroll
+      for (int t = 0; t < TT; ++t) {
+        if (t0 + t >= T) break;
+        logits[(size_t)(t0 + t) * V + n0 + r] = softcap_f(acc[r][t], cap);
+      }
+    }
+  }
+}
+
+// In-place soft cap over n fp32 logits (after the many-token GEMM).
+__global__ __launch_bounds__(GT) void softcap_kernel(float* __restrict__ z, long long n,
+                                                     float cap) {
+  const long long i = (long long)blockIdx.x * GT + threadIdx.x;
+  if (i < n) z[i] = softcap_f(z[i], cap);
+}
+
+int launch_softcap(float* z, long long n, float cap, hipStream_t st) {
+  hipLaunchKernelGGL(softcap_kernel, dim3((unsigned)((n + GT - 1) / GT)), dim3(GT), 0, st, z, n,
+                     cap);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
 // launchers
 static int nb_for(int nc) {
   if (nc % 640 == 0) return 10;
@@ -375,6 +425,25 @@ int launch_gemv_qkvg(int T, int N, int K, int Nqkv, const uint16_t* W, const uin
     const dim3 g4(grid.x, (T + 3) / 4);
     hipLaunchKernelGGL((gemv_qkvg_kernel<R, 4, 4>), g4, dim3(GT), sh, st, W, N, K, X, T, Nqkv,
                        qkv, g_out);
+  }
+  return LAUNCH_OK();
+}
+
+int launch_gemv_lm_head(int T, int V, int K, const uint16_t* W, const uint16_t* X, float cap,
+                        float* logits, hipStream_t st) {
+  constexpr int R = 2;
+  const dim3 grid((V + 4 * R - 1) / (4 * R), 1);
+  if (T == 1) {
+    const size_t sh = (size_t)K * 2;
+    const int nb = nb_for(K >> 3);
+#define H1(NB) hipLaunchKernelGGL((gemv_lm_head_kernel<R, NB, 1>), grid, dim3(GT), sh, st, W, V, K, X, T, cap, logits)
+    if (nb == 10) H1(10); else if (nb == 6) H1(6); else if (nb == 5) H1(5); else H1(4);
+#undef H1
+  } else {
+    const size_t sh = (size_t)K * 2 * 4;
+    const dim3 g4(grid.x, (T + 3) / 4);
+    hipLaunchKernelGGL((gemv_lm_head_kernel<R, 4, 4>), g4, dim3(GT), sh, st, W, V, K, X, T, cap,
+                       logits);
   }
   return LAUNCH_OK();
 }

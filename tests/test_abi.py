@@ -20,7 +20,7 @@ MIS = 0x10002        # misaligned
 
 def test_library_exports_every_declared_symbol():
     names = B.header_functions()
-    assert len(names) == 21
+    assert len(names) == 22
     L = ctypes.CDLL(B.LIB_PATH)
     for n in names:
         assert hasattr(L, n), n
@@ -189,3 +189,16 @@ def test_mx_validation_and_nodev(fmt):
     assert _rc(moe, *args(dims=ctypes.byref(d3))) == -3
     assert _rc(moe, *args(ws=need - 1)) == -5
     assert _rc(moe, *args()) == -7
+
+
+@cpu_only
+def test_lm_head_validation_and_nodev():
+    f = "beam_lm_head_softcap"
+    assert _rc(f, 1, 256, 1000, None, A, ctypes.c_float(30.0), A, None) == -1
+    assert _rc(f, 1, 256, 1000, A, A, ctypes.c_float(30.0), MIS, None) == -4
+    assert _rc(f, 0, 256, 1000, A, A, ctypes.c_float(30.0), A, None) == -2
+    assert _rc(f, 1, 256, 0, A, A, ctypes.c_float(30.0), A, None) == -2
+    assert _rc(f, 1, 256, 1000, A, A, ctypes.c_float(-1.0), A, None) == -2
+    assert _rc(f, 1, 256, 1000, A, A, ctypes.c_float(float("inf")), A, None) == -2
+    assert _rc(f, 1, 260, 1000, A, A, ctypes.c_float(30.0), A, None) == -3
+    assert _rc(f, 1, 256, 1000, A, A, ctypes.c_float(30.0), A, None) == -7

@@ -26,6 +26,8 @@
 // its own L2. Each XCD therefore gets a contiguous eighth of the tile list,
 // walked in column-major groups of kGroupM tile rows, so the ~32 tiles an XCD
 // holds at once share a few A row panels and B column panels in its L2.
+#include <type_traits>
+
 #include "common.h"
 #include "internal.h"
 
@@ -89,6 +91,11 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_bf16_kernel(GemmArgs g) {
   // Grouped mode launches the worst-case number of tile rows; only the first
   // tile_off[E] of them hold rows, so those are what gets split over the XCDs
   // (the rest of the grid exits at once instead of idling whole XCDs).
+  // Grouped mode with full-height tiles walks the list expert by expert (an
+  // expert's few tile rows, column-major): the ~32 tiles an XCD holds at once
+  // then share one expert's A rows and read each of its B panels once, where
+  // groups of kGroupM tile rows would span several experts and refetch their
+  // A panels for every few columns.
   int tm, tn;
   {
     const int rows_m = g.seg_off ? g.tile_off[g.E] : g.tiles_m;
@@ -97,11 +104,23 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_bf16_kernel(GemmArgs g) {
     const int q = nt / kXcds, r = nt % kXcds;
     if (li >= q + (x < r ? 1 : 0)) return;
     const int t = x * q + min(x, r) + li;  // this XCD's li-th tile
-    const int span = kGroupM * g.tiles_n;  // tiles per group of kGroupM tile rows
-    const int grp = t / span, w = t - grp * span;
-    const int rows = min(kGroupM, rows_m - grp * kGroupM);
-    tm = grp * kGroupM + w % rows;
-    tn = w / rows;
+    if (TR == BM && g.seg_off) {
+      int lo = 0, hi = g.E;  // largest e with tile_off[e] * tiles_n <= t (a non-empty expert)
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (g.tile_off[mid] * g.tiles_n <= t) lo = mid; else hi = mid;
+      }
+      const int w = t - g.tile_off[lo] * g.tiles_n;
+      const int rows = g.tile_off[lo + 1] - g.tile_off[lo];
+      tm = g.tile_off[lo] + w % rows;
+      tn = w / rows;
+    } else {
+      const int span = kGroupM * g.tiles_n;  // tiles per group of kGroupM tile rows
+      const int grp = t / span, w = t - grp * span;
+      const int rows = min(kGroupM, rows_m - grp * kGroupM);
+      tm = grp * kGroupM + w % rows;
+      tn = w / rows;
+    }
   }
   // ---- tile -> (rows, expert) ------------------------------------------------
   int m0, mrows, e = 0;
@@ -200,6 +219,11 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_bf16_kernel(GemmArgs g) {
   gload(kt0 * BK, 0);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
+  // Two copies of the K loop: one with the per-block row skip, one without its
+  // branches. A wave whose row blocks all hold rows takes the branch-free copy,
+  // so SKIP costs full tiles nothing (both copies meet the same barriers).
+  auto kloop = [&](auto skip_tag) {
+  constexpr bool SK = decltype(skip_tag)::value;
   for (int kt = kt0; kt < KT; ++kt) {
     const int cur = (kt - kt0) & 1;  // buffer 0 holds the first k-step of this split
     // the other buffer was last read in step kt - 1, which every wave has left
@@ -211,7 +235,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_bf16_kernel(GemmArgs g) {
       if (ks + 1 < BK / 16) frags(cur, ks + 1, af[(ks + 1) & 1], bfr[(ks + 1) & 1]);
 #pragma unroll
       for (int i = 0; i < MI; ++i) {
-        if (SKIP && 32 * i >= band) continue;
+        if (SK && 32 * i >= band) continue;
 #pragma unroll
         for (int j = 0; j < TJ; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks & 1][i], bfr[ks & 1][j],
@@ -221,6 +245,9 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_bf16_kernel(GemmArgs g) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's loads of step kt + 1
     __syncthreads();
   }
+  };
+  if (SKIP && band < MI * 32) kloop(std::integral_constant<bool, SKIP>{});
+  else kloop(std::integral_constant<bool, false>{});
 
   // ---- epilogue -------------------------------------------------------------------
   // acc[i][j][4*ii + jj] = C[row 32 i + 8 ii + 4 lk + jj][col 32 j + lr] of the wave tile
@@ -376,7 +403,7 @@ int launch_gemm_swiglu(int M, int F, int K, const uint16_t* A, int lda, const in
   if (seg_off && gemm_grouped_rows(M, E) == 32)
     return launch<EPI_SWIGLU, true, 32>(a, gn, max_mtiles, st);
   const int gm = seg_off ? max_mtiles : (M + BM - 1) / BM;
-  if (!seg_off && M <= BM / 2) return launch<EPI_SWIGLU, true>(a, gn, gm, st);
+  if (seg_off || M <= BM / 2) return launch<EPI_SWIGLU, true>(a, gn, gm, st);
   return launch<EPI_SWIGLU>(a, gn, gm, st);
 }
 
@@ -391,7 +418,7 @@ int launch_gemm_f32(int M, int N, int K, const uint16_t* A, int lda, const uint1
   if (seg_off && gemm_grouped_rows(M, E) == 32)
     return launch<EPI_F32, true, 32>(a, gn, max_mtiles, st);
   const int gm = seg_off ? max_mtiles : (M + BM - 1) / BM;
-  if (!seg_off && M <= BM / 2) return launch<EPI_F32, true>(a, gn, gm, st);
+  if (seg_off || M <= BM / 2) return launch<EPI_F32, true>(a, gn, gm, st);
   return launch<EPI_F32>(a, gn, gm, st);
 }
 

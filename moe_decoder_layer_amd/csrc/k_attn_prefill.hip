@@ -287,7 +287,7 @@ __global__ __launch_bounds__(768) void attn_prefill_kernel(
 // contiguous 16-byte V^T chunk per P.V step (fk is chosen so the 8 rows read
 // by each group of 8 lanes, perm(0..7) or perm(8..15), hit distinct banks).
 // Keys outside the sequence's [kmin, kmax] may hold anything: scores are
-// replaced by -inf, and on edge tiles the V fragment entries are zeroed.
+// replaced by -inf, and on edge tiles the out-of-range V^T entries are zeroed in LDS.
 constexpr int DMA_HD = 128;
 
 __device__ __forceinline__ int fk_swz(int r) { return (r & 3) | ((r >> 1) & 4); }
@@ -417,6 +417,15 @@ __global__ __launch_bounds__(768) void attn_prefill_dma_kernel(
       if (it + 1 < ntiles) gload(kb + KT, cur ^ 1);
       const bool edge = (kb < kmin) || (kb + KT - 1 > kmax);
       const bool interior = all_mine && kb >= lo_max && kb + KT - 1 <= p_min;
+      if (edge) {  // uniform over the workgroup: [kmin, kmax] is the sequence's
+        // key (column) kk of V^T row d sits in chunk slot (kk / 8) ^ (d % 8)
+        for (int i = tid; i < HD * KT; i += blockDim.x) {
+          const int d = i / KT, kk = i - d * KT, key = kb + kk;
+          if (key < kmin || key > kmax)
+            sV(cur)[d * KT + (((kk >> 3) ^ (d & 7)) << 3) + (kk & 7)] = 0;
+        }
+        __syncthreads();
+      }
       if (__any(mine)) {  // waves with no token of this sequence only load
 #pragma unroll 1
         for (int kh = 0; kh < 2; ++kh) {
@@ -484,19 +493,18 @@ __global__ __launch_bounds__(768) void attn_prefill_dma_kernel(
             const bf16x8 ph = __builtin_bit_cast(bf16x8, uint4{phw[0], phw[1], phw[2], phw[3]});
             // this lane's keys: kbase + 16 st + 8 g + [0, 8), one V^T chunk
             const int vchunk = kh * 4 + 2 * st + g;
-            const int key0 = kbase + 16 * st + 8 * g;
+            // the step's V^T fragments, all requested before the first product
+            // (no masking here: an edge tile's out-of-range entries are zero)
+            bf16x8 vf[DB];
 #pragma unroll
             for (int db = 0; db < DB; ++db) {
               const int d = db * 32 + tc;
-              bf16x8 vf = *reinterpret_cast<const bf16x8*>(sV(cur) + d * KT +
-                                                           (vchunk ^ (d & 7)) * 8);
-              if (edge) {
+              vf[db] = *reinterpret_cast<const bf16x8*>(sV(cur) + d * KT + (vchunk ^ (d & 7)) * 8);
+            }
 #pragma unroll
-                for (int e = 0; e < 8; ++e)
-                  if (key0 + e < kmin || key0 + e > kmax) vf[e] = (__bf16)0.0f;
-              }
-              oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, ph, oacc[db], 0, 0, 0);
-              oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pl, oacc[db], 0, 0, 0);
+            for (int db = 0; db < DB; ++db) {
+              oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[db], ph, oacc[db], 0, 0, 0);
+              oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[db], pl, oacc[db], 0, 0, 0);
             }
           }
         }

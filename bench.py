@@ -13,7 +13,7 @@ stream from HBM rather than the 256 MB Infinity Cache. A chain of steps is
 captured in one HIP graph and replayed; the timed region holds exactly
 --steps steps.
 
-Prints one JSON line (rank 0). --gpus above 1 exits: this build runs on one GPU.
+Prints one JSON line (rank 0). --gpus above 1 exits: the layer runs on one GPU.
 """
 from __future__ import annotations
 
@@ -113,8 +113,8 @@ class LayerSet:
 def main():
     a = parse()
     if a.gpus != 1:
-        print(f"bench.py: this build runs the layer on one GPU only (asked for {a.gpus}); "
-              "the multi-GPU sharding is a design note, not a run.", file=sys.stderr)
+        print(f"bench.py: the layer runs on one GPU only (asked for {a.gpus}); "
+              "sharding the layer across GPUs is not implemented.", file=sys.stderr)
         sys.exit(2)
     import numpy as np
     import torch

@@ -8,12 +8,16 @@
 // (query head of the group, 32-token sub-block), so every wave of the
 // workgroup consumes the same keys. Keys advance in tiles of 64, staged
 // cooperatively into a double-buffered LDS ring: the next tile's global loads
-// are in flight while the current tile is multiplied out of LDS. K and V are
-// held as bf16 (fp8 caches are widened exactly while staged); probabilities
-// enter the P.V product as a hi + lo pair of bf16 values (two MFMAs), so the
-// attention output's only bf16 rounding is its store:
+// are in flight while the current tile is multiplied out of LDS.
+// attn_prefill_kernel (fp8 caches, which it widens exactly while staging, and
+// head dims 32 / 64) holds K and V as bf16 and gives the P.V product each
+// probability as a hi + lo pair of bf16 values (two MFMAs, ~16 bits):
 //   S^T[key][token] = K[key][:] . Q[token][:]            32x32x16 bf16 MFMA
 //   O^T[dim][token] += V^T[dim][key] . (P_hi + P_lo)^T    2 x 32x32x16 bf16 MFMA
+// attn_prefill_dma_kernel (bf16 cache, head dim 128) takes the P.V product on
+// fp16 operands instead, one MFMA: p (<= 1) rounded to fp16 keeps 11
+// significant bits, and the bf16 V^T tile converts to fp16 exactly (values
+// beyond +-65504 are clamped).
 // In the S^T layout lane l owns token l % 32: the online softmax state is
 // lane-local up to one xor-32 shuffle, and a lane's probabilities are the B
 // operand it needs for P.V. LDS rows are padded (K rows by 16 bytes, V^T rows
@@ -287,8 +291,13 @@ __global__ __launch_bounds__(768) void attn_prefill_kernel(
 // contiguous 16-byte V^T chunk per P.V step (fk is chosen so the 8 rows read
 // by each group of 8 lanes, perm(0..7) or perm(8..15), hit distinct banks).
 // Keys outside the sequence's [kmin, kmax] may hold anything: scores are
-// replaced by -inf, and on edge tiles the out-of-range V^T entries are zeroed in LDS.
+// replaced by -inf, and on edge tiles the out-of-range V^T entries are zeroed
+// in LDS by the same pass that turns each V^T tile into fp16 (once per
+// workgroup and tile, so the P.V loop carries no masking and no conversion):
+//   O^T[dim][token] += V^T[dim][key] . P^T              32x32x16 fp16 MFMA
 constexpr int DMA_HD = 128;
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ int fk_swz(int r) { return (r & 3) | ((r >> 1) & 4); }
 __device__ __forceinline__ int perm23(int s) {
@@ -417,12 +426,30 @@ __global__ __launch_bounds__(768) void attn_prefill_dma_kernel(
       if (it + 1 < ntiles) gload(kb + KT, cur ^ 1);
       const bool edge = (kb < kmin) || (kb + KT - 1 > kmax);
       const bool interior = all_mine && kb >= lo_max && kb + KT - 1 <= p_min;
-      if (edge) {  // uniform over the workgroup: [kmin, kmax] is the sequence's
-        // key (column) kk of V^T row d sits in chunk slot (kk / 8) ^ (d % 8)
-        for (int i = tid; i < HD * KT; i += blockDim.x) {
-          const int d = i / KT, kk = i - d * KT, key = kb + kk;
-          if (key < kmin || key > kmax)
-            sV(cur)[d * KT + (((kk >> 3) ^ (d & 7)) << 3) + (kk & 7)] = 0;
+      // The V^T tile becomes fp16 in place (the P.V product runs on fp16
+      // operands: bf16 values in fp16's range convert exactly, larger ones are
+      // clamped to +-65504), and on an edge tile the keys outside the
+      // sequence's [kmin, kmax] become zero (they may hold anything). Chunk
+      // slot s of V^T row d holds keys 8 (s ^ (d % 8)) + [0, 8) of the tile.
+      {
+        uint4* vt = reinterpret_cast<uint4*>(sV(cur));
+        for (int c = tid; c < HD * KT / 8; c += nw * 64) {
+          const int d = c >> 3, k0 = kb + 8 * ((c & 7) ^ (d & 7));
+          const uint4 w = vt[c];
+          const uint32_t in[4] = {w.x, w.y, w.z, w.w};
+          uint32_t out[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            float a = fminf(fmaxf(bf_lo(in[e]), -65504.f), 65504.f);
+            float b = fminf(fmaxf(bf_hi(in[e]), -65504.f), 65504.f);
+            if (edge) {
+              if (k0 + 2 * e < kmin || k0 + 2 * e > kmax) a = 0.f;
+              if (k0 + 2 * e + 1 < kmin || k0 + 2 * e + 1 > kmax) b = 0.f;
+            }
+            const f16x2 h = {(_Float16)a, (_Float16)b};
+            out[e] = __builtin_bit_cast(uint32_t, h);
+          }
+          vt[c] = uint4{out[0], out[1], out[2], out[3]};
         }
         __syncthreads();
       }
@@ -476,36 +503,26 @@ __global__ __launch_bounds__(768) void attn_prefill_dma_kernel(
           }
 #pragma unroll
           for (int st = 0; st < 2; ++st) {
-            // hi = p truncated to bf16 (exact, one AND), lo = bf16(p - hi):
-            // p is carried to ~16 bits as in a round-to-nearest split
-            uint32_t phw[4];
-            bf16x8 pl;
+            // p in fp16 (11 significant bits; p <= 1)
+            f16x8 pf;
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
-              const float p0 = sacc[4 * (2 * st + (k >> 1)) + 2 * (k & 1)];
-              const float p1 = sacc[4 * (2 * st + (k >> 1)) + 2 * (k & 1) + 1];
-              const uint32_t h0 = __float_as_uint(p0) & 0xffff0000u;
-              const uint32_t h1 = __float_as_uint(p1) & 0xffff0000u;
-              phw[k] = __builtin_amdgcn_perm(h1, h0, 0x07060302u);  // (h0 >> 16) | h1
-              pl[2 * k] = (__bf16)(p0 - __uint_as_float(h0));
-              pl[2 * k + 1] = (__bf16)(p1 - __uint_as_float(h1));
+              pf[2 * k] = (_Float16)sacc[4 * (2 * st + (k >> 1)) + 2 * (k & 1)];
+              pf[2 * k + 1] = (_Float16)sacc[4 * (2 * st + (k >> 1)) + 2 * (k & 1) + 1];
             }
-            const bf16x8 ph = __builtin_bit_cast(bf16x8, uint4{phw[0], phw[1], phw[2], phw[3]});
             // this lane's keys: kbase + 16 st + 8 g + [0, 8), one V^T chunk
             const int vchunk = kh * 4 + 2 * st + g;
             // the step's V^T fragments, all requested before the first product
             // (no masking here: an edge tile's out-of-range entries are zero)
-            bf16x8 vf[DB];
+            f16x8 vf[DB];
 #pragma unroll
             for (int db = 0; db < DB; ++db) {
               const int d = db * 32 + tc;
-              vf[db] = *reinterpret_cast<const bf16x8*>(sV(cur) + d * KT + (vchunk ^ (d & 7)) * 8);
+              vf[db] = *reinterpret_cast<const f16x8*>(sV(cur) + d * KT + (vchunk ^ (d & 7)) * 8);
             }
 #pragma unroll
-            for (int db = 0; db < DB; ++db) {
-              oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[db], ph, oacc[db], 0, 0, 0);
-              oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[db], pl, oacc[db], 0, 0, 0);
-            }
+            for (int db = 0; db < DB; ++db)
+              oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf[db], pf, oacc[db], 0, 0, 0);
           }
         }
       }

@@ -93,7 +93,10 @@ def _check(dims, P, cache, g, pos, seq, mode, n, ffn, upto):
     # sequence order so each sequence's cache is fetched once
     o_ref = L.attention(dims, bits_f64(sel("q")), pos[ts], seq[ts], DeviceKV(cache, upto), mode,
                         P.np("sink") if "sink" in P.t else None)
-    assert_rms_close(bits_f64(sel("o")), o_ref, "o")
+    e_max = assert_rms_close(bits_f64(sel("o")), o_ref, "o")
+    e_rms = float(np.sqrt(np.mean((bits_f64(sel("o")) - o_ref) ** 2)) / np.sqrt(np.mean(o_ref ** 2)))
+    print(f"[prefill {mode}] attention output vs oracle: max|err| {e_max:.3e}, "
+          f"rms(err) {e_rms:.3e} of rms(ref)", flush=True)
     z = L.output_gate(dims, bits_f64(sel("o")), bits_f64(sel("g")), P.np("b_gate"))
     assert_rms_close(bits_f64(sel("y")), L.o_proj(z, P.np("w_o")), "y")
     hm, _ = L.boundary(sel("y"), sel("h_in"), P.np("w_attn_post"), P.np("w_ffn_pre"), n, eps)

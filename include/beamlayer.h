@@ -162,7 +162,11 @@ int beam_qk_norm_rope_ssmax_kvwrite(const beam_dims* dims, int T, const uint16_t
  * Kernels: calls of T <= 4 tokens, and of T <= 256 tokens with T <= 4 * kv->S
  * (a batch of decode steps over many sequences), run split-K per token; other
  * calls (prefill chunks) run a flash kernel that shares each key tile among
- * the tokens of a sequence. Both compute the same function.
+ * the tokens of a sequence. Both compute the same function; they differ in the
+ * precision of the P.V product: split-K kernels carry each probability to ~16
+ * bits (a bf16 hi + lo pair), the flash kernel on a bf16 cache with d = 128
+ * rounds probabilities to fp16 and converts V to fp16 (exact for bf16 values
+ * of magnitude <= 65504; larger ones are clamped to +-65504).
  * Errors: window <= 0, max_pos >= Lmax. */
 int beam_attn_swa(const beam_dims* dims, int T, const uint16_t* q, const int32_t* pos,
                   const int32_t* seq, const beam_kv* kv, const float* sink, uint16_t* o,

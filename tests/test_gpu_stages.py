@@ -157,16 +157,24 @@ def _needle_cache(dims, Lmax, fill, kv, q, pos, seq, needles, seed):
 
 
 @pytest.mark.parametrize("case", ["tiny", "tiny_few", "beam_multi", "beam_few", "beam_long",
-                                  "beam_chunk", "beam_mid", "beam_mid2", "group16_short",
-                                  "group16"])
+                                  "beam_chunk", "beam_two_seq", "beam_mid", "beam_mid2",
+                                  "group16_short", "group16"])
 @pytest.mark.parametrize("mode", ["swa", "nope"])
 @pytest.mark.parametrize("kv", ["bf16", "fp8"])
 def test_attention(case, mode, kv):
     """Few tokens (<= 4) take the split-K decode kernel: one chunk normalises
     in place (tiny_few, group16_short), up to 8 chunks merge in their last
     workgroup (SWA windows, beam_mid*), more in the merge kernel (beam_long,
-    NoPE beam_few and group16); more tokens take the flash kernel."""
-    if case == "beam_mid":
+    NoPE beam_few and group16); more tokens take the flash kernel. beam_two_seq:
+    a flash-kernel block of 64 tokens holds the last 37 of one sequence and
+    the first 27 of another, with different key ranges (one pass each, edge
+    tiles at both ends of both ranges)."""
+    seq = None
+    if case == "beam_two_seq":
+        dims, Lmax, fill = BEAM, 4096, 3063
+        pos = np.concatenate([np.arange(1000, 1037), np.arange(3000, 3063)]).astype(np.int32)
+        seq = np.repeat(np.array([0, 1], np.int32), [37, 63])
+    elif case == "beam_mid":
         dims, Lmax, fill = BEAM, 4096, 3000
         pos = np.array([1500], np.int32)
     elif case == "beam_mid2":
@@ -197,8 +205,9 @@ def test_attention(case, mode, kv):
         dims, Lmax, fill = BEAM, 100352, 100001
         pos = np.array([100000], np.int32)
     T = len(pos)
-    seq = (np.arange(T) % 2).astype(np.int32) if case not in ("beam_long", "beam_chunk") \
-        else np.zeros(T, np.int32)
+    if seq is None:
+        seq = (np.arange(T) % 2).astype(np.int32) if case not in ("beam_long", "beam_chunk") \
+            else np.zeros(T, np.int32)
     q = dev(synth.make_h((T, dims.Hq, dims.d), 3, "aq", case))
     W = dims.window
 

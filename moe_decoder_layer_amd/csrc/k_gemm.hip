@@ -223,28 +223,28 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_bf16_kernel(GemmArgs g) {
   // branches. A wave whose row blocks all hold rows takes the branch-free copy,
   // so SKIP costs full tiles nothing (both copies meet the same barriers).
   auto kloop = [&](auto skip_tag) {
-  constexpr bool SK = decltype(skip_tag)::value;
-  for (int kt = kt0; kt < KT; ++kt) {
-    const int cur = (kt - kt0) & 1;  // buffer 0 holds the first k-step of this split
-    // the other buffer was last read in step kt - 1, which every wave has left
-    if (kt + 1 < KT) gload((kt + 1) * BK, cur ^ 1);
-    bf16x8 af[2][MI], bfr[2][TJ];
-    frags(cur, 0, af[0], bfr[0]);
+    constexpr bool SK = decltype(skip_tag)::value;
+    for (int kt = kt0; kt < KT; ++kt) {
+      const int cur = (kt - kt0) & 1;  // buffer 0 holds the first k-step of this split
+      // the other buffer was last read in step kt - 1, which every wave has left
+      if (kt + 1 < KT) gload((kt + 1) * BK, cur ^ 1);
+      bf16x8 af[2][MI], bfr[2][TJ];
+      frags(cur, 0, af[0], bfr[0]);
 #pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
-      if (ks + 1 < BK / 16) frags(cur, ks + 1, af[(ks + 1) & 1], bfr[(ks + 1) & 1]);
+      for (int ks = 0; ks < BK / 16; ++ks) {
+        if (ks + 1 < BK / 16) frags(cur, ks + 1, af[(ks + 1) & 1], bfr[(ks + 1) & 1]);
 #pragma unroll
-      for (int i = 0; i < MI; ++i) {
-        if (SK && 32 * i >= band) continue;
+        for (int i = 0; i < MI; ++i) {
+          if (SK && 32 * i >= band) continue;
 #pragma unroll
-        for (int j = 0; j < TJ; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks & 1][i], bfr[ks & 1][j],
-                                                             acc[i][j], 0, 0, 0);
+          for (int j = 0; j < TJ; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks & 1][i], bfr[ks & 1][j],
+                                                               acc[i][j], 0, 0, 0);
+        }
       }
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's loads of step kt + 1
+      __syncthreads();
     }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's loads of step kt + 1
-    __syncthreads();
-  }
   };
   if (SKIP && band < MI * 32) kloop(std::integral_constant<bool, SKIP>{});
   else kloop(std::integral_constant<bool, false>{});

@@ -127,6 +127,61 @@ __device__ void route_token(const float* lg, float bias, int E, int ng, int tg, 
     sb = sv + bias;
     s_b[e] = sb;
   }
+  if (ng == 1 || tg >= ng) {
+    // Every group kept: the top K of the biased scores, in K rounds of a
+    // workgroup argmax over a key that orders by value, then lower index
+    // (the rank rule below). Keys: the float's bits made order-preserving as
+    // unsigned in the high word, 0xFFFF - e in the low word; a lane without
+    // an expert, or whose expert is taken, holds 0 (below every score).
+    uint32_t khi = 0, klo = 0;
+    if (act) {
+      const uint32_t u = __float_as_uint(sb);
+      khi = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+      klo = 0xFFFFu - (uint32_t)e;
+    }
+    uint32_t* red_hi = reinterpret_cast<uint32_t*>(cand_v);
+    uint32_t* red_lo = reinterpret_cast<uint32_t*>(cand_i);
+    const int nw = (blockDim.x + 63) >> 6, wave = threadIdx.x >> 6;
+    for (int r = 0; r < K; ++r) {
+      uint32_t bh = khi, bl = klo;
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) {
+        const uint32_t oh = __shfl_xor(bh, o, 64), ol = __shfl_xor(bl, o, 64);
+        if (oh > bh || (oh == bh && ol > bl)) {
+          bh = oh;
+          bl = ol;
+        }
+      }
+      if ((threadIdx.x & 63) == 0) {
+        red_hi[wave] = bh;
+        red_lo[wave] = bl;
+      }
+      __syncthreads();
+      bh = red_hi[0];
+      bl = red_lo[0];
+      for (int w = 1; w < nw; ++w) {
+        const uint32_t oh = red_hi[w], ol = red_lo[w];
+        if (oh > bh || (oh == bh && ol > bl)) {
+          bh = oh;
+          bl = ol;
+        }
+      }
+      __syncthreads();  // red_* are rewritten next round
+      if (act && e == (int)(0xFFFFu - bl)) {
+        idx_t[r] = e;
+        ssel[r] = sv;
+        khi = klo = 0;
+      }
+    }
+    __syncthreads();
+    if (e < K) {
+      float sum = 0.f;
+      for (int k = 0; k < K; ++k) sum += ssel[k];
+      w_t[e] = route_scale * ssel[e] / sum;
+    }
+    __syncthreads();  // the LDS arrays are reused for the next token
+    return;
+  }
   if (e < nc) cand_v[e] = -INFINITY;  // slots a group cannot fill stay empty
   __syncthreads();
   // rank inside the group; the two best give the group's score

@@ -15,6 +15,7 @@ pytestmark = pytest.mark.gpu
 
 CFG0 = synth.config(0).dims
 BEAM = synth.config(1).dims
+FLINT = synth.config(4).dims  # 256 experts, sigmoid top-6, no groups
 I16 = dict(dtype=torch.int16, device="cuda")
 
 
@@ -300,8 +301,15 @@ def test_out_gate(base, T):
 
 
 # ------------------------------------------------------------------ router
-@pytest.mark.parametrize("base,T", [(CFG0, 1), (CFG0, 70), (BEAM, 1), (BEAM, 4), (BEAM, 300)])
+@pytest.mark.parametrize("base,T", [(CFG0, 1), (CFG0, 70), (BEAM, 1), (BEAM, 4), (BEAM, 300),
+                                    (FLINT, 1), (FLINT, 3), (FLINT, 128), ("beam_all_groups", 1),
+                                    ("beam_all_groups", 40)])
 def test_router(base, T):
+    """Grouped selection (top groups, then top experts) and, with no groups or
+    every group kept (the second model's layer; the Beam shape with all 8
+    groups kept), the plain top-k path, each against the oracle."""
+    if base == "beam_all_groups":
+        base = _dims(BEAM, topk_group=8)
     dims = base
     P = Params(dims, 0, 5, moe=False)
     x = synth.make_h((T, dims.D), 6, "rx", T)

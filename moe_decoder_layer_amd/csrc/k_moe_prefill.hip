@@ -28,14 +28,13 @@ __device__ __forceinline__ int block_sum_int(int v, int* red) {
   return red[0] + red[1] + red[2] + red[3];
 }
 
-// The (token, slot) pairs are cut into chunks of kRouteChunk; chunk c's
-// per-expert counts go to counts[c][E].
-constexpr int kRouteChunk = 2048;
-
+// The (token, slot) pairs are cut into chunks of moe_route_chunk(P) pairs (a
+// multiple of 256); chunk c's per-expert counts go to counts[c][E].
 __global__ __launch_bounds__(256) void moe_count_kernel(const int32_t* __restrict__ idx, int P,
-                                                        int E, int32_t* __restrict__ counts) {
+                                                        int E, int chunk,
+                                                        int32_t* __restrict__ counts) {
   __shared__ int hist[1024];
-  const int c = blockIdx.x, i0 = c * kRouteChunk, i1 = min(P, i0 + kRouteChunk);
+  const int c = blockIdx.x, i0 = c * chunk, i1 = min(P, i0 + chunk);
   for (int e = threadIdx.x; e < E; e += 256) hist[e] = 0;
   __syncthreads();
   for (int i = i0 + threadIdx.x; i < i1; i += 256) {
@@ -103,13 +102,13 @@ __global__ __launch_bounds__(1024) void moe_scan_kernel(int32_t* __restrict__ co
 // the same expert in the batch of 256 (pairs keep (token, slot) order within
 // every expert). perm[row] = token, inv[pair] = row.
 __global__ __launch_bounds__(256) void moe_scatter_kernel(const int32_t* __restrict__ idx, int P,
-                                                          int K, int E,
+                                                          int K, int E, int chunk,
                                                           const int32_t* __restrict__ base,
                                                           int32_t* __restrict__ perm,
                                                           int32_t* __restrict__ inv) {
   __shared__ int run[1024];
   __shared__ int ex[256];
-  const int c = blockIdx.x, i0 = c * kRouteChunk, i1 = min(P, i0 + kRouteChunk);
+  const int c = blockIdx.x, i0 = c * chunk, i1 = min(P, i0 + chunk);
   for (int e = threadIdx.x; e < E; e += 256) run[e] = base[(size_t)c * E + e];
   for (int b0 = i0; b0 < i1; b0 += 256) {
     const int i = b0 + threadIdx.x;
@@ -185,19 +184,32 @@ __global__ __launch_bounds__(256) void gate_kernel(const uint16_t* __restrict__ 
   *reinterpret_cast<uint4*>(z + i * 8) = uint4{r[0], r[1], r[2], r[3]};
 }
 
-int moe_route_chunks(int P) { return (P + kRouteChunk - 1) / kRouteChunk; }
+// Pairs per routing chunk: 256 for short spans (a batch of decode steps), so
+// the scatter's per-batch ranking runs in several workgroups at once, doubled
+// up to 2048 while there would be more than 64 chunks, so the scan's walk over
+// the chunks stays short.
+static int moe_route_chunk(int P) {
+  int c = 256;
+  while (c < 2048 && (P + c - 1) / c > 64) c *= 2;
+  return c;
+}
+
+int moe_route_chunks(int P) {
+  const int c = moe_route_chunk(P);
+  return (P + c - 1) / c;
+}
 
 int launch_moe_route(int T, int K, int E, const int32_t* idx, int tile_rows, int32_t* counts,
                      int32_t* seg_off, int32_t* tile_off, int32_t* perm, int32_t* inv,
                      hipStream_t st) {
   const int P = T * K;
   if (E > 1024) return -1;
-  const int nch = moe_route_chunks(P);
-  hipLaunchKernelGGL(moe_count_kernel, dim3(nch), dim3(256), 0, st, idx, P, E, counts);
+  const int chunk = moe_route_chunk(P), nch = moe_route_chunks(P);
+  hipLaunchKernelGGL(moe_count_kernel, dim3(nch), dim3(256), 0, st, idx, P, E, chunk, counts);
   hipLaunchKernelGGL(moe_scan_kernel, dim3(1), dim3(1024), 0, st, counts, nch, E, tile_rows,
                      seg_off, tile_off);
-  hipLaunchKernelGGL(moe_scatter_kernel, dim3(nch), dim3(256), 0, st, idx, P, K, E, counts, perm,
-                     inv);
+  hipLaunchKernelGGL(moe_scatter_kernel, dim3(nch), dim3(256), 0, st, idx, P, K, E, chunk, counts,
+                     perm, inv);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

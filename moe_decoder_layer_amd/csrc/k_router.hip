@@ -246,8 +246,17 @@ __global__ __launch_bounds__(EMAX) void router_topk_kernel(
   __shared__ float g1[64], g2[64], ssel[32];
   const int t = blockIdx.x;
   if (part != nullptr && (int)threadIdx.x < E) {
+    // eight partials requested at a time, added in split order
     float v = 0.f;
-    for (int z = 0; z < nsplit; ++z) v += part[((size_t)z * T + t) * E + threadIdx.x];
+    for (int z0 = 0; z0 < nsplit; z0 += 8) {
+      float pz[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        pz[i] = z0 + i < nsplit ? part[((size_t)(z0 + i) * T + t) * E + threadIdx.x] : 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        if (z0 + i < nsplit) v += pz[i];
+    }
     logits[(size_t)t * E + threadIdx.x] = v;
   }
   const float bias = (bcorr && (int)threadIdx.x < E) ? bcorr[threadIdx.x] : 0.f;

@@ -137,26 +137,27 @@ float* ws_router_part(const beam_dims* d, int T, bool own_logits, void* ws) {
   return (float*)(ws_data(ws) + ws_router_logits(d, T, own_logits));
 }
 
-// Many-token MoE workspace, in order: counts[chunks][E], seg_off[E+1], tile_off[E+1],
-// perm[P], inv[P] (int32); act[P][F] bf16; out[P][D] fp32; shared expert
-// act_s[T][F] bf16 and out_s[T][D] fp32.
+// Many-token MoE workspace, in order: counts[chunks][E+1], seg_off[E+2],
+// tile_off[E+2], perm[P], inv[P] (int32); act[P][F] bf16; out[P][D] fp32, for
+// P = T * (topk + 1) (token, slot) rows: a shared expert is routed as one more
+// slot per token, segment E, through the same grouped GEMMs.
 struct MoeWs {
-  size_t counts, seg_off, tile_off, perm, inv, act, out, act_s, out_s, part, total;
+  size_t counts, seg_off, tile_off, perm, inv, act, out, total;
 };
 MoeWs moe_ws_layout(const beam_dims* d, int T) {
-  const size_t P = (size_t)T * d->topk, E = d->E;
+  const size_t P = (size_t)T * (d->topk + 1), E = d->E;
+  // chunk counts are not monotone in the pair count: room for either
+  const size_t nch = std::max(beam::moe_route_chunks(T * d->topk),
+                              beam::moe_route_chunks(T * (d->topk + 1)));
   MoeWs w{};
   size_t o = 0;
-  w.counts = o; o += align256((size_t)beam::moe_route_chunks((int)P) * E * 4);
-  w.seg_off = o; o += align256((E + 1) * 4);
-  w.tile_off = o; o += align256((E + 1) * 4);
+  w.counts = o; o += align256(nch * (E + 1) * 4);
+  w.seg_off = o; o += align256((E + 2) * 4);
+  w.tile_off = o; o += align256((E + 2) * 4);
   w.perm = o; o += align256(P * 4);
   w.inv = o; o += align256(P * 4);
   w.act = o; o += align256(P * d->F * 2);
   w.out = o; o += align256(P * d->D * 4);
-  w.act_s = o; o += align256((size_t)T * d->F * 2);
-  w.out_s = o; o += align256((size_t)T * d->D * 4);
-  w.part = o; o += beam::gemm_split_bytes(T, 2 * d->F, d->D);
   w.total = o;
   return w;
 }
@@ -551,26 +552,21 @@ int beam_moe_swiglu_combine(const beam_dims* dims, int T, const uint16_t* x,
     uint16_t* act = (uint16_t*)(b + L.act);
     float* out = (float*)(b + L.out);
     const int E = dims->E, K = dims->topk, D = dims->D, F = dims->F;
-    const int BMr = beam::gemm_grouped_rows(T * K, dims->E);
-    const int max_tiles = (T * K + BMr - 1) / BMr + E;
+    // a shared expert is one more slot per token (segment E, weight 1) in the
+    // same routing permutation and grouped GEMMs as the routed experts
+    const int spt = K + (shared_w13 ? 1 : 0), NE = E + (shared_w13 ? 1 : 0);
+    const int P = T * spt;
+    const int BMr = beam::gemm_grouped_rows(P, NE);
+    const int max_tiles = (P + BMr - 1) / BMr + NE;
     const hipStream_t st = S_(stream);
-    if (beam::launch_moe_route(T, K, E, idx, BMr, counts, seg_off, tile_off, perm, inv, st) ||
-        beam::launch_gemm_swiglu(T * K, F, D, x, D, perm, w13, seg_off, tile_off, E,
-                                 (long long)2 * F * D, max_tiles, act, nullptr, st) ||
-        beam::launch_gemm_f32(T * K, D, F, act, F, w2, seg_off, tile_off, E, (long long)D * F,
-                              max_tiles, out, D, st))
+    if (beam::launch_moe_route(T, K, spt, E, idx, BMr, counts, seg_off, tile_off, perm, inv,
+                               st) ||
+        beam::launch_gemm_swiglu(P, F, D, x, D, perm, w13, seg_off, tile_off, NE,
+                                 (long long)2 * F * D, max_tiles, act, nullptr, st, shared_w13) ||
+        beam::launch_gemm_f32(P, D, F, act, F, w2, seg_off, tile_off, NE, (long long)D * F,
+                              max_tiles, out, D, st, shared_w2))
       return launched(-1, __func__);
-    float* out_s = nullptr;
-    if (shared_w13) {
-      uint16_t* act_s = (uint16_t*)(b + L.act_s);
-      out_s = (float*)(b + L.out_s);
-      if (beam::launch_gemm_swiglu(T, F, D, x, D, nullptr, shared_w13, nullptr, nullptr, 1, 0, 0,
-                                   act_s, (float*)(b + L.part), st) ||
-          beam::launch_gemm_f32(T, D, F, act_s, F, shared_w2, nullptr, nullptr, 1, 0, 0, out_s,
-                                D, st))
-        return launched(-1, __func__);
-    }
-    return launched(beam::launch_moe_combine(T, K, E, D, out, inv, w, idx, out_s, y, st),
+    return launched(beam::launch_moe_combine(T, K, spt, E, D, out, inv, w, idx, y, st),
                     __func__);
   }
   const int spt = dims->topk + (shared_w13 ? 1 : 0);

@@ -93,18 +93,23 @@ int launch_gemm_bf16(int M, int N, int K, const uint16_t* A, int lda, const uint
 int launch_gemm_swiglu(int M, int F, int K, const uint16_t* A, int lda, const int32_t* gather,
                        const uint16_t* B, const int32_t* seg_off, const int32_t* tile_off, int E,
                        long long b_stride, int max_mtiles, uint16_t* act, float* part,
-                       hipStream_t st);
+                       hipStream_t st, const uint16_t* B_last = nullptr);
+// B_last (grouped mode): the weights of segment E - 1 in place of
+// B + (E - 1) * b_stride (the shared expert after the routed ones)
 int launch_gemm_f32(int M, int N, int K, const uint16_t* A, int lda, const uint16_t* B,
                     const int32_t* seg_off, const int32_t* tile_off, int E, long long b_stride,
-                    int max_mtiles, float* out, int ldo, hipStream_t st);
-// counts: moe_route_chunks(T * K) x E int32 of scratch
+                    int max_mtiles, float* out, int ldo, hipStream_t st,
+                    const uint16_t* B_last = nullptr);
+// Routing permutation over T * spt (token, slot) pairs: slots 0..K-1 the routed
+// experts of idx, slot K (spt = K + 1) the shared expert as segment E.
+// counts: moe_route_chunks(T * spt) x (E + 1) int32 of scratch; seg_off and
+// tile_off: E + 2 entries.
 int moe_route_chunks(int P);
-int launch_moe_route(int T, int K, int E, const int32_t* idx, int tile_rows, int32_t* counts,
-                     int32_t* seg_off, int32_t* tile_off, int32_t* perm, int32_t* inv,
-                     hipStream_t st);
-int launch_moe_combine(int T, int K, int E, int D, const float* out, const int32_t* inv,
-                       const float* w, const int32_t* idx, const float* shared_out, uint16_t* y,
-                       hipStream_t st);
+int launch_moe_route(int T, int K, int spt, int E, const int32_t* idx, int tile_rows,
+                     int32_t* counts, int32_t* seg_off, int32_t* tile_off, int32_t* perm,
+                     int32_t* inv, hipStream_t st);
+int launch_moe_combine(int T, int K, int spt, int E, int D, const float* out, const int32_t* inv,
+                       const float* w, const int32_t* idx, uint16_t* y, hipStream_t st);
 int launch_gate(int T, int Hq, int hd, const uint16_t* o, const uint16_t* g, const uint16_t* b,
                 uint16_t* z, hipStream_t st);
 // the many-token attention kernel covers these GQA group / head-dim shapes

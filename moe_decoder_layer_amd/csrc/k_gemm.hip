@@ -52,6 +52,7 @@ struct GemmArgs {
   const int32_t* tile_off;    // [E+1] prefix sums of per-expert M-tile counts
   int E;
   long long b_expert_stride;  // elements between experts' weight blocks
+  const uint16_t* B_last;     // segment E - 1's weights when set (a shared expert)
   // epilogue
   void* out;
   int ldo;
@@ -141,7 +142,8 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_bf16_kernel(GemmArgs g) {
     mrows = min(TR, g.M - m0);
   }
   const int n0 = tn * BN;  // tile column origin (EPI_SWIGLU: in act columns x 2)
-  const uint16_t* Bbase = g.B + (long long)e * g.b_expert_stride;
+  const uint16_t* Bbase =
+      (g.B_last && e == g.E - 1) ? g.B_last : g.B + (long long)e * g.b_expert_stride;
 
   // ---- global -> LDS loads ------------------------------------------------------
   // gfx950 loads 16 bytes per lane straight into LDS: one wave instruction
@@ -390,10 +392,11 @@ int launch_gemm_bf16(int M, int N, int K, const uint16_t* A, int lda, const uint
 int launch_gemm_swiglu(int M, int F, int K, const uint16_t* A, int lda, const int32_t* gather,
                        const uint16_t* B, const int32_t* seg_off, const int32_t* tile_off, int E,
                        long long b_stride, int max_mtiles, uint16_t* act, float* part,
-                       hipStream_t st) {
+                       hipStream_t st, const uint16_t* B_last) {
   GemmArgs a{};
   a.A = A; a.B = B; a.M = M; a.N = 2 * F; a.K = K; a.lda = lda; a.ldb = K;
   a.a_gather = gather; a.seg_off = seg_off; a.tile_off = tile_off; a.E = E;
+  a.B_last = seg_off ? B_last : nullptr;
   a.b_expert_stride = b_stride; a.out = act; a.ldo = F; a.F = F; a.n1 = 2 * F;
   if (!seg_off) {
     const int s = gemm_splits(M, 2 * F, K);
@@ -409,10 +412,11 @@ int launch_gemm_swiglu(int M, int F, int K, const uint16_t* A, int lda, const in
 
 int launch_gemm_f32(int M, int N, int K, const uint16_t* A, int lda, const uint16_t* B,
                     const int32_t* seg_off, const int32_t* tile_off, int E, long long b_stride,
-                    int max_mtiles, float* out, int ldo, hipStream_t st) {
+                    int max_mtiles, float* out, int ldo, hipStream_t st, const uint16_t* B_last) {
   GemmArgs a{};
   a.A = A; a.B = B; a.M = M; a.N = N; a.K = K; a.lda = lda; a.ldb = K;
   a.seg_off = seg_off; a.tile_off = tile_off; a.E = E; a.b_expert_stride = b_stride;
+  a.B_last = seg_off ? B_last : nullptr;
   a.out = out; a.ldo = ldo; a.n1 = N;
   const int gn = (N + BN - 1) / BN;
   if (seg_off && gemm_grouped_rows(M, E) == 32)

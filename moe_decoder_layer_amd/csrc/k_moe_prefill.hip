@@ -30,20 +30,33 @@ __device__ __forceinline__ int block_sum_int(int v, int* red) {
 
 // The (token, slot) pairs are cut into chunks of moe_route_chunk(P) pairs (a
 // multiple of 256); chunk c's per-expert counts go to counts[c][E].
+// Expert of pair i of the (token, slot) list, spt slots per token: slots
+// 0..K-1 hold the routed experts of idx (-1 for an id outside [0, E)), slot K
+// (when spt = K + 1) the shared expert, numbered E.
+__device__ __forceinline__ int pair_expert(const int32_t* __restrict__ idx, int i, int K, int spt,
+                                           int E) {
+  const int t = i / spt, s = i - t * spt;
+  if (s >= K) return E;
+  const int v = idx[t * K + s];
+  return (v >= 0 && v < E) ? v : -1;
+}
+
+// NE segments: the E routed experts, plus the shared expert when spt > K.
 __global__ __launch_bounds__(256) void moe_count_kernel(const int32_t* __restrict__ idx, int P,
-                                                        int E, int chunk,
+                                                        int K, int spt, int E, int NE,
+                                                        int chunk,
                                                         int32_t* __restrict__ counts) {
   __shared__ int hist[1024];
   const int c = blockIdx.x, i0 = c * chunk, i1 = min(P, i0 + chunk);
-  for (int e = threadIdx.x; e < E; e += 256) hist[e] = 0;
+  for (int e = threadIdx.x; e < NE; e += 256) hist[e] = 0;
   __syncthreads();
   for (int i = i0 + threadIdx.x; i < i1; i += 256) {
-    const int v = idx[i];
-    if (v >= 0 && v < E) atomicAdd(&hist[v], 1);  // an integer count: order-independent
+    const int v = pair_expert(idx, i, K, spt, E);
+    if (v >= 0) atomicAdd(&hist[v], 1);  // an integer count: order-independent
     else BEAM_RAISE(moe, ERR_EXPERT);
   }
   __syncthreads();
-  for (int e = threadIdx.x; e < E; e += 256) counts[(size_t)c * E + e] = hist[e];
+  for (int e = threadIdx.x; e < NE; e += 256) counts[(size_t)c * NE + e] = hist[e];
 }
 
 // One workgroup of 1024 threads, thread e holding expert e (E <= 1024): its
@@ -102,18 +115,19 @@ __global__ __launch_bounds__(1024) void moe_scan_kernel(int32_t* __restrict__ co
 // the same expert in the batch of 256 (pairs keep (token, slot) order within
 // every expert). perm[row] = token, inv[pair] = row.
 __global__ __launch_bounds__(256) void moe_scatter_kernel(const int32_t* __restrict__ idx, int P,
-                                                          int K, int E, int chunk,
+                                                          int K, int spt, int E, int NE,
+                                                          int chunk,
                                                           const int32_t* __restrict__ base,
                                                           int32_t* __restrict__ perm,
                                                           int32_t* __restrict__ inv) {
   __shared__ int run[1024];
   __shared__ int ex[256];
   const int c = blockIdx.x, i0 = c * chunk, i1 = min(P, i0 + chunk);
-  for (int e = threadIdx.x; e < E; e += 256) run[e] = base[(size_t)c * E + e];
+  for (int e = threadIdx.x; e < NE; e += 256) run[e] = base[(size_t)c * NE + e];
   for (int b0 = i0; b0 < i1; b0 += 256) {
     const int i = b0 + threadIdx.x;
-    const int v = i < i1 ? idx[i] : -1;
-    const bool ok = v >= 0 && v < E;
+    const int v = i < i1 ? pair_expert(idx, i, K, spt, E) : -1;
+    const bool ok = v >= 0;
     __syncthreads();  // run[] updated by the previous batch
     ex[threadIdx.x] = ok ? v : -1;
     __syncthreads();
@@ -123,7 +137,7 @@ __global__ __launch_bounds__(256) void moe_scatter_kernel(const int32_t* __restr
     const int row = ok ? run[v] + before : 0;
     __syncthreads();  // every lane has read run[] for this batch
     if (ok) {
-      perm[row] = i / K;
+      perm[row] = i / spt;
       inv[i] = row;
       atomicAdd(&run[v], 1);  // an integer count: order-independent
     }
@@ -135,8 +149,7 @@ __global__ __launch_bounds__(256) void moe_combine_kernel(const float* __restric
                                                           const int32_t* __restrict__ inv,
                                                           const float* __restrict__ w,
                                                           const int32_t* __restrict__ idx, int K,
-                                                          int E, int D,
-                                                          const float* __restrict__ shared_out,
+                                                          int spt, int E, int D,
                                                           uint16_t* __restrict__ y) {
   const int t = blockIdx.x;
   for (int c = threadIdx.x * 4; c < D; c += 256 * 4) {
@@ -145,14 +158,14 @@ __global__ __launch_bounds__(256) void moe_combine_kernel(const float* __restric
       const int e = idx[t * K + k];
       if (e < 0 || e >= E) continue;
       const float wk = w[t * K + k];
-      const f32x4 v = *reinterpret_cast<const f32x4*>(out + (size_t)inv[t * K + k] * D + c);
+      const f32x4 v = *reinterpret_cast<const f32x4*>(out + (size_t)inv[t * spt + k] * D + c);
       a0 = __builtin_fmaf(wk, v[0], a0);
       a1 = __builtin_fmaf(wk, v[1], a1);
       a2 = __builtin_fmaf(wk, v[2], a2);
       a3 = __builtin_fmaf(wk, v[3], a3);
     }
-    if (shared_out) {
-      const f32x4 v = *reinterpret_cast<const f32x4*>(shared_out + (size_t)t * D + c);
+    if (spt > K) {  // the shared expert's row, weight 1
+      const f32x4 v = *reinterpret_cast<const f32x4*>(out + (size_t)inv[t * spt + K] * D + c);
       a0 += v[0];
       a1 += v[1];
       a2 += v[2];
@@ -199,25 +212,25 @@ int moe_route_chunks(int P) {
   return (P + c - 1) / c;
 }
 
-int launch_moe_route(int T, int K, int E, const int32_t* idx, int tile_rows, int32_t* counts,
-                     int32_t* seg_off, int32_t* tile_off, int32_t* perm, int32_t* inv,
-                     hipStream_t st) {
-  const int P = T * K;
-  if (E > 1024) return -1;
+int launch_moe_route(int T, int K, int spt, int E, const int32_t* idx, int tile_rows,
+                     int32_t* counts, int32_t* seg_off, int32_t* tile_off, int32_t* perm,
+                     int32_t* inv, hipStream_t st) {
+  const int P = T * spt, NE = E + (spt > K ? 1 : 0);
+  if (NE > 1024) return -1;
   const int chunk = moe_route_chunk(P), nch = moe_route_chunks(P);
-  hipLaunchKernelGGL(moe_count_kernel, dim3(nch), dim3(256), 0, st, idx, P, E, chunk, counts);
-  hipLaunchKernelGGL(moe_scan_kernel, dim3(1), dim3(1024), 0, st, counts, nch, E, tile_rows,
+  hipLaunchKernelGGL(moe_count_kernel, dim3(nch), dim3(256), 0, st, idx, P, K, spt, E, NE, chunk,
+                     counts);
+  hipLaunchKernelGGL(moe_scan_kernel, dim3(1), dim3(1024), 0, st, counts, nch, NE, tile_rows,
                      seg_off, tile_off);
-  hipLaunchKernelGGL(moe_scatter_kernel, dim3(nch), dim3(256), 0, st, idx, P, K, E, chunk, counts,
-                     perm, inv);
+  hipLaunchKernelGGL(moe_scatter_kernel, dim3(nch), dim3(256), 0, st, idx, P, K, spt, E, NE,
+                     chunk, counts, perm, inv);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
-int launch_moe_combine(int T, int K, int E, int D, const float* out, const int32_t* inv,
-                       const float* w, const int32_t* idx, const float* shared_out, uint16_t* y,
-                       hipStream_t st) {
-  hipLaunchKernelGGL(moe_combine_kernel, dim3(T), dim3(256), 0, st, out, inv, w, idx, K, E, D,
-                     shared_out, y);
+int launch_moe_combine(int T, int K, int spt, int E, int D, const float* out, const int32_t* inv,
+                       const float* w, const int32_t* idx, uint16_t* y, hipStream_t st) {
+  hipLaunchKernelGGL(moe_combine_kernel, dim3(T), dim3(256), 0, st, out, inv, w, idx, K, spt, E, D,
+                     y);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

@@ -139,8 +139,10 @@ __device__ void route_token(const float* lg, float bias, int E, int ng, int tg, 
       khi = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
       klo = 0xFFFFu - (uint32_t)e;
     }
-    uint32_t* red_hi = reinterpret_cast<uint32_t*>(cand_v);
-    uint32_t* red_lo = reinterpret_cast<uint32_t*>(cand_i);
+    // per-wave winners in cand_i: high words at [0, 16), low words at [16, 32)
+    // (every caller's cand_i holds at least 256 entries; at most 16 waves)
+    int* red_hi = cand_i;
+    int* red_lo = cand_i + 16;
     const int nw = (blockDim.x + 63) >> 6, wave = threadIdx.x >> 6;
     for (int r = 0; r < K; ++r) {
       uint32_t bh = khi, bl = klo;
@@ -153,14 +155,14 @@ __device__ void route_token(const float* lg, float bias, int E, int ng, int tg, 
         }
       }
       if ((threadIdx.x & 63) == 0) {
-        red_hi[wave] = bh;
-        red_lo[wave] = bl;
+        red_hi[wave] = static_cast<int>(bh);
+        red_lo[wave] = static_cast<int>(bl);
       }
       __syncthreads();
-      bh = red_hi[0];
-      bl = red_lo[0];
+      bh = static_cast<uint32_t>(red_hi[0]);
+      bl = static_cast<uint32_t>(red_lo[0]);
       for (int w = 1; w < nw; ++w) {
-        const uint32_t oh = red_hi[w], ol = red_lo[w];
+        const uint32_t oh = static_cast<uint32_t>(red_hi[w]), ol = static_cast<uint32_t>(red_lo[w]);
         if (oh > bh || (oh == bh && ol > bl)) {
           bh = oh;
           bl = ol;

@@ -286,17 +286,26 @@ def test_workspace_counters_reused(mode):
 
 
 # ------------------------------------------------------------------ gate + o_proj
-@pytest.mark.parametrize("base,T", [(CFG0, 1), (CFG0, 9), (BEAM, 1), (BEAM, 2)])
+@pytest.mark.parametrize("base,T", [(CFG0, 1), (CFG0, 9), (BEAM, 1), (BEAM, 2),
+                                    ("beam_no_gate", 1), ("beam_no_gate", 3)])
 def test_out_gate(base, T):
-    dims = base
+    """Output gate + o_proj against the oracle; the Beam shape without an
+    output gate runs o_proj on the attention output as it is."""
+    dims = _dims(BEAM, G=0) if base == "beam_no_gate" else base
     P = Params(dims, 0, 4, moe=False)
     o = synth.make_h((T, dims.Hq * dims.d), 5, "go", T)
-    g = synth.make_h((T, dims.G), 5, "gg", T)
     y = torch.empty((T, dims.D), **I16)
-    B.beam_out_gate(dims, T, dev(o), dev(g), P.t["b_gate"], P.t["w_o"], y,
-                    ws(dims, B.BEAM_OP_OUT_GATE, T))
+    if dims.G:
+        g = synth.make_h((T, dims.G), 5, "gg", T)
+        B.beam_out_gate(dims, T, dev(o), dev(g), P.t["b_gate"], P.t["w_o"], y,
+                        ws(dims, B.BEAM_OP_OUT_GATE, T))
+        z = L.output_gate(dims, bits_f64(o).reshape(T, dims.Hq, dims.d), bits_f64(g),
+                          P.np("b_gate"))
+    else:
+        B.beam_out_gate(dims, T, dev(o), None, None, P.t["w_o"], y,
+                        ws(dims, B.BEAM_OP_OUT_GATE, T))
+        z = bits_f64(o)
     B.beam_check()
-    z = L.output_gate(dims, bits_f64(o).reshape(T, dims.Hq, dims.d), bits_f64(g), P.np("b_gate"))
     assert_rms_close(bits_f64(host_bits(y)), L.o_proj(z, P.np("w_o")), "y")
 
 
@@ -326,6 +335,49 @@ def test_router(base, T):
     B.beam_router_fp32_grouped_topk(dims, T, dev(x), P.t["w_r"], P.t["b_corr"], idx2, w2, None,
                                     ws(dims, B.BEAM_OP_ROUTER, T))
     assert torch.equal(idx, idx2) and torch.equal(w, w2)
+
+
+@pytest.mark.parametrize("base,T", [(BEAM, 1), (BEAM, 300), ("beam_all_groups", 1),
+                                    ("beam_all_groups", 40), (FLINT, 1), (FLINT, 128)])
+def test_router_exact_ties(base, T):
+    """Exact ties: inside each expert group, experts come in sets of five
+    consecutive indices whose router rows and biases repeat the set's first
+    (the last set of a group may be shorter), so a set's logits and biased
+    scores are equal bit for bit. Five does not divide top-k (8 or 6), so sets
+    straddle the selection boundary; the selection must then take a set's
+    lowest indices. Checked on the GPU's own logits (rounding cannot undo an
+    exact tie) and against the oracle."""
+    if base == "beam_all_groups":
+        base = _dims(BEAM, topk_group=8)
+    dims = base
+    gs = dims.E // max(dims.n_group, 1)
+    e = np.arange(dims.E)
+    lead = e - e % gs + 5 * ((e % gs) // 5)
+    P = Params(dims, 0, 5, moe=False)
+    for k in ("w_r", "b_corr"):
+        if P.t.get(k) is not None:
+            a = np.array(P.np(k)[lead], copy=True)
+            P._np[k], P.t[k] = a, dev(a)
+    x = synth.make_h((T, dims.D), 6, "rt", T)
+    idx = torch.empty((T, dims.topk), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, dims.topk), dtype=torch.float32, device="cuda")
+    lg = torch.empty((T, dims.E), dtype=torch.float32, device="cuda")
+    B.beam_router_fp32_grouped_topk(dims, T, dev(x), P.t["w_r"], P.t["b_corr"], idx, w, lg,
+                                    ws(dims, B.BEAM_OP_ROUTER, T))
+    B.beam_check()
+    lgh, idh = lg.cpu().numpy(), idx.cpu().numpy()
+    assert np.array_equal(lgh.view(np.uint32), lgh[:, lead].view(np.uint32))
+    split = 0
+    for t in range(T):
+        sel = set(idh[t].tolist())
+        assert len(sel) == dims.topk
+        for j in sel:
+            assert all(i in sel for i in range(lead[j], j)), \
+                f"token {t}: expert {j} taken before a lower index of its tie set"
+        split += any(j + 1 < dims.E and lead[j + 1] == lead[j] and j + 1 not in sel
+                     for j in sel)
+    assert split > 0, "no tie set straddles the selection boundary"
+    check_routing(dims, x, P, idh, w.cpu().numpy(), lgh, "router ties")
 
 
 @pytest.mark.parametrize("base,T", [(CFG0, 1), (BEAM, 1), (BEAM, 3)])

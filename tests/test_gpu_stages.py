@@ -503,6 +503,33 @@ def test_out_gate_gemm_beam():
     test_out_gate(BEAM, 300)
 
 
+def test_moe_bad_expert_id_many_tokens():
+    """Many tokens (routing permutation + grouped GEMMs): ids outside [0, E)
+    are left out of the permutation, skipped by the combine and reported; the
+    other pairs match the oracle with the rejected slots at weight 0."""
+    dims = CFG0
+    P = Params(dims, 0, 6)
+    T = 40
+    x = synth.make_h((T, dims.D), 7, "badm", T)
+    g = np.random.default_rng(11)
+    idx = np.stack([g.choice(dims.E, dims.topk, replace=False) for _ in range(T)]).astype(np.int32)
+    w = g.uniform(0.05, 0.6, (T, dims.topk)).astype(np.float32)
+    bad = [(7, 2, dims.E), (30, 0, -1), (39, 3, dims.E + 100)]
+    for t, k, v in bad:
+        idx[t, k] = v
+    y = torch.empty((T, dims.D), **I16)
+    B.beam_moe_swiglu_combine(dims, T, dev(x), dev(idx), dev(w), P.t["w13"], P.t["w2"], None, None,
+                              y, ws(dims, B.BEAM_OP_MOE, T))
+    with pytest.raises(B.BeamError) as e:
+        B.beam_check()
+    assert e.value.code == -8
+    idx_ok, w_ok = idx.copy(), w.copy()
+    for t, k, _ in bad:  # any valid id not already in the row, at weight 0
+        idx_ok[t, k] = next(i for i in range(dims.E) if i not in idx[t])
+        w_ok[t, k] = 0.0
+    assert_rms_close(bits_f64(host_bits(y)), L.moe(dims, x, idx_ok, w_ok, P.expert), "y2")
+
+
 def test_dense_gemm_beam():
     test_dense(BEAM, 300)
 

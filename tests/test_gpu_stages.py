@@ -337,6 +337,20 @@ def test_router(base, T):
     assert torch.equal(idx, idx2) and torch.equal(w, w2)
 
 
+def _tie_sets(dims, P):
+    """Make the router rows and biases of each set of five consecutive experts
+    inside a group (the last set of a group may be shorter) repeat the set's
+    first; returns each expert's set leader."""
+    gs = dims.E // max(dims.n_group, 1)
+    e = np.arange(dims.E)
+    lead = e - e % gs + 5 * ((e % gs) // 5)
+    for k in ("w_r", "b_corr"):
+        if P.t.get(k) is not None:
+            a = np.array(P.np(k)[lead], copy=True)
+            P._np[k], P.t[k] = a, dev(a)
+    return lead
+
+
 @pytest.mark.parametrize("base,T", [(BEAM, 1), (BEAM, 300), ("beam_all_groups", 1),
                                     ("beam_all_groups", 40), (FLINT, 1), (FLINT, 128)])
 def test_router_exact_ties(base, T):
@@ -350,14 +364,8 @@ def test_router_exact_ties(base, T):
     if base == "beam_all_groups":
         base = _dims(BEAM, topk_group=8)
     dims = base
-    gs = dims.E // max(dims.n_group, 1)
-    e = np.arange(dims.E)
-    lead = e - e % gs + 5 * ((e % gs) // 5)
     P = Params(dims, 0, 5, moe=False)
-    for k in ("w_r", "b_corr"):
-        if P.t.get(k) is not None:
-            a = np.array(P.np(k)[lead], copy=True)
-            P._np[k], P.t[k] = a, dev(a)
+    lead = _tie_sets(dims, P)
     x = synth.make_h((T, dims.D), 6, "rt", T)
     idx = torch.empty((T, dims.topk), dtype=torch.int32, device="cuda")
     w = torch.empty((T, dims.topk), dtype=torch.float32, device="cuda")
@@ -380,12 +388,15 @@ def test_router_exact_ties(base, T):
     check_routing(dims, x, P, idh, w.cpu().numpy(), lgh, "router ties")
 
 
-@pytest.mark.parametrize("base,T", [(CFG0, 1), (BEAM, 1), (BEAM, 3)])
-def test_boundary_router_fused_equals_calls(base, T):
+@pytest.mark.parametrize("base,T,ties", [(CFG0, 1, False), (BEAM, 1, False), (BEAM, 3, False),
+                                         (BEAM, 1, True), ("beam_all_groups", 1, True)])
+def test_boundary_router_fused_equals_calls(base, T, ties):
     """The fused boundary + router call gives the two calls' results bit for
-    bit (T = 1 runs as one kernel), also when repeated on one workspace."""
-    dims = base
+    bit (T = 1 runs as one kernel), also when repeated on one workspace, and
+    with exact ties in the router scores (sets of five equal experts)."""
+    dims = _dims(BEAM, topk_group=8) if base == "beam_all_groups" else base
     P = Params(dims, 0, 5, moe=False)
+    lead = _tie_sets(dims, P) if ties else None
     y = dev(synth.make_h((T, dims.D), 8, "fy", T))
     h0 = synth.make_h((T, dims.D), 9, "fh", T)
     n = 21
@@ -412,6 +423,10 @@ def test_boundary_router_fused_equals_calls(base, T):
                            (l1, l2, "logits")):
             assert torch.equal(a, b), name
         assert int(wsf[:1024].count_nonzero()) == 0
+        if ties:  # a tie set's lowest indices are the ones taken
+            for row in i2.cpu().numpy():
+                sel = set(row.tolist())
+                assert all(i in sel for j in sel for i in range(lead[j], j)), row
 
 
 # ------------------------------------------------------------------ experts

@@ -438,3 +438,213 @@ def test_tiny_layer_runs_and_normalises():
     # x_next = rms(h_out) * w, so x_next / w has unit RMS
     u = r["x_next"] / w
     np.testing.assert_allclose(np.sqrt(np.mean(u * u, axis=-1)), 1.0, rtol=1e-2)
+
+
+# ------------------------------------------- second model: sink, shared expert, pre-norm
+# Flint page, "Flint model architecture": a learned attention-sink logit per
+# head, one always-on shared expert beside the routed ones, and the plain
+# pre-norm residual. Each pin below also evaluates the forms a plausible
+# mistake would produce and checks that the pin tells them apart.
+
+def _sink_loops(dims, q, pos, K, V, mode, sink):
+    """Softmax with one extra logit per head in the denominator only, by
+    explicit loops and without max subtraction (inputs keep exponents small):
+    o = sum_u e^{z_u} v_u / (sum_u e^{z_u} + e^{sink_h}).
+    Also returns two wrong forms: the sink's term added to every numerator
+    element as well (a sink key whose value is all ones), and the sink's term
+    left unshifted after the keys' own max is subtracted."""
+    T, Hq, d = q.shape
+    grp = Hq // dims.Hkv
+    good = np.zeros((T, Hq, d))
+    numer = np.zeros((T, Hq, d))
+    unshift = np.zeros((T, Hq, d))
+    for t in range(T):
+        p = int(pos[t])
+        lo = max(0, p - dims.window + 1) if mode == "swa" else 0
+        for h in range(Hq):
+            j = h // grp
+            ez = []
+            for u in range(lo, p + 1):
+                acc = 0.0
+                for i in range(d):
+                    acc += q[t, h, i] * K[0, j, u, i]
+                ez.append(math.exp(acc / math.sqrt(d)))
+            es = math.exp(float(sink[h]))
+            den = sum(ez) + es
+            zmax = max(math.log(e) for e in ez)
+            den_unshift = sum(e / math.exp(zmax) for e in ez) + es
+            for i in range(d):
+                num = sum(ez[n] * V[0, j, lo + n, i] for n in range(len(ez)))
+                good[t, h, i] = num / den
+                numer[t, h, i] = (num + es) / den
+                unshift[t, h, i] = num / math.exp(zmax) / den_unshift
+    return good, numer, unshift
+
+
+def _ulp_close(got, ref, ulps=1):
+    """Every element within `ulps` bf16 ulps of ref (float64 vs bf16-rounded)."""
+    u = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(ref), np.abs(got)) + 1e-300)) - 7)
+    return np.all(np.abs(got - ref) <= ulps * u)
+
+
+@pytest.mark.parametrize("mode", ["swa", "nope"])
+def test_attention_sink_brute_force(mode):
+    """The sink adds e^{sink} to the denominator only. Catches a sink term in
+    the numerator, a sink exponent not shifted by the subtracted max, and a
+    sink on the wrong head."""
+    dims = synth.with_dims(synth.config(0), sink=True).dims
+    g = np.random.default_rng(31)
+    Lm = 40
+    K = _tbf(g.standard_normal((1, dims.Hkv, Lm, dims.d)))
+    V = _tbf(g.standard_normal((1, dims.Hkv, Lm, dims.d)))
+    q = _tbf(g.standard_normal((3, dims.Hq, dims.d)) * 2.0)   # scores spread well off 0
+    pos = np.array([0, 15, 39])
+    sink = np.array([0.5, -1.0, 2.0, 3.5])
+    o = L.attention(dims, q, pos, np.zeros(3, int), _cache_from(K, V), mode, sink=sink)
+    good, numer, unshift = _sink_loops(dims, q, pos, K, V, mode, sink)
+    assert _ulp_close(o, good)
+    assert np.mean(o == _tbf(good)) > 0.99
+    for wrong in (numer, unshift):
+        assert not _ulp_close(o, wrong, ulps=4)
+    # per-head: the same sinks in another head order change the result
+    o_perm = L.attention(dims, q, pos, np.zeros(3, int), _cache_from(K, V), mode,
+                         sink=sink[::-1].copy())
+    assert not _ulp_close(o, o_perm, ulps=4)
+
+
+def test_attention_sink_limits_and_closed_forms():
+    dims = synth.with_dims(synth.config(0), sink=True).dims
+    g = np.random.default_rng(32)
+    K = _tbf(g.standard_normal((1, dims.Hkv, 64, dims.d)))
+    V = _tbf(g.standard_normal((1, dims.Hkv, 64, dims.d)))
+    q = _tbf(g.standard_normal((2, dims.Hq, dims.d)) * 2.0)
+    cache = _cache_from(K, V)
+    pos = np.array([9, 50])
+    seq = np.zeros(2, int)
+    # sink -> -inf leaves exactly the sink-free attention
+    for mode in ("swa", "nope"):
+        np.testing.assert_array_equal(
+            L.attention(dims, q, pos, seq, cache, mode, sink=np.full(dims.Hq, -1e30)),
+            L.attention(dims, q, pos, seq, cache, mode))
+    # sink -> +inf: every key's weight vanishes
+    big = L.attention(dims, q, pos, seq, cache, "nope", sink=np.full(dims.Hq, 200.0))
+    assert np.all(np.abs(big) < 1e-60)
+    # one key (position 0): o = v0 e^z / (e^z + e^s) = v0 * sigmoid(z - s)
+    grp = dims.Hq // dims.Hkv
+    sink = np.array([-2.0, 0.0, 1.5, 4.0])
+    o = L.attention(dims, q[:1], [0], [0], cache, "nope", sink=sink)
+    for h in range(dims.Hq):
+        z = float(q[0, h] @ K[0, h // grp, 0]) / math.sqrt(dims.d)
+        want = V[0, h // grp, 0] / (1.0 + math.exp(sink[h] - z))
+        assert _ulp_close(o[0, h], want)
+        # the wrong forms: sink in the numerator, or its exponent unshifted
+        wrong_num = (V[0, h // grp, 0] * math.exp(z) + math.exp(sink[h])) / \
+            (math.exp(z) + math.exp(sink[h]))
+        wrong_unshift = V[0, h // grp, 0] / (1.0 + math.exp(sink[h]))
+        assert not _ulp_close(o[0, h], wrong_num, ulps=4)
+        assert not _ulp_close(o[0, h], wrong_unshift, ulps=4)
+    # n identical keys of score z: o = (sum of their values) e^z / (n e^z + e^s)
+    K2 = np.broadcast_to(K[:, :, :1], K.shape).copy()
+    o = L.attention(dims, q[:1], [30], [0], _cache_from(K2, V), "swa", sink=sink)
+    lo = 30 - dims.window + 1
+    n = dims.window
+    for h in range(dims.Hq):
+        z = float(q[0, h] @ K2[0, h // grp, 0]) / math.sqrt(dims.d)
+        want = V[0, h // grp, lo:31].sum(axis=0) * math.exp(z) / (n * math.exp(z) +
+                                                                  math.exp(sink[h]))
+        assert _ulp_close(o[0, h], want)
+
+
+def _torch_swiglu(x, w13_bits, w2_bits, F):
+    """SwiGLU FFN through torch: bf16 after the gate/up product, after the
+    activation, and after the down product."""
+    w13 = torch.tensor(bf16_bits_to_f64(w13_bits))
+    w2 = torch.tensor(bf16_bits_to_f64(w2_bits))
+    u = torch.tensor(_tbf((torch.tensor(x) @ w13.T).numpy()))
+    act = torch.tensor(_tbf((Fn.silu(u[:, :F]) * u[:, F:]).numpy()))
+    return act @ w2.T
+
+
+def test_moe_shared_expert_pins():
+    """The shared expert is one more SwiGLU expert at weight exactly 1, added
+    for every token beside the routed ones. Pinned three ways: all routed
+    weights 0 gives torch's SwiGLU of the shared expert alone; at routed
+    weight 1 the MoE equals one dense FFN over the concatenated routed and
+    shared weights; at routed weights w the dense FFN with each expert's down
+    projection scaled by its weight (shared unscaled) gives the same sum.
+    Catches a shared weight other than 1, a shared term scaled by a routed
+    weight or the route scale, and a shared term that is skipped."""
+    dims = synth.with_dims(synth.config(0), shared=True).dims
+    p = synth.make_params(dims, 0, 2)
+    F = dims.F
+    g = np.random.default_rng(33)
+    T = 5
+    x = _tbf(g.standard_normal((T, dims.D)))
+    sel = [3, 7, 1, 12]
+    idx = np.tile(np.array(sel, np.int32), (T, 1))
+    get = lambda e: (p["w13"][e], p["w2"][e])  # noqa: E731
+    sh = (p["shared_w13"], p["shared_w2"])
+    y_sh = _torch_swiglu(x, sh[0], sh[1], F).numpy()
+    # routed weights 0: the shared expert alone
+    m0 = L.moe(dims, x, idx, np.zeros((T, 4), np.float32), get, shared=sh)
+    assert _ulp_close(m0, y_sh) and np.mean(m0 == _tbf(y_sh)) > 0.99
+    # routed weights 1: one dense FFN over the concatenated five experts
+    all13 = [p["w13"][e] for e in sel] + [sh[0]]
+    all2 = [p["w2"][e] for e in sel] + [sh[1]]
+    w13 = np.concatenate([a[:F] for a in all13] + [a[F:] for a in all13])
+    w2 = np.concatenate(all2, axis=1)
+    dense = L.dense_ffn(x, w13, w2, F * 5)
+    m1 = L.moe(dims, x, idx, np.ones((T, 4), np.float32), get, shared=sh)
+    assert _ulp_close(m1, dense) and np.mean(m1 == dense) > 0.99
+    # routed weights w: scale each routed expert's down projection by its weight
+    w = g.uniform(0.1, 1.2, (T, 4)).astype(np.float32)
+    for t in range(T):
+        w2s = np.concatenate([bf16_bits_to_f64(p["w2"][e]) * float(w[t, k])
+                              for k, e in enumerate(sel)] + [bf16_bits_to_f64(sh[1])], axis=1)
+        d_t = L.dense_ffn(x[t:t + 1], w13, w2s, F * 5)
+        m_t = L.moe(dims, x[t:t + 1], idx[t:t + 1], w[t:t + 1], get, shared=sh)
+        assert _ulp_close(m_t, d_t)
+    # the wrong forms differ from the pinned value by many ulps
+    routed = L.moe(dims, x, idx, np.ones((T, 4), np.float32), get)
+    for k in (0.0, 2.0, 2.5):
+        assert not _ulp_close(m1, _tbf(routed + k * y_sh), ulps=4)
+
+
+def test_prenorm_layer_form():
+    """layer_forward(sandwich=False): the pre-norm, plain-residual layer of
+    the second model: h_mid = h + y and h_out = h_mid + y2 with no post-norm,
+    each bf16; the next sublayer's input is the RMS norm of the residual.
+    Rebuilt from the layer's own intermediates with torch's rms_norm and
+    bf16 cast. Catches a post-norm that is still applied, a depth-scaled add,
+    and the residual index leaking into the plain add."""
+    cfg = synth.config(0)
+    dims = cfg.dims
+    p = synth.make_params(dims, 0, cfg.extra["layer"])
+    K, V, _, _ = synth.make_kv_prior(dims, 1, cfg.extra["ctx"], "bf16", 0, 2)
+
+    def run(params, n, sandwich):
+        cache = L.KVCache.empty(1, dims.Hkv, cfg.extra["Lmax"], dims.d)
+        cache.K[:, :, :cfg.extra["ctx"]] = bf16_bits_to_f64(K)
+        cache.V[:, :, :cfg.extra["ctx"]] = bf16_bits_to_f64(V)
+        h = synth.make_h((3, dims.D), 0, "prenorm")
+        return L.layer_forward(dims, params, h, np.arange(64, 67), np.zeros(3, int), cache,
+                               "swa", n, sandwich=sandwich), bf16_bits_to_f64(h)
+
+    r, h = run(p, cfg.extra["n"], False)
+    D = dims.D
+    rn = lambda v, w: Fn.rms_norm(torch.tensor(v), (D,), torch.tensor(bf16_bits_to_f64(w)),  # noqa
+                                  dims.eps).numpy()
+    np.testing.assert_array_equal(r["h_mid"], _tbf(h + r["y"]))
+    np.testing.assert_array_equal(r["x2"], _tbf(rn(r["h_mid"], p["w_ffn_pre"])))
+    np.testing.assert_array_equal(r["h_out"], _tbf(r["h_mid"] + r["y2"]))
+    np.testing.assert_array_equal(r["x_next"], _tbf(rn(r["h_out"], p["w_next_pre"])))
+    # the post-norm gains and the residual index play no part
+    p2 = dict(p)
+    p2["w_attn_post"] = None
+    p2["w_ffn_post"] = None
+    r2, _ = run(p2, 1, False)
+    for k in ("h_mid", "x2", "h_out", "x_next"):
+        np.testing.assert_array_equal(r2[k], r[k])
+    # and the sandwich form is a different layer
+    rs, _ = run(p, cfg.extra["n"], True)
+    assert not np.array_equal(rs["h_out"], r["h_out"])

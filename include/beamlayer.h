@@ -37,9 +37,12 @@
  *    shapes, alignment, workspace size); then the device is checked
  *    (BEAM_E_NODEV when no GPU is present); launch failures give BEAM_E_HIP.
  *    beam_last_error() returns a thread-local message for the last failure.
- *  - Data-dependent checks run on the device: a position outside the cache
- *    or an expert id outside [0, E) skips the offending token or expert and
- *    raises a device error flag that beam_check() reports.
+ *  - Data-dependent checks run on the device: a position outside the cache,
+ *    a position beyond the max_pos an attention call was given, or an expert
+ *    id outside [0, E) skips the offending token or expert (an attention
+ *    output row it leaves is written as zeros) and raises a device error flag
+ *    that beam_check() reports; so does a value the many-token attention
+ *    kernel had to clamp to the fp16 range of its P.V operand.
  *  - Threading: calls are reentrant; two calls that share output buffers or a
  *    workspace must be ordered by the caller (same stream).
  *
@@ -156,7 +159,9 @@ int beam_qk_norm_rope_ssmax_kvwrite(const beam_dims* dims, int T, const uint16_t
  * [max(0, pos[t]-window+1), pos[t]] (window keys including itself), scores
  * q.k/sqrt(d), fp32 softmax and accumulation, o [T][Hq][d] bf16.
  * sink (optional, [Flint]): per-head fp32 logit added to the softmax
- * denominator only. max_pos >= max(pos) (host value used to size the grid).
+ * denominator only. max_pos >= max(pos) (host value used to size the grid
+ * and the split-K records; a token beyond it is not attended: its output row
+ * is zero and the device flag is raised).
  * ws >= beam_workspace_size(ATTN_SWA, T, max_pos + 1) (counter block and
  * split-K partials).
  * Kernels: calls of T <= 4 tokens, and of T <= 256 tokens with T <= 4 * kv->S
@@ -166,7 +171,8 @@ int beam_qk_norm_rope_ssmax_kvwrite(const beam_dims* dims, int T, const uint16_t
  * precision of the P.V product: split-K kernels carry each probability to ~16
  * bits (a bf16 hi + lo pair), the flash kernel on a bf16 cache with d = 128
  * rounds probabilities to fp16 and converts V to fp16 (exact for bf16 values
- * of magnitude <= 65504; larger ones are clamped to +-65504).
+ * of magnitude <= 65504; larger ones are clamped to +-65504 and the device
+ * flag is raised, so beam_check reports BEAM_E_DEVICE for such a call).
  * Errors: window <= 0, max_pos >= Lmax. */
 int beam_attn_swa(const beam_dims* dims, int T, const uint16_t* q, const int32_t* pos,
                   const int32_t* seq, const beam_kv* kv, const float* sink, uint16_t* o,

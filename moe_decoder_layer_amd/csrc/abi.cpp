@@ -741,14 +741,17 @@ int beam_check(void* stream) {
   hipError_t e = hipStreamSynchronize(S_(stream));
   if (e != hipSuccess) return fail(BEAM_E_HIP, "beam_check: %s", hipGetErrorString(e));
   const int f = beam::gemv_read_clear_err() | beam::qk_read_clear_err() |
-                beam::attn_read_clear_err() | beam::moe_read_clear_err() |
+                beam::attn_read_clear_err() | beam::attnp_read_clear_err() |
+                beam::moe_read_clear_err() |
                 beam::mx_read_clear_err();
   if (f < 0) return fail(BEAM_E_HIP, "beam_check: reading the device flags failed");
   if (f)
-    return fail(BEAM_E_DEVICE, "beam_check: device check tripped:%s%s%s",
+    return fail(BEAM_E_DEVICE, "beam_check: device check tripped:%s%s%s%s%s",
                 (f & 1) ? " position outside the cache" : "",
                 (f & 2) ? " sequence slot outside the cache" : "",
-                (f & 4) ? " expert id outside [0, E)" : "");
+                (f & 4) ? " expert id outside [0, E)" : "",
+                (f & 8) ? " position beyond the call's max_pos" : "",
+                (f & 16) ? " value outside the fp16 range of the attention product" : "");
   return BEAM_OK;
 }
 

@@ -176,6 +176,9 @@ __device__ __forceinline__ float siluf(float x) {
     return v;                                                                    \
   }
 
-enum : int { ERR_POS = 1, ERR_SEQ = 2, ERR_EXPERT = 4 };
+// ERR_SPAN: a token's position lies beyond the max_pos its call was sized for.
+// ERR_RANGE: a value outside the range of an intermediate format (the prefill
+// attention's fp16 P.V operand) was clamped.
+enum : int { ERR_POS = 1, ERR_SEQ = 2, ERR_EXPERT = 4, ERR_SPAN = 8, ERR_RANGE = 16 };
 
 }  // namespace beam

@@ -129,6 +129,7 @@ int launch_hbm_read(const void* p, size_t bytes, unsigned* sink, hipStream_t st)
 int gemv_read_clear_err();
 int qk_read_clear_err();
 int attn_read_clear_err();
+int attnp_read_clear_err();
 int moe_read_clear_err();
 int mx_read_clear_err();
 

@@ -92,17 +92,25 @@ __device__ __forceinline__ void attn_decode_body(
   }
 
   const int p = pos[t], s = seq[t];
-  if (p < 0 || p >= Lmax || s < 0 || s >= S) {
-    if (c == 0 && j == 0 && threadIdx.x == 0) BEAM_RAISE(attn, p < 0 || p >= Lmax ? ERR_POS : ERR_SEQ);
+  const int CK = NW * 64 * tpw;
+  int bad = (p < 0 || p >= Lmax) ? ERR_POS : (s < 0 || s >= S) ? ERR_SEQ : 0;
+  int lo = 0, nch = 0;
+  if (!bad) {
+    lo = SWA ? max(0, p - window + 1) : 0;
+    nch = (p + 1 - (lo & ~63) + CK - 1) / CK;
+    // a position beyond the host's max_pos needs more chunks than the grid
+    // and the record stride were sized for: none of them runs (so no arrival
+    // is counted and no record is written out of place)
+    if (nch > nch_stride) bad = ERR_SPAN;
+  }
+  if (bad) {
+    if (c == 0 && j == 0 && threadIdx.x == 0) BEAM_RAISE(attn, bad);
     if (o_direct && c == 0)
       for (int i = threadIdx.x; i < grp * HD; i += NW * 64)
         o_direct[((size_t)t * Hq + j * grp) * HD + i] = 0;
     return;
   }
-  const int lo = SWA ? max(0, p - window + 1) : 0;
   const int lo_al = lo & ~63;
-  const int CK = NW * 64 * tpw;
-  const int nch = (p + 1 - lo_al + CK - 1) / CK;
   if (c >= nch) return;
 
   const size_t krow0 = ((size_t)s * Hkv + j) * (size_t)Lmax;  // K row of position 0
@@ -366,6 +374,10 @@ __global__ __launch_bounds__(256) void attn_merge_small_kernel(
   const int lo = swa ? max(0, p - window + 1) : 0;
   const int CK = 256 * tpw;
   const int nch = (p + 1 - (lo & ~63) + CK - 1) / CK;
+  if (nch > nch_stride) {  // beyond max_pos: flagged by the partial kernel, no records
+    for (int d = lane; d < HD; d += 64) out[d] = 0;
+    return;
+  }
   const float* rec0 = part + (size_t)u * nch_stride * (HD + 4);
   float mc[MX], lc[MX], oc[MX][DPL];
 #pragma unroll
@@ -429,6 +441,10 @@ __global__ __launch_bounds__(1024) void attn_merge_kernel(
   const int lo_al = lo & ~63;
   const int CK = 256 * tpw;
   const int nch = (p + 1 - lo_al + CK - 1) / CK;
+  if (nch > nch_stride) {  // beyond max_pos: flagged by the partial kernel, no records
+    for (int d = threadIdx.x; d < HD; d += MW * 64) out[d] = 0;
+    return;
+  }
   const float* rec0 = part + ((size_t)t * Hq + h) * nch_stride * (HD + 4);
   float M = -INFINITY, L = 0.f, O[DPL] = {};
   for (int c0 = wave; c0 < nch; c0 += MW * B) {

@@ -31,6 +31,9 @@
 
 namespace beam {
 
+BEAM_ERR_FLAG_DECL(attnp)
+BEAM_ERR_FLAG_READER(attnp)
+
 constexpr int KT = 64;  // keys per LDS tile
 
 template <int HD, bool FP8, bool SWA>
@@ -65,6 +68,7 @@ __global__ __launch_bounds__(768) void attn_prefill_kernel(
   const bool tok = t < T;
   int p = tok ? pos[t] : -1, s = tok ? seq[t] : -1;
   if (p < 0 || p >= Lmax || s < 0 || s >= S) {
+    if (tok && hh == 0) BEAM_RAISE(attnp, (p < 0 || p >= Lmax) ? ERR_POS : ERR_SEQ);
     p = -1;
     s = -1;
   }
@@ -336,6 +340,7 @@ __global__ __launch_bounds__(768) void attn_prefill_dma_kernel(
   const bool tok = t < T;
   int p = tok ? pos[t] : -1, s = tok ? seq[t] : -1;
   if (p < 0 || p >= Lmax || s < 0 || s >= S) {
+    if (tok && hh == 0) BEAM_RAISE(attnp, (p < 0 || p >= Lmax) ? ERR_POS : ERR_SEQ);
     p = -1;
     s = -1;
   }
@@ -428,11 +433,13 @@ __global__ __launch_bounds__(768) void attn_prefill_dma_kernel(
       const bool interior = all_mine && kb >= lo_max && kb + KT - 1 <= p_min;
       // The V^T tile becomes fp16 in place (the P.V product runs on fp16
       // operands: bf16 values in fp16's range convert exactly, larger ones are
-      // clamped to +-65504), and on an edge tile the keys outside the
-      // sequence's [kmin, kmax] become zero (they may hold anything). Chunk
-      // slot s of V^T row d holds keys 8 (s ^ (d % 8)) + [0, 8) of the tile.
+      // clamped to +-65504 and reported), and on an edge tile the keys outside
+      // the sequence's [kmin, kmax] become zero (they may hold anything).
+      // Chunk slot s of V^T row d holds keys 8 (s ^ (d % 8)) + [0, 8) of the
+      // tile.
       {
         uint4* vt = reinterpret_cast<uint4*>(sV(cur));
+        bool big = false;
         for (int c = tid; c < HD * KT / 8; c += nw * 64) {
           const int d = c >> 3, k0 = kb + 8 * ((c & 7) ^ (d & 7));
           const uint4 w = vt[c];
@@ -440,17 +447,20 @@ __global__ __launch_bounds__(768) void attn_prefill_dma_kernel(
           uint32_t out[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            float a = fminf(fmaxf(bf_lo(in[e]), -65504.f), 65504.f);
-            float b = fminf(fmaxf(bf_hi(in[e]), -65504.f), 65504.f);
+            float a = bf_lo(in[e]), b = bf_hi(in[e]);
             if (edge) {
               if (k0 + 2 * e < kmin || k0 + 2 * e > kmax) a = 0.f;
               if (k0 + 2 * e + 1 < kmin || k0 + 2 * e + 1 > kmax) b = 0.f;
             }
+            big |= (fabsf(a) > 65504.f) | (fabsf(b) > 65504.f);
+            a = fminf(fmaxf(a, -65504.f), 65504.f);
+            b = fminf(fmaxf(b, -65504.f), 65504.f);
             const f16x2 h = {(_Float16)a, (_Float16)b};
             out[e] = __builtin_bit_cast(uint32_t, h);
           }
           vt[c] = uint4{out[0], out[1], out[2], out[3]};
         }
+        if (big) BEAM_RAISE(attnp, ERR_RANGE);
         __syncthreads();
       }
       if (__any(mine)) {  // waves with no token of this sequence only load

@@ -13,10 +13,12 @@ import numpy as np
 import pytest
 import torch
 
+import moe_decoder_layer_amd as B
 import synth
-from beamrun import Cache, Params, assert_rms_close, bits_f64, check_routing, run_layer
+from beamrun import (Cache, Params, assert_rms_close, bits_f64, check_routing, dev, run_layer,
+                     ws)
 from oracle import layer as L
-from oracle.numerics import bf16_bits_to_f64, round_bf16
+from oracle.numerics import bf16_bits_to_f64, f64_to_bf16_bits, round_bf16
 
 pytestmark = [pytest.mark.gpu, pytest.mark.timeout(900)]
 
@@ -119,8 +121,69 @@ def _check(dims, P, cache, g, pos, seq, mode, n, ffn, upto):
     assert_rms_close(bits_f64(g["x_next"][ts]), xn, "x_next")
 
 
+NEEDLE_SCORES = (10.0, 10.5, 11.0, 11.5, 12.0, 12.5, 13.0, 13.5, 12.25)
+
+
+def _needle_positions(p, mode, W, prior):
+    """Keys a sampled token at position p gets a needle at: the first key,
+    both sides of a 64-key tile edge, the last prior key and the chunk's first
+    key, the token's own key and the one after it (a later token's: must be
+    masked); on SWA layers the window's first key and the key just before it
+    (outside the window: must be masked) instead of the first key."""
+    edge = p - p % 64
+    if mode == "nope":
+        return [0, 63, 64, edge - 1, edge, prior - 1, prior, p, p + 1]
+    return [p - W, p - W + 1, edge - 1, edge, prior - 1, prior, p, p + 1, p - W + 64]
+
+
+def _check_needles(dims, P, cache, g, pos, seq, mode, upto):
+    """Planted needles at full size: keys aligned with a sampled token's
+    query (score 10-13.5 each, so together they carry most of the softmax
+    mass over 100K random keys and dropping or adding one moves the output
+    by far more than the bar). The attention call is re-run on the needled
+    cache in the benchmark's launch configuration (all 16,384 tokens, the
+    GPU's own q) and the sampled tokens are checked against the oracle."""
+    ts = np.array([s * 2048 + c for s, c in SAMPLES])
+    grp = dims.Hq // dims.Hkv
+    row = {int(t): i for i, t in enumerate(ts)}
+    qf = bits_f64(g["q"][ts])
+    taken = {}
+    for t in ts:
+        for k, u in enumerate(_needle_positions(int(pos[t]), mode, dims.window, 100000)):
+            if 0 <= u < upto and (int(seq[t]), u) not in taken:
+                taken[(int(seq[t]), u)] = (t, NEEDLE_SCORES[k])
+    masked = 0
+    for (s, u), (t, sc) in taken.items():
+        qh = qf[row[int(t)], ::grp]  # the first query head of each kv head's group
+        kv = qh * (sc * np.sqrt(dims.d) / np.sum(qh * qh, axis=1, keepdims=True))
+        cache.K[s, :, u] = dev(f64_to_bf16_bits(kv))
+        p = int(pos[t])
+        lo = max(0, p - dims.window + 1) if mode == "swa" else 0
+        masked += not (lo <= u <= p)
+    assert masked >= len(ts)  # every token has at least one needle it must not see
+    T = len(pos)
+    pos_t = torch.as_tensor(pos).cuda()
+    seq_t = torch.as_tensor(seq).cuda()
+    o = torch.empty((T, dims.Hq, dims.d), dtype=torch.int16, device="cuda")
+    fn = B.beam_attn_swa if mode == "swa" else B.beam_attn_nope_ssmax
+    op = B.BEAM_OP_ATTN_SWA if mode == "swa" else B.BEAM_OP_ATTN_NOPE
+    fn(dims, T, dev(g["q"]), pos_t, seq_t, cache.struct(), None, o, upto - 1,
+       ws(dims, op, T, upto))
+    B.beam_check()
+    got = bits_f64(o[torch.as_tensor(ts).cuda()].cpu().numpy().view(np.uint16))
+    ref = L.attention(dims, qf, pos[ts], seq[ts], DeviceKV(cache, upto), mode)
+    # the needles carry most of the mass: the output is far from the random-key one
+    assert np.abs(ref - bits_f64(g["o"][ts])).max() > 0.3
+    e = assert_rms_close(got, ref, "o needles")
+    print(f"[prefill {mode}] attention with {len(taken)} needles ({masked} outside the "
+          f"token's range): max|err| {e:.3e} of rms(ref)", flush=True)
+
+
 @pytest.mark.parametrize("kind", ["nope_moe", "swa_moe", "dense"])
 def test_full_size_prefill(kind):
     r = _run(kind)
     print(f"[prefill {kind}] GPU layer done", flush=True)
     _check(*r)
+    if kind != "dense":  # the dense layer's attention is the SWA layer's kernel
+        dims, P, cache, g, pos, seq, mode, n, ffn, upto = r
+        _check_needles(dims, P, cache, g, pos, seq, mode, upto)

@@ -285,6 +285,86 @@ def test_workspace_counters_reused(mode):
     assert all(torch.equal(res[0][0], r[0]) and torch.equal(res[0][1], r[1]) for r in res)
 
 
+@pytest.mark.parametrize("mode,max_pos,bad_pos", [("nope", 1499, 1699), ("nope", 2999, 3999),
+                                                 ("swa", 100, 600)])
+def test_attention_beyond_max_pos_is_flagged(mode, max_pos, bad_pos):
+    """The split-K grid and its record stride are sized from the host's
+    max_pos. A token past it is not attended: its output row is zero, the call
+    reports the device flag, and the counter block is left zeroed, so the next
+    call on the same workspace is correct. The cases take the three combine
+    forms: merged by the last workgroup (NoPE, 6 chunks), by the merge kernel
+    (NoPE, 12 chunks) and one pass with no records (SWA, one chunk). A valid
+    token in the same call is unaffected."""
+    dims = BEAM
+    pos = np.array([min(max_pos, 1000), bad_pos], np.int32)
+    seq = np.zeros(2, np.int32)
+    q = dev(synth.make_h((2, dims.Hq, dims.d), 7, "mp", mode))
+    cache = _needle_cache(dims, 4096, 4000, "bf16", q, pos, seq, lambda p: [0, p], 5)
+    fn = B.beam_attn_swa if mode == "swa" else B.beam_attn_nope_ssmax
+    op = B.BEAM_OP_ATTN_SWA if mode == "swa" else B.BEAM_OP_ATTN_NOPE
+    w = ws(dims, op, 2, max_pos + 1)
+    o = torch.full((2, dims.Hq, dims.d), 0x3F80, **I16)  # 1.0: a row left unwritten shows
+    fn(dims, 2, q, dev(pos), dev(seq), cache.struct(), None, o, max_pos, w)
+    with pytest.raises(B.BeamError) as e:
+        B.beam_check()
+    assert e.value.code == -8 and "max_pos" in str(e.value)
+    assert int(w[:1024].count_nonzero()) == 0
+    assert int(o[1].count_nonzero()) == 0
+    qf = bits_f64(host_bits(q))
+    ref = L.attention(dims, qf[:1], pos[:1], seq[:1], cache.oracle(max_pos + 1), mode)
+    assert_rms_close(bits_f64(host_bits(o[:1])), ref, "o (valid token)")
+    # the next call on the same workspace, at max_pos itself
+    p2 = np.array([max_pos], np.int32)
+    o2 = torch.empty((1, dims.Hq, dims.d), **I16)
+    fn(dims, 1, q[1:2].contiguous(), dev(p2), dev(seq[:1]), cache.struct(), None, o2, max_pos, w)
+    B.beam_check()
+    assert int(w[:1024].count_nonzero()) == 0
+    ref2 = L.attention(dims, qf[1:2], p2, seq[:1], cache.oracle(max_pos + 1), mode)
+    assert_rms_close(bits_f64(host_bits(o2)), ref2, "o (next call)")
+
+
+@pytest.mark.parametrize("mode", ["swa", "nope"])
+def test_prefill_attention_flags(mode):
+    """The many-token kernel on a bf16 cache at head dim 128 takes P.V on fp16
+    operands. A cached value beyond fp16's range (7e4) is clamped to 65504 and
+    the call reports the device flag; the output then equals the oracle's
+    attention over the cache with that value clamped. A token at a negative
+    position is reported too and its output row is zero."""
+    dims = BEAM
+    T = 70
+    pos = np.arange(2900, 2970, dtype=np.int32)
+    seq = np.zeros(T, np.int32)
+    q = dev(synth.make_h((T, dims.Hq, dims.d), 3, "vclamp", mode))
+    cache = _needle_cache(dims, 4096, 2970, "bf16", q, pos, seq, lambda p: [], 5)
+    oc = cache.oracle(2970)
+    u = 2950 if mode == "nope" else 2960   # inside every later token's window
+    cache.V[0, 3, 17, u] = dev(_bits(np.array([7.0e4])))[0]
+    oc.V[0, 3, u, 17] = 65504.0
+    fn = B.beam_attn_swa if mode == "swa" else B.beam_attn_nope_ssmax
+    op = B.BEAM_OP_ATTN_SWA if mode == "swa" else B.BEAM_OP_ATTN_NOPE
+    o = torch.empty((T, dims.Hq, dims.d), **I16)
+    fn(dims, T, q, dev(pos), dev(seq), cache.struct(), None, o, 2969, ws(dims, op, T, 2970))
+    with pytest.raises(B.BeamError) as e:
+        B.beam_check()
+    assert e.value.code == -8 and "fp16" in str(e.value)
+    ref = L.attention(dims, bits_f64(host_bits(q)), pos, seq, oc, mode)
+    assert_rms_close(bits_f64(host_bits(o)), ref, "o (value clamped)")
+    # a negative position: reported, row zero, the other tokens unchanged
+    pos2 = pos.copy()
+    pos2[5] = -1
+    cache.V[0, 3, 17, u] = dev(_bits(np.array([1.0])))[0]
+    oc.V[0, 3, u, 17] = 1.0
+    o2 = torch.empty((T, dims.Hq, dims.d), **I16)
+    fn(dims, T, q, dev(pos2), dev(seq), cache.struct(), None, o2, 2969, ws(dims, op, T, 2970))
+    with pytest.raises(B.BeamError) as e:
+        B.beam_check()
+    assert e.value.code == -8 and "outside the cache" in str(e.value)
+    assert int(o2[5].count_nonzero()) == 0
+    keep = np.arange(T) != 5
+    ref2 = L.attention(dims, bits_f64(host_bits(q))[keep], pos[keep], seq[keep], oc, mode)
+    assert_rms_close(bits_f64(host_bits(o2))[keep], ref2, "o (other tokens)")
+
+
 # ------------------------------------------------------------------ gate + o_proj
 @pytest.mark.parametrize("base,T", [(CFG0, 1), (CFG0, 9), (BEAM, 1), (BEAM, 2),
                                     ("beam_no_gate", 1), ("beam_no_gate", 3)])
@@ -455,16 +535,37 @@ def test_moe(base, T):
     assert_rms_close(bits_f64(host_bits(y)), ref, "y2")
 
 
-def test_moe_shared_expert():
+@pytest.mark.parametrize("T,bad", [(3, False), (40, False), (300, False), (40, True),
+                                   (300, True)])
+def test_moe_shared_expert(T, bad):
+    """Shared expert beside the routed ones. T = 3 takes the one-token
+    kernels; T = 40 (200 routed + shared pairs) the grouped GEMM's 32-row
+    tiles; T = 300 (1,200 pairs, more than 16 per expert segment) its
+    256-row tiles walked expert by expert, with the shared expert's weights
+    taken from its own buffer for the last segment. bad: one routed id per
+    row of a few rows is out of range; it is reported and left out, and the
+    shared expert's row still lands in the combine."""
     dims = _dims(CFG0, shared=True, topk=3, n_group=1, topk_group=1)
     P = Params(dims, 0, 6)
-    T = 3
-    x = synth.make_h((T, dims.D), 7, "msx")
-    idx = np.array([[1, 5, 9], [0, 15, 7], [3, 4, 2]], np.int32)
-    w = np.full((T, 3), 0.3, np.float32)
+    x = synth.make_h((T, dims.D), 7, "msx", T)
+    g = np.random.default_rng(12)
+    idx = np.stack([g.choice(dims.E, 3, replace=False) for _ in range(T)]).astype(np.int32)
+    w = g.uniform(0.05, 0.6, (T, 3)).astype(np.float32)
+    rows = [1, T // 2, T - 1]
+    if bad:
+        for r, v in zip(rows, (dims.E, -1, dims.E + 7)):
+            idx[r, r % 3] = v
     y = torch.empty((T, dims.D), **I16)
     B.beam_moe_swiglu_combine(dims, T, dev(x), dev(idx), dev(w), P.t["w13"], P.t["w2"],
                               P.t["shared_w13"], P.t["shared_w2"], y, ws(dims, B.BEAM_OP_MOE, T))
+    if bad:
+        with pytest.raises(B.BeamError) as e:
+            B.beam_check()
+        assert e.value.code == -8
+        for r in rows:  # any valid id not already in the row, at weight 0
+            k = r % 3
+            idx[r, k] = next(i for i in range(dims.E) if i not in idx[r])
+            w[r, k] = 0.0
     B.beam_check()
     ref = L.moe(dims, x, idx, w, P.expert, shared=(P.np("shared_w13"), P.np("shared_w2")))
     assert_rms_close(bits_f64(host_bits(y)), ref, "y2")

@@ -51,12 +51,18 @@ def parse():
     ap.add_argument("--no-head", action="store_true",
                     help="skip the output head (logit soft cap) leg")
     ap.add_argument("--prefill-reps", type=int, default=3)
-    ap.add_argument("--cpu-steps", type=int, default=16)
+    ap.add_argument("--cpu-steps", type=int, default=8)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB copy kernel (HBM counter calibration)")
     ap.add_argument("--counters", action="store_true",
                     help="only launch the expert gate/up kernel, eagerly, 20 times "
                          "(a short program for rocprofv3 --pmc passes)")
+    ap.add_argument("--counters-step", action="store_true",
+                    help="only run 8 decode layer-steps of the SWA layer eagerly (every "
+                         "kernel of the step, for rocprofv3 --pmc passes)")
+    ap.add_argument("--counters-prefill", action="store_true",
+                    help="only run one pass of each prefill layer eagerly (for rocprofv3 "
+                         "--pmc passes)")
     return ap.parse_args()
 
 
@@ -105,6 +111,7 @@ class LayerSet:
         self.K[:, :, :ctx] = K
         self.V[:, :, :, :ctx] = V.transpose(2, 3)
         del K, V
+        self.ks, self.vs = ks, vs
         self.kv = B.kv_struct(self.K, self.V,
                               B.BEAM_KV_BF16 if kv == "bf16" else B.BEAM_KV_FP8_E4M3,
                               ks, vs, 1, Lmax)
@@ -134,8 +141,11 @@ def main():
                           "launches": 5}))
         return
 
+    if a.counters_prefill:
+        prefill_leg(a, counters=True)
+        return
     swa = decode_leg(a, 1)
-    if a.counters:
+    if a.counters or a.counters_step:
         return
     sets, dims, ex = swa.pop("_sets"), swa.pop("_dims"), swa.pop("_ex")
     us_step = swa["us_mean"]
@@ -178,8 +188,8 @@ def main():
         "value": round(us_step, 3),
         "unit": "µs/step",
         "n_gpus": 1,
-        "steps": swa["steps"],
-        "warmup": swa["warmup"],
+        "steps": a.steps,
+        "warmup": a.warmup,
         "ms_per_step": round(us_step / 1000.0, 6),
         "higher_is_better": False,
         "scaling": "weak",
@@ -190,7 +200,9 @@ def main():
                    "kv_cache": "bf16", "hidden": D, "q_heads": dims.Hq, "kv_heads": dims.Hkv,
                    "head_dim": dims.d, "window": dims.window, "experts": dims.E,
                    "topk": dims.topk, "expert_dff": dims.F, "weight_sets": 2,
-                   "graph_chain": a.chain},
+                   "graph_chain": swa["graph_chain"]},
+        "graph_replays": swa["graph_replays"],
+        "us_per_step_distribution": swa["distribution"],
         "us_per_step_median": swa["us_median"],
         "us_per_step_p90": swa["us_p90"],
         "roofline": {"bound": "hbm", "kernel": "expert_w13_swiglu_kernel",
@@ -202,14 +214,21 @@ def main():
                           "frac": round(step_gbs / HBM_PEAK_GBS, 4),
                           "measured_read_ceiling_gbs": round(ceiling, 1)},
     }
-    cpu_set = sets[0] if (a.no_prefill and a.no_nope) else None
+    cpu = {}
+    if not a.no_cpu_baseline:
+        cpu["decode_swa"] = cpu_decode(sets[0], dims, ex, "swa", a.cpu_steps)
     del sets
     torch.cuda.empty_cache()
     if not a.no_nope:
         nope = decode_leg(a, 2)
-        for k in ("_sets", "_dims", "_ex", "_x2", "_idx"):
+        nsets, ndims, nex = nope.pop("_sets"), nope.pop("_dims"), nope.pop("_ex")
+        for k in ("_x2", "_idx"):
             nope.pop(k)
         out["decode_nope"] = nope
+        if not a.no_cpu_baseline:
+            cpu["decode_nope_fp8"] = cpu_decode(nsets[0], ndims, nex, "nope",
+                                                max(2, a.cpu_steps // 2))
+        del nsets
         torch.cuda.empty_cache()
     for fmt in ([] if a.no_mx else ["mxfp8", "mxfp4"]):
         mxr = decode_leg(a, 1, fmt)
@@ -246,11 +265,9 @@ def main():
         out["decode_flint_b128"] = {m: flint_leg(a, m) for m in ("swa", "nope")}
         torch.cuda.empty_cache()
     if not a.no_prefill:
-        out["prefill"] = prefill_leg(a)
+        out["prefill"] = prefill_leg(a, cpu=cpu if not a.no_cpu_baseline else None)
     if not a.no_cpu_baseline:
-        if cpu_set is None:
-            cpu_set = LayerSet(dims, 0, ex["layer"], ex["pos"], ex["Lmax"])
-        out["cpu_baseline"] = cpu_baseline(cpu_set, dims, ex, a.cpu_steps)
+        out["cpu_baseline"] = cpu_summary(cpu)
     print(json.dumps(out))
 
 
@@ -305,6 +322,78 @@ def graph_us(fn, reps):
     e1.record(s)
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) * 1000.0 / (5 * reps)
+
+
+def timed_steps(step, nsets, warmup, steps, chain, min_replays=16):
+    """Exactly `warmup` untimed steps, then exactly `steps` timed steps, of
+    step(k) for absolute step index k (step k runs on weight set k % nsets).
+    Steps are replayed from HIP graphs of `chain` steps (the last replay of a
+    region holds the remainder); a graph is captured per (first weight set,
+    length) so the alternation holds across replay boundaries. The per-step
+    distribution (median, p90) comes from the timed replays when there are
+    at least min_replays of them, else from min_replays further replays of
+    the chain after the timed region (one graph replay costs a launch gap
+    of several us, so a one-step chain would measure launches, not steps).
+    Returns (us per step over the timed region, per-replay us-per-step of the
+    distribution sample, timed replays, chain, distribution source)."""
+    import numpy as np
+    import torch
+    c = max(1, min(chain, steps))
+    graphs = {}
+
+    def graph(k, n):
+        key = (k % nsets, n)
+        if key not in graphs:
+            stream = torch.cuda.Stream()
+            stream.wait_stream(torch.cuda.current_stream())
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.stream(stream):
+                with torch.cuda.graph(g, stream=stream):
+                    for i in range(n):
+                        step(k + i)
+            torch.cuda.current_stream().wait_stream(stream)
+            torch.cuda.synchronize()
+            graphs[key] = g
+        return graphs[key]
+
+    def plan(k0, total):
+        out, k = [], k0
+        while k < k0 + total:
+            n = min(c, k0 + total - k)
+            out.append((k, n))
+            k += n
+        return out
+
+    def replay(pl):
+        s = torch.cuda.current_stream()
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(len(pl) + 1)]
+        evs[0].record(s)
+        for r, (k, n) in enumerate(pl):
+            graph(k, n).replay()
+            evs[r + 1].record(s)
+        torch.cuda.synchronize()
+        per = np.array([evs[r].elapsed_time(evs[r + 1]) * 1000.0 / n
+                        for r, (k, n) in enumerate(pl)])
+        return evs[0].elapsed_time(evs[-1]) * 1000.0, per
+
+    warm, timed = plan(0, warmup), plan(warmup, steps)
+    for k, n in warm + timed:           # capture everything before any timing
+        graph(k, n)
+    for k, n in warm:
+        graph(k, n).replay()
+    torch.cuda.synchronize()
+    total_us, per = replay(timed)
+    us = total_us / steps
+    source = "timed region"
+    if len(timed) < min_replays:
+        k0 = warmup + steps
+        dist = [(k0 + i * c, c) for i in range(min_replays)]
+        for k, n in dist:
+            graph(k, n)
+        _, per = replay(dist)
+        source = f"{min_replays} replays of {c} steps after the timed region"
+    del graphs
+    return us, per, len(timed), c, source
 
 
 def decode_leg(a, ci, experts="bf16", ctx=None):
@@ -386,51 +475,36 @@ def decode_leg(a, ci, experts="bf16", ctx=None):
         print(json.dumps({"counters_run": "expert_w13_swiglu_kernel", "launches": 20,
                           "algorithmic_bytes_per_launch": up_bytes_of(dims)}))
         return {}
+    if a.counters_step:
+        torch.cuda.synchronize()
+        for i in range(8):
+            step(sets[i % 2])
+        torch.cuda.synchronize()
+        B.beam_check()
+        print(json.dumps({"counters_run": f"{mode} decode layer-steps", "steps": 8}))
+        return {}
+    # one eager chain validates the step before anything is captured
     for i in range(a.chain):
         step(sets[i % 2])
     B.beam_check()
     assert torch.isfinite(h.view(torch.bfloat16).float()).all(), "non-finite residual stream"
-
-    stream = torch.cuda.Stream()
-    stream.wait_stream(torch.cuda.current_stream())
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.stream(stream):
-        with torch.cuda.graph(graph, stream=stream):
-            for i in range(a.chain):
-                step(sets[i % 2])
-    torch.cuda.current_stream().wait_stream(stream)
-    torch.cuda.synchronize()
-
-    reps = max(1, a.steps // a.chain)
-    wreps = max(1, a.warmup // a.chain)
-    for _ in range(wreps):
-        graph.replay()
-    torch.cuda.synchronize()
+    steps = a.steps
+    us_step, per, reps, chain, dsrc = timed_steps(lambda k: step(sets[k % 2]), 2, a.warmup,
+                                                  steps, a.chain)
     B.beam_check()
-    s = torch.cuda.current_stream()
-    evs = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
-    evs[0].record(s)
-    for r in range(reps):
-        graph.replay()
-        evs[r + 1].record(s)
-    torch.cuda.synchronize()
-    steps = reps * a.chain
-    per = np.array([evs[r].elapsed_time(evs[r + 1]) for r in range(reps)]) * 1000.0 / a.chain
-    ms_total = evs[0].elapsed_time(evs[-1])
-    us_step = ms_total * 1000.0 / steps
-    B.beam_check()
-    log(f"[bench] {mode} decode: {steps} layer-steps in {ms_total:.2f} ms: {us_step:.2f} us/step "
-        f"(median {np.median(per):.2f}, p90 {np.percentile(per, 90):.2f})")
+    log(f"[bench] {mode} decode: {steps} layer-steps ({reps} graph replays of <= {chain}) in "
+        f"{us_step * steps / 1000:.2f} ms: {us_step:.2f} us/step "
+        f"(median {np.median(per):.2f}, p90 {np.percentile(per, 90):.2f} over {dsrc})")
     kv_read = dims.window if mode == "swa" else pos0 + 1
     kv_bytes = kv_read * dims.Hkv * dims.d * 2 * (2 if kvt == "bf16" else 1)
     kv_write = dims.Hkv * dims.d * 2 * (2 if kvt == "bf16" else 1)
     expert_bytes = dims.topk * 3 * dims.F * D * EXPERT_BYTES_PER_32[experts] // 32
     step_bytes = (dims.qkvg_rows * D * 2 + D * dims.Hq * dims.d * 2 + dims.E * D * 4
                   + expert_bytes + kv_bytes + kv_write)
-    del graph
     res = {"workload": f"beam_{mode}_moe_layer_decode", "kv_cache": kvt, "experts": experts,
            "context": pos0,
-           "steps": steps, "warmup": wreps * a.chain + a.chain,
+           "steps": steps, "warmup": a.warmup, "validation_steps": a.chain,
+           "graph_replays": reps, "graph_chain": chain, "distribution": dsrc,
            "us_mean": round(us_step, 3), "us_median": round(float(np.median(per)), 3),
            "us_p90": round(float(np.percentile(per, 90)), 3), "bytes_per_step": step_bytes,
            "hbm_frac": round(step_bytes / (us_step * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
@@ -539,30 +613,10 @@ def flint_leg(a, mode):
         distinct.append(len(np.unique(idx.cpu().numpy())))
     B.beam_check()
     assert torch.isfinite(h.view(torch.bfloat16).float()).all(), "non-finite residual stream"
-    stream = torch.cuda.Stream()
-    stream.wait_stream(torch.cuda.current_stream())
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.stream(stream):
-        with torch.cuda.graph(graph, stream=stream):
-            for i in range(a.chain):
-                step(sets[i % 2])
-    torch.cuda.current_stream().wait_stream(stream)
-    torch.cuda.synchronize()
-    reps = max(1, min(a.steps, 80) // a.chain)
-    for _ in range(2):
-        graph.replay()
-    torch.cuda.synchronize()
-    s = torch.cuda.current_stream()
-    evs = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
-    evs[0].record(s)
-    for r in range(reps):
-        graph.replay()
-        evs[r + 1].record(s)
-    torch.cuda.synchronize()
+    steps = min(a.steps, 80)
+    us_step, per, reps, chain, _ = timed_steps(lambda k: step(sets[k % 2]), 2,
+                                               min(a.warmup, 16), steps, a.chain)
     B.beam_check()
-    steps = reps * a.chain
-    per = np.array([evs[r].elapsed_time(evs[r + 1]) for r in range(reps)]) * 1000.0 / a.chain
-    us_step = evs[0].elapsed_time(evs[-1]) * 1000.0 / steps
     ne = float(np.mean(distinct))
     keys = (dims.window if mode == "swa" else ctx + 1)
     kv_bytes = T * keys * dims.Hkv * dims.d * 2 * 2
@@ -570,9 +624,10 @@ def flint_leg(a, mode):
                      + (ne + 1) * 3 * dims.F * D * 2 + kv_bytes + T * dims.Hkv * dims.d * 4)
     log(f"[bench] flint {mode} b{S} decode: {us_step:.2f} us/step (median {np.median(per):.2f}), "
         f"{ne:.1f} distinct experts/step, {step_bytes / (us_step * 1e-6) / 1e9:.0f} GB/s")
-    del graph, sets
+    del sets
     return {"workload": f"flint_{mode}_moe_layer_decode_b{S}", "batch": S, "context": ctx,
-            "kv_cache": "bf16", "steps": steps, "us_mean": round(us_step, 3),
+            "kv_cache": "bf16", "steps": steps, "warmup": min(a.warmup, 16),
+            "graph_replays": reps, "us_mean": round(us_step, 3),
             "us_median": round(float(np.median(per)), 3),
             "tokens_per_s": round(T / (us_step * 1e-6), 1),
             "distinct_experts_per_step": round(ne, 1), "bytes_per_step": step_bytes,
@@ -650,10 +705,12 @@ def measured_traffic():
         return None
 
 
-def prefill_leg(a):
+def prefill_leg(a, cpu=None, counters=False):
     """Chunked prefill: 8 sequences x 2048 new tokens, each after 100,000 prior
     tokens (bf16 cache), through one NoPE MoE layer, one SWA MoE layer and the
-    dense layer 0. Returns per-layer ms, tok/s and MFMA-roofline fraction."""
+    dense layer 0. Returns per-layer ms, tok/s and MFMA-roofline fraction.
+    cpu: a dict that gets the CPU oracle's sample of the NoPE layer.
+    counters: one eager pass of each layer only (for rocprofv3 --pmc)."""
     import numpy as np
     import torch
 
@@ -744,6 +801,11 @@ def prefill_leg(a):
         layer_fwd()
         torch.cuda.synchronize()
         B.beam_check()
+        if counters:
+            log(f"[bench] prefill {name}: one pass for counters")
+            del t, w13, w2, K, V, ws_f, ws_q, ws_a
+            torch.cuda.empty_cache()
+            continue
         reps = a.prefill_reps
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
@@ -762,52 +824,135 @@ def prefill_leg(a):
                      "algorithmic_flop": flops, "tflops": round(tf, 1),
                      "mfma_frac": round(tf / MFMA_PEAK_TFLOPS, 4)}
         log(f"[bench] prefill {name}: {ms:.2f} ms/layer, {T / ms * 1e3:.0f} tok/s, {tf:.0f} TFLOP/s")
+        if cpu is not None and name == "nope_moe":
+            cpu["prefill_nope_moe"] = cpu_prefill(t, w13, w2, K, V, h0, dims, mode, n, prior, 6)
+            cpu["prefill_nope_moe"]["gpu_tok_s"] = res[name]["tok_s"]
         del t, w13, w2, K, V, ws_f, ws_q, ws_a
         torch.cuda.empty_cache()
     res["workload"] = "8 sequences x 2048 new tokens after 100,000 prior tokens each, bf16 cache"
     return res
 
 
-def cpu_baseline(L: "LayerSet", dims, ex, nsteps):
-    """The CPU oracle, untuned, timed on this host over a bounded sample: nsteps
-    decode layer-steps of the same workload (same weights, same cache window)."""
-    import numpy as np
-
-    from oracle import layer as OL
+def _host_threads():
+    """Threads the oracle's BLAS actually runs with, the CPU model and the
+    process's CPU affinity."""
     try:
         from threadpoolctl import threadpool_info
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
         threads = os.cpu_count() or 1
-    import synth
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    aff = sorted(os.sched_getaffinity(0))
+    return int(threads), model, aff
 
+
+class _Fetch:
+    """Device -> host copies of expert weights, timed so that their time can
+    be taken out of the oracle's (the copies are not oracle work)."""
+
+    def __init__(self, w13, w2):
+        self.w13, self.w2, self.s = w13, w2, 0.0
+
+    def __call__(self, e):
+        import numpy as np
+        t0 = time.perf_counter()
+        r = (self.w13[e].cpu().numpy().view(np.uint16), self.w2[e].cpu().numpy().view(np.uint16))
+        self.s += time.perf_counter() - t0
+        return r
+
+
+def _host_params(t):
+    import numpy as np
     import torch
+    return {k: (v.cpu().numpy().view(np.uint16) if v.dtype == torch.int16 else v.cpu().numpy())
+            for k, v in t.items() if k not in ("w13", "w2")}
 
-    def hb(t):
-        return t.cpu().numpy().view(np.uint16) if t.dtype == torch.int16 else t.cpu().numpy()
-    P = {k: hb(v) for k, v in L.t.items() if k not in ("w13", "w2")}
-    get_expert = lambda e: (hb(L.t["w13"][e]), hb(L.t["w2"][e]))  # noqa: E731
-    pos0, W = ex["pos"], dims.window
-    lo = pos0 - W + 1
-    Kw = L.K[:, :, lo:pos0].cpu().numpy().view(np.uint16)
-    Vw = L.V[:, :, :, lo:pos0].transpose(2, 3).contiguous().cpu().numpy().view(np.uint16)
-    from oracle.numerics import bf16_bits_to_f64
-    cache = OL.KVCache.empty(1, dims.Hkv, pos0 + 1, dims.d)
-    cache.K[:, :, lo:pos0] = bf16_bits_to_f64(Kw)
-    cache.V[:, :, lo:pos0] = bf16_bits_to_f64(Vw)
-    h = synth.make_h((1, dims.D), 0, "cpu_baseline")
+
+def cpu_decode(L: "LayerSet", dims, ex, mode, nsteps):
+    """The CPU oracle, untuned, on a bounded sample of a decode leg: nsteps
+    chained layer-steps of the same workload (same weights; the same cache,
+    copied to the host before the timer). The expert weights a step selects
+    are copied from the device on demand and that copy time is excluded."""
+    import numpy as np
+
+    import synth
+    from oracle import layer as OL
+    from oracle.numerics import bf16_bits_to_f64, f64_to_bf16_bits
+    P = _host_params(L.t)
+    pos0 = ex["pos"]
+    if mode == "swa":                     # the window is all a sliding-window step reads
+        lo = pos0 - dims.window + 1
+        cache = OL.KVCache.empty(1, dims.Hkv, pos0 + 1, dims.d)
+        cache.K[:, :, lo:pos0] = bf16_bits_to_f64(L.K[:, :, lo:pos0].cpu().numpy().view(np.uint16))
+        cache.V[:, :, lo:pos0] = bf16_bits_to_f64(
+            L.V[:, :, :, lo:pos0].transpose(2, 3).contiguous().cpu().numpy().view(np.uint16))
+    else:                                 # fp8 codes of the whole context
+        cache = OL.KVCache.empty(1, dims.Hkv, pos0 + 1, dims.d, "fp8", L.ks, L.vs)
+        cache.K[:, :, :pos0] = L.K[:, :, :pos0].cpu().numpy()
+        cache.V[:, :, :pos0] = L.V[:, :, :, :pos0].transpose(2, 3).contiguous().cpu().numpy()
+    fetch = _Fetch(L.t["w13"], L.t["w2"])
+    h = synth.make_h((1, dims.D), 0, "cpu_baseline", mode)
     t0 = time.perf_counter()
-    for i in range(nsteps):
-        r = OL.layer_forward(dims, P, h, [pos0], [0], cache, "swa", ex["n"],
-                             get_expert=get_expert)
-        from oracle.numerics import f64_to_bf16_bits
+    for _ in range(nsteps):
+        r = OL.layer_forward(dims, P, h, [pos0], [0], cache, mode, ex["n"], get_expert=fetch)
         h = f64_to_bf16_bits(r["h_out"])
-    dt = time.perf_counter() - t0
-    return {"value": round(dt / nsteps * 1e6, 1), "unit": "µs/step", "cores": int(threads),
+    dt = time.perf_counter() - t0 - fetch.s
+    log(f"[bench] cpu oracle {mode} decode: {dt / nsteps * 1e3:.0f} ms/step over {nsteps} steps "
+        f"({fetch.s:.1f}s of expert copies excluded)")
+    return {"us_per_step": round(dt / nsteps * 1e6, 1), "steps": nsteps,
+            "oracle_s": round(dt, 2), "expert_copy_s_excluded": round(fetch.s, 2),
+            "workload": f"beam_{mode}_moe_layer_decode", "kv_cache": "bf16" if mode == "swa"
+            else "fp8", "context": pos0}
+
+
+def cpu_prefill(t, w13, w2, K, V, h0, dims, mode, n, prior, ntok):
+    """The CPU oracle on a bounded sample of the prefill workload: the first
+    ntok tokens of sequence 0's chunk (positions prior ..), attending over
+    the same prior cache (copied to the host before the timer), through the
+    same layer; reported as tokens per second."""
+    import numpy as np
+
+    from oracle import layer as OL
+    from oracle.numerics import bf16_bits_to_f64
+    P = _host_params(t)
+    cache = OL.KVCache.empty(1, dims.Hkv, prior + ntok, dims.d)
+    cache.K[:, :, :prior] = bf16_bits_to_f64(K[:1, :, :prior].cpu().numpy().view(np.uint16))
+    cache.V[:, :, :prior] = bf16_bits_to_f64(
+        V[:1, :, :, :prior].transpose(2, 3).contiguous().cpu().numpy().view(np.uint16))
+    h = h0[:ntok].cpu().numpy().view(np.uint16)
+    fetch = _Fetch(w13, w2)
+    pos = np.arange(prior, prior + ntok)
+    t0 = time.perf_counter()
+    OL.layer_forward(dims, P, h, pos, np.zeros(ntok, int), cache, mode, n, get_expert=fetch)
+    dt = time.perf_counter() - t0 - fetch.s
+    log(f"[bench] cpu oracle {mode} prefill sample: {ntok} tokens in {dt:.1f}s "
+        f"({fetch.s:.1f}s of expert copies excluded)")
+    return {"tok_s": round(ntok / dt, 4), "tokens": ntok, "oracle_s": round(dt, 2),
+            "expert_copy_s_excluded": round(fetch.s, 2),
+            "workload": f"{ntok} tokens of one sequence's 2048-token chunk after {prior} prior "
+                        f"tokens, {mode} MoE layer"}
+
+
+def cpu_summary(cpu):
+    """The cpu_baseline object: the headline decode leg's oracle time, with
+    the other legs' samples beside it."""
+    threads, model, aff = _host_threads()
+    d = cpu.get("decode_swa", {})
+    return {"value": d.get("us_per_step"), "unit": "µs/step", "cores": threads,
             "kind": "oracle",
-            "sample": f"{nsteps} chained decode layer-steps of the same workload (float64 "
-                      f"NumPy oracle; the 512-key window of the cache and the 8 selected "
-                      f"experts per step read from device memory), {dt:.1f}s total"}
+            "sample": (f"{d.get('steps')} chained decode layer-steps of the same workload "
+                       "(float64 NumPy oracle, cache window copied to the host before the "
+                       "timer, the selected experts' device-to-host copies excluded); "
+                       "further samples under legs"),
+            "cpu_model": model, "affinity": f"{len(aff)} cpus ({aff[0]}-{aff[-1]})" if aff
+            else "", "legs": cpu}
 
 
 if __name__ == "__main__":

@@ -63,7 +63,13 @@ __global__ __launch_bounds__(RT) void router_logits_gemm_kernel(
     Bs[kb + 0][rb] = b0.x; Bs[kb + 1][rb] = b0.y; Bs[kb + 2][rb] = b0.z; Bs[kb + 3][rb] = b0.w;
     Bs[kb + 4][rb] = b1.x; Bs[kb + 5][rb] = b1.y; Bs[kb + 6][rb] = b1.z; Bs[kb + 7][rb] = b1.w;
   };
-  float acc[4][4] = {};
+  // Sums in three levels: each 32-term slab from zero, eight slabs into a
+  // 256-term group, the groups into the total. A plain running sum over D
+  // terms rounds at the magnitude of the whole partial sum on every add (an
+  // error of order 2^-24 * |logit| * sqrt(D / 2)); this way only the D / 256
+  // group adds do.
+  float acc[4][4] = {}, grp[4][4] = {};
+  int nslab = 0;
   uint4 av;
   float4 b0, b1;
   load(kbeg, av, b0, b1);
@@ -71,6 +77,7 @@ __global__ __launch_bounds__(RT) void router_logits_gemm_kernel(
     store(av, b0, b1);
     __syncthreads();
     if (k0 + KB < kend) load(k0 + KB, av, b0, b1);
+    float sl[4][4] = {};
 #pragma unroll 8
     for (int k = 0; k < KB; ++k) {
       float a[4], b[4];
@@ -82,10 +89,28 @@ __global__ __launch_bounds__(RT) void router_logits_gemm_kernel(
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) acc[i][jj] = __builtin_fmaf(a[i], b[jj], acc[i][jj]);
+        for (int jj = 0; jj < 4; ++jj) sl[i][jj] = __builtin_fmaf(a[i], b[jj], sl[i][jj]);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) grp[i][jj] += sl[i][jj];
+    if (++nslab == 8) {
+      nslab = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          acc[i][jj] += grp[i][jj];
+          grp[i][jj] = 0.f;
+        }
     }
     __syncthreads();
   }
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) acc[i][jj] += grp[i][jj];
   float* out = logits + (size_t)blockIdx.z * T * E;
 #pragma unroll
   for (int i = 0; i < 4; ++i)

@@ -152,7 +152,7 @@ def _check_needles(dims, P, cache, g, pos, seq, mode, upto):
         for k, u in enumerate(_needle_positions(int(pos[t]), mode, dims.window, 100000)):
             if 0 <= u < upto and (int(seq[t]), u) not in taken:
                 taken[(int(seq[t]), u)] = (t, NEEDLE_SCORES[k])
-    masked = 0
+    masked = 0  # needles outside their own token's visible range
     for (s, u), (t, sc) in taken.items():
         qh = qf[row[int(t)], ::grp]  # the first query head of each kv head's group
         kv = qh * (sc * np.sqrt(dims.d) / np.sum(qh * qh, axis=1, keepdims=True))
@@ -160,7 +160,9 @@ def _check_needles(dims, P, cache, g, pos, seq, mode, upto):
         p = int(pos[t])
         lo = max(0, p - dims.window + 1) if mode == "swa" else 0
         masked += not (lo <= u <= p)
-    assert masked >= len(ts)  # every token has at least one needle it must not see
+    # a key after the token's own (every sampled token but the two at a chunk's
+    # end, whose sequence has no later key) or, on SWA layers, before its window
+    assert masked >= len(ts) - 2 and len(taken) - masked >= 2 * len(ts)
     T = len(pos)
     pos_t = torch.as_tensor(pos).cuda()
     seq_t = torch.as_tensor(seq).cuda()

@@ -186,6 +186,25 @@ int beam_attn_nope_ssmax(const beam_dims* dims, int T, const uint16_t* q,
                          const float* sink, uint16_t* o, int max_pos, void* ws,
                          size_t ws_bytes, void* stream);
 
+/* Allocation-free beam_attn_nope_ssmax, for callers that cannot allocate or
+ * pass a workspace (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation). Same arguments, results and errors as
+ * beam_attn_nope_ssmax without ws / ws_bytes: the split-K records and
+ * counters live in a static device array of 16 MiB per GPU (held by each GPU
+ * the library runs on until the process ends); its counter block is cleared
+ * by a kernel on `stream` at the start of every call. Calls whose workspace
+ * need (beam_workspace_size(ATTN_NOPE, T, max_pos + 1)) exceeds 16 MiB are
+ * rejected with BEAM_E_WORKSPACE before anything is launched. At the Beam
+ * shape (48 query / 8 kv heads of 128) one to four tokens fit at contexts up
+ * to 8M positions, a batch of 128 decode steps up to 81,920 positions, 256
+ * steps up to 32,768; many-token chunks (flash kernel) need the counters only.
+ * The call allocates nothing. Every call on one GPU shares that GPU's array:
+ * calls that overlap on one GPU (different streams, or threads) race and must
+ * be ordered by the caller. */
+int beam_attn_nope_ssmax_static(const beam_dims* dims, int T, const uint16_t* q,
+                                const int32_t* pos, const int32_t* seq, const beam_kv* kv,
+                                const float* sink, uint16_t* o, int max_pos, void* stream);
+
 /* Sigmoid output gate and o_proj ([Attn]; [Opt]/2 gate kernel):
  *   z = bf16(o * sigmoid(g + b_gate[head]))  elementwise over [T][Hq*d]
  *   y = bf16(z . w_o^T), w_o [D][Hq*d] bf16, y [T][D] bf16.

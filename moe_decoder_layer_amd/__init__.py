@@ -79,6 +79,8 @@ def lib():
                               P, c_size_t, P],
             "beam_attn_nope_ssmax": [POINTER(beam_dims), c_int, P, P, P, POINTER(beam_kv), P, P,
                                      c_int, P, c_size_t, P],
+            "beam_attn_nope_ssmax_static": [POINTER(beam_dims), c_int, P, P, P, POINTER(beam_kv),
+                                            P, P, c_int, P],
             "beam_out_gate": [POINTER(beam_dims), c_int, P, P, P, P, P, P, c_size_t, P],
             "beam_router_fp32_grouped_topk": [POINTER(beam_dims), c_int, P, P, P, P, P, P, P,
                                               c_size_t, P],
@@ -195,6 +197,13 @@ def beam_attn_nope_ssmax(dims, T, q, pos, seq, kv: beam_kv, sink, o, max_pos, ws
     wp, wb = _ws(ws)
     _call("beam_attn_nope_ssmax", ctypes.byref(d), T, _p(q), _p(pos), _p(seq),
           ctypes.byref(kv), _p(sink), _p(o), max_pos, wp, wb, _s(stream))
+
+
+def beam_attn_nope_ssmax_static(dims, T, q, pos, seq, kv: beam_kv, sink, o, max_pos,
+                                stream=None):
+    d = _d(dims)
+    _call("beam_attn_nope_ssmax_static", ctypes.byref(d), T, _p(q), _p(pos), _p(seq),
+          ctypes.byref(kv), _p(sink), _p(o), max_pos, _s(stream))
 
 
 def beam_out_gate(dims, T, o, g, b_gate, w_o, y, ws=None, stream=None):

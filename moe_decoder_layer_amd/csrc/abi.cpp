@@ -175,7 +175,8 @@ size_t ws_dense(int T, int Fd, int D) {
 
 int attn_impl(const beam_dims* dims, int T, const uint16_t* q, const int32_t* pos,
               const int32_t* seq, const beam_kv* kv, const float* sink, uint16_t* o,
-              int max_pos, void* ws, size_t ws_bytes, void* stream, int swa, const char* fn) {
+              int max_pos, void* ws, size_t ws_bytes, void* stream, int swa, const char* fn,
+              bool clear_ctl = false) {
   if (!dims) return fail(BEAM_E_NULL, "%s: dims is NULL", fn);
   if (!q || !pos || !seq || !o) return fail(BEAM_E_NULL, "%s: NULL tensor argument", fn);
   if (misaligned(q) || misaligned(o) || misaligned(ws) || misaligned(sink))
@@ -193,6 +194,8 @@ int attn_impl(const beam_dims* dims, int T, const uint16_t* q, const int32_t* po
       return fail(ws ? BEAM_E_WORKSPACE : BEAM_E_NULL, "%s: workspace %zu < %zu bytes", fn,
                   ws ? ws_bytes : 0, kCtl);
     if ((rc = device_ready())) return rc;
+    if (clear_ctl && beam::launch_zero_words(ws_ctl(ws), (int)(kCtl / 4), S_(stream)))
+      return launched(-1, fn);
     return launched(beam::launch_attn_prefill(T, dims->Hq, dims->Hkv, dims->d, swa, dims->window,
                                               fp8, q, pos, seq, kv->k, kv->v,
                                               fp8 ? kv->k_scale : 1.f, fp8 ? kv->v_scale : 1.f,
@@ -205,6 +208,8 @@ int attn_impl(const beam_dims* dims, int T, const uint16_t* q, const int32_t* po
     return fail(ws ? BEAM_E_WORKSPACE : BEAM_E_NULL, "%s: workspace %zu < %zu bytes", fn,
                 ws ? ws_bytes : 0, need);
   if ((rc = device_ready())) return rc;
+  if (clear_ctl && beam::launch_zero_words(ws_ctl(ws), (int)(kCtl / 4), S_(stream)))
+    return launched(-1, fn);
   return launched(beam::launch_attn_decode(T, dims->Hq, dims->Hkv, dims->d, swa, dims->window,
                                            fp8, q, pos, seq, kv->k, kv->v,
                                            fp8 ? kv->k_scale : 1.f, fp8 ? kv->v_scale : 1.f,
@@ -238,6 +243,28 @@ int check_router(const beam_dims* dims, int T, const uint16_t* x, const float* w
 }
 
 }  // namespace
+
+namespace beam {
+
+int abi_fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int attn_entry(const beam_dims* dims, int T, const uint16_t* q, const int32_t* pos,
+               const int32_t* seq, const beam_kv* kv, const float* sink, uint16_t* o,
+               int max_pos, void* ws, size_t ws_bytes, void* stream, int swa, bool clear_ctl,
+               const char* fn) {
+  return attn_impl(dims, T, q, pos, seq, kv, sink, o, max_pos, ws, ws_bytes, stream, swa, fn,
+                   clear_ctl);
+}
+
+}  // namespace beam
 
 extern "C" {
 

@@ -8,7 +8,20 @@
 
 #include <algorithm>
 
+#include "beamlayer.h"
+
 namespace beam {
+
+// Sets the thread-local message beam_last_error() returns; returns code.
+int abi_fail(int code, const char* fmt, ...);
+// The attention call behind beam_attn_swa / beam_attn_nope_ssmax (swa 1 / 0),
+// with every argument check; clear_ctl zeroes the workspace's counter block
+// (after the checks, on the call's stream) before the attention kernels run.
+int attn_entry(const beam_dims* dims, int T, const uint16_t* q, const int32_t* pos,
+               const int32_t* seq, const beam_kv* kv, const float* sink, uint16_t* o,
+               int max_pos, void* ws, size_t ws_bytes, void* stream, int swa, bool clear_ctl,
+               const char* fn);
+int launch_zero_words(unsigned* p, int n, hipStream_t st);
 
 int launch_boundary(int T, int D, const uint16_t* y, const uint16_t* w_post, uint16_t* h,
                     const uint16_t* w_pre, uint16_t* x_out, int n, float eps, hipStream_t st);

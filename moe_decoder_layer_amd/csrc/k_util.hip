@@ -28,6 +28,19 @@ __global__ __launch_bounds__(kReadThreads) void hbm_read_kernel(const uint4* __r
   if (acc == 0x9e3779b9u) sink[0] = acc;
 }
 
+// Zeroes n 32-bit words (a workspace's counter block) with vector stores: a
+// kernel rather than a memset node, so the clear also replays correctly from
+// a captured graph.
+__global__ __launch_bounds__(256) void zero_words_kernel(unsigned* __restrict__ p, int n) {
+  for (int i = blockIdx.x * 256 + threadIdx.x; i < n; i += gridDim.x * 256) p[i] = 0u;
+}
+
+int launch_zero_words(unsigned* p, int n, hipStream_t st) {
+  hipLaunchKernelGGL(zero_words_kernel, dim3(std::max(1, std::min((n + 255) / 256, 64))),
+                     dim3(256), 0, st, p, n);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
 int launch_hbm_read(const void* p, size_t bytes, unsigned* sink, hipStream_t st) {
   hipLaunchKernelGGL(hbm_read_kernel, dim3(kReadBlocks), dim3(kReadThreads), 0, st,
                      (const uint4*)p, bytes / 16, sink);

@@ -20,7 +20,7 @@ MIS = 0x10002        # misaligned
 
 def test_library_exports_every_declared_symbol():
     names = B.header_functions()
-    assert len(names) == 22
+    assert len(names) == 23
     L = ctypes.CDLL(B.LIB_PATH)
     for n in names:
         assert hasattr(L, n), n
@@ -202,3 +202,19 @@ def test_lm_head_validation_and_nodev():
     assert _rc(f, 1, 256, 1000, A, A, ctypes.c_float(float("inf")), A, None) == -2
     assert _rc(f, 1, 260, 1000, A, A, ctypes.c_float(30.0), A, None) == -3
     assert _rc(f, 1, 256, 1000, A, A, ctypes.c_float(30.0), A, None) == -7
+
+
+@cpu_only
+def test_static_attention_validation():
+    """The allocation-free attention call rejects, before touching the
+    device, a call whose split-K records exceed its static 16 MiB."""
+    d = _dims(1)
+    by = ctypes.byref(d)
+    kv = B.kv_struct(A, A, B.BEAM_KV_BF16, 1.0, 1.0, 128, 131072)
+    f = "beam_attn_nope_ssmax_static"
+    assert _rc(f, None, 1, A, A, A, ctypes.byref(kv), None, A, 100, None) == -1
+    assert _rc(f, by, 0, A, A, A, ctypes.byref(kv), None, A, 100, None) == -2
+    assert _rc(f, by, 128, A, A, A, ctypes.byref(kv), None, A, 100000, None) == -5
+    assert "static" in B.beam_last_error()
+    assert _rc(f, by, 128, A, A, A, ctypes.byref(kv), None, A, 81919, None) == -7  # fits: no device
+    assert _rc(f, by, 1, A, A, A, ctypes.byref(kv), None, A, 100000, None) == -7

@@ -50,6 +50,9 @@ def parse():
                     help="skip the NoPE fp8 decode leg at a 2^20-token context")
     ap.add_argument("--no-head", action="store_true",
                     help="skip the output head (logit soft cap) leg")
+    ap.add_argument("--unfused", action="store_true",
+                    help="batch-1 decode legs with the separate q/k, attention and gate + "
+                         "o_proj calls instead of the fused attention call")
     ap.add_argument("--prefill-reps", type=int, default=3)
     ap.add_argument("--cpu-steps", type=int, default=8)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -442,15 +445,22 @@ def decode_leg(a, ci, experts="bf16", ctx=None):
     wsz = lambda op, ctx=0: torch.zeros(max(256, B.beam_workspace_size(dims, op, 1, ctx)),  # noqa
                                         dtype=torch.uint8, device="cuda")
     ws_qkv, ws_attn = wsz(B.BEAM_OP_QKV), wsz(attn_op, pos0 + 1)
+    ws_fa = wsz(B.BEAM_OP_ATTN_DECODE_FUSED, pos0 + 1) if not a.unfused else None
     ws_r, ws_moe = wsz(B.BEAM_OP_ROUTER), wsz(B.BEAM_OP_MOE)
     moe_mx = getattr(B, f"beam_moe_swiglu_combine_{experts}", None)
+    z = torch.empty((1, dims.Hq * dims.d), **I16)
 
     def step(L: LayerSet):
         t = L.t
-        B.beam_qk_norm_rope_ssmax_kvwrite(dims, 1, x, t["w_qkvg"], t["w_qnorm"], t["w_knorm"],
-                                          pos, seq, m, rope, q, g, L.kv, ws_qkv)
-        attn(dims, 1, q, pos, seq, L.kv, None, o, pos0, ws_attn)
-        B.beam_out_gate(dims, 1, o, g, t["b_gate"], t["w_o"], y)
+        if a.unfused:
+            B.beam_qk_norm_rope_ssmax_kvwrite(dims, 1, x, t["w_qkvg"], t["w_qnorm"], t["w_knorm"],
+                                              pos, seq, m, rope, q, g, L.kv, ws_qkv)
+            attn(dims, 1, q, pos, seq, L.kv, None, o, pos0, ws_attn)
+            B.beam_out_gate(dims, 1, o, g, t["b_gate"], t["w_o"], y)
+        else:  # projection + q/k epilogue + attention + gate, then o_proj alone
+            B.beam_attn_decode_fused(dims, 1, x, t["w_qkvg"], t["w_qnorm"], t["w_knorm"], pos,
+                                     seq, m, rope, L.kv, None, t["b_gate"], None, z, pos0, ws_fa)
+            B.beam_out_gate(dims, 1, z, None, None, t["w_o"], y)
         # attention-side boundary + router in one call (the two calls fused)
         B.beam_boundary_router_fp32_grouped_topk(dims, 1, y, t["w_attn_post"], h, t["w_ffn_pre"],
                                                  x2, n, t["w_r"], t["b_corr"], idx, w, None,
@@ -502,7 +512,7 @@ def decode_leg(a, ci, experts="bf16", ctx=None):
     step_bytes = (dims.qkvg_rows * D * 2 + D * dims.Hq * dims.d * 2 + dims.E * D * 4
                   + expert_bytes + kv_bytes + kv_write)
     res = {"workload": f"beam_{mode}_moe_layer_decode", "kv_cache": kvt, "experts": experts,
-           "context": pos0,
+           "context": pos0, "attention_call": "separate" if a.unfused else "fused",
            "steps": steps, "warmup": a.warmup, "validation_steps": a.chain,
            "graph_replays": reps, "graph_chain": chain, "distribution": dsrc,
            "us_mean": round(us_step, 3), "us_median": round(float(np.median(per)), 3),

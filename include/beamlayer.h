@@ -88,7 +88,8 @@ enum beam_op {
   BEAM_OP_OUT_GATE = 4,  /* beam_out_gate                   */
   BEAM_OP_ROUTER = 5,    /* beam_router_fp32_grouped_topk   */
   BEAM_OP_MOE = 6,       /* beam_moe_swiglu_combine         */
-  BEAM_OP_DENSE = 7      /* beam_dense_swiglu (dims->F read as the dense d_ff) */
+  BEAM_OP_DENSE = 7,     /* beam_dense_swiglu (dims->F read as the dense d_ff) */
+  BEAM_OP_ATTN_DECODE_FUSED = 8 /* beam_attn_decode_fused                   */
 };
 
 /* Layer shape. D hidden size; Hq/Hkv query/kv heads (Hq % Hkv == 0, group
@@ -186,6 +187,30 @@ int beam_attn_nope_ssmax(const beam_dims* dims, int T, const uint16_t* q,
                          const float* sink, uint16_t* o, int max_pos, void* ws,
                          size_t ws_bytes, void* stream);
 
+/* One-token fused attention half for batch-1 decode ([Opt] changes 2, 5 and
+ * 6; [FlintOpt] low-latency path: q/k norm, RoPE and the KV write fused into
+ * the kernels next to them): the packed projection, then ONE attention
+ * kernel that applies the per-head q/k RMSNorm with RoPE (mode
+ * BEAM_SWA_ROPE) or the SSMax query scale (BEAM_NOPE_SSMAX) to the raw
+ * projection, writes the new k and v to the cache at (seq[0], pos[0]),
+ * attends (the sliding window or the full context, as beam_attn_swa /
+ * beam_attn_nope_ssmax) and, when dims->G > 0, applies the output gate at
+ * its merge:
+ *   z_out [1][Hq*d] = bf16(bf16(o) * sigmoid(g + b_gate[head]))   (G > 0)
+ *                   = o                                          (G == 0)
+ * so that beam_out_gate(..., g = NULL, ...) then runs o_proj on z_out alone.
+ * Results are those of beam_qk_norm_rope_ssmax_kvwrite, the attention call
+ * and the gate of beam_out_gate composed (same arithmetic). q_out
+ * (nullable) receives the normed q [1][Hq][d]. T must be 1 (otherwise
+ * BEAM_E_UNSUPPORTED). ws >= beam_workspace_size(ATTN_DECODE_FUSED, 1,
+ * max_pos + 1), counter block zeroed once. Errors as the three calls. */
+int beam_attn_decode_fused(const beam_dims* dims, int T, const uint16_t* x,
+                           const uint16_t* w_qkvg, const uint16_t* w_qnorm,
+                           const uint16_t* w_knorm, const int32_t* pos, const int32_t* seq,
+                           int mode, const float* rope_cs, const beam_kv* kv, const float* sink,
+                           const uint16_t* b_gate, uint16_t* q_out, uint16_t* z_out, int max_pos,
+                           void* ws, size_t ws_bytes, void* stream);
+
 /* Allocation-free beam_attn_nope_ssmax, for callers that cannot allocate or
  * pass a workspace (code under HIP graph capture, tight serving loops,
  * harnesses that forbid allocation). Same arguments, results and errors as
@@ -208,8 +233,10 @@ int beam_attn_nope_ssmax_static(const beam_dims* dims, int T, const uint16_t* q,
 /* Sigmoid output gate and o_proj ([Attn]; [Opt]/2 gate kernel):
  *   z = bf16(o * sigmoid(g + b_gate[head]))  elementwise over [T][Hq*d]
  *   y = bf16(z . w_o^T), w_o [D][Hq*d] bf16, y [T][D] bf16.
- * g == NULL (with G == 0): z = o (no gate). ws >= beam_workspace_size(OUT_GATE).
- * Errors: G not in {0, Hq*d}; g/b_gate NULL while G > 0. */
+ * g == NULL: z = o, o_proj alone (a layer without a gate, G == 0, or an input
+ * the gate was already applied to, e.g. by beam_attn_decode_fused).
+ * ws >= beam_workspace_size(OUT_GATE).
+ * Errors: G not in {0, Hq*d}; b_gate NULL while g is given. */
 int beam_out_gate(const beam_dims* dims, int T, const uint16_t* o, const uint16_t* g,
                   const uint16_t* b_gate, const uint16_t* w_o, uint16_t* y, void* ws,
                   size_t ws_bytes, void* stream);

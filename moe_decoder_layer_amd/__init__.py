@@ -29,7 +29,8 @@ __all__ = [
     "beam_check", "beam_last_error", "beam_version",
     "BEAM_SWA_ROPE", "BEAM_NOPE_SSMAX", "BEAM_KV_BF16", "BEAM_KV_FP8_E4M3",
     "BEAM_OP_QKV", "BEAM_OP_ATTN_SWA", "BEAM_OP_ATTN_NOPE", "BEAM_OP_OUT_GATE",
-    "BEAM_OP_ROUTER", "BEAM_OP_MOE", "BEAM_OP_DENSE", "LIB_PATH", "HEADER_PATH",
+    "BEAM_OP_ROUTER", "BEAM_OP_MOE", "BEAM_OP_DENSE", "BEAM_OP_ATTN_DECODE_FUSED", "LIB_PATH",
+    "HEADER_PATH",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -39,7 +40,7 @@ HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "beamlayer.h")
 BEAM_SWA_ROPE, BEAM_NOPE_SSMAX = 0, 1
 BEAM_KV_BF16, BEAM_KV_FP8_E4M3 = 0, 1
 (BEAM_OP_QKV, BEAM_OP_ATTN_SWA, BEAM_OP_ATTN_NOPE, BEAM_OP_OUT_GATE, BEAM_OP_ROUTER,
- BEAM_OP_MOE, BEAM_OP_DENSE) = range(1, 8)
+ BEAM_OP_MOE, BEAM_OP_DENSE, BEAM_OP_ATTN_DECODE_FUSED) = range(1, 9)
 
 
 class BeamError(RuntimeError):
@@ -81,6 +82,8 @@ def lib():
                                      c_int, P, c_size_t, P],
             "beam_attn_nope_ssmax_static": [POINTER(beam_dims), c_int, P, P, P, POINTER(beam_kv),
                                             P, P, c_int, P],
+            "beam_attn_decode_fused": [POINTER(beam_dims), c_int, P, P, P, P, P, P, c_int, P,
+                                       POINTER(beam_kv), P, P, P, P, c_int, P, c_size_t, P],
             "beam_out_gate": [POINTER(beam_dims), c_int, P, P, P, P, P, P, c_size_t, P],
             "beam_router_fp32_grouped_topk": [POINTER(beam_dims), c_int, P, P, P, P, P, P, P,
                                               c_size_t, P],
@@ -105,7 +108,9 @@ def lib():
             "beam_last_error": [],
         }
         for name, args in sig.items():
-            f = getattr(L, name)
+            f = getattr(L, name, None)
+            if f is None:  # absent from this build: calling it raises AttributeError
+                continue
             f.argtypes = args
             f.restype = c_int
         L.beam_last_error.restype = ctypes.c_char_p
@@ -197,6 +202,15 @@ def beam_attn_nope_ssmax(dims, T, q, pos, seq, kv: beam_kv, sink, o, max_pos, ws
     wp, wb = _ws(ws)
     _call("beam_attn_nope_ssmax", ctypes.byref(d), T, _p(q), _p(pos), _p(seq),
           ctypes.byref(kv), _p(sink), _p(o), max_pos, wp, wb, _s(stream))
+
+
+def beam_attn_decode_fused(dims, T, x, w_qkvg, w_qnorm, w_knorm, pos, seq, mode, rope_cs,
+                           kv: beam_kv, sink, b_gate, q_out, z_out, max_pos, ws, stream=None):
+    d = _d(dims)
+    wp, wb = _ws(ws)
+    _call("beam_attn_decode_fused", ctypes.byref(d), T, _p(x), _p(w_qkvg), _p(w_qnorm),
+          _p(w_knorm), _p(pos), _p(seq), mode, _p(rope_cs), ctypes.byref(kv), _p(sink),
+          _p(b_gate), _p(q_out), _p(z_out), max_pos, wp, wb, _s(stream))
 
 
 def beam_attn_nope_ssmax_static(dims, T, q, pos, seq, kv: beam_kv, sink, o, max_pos,

@@ -114,6 +114,13 @@ size_t ws_attn(const beam_dims* d, int swa, int T, int max_ctx) {
   if (nch == 1) return kCtl;
   return kCtl + align256((size_t)T * d->Hq * nch * (d->d + 4) * 4);
 }
+// One-token fused decode attention: [counters][raw q|k|v][gate][split-K
+// records], the records sized for the NoPE (full-context) span, which bounds
+// the sliding-window one.
+size_t ws_attn_fused(const beam_dims* d, int T, int max_ctx) {
+  return ws_attn(d, 0, T, max_ctx) + ws_qkv_payload(d, T) +
+         align256((size_t)T * d->G * 2);
+}
 size_t ws_out_gate_payload(const beam_dims* d, int T) {
   return align256((size_t)T * d->Hq * d->d * 2);
 }
@@ -347,6 +354,65 @@ int beam_qk_norm_rope_ssmax_kvwrite(const beam_dims* dims, int T, const uint16_t
                   __func__);
 }
 
+int beam_attn_decode_fused(const beam_dims* dims, int T, const uint16_t* x,
+                           const uint16_t* w_qkvg, const uint16_t* w_qnorm,
+                           const uint16_t* w_knorm, const int32_t* pos, const int32_t* seq,
+                           int mode, const float* rope_cs, const beam_kv* kv, const float* sink,
+                           const uint16_t* b_gate, uint16_t* q_out, uint16_t* z_out, int max_pos,
+                           void* ws, size_t ws_bytes, void* stream) {
+  REQ(dims);
+  REQ(x);
+  REQ(w_qkvg);
+  REQ(w_qnorm);
+  REQ(w_knorm);
+  REQ(pos);
+  REQ(seq);
+  REQ(z_out);
+  REQ(ws);
+  ALN(x);
+  ALN(w_qkvg);
+  ALN(q_out);
+  ALN(z_out);
+  ALN(ws);
+  ALN(sink);
+  int rc = check_dims_attn(dims, __func__);
+  if (rc) return rc;
+  if ((rc = check_kv(kv, __func__))) return rc;
+  UNSUP(T == 1, "%s: one token per call (T = %d); use the separate calls for more", __func__, T);
+  if (mode != BEAM_SWA_ROPE && mode != BEAM_NOPE_SSMAX)
+    return fail(BEAM_E_SHAPE, "%s: invalid mode %d", __func__, mode);
+  if (mode == BEAM_SWA_ROPE && !rope_cs)
+    return fail(BEAM_E_NULL, "%s: RoPE mode needs rope_cs", __func__);
+  if (mode == BEAM_SWA_ROPE && dims->window <= 0)
+    return fail(BEAM_E_SHAPE, "%s: window <= 0", __func__);
+  if (dims->G > 0 && !b_gate) return fail(BEAM_E_NULL, "%s: b_gate is NULL", __func__);
+  if (max_pos < 0 || max_pos >= kv->Lmax)
+    return fail(BEAM_E_SHAPE, "%s: max_pos %d outside [0, Lmax)", __func__, max_pos);
+  const size_t need = ws_attn_fused(dims, T, max_pos + 1);
+  if (ws_bytes < need)
+    return fail(BEAM_E_WORKSPACE, "%s: workspace %zu < %zu bytes", __func__, ws_bytes, need);
+  if ((rc = device_ready())) return rc;
+  const int swa = mode == BEAM_SWA_ROPE;
+  const int Nqkv = (dims->Hq + 2 * dims->Hkv) * dims->d;
+  uint16_t* qkv = (uint16_t*)ws_data(ws);
+  uint16_t* gbuf = (uint16_t*)(ws_data(ws) + ws_qkv_payload(dims, T));
+  float* part = (float*)(ws_data(ws) + ws_qkv_payload(dims, T) +
+                         align256((size_t)T * dims->G * 2));
+  if (beam::launch_gemv_qkvg(T, Nqkv + dims->G, dims->D, Nqkv, w_qkvg, x, qkv, gbuf, S_(stream)))
+    return launched(-1, __func__);
+  const int fp8 = kv->dtype == BEAM_KV_FP8_E4M3;
+  beam::AttnFuse fz{qkv, w_qnorm, w_knorm, rope_cs, dims->eps, swa ? 0 : 1,
+                    fp8 ? kv->k_scale : 1.f, fp8 ? kv->v_scale : 1.f,
+                    dims->G > 0 ? gbuf : nullptr, dims->G > 0 ? b_gate : nullptr, q_out};
+  return launched(beam::launch_attn_decode(T, dims->Hq, dims->Hkv, dims->d, swa, dims->window,
+                                           fp8, nullptr, pos, seq, kv->k, kv->v,
+                                           fp8 ? kv->k_scale : 1.f, fp8 ? kv->v_scale : 1.f,
+                                           kv->S, kv->Lmax, sink, z_out,
+                                           attn_span(dims, swa, max_pos + 1), part, ws_ctl(ws),
+                                           S_(stream), &fz),
+                  __func__);
+}
+
 int beam_attn_swa(const beam_dims* dims, int T, const uint16_t* q, const int32_t* pos,
                   const int32_t* seq, const beam_kv* kv, const float* sink, uint16_t* o,
                   int max_pos, void* ws, size_t ws_bytes, void* stream) {
@@ -377,12 +443,12 @@ int beam_out_gate(const beam_dims* dims, int T, const uint16_t* o, const uint16_
   int rc = check_dims_attn(dims, __func__);
   if (rc) return rc;
   SHAPE(T > 0, "%s: T <= 0", __func__);
-  if (dims->G > 0 && (!g || !b_gate))
-    return fail(BEAM_E_NULL, "%s: gate input or bias is NULL", __func__);
+  if (g && !b_gate) return fail(BEAM_E_NULL, "%s: gate bias is NULL", __func__);
+  const bool gate = dims->G > 0 && g != nullptr;
   const int K = dims->Hq * dims->d;
   if (T > beam::kGemvMaxT && K % 64 == 0) {
     const uint16_t* a = o;
-    if (dims->G) {
+    if (gate) {
       REQ(ws);
       if (ws_bytes < ws_out_gate(dims, T))
         return fail(BEAM_E_WORKSPACE, "%s: workspace %zu < %zu bytes", __func__, ws_bytes,
@@ -393,7 +459,7 @@ int beam_out_gate(const beam_dims* dims, int T, const uint16_t* o, const uint16_
                       ? (float*)(ws_data(ws) + ws_out_gate_payload(dims, T))
                       : nullptr;
     if ((rc = device_ready())) return rc;
-    if (dims->G) {
+    if (gate) {
       if (beam::launch_gate(T, dims->Hq, dims->d, o, g, b_gate, (uint16_t*)ws_data(ws),
                             S_(stream)))
         return launched(-1, __func__);
@@ -405,7 +471,7 @@ int beam_out_gate(const beam_dims* dims, int T, const uint16_t* o, const uint16_
   }
   if ((rc = device_ready())) return rc;
   return launched(beam::launch_gemv_gate_oproj(T, dims->D, K, dims->d, w_o, o,
-                                               dims->G ? g : nullptr, b_gate, y, S_(stream)),
+                                               gate ? g : nullptr, b_gate, y, S_(stream)),
                   __func__);
 }
 
@@ -732,6 +798,9 @@ size_t beam_workspace_size(const beam_dims* dims, int op, int T, int max_ctx) {
     case BEAM_OP_ROUTER: return ws_router(dims, T);
     case BEAM_OP_MOE: return ws_moe(dims, T);
     case BEAM_OP_DENSE: return ws_dense(T, dims->F, dims->D);
+    case BEAM_OP_ATTN_DECODE_FUSED:
+      if (max_ctx <= 0 || dims->Hkv <= 0) return (size_t)-1;
+      return ws_attn_fused(dims, T, max_ctx);
     default: return (size_t)-1;
   }
 }

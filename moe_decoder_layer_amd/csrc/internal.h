@@ -68,6 +68,22 @@ constexpr size_t kCtlBytes = 1024;
 constexpr int kAttnCounters = 256;      // (token, kv head) pairs with a fused merge
 constexpr int kAttnFusedMergeMax = 8;   // chunks the last workgroup still merges
 
+// The decode attention kernel's fused mode (one token): the projection's
+// epilogue (per-head q/k norm, RoPE or SSMax, the KV write) runs inside the
+// attention kernel on the raw q|k|v rows, and the output gate at its merge.
+struct AttnFuse {
+  const uint16_t* qkv;    // raw projection [T][(Hq + 2 Hkv) * d]
+  const uint16_t* wq;     // q / k norm gains [d]
+  const uint16_t* wk;
+  const float* rope;      // RoPE table [Lmax][d] (mode 0), else unused
+  float eps;
+  int mode;               // 0 RoPE (sliding window), 1 SSMax (NoPE)
+  float ks, vs;           // fp8 cache scales (1 for bf16)
+  const uint16_t* g;      // gate projection [T][Hq * d] and per-head bias, or null
+  const uint16_t* bgate;
+  uint16_t* q_out;        // normed q [T][Hq][d], or null
+};
+
 void attn_plan(int T, int Hkv, int span, int* tpw, int* nch);
 int attn_nch_bound(int T, int Hkv, int span);
 bool attn_fused_merge(int T, int Hkv, int nch);
@@ -75,7 +91,8 @@ int launch_attn_decode(int T, int Hq, int Hkv, int hd, int swa, int window, int 
                        const uint16_t* q, const int32_t* pos, const int32_t* seq,
                        const void* kc, const void* vc, float k_scale, float v_scale, int S,
                        int Lmax, const float* sink, uint16_t* o, int span, float* part,
-                       unsigned* ctr, hipStream_t st);
+                       unsigned* ctr, hipStream_t st,
+                       const AttnFuse* fuse = nullptr);
 
 // part: K-split partial logits, router_splits(T, E, D) x T x E fp32 (unused
 // and may be null when that is 1).

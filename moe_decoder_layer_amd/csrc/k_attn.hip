@@ -25,6 +25,7 @@
 // attn_merge_kernel; a span that fits one workgroup is normalised in place.
 #include "common.h"
 #include "internal.h"
+#include "qk_head.h"
 
 namespace beam {
 
@@ -62,27 +63,79 @@ __device__ __forceinline__ constexpr int half_key(int kh, int g) {
   return FP8 ? 16 * g + 8 * kh : 32 * kh + 8 * g;
 }
 
-template <int HD, bool FP8, bool SWA, int NW, int GS>
+// Replace element e of a 16-byte fragment (8 bf16 values / 16 fp8 codes).
+__device__ __forceinline__ void frag_set_u16(uint4& v, int e, uint16_t x) {
+  uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (e == 2 * i) w[i] = (w[i] & 0xffff0000u) | x;
+    if (e == 2 * i + 1) w[i] = (w[i] & 0x0000ffffu) | ((uint32_t)x << 16);
+  }
+  v = uint4{w[0], w[1], w[2], w[3]};
+}
+__device__ __forceinline__ void frag_set_u8(uint4& v, int e, uint8_t x) {
+  uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 16; ++i)
+    if (e == i) w[i >> 2] = (w[i >> 2] & ~(0xffu << (8 * (i & 3)))) | ((uint32_t)x << (8 * (i & 3)));
+  v = uint4{w[0], w[1], w[2], w[3]};
+}
+
+// The attention output element o (fp32) as stored with the output gate:
+// bf16(bf16(o) * sigmoid(g + b)), the gate formed exactly as the o_proj call's
+// gate prologue forms it (g: the gate projection's bf16 value, b: the head's
+// bias).
+__device__ __forceinline__ uint16_t attn_out_gated(float o, uint16_t g, float b) {
+  return f2bf(round_bf(o) * sigmoidf_fast(bf2f(g) + b));
+}
+
+template <int HD, bool FP8, bool SWA, int NW, int GS, bool FUSED>
 __device__ __forceinline__ void attn_decode_body(
     const uint16_t* __restrict__ q, const int32_t* __restrict__ pos,
     const int32_t* __restrict__ seq, const void* __restrict__ kc, const void* __restrict__ vc,
     int S, int Lmax, int Hq, int Hkv, int window, int tpw, float score_scale, int nch_stride,
     float* part, uint16_t* __restrict__ o_direct, const float* __restrict__ sink,
-    float v_scale, unsigned* ctr) {
+    float v_scale, unsigned* ctr, const AttnFuse fz) {
   constexpr int KS = HD / 32;  // k-steps of the score product
   constexpr int DT = HD / 16;  // 16-dim tiles of the output
   __shared__ float sm_m[NW][16], sm_l[NW][16];
   __shared__ float sm_o[NW][GS][HD + 4];
   __shared__ int s_last;
+  // FUSED: the group's normed q, and the new key and value (bf16 bits, or
+  // fp8 codes in the first HD bytes)
+  __shared__ __align__(16) uint16_t sq[FUSED ? GS : 1][FUSED ? HD : 8];
+  __shared__ __align__(16) uint16_t skv[FUSED ? 2 : 1][FUSED ? HD : 8];
+  // FUSED with the output gate: the group's gate values and biases
+  __shared__ uint16_t sg[FUSED ? GS * HD : 1];
+  __shared__ float sbg[FUSED ? GS : 1];
 
   const int c = blockIdx.x, j = blockIdx.y, t = blockIdx.z;
   const int grp = Hq / Hkv;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int g = lane >> 4, col = lane & 15;
 
+  // FUSED: the gate values this workgroup may need at its merge are requested
+  // first (they reach LDS with the epilogue's barrier), so the merge does not
+  // wait on them
+  constexpr int GPT = FUSED ? (GS * HD + NW * 64 - 1) / (NW * 64) : 1;
+  uint16_t gpre[GPT];
+  float bpre = 0.f;
+  const bool gated = FUSED && fz.g != nullptr;
+  if (gated) {
+#pragma unroll
+    for (int k = 0; k < GPT; ++k) {
+      const int i = threadIdx.x + k * NW * 64;
+      gpre[k] = i < grp * HD ? fz.g[((size_t)t * Hq + j * grp) * HD + i] : 0;
+    }
+    if ((int)threadIdx.x < grp) bpre = bf2f(fz.bgate[j * grp + threadIdx.x]);
+  }
   // the query fragments do not depend on the position: request them first
+  // (FUSED: formed below from the raw projection)
   bf16x8 qf[KS];
-  if (col < grp) {
+  if (FUSED) {
+#pragma unroll
+    for (int i = 0; i < KS; ++i) qf[i] = bf16x8{};
+  } else if (col < grp) {
     const uint16_t* qp = q + ((size_t)t * Hq + j * grp + col) * HD;
 #pragma unroll
     for (int i = 0; i < KS; ++i) qf[i] = as_bf16x8(ld16(qp + qk_dim<HD, FP8>(i, g)));
@@ -122,15 +175,15 @@ __device__ __forceinline__ void attn_decode_body(
 
   const bool rr = (o_direct != nullptr) && (ctr == nullptr);
   const int tile0 = (lo_al >> 6) + (rr ? wave : (c * NW + wave) * tpw);
-  for (int it = 0; it < tpw; ++it) {
-    const int kb = (tile0 + (rr ? it * NW : it)) << 6;
-    if (kb > p) break;
-    // The tile's K and V fragments are all requested before any is used (key
-    // slots permuted by slot_key, dims by qk_dim). Fragments stay in their
-    // stored form (fp8 codes: half the registers) until the product that uses
-    // them.
-    constexpr int KR = FP8 ? (KS + 1) / 2 : KS;  // 16-byte K loads per slot
-    uint4 kraw[4][KR];
+  // The tile's K and V fragments are all requested before any is used (key
+  // slots permuted by slot_key, dims by qk_dim). Fragments stay in their
+  // stored form (fp8 codes: half the registers) until the product that uses
+  // them.
+  constexpr int KR = FP8 ? (KS + 1) / 2 : KS;  // 16-byte K loads per slot
+  constexpr int VR = FP8 ? 1 : 2;              // 16-byte V loads per output tile
+  uint4 kraw[4][KR];
+  uint4 vraw[DT][VR];
+  auto load_tile = [&](int kb) {
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
       const int key = kb + slot_key<FP8>(st, col >> 2, col & 3);
@@ -149,8 +202,6 @@ __device__ __forceinline__ void attn_decode_body(
           kraw[st][i] = ld16((const uint16_t*)kc + kr + qk_dim<HD, FP8>(i, g));
       }
     }
-    constexpr int VR = FP8 ? 1 : 2;  // 16-byte V loads per output tile
-    uint4 vraw[DT][VR];
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
       const size_t vr = (vrow0 + dt * 16 + col) * (size_t)Lmax + kb;
@@ -161,6 +212,134 @@ __device__ __forceinline__ void attn_decode_body(
         vraw[dt][1] = ld16((const uint16_t*)vc + vr + half_key<FP8>(1, g));
       }
     }
+  };
+  const bool has_p = FUSED && (c == nch - 1);  // this workgroup's span ends at p
+  if constexpr (FUSED) {
+    // The first tile is requested, then the epilogue of the projection runs
+    // while it is in flight: the group's q heads (norm, RoPE or SSMax) into
+    // LDS (chunk 0 also stores them), and in the workgroup whose span holds
+    // position p the new key (norm, RoPE) and value, into LDS and the cache.
+    // No other workgroup reads slot p; this one takes the new key and value
+    // from LDS in place of the slot's old contents.
+    const int kb0 = tile0 << 6;
+    if (kb0 <= p) load_tile(kb0);
+    const int nheads = Hq + 2 * Hkv;
+    const uint16_t* row = fz.qkv + (size_t)t * nheads * HD;
+    const int half = HD / 2;
+    const int nitems = grp + (has_p ? 2 : 0);
+    for (int u = wave; u < nitems; u += NW) {
+      if (u < grp) {
+        const int h = j * grp + u;
+        float a, b;
+        qk_head_pair(row + (size_t)h * HD, true, HD, fz.wq, fz.wk, p, true, fz.mode, fz.rope,
+                     fz.eps, a, b);
+        if (lane < half) {
+          const uint16_t ba = f2bf(a), bb = f2bf(b);
+          sq[u][lane] = ba;
+          sq[u][lane + half] = bb;
+          if (fz.q_out && c == 0) {
+            fz.q_out[((size_t)t * Hq + h) * HD + lane] = ba;
+            fz.q_out[((size_t)t * Hq + h) * HD + lane + half] = bb;
+          }
+        }
+      } else if (u == grp) {  // the new key: K[s][j][p][:]
+        float a, b;
+        qk_head_pair(row + (size_t)(Hq + j) * HD, false, HD, fz.wq, fz.wk, p, true, fz.mode,
+                     fz.rope, fz.eps, a, b);
+        if (lane < half) {
+          const size_t kr = (krow0 + p) * HD;
+          if constexpr (FP8) {
+            uint8_t* k8 = reinterpret_cast<uint8_t*>(skv[0]);
+            const uint8_t ca = f2e4m3(__fdiv_rn(a, fz.ks)), cb = f2e4m3(__fdiv_rn(b, fz.ks));
+            k8[lane] = ca;
+            k8[lane + half] = cb;
+            ((uint8_t*)kc)[kr + lane] = ca;
+            ((uint8_t*)kc)[kr + lane + half] = cb;
+          } else {
+            const uint16_t ba = f2bf(a), bb = f2bf(b);
+            skv[0][lane] = ba;
+            skv[0][lane + half] = bb;
+            ((uint16_t*)kc)[kr + lane] = ba;
+            ((uint16_t*)kc)[kr + lane + half] = bb;
+          }
+        }
+      } else if (lane < half) {  // the new value, as produced: V^T[s][j][:][p]
+        const uint16_t* vsrc = row + (size_t)(Hq + Hkv + j) * HD;
+        const uint16_t va = vsrc[lane], vb = vsrc[lane + half];
+        const size_t ca0 = (vrow0 + lane) * (size_t)Lmax + p;
+        const size_t cb0 = (vrow0 + lane + half) * (size_t)Lmax + p;
+        if constexpr (FP8) {
+          uint8_t* v8 = reinterpret_cast<uint8_t*>(skv[1]);
+          const uint8_t ca = f2e4m3(__fdiv_rn(bf2f(va), fz.vs));
+          const uint8_t cb = f2e4m3(__fdiv_rn(bf2f(vb), fz.vs));
+          v8[lane] = ca;
+          v8[lane + half] = cb;
+          ((uint8_t*)vc)[ca0] = ca;
+          ((uint8_t*)vc)[cb0] = cb;
+        } else {
+          skv[1][lane] = va;
+          skv[1][lane + half] = vb;
+          ((uint16_t*)vc)[ca0] = va;
+          ((uint16_t*)vc)[cb0] = vb;
+        }
+      }
+    }
+    if (gated) {
+#pragma unroll
+      for (int k = 0; k < GPT; ++k) {
+        const int i = threadIdx.x + k * NW * 64;
+        if (i < grp * HD) sg[i] = gpre[k];
+      }
+      if ((int)threadIdx.x < grp) sbg[threadIdx.x] = bpre;
+    }
+    __syncthreads();
+    if (col < grp) {
+#pragma unroll
+      for (int i = 0; i < KS; ++i)
+        qf[i] = as_bf16x8(*reinterpret_cast<const uint4*>(&sq[col][qk_dim<HD, FP8>(i, g)]));
+    }
+  }
+  // FUSED: the new key and value replace slot p's stale contents in the
+  // fragments of the tile that holds p
+  auto patch_tile = [&](int kb) {
+    const uint8_t* k8 = reinterpret_cast<const uint8_t*>(skv[0]);
+    const uint8_t* v8 = reinterpret_cast<const uint8_t*>(skv[1]);
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      if (kb + slot_key<FP8>(st, col >> 2, col & 3) != p) continue;
+      if constexpr (FP8 && KS >= 2) {
+#pragma unroll
+        for (int i = 0; i < KR; ++i)
+          kraw[st][i] = *reinterpret_cast<const uint4*>(k8 + qk_dim<HD, FP8>(2 * i, g));
+      } else if constexpr (FP8) {
+        const uint2 w = *reinterpret_cast<const uint2*>(k8 + qk_dim<HD, FP8>(0, g));
+        kraw[st][0] = uint4{w.x, w.y, 0u, 0u};
+      } else {
+#pragma unroll
+        for (int i = 0; i < KS; ++i)
+          kraw[st][i] = *reinterpret_cast<const uint4*>(&skv[0][qk_dim<HD, FP8>(i, g)]);
+      }
+    }
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const int dim = dt * 16 + col;
+      if constexpr (FP8) {
+        const int e = p - (kb + half_key<FP8>(0, g));
+        if (e >= 0 && e < 16) frag_set_u8(vraw[dt][0], e, v8[dim]);
+      } else {
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh) {
+          const int e = p - (kb + half_key<FP8>(kh, g));
+          if (e >= 0 && e < 8) frag_set_u16(vraw[dt][kh], e, skv[1][dim]);
+        }
+      }
+    }
+  };
+  for (int it = 0; it < tpw; ++it) {
+    const int kb = (tile0 + (rr ? it * NW : it)) << 6;
+    if (kb > p) break;
+    if (!FUSED || it > 0) load_tile(kb);
+    if (has_p && kb <= p && p < kb + 64) patch_tile(kb);
     f32x4 sacc[4];
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
@@ -272,7 +451,9 @@ __device__ __forceinline__ void attn_decode_body(
         L = L * a + exp2f(sl2 - Mn);
         O *= a;
       }
-      o_direct[((size_t)t * Hq + j * grp + hh) * HD + dim] = f2bf(O * (v_scale / L));
+      const size_t oi = ((size_t)t * Hq + j * grp + hh) * HD + dim;
+      o_direct[oi] = gated ? attn_out_gated(O * (v_scale / L), sg[hh * HD + dim], sbg[hh])
+                           : f2bf(O * (v_scale / L));
       continue;
     }
     float* rec = part + (((size_t)t * Hq + j * grp + hh) * nch_stride + c) * (HD + 4);
@@ -323,7 +504,10 @@ __device__ __forceinline__ void attn_decode_body(
 #pragma unroll
     for (int k = 0; k < DPL; ++k) {
       const int d = lane + 64 * k;
-      if (d < HD) o_direct[((size_t)t * Hq + j * grp + hh) * HD + d] = f2bf(O[k] * inv);
+      const size_t oi = ((size_t)t * Hq + j * grp + hh) * HD + d;
+      if (d < HD)
+        o_direct[oi] = gated ? attn_out_gated(O[k] * inv, sg[hh * HD + d], sbg[hh])
+                             : f2bf(O[k] * inv);
     }
   }
 }
@@ -333,22 +517,22 @@ __device__ __forceinline__ void attn_decode_body(
       const int32_t *__restrict__ seq, const void *__restrict__ kc,                         \
       const void *__restrict__ vc, int S, int Lmax, int Hq, int Hkv, int window, int tpw,   \
       float score_scale, int nch_stride, float *part, uint16_t *__restrict__ o_direct,      \
-      const float *__restrict__ sink, float v_scale, unsigned *ctr
+      const float *__restrict__ sink, float v_scale, unsigned *ctr, const AttnFuse fz
 #define ATTN_DECODE_ARGS                                                                 \
   q, pos, seq, kc, vc, S, Lmax, Hq, Hkv, window, tpw, score_scale, nch_stride, part, o_direct, \
-      sink, v_scale, ctr
+      sink, v_scale, ctr, fz
 
-template <int HD, bool FP8, bool SWA, int NW, int GS>
+template <int HD, bool FP8, bool SWA, int NW, int GS, bool FUSED>
 __global__ __launch_bounds__(NW * 64) void attn_decode_partial_kernel(ATTN_DECODE_PARAMS) {
-  attn_decode_body<HD, FP8, SWA, NW, GS>(ATTN_DECODE_ARGS);
+  attn_decode_body<HD, FP8, SWA, NW, GS, FUSED>(ATTN_DECODE_ARGS);
 }
 
 // Long split-K spans over an fp8 cache: the register budget is held to three
 // waves per SIMD (from two), which keeps more of the cache stream in flight.
-template <int HD, bool SWA>
+template <int HD, bool SWA, bool FUSED>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void
 attn_decode_fp8_stream_kernel(ATTN_DECODE_PARAMS) {
-  attn_decode_body<HD, true, SWA, 4, 16>(ATTN_DECODE_ARGS);
+  attn_decode_body<HD, true, SWA, 4, 16, FUSED>(ATTN_DECODE_ARGS);
 }
 
 // The same combine for spans of at most kAttnFusedMergeMax chunks, one wave
@@ -358,7 +542,7 @@ __global__ __launch_bounds__(256) void attn_merge_small_kernel(
     const float* __restrict__ part, const int32_t* __restrict__ pos,
     const int32_t* __restrict__ seq, int S, int Lmax, int T, int Hq, int window, int swa,
     int tpw, int nch_stride, const float* __restrict__ sink, float v_scale,
-    uint16_t* __restrict__ o) {
+    uint16_t* __restrict__ o, const uint16_t* __restrict__ G, const uint16_t* __restrict__ bgate) {
   constexpr int MX = kAttnFusedMergeMax;
   constexpr int DPL = (HD + 63) / 64;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -366,6 +550,14 @@ __global__ __launch_bounds__(256) void attn_merge_small_kernel(
   if (u >= T * Hq) return;
   const int t = u / Hq, h = u - t * Hq;
   uint16_t* out = o + (size_t)u * HD;
+  uint16_t gp[DPL] = {};  // the output gate's inputs, requested first
+  float bp = 0.f;
+  if (G) {
+#pragma unroll
+    for (int k = 0; k < DPL; ++k)
+      if (lane + 64 * k < HD) gp[k] = G[(size_t)u * HD + lane + 64 * k];
+    bp = bf2f(bgate[h]);
+  }
   const int p = pos[t], s = seq[t];
   if (p < 0 || p >= Lmax || s < 0 || s >= S) {
     for (int d = lane; d < HD; d += 64) out[d] = 0;
@@ -412,7 +604,7 @@ __global__ __launch_bounds__(256) void attn_merge_small_kernel(
 #pragma unroll
   for (int k = 0; k < DPL; ++k) {
     const int d = lane + 64 * k;
-    if (d < HD) out[d] = f2bf(O[k] * inv);
+    if (d < HD) out[d] = G ? attn_out_gated(O[k] * inv, gp[k], bp) : f2bf(O[k] * inv);
   }
 }
 
@@ -424,7 +616,8 @@ template <int HD>
 __global__ __launch_bounds__(1024) void attn_merge_kernel(
     const float* __restrict__ part, const int32_t* __restrict__ pos,
     const int32_t* __restrict__ seq, int S, int Lmax, int Hq, int window, int swa, int tpw,
-    int nch_stride, const float* __restrict__ sink, float v_scale, uint16_t* __restrict__ o) {
+    int nch_stride, const float* __restrict__ sink, float v_scale, uint16_t* __restrict__ o,
+    const uint16_t* __restrict__ G, const uint16_t* __restrict__ bgate) {
   constexpr int DPL = (HD + 63) / 64;
   constexpr int B = 8;
   constexpr int MW = 16;  // waves
@@ -432,6 +625,14 @@ __global__ __launch_bounds__(1024) void attn_merge_kernel(
   const int h = blockIdx.x, t = blockIdx.y;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   uint16_t* out = o + ((size_t)t * Hq + h) * HD;
+  uint16_t gp[DPL] = {};  // the output gate's inputs (wave 0 stores), requested first
+  float bp = 0.f;
+  if (G && wave == 0) {
+#pragma unroll
+    for (int k = 0; k < DPL; ++k)
+      if (lane + 64 * k < HD) gp[k] = G[((size_t)t * Hq + h) * HD + lane + 64 * k];
+    bp = bf2f(bgate[h]);
+  }
   const int p = pos[t], s = seq[t];
   if (p < 0 || p >= Lmax || s < 0 || s >= S) {
     for (int d = threadIdx.x; d < HD; d += MW * 64) out[d] = 0;
@@ -510,7 +711,7 @@ __global__ __launch_bounds__(1024) void attn_merge_kernel(
 #pragma unroll
   for (int k = 0; k < DPL; ++k) {
     const int d = lane + 64 * k;
-    if (d < HD) out[d] = f2bf(Ot[k] * inv);
+    if (d < HD) out[d] = G ? attn_out_gated(Ot[k] * inv, gp[k], bp) : f2bf(Ot[k] * inv);
   }
 }
 
@@ -543,7 +744,7 @@ int launch_attn_decode(int T, int Hq, int Hkv, int hd, int swa, int window, int 
                        const uint16_t* q, const int32_t* pos, const int32_t* seq,
                        const void* kc, const void* vc, float k_scale, float v_scale, int S,
                        int Lmax, const float* sink, uint16_t* o, int span, float* part,
-                       unsigned* ctr, hipStream_t st) {
+                       unsigned* ctr, hipStream_t st, const AttnFuse* fuse) {
   const float score_scale = k_scale / sqrtf((float)hd) * 1.4426950408889634f;
   const float vsc = fp8 ? v_scale : 1.0f;
   int tpw, nch;
@@ -552,12 +753,26 @@ int launch_attn_decode(int T, int Hq, int Hkv, int hd, int swa, int window, int 
   const bool fused = attn_fused_merge(T, Hkv, nch);
   uint16_t* od = (nch == 1 || fused) ? o : nullptr;
   unsigned* cp = fused ? ctr : nullptr;
-#define ARGS q, pos, seq, kc, vc, S, Lmax, Hq, Hkv, window, tpw, score_scale, nch, part, od, sink, vsc, cp
-#define PART(HD_, F8, SW)                                                                   \
-  hipLaunchKernelGGL((attn_decode_partial_kernel<HD_, F8, SW, 4, 16>), grid, dim3(256), 0, \
-                     st, ARGS)
-#define STREAM(HD_, SW) \
-  hipLaunchKernelGGL((attn_decode_fp8_stream_kernel<HD_, SW>), grid, dim3(256), 0, st, ARGS)
+  const AttnFuse fz = fuse ? *fuse : AttnFuse{};
+#define ARGS q, pos, seq, kc, vc, S, Lmax, Hq, Hkv, window, tpw, score_scale, nch, part, od, sink, vsc, cp, fz
+#define PART(HD_, F8, SW)                                                                     \
+  do {                                                                                        \
+    if (fuse)                                                                                 \
+      hipLaunchKernelGGL((attn_decode_partial_kernel<HD_, F8, SW, 4, 16, true>), grid,        \
+                         dim3(256), 0, st, ARGS);                                             \
+    else                                                                                      \
+      hipLaunchKernelGGL((attn_decode_partial_kernel<HD_, F8, SW, 4, 16, false>), grid,       \
+                         dim3(256), 0, st, ARGS);                                             \
+  } while (0)
+#define STREAM(HD_, SW)                                                                       \
+  do {                                                                                        \
+    if (fuse)                                                                                 \
+      hipLaunchKernelGGL((attn_decode_fp8_stream_kernel<HD_, SW, true>), grid, dim3(256), 0,  \
+                         st, ARGS);                                                           \
+    else                                                                                      \
+      hipLaunchKernelGGL((attn_decode_fp8_stream_kernel<HD_, SW, false>), grid, dim3(256), 0, \
+                         st, ARGS);                                                           \
+  } while (0)
 #define BY_MODE(HD_)                                                   \
   if (fp8 && !od) {                                                   \
     if (swa) STREAM(HD_, true); else STREAM(HD_, false);              \
@@ -576,11 +791,13 @@ int launch_attn_decode(int T, int Hq, int Hkv, int hd, int swa, int window, int 
   if (hipGetLastError() != hipSuccess) return -1;
   if (od) return 0;
   const float vs = fp8 ? v_scale : 1.0f;
+  const uint16_t* G = fz.g;
+  const uint16_t* bg = fz.bgate;
   if (nch <= kAttnFusedMergeMax) {
     const dim3 sg((T * Hq + 3) / 4);
 #define SMALL(HD_)                                                                              \
   hipLaunchKernelGGL((attn_merge_small_kernel<HD_>), sg, dim3(256), 0, st, part, pos, seq, S,   \
-                     Lmax, T, Hq, window, swa, tpw, nch, sink, vs, o)
+                     Lmax, T, Hq, window, swa, tpw, nch, sink, vs, o, G, bg)
     if (hd == 128) SMALL(128);
     else if (hd == 64) SMALL(64);
     else SMALL(32);
@@ -590,13 +807,13 @@ int launch_attn_decode(int T, int Hq, int Hkv, int hd, int swa, int window, int 
   const dim3 mg(Hq, T);
   if (hd == 128)
     hipLaunchKernelGGL((attn_merge_kernel<128>), mg, dim3(1024), 0, st, part, pos, seq, S, Lmax, Hq,
-                       window, swa, tpw, nch, sink, vs, o);
+                       window, swa, tpw, nch, sink, vs, o, G, bg);
   else if (hd == 64)
     hipLaunchKernelGGL((attn_merge_kernel<64>), mg, dim3(1024), 0, st, part, pos, seq, S, Lmax, Hq,
-                       window, swa, tpw, nch, sink, vs, o);
+                       window, swa, tpw, nch, sink, vs, o, G, bg);
   else
     hipLaunchKernelGGL((attn_merge_kernel<32>), mg, dim3(1024), 0, st, part, pos, seq, S, Lmax, Hq,
-                       window, swa, tpw, nch, sink, vs, o);
+                       window, swa, tpw, nch, sink, vs, o, G, bg);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

@@ -453,6 +453,19 @@ int launch_gemv_gate_oproj(int T, int N, int K, int hd, const uint16_t* W, const
                            hipStream_t st) {
   constexpr int R = 1;
   const dim3 grid((N + 4 * R - 1) / (4 * R), 1);
+  if (T == 1 && G == nullptr && (K & 511) == 0) {
+    // no gate prologue: the weights-first GEMV (each wave's whole row in
+    // flight before the activation is staged)
+    const int nb = K >> 9;  // 16-byte chunks per lane
+    const dim3 g1((N + 3) / 4);
+    const size_t sh = (size_t)K * 2;
+#define WF(NB) hipLaunchKernelGGL((gemv_qkvg_wf_kernel<NB>), g1, dim3(GT), sh, st, W, N, K, O, N, Y, nullptr)
+    if (nb == 12) { WF(12); return LAUNCH_OK(); }
+    if (nb == 10) { WF(10); return LAUNCH_OK(); }
+    if (nb == 8) { WF(8); return LAUNCH_OK(); }
+    if (nb == 4) { WF(4); return LAUNCH_OK(); }
+#undef WF
+  }
   if (T == 1) {
     const size_t sh = (size_t)K * 2;
     const int nb = nb_for(K >> 3);

@@ -10,6 +10,45 @@
 
 namespace beam {
 
+// The per-head RMSNorm of a q or k head (gain wq / wk over d), then RoPE at
+// position p (mode 0, table row p: cos then sin) or, for q, the SSMax scale
+// (1 + (p + 1) / 2048)^0.1 (mode 1). Lane i < d/2 gets elements i and
+// i + d/2 in (a, b); other lanes get zeros. slot_ok false: no rotation.
+__device__ __forceinline__ void qk_head_pair(const uint16_t* src, bool is_q, int hd,
+                                             const uint16_t* __restrict__ wq,
+                                             const uint16_t* __restrict__ wk, int p,
+                                             bool slot_ok, int mode,
+                                             const float* __restrict__ rope_cs, float eps,
+                                             float& a, float& b) {
+  const int lane = threadIdx.x & 63;
+  const int half = hd >> 1;
+  const bool act = lane < half;
+  a = act ? bf2f(src[lane]) : 0.f;
+  b = act ? bf2f(src[lane + half]) : 0.f;
+  // gains and the RoPE row are requested before the reduction needs `a`, `b`
+  const uint16_t* w = is_q ? wq : wk;
+  const float wa = act ? bf2f(w[lane]) : 0.f, wb = act ? bf2f(w[lane + half]) : 0.f;
+  const bool rot = (mode == 0) && slot_ok && act;
+  const float c = rot ? rope_cs[(size_t)p * hd + lane] : 1.f;
+  const float sn = rot ? rope_cs[(size_t)p * hd + half + lane] : 0.f;
+  const float r = rsqrtf(wave_sum(a * a + b * b) / hd + eps);
+  if (act) {
+    a = a * r * wa;
+    b = b * r * wb;
+    if (mode == 0) {  // RoPE at position p (table row p: cos then sin)
+      if (slot_ok) {
+        const float a2 = a * c - b * sn;
+        const float b2 = b * c + a * sn;
+        a = a2;
+        b = b2;
+      }
+    } else if (is_q) {  // SSMax: (1 + p/2048)^0.1 with the 1-based position p+1
+      const float sc = __powf(1.0f + (float)(p + 1) * (1.0f / 2048.0f), 0.1f);
+      a *= sc;
+      b *= sc;
+    }
+  }
+}
 
 // head in [0, Hq + 2 Hkv): q heads, then k heads, then v heads. src: the
 // head's d bf16 projection values; q_row: the token's q output [Hq][d].
@@ -42,29 +81,7 @@ __device__ __forceinline__ void qk_head(const uint16_t* src, int head, int Hq, i
     return;
   }
   const bool is_q = head < Hq;
-  // gains and the RoPE row are requested before the reduction needs `a`, `b`
-  const uint16_t* w = is_q ? wq : wk;
-  const float wa = act ? bf2f(w[lane]) : 0.f, wb = act ? bf2f(w[lane + half]) : 0.f;
-  const bool rot = (mode == 0) && slot_ok && act;
-  const float c = rot ? rope_cs[(size_t)p * hd + lane] : 1.f;
-  const float sn = rot ? rope_cs[(size_t)p * hd + half + lane] : 0.f;
-  const float r = rsqrtf(wave_sum(a * a + b * b) / hd + eps);
-  if (act) {
-    a = a * r * wa;
-    b = b * r * wb;
-    if (mode == 0) {  // RoPE at position p (table row p: cos then sin)
-      if (slot_ok) {
-        const float a2 = a * c - b * sn;
-        const float b2 = b * c + a * sn;
-        a = a2;
-        b = b2;
-      }
-    } else if (is_q) {  // SSMax: (1 + p/2048)^0.1 with the 1-based position p+1
-      const float sc = __powf(1.0f + (float)(p + 1) * (1.0f / 2048.0f), 0.1f);
-      a *= sc;
-      b *= sc;
-    }
-  }
+  qk_head_pair(src, is_q, hd, wq, wk, p, slot_ok, mode, rope_cs, eps, a, b);
   if (is_q) {
     if (act) {
       uint16_t* qo = q_row + (size_t)head * hd;

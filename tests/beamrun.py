@@ -251,9 +251,11 @@ def ws(dims, op, T, ctx=0):
 
 
 def run_layer(dims, P: Params, cache: Cache, h_bits, pos, seq, mode: str, n: int,
-              ffn="moe", rope=None, keep=True, sandwich=True) -> dict:
+              ffn="moe", rope=None, keep=True, sandwich=True, fused=False) -> dict:
     """One layer through the C ABI. Returns host copies of every intermediate.
-    sandwich False: the pre-norm, plain-residual layer form (no post-norms)."""
+    sandwich False: the pre-norm, plain-residual layer form (no post-norms).
+    fused: the attention half through beam_attn_decode_fused (one token), then
+    o_proj alone on its gated output; "z" replaces "o" in the result."""
     T = len(pos)
     D = dims.D
     t = P.t
@@ -270,20 +272,34 @@ def run_layer(dims, P: Params, cache: Cache, h_bits, pos, seq, mode: str, n: int
     m = B.BEAM_SWA_ROPE if mode == "swa" else B.BEAM_NOPE_SSMAX
     if rope is None and mode == "swa":
         rope = rope_table(cache.Lmax, dims.d, dims.theta)
-    wsq = ws(dims, B.BEAM_OP_QKV, T)
-    B.beam_qk_norm_rope_ssmax_kvwrite(dims, T, x, t["w_qkvg"], t["w_qnorm"], t["w_knorm"],
-                                      pos_t, seq_t, m, rope if mode == "swa" else None, q,
-                                      g if dims.G else None, kvs, wsq)
     nqkv = (dims.Hq + 2 * dims.Hkv) * dims.d
-    out["qkv"] = host_bits(ws_payload(wsq, T * nqkv * 2).view(torch.int16).view(T, nqkv))
-    o = torch.empty((T, dims.Hq, dims.d), **I16)
     max_pos = int(np.max(pos))
-    attn = B.beam_attn_swa if mode == "swa" else B.beam_attn_nope_ssmax
-    op = B.BEAM_OP_ATTN_SWA if mode == "swa" else B.BEAM_OP_ATTN_NOPE
-    attn(dims, T, q, pos_t, seq_t, kvs, t.get("sink"), o, max_pos, ws(dims, op, T, max_pos + 1))
     y = torch.empty((T, D), **I16)
-    B.beam_out_gate(dims, T, o, g if dims.G else None, t.get("b_gate"), t["w_o"], y,
-                    ws(dims, B.BEAM_OP_OUT_GATE, T))
+    if fused:
+        wsf = ws(dims, B.BEAM_OP_ATTN_DECODE_FUSED, T, max_pos + 1)
+        z = torch.empty((T, dims.Hq * dims.d), **I16)
+        B.beam_attn_decode_fused(dims, T, x, t["w_qkvg"], t["w_qnorm"], t["w_knorm"], pos_t,
+                                 seq_t, m, rope if mode == "swa" else None, kvs, t.get("sink"),
+                                 t.get("b_gate"), q, z, max_pos, wsf)
+        out["qkv"] = host_bits(ws_payload(wsf, T * nqkv * 2).view(torch.int16).view(T, nqkv))
+        goff = -(-T * nqkv * 2 // 256) * 256  # the gate follows the 256-aligned q|k|v rows
+        if dims.G:
+            g = ws_payload(wsf, goff + T * dims.G * 2)[goff:].view(torch.int16).view(T, dims.G)
+        B.beam_out_gate(dims, T, z, None, None, t["w_o"], y, ws(dims, B.BEAM_OP_OUT_GATE, T))
+        out["z"], o = host_bits(z), None
+    else:
+        wsq = ws(dims, B.BEAM_OP_QKV, T)
+        B.beam_qk_norm_rope_ssmax_kvwrite(dims, T, x, t["w_qkvg"], t["w_qnorm"], t["w_knorm"],
+                                          pos_t, seq_t, m, rope if mode == "swa" else None, q,
+                                          g if dims.G else None, kvs, wsq)
+        out["qkv"] = host_bits(ws_payload(wsq, T * nqkv * 2).view(torch.int16).view(T, nqkv))
+        o = torch.empty((T, dims.Hq, dims.d), **I16)
+        attn = B.beam_attn_swa if mode == "swa" else B.beam_attn_nope_ssmax
+        op = B.BEAM_OP_ATTN_SWA if mode == "swa" else B.BEAM_OP_ATTN_NOPE
+        attn(dims, T, q, pos_t, seq_t, kvs, t.get("sink"), o, max_pos,
+             ws(dims, op, T, max_pos + 1))
+        B.beam_out_gate(dims, T, o, g if dims.G else None, t.get("b_gate"), t["w_o"], y,
+                        ws(dims, B.BEAM_OP_OUT_GATE, T))
     h_in = h.clone()
     x2 = torch.empty((T, D), **I16)
     if sandwich:
@@ -311,7 +327,8 @@ def run_layer(dims, P: Params, cache: Cache, h_bits, pos, seq, mode: str, n: int
     else:
         B.beam_boundary_norm_residual(dims, T, y2, None, h, t["w_next_pre"], xn, 0)
     B.beam_check()
-    out.update(x=host_bits(x), q=host_bits(q), g=host_bits(g), o=host_bits(o), y=host_bits(y),
+    out.update(x=host_bits(x), q=host_bits(q), g=host_bits(g),
+               o=host_bits(o) if o is not None else None, y=host_bits(y),
                h_in=host_bits(h_in), h_mid=host_bits(h_mid), x2=host_bits(x2), y2=host_bits(y2),
                h_out=host_bits(h), x_next=host_bits(xn))
     return out

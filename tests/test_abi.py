@@ -20,7 +20,7 @@ MIS = 0x10002        # misaligned
 
 def test_library_exports_every_declared_symbol():
     names = B.header_functions()
-    assert len(names) == 23
+    assert len(names) == 24
     L = ctypes.CDLL(B.LIB_PATH)
     for n in names:
         assert hasattr(L, n), n
@@ -124,7 +124,8 @@ def test_attention_router_moe_validation():
                None) == -7
     assert _rc("beam_dense_swiglu", 1, 256, 100, A, A, A, A, A, 1 << 20, None) == -2
     assert _rc("beam_dense_swiglu", 1, 256, 512, A, A, A, A, A, 1 << 20, None) == -7
-    assert _rc("beam_out_gate", by, 1, A, None, A, A, A, None, 0, None) == -1
+    assert _rc("beam_out_gate", by, 1, A, A, None, A, A, None, 0, None) == -1  # gate, no bias
+    assert _rc("beam_out_gate", by, 1, A, None, None, A, A, None, 0, None) == -7  # o_proj alone
     assert _rc("beam_out_gate", by, 1, A, A, A, A, A, None, 0, None) == -7
 
 

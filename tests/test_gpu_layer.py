@@ -47,12 +47,20 @@ def check_stages(dims, P: Params, cache: Cache, g, pos, seq, mode, n, ffn, sink=
                                  code_pos(e4m3_quantize(v[t], cache.v_scale)))) <= 1
     mp = int(np.max(pos))
     o_ref = L.attention(dims, bits_f64(g["q"]), pos, seq, cache.oracle(mp + 1), mode, sink)
-    assert_rms_close(bits_f64(g["o"]), o_ref, "o")
     T = len(pos)
-    if dims.G:
-        z = L.output_gate(dims, bits_f64(g["o"]), bits_f64(g["g"]), P.np("b_gate"))
+    if g.get("z") is not None:
+        # fused call: the gated output against the oracle's gate over its
+        # attention (two rounding points: o, then z)
+        z_ref = (L.output_gate(dims, o_ref, bits_f64(g["g"]), P.np("b_gate")) if dims.G
+                 else o_ref.reshape(T, -1))
+        assert_rms_close(bits_f64(g["z"]), z_ref, "z fused", ulps=2)
+        z = bits_f64(g["z"])
     else:
-        z = bits_f64(g["o"]).reshape(T, -1)
+        assert_rms_close(bits_f64(g["o"]), o_ref, "o")
+        if dims.G:
+            z = L.output_gate(dims, bits_f64(g["o"]), bits_f64(g["g"]), P.np("b_gate"))
+        else:
+            z = bits_f64(g["o"]).reshape(T, -1)
     assert_rms_close(bits_f64(g["y"]), L.o_proj(z, P.np("w_o")), "y")
     w_post, n_a = (P.np("w_attn_post"), n) if sandwich else (None, 0)
     hm, _ = L.boundary(g["y"], g["h_in"], w_post, P.np("w_ffn_pre"), n_a, eps)
@@ -148,11 +156,11 @@ def _tiny(mode, kv, T, ffn="moe", S=1):
 
 @pytest.mark.parametrize("mode", ["swa", "nope"])
 @pytest.mark.parametrize("kv", ["bf16", "fp8"])
-@pytest.mark.parametrize("T", [1, 32])
-def test_tiny_layer(mode, kv, T):
+@pytest.mark.parametrize("T,fused", [(1, False), (1, True), (32, False)])
+def test_tiny_layer(mode, kv, T, fused):
     dims, P, cache, h, pos, seq, n = _tiny(mode, kv, T)
     ocache = cache.oracle()                     # prior only, before the layer writes
-    g = run_layer(dims, P, cache, h, pos, seq, mode, n)
+    g = run_layer(dims, P, cache, h, pos, seq, mode, n, fused=fused)
     check_stages(dims, P, cache, g, pos, seq, mode, n, "moe")
     # positions beyond the prior held NaN patterns in the GPU cache: the oracle's zeros
     # stand in for "never read"
@@ -220,15 +228,18 @@ def _full(i):
     return _FULL[i]
 
 
-@pytest.mark.parametrize("i", [1, 2, pytest.param("1m", marks=pytest.mark.timeout(900))])
-def test_full_size_decode(i):
+@pytest.mark.parametrize("i,fused", [(1, False), (1, True), (2, False), (2, True),
+                                     pytest.param("1m", True, marks=pytest.mark.timeout(900))])
+def test_full_size_decode(i, fused):
+    """Full size in the benchmark's launch configuration (fused: the one-token
+    fused attention call and o_proj alone, as the benchmark's decode legs)."""
     cfg, P, cache, = _full(i)
     dims, ex = cfg.dims, cfg.extra
     pos = np.array([ex["pos"]], np.int32)
     seq = np.zeros(1, np.int32)
     h = synth.make_h((1, dims.D), 0, "full", i)
     before = cache.clone()
-    g = run_layer(dims, P, cache, h, pos, seq, ex["mode"], ex["n"])
+    g = run_layer(dims, P, cache, h, pos, seq, ex["mode"], ex["n"], fused=fused)
     check_stages(dims, P, cache, g, pos, seq, ex["mode"], ex["n"], "moe")
     ocache = before.oracle(ex["pos"] + 1)
     check_end_to_end(dims, P, ocache, g, h, pos, seq, ex["mode"], ex["n"], "moe",

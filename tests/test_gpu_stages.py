@@ -104,6 +104,79 @@ def test_qk_norm_kvwrite(base, T, pos0, mode, kv):
     assert np.all(K.view(np.uint16 if kv == "bf16" else np.uint8)[mask] == fill)
 
 
+@pytest.mark.parametrize("case", ["tiny", "beam_near", "beam_mid", "beam_far", "beam_nogate",
+                                  "flint_sink"])
+@pytest.mark.parametrize("mode", ["swa", "nope"])
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_attn_decode_fused(case, mode, kv):
+    """One-token fused attention half against the separate calls: the q it
+    reports and the cache bytes it writes equal those of the q/k call bit for
+    bit, and its gated output matches the oracle's gate over the attention of
+    those same inputs (the stage bar). Spans cover the one-pass workgroup
+    (tiny), the merge by the last workgroup (beam_near, SWA at any position)
+    and the merge kernel (beam_mid / beam_far NoPE: 12 / 47 chunks); the
+    position sits on a tile edge in beam_far. beam_nogate: no output gate
+    (z = o); flint_sink: the second model's shape with per-head sinks."""
+    if case == "tiny":
+        dims, Lmax, fill, p = CFG0, 192, 150, 100
+    elif case == "beam_near":
+        dims, Lmax, fill, p = BEAM, 4096, 3000, 1000
+    elif case == "beam_mid":
+        dims, Lmax, fill, p = BEAM, 4096, 3000, 2999
+    elif case == "beam_far":
+        dims, Lmax, fill, p = BEAM, 12096, 12032, 11968
+    elif case == "beam_nogate":
+        dims, Lmax, fill, p = _dims(BEAM, G=0), 4096, 3000, 2047
+    else:
+        dims, Lmax, fill, p = FLINT, 1024, 900, 700
+    P = Params(dims, 0, 3, moe=False)
+    x = dev(synth.make_h((1, dims.D), 2, "fx", case))
+    pos, seq = np.array([p], np.int32), np.array([1], np.int32)
+    Kp, Vp, ks, vs = synth.torch_kv_prior(dims, 2, fill, kv, 5, 9)
+    c_ref = Cache(dims, 2, Lmax, kv, ks, vs)
+    c_ref.fill_prior(Kp, Vp)
+    c_fus = c_ref.clone()
+    rope = rope_table(Lmax, dims.d, dims.theta) if mode == "swa" else None
+    m = B.BEAM_SWA_ROPE if mode == "swa" else B.BEAM_NOPE_SSMAX
+    sink = P.t.get("sink")
+    # the separate calls
+    q_ref = torch.empty((1, dims.Hq, dims.d), **I16)
+    g_ref = torch.empty((1, max(dims.G, 1)), **I16)
+    B.beam_qk_norm_rope_ssmax_kvwrite(dims, 1, x, P.t["w_qkvg"], P.t["w_qnorm"], P.t["w_knorm"],
+                                      dev(pos), dev(seq), m, rope, q_ref,
+                                      g_ref if dims.G else None, c_ref.struct(),
+                                      ws(dims, B.BEAM_OP_QKV, 1))
+    o_ref = torch.empty((1, dims.Hq, dims.d), **I16)
+    attn = B.beam_attn_swa if mode == "swa" else B.beam_attn_nope_ssmax
+    op = B.BEAM_OP_ATTN_SWA if mode == "swa" else B.BEAM_OP_ATTN_NOPE
+    attn(dims, 1, q_ref, dev(pos), dev(seq), c_ref.struct(), sink, o_ref, p, ws(dims, op, 1, p + 1))
+    # the fused call
+    q_f = torch.empty((1, dims.Hq, dims.d), **I16)
+    z_f = torch.full((1, dims.Hq * dims.d), 0x7FC0, **I16)
+    B.beam_attn_decode_fused(dims, 1, x, P.t["w_qkvg"], P.t["w_qnorm"], P.t["w_knorm"],
+                             dev(pos), dev(seq), m, rope, c_fus.struct(), sink, P.t.get("b_gate"),
+                             q_f, z_f, p, ws(dims, B.BEAM_OP_ATTN_DECODE_FUSED, 1, p + 1))
+    B.beam_check()
+    assert torch.equal(q_f, q_ref), "fused q differs from the q/k call's"
+    assert torch.equal(c_fus.K, c_ref.K) and torch.equal(c_fus.V, c_ref.V), "cache bytes differ"
+    o_gpu = bits_f64(host_bits(o_ref))
+    if dims.G:
+        z_want = L.output_gate(dims, o_gpu, bits_f64(host_bits(g_ref)), P.np("b_gate"))
+    else:
+        z_want = o_gpu.reshape(1, -1)
+    assert_rms_close(bits_f64(host_bits(z_f)), z_want, "z fused")
+    # and the attention itself against the oracle on the same q and cache
+    o_want = L.attention(dims, bits_f64(host_bits(q_ref)), pos, seq, c_ref.oracle(p + 1), mode,
+                         P.np("sink") if sink is not None else None)
+    assert_rms_close(o_gpu, o_want, "o")
+    # o_proj on the gated output (no gate in the call): the weights-first GEMV
+    y = torch.empty((1, dims.D), **I16)
+    B.beam_out_gate(dims, 1, z_f, None, None, P.t["w_o"], y, ws(dims, B.BEAM_OP_OUT_GATE, 1))
+    B.beam_check()
+    assert_rms_close(bits_f64(host_bits(y)), L.o_proj(bits_f64(host_bits(z_f)), P.np("w_o")),
+                     "y")
+
+
 @pytest.mark.parametrize("base,T", [(BEAM, 1), (CFG0, 3), (BEAM, 40)])
 def test_qk_slot_outside_cache_is_flagged(base, T):
     """A position at Lmax (or a slot index at S) skips that token's cache write

@@ -284,16 +284,20 @@ __global__ __launch_bounds__(768) void attn_prefill_kernel(
 // bf16 cache, head dim 128: K and V^T tiles go from global memory straight into
 // LDS (16 bytes per lane; one wave instruction fills 1 KiB), double-buffered,
 // so no registers hold staged data and no padding is possible: bank conflicts
-// are avoided with XOR swizzles instead.
-//   K tile  [64 keys][128 dims]: row r = 16 chunks of 16 B; chunk c of row r
-//           sits at slot c ^ fk(r), fk(r) = (r & 3) | ((r >> 1) & 4).
-//   V^T tile [128 dims][64 keys]: row = 8 chunks (8 keys each); chunk c of
-//           dim row d sits at slot c ^ (d & 7).
+// are avoided with XOR swizzles instead. A 16-byte fragment read is served
+// 16 lanes at a time (256 bytes: one line of the 64 banks).
+//   K tile  [64 keys][128 dims]: row r = 16 chunks of 16 B, a full bank line;
+//           chunk c of row r sits at slot c ^ fk(r), fk(r) = r & 15, so the
+//           16 rows read by a group of 16 lanes (perm(0..15)) hit 16
+//           distinct slots.
+//   V^T tile [128 dims][64 keys]: row = 8 chunks (8 keys each), two rows per
+//           bank line; chunk c of dim row d sits at slot c ^ ((d >> 1) & 7),
+//           so the 8 rows of each parity among 16 consecutive dims get 8
+//           distinct slots.
 // The score MFMA takes key slot s of a 32-key half from K row perm(s), perm
 // swapping bits 2 and 3, so that after the product lane (tc, g) holds the
 // probabilities of keys 16 st + 8 g + [0, 8) for st = 0, 1: exactly one
-// contiguous 16-byte V^T chunk per P.V step (fk is chosen so the 8 rows read
-// by each group of 8 lanes, perm(0..7) or perm(8..15), hit distinct banks).
+// contiguous 16-byte V^T chunk per P.V step.
 // Keys outside the sequence's [kmin, kmax] may hold anything: scores are
 // replaced by -inf, and on edge tiles the out-of-range V^T entries are zeroed
 // in LDS by the same pass that turns each V^T tile into fp16 (once per
@@ -302,8 +306,10 @@ __global__ __launch_bounds__(768) void attn_prefill_kernel(
 constexpr int DMA_HD = 128;
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
-__device__ __forceinline__ int fk_swz(int r) { return (r & 3) | ((r >> 1) & 4); }
+__device__ __forceinline__ int fk_swz(int r) { return r & 15; }
+__device__ __forceinline__ int fv_swz(int d) { return (d >> 1) & 7; }
 __device__ __forceinline__ int perm23(int s) {
   return (s & ~12) | ((s & 4) << 1) | ((s & 8) >> 1);
 }
@@ -406,18 +412,30 @@ __global__ __launch_bounds__(768) void attn_prefill_dma_kernel(
 
     // instruction u < 16: K rows 4u..4u+3; u >= 16: V^T dim rows 8(u-16)..+7.
     // kb + 63 <= Lmax - 1 (kb is 64-aligned, kb <= kmax < Lmax, Lmax % 64 == 0).
+    // Wave w issues units w, w + nw, ... (at most MAXU: nw >= 8); each lane's
+    // address at key 0 is formed once per sequence, a tile adds kb to it.
+    // (element offsets from the sequence's K / V^T base: d * Lmax < 2^31)
+    constexpr int MAXU = 4;
+    uint32_t go[MAXU];
+#pragma unroll
+    for (int i = 0; i < MAXU; ++i) {
+      const int u = wave + i * nw;
+      if (u < NI / 2) {
+        const int r = 4 * u + (lane >> 4);
+        go[i] = (uint32_t)(r * HD + ((lane & 15) ^ fk_swz(r)) * 8);
+      } else {
+        const int d = 8 * (u - NI / 2) + (lane >> 3);
+        go[i] = (uint32_t)d * (uint32_t)Lmax + (uint32_t)(((lane & 7) ^ fv_swz(d)) * 8);
+      }
+    }
     auto gload = [&](int kb, int buf) {
-      for (int u = wave; u < NI; u += nw) {
-        if (u < NI / 2) {
-          const int r = 4 * u + (lane >> 4);
-          const int c = (lane & 15) ^ fk_swz(r);
-          load_lds16(kbase_p + (size_t)(kb + r) * HD + c * 8, sK(buf) + 4 * u * HD);
-        } else {
-          const int u2 = u - NI / 2;
-          const int d = 8 * u2 + (lane >> 3);
-          const int c = (lane & 7) ^ (d & 7);
-          load_lds16(vbase_p + (size_t)d * Lmax + kb + c * 8, sV(buf) + 8 * u2 * KT);
-        }
+#pragma unroll
+      for (int i = 0; i < MAXU; ++i) {
+        const int u = wave + i * nw;
+        if (u < NI / 2)
+          load_lds16(kbase_p + (go[i] + (uint32_t)kb * HD), sK(buf) + 4 * u * HD);
+        else if (u < NI)
+          load_lds16(vbase_p + (go[i] + (uint32_t)kb), sV(buf) + 8 * (u - NI / 2) * KT);
       }
     };
 
@@ -439,28 +457,28 @@ __global__ __launch_bounds__(768) void attn_prefill_dma_kernel(
       // tile.
       {
         uint4* vt = reinterpret_cast<uint4*>(sV(cur));
-        bool big = false;
+        u16x2 mag = {0, 0};  // largest |bf16| bit pattern seen, per half
         for (int c = tid; c < HD * KT / 8; c += nw * 64) {
-          const int d = c >> 3, k0 = kb + 8 * ((c & 7) ^ (d & 7));
+          const int d = c >> 3, k0 = kb + 8 * ((c & 7) ^ fv_swz(d));
           const uint4 w = vt[c];
-          const uint32_t in[4] = {w.x, w.y, w.z, w.w};
+          uint32_t in[4] = {w.x, w.y, w.z, w.w};
           uint32_t out[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            float a = bf_lo(in[e]), b = bf_hi(in[e]);
             if (edge) {
-              if (k0 + 2 * e < kmin || k0 + 2 * e > kmax) a = 0.f;
-              if (k0 + 2 * e + 1 < kmin || k0 + 2 * e + 1 > kmax) b = 0.f;
+              if (k0 + 2 * e < kmin || k0 + 2 * e > kmax) in[e] &= 0xffff0000u;
+              if (k0 + 2 * e + 1 < kmin || k0 + 2 * e + 1 > kmax) in[e] &= 0x0000ffffu;
             }
-            big |= (fabsf(a) > 65504.f) | (fabsf(b) > 65504.f);
-            a = fminf(fmaxf(a, -65504.f), 65504.f);
-            b = fminf(fmaxf(b, -65504.f), 65504.f);
-            const f16x2 h = {(_Float16)a, (_Float16)b};
+            mag = __builtin_elementwise_max(mag, __builtin_bit_cast(u16x2, in[e] & 0x7fff7fffu));
+            const f16x2 h = {(_Float16)__builtin_amdgcn_fmed3f(bf_lo(in[e]), -65504.f, 65504.f),
+                             (_Float16)__builtin_amdgcn_fmed3f(bf_hi(in[e]), -65504.f, 65504.f)};
             out[e] = __builtin_bit_cast(uint32_t, h);
           }
           vt[c] = uint4{out[0], out[1], out[2], out[3]};
         }
-        if (big) BEAM_RAISE(attnp, ERR_RANGE);
+        // a bf16 magnitude of 65536 or more (pattern 0x4780) is beyond fp16's
+        // range: clamped to +-65504 above, and reported
+        if (max(mag.x, mag.y) >= 0x4780) BEAM_RAISE(attnp, ERR_RANGE);
         __syncthreads();
       }
       if (__any(mine)) {  // waves with no token of this sequence only load
@@ -496,14 +514,32 @@ __global__ __launch_bounds__(768) void attn_prefill_dma_kernel(
           const float alpha =
               (mn == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f((m - mn) * score_scale);
           const float moff = (mn == -INFINITY) ? 0.f : -mn * score_scale;
-          float rs = 0.f;
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            // masked scores are -inf: exp2(-inf) = 0
-            const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[i], score_scale, moff));
-            sacc[i] = pr;
-            rs += pr;
-          }
+          for (int i = 0; i < 16; ++i)  // masked scores are -inf: exp2(-inf) = 0
+            sacc[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[i], score_scale, moff));
+          // p in fp16 (11 significant bits; p <= 1): the P.V operand, and the
+          // row sum taken over the same rounded values (two per dot instruction)
+          f16x2 pp[2][4];
+#pragma unroll
+          for (int st = 0; st < 2; ++st)
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+              pp[st][k] = f16x2{(_Float16)sacc[4 * (2 * st + (k >> 1)) + 2 * (k & 1)],
+                                (_Float16)sacc[4 * (2 * st + (k >> 1)) + 2 * (k & 1) + 1]};
+          float rs = 0.f;
+          const f16x2 one2 = {(_Float16)1.0f, (_Float16)1.0f};
+#pragma unroll
+          for (int st = 0; st < 2; ++st)
+#pragma unroll
+            for (int k = 0; k < 4; ++k) rs = __builtin_amdgcn_fdot2(pp[st][k], one2, rs, false);
+          f16x8 pfs[2];
+#pragma unroll
+          for (int st = 0; st < 2; ++st)
+            pfs[st] = __builtin_bit_cast(
+                f16x8, uint4{__builtin_bit_cast(uint32_t, pp[st][0]),
+                             __builtin_bit_cast(uint32_t, pp[st][1]),
+                             __builtin_bit_cast(uint32_t, pp[st][2]),
+                             __builtin_bit_cast(uint32_t, pp[st][3])});
           rs += __shfl_xor(rs, 32, 64);
           lsum = lsum * alpha + rs;
           m = mn;
@@ -513,13 +549,7 @@ __global__ __launch_bounds__(768) void attn_prefill_dma_kernel(
           }
 #pragma unroll
           for (int st = 0; st < 2; ++st) {
-            // p in fp16 (11 significant bits; p <= 1)
-            f16x8 pf;
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-              pf[2 * k] = (_Float16)sacc[4 * (2 * st + (k >> 1)) + 2 * (k & 1)];
-              pf[2 * k + 1] = (_Float16)sacc[4 * (2 * st + (k >> 1)) + 2 * (k & 1) + 1];
-            }
+            const f16x8 pf = pfs[st];
             // this lane's keys: kbase + 16 st + 8 g + [0, 8), one V^T chunk
             const int vchunk = kh * 4 + 2 * st + g;
             // the step's V^T fragments, all requested before the first product
@@ -528,7 +558,7 @@ __global__ __launch_bounds__(768) void attn_prefill_dma_kernel(
 #pragma unroll
             for (int db = 0; db < DB; ++db) {
               const int d = db * 32 + tc;
-              vf[db] = *reinterpret_cast<const f16x8*>(sV(cur) + d * KT + (vchunk ^ (d & 7)) * 8);
+              vf[db] = *reinterpret_cast<const f16x8*>(sV(cur) + d * KT + (vchunk ^ fv_swz(d)) * 8);
             }
 #pragma unroll
             for (int db = 0; db < DB; ++db)

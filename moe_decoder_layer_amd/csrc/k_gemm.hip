@@ -8,9 +8,10 @@
 // is loaded from global memory straight into the other half of a double
 // buffer in LDS (no register staging) while the current one is multiplied
 // out; inside a slab the operand fragments of k-step ks + 1 are read from LDS
-// while the MFMAs of k-step ks run. LDS rows are 128 bytes (64 bf16); the
-// eight 16-byte chunks of row r are stored at chunk ^ (r & 7) so the 16-byte
-// fragment reads of 8 consecutive rows land on distinct banks.
+// while the MFMAs of k-step ks run. LDS rows are 128 bytes (64 bf16), two to
+// a 256-byte line of the 64 banks; the eight 16-byte chunks of row r are
+// stored at chunk ^ ((r >> 1) & 7) so the 16-byte fragment reads of 16
+// consecutive rows (16 lanes served per cycle) land on distinct banks.
 //
 // Variants (template Epi) cover the projections of the Beam layer ("Reflection
 // Beam 1.0 on vLLM": packed q|k|v|gate GEMM of optimisation change 5, o_proj,
@@ -65,7 +66,11 @@ struct GemmArgs {
   long long split_stride;
 };
 
-__device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ (row & 7); }
+// LDS slot of k-chunk `chunk` (16 B) in tile row `row` (BK = 64 bf16 = 128 B,
+// two rows per 256-byte line of the 64 banks). A fragment read has 16 lanes
+// in flight per cycle, on 16 consecutive rows: the 8 rows of one parity share
+// a bank half, so they get 8 distinct slots from (row >> 1) & 7.
+__device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ ((row >> 1) & 7); }
 
 // WAVES = 4: waves in a 2 x 2 grid, 128 x 128 each (1 wave per SIMD);
 // WAVES = 8: waves in a 2 x 4 grid, 128 x 64 each (2 waves per SIMD, so one
@@ -149,7 +154,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_bf16_kernel(GemmArgs g) {
   // gfx950 loads 16 bytes per lane straight into LDS: one wave instruction
   // fills 1 KiB = 8 consecutive tile rows at a wave-uniform LDS address, lane l
   // landing at row l / 8, chunk slot l % 8. With the XOR swizzle, slot p of
-  // row r holds k-chunk p ^ (r & 7), so that is the chunk lane l fetches.
+  // row r holds k-chunk swz(r, p), so that is the chunk lane l fetches.
   // Wave w fills rows [RPW w, RPW (w + 1)) of the A and of the B tile.
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
@@ -159,7 +164,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_bf16_kernel(GemmArgs g) {
 #pragma unroll
   for (int i = 0; i < NL; ++i) {
     const int r = wave * RPW + i * 8 + (lane >> 3);
-    const int c = (lane & 7) ^ (r & 7);
+    const int c = swz(r, lane & 7);
     const int rr = min(r, mrows - 1);
     const int arow = g.a_gather ? g.a_gather[m0 + rr] : m0 + rr;
     a_src[i] = g.A + (long long)arow * g.lda + c * 8;

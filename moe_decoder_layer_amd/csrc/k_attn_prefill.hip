@@ -15,9 +15,10 @@
 //   S^T[key][token] = K[key][:] . Q[token][:]            32x32x16 bf16 MFMA
 //   O^T[dim][token] += V^T[dim][key] . (P_hi + P_lo)^T    2 x 32x32x16 bf16 MFMA
 // attn_prefill_dma_kernel (bf16 cache, head dim 128) takes the P.V product on
-// fp16 operands instead, one MFMA: p (<= 1) rounded to fp16 keeps 11
-// significant bits, and the bf16 V^T tile converts to fp16 exactly (values
-// beyond +-65504 are clamped).
+// fp16 operands instead, one MFMA: p (< 256: the running max only moves when
+// a score passes it by more than 2^8) rounded to fp16 keeps 11 significant
+// bits, and the bf16 V^T tile converts to fp16 exactly (values beyond +-65504
+// are clamped).
 // In the S^T layout lane l owns token l % 32: the online softmax state is
 // lane-local up to one xor-32 shuffle, and a lane's probabilities are the B
 // operand it needs for P.V. LDS rows are padded (K rows by 16 bytes, V^T rows
@@ -306,12 +307,22 @@ __global__ __launch_bounds__(768) void attn_prefill_kernel(
 constexpr int DMA_HD = 128;
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ int fk_swz(int r) { return r & 15; }
 __device__ __forceinline__ int fv_swz(int d) { return (d >> 1) & 7; }
 __device__ __forceinline__ int perm23(int s) {
   return (s & ~12) | ((s & 4) << 1) | ((s & 8) >> 1);
+}
+// max and sum of a value over lanes l and l ^ 32
+__device__ __forceinline__ float pair_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v),
+                                                  false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v),
+                                                  false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 template <bool SWA>
@@ -334,14 +345,20 @@ __global__ __launch_bounds__(768) void attn_prefill_dma_kernel(
   __shared__ int sinfo[3];
 
   const int nw = blockDim.x >> 6, tid = threadIdx.x;
-  const int j = blockIdx.y;
+  // Workgroups are handed to the eight XCDs in turn: logical index L sends a
+  // contiguous eighth of the (token block, kv head) grid to each XCD, so the
+  // blocks that read one kv head's keys share that XCD's L2.
+  const int nx = (int)gridDim.x, nwg = nx * (int)gridDim.y;
+  const int b = (int)(blockIdx.y * gridDim.x + blockIdx.x);
+  const int L = (nwg % 8 == 0) ? (b & 7) * (nwg >> 3) + (b >> 3) : b;
+  const int xb = L % nx, j = L / nx;
   const int grp = Hq / Hkv;
   const int wave = tid >> 6, lane = tid & 63;
   const int hh = wave % grp, tb = wave / grp;
   const int h = j * grp + hh;
   const int tc = lane & 31, g = lane >> 5;
   const int tblk = 32 * ntb;
-  const int t0 = blockIdx.x * tblk;
+  const int t0 = xb * tblk;
   const int t = t0 + 32 * tb + tc;
   const bool tok = t < T;
   int p = tok ? pos[t] : -1, s = tok ? seq[t] : -1;
@@ -457,7 +474,7 @@ __global__ __launch_bounds__(768) void attn_prefill_dma_kernel(
       // tile.
       {
         uint4* vt = reinterpret_cast<uint4*>(sV(cur));
-        u16x2 mag = {0, 0};  // largest |bf16| bit pattern seen, per half
+        float mag = 0.f;  // largest magnitude converted
         for (int c = tid; c < HD * KT / 8; c += nw * 64) {
           const int d = c >> 3, k0 = kb + 8 * ((c & 7) ^ fv_swz(d));
           const uint4 w = vt[c];
@@ -469,16 +486,18 @@ __global__ __launch_bounds__(768) void attn_prefill_dma_kernel(
               if (k0 + 2 * e < kmin || k0 + 2 * e > kmax) in[e] &= 0xffff0000u;
               if (k0 + 2 * e + 1 < kmin || k0 + 2 * e + 1 > kmax) in[e] &= 0x0000ffffu;
             }
-            mag = __builtin_elementwise_max(mag, __builtin_bit_cast(u16x2, in[e] & 0x7fff7fffu));
-            const f16x2 h = {(_Float16)__builtin_amdgcn_fmed3f(bf_lo(in[e]), -65504.f, 65504.f),
-                             (_Float16)__builtin_amdgcn_fmed3f(bf_hi(in[e]), -65504.f, 65504.f)};
-            out[e] = __builtin_bit_cast(uint32_t, h);
+            const float lo_v = bf_lo(in[e]), hi_v = bf_hi(in[e]);
+            mag = fmaxf(mag, fmaxf(fabsf(lo_v), fabsf(hi_v)));
+            // round toward zero: exact for bf16 values in fp16's range (but
+            // those below 2^-17, off by under 2^-24), and an overflow gives
+            // the largest finite value, +-65504
+            out[e] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo_v, hi_v));
           }
           vt[c] = uint4{out[0], out[1], out[2], out[3]};
         }
-        // a bf16 magnitude of 65536 or more (pattern 0x4780) is beyond fp16's
-        // range: clamped to +-65504 above, and reported
-        if (max(mag.x, mag.y) >= 0x4780) BEAM_RAISE(attnp, ERR_RANGE);
+        // beyond fp16's range (bf16 magnitudes of 65536 and up; NaN compares
+        // false): clamped to +-65504 above, and reported
+        if (mag >= 65536.f) BEAM_RAISE(attnp, ERR_RANGE);
         __syncthreads();
       }
       if (__any(mine)) {  // waves with no token of this sequence only load
@@ -495,8 +514,10 @@ __global__ __launch_bounds__(768) void attn_prefill_dma_kernel(
             sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[i], sacc, 0, 0, 0);
           }
           // sacc[4 i + jj] = S[key kbase + 16 (i >> 1) + 8 g + 4 (i & 1) + jj][token tc],
-          // raw (unscaled) scores; m is the running max of raw scores and the
-          // scale (> 0) enters once, inside exp2(s * c - m * c)
+          // raw (unscaled) scores; m is the running max of raw scores (it only
+          // moves when a score passes it by more than 2^8 in exp2 units, so the
+          // probabilities stay below 256 and the output rescale is rare), and
+          // the scale (> 0) enters once, inside exp2(s * c - m * c)
           if (!interior) {
 #pragma unroll
             for (int i = 0; i < 4; ++i)
@@ -509,15 +530,15 @@ __global__ __launch_bounds__(768) void attn_prefill_dma_kernel(
           float mx = -INFINITY;
 #pragma unroll
           for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[i]);
-          mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-          const float mn = fmaxf(m, mx);
-          const float alpha =
-              (mn == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f((m - mn) * score_scale);
+          mx = pair_max(mx);
+          // also true when m is -inf and mx finite; false when both are -inf
+          const bool grow = (mx - m) * score_scale > 8.f;
+          const float mn = grow ? mx : m;
           const float moff = (mn == -INFINITY) ? 0.f : -mn * score_scale;
 #pragma unroll
           for (int i = 0; i < 16; ++i)  // masked scores are -inf: exp2(-inf) = 0
             sacc[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[i], score_scale, moff));
-          // p in fp16 (11 significant bits; p <= 1): the P.V operand, and the
+          // p in fp16 (11 significant bits; p < 256): the P.V operand, and the
           // row sum taken over the same rounded values (two per dot instruction)
           f16x2 pp[2][4];
 #pragma unroll
@@ -540,13 +561,17 @@ __global__ __launch_bounds__(768) void attn_prefill_dma_kernel(
                              __builtin_bit_cast(uint32_t, pp[st][1]),
                              __builtin_bit_cast(uint32_t, pp[st][2]),
                              __builtin_bit_cast(uint32_t, pp[st][3])});
-          rs += __shfl_xor(rs, 32, 64);
-          lsum = lsum * alpha + rs;
-          m = mn;
-          if (__any(alpha != 1.f)) {  // rescale only when some running max moved
+          // lsum: this lane's share of the row sum (the two halves add up at
+          // the end)
+          if (__any(grow)) {  // rescale only when some running max moved
+            // exp2(-inf) = 0 when nothing was accumulated yet
+            const float alpha = grow ? __builtin_amdgcn_exp2f((m - mn) * score_scale) : 1.f;
+            lsum *= alpha;
 #pragma unroll
             for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
           }
+          lsum += rs;
+          m = mn;
 #pragma unroll
           for (int st = 0; st < 2; ++st) {
             const f16x8 pf = pfs[st];
@@ -570,6 +595,7 @@ __global__ __launch_bounds__(768) void attn_prefill_dma_kernel(
       __syncthreads();
     }
   }
+  lsum = pair_sum(lsum);
   if (!tok || tb >= ntb) return;
   if (sink) {
     const float sl2 = sink[h] * 1.4426950408889634f;

@@ -53,7 +53,8 @@
  *                           keys reads contiguous runs for the matrix cores.
  *  - Element type bf16, or fp8 e4m3fn codes c with value decode(c) * scale
  *    (one k_scale for the whole K cache, one v_scale for V).
- *  - Lmax must be a multiple of 64.
+ *  - Lmax must be a multiple of 64. The index over Lmax is a slot: the
+ *    position itself, or the position mod Lmax in a ring (beam_kv.npos).
  */
 #ifndef BEAMLAYER_H
 #define BEAMLAYER_H
@@ -105,13 +106,24 @@ typedef struct beam_dims {
 
 /* One layer's KV cache (see the layout above). k, v: device pointers;
  * dtype: beam_kv_dtype; k_scale/v_scale: fp8 dequantisation scales (> 0,
- * ignored for bf16); S sequence slots; Lmax positions per slot. */
+ * ignored for bf16); S sequence slots; Lmax slots per sequence (a multiple
+ * of 64); npos the positions the cache accepts: 0 (or Lmax) for one slot per
+ * position, positions [0, Lmax); a value above Lmax makes each sequence's
+ * slots a ring: position p lives in slot p mod Lmax and positions [0, npos)
+ * are accepted ([Attn]: a sliding-window layer keeps only its last `window`
+ * keys). A ring serves sliding-window attention only (calls in mode
+ * BEAM_NOPE_SSMAX reject it) and needs window <= Lmax; within one call the
+ * keys each token reads must still be in the ring after the call's own cache
+ * writes, i.e. Lmax >= window + (tokens of one sequence in the call) - 1 (not
+ * checked: a smaller ring silently reads newer keys in place of old ones).
+ * The RoPE table passed with a cache has a row for every accepted position. */
 typedef struct beam_kv {
   void* k;
   void* v;
   int dtype;
   float k_scale, v_scale;
   int S, Lmax;
+  int npos;
 } beam_kv;
 
 /* Sublayer boundary [MoE] sandwich norm + depth-scaled residual, fused as in
@@ -139,14 +151,14 @@ int beam_boundary_norm_residual(const beam_dims* dims, int T, const uint16_t* y,
  *     mode BEAM_SWA_ROPE:   rotate q and k at position pos[t] (rotate-half
  *                           pairs (i, i+d/2); rope_cs[pos][i] = cos, and
  *                           rope_cs[pos][d/2+i] = sin, of pos*theta^(-2i/d),
- *                           table [Lmax][d] fp32, see beam_rope_table);
+ *                           table [npos][d] fp32, see beam_rope_table);
  *     mode BEAM_NOPE_SSMAX: q <- q * (1 + (pos[t]+1)/2048)^0.1, keys as is.
  *   q_out [T][Hq][d] = bf16(q); g_out [T][G] = the gate rows (bf16);
  *   cache slot (seq[t], pos[t]) <- k, v (bf16, or e4m3 of value/scale with
  *   round-to-nearest-even and saturation at 448).
  * x [T][D] bf16; pos, seq [T] int32 (device). ws >= beam_workspace_size(QKV).
  * Errors: invalid mode; RoPE without rope_cs; Hq % Hkv; d unsupported; fp8
- * with a scale <= 0. Device check: pos outside [0, Lmax) or seq outside
+ * with a scale <= 0. Device check: pos outside [0, npos) or seq outside
  * [0, S) skips that token's cache write and raises the device flag. */
 int beam_qk_norm_rope_ssmax_kvwrite(const beam_dims* dims, int T, const uint16_t* x,
                                     const uint16_t* w_qkvg, const uint16_t* w_qnorm,
@@ -174,7 +186,7 @@ int beam_qk_norm_rope_ssmax_kvwrite(const beam_dims* dims, int T, const uint16_t
  * rounds probabilities to fp16 and converts V to fp16 (exact for bf16 values
  * of magnitude <= 65504; larger ones are clamped to +-65504 and the device
  * flag is raised, so beam_check reports BEAM_E_DEVICE for such a call).
- * Errors: window <= 0, max_pos >= Lmax. */
+ * Errors: window <= 0, max_pos >= npos; a ring cache with window > Lmax. */
 int beam_attn_swa(const beam_dims* dims, int T, const uint16_t* q, const int32_t* pos,
                   const int32_t* seq, const beam_kv* kv, const float* sink, uint16_t* o,
                   int max_pos, void* ws, size_t ws_bytes, void* stream);

@@ -57,7 +57,7 @@ class beam_dims(ctypes.Structure):
 
 class beam_kv(ctypes.Structure):
     _fields_ = [("k", c_void_p), ("v", c_void_p), ("dtype", c_int), ("k_scale", c_float),
-                ("v_scale", c_float), ("S", c_int), ("Lmax", c_int)]
+                ("v_scale", c_float), ("S", c_int), ("Lmax", c_int), ("npos", c_int)]
 
 
 _lib = None
@@ -137,8 +137,10 @@ def dims_from(obj) -> beam_dims:
                      float(get("eps")), float(get("route_scale")))
 
 
-def kv_struct(k, v, dtype: int, k_scale: float, v_scale: float, S: int, Lmax: int) -> beam_kv:
-    return beam_kv(_p(k), _p(v), dtype, k_scale, v_scale, S, Lmax)
+def kv_struct(k, v, dtype: int, k_scale: float, v_scale: float, S: int, Lmax: int,
+              npos: int = 0) -> beam_kv:
+    """npos > Lmax: a ring of Lmax slots per sequence (slot = position mod Lmax)."""
+    return beam_kv(_p(k), _p(v), dtype, k_scale, v_scale, S, Lmax, npos)
 
 
 def _p(x):

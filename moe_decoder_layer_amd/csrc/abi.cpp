@@ -82,6 +82,24 @@ int check_kv(const beam_kv* kv, const char* fn) {
     return fail(BEAM_E_UNSUPPORTED, "%s: unknown kv dtype %d", fn, kv->dtype);
   if (kv->dtype == BEAM_KV_FP8_E4M3 && !(kv->k_scale > 0.f && kv->v_scale > 0.f))
     return fail(BEAM_E_SHAPE, "%s: fp8 cache scales must be > 0", fn);
+  if (kv->npos != 0 && kv->npos < kv->Lmax)
+    return fail(BEAM_E_SHAPE, "%s: npos %d is neither 0 nor >= Lmax %d", fn, kv->npos, kv->Lmax);
+  return BEAM_OK;
+}
+// Positions a cache accepts, and whether it is a ring (slot = position mod Lmax).
+int kv_npos(const beam_kv* kv) { return kv->npos ? kv->npos : kv->Lmax; }
+bool kv_ring(const beam_kv* kv) { return kv->npos > kv->Lmax; }
+// Attention over a cache: max_pos below npos; a ring serves sliding-window
+// attention only, with the window inside the ring.
+int check_attn_cache(const beam_dims* dims, const beam_kv* kv, int swa, int max_pos,
+                     const char* fn) {
+  if (max_pos < 0 || max_pos >= kv_npos(kv))
+    return fail(BEAM_E_SHAPE, "%s: max_pos %d outside [0, %d)", fn, max_pos, kv_npos(kv));
+  if (kv_ring(kv) && !swa)
+    return fail(BEAM_E_UNSUPPORTED, "%s: a ring cache serves sliding-window attention only", fn);
+  if (kv_ring(kv) && dims->window > kv->Lmax)
+    return fail(BEAM_E_SHAPE, "%s: window %d exceeds the ring's %d slots", fn, dims->window,
+                kv->Lmax);
   return BEAM_OK;
 }
 
@@ -193,8 +211,7 @@ int attn_impl(const beam_dims* dims, int T, const uint16_t* q, const int32_t* po
   if ((rc = check_kv(kv, fn))) return rc;
   if (T <= 0) return fail(BEAM_E_SHAPE, "%s: T <= 0", fn);
   if (swa && dims->window <= 0) return fail(BEAM_E_SHAPE, "%s: window <= 0", fn);
-  if (max_pos < 0 || max_pos >= kv->Lmax)
-    return fail(BEAM_E_SHAPE, "%s: max_pos %d outside [0, Lmax)", fn, max_pos);
+  if ((rc = check_attn_cache(dims, kv, swa, max_pos, fn))) return rc;
   const int fp8 = kv->dtype == BEAM_KV_FP8_E4M3;
   if (attn_flash(dims, T, kv->S)) {
     if (!ws || ws_bytes < kCtl)
@@ -206,7 +223,8 @@ int attn_impl(const beam_dims* dims, int T, const uint16_t* q, const int32_t* po
     return launched(beam::launch_attn_prefill(T, dims->Hq, dims->Hkv, dims->d, swa, dims->window,
                                               fp8, q, pos, seq, kv->k, kv->v,
                                               fp8 ? kv->k_scale : 1.f, fp8 ? kv->v_scale : 1.f,
-                                              kv->S, kv->Lmax, sink, o, S_(stream)),
+                                              kv->S, kv->Lmax, kv_npos(kv), sink, o,
+                                              S_(stream)),
                     fn);
   }
   const int span = attn_span(dims, swa, max_pos + 1);
@@ -220,7 +238,8 @@ int attn_impl(const beam_dims* dims, int T, const uint16_t* q, const int32_t* po
   return launched(beam::launch_attn_decode(T, dims->Hq, dims->Hkv, dims->d, swa, dims->window,
                                            fp8, q, pos, seq, kv->k, kv->v,
                                            fp8 ? kv->k_scale : 1.f, fp8 ? kv->v_scale : 1.f,
-                                           kv->S, kv->Lmax, sink, o, span, (float*)ws_data(ws),
+                                           kv->S, kv->Lmax, kv_npos(kv), sink, o, span,
+                                           (float*)ws_data(ws),
                                            ws_ctl(ws), S_(stream)),
                   fn);
 }
@@ -330,6 +349,9 @@ int beam_qk_norm_rope_ssmax_kvwrite(const beam_dims* dims, int T, const uint16_t
     return fail(BEAM_E_SHAPE, "%s: invalid mode %d", __func__, mode);
   if (mode == BEAM_SWA_ROPE && !rope_cs)
     return fail(BEAM_E_NULL, "%s: RoPE mode needs rope_cs", __func__);
+  if (mode == BEAM_NOPE_SSMAX && kv_ring(kv))
+    return fail(BEAM_E_UNSUPPORTED, "%s: a ring cache serves sliding-window layers only",
+                __func__);
   if (dims->G > 0 && !g_out) return fail(BEAM_E_NULL, "%s: g_out is NULL", __func__);
   if (ws_bytes < ws_qkv(dims, T))
     return fail(BEAM_E_WORKSPACE, "%s: workspace %zu < %zu bytes", __func__, ws_bytes,
@@ -350,7 +372,7 @@ int beam_qk_norm_rope_ssmax_kvwrite(const beam_dims* dims, int T, const uint16_t
                                            w_knorm, pos, seq, mode, rope_cs, q_out, kv->k,
                                            kv->v, fp8, fp8 ? kv->k_scale : 1.f,
                                            fp8 ? kv->v_scale : 1.f, kv->S, kv->Lmax,
-                                           dims->eps, S_(stream)),
+                                           kv_npos(kv), dims->eps, S_(stream)),
                   __func__);
 }
 
@@ -386,8 +408,7 @@ int beam_attn_decode_fused(const beam_dims* dims, int T, const uint16_t* x,
   if (mode == BEAM_SWA_ROPE && dims->window <= 0)
     return fail(BEAM_E_SHAPE, "%s: window <= 0", __func__);
   if (dims->G > 0 && !b_gate) return fail(BEAM_E_NULL, "%s: b_gate is NULL", __func__);
-  if (max_pos < 0 || max_pos >= kv->Lmax)
-    return fail(BEAM_E_SHAPE, "%s: max_pos %d outside [0, Lmax)", __func__, max_pos);
+  if ((rc = check_attn_cache(dims, kv, mode == BEAM_SWA_ROPE, max_pos, __func__))) return rc;
   const size_t need = ws_attn_fused(dims, T, max_pos + 1);
   if (ws_bytes < need)
     return fail(BEAM_E_WORKSPACE, "%s: workspace %zu < %zu bytes", __func__, ws_bytes, need);
@@ -407,7 +428,7 @@ int beam_attn_decode_fused(const beam_dims* dims, int T, const uint16_t* x,
   return launched(beam::launch_attn_decode(T, dims->Hq, dims->Hkv, dims->d, swa, dims->window,
                                            fp8, nullptr, pos, seq, kv->k, kv->v,
                                            fp8 ? kv->k_scale : 1.f, fp8 ? kv->v_scale : 1.f,
-                                           kv->S, kv->Lmax, sink, z_out,
+                                           kv->S, kv->Lmax, kv_npos(kv), sink, z_out,
                                            attn_span(dims, swa, max_pos + 1), part, ws_ctl(ws),
                                            S_(stream), &fz),
                   __func__);

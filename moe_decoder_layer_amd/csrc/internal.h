@@ -59,7 +59,7 @@ int launch_expert_w2(int T, int D, int F, int E, int topk, int spt, const uint16
 int launch_qk_epilogue(int T, int Hq, int Hkv, int hd, const uint16_t* qkv, const uint16_t* wq,
                        const uint16_t* wk, const int32_t* pos, const int32_t* seq, int mode,
                        const float* rope_cs, uint16_t* q_out, void* kc, void* vc, int fp8,
-                       float k_scale, float v_scale, int S, int Lmax, float eps,
+                       float k_scale, float v_scale, int S, int Lmax, int npos, float eps,
                        hipStream_t st);
 
 // Every workspace starts with a block of kCtlBytes of zeroed uint32 counters
@@ -90,8 +90,8 @@ bool attn_fused_merge(int T, int Hkv, int nch);
 int launch_attn_decode(int T, int Hq, int Hkv, int hd, int swa, int window, int fp8,
                        const uint16_t* q, const int32_t* pos, const int32_t* seq,
                        const void* kc, const void* vc, float k_scale, float v_scale, int S,
-                       int Lmax, const float* sink, uint16_t* o, int span, float* part,
-                       unsigned* ctr, hipStream_t st,
+                       int Lmax, int npos, const float* sink, uint16_t* o, int span,
+                       float* part, unsigned* ctr, hipStream_t st,
                        const AttnFuse* fuse = nullptr);
 
 // part: K-split partial logits, router_splits(T, E, D) x T x E fp32 (unused
@@ -151,7 +151,7 @@ inline bool attn_prefill_ok(int grp, int hd) {
 int launch_attn_prefill(int T, int Hq, int Hkv, int hd, int swa, int window, int fp8,
                         const uint16_t* q, const int32_t* pos, const int32_t* seq,
                         const void* kc, const void* vc, float k_scale, float v_scale, int S,
-                        int Lmax, const float* sink, uint16_t* o, hipStream_t st);
+                        int Lmax, int npos, const float* sink, uint16_t* o, hipStream_t st);
 
 int launch_hbm_read(const void* p, size_t bytes, unsigned* sink, hipStream_t st);
 

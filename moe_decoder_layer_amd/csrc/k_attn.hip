@@ -93,8 +93,8 @@ template <int HD, bool FP8, bool SWA, int NW, int GS, bool FUSED>
 __device__ __forceinline__ void attn_decode_body(
     const uint16_t* __restrict__ q, const int32_t* __restrict__ pos,
     const int32_t* __restrict__ seq, const void* __restrict__ kc, const void* __restrict__ vc,
-    int S, int Lmax, int Hq, int Hkv, int window, int tpw, float score_scale, int nch_stride,
-    float* part, uint16_t* __restrict__ o_direct, const float* __restrict__ sink,
+    int S, int Lmax, int npos, int Hq, int Hkv, int window, int tpw, float score_scale,
+    int nch_stride, float* part, uint16_t* __restrict__ o_direct, const float* __restrict__ sink,
     float v_scale, unsigned* ctr, const AttnFuse fz) {
   constexpr int KS = HD / 32;  // k-steps of the score product
   constexpr int DT = HD / 16;  // 16-dim tiles of the output
@@ -146,7 +146,7 @@ __device__ __forceinline__ void attn_decode_body(
 
   const int p = pos[t], s = seq[t];
   const int CK = NW * 64 * tpw;
-  int bad = (p < 0 || p >= Lmax) ? ERR_POS : (s < 0 || s >= S) ? ERR_SEQ : 0;
+  int bad = (p < 0 || p >= npos) ? ERR_POS : (s < 0 || s >= S) ? ERR_SEQ : 0;
   int lo = 0, nch = 0;
   if (!bad) {
     lo = SWA ? max(0, p - window + 1) : 0;
@@ -166,7 +166,11 @@ __device__ __forceinline__ void attn_decode_body(
   const int lo_al = lo & ~63;
   if (c >= nch) return;
 
-  const size_t krow0 = ((size_t)s * Hkv + j) * (size_t)Lmax;  // K row of position 0
+  // Position k lives in slot k mod Lmax (the identity unless the cache is a
+  // ring, npos > Lmax); a 64-key tile never wraps (Lmax % 64 == 0).
+  const bool ring = npos > Lmax;
+  const int ps = ring ? p % Lmax : p;                          // slot of position p
+  const size_t krow0 = ((size_t)s * Hkv + j) * (size_t)Lmax;  // K row of slot 0
   const size_t vrow0 = ((size_t)s * Hkv + j) * (size_t)HD;    // V^T row of dim 0
   float m = -INFINITY, lsum = 0.f;
   f32x4 o[DT];
@@ -184,9 +188,10 @@ __device__ __forceinline__ void attn_decode_body(
   uint4 kraw[4][KR];
   uint4 vraw[DT][VR];
   auto load_tile = [&](int kb) {
+    const int kbs = ring ? kb % Lmax : kb;  // slot of the tile's first key
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
-      const int key = kb + slot_key<FP8>(st, col >> 2, col & 3);
+      const int key = kbs + slot_key<FP8>(st, col >> 2, col & 3);
       const size_t kr = (krow0 + key) * HD;
       if constexpr (FP8 && KS >= 2) {  // steps 2h, 2h+1 share one 16-byte load
 #pragma unroll
@@ -204,7 +209,7 @@ __device__ __forceinline__ void attn_decode_body(
     }
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
-      const size_t vr = (vrow0 + dt * 16 + col) * (size_t)Lmax + kb;
+      const size_t vr = (vrow0 + dt * 16 + col) * (size_t)Lmax + kbs;
       if constexpr (FP8) {
         vraw[dt][0] = ld16((const uint8_t*)vc + vr + half_key<FP8>(0, g));
       } else {
@@ -247,7 +252,7 @@ __device__ __forceinline__ void attn_decode_body(
         qk_head_pair(row + (size_t)(Hq + j) * HD, false, HD, fz.wq, fz.wk, p, true, fz.mode,
                      fz.rope, fz.eps, a, b);
         if (lane < half) {
-          const size_t kr = (krow0 + p) * HD;
+          const size_t kr = (krow0 + ps) * HD;
           if constexpr (FP8) {
             uint8_t* k8 = reinterpret_cast<uint8_t*>(skv[0]);
             const uint8_t ca = f2e4m3(__fdiv_rn(a, fz.ks)), cb = f2e4m3(__fdiv_rn(b, fz.ks));
@@ -266,8 +271,8 @@ __device__ __forceinline__ void attn_decode_body(
       } else if (lane < half) {  // the new value, as produced: V^T[s][j][:][p]
         const uint16_t* vsrc = row + (size_t)(Hq + Hkv + j) * HD;
         const uint16_t va = vsrc[lane], vb = vsrc[lane + half];
-        const size_t ca0 = (vrow0 + lane) * (size_t)Lmax + p;
-        const size_t cb0 = (vrow0 + lane + half) * (size_t)Lmax + p;
+        const size_t ca0 = (vrow0 + lane) * (size_t)Lmax + ps;
+        const size_t cb0 = (vrow0 + lane + half) * (size_t)Lmax + ps;
         if constexpr (FP8) {
           uint8_t* v8 = reinterpret_cast<uint8_t*>(skv[1]);
           const uint8_t ca = f2e4m3(__fdiv_rn(bf2f(va), fz.vs));
@@ -515,11 +520,13 @@ __device__ __forceinline__ void attn_decode_body(
 #define ATTN_DECODE_PARAMS                                                                    \
   const uint16_t *__restrict__ q, const int32_t *__restrict__ pos,                          \
       const int32_t *__restrict__ seq, const void *__restrict__ kc,                         \
-      const void *__restrict__ vc, int S, int Lmax, int Hq, int Hkv, int window, int tpw,   \
-      float score_scale, int nch_stride, float *part, uint16_t *__restrict__ o_direct,      \
+      const void *__restrict__ vc, int S, int Lmax, int npos, int Hq, int Hkv, int window,  \
+      int tpw, float score_scale, int nch_stride, float *part,                              \
+      uint16_t *__restrict__ o_direct,                                                      \
       const float *__restrict__ sink, float v_scale, unsigned *ctr, const AttnFuse fz
 #define ATTN_DECODE_ARGS                                                                 \
-  q, pos, seq, kc, vc, S, Lmax, Hq, Hkv, window, tpw, score_scale, nch_stride, part, o_direct, \
+  q, pos, seq, kc, vc, S, Lmax, npos, Hq, Hkv, window, tpw, score_scale, nch_stride, part,    \
+      o_direct,                                                                              \
       sink, v_scale, ctr, fz
 
 template <int HD, bool FP8, bool SWA, int NW, int GS, bool FUSED>
@@ -540,7 +547,7 @@ attn_decode_fp8_stream_kernel(ATTN_DECODE_PARAMS) {
 template <int HD>
 __global__ __launch_bounds__(256) void attn_merge_small_kernel(
     const float* __restrict__ part, const int32_t* __restrict__ pos,
-    const int32_t* __restrict__ seq, int S, int Lmax, int T, int Hq, int window, int swa,
+    const int32_t* __restrict__ seq, int S, int npos, int T, int Hq, int window, int swa,
     int tpw, int nch_stride, const float* __restrict__ sink, float v_scale,
     uint16_t* __restrict__ o, const uint16_t* __restrict__ G, const uint16_t* __restrict__ bgate) {
   constexpr int MX = kAttnFusedMergeMax;
@@ -559,7 +566,7 @@ __global__ __launch_bounds__(256) void attn_merge_small_kernel(
     bp = bf2f(bgate[h]);
   }
   const int p = pos[t], s = seq[t];
-  if (p < 0 || p >= Lmax || s < 0 || s >= S) {
+  if (p < 0 || p >= npos || s < 0 || s >= S) {
     for (int d = lane; d < HD; d += 64) out[d] = 0;
     return;
   }
@@ -615,7 +622,7 @@ __global__ __launch_bounds__(256) void attn_merge_small_kernel(
 template <int HD>
 __global__ __launch_bounds__(1024) void attn_merge_kernel(
     const float* __restrict__ part, const int32_t* __restrict__ pos,
-    const int32_t* __restrict__ seq, int S, int Lmax, int Hq, int window, int swa, int tpw,
+    const int32_t* __restrict__ seq, int S, int npos, int Hq, int window, int swa, int tpw,
     int nch_stride, const float* __restrict__ sink, float v_scale, uint16_t* __restrict__ o,
     const uint16_t* __restrict__ G, const uint16_t* __restrict__ bgate) {
   constexpr int DPL = (HD + 63) / 64;
@@ -634,7 +641,7 @@ __global__ __launch_bounds__(1024) void attn_merge_kernel(
     bp = bf2f(bgate[h]);
   }
   const int p = pos[t], s = seq[t];
-  if (p < 0 || p >= Lmax || s < 0 || s >= S) {
+  if (p < 0 || p >= npos || s < 0 || s >= S) {
     for (int d = threadIdx.x; d < HD; d += MW * 64) out[d] = 0;
     return;
   }
@@ -743,7 +750,7 @@ bool attn_fused_merge(int T, int Hkv, int nch) {
 int launch_attn_decode(int T, int Hq, int Hkv, int hd, int swa, int window, int fp8,
                        const uint16_t* q, const int32_t* pos, const int32_t* seq,
                        const void* kc, const void* vc, float k_scale, float v_scale, int S,
-                       int Lmax, const float* sink, uint16_t* o, int span, float* part,
+                       int Lmax, int npos, const float* sink, uint16_t* o, int span, float* part,
                        unsigned* ctr, hipStream_t st, const AttnFuse* fuse) {
   const float score_scale = k_scale / sqrtf((float)hd) * 1.4426950408889634f;
   const float vsc = fp8 ? v_scale : 1.0f;
@@ -754,7 +761,7 @@ int launch_attn_decode(int T, int Hq, int Hkv, int hd, int swa, int window, int 
   uint16_t* od = (nch == 1 || fused) ? o : nullptr;
   unsigned* cp = fused ? ctr : nullptr;
   const AttnFuse fz = fuse ? *fuse : AttnFuse{};
-#define ARGS q, pos, seq, kc, vc, S, Lmax, Hq, Hkv, window, tpw, score_scale, nch, part, od, sink, vsc, cp, fz
+#define ARGS q, pos, seq, kc, vc, S, Lmax, npos, Hq, Hkv, window, tpw, score_scale, nch, part, od, sink, vsc, cp, fz
 #define PART(HD_, F8, SW)                                                                     \
   do {                                                                                        \
     if (fuse)                                                                                 \
@@ -797,7 +804,7 @@ int launch_attn_decode(int T, int Hq, int Hkv, int hd, int swa, int window, int 
     const dim3 sg((T * Hq + 3) / 4);
 #define SMALL(HD_)                                                                              \
   hipLaunchKernelGGL((attn_merge_small_kernel<HD_>), sg, dim3(256), 0, st, part, pos, seq, S,   \
-                     Lmax, T, Hq, window, swa, tpw, nch, sink, vs, o, G, bg)
+                     npos, T, Hq, window, swa, tpw, nch, sink, vs, o, G, bg)
     if (hd == 128) SMALL(128);
     else if (hd == 64) SMALL(64);
     else SMALL(32);
@@ -806,13 +813,13 @@ int launch_attn_decode(int T, int Hq, int Hkv, int hd, int swa, int window, int 
   }
   const dim3 mg(Hq, T);
   if (hd == 128)
-    hipLaunchKernelGGL((attn_merge_kernel<128>), mg, dim3(1024), 0, st, part, pos, seq, S, Lmax, Hq,
+    hipLaunchKernelGGL((attn_merge_kernel<128>), mg, dim3(1024), 0, st, part, pos, seq, S, npos, Hq,
                        window, swa, tpw, nch, sink, vs, o, G, bg);
   else if (hd == 64)
-    hipLaunchKernelGGL((attn_merge_kernel<64>), mg, dim3(1024), 0, st, part, pos, seq, S, Lmax, Hq,
+    hipLaunchKernelGGL((attn_merge_kernel<64>), mg, dim3(1024), 0, st, part, pos, seq, S, npos, Hq,
                        window, swa, tpw, nch, sink, vs, o, G, bg);
   else
-    hipLaunchKernelGGL((attn_merge_kernel<32>), mg, dim3(1024), 0, st, part, pos, seq, S, Lmax, Hq,
+    hipLaunchKernelGGL((attn_merge_kernel<32>), mg, dim3(1024), 0, st, part, pos, seq, S, npos, Hq,
                        window, swa, tpw, nch, sink, vs, o, G, bg);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }

@@ -41,7 +41,7 @@ template <int HD, bool FP8, bool SWA>
 __global__ __launch_bounds__(768) void attn_prefill_kernel(
     const uint16_t* __restrict__ q, const int32_t* __restrict__ pos,
     const int32_t* __restrict__ seq, const void* __restrict__ kc, const void* __restrict__ vc,
-    int S, int Lmax, int Hq, int Hkv, int window, float score_scale, int T, int ntb,
+    int S, int Lmax, int npos, int Hq, int Hkv, int window, float score_scale, int T, int ntb,
     const float* __restrict__ sink, float v_scale, uint16_t* __restrict__ o) {
   constexpr int KS = HD / 16;    // k-steps of the score product
   constexpr int DB = HD / 32;    // 32-dim blocks of the output
@@ -68,8 +68,8 @@ __global__ __launch_bounds__(768) void attn_prefill_kernel(
   const int t = t0 + 32 * tb + tc;
   const bool tok = t < T;
   int p = tok ? pos[t] : -1, s = tok ? seq[t] : -1;
-  if (p < 0 || p >= Lmax || s < 0 || s >= S) {
-    if (tok && hh == 0) BEAM_RAISE(attnp, (p < 0 || p >= Lmax) ? ERR_POS : ERR_SEQ);
+  if (p < 0 || p >= npos || s < 0 || s >= S) {
+    if (tok && hh == 0) BEAM_RAISE(attnp, (p < 0 || p >= npos) ? ERR_POS : ERR_SEQ);
     p = -1;
     s = -1;
   }
@@ -101,7 +101,7 @@ __global__ __launch_bounds__(768) void attn_prefill_kernel(
       if (lane < tblk && tt < T) {
         pp = pos[tt];
         ss = seq[tt];
-        if (pp < 0 || pp >= Lmax || ss < 0 || ss >= S) ss = -1;
+        if (pp < 0 || pp >= npos || ss < 0 || ss >= S) ss = -1;
       }
       sc = (ss > s_prev) ? ss : 0x7fffffff;
       for (int o2 = 32; o2 > 0; o2 >>= 1) sc = min(sc, __shfl_xor(sc, o2, 64));
@@ -130,13 +130,14 @@ __global__ __launch_bounds__(768) void attn_prefill_kernel(
     const int ntiles = (kmax - kb0) / KT + 1;
 
     auto gload = [&](int kb) {
+      const int kbs = (npos > Lmax) ? kb % Lmax : kb;  // ring cache: slot of the first key
 #pragma unroll
       for (int n = 0; n < UPT; ++n) {
         const int u = tid + n * nthr;
         if (u >= NU) break;
         if (u < NKU) {
           const int row = u / (HD / 8), c = u % (HD / 8);
-          const size_t off = (krow0 + kb + row) * HD + c * 8;
+          const size_t off = (krow0 + kbs + row) * HD + c * 8;
           if constexpr (FP8) {
             const uint2 w = *reinterpret_cast<const uint2*>((const uint8_t*)kc + off);
             reg[n] = uint4{w.x, w.y, 0u, 0u};
@@ -145,7 +146,7 @@ __global__ __launch_bounds__(768) void attn_prefill_kernel(
           }
         } else {
           const int u2 = u - NKU, dim = u2 >> 3, c = u2 & 7;
-          const size_t off = (vrow0 + dim) * (size_t)Lmax + kb + c * 8;
+          const size_t off = (vrow0 + dim) * (size_t)Lmax + kbs + c * 8;
           if constexpr (FP8) {
             const uint2 w = *reinterpret_cast<const uint2*>((const uint8_t*)vc + off);
             reg[n] = uint4{w.x, w.y, 0u, 0u};
@@ -329,7 +330,7 @@ template <bool SWA>
 __global__ __launch_bounds__(768) void attn_prefill_dma_kernel(
     const uint16_t* __restrict__ q, const int32_t* __restrict__ pos,
     const int32_t* __restrict__ seq, const uint16_t* __restrict__ kc,
-    const uint16_t* __restrict__ vc, int S, int Lmax, int Hq, int Hkv, int window,
+    const uint16_t* __restrict__ vc, int S, int Lmax, int npos, int Hq, int Hkv, int window,
     float score_scale, int T, int ntb, const float* __restrict__ sink,
     uint16_t* __restrict__ o) {
   constexpr int HD = DMA_HD;
@@ -362,8 +363,8 @@ __global__ __launch_bounds__(768) void attn_prefill_dma_kernel(
   const int t = t0 + 32 * tb + tc;
   const bool tok = t < T;
   int p = tok ? pos[t] : -1, s = tok ? seq[t] : -1;
-  if (p < 0 || p >= Lmax || s < 0 || s >= S) {
-    if (tok && hh == 0) BEAM_RAISE(attnp, (p < 0 || p >= Lmax) ? ERR_POS : ERR_SEQ);
+  if (p < 0 || p >= npos || s < 0 || s >= S) {
+    if (tok && hh == 0) BEAM_RAISE(attnp, (p < 0 || p >= npos) ? ERR_POS : ERR_SEQ);
     p = -1;
     s = -1;
   }
@@ -391,7 +392,7 @@ __global__ __launch_bounds__(768) void attn_prefill_dma_kernel(
       if (lane < tblk && tt < T) {
         pp = pos[tt];
         ss = seq[tt];
-        if (pp < 0 || pp >= Lmax || ss < 0 || ss >= S) ss = -1;
+        if (pp < 0 || pp >= npos || ss < 0 || ss >= S) ss = -1;
       }
       int sc = (ss > s_prev) ? ss : 0x7fffffff;
       for (int o2 = 32; o2 > 0; o2 >>= 1) sc = min(sc, __shfl_xor(sc, o2, 64));
@@ -428,7 +429,8 @@ __global__ __launch_bounds__(768) void attn_prefill_dma_kernel(
     const int ntiles = (kmax - kb0) / KT + 1;
 
     // instruction u < 16: K rows 4u..4u+3; u >= 16: V^T dim rows 8(u-16)..+7.
-    // kb + 63 <= Lmax - 1 (kb is 64-aligned, kb <= kmax < Lmax, Lmax % 64 == 0).
+    // kb + 63 <= Lmax - 1 for the tile's slot kb (64-aligned, below Lmax, and
+    // Lmax % 64 == 0; on a ring cache, position kb mod Lmax).
     // Wave w issues units w, w + nw, ... (at most MAXU: nw >= 8); each lane's
     // address at key 0 is formed once per sequence, a tile adds kb to it.
     // (element offsets from the sequence's K / V^T base: d * Lmax < 2^31)
@@ -446,13 +448,14 @@ __global__ __launch_bounds__(768) void attn_prefill_dma_kernel(
       }
     }
     auto gload = [&](int kb, int buf) {
+      const int kbs = (npos > Lmax) ? kb % Lmax : kb;  // ring cache: slot of the first key
 #pragma unroll
       for (int i = 0; i < MAXU; ++i) {
         const int u = wave + i * nw;
         if (u < NI / 2)
-          load_lds16(kbase_p + (go[i] + (uint32_t)kb * HD), sK(buf) + 4 * u * HD);
+          load_lds16(kbase_p + (go[i] + (uint32_t)kbs * HD), sK(buf) + 4 * u * HD);
         else if (u < NI)
-          load_lds16(vbase_p + (go[i] + (uint32_t)kb), sV(buf) + 8 * (u - NI / 2) * KT);
+          load_lds16(vbase_p + (go[i] + (uint32_t)kbs), sV(buf) + 8 * (u - NI / 2) * KT);
       }
     };
 
@@ -628,7 +631,7 @@ static size_t attn_prefill_lds(int hd) {
 int launch_attn_prefill(int T, int Hq, int Hkv, int hd, int swa, int window, int fp8,
                         const uint16_t* q, const int32_t* pos, const int32_t* seq,
                         const void* kc, const void* vc, float k_scale, float v_scale, int S,
-                        int Lmax, const float* sink, uint16_t* o, hipStream_t st) {
+                        int Lmax, int npos, const float* sink, uint16_t* o, hipStream_t st) {
   const float score_scale = k_scale / sqrtf((float)hd) * 1.4426950408889634f;
   const int grp = Hq / Hkv;
   // waves per workgroup = grp * ntb <= 12; every thread stages at most 4 units
@@ -648,7 +651,7 @@ int launch_attn_prefill(int T, int Hq, int Hkv, int hd, int swa, int window, int
         attr = true;
       }
       hipLaunchKernelGGL(kern, grid, block, sh, st, q, pos, seq, (const uint16_t*)kc,
-                         (const uint16_t*)vc, S, Lmax, Hq, Hkv, window, score_scale, T, ntb,
+                         (const uint16_t*)vc, S, Lmax, npos, Hq, Hkv, window, score_scale, T, ntb,
                          sink, o);
     };
     if (swa) go(attn_prefill_dma_kernel<true>);
@@ -665,7 +668,7 @@ int launch_attn_prefill(int T, int Hq, int Hkv, int hd, int swa, int window, int
       attr = true;                                                                             \
     }                                                                                          \
     hipLaunchKernelGGL((attn_prefill_kernel<HD_, F8, SW>), grid, block, sh, st, q, pos, seq,  \
-                       kc, vc, S, Lmax, Hq, Hkv, window, score_scale, T, ntb, sink, vs, o);    \
+                       kc, vc, S, Lmax, npos, Hq, Hkv, window, score_scale, T, ntb, sink, vs, o); \
   } while (0)
 #define BY_MODE(HD_)                                                  \
   if (fp8) {                                                         \

@@ -3,7 +3,9 @@
 // Beam 1.0 on vLLM": Attention section for the maths; optimisation changes 2
 // and 6 for the fusion).
 //
-// One wave per head (qk_head). Input is the bf16 q|k|v projection.
+// One wave per head (qk_head). Input is the bf16 q|k|v projection. Position p
+// goes to cache slot p mod Lmax (the identity unless the cache is a ring of
+// Lmax slots accepting positions up to npos > Lmax).
 #include "common.h"
 #include "internal.h"
 #include "qk_head.h"
@@ -21,8 +23,8 @@ __global__ __launch_bounds__(256) void qk_norm_pos_kvwrite_kernel(
     const uint16_t* __restrict__ wq, const uint16_t* __restrict__ wk,
     const int32_t* __restrict__ pos, const int32_t* __restrict__ seq, int mode,
     const float* __restrict__ rope_cs, uint16_t* __restrict__ q_out, void* __restrict__ kc,
-    void* __restrict__ vc, int fp8, float ks, float vs, int S, int Lmax, float eps, int T,
-    int nh, int tpt, int tstride) {
+    void* __restrict__ vc, int fp8, float ks, float vs, int S, int Lmax, int npos, float eps,
+    int T, int nh, int tpt, int tstride) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int head = blockIdx.x * 4 + wave;
   const int nheads = Hq + 2 * Hkv;
@@ -31,11 +33,13 @@ __global__ __launch_bounds__(256) void qk_norm_pos_kvwrite_kernel(
   const int t = blockIdx.y + k * tstride;
   if (t >= T) return;
   const int p = pos[t], s = seq[t];
-  const bool slot_ok = (p >= 0 && p < Lmax && s >= 0 && s < S);
+  const bool slot_ok = (p >= 0 && p < npos && s >= 0 && s < S);
   if (!slot_ok && head == 0 && lane == 0)
-    BEAM_RAISE(qk, (p < 0 || p >= Lmax) ? ERR_POS : ERR_SEQ);
-  qk_head(qkv + (size_t)t * nheads * hd + (size_t)head * hd, head, Hq, Hkv, hd, wq, wk, p, s,
-          slot_ok, mode, rope_cs, q_out + (size_t)t * Hq * hd, kc, vc, fp8, ks, vs, Lmax, eps);
+    BEAM_RAISE(qk, (p < 0 || p >= npos) ? ERR_POS : ERR_SEQ);
+  const int ps = slot_ok ? p % Lmax : 0;
+  qk_head(qkv + (size_t)t * nheads * hd + (size_t)head * hd, head, Hq, Hkv, hd, wq, wk, p, ps,
+          s, slot_ok, mode, rope_cs, q_out + (size_t)t * Hq * hd, kc, vc, fp8, ks, vs, Lmax,
+          eps);
   }
 }
 
@@ -48,7 +52,7 @@ __global__ __launch_bounds__(256) void qk_rows_kernel(
     const uint16_t* __restrict__ wk, const int32_t* __restrict__ pos,
     const int32_t* __restrict__ seq, int mode, const float* __restrict__ rope_cs,
     uint16_t* __restrict__ q_out, void* __restrict__ kc, int fp8, float ks, int S, int Lmax,
-    float eps, int T) {
+    int npos, float eps, int T) {
   constexpr int HD = 128;
   const int lane = threadIdx.x & 63, j = lane & 15;
   const int nhq = Hq + Hkv, nheads = Hq + 2 * Hkv;
@@ -57,9 +61,9 @@ __global__ __launch_bounds__(256) void qk_rows_kernel(
   const int t = live ? (int)(u / nhq) : 0, head = live ? (int)(u - (long long)t * nhq) : 0;
   const bool is_q = head < Hq;
   const int p = pos[t], s = seq[t];
-  const bool slot_ok = (p >= 0 && p < Lmax && s >= 0 && s < S);
+  const bool slot_ok = (p >= 0 && p < npos && s >= 0 && s < S);
   if (live && !slot_ok && head == 0 && j == 0)
-    BEAM_RAISE(qk, (p < 0 || p >= Lmax) ? ERR_POS : ERR_SEQ);
+    BEAM_RAISE(qk, (p < 0 || p >= npos) ? ERR_POS : ERR_SEQ);
   // all loads first: the head's 8 values, the gains, this lane's cos/sin run
   const uint4 xv = ld16(qkv + (size_t)t * nheads * HD + (size_t)head * HD + 8 * j);
   const uint4 wv = ld16((is_q ? wq : wk) + 8 * j);
@@ -118,7 +122,8 @@ __global__ __launch_bounds__(256) void qk_rows_kernel(
     return;
   }
   if (!slot_ok) return;
-  const size_t row = (((size_t)s * Hkv + (head - Hq)) * Lmax + p) * HD + 8 * j;  // K[s][kv][p]
+  const size_t row =
+      (((size_t)s * Hkv + (head - Hq)) * Lmax + p % Lmax) * HD + 8 * j;  // K[s][kv][slot]
   if (fp8) {
     uint32_t lo = 0, hi = 0;
 #pragma unroll
@@ -147,15 +152,15 @@ __global__ __launch_bounds__(64) void v_write_kernel(const uint16_t* __restrict_
                                                      const int32_t* __restrict__ pos,
                                                      const int32_t* __restrict__ seq,
                                                      void* __restrict__ vc, int fp8, float vs,
-                                                     int S, int Lmax, int T) {
+                                                     int S, int Lmax, int npos, int T) {
   const int j = blockIdx.x;
   const int t = blockIdx.y * 64 + threadIdx.x;
   if (t >= T) return;
   const int p = pos[t], s = seq[t];
-  if (p < 0 || p >= Lmax || s < 0 || s >= S) return;  // flagged by the q/k kernel
+  if (p < 0 || p >= npos || s < 0 || s >= S) return;  // flagged by the q/k kernel
   const int nheads = Hq + 2 * Hkv;
   const uint16_t* src = qkv + (size_t)t * nheads * hd + (size_t)(Hq + Hkv + j) * hd;
-  const size_t col = (((size_t)s * Hkv + j) * hd) * (size_t)Lmax + p;  // V^T[s][j][0][p]
+  const size_t col = (((size_t)s * Hkv + j) * hd) * (size_t)Lmax + p % Lmax;  // V^T[s][j][0][slot]
   for (int d0 = 0; d0 < hd; d0 += 8) {
     const uint4 u = ld16(src + d0);
     const uint32_t w[4] = {u.x, u.y, u.z, u.w};
@@ -172,7 +177,7 @@ __global__ __launch_bounds__(64) void v_write_kernel(const uint16_t* __restrict_
 int launch_qk_epilogue(int T, int Hq, int Hkv, int hd, const uint16_t* qkv, const uint16_t* wq,
                        const uint16_t* wk, const int32_t* pos, const int32_t* seq, int mode,
                        const float* rope_cs, uint16_t* q_out, void* kc, void* vc, int fp8,
-                       float k_scale, float v_scale, int S, int Lmax, float eps,
+                       float k_scale, float v_scale, int S, int Lmax, int npos, float eps,
                        hipStream_t st) {
   if (T <= kGemvMaxT || (T <= kDecodeBatchMaxT && T <= 4 * S)) {
     // few tokens, or a batch of decode steps spread over many sequences: one
@@ -180,25 +185,25 @@ int launch_qk_epilogue(int T, int Hq, int Hkv, int hd, const uint16_t* qkv, cons
     const dim3 grid((Hq + 2 * Hkv + 3) / 4, T);
     hipLaunchKernelGGL(qk_norm_pos_kvwrite_kernel, grid, dim3(256), 0, st, qkv, Hq, Hkv, hd, wq,
                        wk, pos, seq, mode, rope_cs, q_out, kc, vc, fp8, k_scale, v_scale, S,
-                       Lmax, eps, T, Hq + 2 * Hkv, 1, T);
+                       Lmax, npos, eps, T, Hq + 2 * Hkv, 1, T);
     return hipGetLastError() == hipSuccess ? 0 : -1;
   }
   if (hd == 128) {
     const long long items = (long long)T * (Hq + Hkv);  // (token, q or k head)
     hipLaunchKernelGGL(qk_rows_kernel, dim3((unsigned)((items + 15) / 16)), dim3(256), 0, st,
                        qkv, Hq, Hkv, wq, wk, pos, seq, mode, rope_cs, q_out, kc, fp8, k_scale,
-                       S, Lmax, eps, T);
+                       S, Lmax, npos, eps, T);
   } else {
     constexpr int TPT = 8;  // tokens per wave
     const int tb = (T + TPT - 1) / TPT;
     const dim3 grid((Hq + Hkv + 3) / 4, tb);
     hipLaunchKernelGGL(qk_norm_pos_kvwrite_kernel, grid, dim3(256), 0, st, qkv, Hq, Hkv, hd, wq,
                        wk, pos, seq, mode, rope_cs, q_out, kc, vc, fp8, k_scale, v_scale, S,
-                       Lmax, eps, T, Hq + Hkv, TPT, tb);
+                       Lmax, npos, eps, T, Hq + Hkv, TPT, tb);
   }
   if (hipGetLastError() != hipSuccess) return -1;
   hipLaunchKernelGGL(v_write_kernel, dim3(Hkv, (T + 63) / 64), dim3(64), 0, st, qkv, Hq, Hkv,
-                     hd, pos, seq, vc, fp8, v_scale, S, Lmax, T);
+                     hd, pos, seq, vc, fp8, v_scale, S, Lmax, npos, T);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

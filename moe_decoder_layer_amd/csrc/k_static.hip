@@ -54,6 +54,9 @@ extern "C" int beam_attn_nope_ssmax_static(const beam_dims* dims, int T, const u
   if (!dims) return abi_fail(BEAM_E_NULL, "%s: dims is NULL", __func__);
   if (T <= 0) return abi_fail(BEAM_E_SHAPE, "%s: T <= 0", __func__);
   if (max_pos < 0) return abi_fail(BEAM_E_SHAPE, "%s: max_pos < 0", __func__);
+  if (kv && kv->npos > kv->Lmax)
+    return abi_fail(BEAM_E_UNSUPPORTED, "%s: a ring cache serves sliding-window attention only",
+                    __func__);
   const size_t need = beam_workspace_size(dims, BEAM_OP_ATTN_NOPE, T, max_pos + 1);
   if (need == (size_t)-1) return abi_fail(BEAM_E_SHAPE, "%s: invalid dims", __func__);
   if (need > kStaticScratchBytes)

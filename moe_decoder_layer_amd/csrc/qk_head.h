@@ -51,10 +51,11 @@ __device__ __forceinline__ void qk_head_pair(const uint16_t* src, bool is_q, int
 }
 
 // head in [0, Hq + 2 Hkv): q heads, then k heads, then v heads. src: the
-// head's d bf16 projection values; q_row: the token's q output [Hq][d].
+// head's d bf16 projection values; q_row: the token's q output [Hq][d]; p the
+// position (RoPE, SSMax), ps its cache slot (p mod Lmax).
 __device__ __forceinline__ void qk_head(const uint16_t* src, int head, int Hq, int Hkv, int hd,
                                         const uint16_t* __restrict__ wq,
-                                        const uint16_t* __restrict__ wk, int p, int s,
+                                        const uint16_t* __restrict__ wk, int p, int ps, int s,
                                         bool slot_ok, int mode,
                                         const float* __restrict__ rope_cs, uint16_t* q_row,
                                         void* kc, void* vc, int fp8, float ks, float vs,
@@ -67,8 +68,8 @@ __device__ __forceinline__ void qk_head(const uint16_t* src, int head, int Hq, i
   if (head >= Hq + Hkv) {  // value head: stored as produced (bf16), or quantised
     if (!slot_ok || !act) return;
     const int j = head - Hq - Hkv;
-    // V^T[s][j][dim][p]
-    const size_t col = ((size_t)s * Hkv + j) * (size_t)hd * (size_t)Lmax + (size_t)p;
+    // V^T[s][j][dim][slot]
+    const size_t col = ((size_t)s * Hkv + j) * (size_t)hd * (size_t)Lmax + (size_t)ps;
     if (fp8) {
       uint8_t* v = (uint8_t*)vc;
       v[col + (size_t)lane * Lmax] = f2e4m3(__fdiv_rn(a, vs));
@@ -92,7 +93,7 @@ __device__ __forceinline__ void qk_head(const uint16_t* src, int head, int Hq, i
   }
   if (!slot_ok || !act) return;
   const int j = head - Hq;
-  const size_t row = (((size_t)s * Hkv + j) * Lmax + p) * hd;  // K[s][j][p][:]
+  const size_t row = (((size_t)s * Hkv + j) * Lmax + ps) * hd;  // K[s][j][slot][:]
   if (fp8) {
     uint8_t* k = (uint8_t*)kc;
     k[row + lane] = f2e4m3(__fdiv_rn(a, ks));

@@ -101,6 +101,25 @@ def test_attention_router_moe_validation():
     dw = _dims(window=0)
     assert _rc("beam_attn_swa", ctypes.byref(dw), 1, A, A, A, ctypes.byref(kv), None, A, 64, A,
                ws, None) == -2
+    # ring caches (slot = position mod Lmax): npos above Lmax, sliding window only,
+    # window inside the ring, max_pos below npos
+    ring = B.kv_struct(A, A, B.BEAM_KV_BF16, 1.0, 1.0, 1, 512, 1 << 20)
+    wsr = B.beam_workspace_size(d, B.BEAM_OP_ATTN_SWA, 1, 1 << 20)
+    assert _rc("beam_attn_swa", by, 1, A, A, A, ctypes.byref(ring), None, A, 900000, A, wsr,
+               None) == -7                                     # accepted (no device here)
+    assert _rc("beam_attn_swa", by, 1, A, A, A, ctypes.byref(ring), None, A, 1 << 20, A, wsr,
+               None) == -2                                     # max_pos >= npos
+    assert _rc("beam_attn_nope_ssmax", by, 1, A, A, A, ctypes.byref(ring), None, A, 900, A,
+               wsr, None) == -3                                # full context on a ring
+    assert _rc("beam_attn_nope_ssmax_static", by, 1, A, A, A, ctypes.byref(ring), None, A, 900,
+               None) == -3
+    small = B.kv_struct(A, A, B.BEAM_KV_BF16, 1.0, 1.0, 1, 448, 1 << 20)
+    d512 = _dims(window=512)
+    assert _rc("beam_attn_swa", ctypes.byref(d512), 1, A, A, A, ctypes.byref(small), None, A,
+               900, A, wsr, None) == -2                        # window 512 > 448 slots
+    part = B.kv_struct(A, A, B.BEAM_KV_BF16, 1.0, 1.0, 1, 512, 300)
+    assert _rc("beam_attn_swa", by, 1, A, A, A, ctypes.byref(part), None, A, 200, A, wsr,
+               None) == -2                                     # 0 < npos < Lmax
     # router: topk larger than the kept groups can hold
     dr = _dims(topk=9)
     assert _rc("beam_router_fp32_grouped_topk", ctypes.byref(dr), 1, A, A, None, A, A, A, None,

@@ -50,6 +50,10 @@ def parse():
                     help="skip the NoPE fp8 decode leg at a 2^20-token context")
     ap.add_argument("--no-head", action="store_true",
                     help="skip the output head (logit soft cap) leg")
+    ap.add_argument("--no-stack", action="store_true",
+                    help="skip the 52-layer decode step at a 2^20-token context")
+    ap.add_argument("--stack-steps", type=int, default=10,
+                    help="timed whole-model decode steps (each about 14 ms)")
     ap.add_argument("--unfused", action="store_true",
                     help="batch-1 decode legs with the separate q/k, attention and gate + "
                          "o_proj calls instead of the fused attention call")
@@ -264,6 +268,9 @@ def main():
     if not a.no_head:
         out["lm_head_softcap_b1"] = head_leg()
         torch.cuda.empty_cache()
+    if not a.no_stack:
+        out["decode_stack_52"] = stack_leg(a)
+        torch.cuda.empty_cache()
     if not a.no_flint:
         out["decode_flint_b128"] = {m: flint_leg(a, m) for m in ("swa", "nope")}
         torch.cuda.empty_cache()
@@ -300,6 +307,102 @@ def head_leg():
     return {"workload": "lm_head_softcap_decode", "hidden": D, "vocab": V, "cap": 30.0,
             "us": round(us, 3), "bytes": nbytes, "achieved_gbs": round(gbs, 1),
             "frac": round(gbs / HBM_PEAK_GBS, 4)}
+
+
+def stack_leg(a):
+    """One decode token through the whole Beam model on one GPU: the 52 layers
+    in the model's schedule (beam_layer_kind: 43 sliding-window layers on
+    512-slot ring caches, 9 NoPE layers on full caches, the token at position
+    2^20, fp8 KV throughout; layers 0-2 dense) in one beam_decode_stack call,
+    then the output head with the soft cap, one HIP graph per step. One GPU
+    cannot hold 49 layers of bf16 experts (about 20 GB each), so the MoE layers
+    take their weights from two sets used by alternate layers, and the dense
+    layers likewise (a layer's selected experts, ~0.6 GB, evict the other set
+    from the caches, so every layer still streams its weights from HBM); every
+    layer has its own KV cache (18 GiB for the nine NoPE layers)."""
+    import numpy as np
+    import torch
+
+    import moe_decoder_layer_amd as B
+    import synth
+    t0 = time.time()
+    dims = synth.config(1).dims
+    D, Fd, NL, ctx, V = dims.D, dims.Fd, 52, 1 << 20, 131072
+    kinds = [B.beam_layer_kind(l, NL) for l in range(NL)]
+    msets = [LayerSet(dims, seed, 200 + seed, 64, 64, "fp8") for seed in (0, 1)]
+    dsets = [(synth.torch_normal_bf16((2 * Fd, D), 0.02, seed, "stack_dense_w13"),
+              synth.torch_normal_bf16((D, Fd), 0.02, seed, "stack_dense_w2")) for seed in (0, 1)]
+    U8 = dict(dtype=torch.uint8, device="cuda")
+    npos = ctx + 64                   # positions [0, 2^20] (the token sits at 2^20)
+    caches, kvs = [], []
+    for l, (mode, dense) in enumerate(kinds):
+        slots = 512 if mode == B.BEAM_SWA_ROPE else npos
+        fill = 512 if mode == B.BEAM_SWA_ROPE else ctx
+        Kp, Vp, ks, vs = synth.torch_kv_prior(dims, 1, fill, "fp8", 300, l)
+        K = torch.empty((1, dims.Hkv, slots, dims.d), **U8)
+        Vt = torch.empty((1, dims.Hkv, dims.d, slots), **U8)
+        K[:, :, :fill] = Kp
+        Vt[:, :, :, :fill] = Vp.transpose(2, 3)
+        del Kp, Vp
+        caches.append((K, Vt))
+        kvs.append(B.kv_struct(K, Vt, B.BEAM_KV_FP8_E4M3, ks, vs, 1, slots,
+                               npos if mode == B.BEAM_SWA_ROPE else 0))
+    rope_h = np.zeros((npos, dims.d), np.float32)
+    B.beam_rope_table(rope_h, npos, dims.d, dims.theta)
+    rope = torch.from_numpy(rope_h).cuda()
+    del rope_h
+    layers = []
+    for l, (mode, dense) in enumerate(kinds):
+        w = dict(msets[l % 2].t)
+        if dense:
+            w["w13"], w["w2"] = dsets[l % 2]
+        layers.append(B.stack_layer(mode, dense, w, kvs[l]))
+    w_final = msets[0].t["w_next_pre"]
+    w_head = synth.torch_normal_bf16((V, D), 0.02, 0, "stack_head_w")
+    I16 = dict(dtype=torch.int16, device="cuda")
+    h = synth.torch_normal_bf16((1, D), 1.0, 0, "stack_h")
+    x = torch.empty((1, D), **I16)
+    logits = torch.empty((1, V), dtype=torch.float32, device="cuda")
+    pos = torch.tensor([ctx], dtype=torch.int32, device="cuda")
+    seq = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ws = torch.zeros(B.beam_decode_stack_workspace(dims, Fd, ctx + 1), **U8)
+    log(f"[bench] 52-layer stack: weights, caches and RoPE table set up in "
+        f"{time.time() - t0:.1f}s ({torch.cuda.memory_allocated() / 2**30:.1f} GiB)")
+
+    def step(k):
+        B.beam_decode_stack(dims, Fd, 0, layers, w_final, h, x, pos, seq, rope, ctx, ws)
+        B.beam_lm_head_softcap(1, D, V, x, w_head, 30.0, logits)
+
+    step(0)                              # one eager step validates the composition
+    torch.cuda.synchronize()
+    B.beam_check()
+    assert torch.isfinite(logits).all(), "non-finite logits"
+    warm = max(1, min(a.warmup, 3))
+    us, per, reps, _, dsrc = timed_steps(step, 1, warm, a.stack_steps, 1)
+    B.beam_check()
+    # algorithmic bytes: weights each layer reads, KV read and written, the head
+    attn_w = dims.qkvg_rows * D * 2 + D * dims.Hq * dims.d * 2
+    kv_tok = dims.Hkv * dims.d * 2          # K and V bytes of one position (fp8)
+    nbytes = V * D * 2
+    for mode, dense in kinds:
+        nbytes += attn_w + kv_tok
+        nbytes += (dims.window if mode == B.BEAM_SWA_ROPE else ctx + 1) * kv_tok
+        nbytes += 3 * Fd * D * 2 if dense else dims.E * D * 4 + dims.topk * 3 * dims.F * D * 2
+    gbs = nbytes / (us * 1e-6) / 1e9
+    log(f"[bench] 52-layer decode step + head at 2^20 context: {us / 1000:.3f} ms/token "
+        f"(median {np.median(per) / 1000:.3f}, p90 {np.percentile(per, 90) / 1000:.3f} over "
+        f"{dsrc}), {1e6 / us:.1f} tok/s, {gbs:.0f} GB/s")
+    res = {"workload": "beam_52_layer_decode_step", "layers": NL, "sliding_window_layers":
+           sum(m == B.BEAM_SWA_ROPE for m, _ in kinds), "dense_layers": sum(d for _, d in kinds),
+           "context": ctx, "kv_cache": "fp8", "sliding_window_cache": "ring of 512 slots",
+           "experts": "bf16", "moe_weight_sets": 2, "lm_head_vocab": V, "steps": a.stack_steps,
+           "warmup": warm, "graph_replays": reps, "distribution": dsrc,
+           "ms_per_token": round(us / 1000, 4), "ms_median": round(float(np.median(per)) / 1000, 4),
+           "ms_p90": round(float(np.percentile(per, 90)) / 1000, 4),
+           "tokens_per_s": round(1e6 / us, 2), "bytes_per_step": nbytes,
+           "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+    del layers, kvs, caches, msets, dsets, rope, w_head
+    return res
 
 
 def graph_us(fn, reps):

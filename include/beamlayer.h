@@ -390,6 +390,62 @@ int beam_dense_swiglu(int T, int D, int Fd, const uint16_t* x, const uint16_t* w
  * Returns 0 for ops that need none and (size_t)-1 for invalid arguments. */
 size_t beam_workspace_size(const beam_dims* dims, int op, int T, int max_ctx);
 
+/* The Beam model's layer schedule ("Reflection Beam 1.0 on vLLM": model
+ * architecture, Attention, MoE and residual stream sections): layer (0-based)
+ * of an n_layers stack attends the full context without positions
+ * (BEAM_NOPE_SSMAX) when its 1-based number is a multiple of 6 or it is the
+ * last layer, else a sliding window with RoPE (BEAM_SWA_ROPE); layers 0-2 run
+ * a dense SwiGLU FFN (*dense = 1), the others MoE. Of 52 layers: 43 + 9, and
+ * 3 dense + 49 MoE. Errors: NULL outputs, layer outside [0, n_layers). */
+int beam_layer_kind(int layer, int n_layers, int* attn_mode, int* dense);
+
+/* One layer of a decode stack: attention mode (BEAM_SWA_ROPE or
+ * BEAM_NOPE_SSMAX), FFN kind (dense 1: w13 [2 Fd][D] and w2 [D][Fd] of the
+ * dense SwiGLU; dense 0: experts w13 [E][2F][D], w2 [E][D][F] and the fp32
+ * router w_r [E][D], b_corr [E]), the sandwich norm gains, the attention
+ * weights of the single-layer calls (device pointers) and the layer's KV cache
+ * (a ring on sliding-window layers, see beam_kv). */
+typedef struct beam_stack_layer {
+  int attn_mode;
+  int dense;
+  const uint16_t *w_attn_pre, *w_attn_post, *w_ffn_pre, *w_ffn_post;
+  const uint16_t *w_qnorm, *w_knorm, *w_qkvg, *b_gate, *w_o;
+  const float *w_r, *b_corr;
+  const uint16_t *w13, *w2;
+  beam_kv kv;
+} beam_stack_layer;
+
+/* Workspace bytes of beam_decode_stack (counter block first; zero it once). */
+size_t beam_decode_stack_workspace(const beam_dims* dims, int Fd, int max_ctx);
+
+/* One decode step of one token through n_layers consecutive layers of a
+ * sandwich-norm stack (the layer as the single-layer calls compose it, the
+ * attention half through beam_attn_decode_fused), layers[0] being layer
+ * `layer0` of the model:
+ *   x = RMSNorm(h; layers[0].w_attn_pre)
+ *   for each layer l (model index L = layer0 + l):
+ *     z = attention half of x (cache write at pos); y = z . w_o^T
+ *     h, x2 = boundary(y; w_attn_post, w_ffn_pre; residual add 2L + 1)
+ *             (MoE layers: with the router's grouped top-k)
+ *     y2 = MoE(x2) or dense SwiGLU(x2)
+ *     h, x = boundary(y2; w_ffn_post, w_next; residual add 2L + 2),
+ *            w_next = the next layer's w_attn_pre, or w_final after the last
+ *   x_out = x (the output head's input when the run ends the model).
+ * h [1][D] bf16 in/out; x_out [1][D]; pos, seq [1] int32 (device); rope_cs
+ * the RoPE table of the sliding-window layers (a row per position up to
+ * max_pos); max_pos >= pos[0]; Fd the dense d_ff (0 when no layer is dense).
+ * dims describes every layer (dims->F the expert d_ff). Launches 6 calls per
+ * layer on `stream`, so a whole step can be captured in one HIP graph.
+ * ws >= beam_decode_stack_workspace(dims, Fd, max_pos + 1).
+ * Errors: those of the composed calls (the first failing one), plus NULL
+ * arguments, an invalid mode, a dense layer with Fd = 0, an MoE layer
+ * without router weights. */
+int beam_decode_stack(const beam_dims* dims, int Fd, int layer0, int n_layers,
+                      const beam_stack_layer* layers, const uint16_t* w_final, uint16_t* h,
+                      uint16_t* x_out, const int32_t* pos, const int32_t* seq,
+                      const float* rope_cs, int max_pos, void* ws, size_t ws_bytes,
+                      void* stream);
+
 /* Host helper: fill out[Lmax][d] (host memory) with the RoPE table used by
  * beam_qk_norm_rope_ssmax_kvwrite, computed in double and stored as float. */
 int beam_rope_table(float* out, int Lmax, int d, double theta);

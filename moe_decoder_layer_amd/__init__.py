@@ -60,6 +60,13 @@ class beam_kv(ctypes.Structure):
                 ("v_scale", c_float), ("S", c_int), ("Lmax", c_int), ("npos", c_int)]
 
 
+class beam_stack_layer(ctypes.Structure):
+    _fields_ = [("attn_mode", c_int), ("dense", c_int)] + \
+               [(n, c_void_p) for n in ("w_attn_pre", "w_attn_post", "w_ffn_pre", "w_ffn_post",
+                                        "w_qnorm", "w_knorm", "w_qkvg", "b_gate", "w_o", "w_r",
+                                        "b_corr", "w13", "w2")] + [("kv", beam_kv)]
+
+
 _lib = None
 
 
@@ -103,6 +110,10 @@ def lib():
             "beam_lm_head_softcap": [c_int, c_int, c_int, P, P, c_float, P, P],
             "beam_moe_swiglu_combine_mxfp4": [POINTER(beam_dims), c_int, P, P, P, P, P, P, P, P,
                                               P, c_size_t, P],
+            "beam_layer_kind": [c_int, c_int, POINTER(c_int), POINTER(c_int)],
+            "beam_decode_stack": [POINTER(beam_dims), c_int, c_int, c_int,
+                                  POINTER(beam_stack_layer), P, P, P, P, P, P, c_int, P,
+                                  c_size_t, P],
             "beam_check": [P],
             "beam_version": [],
             "beam_last_error": [],
@@ -116,6 +127,9 @@ def lib():
         L.beam_last_error.restype = ctypes.c_char_p
         L.beam_workspace_size.argtypes = [POINTER(beam_dims), c_int, c_int, c_int]
         L.beam_workspace_size.restype = c_size_t
+        if hasattr(L, "beam_decode_stack_workspace"):
+            L.beam_decode_stack_workspace.argtypes = [POINTER(beam_dims), c_int, c_int]
+            L.beam_decode_stack_workspace.restype = c_size_t
         _lib = L
     return _lib
 
@@ -293,6 +307,36 @@ def beam_moe_swiglu_combine_mxfp4(dims, T, x, idx, w, w13_codes, w13_scales, w2_
     wp, wb = _ws(ws)
     _call("beam_moe_swiglu_combine_mxfp4", ctypes.byref(d), T, _p(x), _p(idx), _p(w),
           _p(w13_codes), _p(w13_scales), _p(w2_codes), _p(w2_scales), _p(y), wp, wb, _s(stream))
+
+
+def stack_layer(attn_mode: int, dense: int, w: dict, kv: beam_kv) -> beam_stack_layer:
+    """One beam_stack_layer from a dict of device tensors (keys as the struct's
+    pointer fields; w13/w2 the experts, or the dense FFN when dense=1)."""
+    ptrs = [_p(w.get(n)) for n in ("w_attn_pre", "w_attn_post", "w_ffn_pre", "w_ffn_post",
+                                   "w_qnorm", "w_knorm", "w_qkvg", "b_gate", "w_o", "w_r",
+                                   "b_corr", "w13", "w2")]
+    return beam_stack_layer(attn_mode, dense, *ptrs, kv)
+
+
+def beam_layer_kind(layer, n_layers):
+    """(attention mode, dense) of a 0-based layer of an n_layers stack."""
+    m, d = ctypes.c_int(), ctypes.c_int()
+    _call("beam_layer_kind", layer, n_layers, ctypes.byref(m), ctypes.byref(d))
+    return m.value, d.value
+
+
+def beam_decode_stack_workspace(dims, Fd, max_ctx):
+    return lib().beam_decode_stack_workspace(ctypes.byref(_d(dims)), Fd, max_ctx)
+
+
+def beam_decode_stack(dims, Fd, layer0, layers, w_final, h, x_out, pos, seq, rope_cs, max_pos,
+                      ws, stream=None):
+    """layers: a sequence of beam_stack_layer (see stack_layer)."""
+    d = _d(dims)
+    arr = (beam_stack_layer * len(layers))(*layers)
+    wp, wb = _ws(ws)
+    _call("beam_decode_stack", ctypes.byref(d), Fd, layer0, len(layers), arr, _p(w_final), _p(h),
+          _p(x_out), _p(pos), _p(seq), _p(rope_cs), max_pos, wp, wb, _s(stream))
 
 
 def beam_lm_head_softcap(T, D, V, x, w, cap, logits, stream=None):

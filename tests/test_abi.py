@@ -20,7 +20,7 @@ MIS = 0x10002        # misaligned
 
 def test_library_exports_every_declared_symbol():
     names = B.header_functions()
-    assert len(names) == 24
+    assert len(names) == 27
     L = ctypes.CDLL(B.LIB_PATH)
     for n in names:
         assert hasattr(L, n), n
@@ -238,3 +238,41 @@ def test_static_attention_validation():
     assert "static" in B.beam_last_error()
     assert _rc(f, by, 128, A, A, A, ctypes.byref(kv), None, A, 81919, None) == -7  # fits: no device
     assert _rc(f, by, 1, A, A, A, ctypes.byref(kv), None, A, 100000, None) == -7
+
+
+def test_layer_schedule_matches_oracle():
+    """The library's layer schedule (a host helper) against the oracle's, which
+    is pinned to the pages' 43 / 9 / 3 / 49 counts."""
+    from oracle import accounting as acc
+    for n in (52, 7, 12, 13, 1):
+        for l in range(n):
+            attn, ffn = acc.layer_kind(l, n)
+            want = (B.BEAM_NOPE_SSMAX if attn == "nope" else B.BEAM_SWA_ROPE,
+                    1 if ffn == "dense" else 0)
+            assert B.beam_layer_kind(l, n) == want, (n, l)
+    with pytest.raises(B.BeamError):
+        B.beam_layer_kind(52, 52)
+    with pytest.raises(B.BeamError):
+        B.beam_layer_kind(-1, 52)
+
+
+@cpu_only
+def test_decode_stack_validation_and_nodev():
+    d = _dims()
+    kv = B.kv_struct(A, A, B.BEAM_KV_BF16, 1.0, 1.0, 1, 1024)
+    w = {n: A for n in ("w_attn_pre", "w_attn_post", "w_ffn_pre", "w_ffn_post", "w_qnorm",
+                        "w_knorm", "w_qkvg", "b_gate", "w_o", "w_r", "b_corr", "w13", "w2")}
+    moe = B.stack_layer(B.BEAM_SWA_ROPE, 0, w, kv)
+    dense = B.stack_layer(B.BEAM_SWA_ROPE, 1, w, kv)
+    need = B.beam_decode_stack_workspace(d, 512, 1024)
+    assert 0 < need < (1 << 30)
+    arr = lambda *ls: (B.beam_stack_layer * len(ls))(*ls)  # noqa: E731
+    call = lambda ls, Fd=512, ws=need: _rc("beam_decode_stack", ctypes.byref(d), Fd, 0, len(ls),  # noqa
+                                           arr(*ls), A, A, A, A, A, A, 1000, A, ws, None)
+    assert call([dense], Fd=0) == -2                   # dense layer without Fd
+    assert call([moe], ws=need - 1) == -5
+    bad = B.stack_layer(7, 0, w, kv)
+    assert call([bad]) == -2
+    w2 = dict(w, w_r=None)
+    assert call([B.stack_layer(B.BEAM_SWA_ROPE, 0, w2, kv)]) == -1
+    assert call([dense, moe]) == -7                    # valid: no device here

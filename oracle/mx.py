@@ -125,3 +125,39 @@ def mxfp4_dequantize(packed, scales) -> np.ndarray:
     s = np.asarray(scales, dtype=np.int64) - 127
     v = e2m1_decode(c).reshape(*c.shape[:-1], -1, BLOCK)
     return np.ldexp(v, s[..., None]).reshape(c.shape)
+
+
+# ---------------------------------------------------------------------------
+# Block-scaled operands on both sides (prefill experts on scaled matrix cores)
+# ---------------------------------------------------------------------------
+
+def mxfp8_round(a) -> np.ndarray:
+    """An activation tensor as an MXFP8 operand: each row quantised along its
+    last axis in blocks of 32 (the weights' rule) and decoded."""
+    c, s = mxfp8_quantize(a)
+    return mxfp8_dequantize(c, s)
+
+
+def moe_mx_scaled(dims, x, idx, w, get_expert, q=mxfp8_round) -> np.ndarray:
+    """Top-k SwiGLU experts whose products take block-scaled operands on both
+    sides: the token's x enters the gate/up product as q(x) and each expert's
+    activation enters the down product as q(act); get_expert(e) gives the
+    (decoded) block-scaled weights (w13 [2F][D], w2 [D][F]). Otherwise the
+    bf16 MoE: gate and up rounded to bf16, act = bf16(silu(gate) * up), the
+    weighted combine summed wide and rounded once. q = identity gives that
+    MoE on the same weights."""
+    from .layer import as_f64, bf, silu
+    x = as_f64(x)
+    T = x.shape[0]
+    idx = np.asarray(idx)
+    xq = q(x)
+    acc = np.zeros((T, dims.D), F64)
+    for e in np.unique(idx):
+        w13, w2 = get_expert(int(e))
+        tt, kk = np.nonzero(idx == e)
+        u = bf(xq[tt] @ as_f64(w13).T)
+        act = bf(silu(u[:, :dims.F]) * u[:, dims.F:])
+        y = q(act) @ as_f64(w2).T
+        for r, (t, k) in enumerate(zip(tt, kk)):
+            acc[t] += float(w[t, k]) * y[r]
+    return bf(acc)

@@ -154,3 +154,62 @@ def test_mxfp4_error_bound_and_saturation():
     p, s = mx.mxfp4_quantize(block)
     assert int(s[0]) == 127 and (p[0] & 15) == 7
     assert mx.mxfp4_dequantize(p, s)[0] == 6.0
+
+
+# ---- block-scaled operands on both sides (scaled matrix-core experts) --------
+def _tiny_moe_case(seed=5):
+    import synth
+    from oracle import layer as L
+    dims = synth.with_dims(synth.config(0), F=64, E=4, topk=2, n_group=1, topk_group=1).dims
+    g = np.random.default_rng(seed)
+    T = 5
+    x = L.bf(g.standard_normal((T, dims.D)))
+    idx = np.stack([g.choice(dims.E, dims.topk, replace=False) for _ in range(T)])
+    w = g.uniform(0.1, 0.9, (T, dims.topk)).astype(np.float32)
+    ex = {e: (L.bf(g.standard_normal((2 * dims.F, dims.D)) * 0.05),
+              L.bf(g.standard_normal((dims.D, dims.F)) * 0.05)) for e in range(dims.E)}
+    return dims, x, idx, w, ex
+
+
+def test_mxfp8_round_is_a_projection():
+    """Quantising twice gives the first result; representable blocks are
+    fixed points; the error stays within half an e4m3 step of the block."""
+    g = np.random.default_rng(1)
+    a = g.standard_normal((7, 96)) * np.exp(g.uniform(-8, 8, (7, 1)))
+    r = mx.mxfp8_round(a)
+    assert np.array_equal(mx.mxfp8_round(r), r)
+    s = mx.shared_exponents(a)[..., None]
+    X = np.ldexp(1.0, s)                          # block scale
+    half = np.ldexp(1.0, s + 8 - 3 - 1)          # half the e4m3 spacing of the top binade
+    a3, r3 = a.reshape(7, 3, 32), r.reshape(7, 3, 32)
+    inside = np.abs(a3) <= 448 * X
+    assert np.all(np.abs(r3 - a3)[inside] <= (half * np.ones_like(a3))[inside] * 1.0000001)
+    assert np.array_equal(r3[~inside], (np.sign(a3) * 448 * X)[~inside])   # saturation
+
+
+def test_moe_mx_scaled_reduces_to_the_bf16_moe():
+    """With an identity quantiser the scaled MoE is the pinned bf16 MoE on the
+    same weights, bit for bit: the two differ only in the quantiser calls."""
+    from oracle import layer as L
+    dims, x, idx, w, ex = _tiny_moe_case()
+    ident = mx.moe_mx_scaled(dims, x, idx, w, lambda e: ex[e], q=lambda a: np.asarray(a))
+    assert np.array_equal(ident, L.moe(dims, x, idx, w, lambda e: ex[e]))
+
+
+def test_moe_mx_scaled_quantises_both_product_inputs():
+    """The quantiser sees the token rows (x, [T][D]) once and each expert's
+    activation rows ([rows][F]) before its down product, and nothing else;
+    quantising x beforehand changes nothing (the first call is a projection)."""
+    dims, x, idx, w, ex = _tiny_moe_case(7)
+    seen = []
+
+    def spy(a):
+        seen.append(np.asarray(a).shape)
+        return mx.mxfp8_round(a)
+    y = mx.moe_mx_scaled(dims, x, idx, w, lambda e: ex[e], q=spy)
+    n_e = [int(np.sum(idx == e)) for e in np.unique(idx)]
+    assert seen == [x.shape] + [(n, dims.F) for n in n_e]
+    assert np.array_equal(mx.moe_mx_scaled(dims, mx.mxfp8_round(x), idx, w, lambda e: ex[e]), y)
+    # and it matters: the scaled result differs from the unscaled one
+    from oracle import layer as L
+    assert not np.array_equal(y, L.moe(dims, x, idx, w, lambda e: ex[e]))

@@ -50,6 +50,8 @@ def parse():
                     help="skip the NoPE fp8 decode leg at a 2^20-token context")
     ap.add_argument("--no-head", action="store_true",
                     help="skip the output head (logit soft cap) leg")
+    ap.add_argument("--no-mx-prefill", action="store_true",
+                    help="skip the prefill MoE leg on block-scaled operands")
     ap.add_argument("--no-stack", action="store_true",
                     help="skip the 52-layer decode step at a 2^20-token context")
     ap.add_argument("--stack-steps", type=int, default=10,
@@ -70,6 +72,9 @@ def parse():
     ap.add_argument("--counters-prefill", action="store_true",
                     help="only run one pass of each prefill layer eagerly (for rocprofv3 "
                          "--pmc passes)")
+    ap.add_argument("--counters-mx", choices=["bf16", "mxfp8", "mxfp4"],
+                    help="only run the prefill MoE once with the given expert format "
+                         "(for rocprofv3 --pmc passes)")
     return ap.parse_args()
 
 
@@ -150,6 +155,9 @@ def main():
 
     if a.counters_prefill:
         prefill_leg(a, counters=True)
+        return
+    if a.counters_mx:
+        mx_prefill_leg(a, only=a.counters_mx)
         return
     swa = decode_leg(a, 1)
     if a.counters or a.counters_step:
@@ -276,6 +284,9 @@ def main():
         torch.cuda.empty_cache()
     if not a.no_prefill:
         out["prefill"] = prefill_leg(a, cpu=cpu if not a.no_cpu_baseline else None)
+        torch.cuda.empty_cache()
+    if not a.no_mx_prefill:
+        out["prefill_moe_mx"] = mx_prefill_leg(a)
     if not a.no_cpu_baseline:
         out["cpu_baseline"] = cpu_summary(cpu)
     print(json.dumps(out))
@@ -943,6 +954,92 @@ def prefill_leg(a, cpu=None, counters=False):
         del t, w13, w2, K, V, ws_f, ws_q, ws_a
         torch.cuda.empty_cache()
     res["workload"] = "8 sequences x 2048 new tokens after 100,000 prior tokens each, bf16 cache"
+    return res
+
+
+FP8_PEAK_TFLOPS = 5000.0    # MI355X dense fp8 matrix peak (published)
+
+
+def mx_prefill_leg(a, only=None):
+    """The routed-expert FFN of a prefill chunk alone (8 x 2048 tokens, the
+    router's own top-8 choice over all 256 experts of random weights): the
+    bf16 grouped GEMMs against the block-scaled ones (MXFP8 activations times
+    MXFP8 or MXFP4 weights on the scaled matrix cores). Each variant's
+    algorithmic flops (T * topk * 3 * 2 * D * F) per call, against the bf16
+    peak for bf16 and the fp8 peak for the scaled variants (e2m1 weights with
+    e4m3 activations run at the fp8 rate). only: run one variant once (for
+    rocprofv3 --pmc)."""
+    import numpy as np
+    import torch
+
+    import moe_decoder_layer_amd as B
+    import synth
+    dims = synth.config(1).dims
+    T = 8 * 2048
+    I16 = dict(dtype=torch.int16, device="cuda")
+    U8 = dict(dtype=torch.uint8, device="cuda")
+    t0 = time.time()
+    p = synth.make_params(dims, 0, 4, experts=False, projections=False)
+    w_r = torch.from_numpy(np.ascontiguousarray(p["w_r"])).cuda()
+    b_corr = torch.from_numpy(np.ascontiguousarray(p["b_corr"])).cuda()
+    x = synth.torch_normal_bf16((T, dims.D), 1.0, 0, "mx_prefill_x")
+    idx = torch.empty((T, dims.topk), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, dims.topk), dtype=torch.float32, device="cuda")
+    ws = lambda op: torch.zeros(max(256, B.beam_workspace_size(dims, op, T)), **U8)  # noqa: E731
+    B.beam_router_fp32_grouped_topk(dims, T, x, w_r, b_corr, idx, w, None, ws(B.BEAM_OP_ROUTER))
+    E, F, D = dims.E, dims.F, dims.D
+    w13 = torch.empty((E, 2 * F, D), **I16)
+    w2 = torch.empty((E, D, F), **I16)
+    for e in range(E):
+        synth.torch_normal_bf16((2 * F, D), 0.02, 0, 4, "w13", e, out=w13[e])
+        synth.torch_normal_bf16((D, F), 0.02, 0, 4, "w2", e, out=w2[e])
+    y = torch.empty((T, D), **I16)
+    variants = {}
+    for fmt, wbits in (("mxfp8", 8), ("mxfp4", 4)):
+        if only is not None and only != fmt:
+            continue
+        div = 1 if wbits == 8 else 2
+        c13, s13 = torch.empty((E * 2 * F, D // div), **U8), torch.empty((E * 2 * F, D // 32), **U8)
+        c2, s2 = torch.empty((E * D, F // div), **U8), torch.empty((E * D, F // 32), **U8)
+        getattr(B, f"beam_{fmt}_quantize")(w13, E * 2 * F, D, c13, s13)
+        getattr(B, f"beam_{fmt}_quantize")(w2, E * D, F, c2, s2)
+        wsm = ws(B.BEAM_OP_MOE_MX_SCALED)
+        variants[fmt] = (lambda wb=wbits, c13=c13, s13=s13, c2=c2, s2=s2, wsm=wsm:
+                         B.beam_moe_swiglu_combine_mx_scaled(dims, T, x, idx, w, wb, c13, s13, c2,
+                                                             s2, y, wsm))
+    if only is None or only == "bf16":
+        wsb = ws(B.BEAM_OP_MOE)
+        variants["bf16"] = lambda: B.beam_moe_swiglu_combine(dims, T, x, idx, w, w13, w2, None,
+                                                             None, y, wsb)
+    torch.cuda.synchronize()
+    B.beam_check()
+    log(f"[bench] prefill MoE (block-scaled): set up in {time.time() - t0:.1f}s")
+    flops = T * dims.topk * 3 * 2 * D * F
+    res = {}
+    for name, fn in variants.items():
+        fn()
+        torch.cuda.synchronize()
+        B.beam_check()
+        if only is not None:
+            continue
+        reps = max(3, a.prefill_reps * 2)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        B.beam_check()
+        ms = e0.elapsed_time(e1) / reps
+        tf = flops / (ms * 1e-3) / 1e12
+        peak = MFMA_PEAK_TFLOPS if name == "bf16" else FP8_PEAK_TFLOPS
+        res[name] = {"ms": round(ms, 3), "tflops": round(tf, 1), "peak_tflops": peak,
+                     "frac": round(tf / peak, 4)}
+        log(f"[bench] prefill MoE {name}: {ms:.3f} ms, {tf:.0f} TFLOP/s ({tf / peak:.3f} of peak)")
+    res["algorithmic_flop"] = flops
+    res["workload"] = ("routed experts of 8 x 2048 prefill tokens, top-8 of 256 experts "
+                       "(router on random weights), D 5120, F 2560")
+    del w13, w2, variants
     return res
 
 

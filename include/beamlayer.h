@@ -90,7 +90,8 @@ enum beam_op {
   BEAM_OP_ROUTER = 5,    /* beam_router_fp32_grouped_topk   */
   BEAM_OP_MOE = 6,       /* beam_moe_swiglu_combine         */
   BEAM_OP_DENSE = 7,     /* beam_dense_swiglu (dims->F read as the dense d_ff) */
-  BEAM_OP_ATTN_DECODE_FUSED = 8 /* beam_attn_decode_fused                   */
+  BEAM_OP_ATTN_DECODE_FUSED = 8, /* beam_attn_decode_fused                  */
+  BEAM_OP_MOE_MX_SCALED = 9      /* beam_moe_swiglu_combine_mx_scaled       */
 };
 
 /* Layer shape. D hidden size; Hq/Hkv query/kv heads (Hq % Hkv == 0, group
@@ -364,6 +365,37 @@ int beam_moe_swiglu_combine_mxfp4(const beam_dims* dims, int T, const uint16_t* 
                                   const uint8_t* w13_scales, const uint8_t* w2_codes,
                                   const uint8_t* w2_scales, uint16_t* y, void* ws,
                                   size_t ws_bytes, void* stream);
+
+/* Routed experts of a many-token step on block-scaled operands on both sides
+ * of the products ([MoE]: experts in a 4-bit block format; [Opt]: the
+ * library MoE path quantises the activations and runs two grouped GEMMs),
+ * on gfx950's scaled matrix cores (v_mfma_scale_f32_32x32x64_f8f6f4):
+ *   xq = MXFP8(x)         each token row in blocks of 32 along D (e4m3 codes,
+ *                         one E8M0 scale: floor(log2(amax)) - 8, RNE, saturating
+ *                         at 448; the weights' rule)
+ *   gate, up = bf16(xq . W13_e^T) (fp32 accumulation), act = bf16(silu(gate) * up)
+ *   aq = MXFP8(act)       in blocks of 32 along F
+ *   y = bf16(sum_k w[t][k] * (aq . W2_e^T))
+ * with W13_e, W2_e the decoded block-scaled weights: wbits 8 (MXFP8: codes
+ * w13 [E][2F][D], w2 [E][D][F]) or 4 (MXFP4: codes w13 [E][2F][D/2], w2
+ * [E][D][F/2]); scales w13 [E][2F][D/32], w2 [E][D][F/32] (4-byte aligned),
+ * as beam_mxfp8_quantize / beam_mxfp4_quantize write them. The activation
+ * quantisation makes this a different function from beam_moe_swiglu_combine
+ * on the decoded weights (each product input carries up to half an e4m3 step
+ * of its block). Rows are routed as in beam_moe_swiglu_combine (tile rows
+ * 256; ids outside [0, E) flagged and left out). T >= 1, D and F multiples
+ * of 128, E <= 1024, no shared expert.
+ * ws >= beam_workspace_size(BEAM_OP_MOE_MX_SCALED, T). After the call the
+ * workspace's data area (past its 1 KiB counter block) starts with the staged
+ * operands, each at a 256-byte-aligned offset, for inspection: the routed row
+ * of each (token, slot) pair (int32 [T][topk]), xq's codes [T][D] and scales
+ * [T][D/32], and the activations act (bf16 [T*topk][F], rows in expert order).
+ * Errors: wbits not 8 or 4, sizes as above. */
+int beam_moe_swiglu_combine_mx_scaled(const beam_dims* dims, int T, const uint16_t* x,
+                                      const int32_t* idx, const float* w, int wbits,
+                                      const uint8_t* w13_codes, const uint8_t* w13_scales,
+                                      const uint8_t* w2_codes, const uint8_t* w2_scales,
+                                      uint16_t* y, void* ws, size_t ws_bytes, void* stream);
 
 /* Output head with the logit soft cap (after the layer stack; Beam's
  * architecture notes give logits = 30 * tanh(z / 30)): x [T][D] bf16 (the

@@ -29,7 +29,8 @@ __all__ = [
     "beam_check", "beam_last_error", "beam_version",
     "BEAM_SWA_ROPE", "BEAM_NOPE_SSMAX", "BEAM_KV_BF16", "BEAM_KV_FP8_E4M3",
     "BEAM_OP_QKV", "BEAM_OP_ATTN_SWA", "BEAM_OP_ATTN_NOPE", "BEAM_OP_OUT_GATE",
-    "BEAM_OP_ROUTER", "BEAM_OP_MOE", "BEAM_OP_DENSE", "BEAM_OP_ATTN_DECODE_FUSED", "LIB_PATH",
+    "BEAM_OP_ROUTER", "BEAM_OP_MOE", "BEAM_OP_DENSE", "BEAM_OP_ATTN_DECODE_FUSED",
+    "BEAM_OP_MOE_MX_SCALED", "beam_moe_swiglu_combine_mx_scaled", "LIB_PATH",
     "HEADER_PATH",
 ]
 
@@ -40,7 +41,7 @@ HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "beamlayer.h")
 BEAM_SWA_ROPE, BEAM_NOPE_SSMAX = 0, 1
 BEAM_KV_BF16, BEAM_KV_FP8_E4M3 = 0, 1
 (BEAM_OP_QKV, BEAM_OP_ATTN_SWA, BEAM_OP_ATTN_NOPE, BEAM_OP_OUT_GATE, BEAM_OP_ROUTER,
- BEAM_OP_MOE, BEAM_OP_DENSE, BEAM_OP_ATTN_DECODE_FUSED) = range(1, 9)
+ BEAM_OP_MOE, BEAM_OP_DENSE, BEAM_OP_ATTN_DECODE_FUSED, BEAM_OP_MOE_MX_SCALED) = range(1, 10)
 
 
 class BeamError(RuntimeError):
@@ -110,6 +111,8 @@ def lib():
             "beam_lm_head_softcap": [c_int, c_int, c_int, P, P, c_float, P, P],
             "beam_moe_swiglu_combine_mxfp4": [POINTER(beam_dims), c_int, P, P, P, P, P, P, P, P,
                                               P, c_size_t, P],
+            "beam_moe_swiglu_combine_mx_scaled": [POINTER(beam_dims), c_int, P, P, P, c_int,
+                                                  P, P, P, P, P, P, c_size_t, P],
             "beam_layer_kind": [c_int, c_int, POINTER(c_int), POINTER(c_int)],
             "beam_decode_stack": [POINTER(beam_dims), c_int, c_int, c_int,
                                   POINTER(beam_stack_layer), P, P, P, P, P, P, c_int, P,
@@ -306,6 +309,14 @@ def beam_moe_swiglu_combine_mxfp4(dims, T, x, idx, w, w13_codes, w13_scales, w2_
     d = _d(dims)
     wp, wb = _ws(ws)
     _call("beam_moe_swiglu_combine_mxfp4", ctypes.byref(d), T, _p(x), _p(idx), _p(w),
+          _p(w13_codes), _p(w13_scales), _p(w2_codes), _p(w2_scales), _p(y), wp, wb, _s(stream))
+
+
+def beam_moe_swiglu_combine_mx_scaled(dims, T, x, idx, w, wbits, w13_codes, w13_scales,
+                                      w2_codes, w2_scales, y, ws, stream=None):
+    d = _d(dims)
+    wp, wb = _ws(ws)
+    _call("beam_moe_swiglu_combine_mx_scaled", ctypes.byref(d), T, _p(x), _p(idx), _p(w), wbits,
           _p(w13_codes), _p(w13_scales), _p(w2_codes), _p(w2_scales), _p(y), wp, wb, _s(stream))
 
 

@@ -186,6 +186,32 @@ MoeWs moe_ws_layout(const beam_dims* d, int T) {
   w.total = o;
   return w;
 }
+// Scaled-operand MoE: the pair -> row map, the MXFP8 copy of x, the
+// activations (rows in expert order), then the other routing buffers, the
+// MXFP8 copy of the activations and the per-pair outputs.
+struct MoeMxWs {
+  size_t counts, seg_off, tile_off, perm, inv, xq, xs, act, aq, as, out, total;
+};
+MoeMxWs moe_mx_ws_layout(const beam_dims* d, int T) {
+  const size_t P = (size_t)T * d->topk, E = d->E, D = d->D, F = d->F;
+  MoeMxWs w{};
+  size_t o = 0;
+  // the staged operands first (inv, xq, xs, act), at offsets a caller can
+  // compute from T, topk, D and F alone
+  w.inv = o; o += align256(P * 4);
+  w.xq = o; o += align256((size_t)T * D);
+  w.xs = o; o += align256((size_t)T * D / 32);
+  w.act = o; o += align256(P * F * 2);
+  w.counts = o; o += align256(beam::moe_route_chunks((int)P) * (E + 1) * 4);
+  w.seg_off = o; o += align256((E + 2) * 4);
+  w.tile_off = o; o += align256((E + 2) * 4);
+  w.perm = o; o += align256(P * 4);
+  w.aq = o; o += align256(P * F);
+  w.as = o; o += align256(P * F / 32);
+  w.out = o; o += align256(P * D * 4);
+  w.total = o;
+  return w;
+}
 bool moe_many(const beam_dims* d, int T) {
   return T > beam::kGemvMaxT && d->D % 64 == 0 && d->F % 64 == 0;
 }
@@ -622,6 +648,71 @@ int beam_moe_swiglu_combine_mxfp4(const beam_dims* dims, int T, const uint16_t* 
                 ws_bytes, stream, __func__);
 }
 
+int beam_moe_swiglu_combine_mx_scaled(const beam_dims* dims, int T, const uint16_t* x,
+                                      const int32_t* idx, const float* w, int wbits,
+                                      const uint8_t* w13_codes, const uint8_t* w13_scales,
+                                      const uint8_t* w2_codes, const uint8_t* w2_scales,
+                                      uint16_t* y, void* ws, size_t ws_bytes, void* stream) {
+  REQ(dims);
+  REQ(x);
+  REQ(idx);
+  REQ(w);
+  REQ(w13_codes);
+  REQ(w13_scales);
+  REQ(w2_codes);
+  REQ(w2_scales);
+  REQ(y);
+  REQ(ws);
+  ALN(x);
+  ALN(w13_codes);
+  ALN(w2_codes);
+  ALN(y);
+  ALN(ws);
+  if (((uintptr_t)w13_scales | (uintptr_t)w2_scales) & 3)
+    return fail(BEAM_E_ALIGN, "%s: scales not 4-byte aligned", __func__);
+  SHAPE(T > 0, "%s: T <= 0", __func__);
+  SHAPE(wbits == 8 || wbits == 4, "%s: weight format %d is neither 8 (MXFP8) nor 4 (MXFP4)",
+        __func__, wbits);
+  SHAPE(dims->E > 0 && dims->E <= 1024 && dims->topk > 0 && dims->F > 0,
+        "%s: E must be in [1, 1024], topk and F positive", __func__);
+  UNSUP(dims->D % 128 == 0 && dims->F % 128 == 0,
+        "%s: D and F must be multiples of 128 (the slab depth)", __func__);
+  const size_t need = kCtl + moe_mx_ws_layout(dims, T).total;
+  if (ws_bytes < need)
+    return fail(BEAM_E_WORKSPACE, "%s: workspace %zu < %zu bytes", __func__, ws_bytes, need);
+  int rc = device_ready();
+  if (rc) return rc;
+  const MoeMxWs L = moe_mx_ws_layout(dims, T);
+  char* b = ws_data(ws);
+  int32_t* counts = (int32_t*)(b + L.counts);
+  int32_t* seg_off = (int32_t*)(b + L.seg_off);
+  int32_t* tile_off = (int32_t*)(b + L.tile_off);
+  int32_t* perm = (int32_t*)(b + L.perm);
+  int32_t* inv = (int32_t*)(b + L.inv);
+  uint8_t* xq = (uint8_t*)(b + L.xq);
+  uint8_t* xs = (uint8_t*)(b + L.xs);
+  uint16_t* act = (uint16_t*)(b + L.act);
+  uint8_t* aq = (uint8_t*)(b + L.aq);
+  uint8_t* as = (uint8_t*)(b + L.as);
+  float* out = (float*)(b + L.out);
+  const int E = dims->E, K = dims->topk, D = dims->D, F = dims->F;
+  const int P = T * K;
+  const int BMr = beam::gemm_mx_rows();
+  const int max_tiles = (P + BMr - 1) / BMr + E;
+  const bool b4 = wbits == 4;
+  const hipStream_t st = S_(stream);
+  // route; x -> MXFP8; gate/up with SwiGLU; act -> MXFP8; down; combine
+  if (beam::launch_moe_route(T, K, K, E, idx, BMr, counts, seg_off, tile_off, perm, inv, st) ||
+      beam::launch_mxfp8_quantize(x, (long long)T * D / 32, xq, xs, st) ||
+      beam::launch_gemm_mx_swiglu(F, D, xq, xs, perm, w13_codes, w13_scales, b4, seg_off,
+                                  tile_off, E, max_tiles, act, st) ||
+      beam::launch_mxfp8_quantize(act, (long long)P * F / 32, aq, as, st) ||
+      beam::launch_gemm_mx_f32(D, F, aq, as, w2_codes, w2_scales, b4, seg_off, tile_off, E,
+                               max_tiles, out, st))
+    return launched(-1, __func__);
+  return launched(beam::launch_moe_combine(T, K, K, E, D, out, inv, w, idx, y, st), __func__);
+}
+
 int beam_moe_swiglu_combine(const beam_dims* dims, int T, const uint16_t* x,
                             const int32_t* idx, const float* w, const uint16_t* w13,
                             const uint16_t* w2, const uint16_t* shared_w13,
@@ -819,6 +910,9 @@ size_t beam_workspace_size(const beam_dims* dims, int op, int T, int max_ctx) {
     case BEAM_OP_ROUTER: return ws_router(dims, T);
     case BEAM_OP_MOE: return ws_moe(dims, T);
     case BEAM_OP_DENSE: return ws_dense(T, dims->F, dims->D);
+    case BEAM_OP_MOE_MX_SCALED:
+      if (dims->D <= 0 || dims->F <= 0 || dims->topk <= 0 || dims->E <= 0) return (size_t)-1;
+      return kCtl + moe_mx_ws_layout(dims, T).total;
     case BEAM_OP_ATTN_DECODE_FUSED:
       if (max_ctx <= 0 || dims->Hkv <= 0) return (size_t)-1;
       return ws_attn_fused(dims, T, max_ctx);

@@ -45,6 +45,19 @@ int launch_moe_mxfp8(int T, int D, int F, int E, int topk, const uint8_t* w13c,
                      const uint8_t* w13s, const uint8_t* w2c, const uint8_t* w2s,
                      const int32_t* idx, const float* wts, const uint16_t* X, uint16_t* act,
                      uint16_t* Y, hipStream_t st);
+// block-scaled operands on both sides (MXFP8 activations; MXFP8 or MXFP4
+// weights), grouped expert GEMMs of many-token steps on the scaled matrix
+// cores; K % 128 == 0, tile rows gemm_mx_rows()
+int gemm_mx_rows();
+int launch_gemm_mx_swiglu(int F, int K, const uint8_t* A, const uint8_t* As,
+                          const int32_t* gather, const uint8_t* B, const uint8_t* Bs, bool b4,
+                          const int32_t* seg_off, const int32_t* tile_off, int E,
+                          int max_mtiles, uint16_t* act, hipStream_t st);
+int launch_gemm_mx_f32(int N, int K, const uint8_t* A, const uint8_t* As, const uint8_t* B,
+                       const uint8_t* Bs, bool b4, const int32_t* seg_off,
+                       const int32_t* tile_off, int E, int max_mtiles, float* out,
+                       hipStream_t st);
+
 // block-scaled fp4 (MXFP4) experts, decode steps
 int launch_mxfp4_quantize(const uint16_t* w, long long nblocks, uint8_t* codes, uint8_t* scales,
                           hipStream_t st);

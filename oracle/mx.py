@@ -138,6 +138,46 @@ def mxfp8_round(a) -> np.ndarray:
     return mxfp8_dequantize(c, s)
 
 
+def moe_mx_scaled_act(dims, x, idx, get_expert, q=mxfp8_round, gate_up=False):
+    """The gate/up product of moe_mx_scaled: act[t][k] = bf16(silu(gate) * up)
+    with gate, up = bf16(q(x[t]) . W13_e^T) for e = idx[t][k] (F values per
+    pair; NaN rows for ids outside [0, E)). gate_up: also return gate and up."""
+    from .layer import as_f64, bf, silu
+    x = as_f64(x)
+    idx = np.asarray(idx)
+    T, K = idx.shape
+    xq = q(x)
+    act, gate, up = (np.full((T, K, dims.F), np.nan) for _ in range(3))
+    for e in np.unique(idx):
+        if not 0 <= e < dims.E:
+            continue
+        w13, _ = get_expert(int(e))
+        tt, kk = np.nonzero(idx == e)
+        u = bf(xq[tt] @ as_f64(w13).T)
+        gate[tt, kk], up[tt, kk] = u[:, :dims.F], u[:, dims.F:]
+        act[tt, kk] = bf(silu(u[:, :dims.F]) * u[:, dims.F:])
+    return (act, gate, up) if gate_up else act
+
+
+def moe_mx_scaled_down(dims, act, idx, w, get_expert, q=mxfp8_round) -> np.ndarray:
+    """The down product and combine of moe_mx_scaled from given activations
+    act [T][K][F]: y[t] = bf16(sum_k w[t][k] * (q(act[t][k]) . W2_e^T)) over
+    the slots whose id is in [0, E)."""
+    from .layer import as_f64, bf
+    idx = np.asarray(idx)
+    T, K = idx.shape
+    acc = np.zeros((T, dims.D), F64)
+    for e in np.unique(idx):
+        if not 0 <= e < dims.E:
+            continue
+        _, w2 = get_expert(int(e))
+        tt, kk = np.nonzero(idx == e)
+        y = q(as_f64(act[tt, kk])) @ as_f64(w2).T
+        for r, (t, k) in enumerate(zip(tt, kk)):
+            acc[t] += float(w[t, k]) * y[r]
+    return bf(acc)
+
+
 def moe_mx_scaled(dims, x, idx, w, get_expert, q=mxfp8_round) -> np.ndarray:
     """Top-k SwiGLU experts whose products take block-scaled operands on both
     sides: the token's x enters the gate/up product as q(x) and each expert's
@@ -145,19 +185,7 @@ def moe_mx_scaled(dims, x, idx, w, get_expert, q=mxfp8_round) -> np.ndarray:
     (decoded) block-scaled weights (w13 [2F][D], w2 [D][F]). Otherwise the
     bf16 MoE: gate and up rounded to bf16, act = bf16(silu(gate) * up), the
     weighted combine summed wide and rounded once. q = identity gives that
-    MoE on the same weights."""
-    from .layer import as_f64, bf, silu
-    x = as_f64(x)
-    T = x.shape[0]
-    idx = np.asarray(idx)
-    xq = q(x)
-    acc = np.zeros((T, dims.D), F64)
-    for e in np.unique(idx):
-        w13, w2 = get_expert(int(e))
-        tt, kk = np.nonzero(idx == e)
-        u = bf(xq[tt] @ as_f64(w13).T)
-        act = bf(silu(u[:, :dims.F]) * u[:, dims.F:])
-        y = q(act) @ as_f64(w2).T
-        for r, (t, k) in enumerate(zip(tt, kk)):
-            acc[t] += float(w[t, k]) * y[r]
-    return bf(acc)
+    MoE on the same weights. Slots with ids outside [0, E) contribute
+    nothing."""
+    act = moe_mx_scaled_act(dims, x, idx, get_expert, q)
+    return moe_mx_scaled_down(dims, act, idx, w, get_expert, q)

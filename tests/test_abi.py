@@ -20,7 +20,7 @@ MIS = 0x10002        # misaligned
 
 def test_library_exports_every_declared_symbol():
     names = B.header_functions()
-    assert len(names) == 27
+    assert len(names) == 28
     L = ctypes.CDLL(B.LIB_PATH)
     for n in names:
         assert hasattr(L, n), n
@@ -209,6 +209,32 @@ def test_mx_validation_and_nodev(fmt):
     assert _rc(moe, *args(dims=ctypes.byref(d3))) == -3
     assert _rc(moe, *args(ws=need - 1)) == -5
     assert _rc(moe, *args()) == -7
+
+
+@cpu_only
+def test_mx_scaled_validation_and_nodev():
+    f = "beam_moe_swiglu_combine_mx_scaled"
+    d = _dims(D=256, F=128, E=8, topk=2)
+    by = ctypes.byref(d)
+    T = 300
+    need = B.beam_workspace_size(d, B.BEAM_OP_MOE_MX_SCALED, T)
+    # staged operands, expert-ordered activations, MXFP8 copies, per-pair fp32 outputs
+    P = T * 2
+    assert need >= 1024 + P * 4 + T * 256 * (1 + 1 / 32) + P * 128 * (2 + 1 + 1 / 32) + P * 256 * 4
+
+    def args(T=T, wbits=8, scales=A, ws=need, dims=by, x=A):
+        return [dims, T, x, A, A, wbits, A, scales, A, A, A, A, ws, None]
+    assert _rc(f, *args(dims=None)) == -1
+    assert _rc(f, *args(x=None)) == -1
+    assert _rc(f, *args(x=MIS)) == -4
+    assert _rc(f, *args(scales=A + 2)) == -4
+    assert _rc(f, *args(T=0)) == -2
+    assert _rc(f, *args(wbits=6)) == -2
+    for bad in (dict(D=192), dict(F=192), dict(E=1025)):
+        db = _dims(**{**dict(D=256, F=128, E=8, topk=2), **bad})
+        assert _rc(f, *args(dims=ctypes.byref(db))) in (-2, -3)
+    assert _rc(f, *args(ws=need - 1)) == -5
+    assert _rc(f, *args()) == -7
 
 
 @cpu_only

@@ -132,72 +132,74 @@ int router_splits(int T, int E, int D) {
 
 constexpr int EMAX = 1024;
 
+// Number of the n keys k[0, n) in LDS above `mine`. For even n (k 16-byte
+// aligned) they are read two to a 16-byte vector, up to 16 keys requested
+// before the first comparison, so the reads overlap.
+__device__ __forceinline__ int count_above(const uint64_t* k, int n, uint64_t mine) {
+  int r = 0;
+  if ((n & 1) == 0) {
+    typedef uint64_t u64x2 __attribute__((ext_vector_type(2)));
+    for (int j0 = 0; j0 < n; j0 += 16) {
+      u64x2 v[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        if (j0 + 2 * q < n) v[q] = *reinterpret_cast<const u64x2*>(k + j0 + 2 * q);
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        if (j0 + 2 * q < n) r += (int)(v[q][0] > mine) + (int)(v[q][1] > mine);
+    }
+  } else {
+    for (int j = 0; j < n; ++j) r += (int)(k[j] > mine);
+  }
+  return r;
+}
+
 // Grouped top-k of one token, one thread per expert (E <= blockDim.x).
 // lg: the token's logits; bias: this thread's correction bias (0 when none).
-// LDS scratch: s_b, cand_v, cand_i >= E entries, g1, g2 >= ng, ssel >= K.
+// Each expert's rank key is its biased score made order-preserving as an
+// unsigned high word, over 0xFFFFFFFF - e in the low word: a key is above
+// another exactly when its score is larger, or equal with a lower index (the
+// rank rule), so every rank is a count of larger keys.
+// LDS scratch (16-byte aligned): key, ckey >= E entries, g1, g2 >= ng,
+// ssel >= K, red >= 32.
 // An expert among the overall top K is among the top K of its own group, so
 // the final ranking only runs over each kept group's best min(K, group size).
-__device__ void route_token(const float* lg, float bias, int E, int ng, int tg, int K,
-                            float route_scale, int32_t* idx_t, float* w_t, float* s_b,
-                            float* cand_v, int* cand_i, float* g1, float* g2, float* ssel) {
+__device__ __forceinline__ void route_token(const float* lg, float bias, int E, int ng, int tg,
+                                            int K, float route_scale, int32_t* idx_t, float* w_t,
+                                            uint64_t* key, uint64_t* ckey, float* g1, float* g2,
+                                            float* ssel, int* red) {
   const int e = threadIdx.x;
   const bool act = e < E;
-  const int gs = E / ng;
-  const int kc = min(K, gs);  // candidates per kept group
-  const int nc = tg * kc;     // <= E
-  const int grp = act ? e / gs : 0;
   float sv = 0.f, sb = -INFINITY;
+  uint64_t my = 0;  // below every expert's key
   if (act) {
     sv = 1.0f / (1.0f + expf(-lg[e]));
     sb = sv + bias;
-    s_b[e] = sb;
+    const uint32_t u = __float_as_uint(sb + 0.0f);  // -0 -> +0: equal scores, equal words
+    const uint32_t o = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    my = ((uint64_t)o << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)e);
   }
   if (ng == 1 || tg >= ng) {
-    // Every group kept: the top K of the biased scores, in K rounds of a
-    // workgroup argmax over a key that orders by value, then lower index
-    // (the rank rule below). Keys: the float's bits made order-preserving as
-    // unsigned in the high word, 0xFFFF - e in the low word; a lane without
-    // an expert, or whose expert is taken, holds 0 (below every score).
-    uint32_t khi = 0, klo = 0;
-    if (act) {
-      const uint32_t u = __float_as_uint(sb);
-      khi = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-      klo = 0xFFFFu - (uint32_t)e;
-    }
-    // per-wave winners in cand_i: high words at [0, 16), low words at [16, 32)
-    // (every caller's cand_i holds at least 256 entries; at most 16 waves)
-    int* red_hi = cand_i;
-    int* red_lo = cand_i + 16;
+    // Every group kept: the top K keys, in K rounds of a workgroup argmax;
+    // a lane whose expert is taken drops its key to 0.
+    uint64_t* red64 = reinterpret_cast<uint64_t*>(red);  // one key per wave (<= 16)
     const int nw = (blockDim.x + 63) >> 6, wave = threadIdx.x >> 6;
     for (int r = 0; r < K; ++r) {
-      uint32_t bh = khi, bl = klo;
+      uint64_t b = my;
 #pragma unroll
       for (int o = 32; o > 0; o >>= 1) {
-        const uint32_t oh = __shfl_xor(bh, o, 64), ol = __shfl_xor(bl, o, 64);
-        if (oh > bh || (oh == bh && ol > bl)) {
-          bh = oh;
-          bl = ol;
-        }
+        const uint64_t ob = __shfl_xor(b, o, 64);
+        b = ob > b ? ob : b;
       }
-      if ((threadIdx.x & 63) == 0) {
-        red_hi[wave] = static_cast<int>(bh);
-        red_lo[wave] = static_cast<int>(bl);
-      }
+      if ((threadIdx.x & 63) == 0) red64[wave] = b;
       __syncthreads();
-      bh = static_cast<uint32_t>(red_hi[0]);
-      bl = static_cast<uint32_t>(red_lo[0]);
-      for (int w = 1; w < nw; ++w) {
-        const uint32_t oh = static_cast<uint32_t>(red_hi[w]), ol = static_cast<uint32_t>(red_lo[w]);
-        if (oh > bh || (oh == bh && ol > bl)) {
-          bh = oh;
-          bl = ol;
-        }
-      }
-      __syncthreads();  // red_* are rewritten next round
-      if (act && e == (int)(0xFFFFu - bl)) {
+      b = red64[0];
+      for (int w = 1; w < nw; ++w) b = red64[w] > b ? red64[w] : b;
+      __syncthreads();  // red is rewritten next round
+      if (act && b == my) {
         idx_t[r] = e;
         ssel[r] = sv;
-        khi = klo = 0;
+        my = 0;
       }
     }
     __syncthreads();
@@ -209,49 +211,40 @@ __device__ void route_token(const float* lg, float bias, int E, int ng, int tg, 
     __syncthreads();  // the LDS arrays are reused for the next token
     return;
   }
-  if (e < nc) cand_v[e] = -INFINITY;  // slots a group cannot fill stay empty
+  const int gs = E / ng;
+  const int kc = min(K, gs);  // candidates per kept group
+  const int nc = tg * kc;     // <= E
+  const int grp = act ? e / gs : 0;
+  if (act) key[e] = my;
+  if (e < nc) ckey[e] = 0;  // slots a group cannot fill stay empty (below every key)
   __syncthreads();
   // rank inside the group; the two best give the group's score
   int rin = 0;
   if (act) {
-    const int g0 = grp * gs;
-#pragma unroll 8
-    for (int m = g0; m < g0 + gs; ++m) {
-      const float v = s_b[m];
-      rin += (v > sb) || (v == sb && m < e);
-    }
+    rin = count_above(key + grp * gs, gs, my);
     if (rin == 0) g1[grp] = sb;
     if (rin == 1) g2[grp] = sb;
   }
   __syncthreads();
   bool cand = false;  // in a kept group and among its best kc
   if (act && rin < kc) {
-    const float my = (gs >= 2) ? g1[grp] + g2[grp] : g1[grp];
+    const float mine = (gs >= 2) ? g1[grp] + g2[grp] : g1[grp];
     int rg = 0;
     for (int h = 0; h < ng; ++h) {
       const float sc = (gs >= 2) ? g1[h] + g2[h] : g1[h];
-      rg += (sc > my) || (sc == my && h < grp);
+      rg += (int)((sc > mine) | ((sc == mine) & (h < grp)));
     }
     cand = rg < tg;
-    if (cand) {
-      cand_v[rg * kc + rin] = sb;
-      cand_i[rg * kc + rin] = e;
-    }
+    if (cand) ckey[rg * kc + rin] = my;
   }
   __syncthreads();
-  // final rank among the candidates (same order: value, then lower index);
-  // empty slots hold -inf and never beat a candidate
-  int r = 0;
+  // final rank among the candidates
   if (cand) {
-#pragma unroll 8
-    for (int c = 0; c < nc; ++c) {
-      const float v = cand_v[c];
-      r += (v > sb) || (v == sb && cand_i[c] < e);
+    const int r = count_above(ckey, nc, my);
+    if (r < K) {
+      idx_t[r] = e;
+      ssel[r] = sv;
     }
-  }
-  if (cand && r < K) {
-    idx_t[r] = e;
-    ssel[r] = sv;
   }
   __syncthreads();
   if (e < K) {
@@ -268,9 +261,9 @@ __global__ __launch_bounds__(EMAX) void router_topk_kernel(
     float* __restrict__ logits, const float* __restrict__ part, int nsplit,
     const float* __restrict__ bcorr, int T, int E, int ng, int tg, int K, float route_scale,
     int32_t* __restrict__ idx, float* __restrict__ wout) {
-  __shared__ float s_b[EMAX], cand_v[EMAX];
-  __shared__ int cand_i[EMAX];
-  __shared__ float g1[64], g2[64], ssel[32];
+  __shared__ __align__(16) uint64_t key[EMAX], ckey[EMAX];
+  __shared__ __align__(16) float g1[64], g2[64], ssel[32];
+  __shared__ __align__(16) int sred[32];
   const int t = blockIdx.x;
   if (part != nullptr && (int)threadIdx.x < E) {
     // eight partials requested at a time, added in split order
@@ -288,7 +281,7 @@ __global__ __launch_bounds__(EMAX) void router_topk_kernel(
   }
   const float bias = (bcorr && (int)threadIdx.x < E) ? bcorr[threadIdx.x] : 0.f;
   route_token(logits + (size_t)t * E, bias, E, ng, tg, K, route_scale, idx + (size_t)t * K,
-              wout + (size_t)t * K, s_b, cand_v, cand_i, g1, g2, ssel);
+              wout + (size_t)t * K, key, ckey, g1, g2, ssel, sred);
 }
 
 // Few tokens: wave w of workgroup b computes the logits of expert 4b + w for
@@ -301,9 +294,9 @@ __global__ __launch_bounds__(RT) void router_decode_kernel(
     const uint16_t* __restrict__ X, const float* __restrict__ Wr, int T, int E, int D,
     float* logits, const float* __restrict__ bcorr, int ng, int tg, int K, float route_scale,
     int32_t* __restrict__ idx, float* __restrict__ wout, unsigned* ctr) {
-  __shared__ float s_b[RT], cand_v[RT];
-  __shared__ int cand_i[RT];
-  __shared__ float g1[64], g2[64], ssel[32];
+  __shared__ __align__(16) uint64_t key[RT], ckey[RT];
+  __shared__ __align__(16) float g1[64], g2[64], ssel[32];
+  __shared__ __align__(16) int sred[32];
   __shared__ int s_last;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   // the selection needs the bias in whichever workgroup ends up last
@@ -350,7 +343,7 @@ __global__ __launch_bounds__(RT) void router_decode_kernel(
   if (!last_arrival(ctr, gridDim.x, &s_last)) return;
   for (int t = 0; t < T; ++t)
     route_token(logits + (size_t)t * E, bias, E, ng, tg, K, route_scale, idx + (size_t)t * K,
-                wout + (size_t)t * K, s_b, cand_v, cand_i, g1, g2, ssel);
+                wout + (size_t)t * K, key, ckey, g1, g2, ssel, sred);
 }
 
 // One token: the attention-side sublayer boundary as the router's prologue.
@@ -369,9 +362,9 @@ __global__ __launch_bounds__(RT) void boundary_router_kernel(
   constexpr int CPT = 4;  // D <= RT * CPT * 8
   extern __shared__ __align__(16) uint16_t xs[];  // the token's pre-normed row
   __shared__ float red[RT / 64];
-  __shared__ float s_b[RT], cand_v[RT];
-  __shared__ int cand_i[RT];
-  __shared__ float g1[64], g2[64], ssel[32];
+  __shared__ __align__(16) uint64_t key[RT], ckey[RT];
+  __shared__ __align__(16) float g1[64], g2[64], ssel[32];
+  __shared__ __align__(16) int sred[32];
   __shared__ int s_last;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int e = blockIdx.x * 4 + wave;
@@ -393,16 +386,20 @@ __global__ __launch_bounds__(RT) void boundary_router_kernel(
     if (c < nc8) *reinterpret_cast<uint4*>(xs + c * 8) = xo[i];
   }
   __syncthreads();
+  // every x chunk is read before the first product (chunks past the row read
+  // the last one and are left out), so no branch waits on its own read
+  uint2 xv[MAXC];
+#pragma unroll
+  for (int i = 0; i < MAXC; ++i)
+    xv[i] = *reinterpret_cast<const uint2*>(xs + min(lane + 64 * i, nc - 1) * 4);
   float a = 0.f;
 #pragma unroll
   for (int i = 0; i < MAXC; ++i) {
-    const int c = lane + 64 * i;
-    if (c < nc) {
-      const uint2 xv = *reinterpret_cast<const uint2*>(xs + c * 4);
-      a = __builtin_fmaf(bf_lo(xv.x), wv[i][0], a);
-      a = __builtin_fmaf(bf_hi(xv.x), wv[i][1], a);
-      a = __builtin_fmaf(bf_lo(xv.y), wv[i][2], a);
-      a = __builtin_fmaf(bf_hi(xv.y), wv[i][3], a);
+    if (lane + 64 * i < nc) {
+      a = __builtin_fmaf(bf_lo(xv[i].x), wv[i][0], a);
+      a = __builtin_fmaf(bf_hi(xv[i].x), wv[i][1], a);
+      a = __builtin_fmaf(bf_lo(xv[i].y), wv[i][2], a);
+      a = __builtin_fmaf(bf_hi(xv[i].y), wv[i][3], a);
     }
   }
   const float v = wave_sum(a);
@@ -416,8 +413,7 @@ __global__ __launch_bounds__(RT) void boundary_router_kernel(
       *reinterpret_cast<uint4*>(x_out + c * 8) = xo[i];
     }
   }
-  route_token(logits, bias, E, ng, tg, K, route_scale, idx, wout, s_b, cand_v, cand_i, g1, g2,
-              ssel);
+  route_token(logits, bias, E, ng, tg, K, route_scale, idx, wout, key, ckey, g1, g2, ssel, sred);
 }
 
 bool boundary_router_fused(int T, int E, int D) {

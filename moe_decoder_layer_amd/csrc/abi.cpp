@@ -133,11 +133,12 @@ size_t ws_attn(const beam_dims* d, int swa, int T, int max_ctx) {
   return kCtl + align256((size_t)T * d->Hq * nch * (d->d + 4) * 4);
 }
 // One-token fused decode attention: [counters][raw q|k|v][gate][split-K
-// records], the records sized for the NoPE (full-context) span, which bounds
-// the sliding-window one.
+// records][normed q, for the long-context plan that runs the q/k epilogue in
+// its own kernel], the records sized for the NoPE (full-context) span, which
+// bounds the sliding-window one.
 size_t ws_attn_fused(const beam_dims* d, int T, int max_ctx) {
   return ws_attn(d, 0, T, max_ctx) + ws_qkv_payload(d, T) +
-         align256((size_t)T * d->G * 2);
+         align256((size_t)T * d->G * 2) + align256((size_t)T * d->Hq * d->d * 2);
 }
 size_t ws_out_gate_payload(const beam_dims* d, int T) {
   return align256((size_t)T * d->Hq * d->d * 2);
@@ -448,15 +449,32 @@ int beam_attn_decode_fused(const beam_dims* dims, int T, const uint16_t* x,
   if (beam::launch_gemv_qkvg(T, Nqkv + dims->G, dims->D, Nqkv, w_qkvg, x, qkv, gbuf, S_(stream)))
     return launched(-1, __func__);
   const int fp8 = kv->dtype == BEAM_KV_FP8_E4M3;
-  beam::AttnFuse fz{qkv, w_qnorm, w_knorm, rope_cs, dims->eps, swa ? 0 : 1,
-                    fp8 ? kv->k_scale : 1.f, fp8 ? kv->v_scale : 1.f,
+  const float ks = fp8 ? kv->k_scale : 1.f, vs = fp8 ? kv->v_scale : 1.f;
+  const int span = attn_span(dims, swa, max_pos + 1);
+  beam::AttnFuse fz{qkv, w_qnorm, w_knorm, rope_cs, dims->eps, swa ? 0 : 1, ks, vs,
                     dims->G > 0 ? gbuf : nullptr, dims->G > 0 ? b_gate : nullptr, q_out};
+  // A long fp8 context streams through thousands of split-K workgroups with a
+  // separate merge; fused, each of them would first form q from the raw
+  // projection, a start-up repeated for every round of resident workgroups.
+  // There the q/k epilogue (with the cache write) runs once in its own kernel
+  // and only the gate stays fused, into the merge.
+  int tpw, nch;
+  beam::attn_plan(T, dims->Hkv, span, &tpw, &nch);
+  const uint16_t* q_in = nullptr;
+  if (fp8 && nch > 1 && !beam::attn_fused_merge(T, dims->Hkv, nch)) {
+    uint16_t* qn = q_out ? q_out
+                         : (uint16_t*)((char*)part + (ws_attn(dims, 0, T, max_pos + 1) - kCtl));
+    if (beam::launch_qk_epilogue(T, dims->Hq, dims->Hkv, dims->d, qkv, w_qnorm, w_knorm, pos,
+                                 seq, swa ? 0 : 1, rope_cs, qn, kv->k, kv->v, fp8, ks, vs, kv->S,
+                                 kv->Lmax, kv_npos(kv), dims->eps, S_(stream)))
+      return launched(-1, __func__);
+    q_in = qn;
+    fz.qkv = nullptr;
+  }
   return launched(beam::launch_attn_decode(T, dims->Hq, dims->Hkv, dims->d, swa, dims->window,
-                                           fp8, nullptr, pos, seq, kv->k, kv->v,
-                                           fp8 ? kv->k_scale : 1.f, fp8 ? kv->v_scale : 1.f,
-                                           kv->S, kv->Lmax, kv_npos(kv), sink, z_out,
-                                           attn_span(dims, swa, max_pos + 1), part, ws_ctl(ws),
-                                           S_(stream), &fz),
+                                           fp8, q_in, pos, seq, kv->k, kv->v, ks, vs, kv->S,
+                                           kv->Lmax, kv_npos(kv), sink, z_out, span, part,
+                                           ws_ctl(ws), S_(stream), &fz),
                   __func__);
 }
 

@@ -85,7 +85,8 @@ constexpr int kAttnFusedMergeMax = 8;   // chunks the last workgroup still merge
 // epilogue (per-head q/k norm, RoPE or SSMax, the KV write) runs inside the
 // attention kernel on the raw q|k|v rows, and the output gate at its merge.
 struct AttnFuse {
-  const uint16_t* qkv;    // raw projection [T][(Hq + 2 Hkv) * d]
+  const uint16_t* qkv;    // raw projection [T][(Hq + 2 Hkv) * d], or null when q is given
+                          // (then only the gate below is fused, into a separate merge)
   const uint16_t* wq;     // q / k norm gains [d]
   const uint16_t* wk;
   const float* rope;      // RoPE table [Lmax][d] (mode 0), else unused

@@ -761,10 +761,14 @@ int launch_attn_decode(int T, int Hq, int Hkv, int hd, int swa, int window, int 
   uint16_t* od = (nch == 1 || fused) ? o : nullptr;
   unsigned* cp = fused ? ctr : nullptr;
   const AttnFuse fz = fuse ? *fuse : AttnFuse{};
+  // q epilogue and cache write fused into the attention kernel, or (qkv null)
+  // only the gate, applied by the separate merge
+  const bool fuse_qk = fuse != nullptr && fuse->qkv != nullptr;
+  if (fuse != nullptr && !fuse_qk && od != nullptr) return -1;
 #define ARGS q, pos, seq, kc, vc, S, Lmax, npos, Hq, Hkv, window, tpw, score_scale, nch, part, od, sink, vsc, cp, fz
 #define PART(HD_, F8, SW)                                                                     \
   do {                                                                                        \
-    if (fuse)                                                                                 \
+    if (fuse_qk)                                                                              \
       hipLaunchKernelGGL((attn_decode_partial_kernel<HD_, F8, SW, 4, 16, true>), grid,        \
                          dim3(256), 0, st, ARGS);                                             \
     else                                                                                      \
@@ -773,7 +777,7 @@ int launch_attn_decode(int T, int Hq, int Hkv, int hd, int swa, int window, int 
   } while (0)
 #define STREAM(HD_, SW)                                                                       \
   do {                                                                                        \
-    if (fuse)                                                                                 \
+    if (fuse_qk)                                                                              \
       hipLaunchKernelGGL((attn_decode_fp8_stream_kernel<HD_, SW, true>), grid, dim3(256), 0,  \
                          st, ARGS);                                                           \
     else                                                                                      \

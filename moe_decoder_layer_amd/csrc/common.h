@@ -119,6 +119,12 @@ __device__ __forceinline__ void load_lds16(const void* g, void* lds) {
   __builtin_amdgcn_global_load_lds(g, lds, 16, 0, 0);
 #endif
 }
+// The same with 4 bytes per lane (64 x 4 B written contiguously).
+__device__ __forceinline__ void load_lds4(const void* g, void* lds) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_global_load_lds(g, lds, 4, 0, 0);
+#endif
+}
 
 // ---- last-arriver election ---------------------------------------------------
 // Workgroups that each publish partial results and then need one of them to

@@ -21,9 +21,12 @@
 // the current one is multiplied out. A rows and e4m3 B rows are 128 bytes per
 // slab (16-byte chunk c of row r at slot c ^ ((r >> 1) & 7)), e2m1 B rows 64
 // bytes (slot c ^ ((r >> 2) & 3)): the 16-byte reads of 16 consecutive rows
-// hit 16 distinct slots of the 64 banks. Each lane fetches its rows' and
-// columns' scale words (four blocks of a slab in one 32-bit word) from global
-// memory a slab ahead.
+// hit 16 distinct slots of the 64 banks. The scale words (four K-blocks of a
+// row per slab in one 32-bit word) travel with the slabs: each wave loads the
+// words of 64 A or B rows straight into LDS, so every row's words are fetched
+// once per workgroup, and the lanes read theirs from LDS. When K is a multiple
+// of 512 a row's 16 bytes of four consecutive slabs come in one load, with
+// the first of those slabs; otherwise each slab brings its own word.
 #include <type_traits>
 
 #include "common.h"
@@ -70,6 +73,12 @@ __global__ __launch_bounds__(XWAVES * 64) void gemm_mx_kernel(MxGemmArgs g) {
   extern __shared__ __align__(16) uint8_t lds8[];
   auto Asl = [&](int buf) { return lds8 + buf * (XBM * XBK); };
   auto Bsl = [&](int buf) { return lds8 + 2 * XBM * XBK + buf * (XBN * BROW); };
+  // scale words, A rows [0, 256) then B rows [256, 512): per buffer the four
+  // slabs of a group ([row][4] words, g4) or one slab ([row] words)
+  auto Ssl = [&](int buf) {
+    return reinterpret_cast<uint32_t*>(lds8 + 2 * XBM * XBK + 2 * XBN * BROW) +
+           buf * 4 * (XBM + XBN);
+  };
 
   // ---- workgroup -> tile: XCD-contiguous, expert by expert ---------------------
   int tm, tn;
@@ -144,7 +153,23 @@ __global__ __launch_bounds__(XWAVES * 64) void gemm_mx_kernel(MxGemmArgs g) {
       b_off[i] = (uint32_t)brow_of(r) * (uint32_t)K + (uint32_t)(sw8(r, lane & 7) * 16);
     }
   }
+  // scale words: wave w < 4 loads those of A rows 64 w + lane, wave w >= 4
+  // those of B rows 64 (w - 4) + lane (row offsets in bytes, < 2^32)
+  const uint8_t* s_src;
+  uint32_t s_off;
+  if (wave < 4) {
+    s_src = g.As;
+    s_off = (uint32_t)arow_of(64 * wave + lane) * (uint32_t)ksc;
+  } else {
+    s_src = Bsc;
+    s_off = (uint32_t)brow_of(64 * (wave - 4) + lane) * (uint32_t)ksc;
+  }
+  const bool g4 = (ksc & 15) == 0;
   auto gload = [&](int kt, int buf) {
+    if (!g4)
+      load_lds4(s_src + s_off + (uint32_t)kt * 4, Ssl(buf) + 64 * wave);
+    else if ((kt & 3) == 0)  // this group's buffer was last read four slabs ago
+      load_lds16(s_src + s_off + (uint32_t)kt * 4, Ssl((kt >> 2) & 1) + 4 * 64 * wave);
 #pragma unroll
     for (int i = 0; i < NA; ++i)
       if (wave * RPW + i * 8 < mrows)  // rows past the segment feed no stored output
@@ -163,21 +188,7 @@ __global__ __launch_bounds__(XWAVES * 64) void gemm_mx_kernel(MxGemmArgs g) {
   const int wm = wave / WCOLS, wn = wave % WCOLS;
   const int band = mrows - wm * 128;  // rows of this wave's 128-row band that exist
   const int lr = lane & 31, lh = lane >> 5;
-  // scale words: the lane's rows (A) and columns (B), four K-blocks per slab
-  uint32_t as_off[MI], bs_off[TJ];
-#pragma unroll
-  for (int i = 0; i < MI; ++i) as_off[i] = (uint32_t)arow_of(wm * 128 + 32 * i + lr) * ksc;
-#pragma unroll
-  for (int j = 0; j < TJ; ++j) bs_off[j] = (uint32_t)brow_of(wn * WN + 32 * j + lr) * ksc;
-  uint32_t sa[MI], sb[TJ], sa_n[MI], sb_n[TJ];
-  auto sload = [&](int kt, uint32_t (&da)[MI], uint32_t (&db)[TJ]) {
-#pragma unroll
-    for (int i = 0; i < MI; ++i)
-      da[i] = *reinterpret_cast<const uint32_t*>(g.As + as_off[i] + (uint32_t)kt * 4);
-#pragma unroll
-    for (int j = 0; j < TJ; ++j)
-      db[j] = *reinterpret_cast<const uint32_t*>(Bsc + bs_off[j] + (uint32_t)kt * 4);
-  };
+  uint32_t sa[MI], sb[TJ];  // the lane's rows' (A) and columns' (B) scale words
 
   f32x16 acc[MI][TJ];
 #pragma unroll
@@ -187,7 +198,6 @@ __global__ __launch_bounds__(XWAVES * 64) void gemm_mx_kernel(MxGemmArgs g) {
 
   const int KT = K / XBK;
   gload(0, 0);
-  sload(0, sa, sb);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   auto kloop = [&](auto skip_tag) {
@@ -195,9 +205,14 @@ __global__ __launch_bounds__(XWAVES * 64) void gemm_mx_kernel(MxGemmArgs g) {
     for (int kt = 0; kt < KT; ++kt) {
       const int cur = kt & 1;
       // the other buffer was last read in step kt - 1, which every wave has left
-      if (kt + 1 < KT) {
-        gload(kt + 1, cur ^ 1);
-        sload(kt + 1, sa_n, sb_n);
+      if (kt + 1 < KT) gload(kt + 1, cur ^ 1);
+      {
+        const uint32_t* S = g4 ? Ssl((kt >> 2) & 1) + (kt & 3) : Ssl(cur);
+        const int rs = g4 ? 4 : 1;  // words per row
+#pragma unroll
+        for (int i = 0; i < MI; ++i) sa[i] = S[(wm * 128 + 32 * i + lr) * rs];
+#pragma unroll
+        for (int j = 0; j < TJ; ++j) sb[j] = S[(XBM + wn * WN + 32 * j + lr) * rs];
       }
       const uint8_t* Ab = Asl(cur) + (wm * 128) * XBK;
       const uint8_t* Bb = Bsl(cur) + (wn * WN) * BROW;
@@ -237,10 +252,6 @@ __global__ __launch_bounds__(XWAVES * 64) void gemm_mx_kernel(MxGemmArgs g) {
       }
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's loads of step kt + 1
       __syncthreads();
-#pragma unroll
-      for (int i = 0; i < MI; ++i) sa[i] = sa_n[i];
-#pragma unroll
-      for (int j = 0; j < TJ; ++j) sb[j] = sb_n[j];
     }
   };
   if (band < MI * 32) kloop(std::integral_constant<bool, true>{});
@@ -277,7 +288,8 @@ __global__ __launch_bounds__(XWAVES * 64) void gemm_mx_kernel(MxGemmArgs g) {
 }
 
 static size_t mx_lds_bytes(bool b4) {
-  return (size_t)2 * XBM * XBK + (size_t)2 * XBN * (b4 ? XBK / 2 : XBK);
+  return (size_t)2 * XBM * XBK + (size_t)2 * XBN * (b4 ? XBK / 2 : XBK) +
+         (size_t)2 * 4 * (XBM + XBN) * 4;
 }
 
 template <int EPI, bool B4>

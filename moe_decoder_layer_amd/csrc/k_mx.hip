@@ -272,9 +272,25 @@ __global__ __launch_bounds__(MT) void mxfp4_quantize_kernel(const uint16_t* __re
   scales[i] = (uint8_t)(s + 127);
 }
 
-// Gate/up rows, MXFP4: as expert_w13_swiglu_mx_kernel with 8-byte chunks of
-// 16 codes (half a scaled block: chunk c of a row has scale byte c / 2); wave
-// w takes rows f0 = NR * (4 * blockIdx.x + w) .. + NR - 1.
+// MXFP4 rows are read in 16-byte chunks of 32 codes: exactly one scaled
+// block, so chunk c of a row has scale byte c, and one wave instruction
+// covers 1 KiB of codes. A lane's chunk meets 32 activations (64 bytes); in
+// LDS the four 16-byte pieces q of activation chunk c sit at slot
+// 4 c + (q ^ ((c >> 2) & 3)), so the 16 lanes served per LDS cycle (chunks
+// c .. c + 15, one piece each) hit 16 distinct slots of the 64 banks.
+__device__ __forceinline__ int mx4_xslot(int c, int q) { return 4 * c + (q ^ ((c >> 2) & 3)); }
+
+__device__ __forceinline__ float mx4_chunk_dot(uint4 w, const uint4 (&x)[4], float acc) {
+  acc = dot8_bf16_d2(e2m1x8_bits(w.x), x[0], acc);
+  acc = dot8_bf16_d2(e2m1x8_bits(w.y), x[1], acc);
+  acc = dot8_bf16_d2(e2m1x8_bits(w.z), x[2], acc);
+  return dot8_bf16_d2(e2m1x8_bits(w.w), x[3], acc);
+}
+
+// Gate/up rows, MXFP4, with SwiGLU: wave w takes rows
+// f0 = NR * (4 * blockIdx.x + w) .. + NR - 1 of the expert of slot s; every
+// code and scale load of the wave is in flight before the activation is
+// staged.
 template <int NB, int NR>
 __global__ __launch_bounds__(MT) void expert_w13_swiglu_mx4_kernel(
     const uint8_t* __restrict__ w13c, const uint8_t* __restrict__ w13s,
@@ -291,59 +307,57 @@ __global__ __launch_bounds__(MT) void expert_w13_swiglu_mx4_kernel(
     if (lane < NR && f0 + lane < F) act[(size_t)s * F + f0 + lane] = 0;
     return;
   }
-  const int nc = D >> 4, nb = D >> 5;  // 16-code chunks and 32-code blocks of a row
-  const size_t rb = (size_t)D >> 1;    // bytes of a row
-  uint2 gw[NR][NB], uw[NR][NB];
+  const int nch = D >> 5;            // 32-code chunks (scaled blocks) of a row
+  const size_t rb = (size_t)D >> 1;  // bytes of a row
+  uint4 gw[NR][NB], uw[NR][NB];
   uint32_t gsc[NR][NB], usc[NR][NB];
 #pragma unroll
   for (int r = 0; r < NR; ++r) {
     const size_t grow = (size_t)e * 2 * F + min(f0 + r, F - 1);
     const uint8_t* gc = w13c + grow * rb;
     const uint8_t* uc = gc + (size_t)F * rb;
-    const uint8_t* gs = w13s + grow * nb;
-    const uint8_t* us = gs + (size_t)F * nb;
+    const uint8_t* gs = w13s + grow * nch;
+    const uint8_t* us = gs + (size_t)F * nch;
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
-      const int c = lane + 64 * b;
-      const bool ok = c < nc;
-      gw[r][b] = ok ? *reinterpret_cast<const uint2*>(gc + (size_t)c * 8) : uint2{0u, 0u};
-      uw[r][b] = ok ? *reinterpret_cast<const uint2*>(uc + (size_t)c * 8) : uint2{0u, 0u};
-      gsc[r][b] = ok ? gs[c >> 1] : 0u;
-      usc[r][b] = ok ? us[c >> 1] : 0u;
+      const int c = min(lane + 64 * b, nch - 1);  // past the row: re-read, left out below
+      gw[r][b] = ld16_nt(gc + (size_t)c * 16);
+      uw[r][b] = ld16_nt(uc + (size_t)c * 16);
+      gsc[r][b] = gs[c];
+      usc[r][b] = us[c];
     }
   }
   for (int i = threadIdx.x; i < (D >> 3); i += MT)
-    *reinterpret_cast<uint4*>(xs + i * 8) = ld16(X + (size_t)t * D + i * 8);
+    *reinterpret_cast<uint4*>(xs + mx4_xslot(i >> 2, i & 3) * 8) =
+        ld16(X + (size_t)t * D + i * 8);
   __syncthreads();
+  float ag[NR] = {}, au[NR] = {};
 #pragma unroll
-  for (int r = 0; r < NR; ++r) {
-    if (f0 + r >= F) break;  // uniform over the wave
-    float ag = 0.f, au = 0.f;
+  for (int b = 0; b < NB; ++b) {
+    const int c = lane + 64 * b;
+    if (c < nch) {
+      uint4 x[4];
 #pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      const int c = lane + 64 * b;
-      if (c < nc) {
-        const uint4 x0 = *reinterpret_cast<const uint4*>(xs + c * 16);
-        const uint4 x1 = *reinterpret_cast<const uint4*>(xs + c * 16 + 8);
-        const float pg = dot8_bf16_d2(e2m1x8_bits(gw[r][b].y), x1,
-                                      dot8_bf16_d2(e2m1x8_bits(gw[r][b].x), x0, 0.f));
-        const float pu = dot8_bf16_d2(e2m1x8_bits(uw[r][b].y), x1,
-                                      dot8_bf16_d2(e2m1x8_bits(uw[r][b].x), x0, 0.f));
-        ag = __builtin_fmaf(pg, e8m0_value(gsc[r][b]), ag);
-        au = __builtin_fmaf(pu, e8m0_value(usc[r][b]), au);
+      for (int q = 0; q < 4; ++q) x[q] = *reinterpret_cast<const uint4*>(xs + mx4_xslot(c, q) * 8);
+#pragma unroll
+      for (int r = 0; r < NR; ++r) {
+        ag[r] = __builtin_fmaf(mx4_chunk_dot(gw[r][b], x, 0.f), e8m0_value(gsc[r][b]), ag[r]);
+        au[r] = __builtin_fmaf(mx4_chunk_dot(uw[r][b], x, 0.f), e8m0_value(usc[r][b]), au[r]);
       }
     }
-    ag = wave_sum(ag);
-    au = wave_sum(au);
-    if (lane == 0) act[(size_t)s * F + f0 + r] = f2bf(siluf(round_bf(ag)) * round_bf(au));
+  }
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    const float g = wave_sum(ag[r]), u = wave_sum(au[r]);
+    if (lane == 0 && f0 + r < F) act[(size_t)s * F + f0 + r] = f2bf(siluf(round_bf(g)) * round_bf(u));
   }
 }
 
-// Down projection + weighted combine, MXFP4: as expert_w2_combine_mx_kernel
-// with 8-byte chunks of 16 codes (scale byte c / 2), ROWS output rows per
-// workgroup and NW waves, wave w taking slots w, w + NW, ... (one each when
-// topk <= NW, so every weight load of the workgroup is in flight at once);
-// each act chunk is read once per slot for all ROWS rows.
+// Down projection + weighted combine, MXFP4: ROWS output rows per workgroup
+// and NW waves, wave w taking slots w, w + NW, ... (one each when topk <= NW,
+// so every weight load of the workgroup is in flight at once); a slot's
+// activation chunk (64 bytes per lane, straight from global memory) serves
+// all ROWS rows. The waves' partials are added in a fixed order.
 template <int ROWS, int NA, int NW>
 __global__ __launch_bounds__(NW * 64) void expert_w2_combine_mx4_kernel(
     const uint8_t* __restrict__ w2c, const uint8_t* __restrict__ w2s,
@@ -353,7 +367,7 @@ __global__ __launch_bounds__(NW * 64) void expert_w2_combine_mx4_kernel(
   const int t = blockIdx.y;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int d0 = blockIdx.x * ROWS;
-  const int nc = F >> 4, nb = F >> 5;
+  const int nch = F >> 5;
   const size_t rb = (size_t)F >> 1;
   float accr[ROWS] = {};
   for (int k = wave; k < topk; k += NW) {
@@ -363,39 +377,35 @@ __global__ __launch_bounds__(NW * 64) void expert_w2_combine_mx4_kernel(
       continue;
     }
     const uint8_t* wb = w2c + (size_t)e * D * rb;
-    const uint8_t* sb = w2s + (size_t)e * D * nb;
+    const uint8_t* sb = w2s + (size_t)e * D * nch;
     const uint16_t* ab = act + ((size_t)t * topk + k) * F;
     const float coef = wts[t * topk + k];
-    uint2 wv[ROWS][NA];
+    uint4 wv[ROWS][NA];
     uint32_t sc[ROWS][NA];
 #pragma unroll
     for (int r = 0; r < ROWS; ++r) {
       const int row = min(d0 + r, D - 1);
 #pragma unroll
       for (int i = 0; i < NA; ++i) {
-        const int c = lane + 64 * i;
-        const bool ok = c < nc;
-        wv[r][i] = ok ? *reinterpret_cast<const uint2*>(wb + (size_t)row * rb + (size_t)c * 8)
-                      : uint2{0u, 0u};
-        sc[r][i] = ok ? sb[(size_t)row * nb + (c >> 1)] : 0u;
+        const int c = min(lane + 64 * i, nch - 1);  // past the row: re-read, left out below
+        wv[r][i] = ld16_nt(wb + (size_t)row * rb + (size_t)c * 16);
+        sc[r][i] = sb[(size_t)row * nch + c];
       }
     }
-    uint4 av[NA][2];
+    uint4 av[NA][4];
 #pragma unroll
     for (int i = 0; i < NA; ++i) {
-      const int c = lane + 64 * i;
-      av[i][0] = c < nc ? ld16(ab + (size_t)c * 16) : uint4{0u, 0u, 0u, 0u};
-      av[i][1] = c < nc ? ld16(ab + (size_t)c * 16 + 8) : uint4{0u, 0u, 0u, 0u};
+      const int c = min(lane + 64 * i, nch - 1);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) av[i][q] = ld16(ab + (size_t)c * 32 + q * 8);
     }
 #pragma unroll
     for (int r = 0; r < ROWS; ++r) {
       float a = 0.f;
 #pragma unroll
-      for (int i = 0; i < NA; ++i) {
-        const float p = dot8_bf16_d2(e2m1x8_bits(wv[r][i].y), av[i][1],
-                                     dot8_bf16_d2(e2m1x8_bits(wv[r][i].x), av[i][0], 0.f));
-        a = __builtin_fmaf(p, e8m0_value(sc[r][i]), a);
-      }
+      for (int i = 0; i < NA; ++i)
+        if (lane + 64 * i < nch)
+          a = __builtin_fmaf(mx4_chunk_dot(wv[r][i], av[i], 0.f), e8m0_value(sc[r][i]), a);
       accr[r] = __builtin_fmaf(coef, a, accr[r]);
     }
   }
@@ -466,24 +476,27 @@ int launch_moe_mxfp4(int T, int D, int F, int E, int topk, const uint8_t* w13c,
                      const uint8_t* w13s, const uint8_t* w2c, const uint8_t* w2s,
                      const int32_t* idx, const float* wts, const uint16_t* X, uint16_t* act,
                      uint16_t* Y, hipStream_t st) {
-  constexpr int NR = 2, ROWS = 4, NW = 4;  // NW: waves of the down-projection workgroup
-  const int nc13 = D / 16, nc2 = F / 16;   // 16-code chunks
-  if (nc13 > 64 * 5 || nc2 > 64 * 3) return -2;
+  // measured best on MI355X at Beam's shapes (more rows per wave, or more
+  // waves per down-projection workgroup, ran slower); NW: waves of the
+  // down-projection workgroup
+  constexpr int NR = 2, ROWS = 4, NW = 4;
+  const int nch13 = D / 32, nch2 = F / 32;  // 32-code chunks
+  if (nch13 > 64 * 3 || nch2 > 64 * 2) return -2;
   const dim3 g13((F + 4 * NR - 1) / (4 * NR), T * topk);
   const size_t sh = (size_t)D * 2;
-  if (nc13 <= 64)
+  if (nch13 <= 64)
     hipLaunchKernelGGL((expert_w13_swiglu_mx4_kernel<1, NR>), g13, dim3(MT), sh, st, w13c, w13s,
                        idx, E, topk, F, D, X, act);
   else
-    hipLaunchKernelGGL((expert_w13_swiglu_mx4_kernel<5, NR>), g13, dim3(MT), sh, st, w13c, w13s,
+    hipLaunchKernelGGL((expert_w13_swiglu_mx4_kernel<3, NR>), g13, dim3(MT), sh, st, w13c, w13s,
                        idx, E, topk, F, D, X, act);
   if (hipGetLastError() != hipSuccess) return -1;
   const dim3 g2((D + ROWS - 1) / ROWS, T);
-  if (nc2 <= 64)
+  if (nch2 <= 64)
     hipLaunchKernelGGL((expert_w2_combine_mx4_kernel<ROWS, 1, NW>), g2, dim3(NW * 64), 0, st,
                        w2c, w2s, idx, wts, E, topk, F, D, act, Y);
   else
-    hipLaunchKernelGGL((expert_w2_combine_mx4_kernel<ROWS, 3, NW>), g2, dim3(NW * 64), 0, st,
+    hipLaunchKernelGGL((expert_w2_combine_mx4_kernel<ROWS, 2, NW>), g2, dim3(NW * 64), 0, st,
                        w2c, w2s, idx, wts, E, topk, F, D, act, Y);
   return LAUNCH_OK();
 }

@@ -196,3 +196,49 @@ def test_moe_mx_scaled_rejections():
         B.beam_moe_swiglu_combine_mx_scaled(dims, T, x, idx, w, 8, X.c13, X.s13, X.c2, X.s2,
                                             y, wsb[:512])
     assert e.value.code == -5
+
+
+def test_moe_mx_scaled_full_size():
+    """The benchmark's prefill MoE shape: 16,384 tokens, top-8 of all 256
+    experts of Beam's size (uniform routing), MXFP8 weights. Sampled: the
+    MXFP8 copy of x bit for bit on 512 tokens; one token's eight activation
+    rows and its output row stage by stage against the oracle; every output
+    row finite and no device flag."""
+    dims = BEAM
+    T = 8 * 2048
+    X = MxExperts("mxfp8", dims, "sc_full", device_draw=True)
+    x = synth.make_h((T, dims.D), 7, "mxsfull")
+    g = np.random.default_rng(31)
+    idx = np.argsort(g.random((T, dims.E)), axis=1)[:, :dims.topk].astype(np.int32)
+    w = g.uniform(0.05, 0.6, (T, dims.topk)).astype(np.float32)
+    K, D, F = dims.topk, dims.D, dims.F
+    P = T * K
+    y = torch.empty((T, D), **I16)
+    wsb = ws(dims, B.BEAM_OP_MOE_MX_SCALED, T)
+    B.beam_moe_swiglu_combine_mx_scaled(dims, T, dev(x), dev(idx), dev(w), 8, X.c13, X.s13, X.c2,
+                                        X.s2, y, wsb)
+    B.beam_check()
+    yb = y.view(torch.bfloat16)
+    assert bool(torch.isfinite(yb.float()).all()), "non-finite output rows"
+    # staged operands at the head of the workspace (see _run)
+    data = wsb[CTL_BYTES:]
+    o = 0
+    inv = data[o:o + 4 * P].view(torch.int32).view(T, K)
+    o += _al(4 * P)
+    xq = data[o:o + T * D].view(T, D)
+    o += _al(T * D)
+    xs = data[o:o + T * D // 32].view(T, D // 32)
+    o += _al(T * D // 32)
+    act_rows = data[o:o + 2 * P * F].view(torch.int16).view(P, F)
+    rows = np.sort(g.choice(T, 512, replace=False))
+    c_ref, s_ref = mx.mxfp8_quantize(bits_f64(x[rows]))
+    np.testing.assert_array_equal(xs[rows].cpu().numpy(), s_ref)
+    np.testing.assert_array_equal(xq[rows].cpu().numpy(), c_ref)
+    t = int(rows[len(rows) // 2])
+    act = np.full((1, K, F), np.nan)
+    act[0] = bits_f64(host_bits(act_rows[inv[t].long()]))
+    xt, it, wt = x[t:t + 1], idx[t:t + 1], w[t:t + 1]
+    act_ref, gate, up = mx.moe_mx_scaled_act(dims, xt, it, X.expert, gate_up=True)
+    _assert_act_close(act[0], act_ref[0], gate[0], up[0])
+    assert_rms_close(bits_f64(host_bits(y[t:t + 1])),
+                     mx.moe_mx_scaled_down(dims, act, it, wt, X.expert), "y2 full size")

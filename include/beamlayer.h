@@ -186,7 +186,8 @@ int beam_qk_norm_rope_ssmax_kvwrite(const beam_dims* dims, int T, const uint16_t
  * bits (a bf16 hi + lo pair), the flash kernel on a bf16 cache with d = 128
  * rounds probabilities to fp16 and converts V to fp16 (exact for bf16 values
  * of magnitude <= 65504; larger ones are clamped to +-65504 and the device
- * flag is raised, so beam_check reports BEAM_E_DEVICE for such a call).
+ * flag is raised, so beam_check reports BEAM_E_DEVICE for such a call; an
+ * infinite or NaN cached value among the keys a call reads raises it too).
  * Errors: window <= 0, max_pos >= npos; a ring cache with window > Lmax. */
 int beam_attn_swa(const beam_dims* dims, int T, const uint16_t* q, const int32_t* pos,
                   const int32_t* seq, const beam_kv* kv, const float* sink, uint16_t* o,

@@ -308,6 +308,7 @@ __global__ __launch_bounds__(768) void attn_prefill_kernel(
 constexpr int DMA_HD = 128;
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ int fk_swz(int r) { return r & 15; }
 __device__ __forceinline__ int fv_swz(int d) { return (d >> 1) & 7; }
@@ -477,30 +478,37 @@ __global__ __launch_bounds__(768) void attn_prefill_dma_kernel(
       // tile.
       {
         uint4* vt = reinterpret_cast<uint4*>(sV(cur));
-        float mag = 0.f;  // largest magnitude converted
+        uint32_t mag = 0;  // per 16-bit half: the largest fp16 magnitude written
         for (int c = tid; c < HD * KT / 8; c += nw * 64) {
-          const int d = c >> 3, k0 = kb + 8 * ((c & 7) ^ fv_swz(d));
           const uint4 w = vt[c];
           uint32_t in[4] = {w.x, w.y, w.z, w.w};
-          uint32_t out[4];
+          if (edge) {
+            const int d = c >> 3, k0 = kb + 8 * ((c & 7) ^ fv_swz(d));
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            if (edge) {
+            for (int e = 0; e < 4; ++e) {
               if (k0 + 2 * e < kmin || k0 + 2 * e > kmax) in[e] &= 0xffff0000u;
               if (k0 + 2 * e + 1 < kmin || k0 + 2 * e + 1 > kmax) in[e] &= 0x0000ffffu;
             }
-            const float lo_v = bf_lo(in[e]), hi_v = bf_hi(in[e]);
-            mag = fmaxf(mag, fmaxf(fabsf(lo_v), fabsf(hi_v)));
+          }
+          uint32_t out[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
             // round toward zero: exact for bf16 values in fp16's range (but
             // those below 2^-17, off by under 2^-24), and an overflow gives
             // the largest finite value, +-65504
-            out[e] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo_v, hi_v));
+            out[e] = __builtin_bit_cast(
+                uint32_t, __builtin_amdgcn_cvt_pkrtz(bf_lo(in[e]), bf_hi(in[e])));
+            // integer max per 16-bit half of the magnitudes written
+            mag = __builtin_bit_cast(
+                uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2, mag),
+                                                    __builtin_bit_cast(u16x2, out[e] & 0x7fff7fffu)));
           }
           vt[c] = uint4{out[0], out[1], out[2], out[3]};
         }
-        // beyond fp16's range (bf16 magnitudes of 65536 and up; NaN compares
-        // false): clamped to +-65504 above, and reported
-        if (mag >= 65536.f) BEAM_RAISE(attnp, ERR_RANGE);
+        // 65504 (0x7bff) is written only for a clamped value (no bf16 value
+        // lies in [65504, 65536)); infinities and NaN (0x7c00 and up) are
+        // reported with them
+        if ((mag & 0xffffu) >= 0x7bffu || (mag >> 16) >= 0x7bffu) BEAM_RAISE(attnp, ERR_RANGE);
         __syncthreads();
       }
       if (__any(mine)) {  // waves with no token of this sequence only load

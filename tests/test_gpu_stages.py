@@ -401,8 +401,9 @@ def test_prefill_attention_flags(mode):
     """The many-token kernel on a bf16 cache at head dim 128 takes P.V on fp16
     operands. A cached value beyond fp16's range (7e4) is clamped to 65504 and
     the call reports the device flag; the output then equals the oracle's
-    attention over the cache with that value clamped. A token at a negative
-    position is reported too and its output row is zero."""
+    attention over the cache with that value clamped. The largest bf16 value
+    below 65536 (65280) converts exactly and is not reported. A token at a
+    negative position is reported and its output row is zero."""
     dims = BEAM
     T = 70
     pos = np.arange(2900, 2970, dtype=np.int32)
@@ -422,16 +423,18 @@ def test_prefill_attention_flags(mode):
     assert e.value.code == -8 and "fp16" in str(e.value)
     ref = L.attention(dims, bits_f64(host_bits(q)), pos, seq, oc, mode)
     assert_rms_close(bits_f64(host_bits(o)), ref, "o (value clamped)")
-    # a negative position: reported, row zero, the other tokens unchanged
+    # a negative position: reported, row zero, the other tokens unchanged; the
+    # value at 65280 is in fp16's range (no range report)
     pos2 = pos.copy()
     pos2[5] = -1
-    cache.V[0, 3, 17, u] = dev(_bits(np.array([1.0])))[0]
-    oc.V[0, 3, u, 17] = 1.0
+    cache.V[0, 3, 17, u] = dev(_bits(np.array([65280.0])))[0]
+    oc.V[0, 3, u, 17] = 65280.0
     o2 = torch.empty((T, dims.Hq, dims.d), **I16)
     fn(dims, T, q, dev(pos2), dev(seq), cache.struct(), None, o2, 2969, ws(dims, op, T, 2970))
     with pytest.raises(B.BeamError) as e:
         B.beam_check()
     assert e.value.code == -8 and "outside the cache" in str(e.value)
+    assert "fp16" not in str(e.value)
     assert int(o2[5].count_nonzero()) == 0
     keep = np.arange(T) != 5
     ref2 = L.attention(dims, bits_f64(host_bits(q))[keep], pos[keep], seq[keep], oc, mode)

@@ -324,13 +324,19 @@ static int launch(const GemmArgs& a, int grid_n, int grid_m, hipStream_t st, int
 // [split][M][N]; gemm_split_reduce adds the partials in split order and
 // applies the epilogue (bf16 store with optional column split, or SwiGLU of
 // the gate / up column halves).
+// Tile rows of the split product: 32-row tiles for at most 128 tokens (72 KiB
+// of LDS, two workgroups per CU, so twice the splits are in flight), else 256.
+static int split_rows(int M) { return M <= 128 ? 32 : BM; }
+
 int gemm_splits(int M, int N, int K) {
   if (M > BM || K % BK) return 1;
-  const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+  const int tr = split_rows(M);
+  const int tiles = ((M + tr - 1) / tr) * ((N + BN - 1) / BN);
+  const int cap = tr == BM ? 256 : 512;  // workgroups the chip holds at once
   const int ks = K / BK;
   int s = 1;
   // the partials (written, then read back) stay within half the weight bytes
-  while (tiles * s * 2 <= 256 && ks % (s * 2) == 0 && (long long)s * 2 * 4 * M <= K) s *= 2;
+  while (tiles * s * 2 <= cap && ks % (s * 2) == 0 && (long long)s * 2 * 4 * M <= K) s *= 2;
   return s;
 }
 
@@ -372,8 +378,11 @@ static int launch_split(const GemmArgs& a0, int splits, float* part, hipStream_t
   a.ldo = a.N;
   a.kt_split = a.K / BK / splits;
   a.split_stride = (long long)a.M * a.N;
-  const int tn = (a.N + BN - 1) / BN, tm = (a.M + BM - 1) / BM;
-  if (launch<EPI_F32, true>(a, tn, tm, st, splits)) return -1;
+  const int tr = split_rows(a.M);
+  const int tn = (a.N + BN - 1) / BN, tm = (a.M + tr - 1) / tr;
+  if (tr == BM ? launch<EPI_F32, true>(a, tn, tm, st, splits)
+               : launch<EPI_F32, true, 32>(a, tn, tm, st, splits))
+    return -1;
   const long long n = (long long)a.M * (EPI == EPI_SWIGLU ? a0.F : a.N);
   hipLaunchKernelGGL((gemm_split_reduce_kernel<EPI>), dim3((unsigned)((n + 255) / 256)),
                      dim3(256), 0, st, part, splits, a.M, a.N,

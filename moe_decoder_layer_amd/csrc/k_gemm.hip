@@ -81,17 +81,20 @@ __device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ ((row >>
 // TR: tile rows (256, or 32 for grouped segments of a few rows each, which
 // need only a 32-row A tile in LDS: 72 KiB instead of 128, two workgroups per
 // CU, twice the weight streams in flight).
-template <int EPI, int WAVES, bool SKIP, int TR = BM>
+template <int EPI, int WAVES, bool SKIP, int TR = BM, int NS = 2>
 __global__ __launch_bounds__(WAVES * 64) void gemm_bf16_kernel(GemmArgs g) {
   static_assert(TR == BM || (SKIP && TR == 32), "short tiles need the row skip");
+  static_assert(NS == 2 || (NS == 4 && TR == 32), "a four-slab ring only for 32-row tiles");
   constexpr int WCOLS = WAVES / 2;     // wave grid columns
   constexpr int WN = BN / WCOLS;       // wave tile width (128 or 64)
   constexpr int TJ = WN / 32;          // 32-wide MFMA blocks per wave row
   constexpr int RPW = BM / WAVES;      // tile rows each wave loads (A and B)
+  // K slabs in LDS (NS): two, or four for 32-row tiles bound by the weight
+  // stream (three slabs in flight instead of one)
   extern __shared__ __align__(16) uint16_t lds[];
-  // double buffer: A0 | A1 | B0 | B1
+  // ring of NS slabs: A0 .. A(NS-1) | B0 .. B(NS-1)
   auto As = [&](int buf) { return lds + buf * (TR * BK); };
-  auto Bs = [&](int buf) { return lds + 2 * TR * BK + buf * (BN * BK); };
+  auto Bs = [&](int buf) { return lds + NS * TR * BK + buf * (BN * BK); };
 
   // ---- workgroup -> tile (XCD-contiguous, grouped column-major) ---------------
   // Grouped mode launches the worst-case number of tile rows; only the first
@@ -184,8 +187,10 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_bf16_kernel(GemmArgs g) {
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
       // SKIP: A rows past the tile's last row are not fetched (their LDS rows
-      // only feed outputs that are never stored)
-      if (!SKIP || wave * RPW + i * 8 < mrows)  // (mrows <= TR)
+      // only feed outputs that are never stored); with 32-row tiles all of
+      // wave 0's A rows are (clamped to the last row), so every wave issues a
+      // fixed number of copies per slab
+      if (!SKIP || wave * RPW + i * 8 < (NS > 2 ? TR : mrows))  // (mrows <= TR)
         load_lds16(a_src[i] + k0, As(buf) + (wave * RPW + i * 8) * BK);
       load_lds16(b_src[i] + k0, Bs(buf) + (wave * RPW + i * 8) * BK);
     }
@@ -223,18 +228,38 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_bf16_kernel(GemmArgs g) {
 
   const int kt0 = g.kt_split ? blockIdx.y * g.kt_split : 0;
   const int KT = g.kt_split ? kt0 + g.kt_split : g.K / BK;
-  gload(kt0 * BK, 0);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
+  // Ring: this wave's copies of one slab are NL (B rows) plus, in wave 0 of a
+  // 32-row tile, NL more (A rows). Waiting for slab kt + 1 leaves the copies
+  // of the `ahead` slabs issued after it in flight; the barrier then makes
+  // every wave's copies of slab kt + 1 visible, and no wave still reads the
+  // slab the next copy overwrites (its fragment reads have completed).
+  const int per_slab = (NS > 2 && wave == 0) ? 2 * NL : NL;
+  auto ring_barrier = [&](int ahead) {
+    const int n = ahead * per_slab;  // 0, NL, 2 NL or 4 NL
+    if (n == 0) asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    else if (n == NL) asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(NL) : "memory");
+    else if (n == 2 * NL)
+      asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(2 * NL) : "memory");
+    else asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(4 * NL) : "memory");
+  };
+  if constexpr (NS == 2) {
+    gload(kt0 * BK, 0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+  } else {
+    const int pre = min(NS - 1, KT - kt0);  // slabs requested ahead of the loop
+    for (int p = 0; p < pre; ++p) gload((kt0 + p) * BK, p);
+    ring_barrier(pre - 1);
+  }
   // Two copies of the K loop: one with the per-block row skip, one without its
   // branches. A wave whose row blocks all hold rows takes the branch-free copy,
   // so SKIP costs full tiles nothing (both copies meet the same barriers).
   auto kloop = [&](auto skip_tag) {
     constexpr bool SK = decltype(skip_tag)::value;
     for (int kt = kt0; kt < KT; ++kt) {
-      const int cur = (kt - kt0) & 1;  // buffer 0 holds the first k-step of this split
-      // the other buffer was last read in step kt - 1, which every wave has left
-      if (kt + 1 < KT) gload((kt + 1) * BK, cur ^ 1);
+      const int cur = (kt - kt0) % NS;  // slot 0 holds the first k-step of this split
+      // the slot copied into was last read in step kt - 1, which every wave has left
+      if (kt + NS - 1 < KT) gload((kt + NS - 1) * BK, (kt - kt0 + NS - 1) % NS);
       bf16x8 af[2][MI], bfr[2][TJ];
       frags(cur, 0, af[0], bfr[0]);
 #pragma unroll
@@ -249,8 +274,12 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_bf16_kernel(GemmArgs g) {
                                                                acc[i][j], 0, 0, 0);
         }
       }
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's loads of step kt + 1
-      __syncthreads();
+      if constexpr (NS == 2) {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's loads of step kt + 1
+        __syncthreads();
+      } else {
+        ring_barrier(max(0, min(NS - 2, KT - 2 - kt)));  // slabs kt + 2 .. issued
+      }
     }
   };
   if (SKIP && band < MI * 32) kloop(std::integral_constant<bool, SKIP>{});
@@ -298,22 +327,22 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_bf16_kernel(GemmArgs g) {
   }
 }
 
-static size_t gemm_lds_bytes(int tr = BM) { return (size_t)2 * (tr + BN) * BK * 2; }
+static size_t gemm_lds_bytes(int tr = BM, int ns = 2) { return (size_t)ns * (tr + BN) * BK * 2; }
 
-template <int EPI, bool SKIP = false, int TR = BM, int WAVES = kGemmWaves>
+template <int EPI, bool SKIP = false, int TR = BM, int WAVES = kGemmWaves, int NS = 2>
 static int launch(const GemmArgs& a, int grid_n, int grid_m, hipStream_t st, int splits = 1) {
   static bool attr_set = false;
   if (!attr_set) {
     (void)hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&gemm_bf16_kernel<EPI, WAVES, SKIP, TR>),
-        hipFuncAttributeMaxDynamicSharedMemorySize, (int)gemm_lds_bytes(TR));
+        reinterpret_cast<const void*>(&gemm_bf16_kernel<EPI, WAVES, SKIP, TR, NS>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, (int)gemm_lds_bytes(TR, NS));
     attr_set = true;
   }
   GemmArgs g = a;
   g.tiles_m = grid_m;
   g.tiles_n = grid_n;
-  hipLaunchKernelGGL((gemm_bf16_kernel<EPI, WAVES, SKIP, TR>), dim3(grid_m * grid_n, splits),
-                     dim3(WAVES * 64), gemm_lds_bytes(TR), st, g);
+  hipLaunchKernelGGL((gemm_bf16_kernel<EPI, WAVES, SKIP, TR, NS>), dim3(grid_m * grid_n, splits),
+                     dim3(WAVES * 64), gemm_lds_bytes(TR, NS), st, g);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
@@ -417,8 +446,10 @@ int launch_gemm_swiglu(int M, int F, int K, const uint16_t* A, int lda, const in
     if (s > 1 && part) return launch_split<EPI_SWIGLU>(a, s, part, st);
   }
   const int gn = (2 * F + BN - 1) / BN;
+  // the gate/up rows (K = D) stream through a four-slab ring: one workgroup
+  // per CU with three slabs in flight beats two with one each here
   if (seg_off && gemm_grouped_rows(M, E) == 32)
-    return launch<EPI_SWIGLU, true, 32>(a, gn, max_mtiles, st);
+    return launch<EPI_SWIGLU, true, 32, kGemmWaves, 4>(a, gn, max_mtiles, st);
   const int gm = seg_off ? max_mtiles : (M + BM - 1) / BM;
   if (seg_off || M <= BM / 2) return launch<EPI_SWIGLU, true>(a, gn, gm, st);
   return launch<EPI_SWIGLU>(a, gn, gm, st);

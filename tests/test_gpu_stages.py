@@ -647,6 +647,28 @@ def test_moe_shared_expert(T, bad):
     assert_rms_close(bits_f64(host_bits(y)), ref, "y2")
 
 
+@pytest.mark.parametrize("D", [64, 128, 192, 320])
+def test_moe_sparse_tiles_short_k(D):
+    """Many tokens with a few rows per expert (T = 40, 160 pairs over 16
+    experts: 32-row tiles). The gate/up product stages its K slabs of 64
+    through a ring of four; D = 64, 128, 192 and 320 give 1, 2, 3 and 5 slabs,
+    so the ring's prologue, its waits near the end of K and its wrap-around
+    all run."""
+    dims = _dims(CFG0, D=D)
+    T = 40
+    P = Params(dims, 0, 6)
+    x = synth.make_h((T, D), 7, "mshort", D)
+    g = np.random.default_rng(D)
+    idx = np.stack([g.choice(dims.E, dims.topk, replace=False) for _ in range(T)]).astype(np.int32)
+    w = g.uniform(0.05, 0.6, (T, dims.topk)).astype(np.float32)
+    y = torch.empty((T, D), **I16)
+    B.beam_moe_swiglu_combine(dims, T, dev(x), dev(idx), dev(w), P.t["w13"], P.t["w2"], None, None,
+                              y, ws(dims, B.BEAM_OP_MOE, T))
+    B.beam_check()
+    ref = L.moe(dims, x, idx, w, P.expert)
+    assert_rms_close(bits_f64(host_bits(y)), ref, "y2")
+
+
 def test_moe_bad_expert_id_is_flagged():
     """An id outside [0, E) is skipped by the kernels' own check and reported."""
     dims = CFG0

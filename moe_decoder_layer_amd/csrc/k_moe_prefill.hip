@@ -144,6 +144,108 @@ __global__ __launch_bounds__(256) void moe_scatter_kernel(const int32_t* __restr
   }
 }
 
+// The whole routing in one workgroup for at most 2,048 pairs (a batch of
+// decode steps), with the same results as the three kernels above: per-expert
+// counts by LDS atomics, the scan of (rows, tiles), then the pairs ranked in
+// (token, slot) order, 1,024 at a time. Within a wave, the lanes that share an
+// expert are found one distinct expert per round (a ballot against the first
+// unresolved lane's expert); each wave's lowest lane per expert enters the
+// group's size in a [wave][expert] table, and thread e turns expert e's column
+// into each wave's first row (a prefix over the waves in order).
+constexpr int kRouteSmallMax = 2048;
+
+__global__ __launch_bounds__(1024) void moe_route_small_kernel(
+    const int32_t* __restrict__ idx, int P, int K, int spt, int E, int NE, int tile_rows,
+    int32_t* __restrict__ seg_off, int32_t* __restrict__ tile_off, int32_t* __restrict__ perm,
+    int32_t* __restrict__ inv) {
+  __shared__ int run[1024];
+  __shared__ int wcnt[16 * 1024];
+  __shared__ int wr[16], wt[16];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  int ev[2];  // experts of pairs tid and tid + 1024 (-1: an id outside [0, E); -2: no pair)
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int i = tid + h * 1024;
+    ev[h] = i < P ? pair_expert(idx, i, K, spt, E) : -2;
+    if (ev[h] == -1) BEAM_RAISE(moe, ERR_EXPERT);
+  }
+  if (tid < NE) run[tid] = 0;
+  __syncthreads();
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+    if (ev[h] >= 0) atomicAdd(&run[ev[h]], 1);  // an integer count: order-independent
+  __syncthreads();
+  // thread e: expert e's rows and tiles, inclusive scan within the wave, then
+  // across the waves
+  const int c = tid < NE ? run[tid] : 0;
+  const int tc = (c + tile_rows - 1) / tile_rows;
+  int r = c, t = tc;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int ro = __shfl_up(r, o, 64), to = __shfl_up(t, o, 64);
+    if (lane >= o) {
+      r += ro;
+      t += to;
+    }
+  }
+  if (lane == 63) {
+    wr[wave] = r;
+    wt[wave] = t;
+  }
+  __syncthreads();
+  for (int w = 0; w < wave; ++w) {
+    r += wr[w];
+    t += wt[w];
+  }
+  if (tid < NE) {
+    seg_off[tid] = r - c;  // exclusive prefix
+    tile_off[tid] = t - tc;
+    run[tid] = r - c;      // the next row of expert tid
+  }
+  if (tid == NE - 1) {
+    seg_off[NE] = r;
+    tile_off[NE] = t;
+  }
+  __syncthreads();
+  for (int h = 0; h < 2 && h * 1024 < P; ++h) {
+    const int i = tid + h * 1024, v = ev[h];
+    const bool ok = v >= 0;
+    uint64_t same = 0;  // lanes of this wave with expert v
+    uint64_t pend = __ballot(ok);
+    while (pend) {
+      const int lead = __ffsll((unsigned long long)pend) - 1;
+      const int lv = __shfl(v, lead, 64);
+      const uint64_t m = __ballot(ok && v == lv);
+      if (ok && v == lv) same = m;
+      pend &= ~m;
+    }
+    const int rank = __popcll(same & ((1ull << lane) - 1));
+    // wcnt[w][e]: pairs of expert e in wave w, then wave w's first row for e
+    // (cleared once every wave has read its rows of the previous batch)
+    __syncthreads();
+    for (int k = tid; k < 16 * NE; k += 1024) wcnt[k] = 0;
+    __syncthreads();
+    if (ok && rank == 0) wcnt[wave * NE + v] = __popcll(same);
+    __syncthreads();
+    if (tid < NE) {
+      int row = run[tid];
+#pragma unroll
+      for (int w = 0; w < 16; ++w) {
+        const int n = wcnt[w * NE + tid];
+        wcnt[w * NE + tid] = row;
+        row += n;
+      }
+      run[tid] = row;
+    }
+    __syncthreads();
+    if (ok) {
+      const int row = wcnt[wave * NE + v] + rank;
+      perm[row] = i / spt;
+      inv[i] = row;
+    }
+  }
+}
+
 // One workgroup per token row; each thread covers 4 columns per pass.
 __global__ __launch_bounds__(256) void moe_combine_kernel(const float* __restrict__ out,
                                                           const int32_t* __restrict__ inv,
@@ -217,6 +319,11 @@ int launch_moe_route(int T, int K, int spt, int E, const int32_t* idx, int tile_
                      int32_t* inv, hipStream_t st) {
   const int P = T * spt, NE = E + (spt > K ? 1 : 0);
   if (NE > 1024) return -1;
+  if (P <= kRouteSmallMax) {
+    hipLaunchKernelGGL(moe_route_small_kernel, dim3(1), dim3(1024), 0, st, idx, P, K, spt, E, NE,
+                       tile_rows, seg_off, tile_off, perm, inv);
+    return hipGetLastError() == hipSuccess ? 0 : -1;
+  }
   const int chunk = moe_route_chunk(P), nch = moe_route_chunks(P);
   hipLaunchKernelGGL(moe_count_kernel, dim3(nch), dim3(256), 0, st, idx, P, K, spt, E, NE, chunk,
                      counts);

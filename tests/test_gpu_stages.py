@@ -669,6 +669,25 @@ def test_moe_sparse_tiles_short_k(D):
     assert_rms_close(bits_f64(host_bits(y)), ref, "y2")
 
 
+@pytest.mark.parametrize("T", [256, 512, 513])
+def test_moe_routing_pair_counts(T):
+    """The routing permutation at the one-workgroup kernel's edges: 1,024 and
+    2,048 (token, slot) pairs (one and two full batches of its ranking) and
+    2,052 (past its limit: the chunked three-kernel path)."""
+    dims = CFG0
+    P = Params(dims, 0, 6)
+    x = synth.make_h((T, dims.D), 7, "mroute", T)
+    g = np.random.default_rng(T)
+    idx = np.stack([g.choice(dims.E, dims.topk, replace=False) for _ in range(T)]).astype(np.int32)
+    w = g.uniform(0.05, 0.6, (T, dims.topk)).astype(np.float32)
+    y = torch.empty((T, dims.D), **I16)
+    B.beam_moe_swiglu_combine(dims, T, dev(x), dev(idx), dev(w), P.t["w13"], P.t["w2"], None, None,
+                              y, ws(dims, B.BEAM_OP_MOE, T))
+    B.beam_check()
+    ref = L.moe(dims, x, idx, w, P.expert)
+    assert_rms_close(bits_f64(host_bits(y)), ref, "y2")
+
+
 def test_moe_bad_expert_id_is_flagged():
     """An id outside [0, E) is skipped by the kernels' own check and reported."""
     dims = CFG0

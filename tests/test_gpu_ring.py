@@ -88,7 +88,7 @@ def test_ring_attention_equals_linear(case, kv):
         B.beam_check()
         outs.append(o)
     assert torch.equal(outs[0], outs[1]), "ring and linear caches give different outputs"
-    if kv == "bf16" and case in ("decode", "two_chunks"):
+    if kv == "bf16" and case in ("decode", "batch", "two_chunks"):
         want = L.attention(dims, bits_f64(host_bits(q)), pos, seq, lin.oracle(ctx), "swa")
         assert_rms_close(bits_f64(host_bits(outs[1])), want, "o (ring)")
 

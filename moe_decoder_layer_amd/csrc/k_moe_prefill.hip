@@ -280,6 +280,58 @@ __global__ __launch_bounds__(256) void moe_combine_kernel(const float* __restric
   }
 }
 
+// The same combine for at most KM routed slots: the token's ids, weights and
+// rows are requested once, before any row, and each pass requests every slot's
+// row chunk before the first product (the products and sums in the order of
+// moe_combine_kernel, so both give identical results).
+template <int KM>
+__global__ __launch_bounds__(256) void moe_combine_rows_kernel(const float* __restrict__ out,
+                                                               const int32_t* __restrict__ inv,
+                                                               const float* __restrict__ w,
+                                                               const int32_t* __restrict__ idx,
+                                                               int K, int spt, int E, int D,
+                                                               uint16_t* __restrict__ y) {
+  const int t = blockIdx.x;
+  const bool shared = spt > K;
+  bool ok[KM];
+  float wk[KM];
+  size_t row[KM + 1];
+#pragma unroll
+  for (int k = 0; k < KM; ++k) {
+    const int e = k < K ? idx[t * K + k] : -1;
+    ok[k] = e >= 0 && e < E;  // an id outside [0, E): its slot has no row
+    wk[k] = ok[k] ? w[t * K + k] : 0.f;
+    row[k] = ok[k] ? (size_t)inv[t * spt + k] * D : 0;
+  }
+  row[KM] = shared ? (size_t)inv[t * spt + K] * D : 0;
+  for (int c = threadIdx.x * 4; c < D; c += 256 * 4) {
+    f32x4 v[KM + 1];
+#pragma unroll
+    for (int k = 0; k < KM; ++k)
+      v[k] = ok[k] ? *reinterpret_cast<const f32x4*>(out + row[k] + c) : f32x4{0.f, 0.f, 0.f, 0.f};
+    v[KM] = shared ? *reinterpret_cast<const f32x4*>(out + row[KM] + c) : f32x4{0.f, 0.f, 0.f, 0.f};
+    float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+#pragma unroll
+    for (int k = 0; k < KM; ++k) {
+      if (!ok[k]) continue;
+      a0 = __builtin_fmaf(wk[k], v[k][0], a0);
+      a1 = __builtin_fmaf(wk[k], v[k][1], a1);
+      a2 = __builtin_fmaf(wk[k], v[k][2], a2);
+      a3 = __builtin_fmaf(wk[k], v[k][3], a3);
+    }
+    if (shared) {  // the shared expert's row, weight 1
+      a0 += v[KM][0];
+      a1 += v[KM][1];
+      a2 += v[KM][2];
+      a3 += v[KM][3];
+    }
+    uint2 o;
+    o.x = pack_bf2(a0, a1);
+    o.y = pack_bf2(a2, a3);
+    *reinterpret_cast<uint2*>(y + (size_t)t * D + c) = o;
+  }
+}
+
 // z = bf16(o * sigmoid(g + b[head])) over [T][HD] with HD = Hq * hd; 8 per thread.
 __global__ __launch_bounds__(256) void gate_kernel(const uint16_t* __restrict__ o,
                                                    const uint16_t* __restrict__ g,
@@ -336,8 +388,12 @@ int launch_moe_route(int T, int K, int spt, int E, const int32_t* idx, int tile_
 
 int launch_moe_combine(int T, int K, int spt, int E, int D, const float* out, const int32_t* inv,
                        const float* w, const int32_t* idx, uint16_t* y, hipStream_t st) {
-  hipLaunchKernelGGL(moe_combine_kernel, dim3(T), dim3(256), 0, st, out, inv, w, idx, K, spt, E, D,
-                     y);
+  if (K <= 8)
+    hipLaunchKernelGGL((moe_combine_rows_kernel<8>), dim3(T), dim3(256), 0, st, out, inv, w, idx,
+                       K, spt, E, D, y);
+  else
+    hipLaunchKernelGGL(moe_combine_kernel, dim3(T), dim3(256), 0, st, out, inv, w, idx, K, spt, E,
+                       D, y);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

@@ -249,7 +249,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_bf16_kernel(GemmArgs g) {
   } else {
     const int pre = min(NS - 1, KT - kt0);  // slabs requested ahead of the loop
     for (int p = 0; p < pre; ++p) gload((kt0 + p) * BK, p);
-    ring_barrier(pre - 1);
+    ring_barrier(max(0, pre - 1));
   }
   // Two copies of the K loop: one with the per-block row skip, one without its
   // branches. A wave whose row blocks all hold rows takes the branch-free copy,
